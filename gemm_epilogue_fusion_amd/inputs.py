@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs for the fused GEMM -> residual -> RMSNorm -> GEMM block.
+
+This module only draws random tensors.  It holds none of the block's arithmetic, and both the GPU path and
+the CPU oracle take their inputs from it (nothing else is shared between them).
+
+Workloads (shapes of a LLaMA-3-style decoder, the model family the CODA write-up profiles in its section
+on where training time goes: a 1B model trained with TorchTitan on one GPU).  Real activations are replaced
+by seeded Gaussians of the stated spread; real activations may carry outlier channels that these lack.
+
+Generation recipe: one CPU ``torch.Generator`` per tensor, seeded ``16 * seed + idx`` with idx X=0, W1=1,
+R=2, gamma=3, W2=4; values are drawn in fp32 and rounded to nearest-even bf16 (gamma stays fp32).  The
+fp8 workload draws the same fp32 values and quantises X per row and the weights per output column to OCP
+e4m3fn with scale amax/448 (an all-zero row or column gets scale 1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Dict, Optional
+
+import torch
+
+EPI_IDENTITY = 0
+EPI_SWIGLU = 1
+E4M3_MAX = 448.0
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    K1: int
+    D: int
+    N2: int
+    epi: int
+    eps: float
+    x_std: float = 1.0
+    w1_std: float = 0.02
+    r_std: float = 1.0
+    w2_std: float = 0.02
+    gamma_lo: float = 0.5
+    gamma_hi: float = 1.5
+    fp8: bool = False
+    seed: int = 0
+
+    @property
+    def n_out(self) -> int:
+        return self.N2 if self.epi == EPI_IDENTITY else self.N2 // 2
+
+    @property
+    def flops(self) -> int:
+        """Multiply-adds of the two products, counted as 2 flops each (epilogue work excluded)."""
+        return 2 * self.M * self.K1 * self.D + 2 * self.M * self.D * self.N2
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads.  "tiny" is the case the oracle finishes in well under a second; the others are the
+# full-size shapes.
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", M=64, K1=256, D=256, N2=512, epi=EPI_IDENTITY, eps=1e-6,
+                     w1_std=(1 / 256) ** 0.5, w2_std=(1 / 256) ** 0.5),
+    # attention output projection -> RMSNorm -> gate|up projection with SwiGLU, 1B-style (hidden 2048,
+    # intermediate 8192), 4 sequences of 2048 tokens
+    "1b_attn_out_mlp_in": Workload("1b_attn_out_mlp_in", M=8192, K1=2048, D=2048, N2=16384,
+                                   epi=EPI_SWIGLU, eps=1e-5),
+    # MLP down projection -> RMSNorm -> QKV projection (32 q heads + 8 k + 8 v heads of 64), 1B-style
+    "1b_mlp_out_qkv": Workload("1b_mlp_out_qkv", M=8192, K1=8192, D=2048, N2=3072, epi=EPI_IDENTITY,
+                               eps=1e-5, x_std=0.5),
+    # attention output projection -> RMSNorm -> gate|up with SwiGLU, 8B-style (hidden 4096, inter 14336)
+    "8b_attn_out_mlp_in": Workload("8b_attn_out_mlp_in", M=16384, K1=4096, D=4096, N2=28672,
+                                   epi=EPI_SWIGLU, eps=1e-5),
+    # the 1B attention-out -> MLP-in block with e4m3 X / weights and per-row / per-column fp32 scales
+    "1b_attn_out_mlp_in_fp8": Workload("1b_attn_out_mlp_in_fp8", M=8192, K1=2048, D=2048, N2=16384,
+                                       epi=EPI_SWIGLU, eps=1e-5, fp8=True),
+}
+
+
+def _gen(seed: int, idx: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    g.manual_seed(16 * seed + idx)
+    return g
+
+
+def _normal(shape, std, seed, idx) -> torch.Tensor:
+    return torch.randn(*shape, generator=_gen(seed, idx), dtype=torch.float32) * std
+
+
+def _quantize_e4m3(t: torch.Tensor, dim: int):
+    """Per-row (dim=1 reduces along columns) or per-column (dim=0) e4m3fn quantisation, scale amax/448."""
+    amax = t.abs().amax(dim=dim)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax)).to(torch.float32)
+    s = scale.unsqueeze(dim)
+    q = (t / s).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return q, scale
+
+
+@dataclass
+class BlockInputs:
+    wl: Workload
+    X: torch.Tensor        # [M, K1] bf16 (fp8 workloads: the unquantised draw, for reference only)
+    W1: torch.Tensor       # [K1, D] bf16
+    R: torch.Tensor        # [M, D] bf16
+    gamma: torch.Tensor    # [D] fp32
+    W2: torch.Tensor       # [D, N2] bf16
+    Xq: Optional[torch.Tensor] = None    # [M, K1] float8_e4m3fn
+    sx: Optional[torch.Tensor] = None    # [M] fp32
+    W1q: Optional[torch.Tensor] = None   # [K1, D] float8_e4m3fn
+    sw1: Optional[torch.Tensor] = None   # [D] fp32
+    W2q: Optional[torch.Tensor] = None   # [D, N2] float8_e4m3fn
+    sw2: Optional[torch.Tensor] = None   # [N2] fp32
+    extras: dict = field(default_factory=dict)
+
+
+def make_inputs(wl: Workload) -> BlockInputs:
+    """Draw the inputs of workload ``wl`` on the CPU.  Deterministic in (wl, seed)."""
+    s = wl.seed
+    Xf = _normal((wl.M, wl.K1), wl.x_std, s, 0)
+    W1f = _normal((wl.K1, wl.D), wl.w1_std, s, 1)
+    Rf = _normal((wl.M, wl.D), wl.r_std, s, 2)
+    gamma = torch.rand(wl.D, generator=_gen(s, 3), dtype=torch.float32) * (wl.gamma_hi - wl.gamma_lo) + wl.gamma_lo
+    W2f = _normal((wl.D, wl.N2), wl.w2_std, s, 4)
+    out = BlockInputs(wl, Xf.to(torch.bfloat16), W1f.to(torch.bfloat16), Rf.to(torch.bfloat16), gamma,
+                      W2f.to(torch.bfloat16))
+    if wl.fp8:
+        out.Xq, out.sx = _quantize_e4m3(Xf, dim=1)
+        out.W1q, out.sw1 = _quantize_e4m3(W1f, dim=0)
+        out.W2q, out.sw2 = _quantize_e4m3(W2f, dim=0)
+    return out

@@ -1,0 +1,211 @@
+"""fp64 CPU oracle for the fused GEMM -> residual -> RMSNorm -> GEMM block.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library (``gemm_epilogue_fusion_amd``) never imports it and
+shares no code with it; the two meet only in the tests, on the same seeded inputs.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, compiled with gcc).  This module builds it, loads it
+with ctypes and wraps each entry point for numpy arrays.  Every function follows the CODA write-up
+("CODA: new research optimizes Transformer training with GEMM-epilogue programming", section
+"CODA: the treasure hidden in the epilogue"); the readings of what the pages leave open are listed in
+``oracle.h``.
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py`` against closed forms,
+invariants, library routines (torch's rms_norm / silu / dtype casts) or exhaustive code tables.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+EPI_IDENTITY = 0
+EPI_SWIGLU = 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (-O2, no fast-math: IEEE semantics are part of the
+    contract).  Returns the library path."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    i64, dp, f = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.c_double
+    block_sig = [i64, i64, i64, i64, dp, dp, dp, dp, dp, f, ctypes.c_int, dp, dp, dp, ctypes.c_int]
+    for name in ("oracle_block_unfused_f64", "oracle_block_fused_f64", "oracle_block_roundpts_f64"):
+        getattr(lib, name).argtypes = block_sig
+        getattr(lib, name).restype = ctypes.c_int
+    lib.oracle_gemm_residual_f64.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_gemm_residual_f64.restype = ctypes.c_int
+    lib.oracle_rms_scale_f64.argtypes = [i64, i64, dp, f, dp]
+    lib.oracle_rms_scale_f64.restype = ctypes.c_int
+    lib.oracle_rms_from_partials_f64.argtypes = [i64, i64, dp, i64, f, dp]
+    lib.oracle_rms_from_partials_f64.restype = ctypes.c_int
+    lib.oracle_silu.argtypes = [f]
+    lib.oracle_silu.restype = f
+    lib.oracle_bf16_round.argtypes = [f]
+    lib.oracle_bf16_round.restype = f
+    lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_decode.restype = f
+    lib.oracle_e4m3_encode.argtypes = [f]
+    lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+    u8p, fp = ctypes.POINTER(ctypes.c_uint8), ctypes.POINTER(ctypes.c_float)
+    for name in ("oracle_dequant_rows_e4m3", "oracle_dequant_cols_e4m3"):
+        getattr(lib, name).argtypes = [i64, i64, u8p, fp, dp]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.oracle_default_threads.argtypes = []
+    lib.oracle_default_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray, ctype=ctypes.c_double):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    return _load().oracle_default_threads()
+
+
+def _block(name, X, W1, R, gamma, W2, eps, epi, nthreads):
+    lib = _load()
+    X, W1, R, gamma, W2 = (_f64(a) for a in (X, W1, R, gamma, W2))
+    M, K1 = X.shape
+    K1b, D = W1.shape
+    Db, N2 = W2.shape
+    if K1b != K1 or Db != D or R.shape != (M, D) or gamma.shape != (D,):
+        raise ValueError("oracle: inconsistent shapes")
+    ncols = N2 if epi == EPI_IDENTITY else N2 // 2
+    h = np.empty((M, D), np.float64)
+    r = np.empty((M,), np.float64)
+    y = np.empty((M, ncols), np.float64)
+    rc = getattr(lib, name)(M, K1, D, N2, _ptr(X), _ptr(W1), _ptr(R), _ptr(gamma), _ptr(W2), float(eps),
+                            int(epi), _ptr(h), _ptr(r), _ptr(y), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"{name} failed with {rc}")
+    return h, r, y
+
+
+def block_unfused(X, W1, R, gamma, W2, eps, epi, nthreads=0):
+    """h = X W1 + R; r = 1/sqrt(mean(h^2)+eps); y = epi((h * r * gamma) W2).  Returns (h, r, y) in fp64."""
+    return _block("oracle_block_unfused_f64", X, W1, R, gamma, W2, eps, epi, nthreads)
+
+
+def block_fused(X, W1, R, gamma, W2, eps, epi, nthreads=0):
+    """Reparameterised order: y = epi(r * (h (diag(gamma) W2))).  Returns (h, r, y) in fp64."""
+    return _block("oracle_block_fused_f64", X, W1, R, gamma, W2, eps, epi, nthreads)
+
+
+def block_roundpts(X, W1, R, gamma, W2, eps, epi, nthreads=0):
+    """Reparameterised order with bf16 storage roundings of h, diag(gamma) W2 and y (diagnostic)."""
+    return _block("oracle_block_roundpts_f64", X, W1, R, gamma, W2, eps, epi, nthreads)
+
+
+def gemm_residual(X, W1, R=None, nthreads=0):
+    lib = _load()
+    X, W1 = _f64(X), _f64(W1)
+    M, K1 = X.shape
+    D = W1.shape[1]
+    h = np.empty((M, D), np.float64)
+    Rp = None
+    if R is not None:
+        R = _f64(R)
+        Rp = _ptr(R)
+    rc = lib.oracle_gemm_residual_f64(M, K1, D, _ptr(X), _ptr(W1), Rp, _ptr(h), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_gemm_residual_f64 failed with {rc}")
+    return h
+
+
+def rms_scale(h, eps):
+    lib = _load()
+    h = _f64(h)
+    M, D = h.shape
+    r = np.empty((M,), np.float64)
+    if lib.oracle_rms_scale_f64(M, D, _ptr(h), float(eps), _ptr(r)) != 0:
+        raise RuntimeError("oracle_rms_scale_f64 failed")
+    return r
+
+
+def rms_from_partials(part, D, eps):
+    """part [T, M] partial sums of squares -> r [M]."""
+    lib = _load()
+    part = _f64(part)
+    T, M = part.shape
+    r = np.empty((M,), np.float64)
+    if lib.oracle_rms_from_partials_f64(T, M, _ptr(part), int(D), float(eps), _ptr(r)) != 0:
+        raise RuntimeError("oracle_rms_from_partials_f64 failed")
+    return r
+
+
+def silu(x: float) -> float:
+    return _load().oracle_silu(float(x))
+
+
+def bf16_round(x) -> np.ndarray:
+    lib = _load()
+    a = _f64(x)
+    out = np.fromiter((lib.oracle_bf16_round(float(v)) for v in a.ravel()), np.float64, a.size)
+    return out.reshape(a.shape)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    out = np.fromiter((lib.oracle_e4m3_decode(int(v)) for v in c.ravel()), np.float64, c.size)
+    return out.reshape(c.shape)
+
+
+def e4m3_encode(x) -> np.ndarray:
+    lib = _load()
+    a = _f64(x)
+    out = np.fromiter((lib.oracle_e4m3_encode(float(v)) for v in a.ravel()), np.uint8, a.size)
+    return out.reshape(a.shape)
+
+
+def dequant_rows_e4m3(q, s) -> np.ndarray:
+    """Activations: out[i, k] = decode(q[i, k]) * s[i]."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    rows, cols = q.shape
+    out = np.empty((rows, cols), np.float64)
+    if lib.oracle_dequant_rows_e4m3(rows, cols, _ptr(q, ctypes.c_uint8), _ptr(s, ctypes.c_float), _ptr(out)) != 0:
+        raise RuntimeError("oracle_dequant_rows_e4m3 failed")
+    return out
+
+
+def dequant_cols_e4m3(q, s) -> np.ndarray:
+    """Weights: out[k, n] = decode(q[k, n]) * s[n]."""
+    lib = _load()
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    rows, cols = q.shape
+    out = np.empty((rows, cols), np.float64)
+    if lib.oracle_dequant_cols_e4m3(rows, cols, _ptr(q, ctypes.c_uint8), _ptr(s, ctypes.c_float), _ptr(out)) != 0:
+        raise RuntimeError("oracle_dequant_cols_e4m3 failed")
+    return out

@@ -1,0 +1,344 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for the GEMM -> residual -> RMSNorm -> GEMM block.
+ *
+ * TEST INFRASTRUCTURE ONLY (see oracle.h).  Written to be checked by eye, not to be fast: the products are
+ * textbook triple loops (the k loop sits outside the column loop so the inner loop runs along a row, which
+ * leaves every output's sum in plain k order), rows are shared between threads, and nothing is blocked,
+ * fused or reordered beyond that.
+ *
+ * Source of the method: the CODA write-up ("CODA: new research optimizes Transformer training with
+ * GEMM-epilogue programming", KuCoin news flash; the same article on itsolotime.com), section "CODA: the
+ * treasure hidden in the epilogue": a GEMM, a residual add, RMS normalisation and a second GEMM; the per-row
+ * RMS factor is a scalar per row, so it commutes with the second GEMM and can be applied after it, with a
+ * light reduction merging per-tile partial RMS values; the same section says SwiGLU admits a similar
+ * rewrite.
+ */
+#define _GNU_SOURCE
+#include "oracle.h"
+
+#include <fenv.h>
+#include <math.h>
+#include <pthread.h>
+#include <sched.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+int oracle_default_threads(void) {
+  cpu_set_t set;
+  if (sched_getaffinity(0, sizeof(set), &set) == 0) {
+    int n = CPU_COUNT(&set);
+    if (n > 0) return n;
+  }
+  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  return n > 0 ? (int)n : 1;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* scalar helpers                                                                                   */
+
+double oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+/* Round x to the grid of a binary format with `sig` significant bits whose smallest normal exponent is
+ * emin (the weight of the leading bit of the smallest normal number is 2^emin).  Ties go to even because
+ * nearbyint follows the default rounding mode, round-to-nearest-even. */
+static double round_to_grid(double x, int sig, int emin) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  frexp(x, &e);          /* |x| = m * 2^e with 0.5 <= m < 1: the leading bit has weight 2^(e-1) */
+  int lead = e - 1;
+  if (lead < emin) lead = emin; /* subnormal range: fixed spacing */
+  double ulp = ldexp(1.0, lead - (sig - 1));
+  return nearbyint(x / ulp) * ulp;
+}
+
+double oracle_bf16_round(double x) {
+  if (isnan(x)) return x;
+  /* bfloat16: 8 significant bits, same exponent range as fp32 (smallest normal 2^-126). */
+  double r = round_to_grid(x, 8, -126);
+  const double bf16_max = 3.38953138925153547590470800371487866880e+38; /* (2 - 2^-7) * 2^127 */
+  if (fabs(r) > bf16_max) return copysign(INFINITY, x);
+  return r;
+}
+
+double oracle_e4m3_decode(uint8_t code) {
+  int sign = code >> 7;
+  int exp_bits = (code >> 3) & 0xF;
+  int mant = code & 0x7;
+  double v;
+  if (exp_bits == 0xF && mant == 0x7) return NAN; /* the only NaN pattern; e4m3fn has no infinities */
+  if (exp_bits == 0)
+    v = ldexp((double)mant, -9); /* subnormal: mant/8 * 2^(1-7) */
+  else
+    v = ldexp(1.0 + mant / 8.0, exp_bits - 7);
+  return sign ? -v : v;
+}
+
+uint8_t oracle_e4m3_encode(double x) {
+  if (isnan(x)) return 0x7F;
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs(x);
+  if (a > 448.0) a = 448.0;             /* saturate */
+  double r = round_to_grid(a, 4, -6);   /* 4 significant bits, smallest normal 2^-6 */
+  if (r > 448.0) r = 448.0;
+  if (r == 0.0) return sign;
+  int e;
+  frexp(r, &e);
+  int lead = e - 1;
+  if (lead < -6) { /* subnormal: value = mant * 2^-9 */
+    int mant = (int)nearbyint(r / ldexp(1.0, -9));
+    return sign | (uint8_t)mant;
+  }
+  int mant = (int)nearbyint((r / ldexp(1.0, lead) - 1.0) * 8.0);
+  return sign | (uint8_t)(((lead + 7) << 3) | mant);
+}
+
+int oracle_dequant_rows_e4m3(int64_t rows, int64_t cols, const uint8_t* q, const float* s, double* out) {
+  if (rows < 0 || cols < 0 || !q || !s || !out) return -1;
+  for (int64_t i = 0; i < rows; ++i)
+    for (int64_t k = 0; k < cols; ++k) out[i * cols + k] = oracle_e4m3_decode(q[i * cols + k]) * (double)s[i];
+  return 0;
+}
+
+int oracle_dequant_cols_e4m3(int64_t rows, int64_t cols, const uint8_t* q, const float* s, double* out) {
+  if (rows < 0 || cols < 0 || !q || !s || !out) return -1;
+  for (int64_t k = 0; k < rows; ++k)
+    for (int64_t n = 0; n < cols; ++n) out[k * cols + n] = oracle_e4m3_decode(q[k * cols + n]) * (double)s[n];
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* row-parallel driver                                                                              */
+
+typedef void (*row_fn)(void* ctx, int64_t row, double* scratch);
+
+typedef struct {
+  row_fn fn;
+  void* ctx;
+  int64_t row_begin, row_end;
+  size_t scratch_doubles;
+  int failed;
+} row_job;
+
+static void* row_worker(void* p) {
+  row_job* job = (row_job*)p;
+  double* scratch = NULL;
+  if (job->scratch_doubles) {
+    scratch = (double*)malloc(job->scratch_doubles * sizeof(double));
+    if (!scratch) { job->failed = 1; return NULL; }
+  }
+  for (int64_t i = job->row_begin; i < job->row_end; ++i) job->fn(job->ctx, i, scratch);
+  free(scratch);
+  return NULL;
+}
+
+/* Runs fn(ctx, i, scratch) for every row i in [0, M), spread over contiguous row ranges. */
+static int for_each_row(int64_t M, int nthreads, size_t scratch_doubles, row_fn fn, void* ctx) {
+  if (nthreads <= 0) nthreads = oracle_default_threads();
+  if (nthreads > M) nthreads = M > 0 ? (int)M : 1;
+  row_job* jobs = (row_job*)calloc((size_t)nthreads, sizeof(row_job));
+  pthread_t* tids = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+  if (!jobs || !tids) { free(jobs); free(tids); return -2; }
+  int64_t per = (M + nthreads - 1) / nthreads;
+  int started = 0, failed = 0;
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t].fn = fn;
+    jobs[t].ctx = ctx;
+    jobs[t].row_begin = t * per < M ? t * per : M;
+    jobs[t].row_end = (t + 1) * per < M ? (t + 1) * per : M;
+    jobs[t].scratch_doubles = scratch_doubles;
+    if (pthread_create(&tids[t], NULL, row_worker, &jobs[t]) != 0) { /* run it here instead */
+      row_worker(&jobs[t]);
+      tids[t] = 0;
+      continue;
+    }
+    ++started;
+  }
+  for (int t = 0; t < nthreads; ++t) {
+    if (tids[t]) pthread_join(tids[t], NULL);
+    failed |= jobs[t].failed;
+  }
+  (void)started;
+  free(jobs);
+  free(tids);
+  return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* first product plus residual: h_ij = sum_k X_ik W1_kj + R_ij                                     */
+
+typedef struct {
+  int64_t K1, D;
+  const double *X, *W1, *R;
+  double* h;
+} gemm_res_ctx;
+
+static void gemm_res_row(void* p, int64_t i, double* scratch) {
+  gemm_res_ctx* c = (gemm_res_ctx*)p;
+  (void)scratch;
+  double* hi = c->h + i * c->D;
+  for (int64_t j = 0; j < c->D; ++j) hi[j] = 0.0;
+  for (int64_t k = 0; k < c->K1; ++k) {
+    double x = c->X[i * c->K1 + k];
+    const double* w = c->W1 + k * c->D;
+    for (int64_t j = 0; j < c->D; ++j) hi[j] += x * w[j];
+  }
+  if (c->R)
+    for (int64_t j = 0; j < c->D; ++j) hi[j] += c->R[i * c->D + j];
+}
+
+int oracle_gemm_residual_f64(int64_t M, int64_t K1, int64_t D, const double* X, const double* W1,
+                             const double* R, double* out_h, int nthreads) {
+  if (M < 0 || K1 < 0 || D < 0 || !X || !W1 || !out_h) return -1;
+  gemm_res_ctx c = {K1, D, X, W1, R, out_h};
+  return for_each_row(M, nthreads, 0, gemm_res_row, &c);
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* RMS row scale                                                                                    */
+
+static double rms_scale_of_row(const double* h, int64_t D, double eps) {
+  double ss = 0.0;
+  for (int64_t j = 0; j < D; ++j) ss += h[j] * h[j];
+  return 1.0 / sqrt(ss / (double)D + eps);
+}
+
+int oracle_rms_scale_f64(int64_t M, int64_t D, const double* h, double eps, double* out_r) {
+  if (M < 0 || D <= 0 || !h || !out_r) return -1;
+  for (int64_t i = 0; i < M; ++i) out_r[i] = rms_scale_of_row(h + i * D, D, eps);
+  return 0;
+}
+
+int oracle_rms_from_partials_f64(int64_t T, int64_t M, const double* part, int64_t D, double eps,
+                                 double* out_r) {
+  if (T <= 0 || M < 0 || D <= 0 || !part || !out_r) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    double ss = 0.0;
+    for (int64_t t = 0; t < T; ++t) ss += part[t * M + i];
+    out_r[i] = 1.0 / sqrt(ss / (double)D + eps);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------------------------------ */
+/* the whole block                                                                                  */
+
+enum { FORM_UNFUSED = 0, FORM_FUSED = 1, FORM_ROUNDPTS = 2 };
+
+typedef struct {
+  int form;
+  int64_t K1, D, N2;
+  const double *X, *W1, *R, *gamma, *W2;
+  const double* W2g; /* diag(gamma) W2 (fused forms), bf16-rounded for the round-points form */
+  double eps;
+  int epi;
+  double *h, *r, *y;
+} block_ctx;
+
+/* scratch per thread: h row (D), second operand row (D), z row (N2) */
+static void block_row(void* p, int64_t i, double* scratch) {
+  block_ctx* c = (block_ctx*)p;
+  const int64_t K1 = c->K1, D = c->D, N2 = c->N2;
+  double* hrow = scratch;
+  double* arow = scratch + D;
+  double* z = scratch + 2 * D;
+
+  /* h = X W1 + R */
+  for (int64_t j = 0; j < D; ++j) hrow[j] = 0.0;
+  for (int64_t k = 0; k < K1; ++k) {
+    double x = c->X[i * K1 + k];
+    const double* w = c->W1 + k * D;
+    for (int64_t j = 0; j < D; ++j) hrow[j] += x * w[j];
+  }
+  for (int64_t j = 0; j < D; ++j) hrow[j] += c->R[i * D + j];
+
+  /* r = 1 / sqrt(mean(h^2) + eps), from the unrounded h in every form */
+  double r = rms_scale_of_row(hrow, D, c->eps);
+
+  const double* w2;
+  if (c->form == FORM_UNFUSED) {
+    /* normalise first: n_j = h_j * r * gamma_j, then z = n W2 */
+    for (int64_t j = 0; j < D; ++j) arow[j] = hrow[j] * r * c->gamma[j];
+    w2 = c->W2;
+  } else {
+    /* reparameterised: the product runs on h itself (bf16-rounded in the round-points form) against
+     * W2' = diag(gamma) W2, and r scales the product's row afterwards */
+    for (int64_t j = 0; j < D; ++j) arow[j] = c->form == FORM_ROUNDPTS ? oracle_bf16_round(hrow[j]) : hrow[j];
+    w2 = c->W2g;
+  }
+  for (int64_t n = 0; n < N2; ++n) z[n] = 0.0;
+  for (int64_t j = 0; j < D; ++j) {
+    double a = arow[j];
+    const double* w = w2 + j * N2;
+    for (int64_t n = 0; n < N2; ++n) z[n] += a * w[n];
+  }
+  if (c->form != FORM_UNFUSED)
+    for (int64_t n = 0; n < N2; ++n) z[n] *= r;
+
+  /* epilogue */
+  if (c->epi == ORACLE_EPI_IDENTITY) {
+    for (int64_t n = 0; n < N2; ++n) {
+      double v = z[n];
+      c->y[i * N2 + n] = c->form == FORM_ROUNDPTS ? oracle_bf16_round(v) : v;
+    }
+  } else {
+    const int64_t half = N2 / 2;
+    for (int64_t n = 0; n < half; ++n) {
+      double v = oracle_silu(z[n]) * z[half + n]; /* gate in the first half, up in the second */
+      c->y[i * half + n] = c->form == FORM_ROUNDPTS ? oracle_bf16_round(v) : v;
+    }
+  }
+
+  if (c->h)
+    for (int64_t j = 0; j < D; ++j) c->h[i * D + j] = hrow[j];
+  if (c->r) c->r[i] = r;
+}
+
+static int run_block(int form, int64_t M, int64_t K1, int64_t D, int64_t N2, const double* X,
+                     const double* W1, const double* R, const double* gamma, const double* W2, double eps,
+                     int epi, double* out_h, double* out_r, double* out_y, int nthreads) {
+  if (M < 0 || K1 <= 0 || D <= 0 || N2 <= 0) return -1;
+  if (!X || !W1 || !R || !gamma || !W2 || !out_y) return -1;
+  if (epi != ORACLE_EPI_IDENTITY && epi != ORACLE_EPI_SWIGLU) return -1;
+  if (epi == ORACLE_EPI_SWIGLU && (N2 % 2) != 0) return -1;
+  if (!(eps >= 0.0)) return -1;
+
+  double* W2g = NULL;
+  if (form != FORM_UNFUSED) {
+    /* W2'_jn = gamma_j * W2_jn.  The round-points form rounds the product to fp32 and then to bf16,
+     * the two roundings a bf16 kernel makes when it scales a bf16 weight by an fp32 gamma. */
+    W2g = (double*)malloc((size_t)D * (size_t)N2 * sizeof(double));
+    if (!W2g) return -2;
+    for (int64_t j = 0; j < D; ++j)
+      for (int64_t n = 0; n < N2; ++n) {
+        double v = gamma[j] * W2[j * N2 + n];
+        if (form == FORM_ROUNDPTS) v = oracle_bf16_round((double)(float)v);
+        W2g[j * N2 + n] = v;
+      }
+  }
+  block_ctx c = {form, K1, D, N2, X, W1, R, gamma, W2, W2g, eps, epi, out_h, out_r, out_y};
+  int rc = for_each_row(M, nthreads, (size_t)(2 * D + N2), block_row, &c);
+  free(W2g);
+  return rc;
+}
+
+int oracle_block_unfused_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const double* X,
+                             const double* W1, const double* R, const double* gamma, const double* W2,
+                             double eps, int epi, double* out_h, double* out_r, double* out_y,
+                             int nthreads) {
+  return run_block(FORM_UNFUSED, M, K1, D, N2, X, W1, R, gamma, W2, eps, epi, out_h, out_r, out_y, nthreads);
+}
+
+int oracle_block_fused_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const double* X,
+                           const double* W1, const double* R, const double* gamma, const double* W2,
+                           double eps, int epi, double* out_h, double* out_r, double* out_y,
+                           int nthreads) {
+  return run_block(FORM_FUSED, M, K1, D, N2, X, W1, R, gamma, W2, eps, epi, out_h, out_r, out_y, nthreads);
+}
+
+int oracle_block_roundpts_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const double* X,
+                              const double* W1, const double* R, const double* gamma, const double* W2,
+                              double eps, int epi, double* out_h, double* out_r, double* out_y,
+                              int nthreads) {
+  return run_block(FORM_ROUNDPTS, M, K1, D, N2, X, W1, R, gamma, W2, eps, epi, out_h, out_r, out_y, nthreads);
+}

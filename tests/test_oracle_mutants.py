@@ -1,0 +1,45 @@
+"""Planted-mistake check of the oracle's pins (CPU only).
+
+Each case copies the oracle's C source, plants one plausible mistake (eps outside the square root, a
+dropped residual, a transposed operand, gate and up swapped, r applied twice, gamma dropped, a wrong
+mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent in the fp8
+decoder), rebuilds it in a temporary directory and runs the pin tests against it.  Every mutant must fail
+at least one pin; the unmodified oracle is never touched.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = [
+    ("eps_outside_sqrt", "return 1.0 / sqrt(ss / (double)D + eps);", "return 1.0 / (sqrt(ss / (double)D) + eps);"),
+    ("dropped_residual", "for (int64_t j = 0; j < D; ++j) hrow[j] += c->R[i * D + j];", ";"),
+    ("transposed_w1", "const double* w = c->W1 + k * D;\n    for (int64_t j = 0; j < D; ++j) hrow[j] += x * w[j];",
+     "const double* w = c->W1 + k;\n    for (int64_t j = 0; j < D; ++j) hrow[j] += x * w[j * K1];"),
+    ("gate_up_swapped", "double v = oracle_silu(z[n]) * z[half + n];", "double v = oracle_silu(z[half + n]) * z[n];"),
+    ("row_scale_twice", "z[n] *= r;", "z[n] *= r * r;"),
+    ("gamma_dropped", "arow[j] = hrow[j] * r * c->gamma[j];", "arow[j] = hrow[j] * r;"),
+    ("mean_denominator", "return 1.0 / sqrt(ss / (double)D + eps);", "return 1.0 / sqrt(ss / (double)(D - 1) + eps);"),
+    ("gamma_wrong_index", "double v = gamma[j] * W2[j * N2 + n];", "double v = gamma[n % D] * W2[j * N2 + n];"),
+    ("silu_sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
+    ("e4m3_subnormal", "v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
+]
+
+
+@pytest.mark.parametrize("name,before,after", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(tmp_path, name, before, after):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert before in src, f"mutation site for {name} no longer exists"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tmp_path / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py"))
+    (tmp_path / "oracle" / "oracle.c").write_text(src.replace(before, after, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-q", "-x",
+                        "-p", "no:cacheprovider"], cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, f"mutant {name} was not caught:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout
