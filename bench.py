@@ -1,0 +1,213 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM -> residual -> RMSNorm -> GEMM block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one coda_block_fwd call (all three kernels: GEMM1 + residual + partial sums of squares, the
+row-scale reduction, GEMM2 with the gamma fold, row scale and SwiGLU) on inputs already resident in HBM.
+W untimed steps, then K timed steps between two device synchronisations.  Prints ONE JSON line.
+
+Besides the headline the line carries:
+  roofline      the dominant kernel (GEMM2) timed alone with HIP events on the stream it runs on, its
+                algorithmic flops (2 M D N2) per launch divided by the average launch time, against the
+                published bf16 dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3 counter
+                summary if it was taken on the current kernel sources, else null
+  cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the same workload (rows are
+                independent), scaled to TFLOP/s
+  unfused       the three-kernel baseline timed the same way, and the algorithmic HBM bytes both paths move
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+HBM_PEAK_GBS = 8000.0
+METRIC = "fused block TFLOP/s + % bf16 MFMA peak at 1B shape M=8192; HBM bytes saved"
+KERNEL_SOURCES = ["gemm_epilogue_fusion_amd/csrc/gemm_core.h", "gemm_epilogue_fusion_amd/csrc/kernels.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_rowscale_1b_attn_out_mlp_in.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl, fused: bool) -> int:
+    """Compulsory HBM bytes of one block: every input read once, every output written once, plus the
+    intermediates each path writes and reads back (part/r for the fused path; T and n for the unfused)."""
+    M, K1, D, N2, ny = wl.M, wl.K1, wl.D, wl.N2, wl.n_out
+    b = 2 * (M * K1 + K1 * D + M * D + D * N2) + 4 * D   # X, W1, R, W2, gamma
+    b += 2 * M * D + 2 * M * ny                          # h, y
+    if fused:
+        T = D // 256
+        b += 2 * 4 * T * M + 2 * 4 * M                    # part written + read, r written + read
+        b += 2 * M * D                                    # GEMM2 reads h back
+    else:
+        b += 2 * 2 * M * D                                # T written + read
+        b += 2 * 2 * M * D + 4 * M                        # n written + read, r written
+    return b
+
+
+def time_loop(fn, n: int, torch) -> float:
+    """Average ms per call of fn over n back-to-back calls, with HIP events on the current stream."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(n):
+        fn()
+    end.record()
+    end.synchronize()
+    return start.elapsed_time(end) / n
+
+
+def cpu_baseline(wl, inp, target_s: float = 15.0) -> dict:
+    import numpy as np
+    import torch
+
+    import oracle
+
+    f = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    W1, g, W2 = f(inp.W1), f(inp.gamma), f(inp.W2)
+    per_row = 2 * (wl.K1 * wl.D + wl.D * wl.N2)
+    rows = 64
+    t0 = time.perf_counter()
+    oracle.block_fused(f(inp.X[:rows]), W1, f(inp.R[:rows]), g, W2, wl.eps, wl.epi)
+    dt = time.perf_counter() - t0
+    rows2 = int(min(wl.M, max(rows, rows * target_s / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.block_fused(f(inp.X[:rows2]), W1, f(inp.R[:rows2]), g, W2, wl.eps, wl.epi)
+    dt2 = time.perf_counter() - t0
+    return {"value": round(per_row * rows2 / dt2 / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.default_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle (fused order) on rows 0..{rows2 - 1} of the {wl.M}-row workload, {dt2:.1f} s; "
+                      f"rows are independent so the rate scales to the full block"}
+
+
+def traffic_record(src_hash: str):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="1b_attn_out_mlp_in")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this block runs on one GPU; multi-GPU runs are not part of it "
+              "(the forward pass shards along rows with no communication).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from gemm_epilogue_fusion_amd import binding as cb
+    from gemm_epilogue_fusion_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        return 2
+    cb.load()
+    wl = WORKLOADS[args.workload]
+    if wl.fp8:
+        print("bench.py: fp8 workload is benchmarked with its own entry point", file=sys.stderr)
+        return 2
+    inp = make_inputs(wl)
+    dev = torch.device("cuda:0")
+    X, W1, R, g, W2 = (t.to(dev) for t in (inp.X, inp.W1, inp.R, inp.gamma, inp.W2))
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev)
+    ws_u = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=1, device=dev)
+
+    def step():
+        cb.coda_block_fwd(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws)
+
+    def step_unfused():
+        cb.coda_block_unfused(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws_u)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    tflops = wl.flops / (ms * 1e-3) / 1e12
+    if args.only_fused:
+        print(json.dumps({"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": ms}))
+        return 0
+
+    # per-step kernels timed alone with HIP events (same stream as the launches: torch's current stream)
+    T = wl.D // 256
+    part = torch.empty(T, wl.M, dtype=torch.float32, device=dev)
+    r = torch.empty(wl.M, dtype=torch.float32, device=dev)
+    n_ev = max(20, args.steps // 2)
+    k1 = lambda: cb.coda_gemm1_residual_partial_rms(X, W1, R, h, part)
+    k2 = lambda: cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r)
+    k3 = lambda: cb.coda_gemm2_rowscale(h, W2, g, r, wl.epi, y)
+    for fn in (k1, k2, k3):
+        fn()
+    torch.cuda.synchronize()
+    k1_ms, k2_ms, k3_ms = (time_loop(fn, n_ev, torch) for fn in (k1, k2, k3))
+    for _ in range(args.warmup):
+        step_unfused()
+    unf_ms = time_loop(step_unfused, n_ev, torch)
+    fused_ev_ms = time_loop(step, n_ev, torch)
+
+    k3_flops = 2 * wl.M * wl.D * wl.N2
+    k3_tflops = k3_flops / (k3_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = traffic_record(src_hash)
+    roofline = {"bound": "mfma", "achieved": round(k3_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(k3_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic["bytes_per_launch"] if traffic else None,
+                "kernel": "gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU, FOLD_GAMMA> (GEMM2)",
+                "kernel_ms": round(k3_ms, 4), "algorithmic_flops_per_launch": k3_flops}
+
+    fb, ub = algorithmic_bytes(wl, True), algorithmic_bytes(wl, False)
+    line = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussian inputs of the workload's shapes)",
+        "config": {"workload": wl.name, "M": wl.M, "K1": wl.K1, "D": wl.D, "N2": wl.N2,
+                   "epilogue": "swiglu" if wl.epi else "identity", "eps": wl.eps},
+        "pct_bf16_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
+        "roofline": roofline,
+        "kernels_ms": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
+                       "gemm2_rowscale": round(k3_ms, 4), "fused_block_events": round(fused_ev_ms, 4)},
+        "unfused": {"ms_per_step": round(unf_ms, 4), "tflops": round(wl.flops / (unf_ms * 1e-3) / 1e12, 2),
+                    "speedup_fused_vs_unfused": round(unf_ms / fused_ev_ms, 4)},
+        "hbm_bytes": {"fused_algorithmic": fb, "unfused_algorithmic": ub, "saved_algorithmic": ub - fb},
+        "kernel_source_hash": src_hash,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(line))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

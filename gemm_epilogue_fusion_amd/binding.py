@@ -1,0 +1,172 @@
+"""ctypes binding of libcoda.so (include/coda.h) for torch tensors.
+
+Argument marshalling only: every step of the block runs in the library's HIP kernels.  Each function has the
+name of the C entry point it calls, takes device tensors (torch is used for device memory and streams),
+checks dtype / shape / device / contiguity on the host, passes raw pointers, sizes and the current HIP
+stream, and raises CodaError with the library's own message on a non-zero status.  There is no fallback: if
+the library is missing or fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcoda.so")
+
+EPI_IDENTITY = 0
+EPI_SWIGLU = 1
+
+STATUS = {0: "CODA_OK", 1: "CODA_ERR_INVALID_ARG", 2: "CODA_ERR_UNSUPPORTED", 3: "CODA_ERR_ALIAS",
+          4: "CODA_ERR_WORKSPACE", 5: "CODA_ERR_HIP", 6: "CODA_ERR_INTERNAL"}
+
+# every symbol include/coda.h declares
+EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_workspace_bytes",
+           "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused",
+           "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale")
+
+
+class CodaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libcoda.so (built by gemm_epilogue_fusion_amd.build); raises if it is absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m gemm_epilogue_fusion_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    lib.coda_abi_version.argtypes, lib.coda_abi_version.restype = [], i32
+    lib.coda_status_string.argtypes, lib.coda_status_string.restype = [i32], ctypes.c_char_p
+    lib.coda_last_error.argtypes, lib.coda_last_error.restype = [], ctypes.c_char_p
+    lib.coda_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32, i32]
+    lib.coda_workspace_bytes.restype = sz
+    lib.coda_workspace_r_offset.argtypes, lib.coda_workspace_r_offset.restype = [i64, i64], sz
+    block = [vp, vp, vp, vp, vp, f32, i32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+    for name in ("coda_block_fwd", "coda_block_unfused"):
+        getattr(lib, name).argtypes = block
+        getattr(lib, name).restype = i32
+    lib.coda_gemm1_residual_partial_rms.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.coda_gemm1_residual_partial_rms.restype = i32
+    lib.coda_partial_rms_reduce.argtypes = [vp, i64, i64, i64, f32, vp, vp]
+    lib.coda_partial_rms_reduce.restype = i32
+    lib.coda_gemm2_rowscale.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, i64, vp]
+    lib.coda_gemm2_rowscale.restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        detail = load().coda_last_error().decode(errors="replace")
+        raise CodaError(status, where, detail)
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (HIP) tensor, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def coda_abi_version() -> int:
+    return load().coda_abi_version()
+
+
+def coda_workspace_bytes(M: int, K1: int, D: int, N2: int, epi_kind: int, fp8: int = 0, unfused: int = 0) -> int:
+    return load().coda_workspace_bytes(M, K1, D, N2, epi_kind, fp8, unfused)
+
+
+def coda_workspace_r_offset(M: int, D: int) -> int:
+    return load().coda_workspace_r_offset(M, D)
+
+
+def alloc_workspace(M: int, K1: int, D: int, N2: int, epi_kind: int, unfused: int = 0, device="cuda"):
+    n = coda_workspace_bytes(M, K1, D, N2, epi_kind, 0, unfused)
+    if n == 0:
+        raise ValueError("no workspace size for these dimensions")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _block(name: str, X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspace, stream):
+    M, K1 = X.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    ny = N2 if epi_kind == EPI_IDENTITY else N2 // 2
+    args = (_dev(X, "X", torch.bfloat16, (M, K1)), _dev(W1, "W1", torch.bfloat16, (K1, D)),
+            _dev(R, "R", torch.bfloat16, (M, D)), _dev(gamma, "gamma", torch.float32, (D,)),
+            _dev(W2, "W2", torch.bfloat16, (D, N2)))
+    h = _dev(out_h, "out_h", torch.bfloat16, (M, D))
+    y = _dev(out_y, "out_y", torch.bfloat16, (M, ny))
+    ws = _dev(workspace, "workspace", torch.uint8)
+    st = getattr(load(), name)(*args, float(eps), int(epi_kind), h, y, M, K1, D, N2, ws, workspace.numel(),
+                               _stream(stream))
+    _check(st, name)
+
+
+def coda_block_fwd(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y, workspace, stream=None):
+    """Fused block: out_h = bf16(X W1 + R); out_y = bf16(epi(r * (h diag(gamma) W2)))."""
+    _block("coda_block_fwd", X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspace, stream)
+
+
+def coda_block_unfused(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y, workspace, stream=None):
+    """Unfused three-kernel baseline with the same outputs."""
+    _block("coda_block_unfused", X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspace, stream)
+
+
+def coda_gemm1_residual_partial_rms(X, W1, R, out_h, part, stream=None):
+    M, K1 = X.shape
+    D = W1.shape[1]
+    st = load().coda_gemm1_residual_partial_rms(
+        _dev(X, "X", torch.bfloat16, (M, K1)), _dev(W1, "W1", torch.bfloat16, (K1, D)),
+        _dev(R, "R", torch.bfloat16, (M, D)), _dev(out_h, "out_h", torch.bfloat16, (M, D)),
+        _dev(part, "part", torch.float32, (D // 256, M)), M, K1, D, _stream(stream))
+    _check(st, "coda_gemm1_residual_partial_rms")
+
+
+def coda_partial_rms_reduce(part, D: int, eps: float, r, stream=None):
+    T, M = part.shape
+    st = load().coda_partial_rms_reduce(_dev(part, "part", torch.float32, (T, M)), T, M, D, float(eps),
+                                        _dev(r, "r", torch.float32, (M,)), _stream(stream))
+    _check(st, "coda_partial_rms_reduce")
+
+
+def coda_gemm2_rowscale(h, W2, gamma, r, epi_kind: int, out_y, stream=None):
+    M, D = h.shape
+    N2 = W2.shape[1]
+    ny = N2 if epi_kind == EPI_IDENTITY else N2 // 2
+    st = load().coda_gemm2_rowscale(
+        _dev(h, "h", torch.bfloat16, (M, D)), _dev(W2, "W2", torch.bfloat16, (D, N2)),
+        _dev(gamma, "gamma", torch.float32, (D,)), _dev(r, "r", torch.float32, (M,)), int(epi_kind),
+        _dev(out_y, "out_y", torch.bfloat16, (M, ny)), M, D, N2, _stream(stream))
+    _check(st, "coda_gemm2_rowscale")
+
+
+def workspace_r(workspace: torch.Tensor, M: int, D: int) -> torch.Tensor:
+    """View of r [M] fp32 inside a workspace after coda_block_fwd / coda_block_unfused."""
+    off = coda_workspace_r_offset(M, D)
+    return workspace[off: off + 4 * M].view(torch.float32)

@@ -1,0 +1,298 @@
+// api.hip -- the C ABI declared in include/coda.h: argument validation, workspace layout, error reporting
+// and the launch sequences of the fused block and of the unfused baseline.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "coda.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return CODA_OK;
+}
+
+int hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(CODA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every row index and per-matrix element count in range
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Range {
+  const char* name;
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const char* name, const void* p, size_t bytes) {
+  return Range{name, (uintptr_t)p, (uintptr_t)p + bytes};
+}
+
+bool overlap(const Range& a, const Range& b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(CODA_ERR_INVALID_ARG, "%s is NULL", name);
+  if ((uintptr_t)p & 15) return fail(CODA_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return CODA_OK;
+}
+
+// Shape rules of the GEMM tiling: row tiles are masked, column tiles and the K step are not.
+int check_dims(int64_t M, int64_t K1, int64_t D, int64_t N2) {
+  if (M < 1 || K1 < 1 || D < 1 || N2 < 1)
+    return fail(CODA_ERR_INVALID_ARG, "dimensions must be >= 1 (M=%lld K1=%lld D=%lld N2=%lld)", (long long)M,
+                (long long)K1, (long long)D, (long long)N2);
+  if (M > kMaxDim || K1 > kMaxDim || D > kMaxDim || N2 > kMaxDim || M * K1 > kMaxDim * 2 ||
+      M * D > kMaxDim * 2 || M * N2 > kMaxDim * 2 || D * N2 > kMaxDim * 2 || K1 * D > kMaxDim * 2)
+    return fail(CODA_ERR_UNSUPPORTED, "dimensions too large");
+  if (K1 % 64) return fail(CODA_ERR_UNSUPPORTED, "K1=%lld is not a multiple of 64", (long long)K1);
+  if (D % 256) return fail(CODA_ERR_UNSUPPORTED, "D=%lld is not a multiple of 256", (long long)D);
+  if (N2 % 256) return fail(CODA_ERR_UNSUPPORTED, "N2=%lld is not a multiple of 256", (long long)N2);
+  return CODA_OK;
+}
+
+int check_epi_eps(int epi, float eps) {
+  if (epi != CODA_EPI_IDENTITY && epi != CODA_EPI_SWIGLU) return fail(CODA_ERR_INVALID_ARG, "bad epi_kind %d", epi);
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(CODA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return CODA_OK;
+}
+
+// Outputs may not overlap inputs or each other; out_h == R (same start and size) is the one allowed alias.
+int check_alias(const Range* in, int nin, const Range* out, int nout, const void* allowed_out,
+                const void* allowed_in) {
+  for (int o = 0; o < nout; ++o) {
+    for (int i = 0; i < nin; ++i) {
+      if (!overlap(out[o], in[i])) continue;
+      if (out[o].lo == (uintptr_t)allowed_out && in[i].lo == (uintptr_t)allowed_in && out[o].lo == in[i].lo &&
+          out[o].hi == in[i].hi)
+        continue;
+      return fail(CODA_ERR_ALIAS, "%s overlaps %s", out[o].name, in[i].name);
+    }
+    for (int p = o + 1; p < nout; ++p)
+      if (overlap(out[o], out[p])) return fail(CODA_ERR_ALIAS, "%s overlaps %s", out[o].name, out[p].name);
+  }
+  return CODA_OK;
+}
+
+struct Workspace {
+  float* part;
+  float* r;
+  uint16_t* t;  // unfused: T = X W1
+  uint16_t* n;  // unfused: normalised rows
+};
+
+size_t ws_part_bytes(int64_t M, int64_t D) { return align256((size_t)(D / 256) * (size_t)M * 4); }
+size_t ws_r_bytes(int64_t M) { return align256((size_t)M * 4); }
+size_t ws_mat_bytes(int64_t M, int64_t D) { return align256((size_t)M * (size_t)D * 2); }
+
+size_t ws_bytes(int64_t M, int64_t D, int unfused) {
+  size_t b = ws_part_bytes(M, D) + ws_r_bytes(M);
+  if (unfused) b += 2 * ws_mat_bytes(M, D);
+  return b;
+}
+
+Workspace carve(void* ws, int64_t M, int64_t D, int unfused) {
+  char* p = (char*)ws;
+  Workspace w{};
+  w.part = (float*)p;
+  p += ws_part_bytes(M, D);
+  w.r = (float*)p;
+  p += ws_r_bytes(M);
+  if (unfused) {
+    w.t = (uint16_t*)p;
+    p += ws_mat_bytes(M, D);
+    w.n = (uint16_t*)p;
+  }
+  return w;
+}
+
+// Validation shared by coda_block_fwd and coda_block_unfused.
+int validate_block(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                   int epi, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                   void* workspace, size_t workspace_bytes, int unfused) {
+  int s;
+  if ((s = check_ptr(X, "X")) || (s = check_ptr(W1, "W1")) || (s = check_ptr(R, "R")) ||
+      (s = check_ptr(gamma, "gamma")) || (s = check_ptr(W2, "W2")) || (s = check_ptr(out_h, "out_h")) ||
+      (s = check_ptr(out_y, "out_y")))
+    return s;
+  if ((s = check_dims(M, K1, D, N2))) return s;
+  if ((s = check_epi_eps(epi, eps))) return s;
+  if (unfused && D > 8192) return fail(CODA_ERR_UNSUPPORTED, "unfused path supports D <= 8192");
+  const size_t need = ws_bytes(M, D, unfused);
+  if (!workspace) return fail(CODA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)workspace & 255) return fail(CODA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CODA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const int64_t ny = epi == CODA_EPI_SWIGLU ? N2 / 2 : N2;
+  const Range in[5] = {rng("X", X, (size_t)(M * K1 * 2)), rng("W1", W1, (size_t)(K1 * D * 2)),
+                       rng("R", R, (size_t)(M * D * 2)), rng("gamma", gamma, (size_t)D * 4),
+                       rng("W2", W2, (size_t)(D * N2 * 2))};
+  const Range out[3] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("out_y", out_y, (size_t)(M * ny * 2)),
+                        rng("workspace", workspace, need)};
+  return check_alias(in, 5, out, 3, out_h, R);
+}
+
+}  // namespace
+
+extern "C" {
+
+int coda_abi_version(void) { return CODA_ABI_VERSION; }
+
+const char* coda_status_string(int status) {
+  switch (status) {
+    case CODA_OK: return "CODA_OK";
+    case CODA_ERR_INVALID_ARG: return "CODA_ERR_INVALID_ARG";
+    case CODA_ERR_UNSUPPORTED: return "CODA_ERR_UNSUPPORTED";
+    case CODA_ERR_ALIAS: return "CODA_ERR_ALIAS";
+    case CODA_ERR_WORKSPACE: return "CODA_ERR_WORKSPACE";
+    case CODA_ERR_HIP: return "CODA_ERR_HIP";
+    case CODA_ERR_INTERNAL: return "CODA_ERR_INTERNAL";
+    default: return "CODA_ERR_UNKNOWN";
+  }
+}
+
+const char* coda_last_error(void) { return g_last_error.c_str(); }
+
+size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused) {
+  (void)K1;
+  (void)N2;
+  (void)epi_kind;
+  if (fp8 || M < 1 || D < 256) return 0;
+  return ws_bytes(M, D, unfused);
+}
+
+size_t coda_workspace_r_offset(int64_t M, int64_t D) { return ws_part_bytes(M, D); }
+
+int coda_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                   int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    int s = validate_block(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
+                           workspace_bytes, 0);
+    if (s) return s;
+    hipStream_t st = (hipStream_t)stream;
+    Workspace w = carve(workspace, M, D, 0);
+    if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
+                                                   (uint16_t*)out_h, w.part, (int)M, (int)K1, (int)D, st),
+                       "gemm1_res_prms launch")))
+      return s;
+    if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
+                       "prms_reduce launch")))
+      return s;
+    return hip_check(coda::launch_gemm2_rowscale((const uint16_t*)out_h, (const uint16_t*)W2, gamma, w.r,
+                                                 epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
+                                                 (int)N2, st),
+                     "gemm2_rowscale launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_block_unfused(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
+                       float eps, int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D,
+                       int64_t N2, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    int s = validate_block(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
+                           workspace_bytes, 1);
+    if (s) return s;
+    hipStream_t st = (hipStream_t)stream;
+    Workspace w = carve(workspace, M, D, 1);
+    if ((s = hip_check(coda::launch_gemm_store((const uint16_t*)X, (const uint16_t*)W1, w.t, (int)M, (int)K1,
+                                               (int)D, st),
+                       "gemm_store launch")))
+      return s;
+    if ((s = hip_check(coda::launch_add_rmsnorm(w.t, (const uint16_t*)R, gamma, (uint16_t*)out_h, w.n, w.r,
+                                                (int)M, (int)D, eps, st),
+                       "add_rmsnorm launch")))
+      return s;
+    return hip_check(coda::launch_gemm2_rowscale(w.n, (const uint16_t*)W2, nullptr, nullptr,
+                                                 epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
+                                                 (int)N2, st),
+                     "unfused gemm2 launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_gemm1_residual_partial_rms(const void* X, const void* W1, const void* R, void* out_h, float* part,
+                                    int64_t M, int64_t K1, int64_t D, void* stream) {
+  try {
+    int s;
+    if ((s = check_ptr(X, "X")) || (s = check_ptr(W1, "W1")) || (s = check_ptr(R, "R")) ||
+        (s = check_ptr(out_h, "out_h")) || (s = check_ptr(part, "part")))
+      return s;
+    if ((s = check_dims(M, K1, D, 256))) return s;
+    const Range in[3] = {rng("X", X, (size_t)(M * K1 * 2)), rng("W1", W1, (size_t)(K1 * D * 2)),
+                         rng("R", R, (size_t)(M * D * 2))};
+    const Range out[2] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("part", part, (size_t)(D / 256 * M * 4))};
+    if ((s = check_alias(in, 3, out, 2, out_h, R))) return s;
+    return hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
+                                                 (uint16_t*)out_h, part, (int)M, (int)K1, (int)D,
+                                                 (hipStream_t)stream),
+                     "gemm1_res_prms launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_partial_rms_reduce(const float* part, int64_t T, int64_t M, int64_t D, float eps, float* r,
+                            void* stream) {
+  try {
+    int s;
+    if ((s = check_ptr(part, "part")) || (s = check_ptr(r, "r"))) return s;
+    if (T < 1 || M < 1 || D < 1 || T > kMaxDim || M > kMaxDim || T * M > kMaxDim * 2)
+      return fail(CODA_ERR_INVALID_ARG, "bad T/M/D");
+    if ((s = check_epi_eps(CODA_EPI_IDENTITY, eps))) return s;
+    const Range in[1] = {rng("part", part, (size_t)(T * M * 4))};
+    const Range out[1] = {rng("r", r, (size_t)M * 4)};
+    if ((s = check_alias(in, 1, out, 1, nullptr, nullptr))) return s;
+    return hip_check(coda::launch_prms_reduce(part, (int)T, (int)M, (int)D, eps, r, (hipStream_t)stream),
+                     "prms_reduce launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_gemm2_rowscale(const void* h, const void* W2, const float* gamma, const float* r, int epi_kind,
+                        void* out_y, int64_t M, int64_t D, int64_t N2, void* stream) {
+  try {
+    int s;
+    if ((s = check_ptr(h, "h")) || (s = check_ptr(W2, "W2")) || (s = check_ptr(gamma, "gamma")) ||
+        (s = check_ptr(r, "r")) || (s = check_ptr(out_y, "out_y")))
+      return s;
+    if ((s = check_dims(M, 64, D, N2))) return s;
+    if ((s = check_epi_eps(epi_kind, 0.0f))) return s;
+    const int64_t ny = epi_kind == CODA_EPI_SWIGLU ? N2 / 2 : N2;
+    const Range in[4] = {rng("h", h, (size_t)(M * D * 2)), rng("W2", W2, (size_t)(D * N2 * 2)),
+                         rng("gamma", gamma, (size_t)D * 4), rng("r", r, (size_t)M * 4)};
+    const Range out[1] = {rng("out_y", out_y, (size_t)(M * ny * 2))};
+    if ((s = check_alias(in, 4, out, 1, nullptr, nullptr))) return s;
+    return hip_check(coda::launch_gemm2_rowscale((const uint16_t*)h, (const uint16_t*)W2, gamma, r,
+                                                 epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
+                                                 (int)N2, (hipStream_t)stream),
+                     "gemm2_rowscale launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+}  // extern "C"

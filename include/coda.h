@@ -1,0 +1,127 @@
+/*
+ * coda.h -- C ABI of the MI355X (gfx950) fused GEMM -> residual -> RMSNorm -> GEMM block.
+ *
+ * The method (CODA write-up, "CODA: new research optimizes Transformer training with GEMM-epilogue
+ * programming", section "CODA: the treasure hidden in the epilogue"):
+ *   h  = X W1 + R                      formed in the first GEMM's epilogue while the accumulator tile is
+ *                                      still in registers; h is stored (it is the residual stream and the
+ *                                      activation kept for backward, section "Five blocks and a Lego
+ *                                      language": tiled matrix store)
+ *   part[t][i] = sum_{j in tile t} h_ij^2   per-row, per-column-tile partial sums from the same epilogue
+ *                                      (block reduction primitive: "local RMS")
+ *   r_i = 1 / sqrt(sum_t part[t][i] / D + eps)   a light reduction kernel
+ *   y  = epi(r_i * (h W2'))  with W2' = diag(gamma) W2: the per-row scale commutes with the second GEMM,
+ *                                      so the second mainloop runs on h itself and r is applied in its
+ *                                      epilogue, optionally followed by SwiGLU on a fused gate|up product
+ *                                      (the same section: SwiGLU admits the same rewrite).
+ * No normalised tensor is ever written to or read from HBM.
+ *
+ * Conventions shared by every entry point
+ *   - All matrices are dense and row-major with no padding: X [M,K1], W1 [K1,D] (weights are [in,out]),
+ *     R, out_h [M,D], gamma [D] fp32, W2 [D,N2], out_y [M,N2] (identity) or [M,N2/2] (SwiGLU: columns
+ *     [0,N2/2) of W2 are the gate projection, [N2/2,N2) the up projection, y = silu(gate) * up with
+ *     silu(x) = x / (1 + exp(-x)), r applied to both halves before silu).
+ *   - bf16 tensors are IEEE bfloat16 bit patterns (uint16); fp8 tensors are OCP e4m3fn bytes with fp32
+ *     scales: dequantised value = code * scale, per row for activations (sx [M]) and per output column for
+ *     weights (sw1 [D], sw2 [N2]).
+ *   - Every pointer is a device pointer (HBM of the current HIP device), 16-byte aligned.  The caller owns
+ *     every buffer, including the workspace (size from coda_workspace_bytes).  The library allocates
+ *     nothing, keeps no pointer after returning and has no mutable global state except a thread-local
+ *     error string.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and is asynchronous: buffers
+ *     must stay alive until the stream has passed the call.  Calls on distinct streams with distinct
+ *     workspaces may run concurrently; calls sharing a workspace must be ordered by the caller.
+ *   - Shape rules: M >= 1 (any value; the last row tile is masked); K1 a multiple of 64; D and N2
+ *     multiples of 256 (for SwiGLU N2/2 is then a multiple of 128).  Other shapes return
+ *     CODA_ERR_UNSUPPORTED.  eps must be finite and >= 0.
+ *   - Aliasing: no output may overlap an input or another output, except the exact in-place residual
+ *     update out_h == R (same pointer), which is supported.
+ *   - Errors: arguments are validated synchronously before anything is enqueued; a failed validation
+ *     returns its code and enqueues nothing.  A launch failure returns CODA_ERR_HIP.  Device faults surface
+ *     at the caller's next synchronisation.  No C++ exception crosses this boundary and nothing aborts.
+ *     coda_last_error() gives a human-readable detail of the last failure on the calling thread.
+ */
+#ifndef CODA_H
+#define CODA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CODA_ABI_VERSION 1
+
+typedef enum {
+  CODA_OK = 0,
+  CODA_ERR_INVALID_ARG = 1, /* null or misaligned pointer, bad dimension, bad eps or epilogue kind */
+  CODA_ERR_UNSUPPORTED = 2, /* a shape the kernels do not tile (see shape rules) */
+  CODA_ERR_ALIAS = 3,       /* overlapping input/output buffers (other than out_h == R) */
+  CODA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than coda_workspace_bytes() */
+  CODA_ERR_HIP = 5,         /* the HIP runtime reported an error */
+  CODA_ERR_INTERNAL = 6     /* unexpected internal failure */
+} coda_status;
+
+typedef enum { CODA_EPI_IDENTITY = 0, CODA_EPI_SWIGLU = 1 } coda_epi_kind;
+
+/* Version of this interface (CODA_ABI_VERSION of the built library). */
+int coda_abi_version(void);
+
+/* Static name of a status code. */
+const char* coda_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none).  Valid until the next call. */
+const char* coda_last_error(void);
+
+/* Workspace bytes an entry point needs for these dimensions.
+ *   fp8:     0 for the bf16 entry points, 1 for the *_fp8 ones
+ *   unfused: 0 for coda_block_fwd*, 1 for coda_block_unfused*
+ * Layout (fused): part [D/256][M] fp32 partial sums of squares, then r [M] fp32, each 256-byte aligned;
+ * the unfused path adds its two [M,D] bf16 intermediates T and n.  fp8 must be 0 (bf16 operands). */
+size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
+
+/* The fused block, bf16 operands.
+ *   X [M,K1] bf16, W1 [K1,D] bf16, R [M,D] bf16, gamma [D] fp32, W2 [D,N2] bf16  (inputs)
+ *   out_h [M,D] bf16 = bf16(X W1 + R) (the fp32 sum rounded once)                   (output)
+ *   out_y [M,N2 or N2/2] bf16 = bf16(epi(r * (h W2')))                               (output)
+ * Three kernels on `stream`: GEMM1 + residual + partial sums of squares, the row-scale reduction, and
+ * GEMM2 (gamma folded into W2 while its tiles are staged) + row scale (+ SwiGLU).  After the call the
+ * workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D). */
+int coda_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
+                   float eps, int epi_kind, void* out_h, void* out_y,
+                   int64_t M, int64_t K1, int64_t D, int64_t N2,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* The unfused three-kernel baseline, kept to measure the HBM traffic the fusion saves:
+ *   T = bf16(X W1)  ->  h = bf16(T + R), r from the fp32 T + R, n = bf16(h * r * gamma)  ->  y = epi(n W2).
+ * T and n live in the workspace.  Same arguments and outputs as coda_block_fwd. */
+int coda_block_unfused(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
+                       float eps, int epi_kind, void* out_h, void* out_y,
+                       int64_t M, int64_t K1, int64_t D, int64_t N2,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Byte offset of r [M] (fp32) inside the workspace of coda_block_fwd and coda_block_unfused. */
+size_t coda_workspace_r_offset(int64_t M, int64_t D);
+
+/* ---- the three steps of coda_block_fwd, exposed one by one (same conventions) ---- */
+
+/* Step 1: out_h = bf16(X W1 + R); part[t][i] = sum over the 256 columns of tile t of the fp32 h_ij^2.
+ * part is [D/256][M] fp32 (device). */
+int coda_gemm1_residual_partial_rms(const void* X, const void* W1, const void* R, void* out_h, float* part,
+                                    int64_t M, int64_t K1, int64_t D, void* stream);
+
+/* Step 2: r[i] = 1 / sqrt((sum_{t=0..T-1} part[t][i]) / D + eps), summed in t order.  part [T][M] fp32,
+ * r [M] fp32 (device). */
+int coda_partial_rms_reduce(const float* part, int64_t T, int64_t M, int64_t D, float eps, float* r,
+                            void* stream);
+
+/* Step 3: out_y = bf16(epi(r_i * (h W2'))) with W2'[k][n] = bf16(fp32(gamma_k * W2_kn)) formed while the
+ * W2 tiles are staged.  h [M,D] bf16, W2 [D,N2] bf16, gamma [D] fp32, r [M] fp32 (device). */
+int coda_gemm2_rowscale(const void* h, const void* W2, const float* gamma, const float* r, int epi_kind,
+                        void* out_y, int64_t M, int64_t D, int64_t N2, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -31,12 +31,12 @@ _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (-O2, no fast-math: IEEE semantics are part of the
+    """Compile oracle.c into liboracle.so with gcc (-O3, no fast-math: IEEE semantics are part of the
     contract).  Returns the library path."""
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
+    cmd = ["gcc", "-O3", "-std=c11", "-fPIC", "-shared", "-fno-fast-math", "-ffp-contract=off",
            "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)

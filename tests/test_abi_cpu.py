@@ -1,0 +1,143 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function include/coda.h
+declares, and rejects bad arguments with the documented status before enqueuing anything.
+
+Pointers here are fake, aligned integers: validation never dereferences them, and no test below reaches a
+launch on a machine that has a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from gemm_epilogue_fusion_amd import binding as cb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, ALIAS, WORKSPACE, HIP = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cb.load()
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "coda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(coda_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"libcoda.so does not export {n}"
+    assert set(names) == set(cb.EXPORTS)
+
+
+def test_version_and_strings(lib):
+    assert lib.coda_abi_version() == 1
+    assert lib.coda_status_string(0) == b"CODA_OK"
+    assert lib.coda_status_string(4) == b"CODA_ERR_WORKSPACE"
+    assert lib.coda_status_string(99) == b"CODA_ERR_UNKNOWN"
+
+
+# fake, 256-byte aligned, non-overlapping "device" addresses
+BASE = 1 << 40
+GB = 1 << 32
+
+
+def _args(M=512, K1=256, D=256, N2=512, epi=0, eps=1e-5, ws_bytes=None, **over):
+    a = dict(X=BASE, W1=BASE + GB, R=BASE + 2 * GB, gamma=BASE + 3 * GB, W2=BASE + 4 * GB, eps=eps, epi=epi,
+             out_h=BASE + 5 * GB, out_y=BASE + 6 * GB, M=M, K1=K1, D=D, N2=N2, ws=BASE + 7 * GB)
+    a.update(over)
+    need = cb.load().coda_workspace_bytes(a["M"], a["K1"], a["D"], a["N2"], a["epi"], 0, 1)  # fits both paths
+    a["ws_bytes"] = need if ws_bytes is None else ws_bytes
+    return a
+
+
+def _call(lib, a, fn="coda_block_fwd"):
+    return getattr(lib, fn)(a["X"], a["W1"], a["R"], a["gamma"], a["W2"], a["eps"], a["epi"], a["out_h"],
+                            a["out_y"], a["M"], a["K1"], a["D"], a["N2"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("fn", ["coda_block_fwd", "coda_block_unfused"])
+@pytest.mark.parametrize("case,over,want", [
+    ("null_X", dict(X=0), INVALID),
+    ("null_out_y", dict(out_y=0), INVALID),
+    ("misaligned_W2", dict(W2=BASE + 4 * GB + 8), INVALID),
+    ("M_zero", dict(M=0), INVALID),
+    ("K1_negative", dict(K1=-64), INVALID),
+    ("K1_not_64", dict(K1=96), UNSUPPORTED),
+    ("D_not_256", dict(D=320), UNSUPPORTED),
+    ("N2_not_256", dict(N2=384), UNSUPPORTED),
+    ("bad_epi", dict(epi=7), INVALID),
+    ("eps_negative", dict(eps=-1.0), INVALID),
+    ("eps_nan", dict(eps=float("nan")), INVALID),
+    ("eps_inf", dict(eps=float("inf")), INVALID),
+    ("out_y_on_X", dict(out_y=BASE + 16), ALIAS),
+    ("out_h_on_W1", dict(out_h=BASE + GB), ALIAS),
+    ("out_y_on_out_h", dict(out_y=BASE + 5 * GB + 256), ALIAS),
+    ("ws_on_gamma", dict(ws=BASE + 3 * GB), ALIAS),
+    ("out_h_partly_on_R", dict(out_h=BASE + 2 * GB + 256), ALIAS),
+    ("null_workspace", dict(ws=0), WORKSPACE),
+    ("small_workspace", dict(ws_bytes=1024), WORKSPACE),
+    ("misaligned_workspace", dict(ws=BASE + 7 * GB + 16), WORKSPACE),
+])
+def test_validation(lib, fn, case, over, want):
+    a = _args()
+    over = dict(over)
+    ws_bytes = over.pop("ws_bytes", None)
+    a.update(over)
+    if ws_bytes is not None:
+        a["ws_bytes"] = ws_bytes
+    assert _call(lib, a, fn) == want, lib.coda_last_error()
+    assert lib.coda_last_error() != b""
+
+
+def test_unfused_hidden_limit(lib):
+    a = _args(D=8448)
+    assert _call(lib, a, "coda_block_unfused") == UNSUPPORTED
+
+
+def test_workspace_bytes(lib):
+    # part [D/256][M] + r [M], each 256-byte aligned; the unfused path adds two [M, D] bf16 matrices
+    assert lib.coda_workspace_bytes(8192, 2048, 2048, 16384, 1, 0, 0) == 8 * 8192 * 4 + 8192 * 4
+    assert lib.coda_workspace_bytes(8192, 2048, 2048, 16384, 1, 0, 1) == 8 * 8192 * 4 + 8192 * 4 + 2 * 8192 * 2048 * 2
+    assert lib.coda_workspace_bytes(5, 64, 256, 256, 0, 0, 0) == 256 + 256
+    assert lib.coda_workspace_r_offset(8192, 2048) == 8 * 8192 * 4
+    assert lib.coda_workspace_bytes(0, 64, 256, 256, 0, 0, 0) == 0
+
+
+def test_step_entry_points_validate(lib):
+    assert lib.coda_partial_rms_reduce(0, 8, 100, 2048, 1e-5, BASE, None) == INVALID
+    assert lib.coda_partial_rms_reduce(BASE, 0, 100, 2048, 1e-5, BASE + GB, None) == INVALID
+    assert lib.coda_partial_rms_reduce(BASE, 8, 100, 2048, -1.0, BASE + GB, None) == INVALID
+    assert lib.coda_partial_rms_reduce(BASE, 8, 100, 2048, 1e-5, BASE + 256, None) == ALIAS
+    assert lib.coda_gemm1_residual_partial_rms(BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB,
+                                               100, 96, 256, None) == UNSUPPORTED
+    assert lib.coda_gemm2_rowscale(BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, 2, BASE + 4 * GB,
+                                   100, 256, 512, None) == INVALID
+    assert lib.coda_gemm2_rowscale(BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, 0, BASE + 16,
+                                   100, 256, 512, None) == ALIAS
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_no_gpu_reports_hip_error(lib):
+    """With no GPU, a call that passes validation fails at the launch with CODA_ERR_HIP (no crash)."""
+    a = _args()
+    assert _call(lib, a) == HIP
+    assert b"launch" in lib.coda_last_error()
+    # the allowed exact alias out_h == R passes validation and also reaches the launch
+    a = _args(out_h=BASE + 2 * GB)
+    assert _call(lib, a) == HIP
+
+
+def test_binding_rejects_host_tensors():
+    X = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        cb.coda_block_fwd(X, torch.zeros(64, 256, dtype=torch.bfloat16), torch.zeros(4, 256, dtype=torch.bfloat16),
+                          torch.ones(256), torch.zeros(256, 256, dtype=torch.bfloat16), 1e-5, 0,
+                          torch.zeros(4, 256, dtype=torch.bfloat16), torch.zeros(4, 256, dtype=torch.bfloat16),
+                          torch.zeros(1024, dtype=torch.uint8))

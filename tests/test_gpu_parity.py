@@ -1,0 +1,165 @@
+"""GPU parity of the fused block (and its unfused baseline) against the fp64 oracle, through the C ABI.
+
+Small cases span several tiles and a ragged row tail and are compared element by element; the full-size
+workloads run in the launch configuration the benchmark times and are compared on sampled rows (rows are
+independent, which the oracle's row-independence pin establishes).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gemm_epilogue_fusion_amd import binding as cb
+from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, EPI_SWIGLU, WORKLOADS, Workload, make_inputs
+
+from parity import (DeviceInputs, check_h, check_roundpts, check_y, f64, normwise, oracle_rows, run_block,
+                    sample_rows)
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cb.load()
+
+
+SMALL = [
+    WORKLOADS["tiny"],
+    Workload("ragged_swiglu", M=300, K1=512, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, x_std=1.0, seed=1),
+    Workload("ragged_identity", M=300, K1=320, D=768, N2=768, epi=EPI_IDENTITY, eps=1e-5, seed=2),
+    Workload("one_row", M=1, K1=64, D=256, N2=256, epi=EPI_SWIGLU, eps=1e-6, seed=3),
+    Workload("many_tiles", M=777, K1=1024, D=1024, N2=2048, epi=EPI_SWIGLU, eps=1e-5, seed=4),
+    Workload("k64_tail", M=257, K1=64, D=256, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=5),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_fused_block_small(wl):
+    _say(f"[gpu] fused block {wl}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h, y, r = run_block(d)
+    oh, orr, oy = oracle_rows(inp)
+    check_h(f64(h), oh)
+    check_y(f64(y), oy)
+    np.testing.assert_allclose(f64(r), orr, rtol=2e-5)
+    _, _, oy_rp = oracle_rows(inp, form="roundpts")
+    check_roundpts(f64(y), oy_rp)
+
+
+@pytest.mark.parametrize("wl", SMALL[:3], ids=[w.name for w in SMALL[:3]])
+def test_unfused_block_small(wl):
+    _say(f"[gpu] unfused block {wl}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h, y, r = run_block(d, unfused=True)
+    oh, orr, oy = oracle_rows(inp, form="unfused")
+    check_h(f64(h), oh)
+    check_y(f64(y), oy)
+    # the unfused GEMM1 stores T = X W1 in bf16 before the residual add (three separate operators), so its
+    # row scale carries that rounding: about 2^-9 relative on T, hence a looser bound than the fused path
+    np.testing.assert_allclose(f64(r), orr, rtol=2e-3)
+
+
+def test_deterministic_and_in_place_residual():
+    wl = SMALL[1]
+    _say(f"[gpu] determinism / in-place {wl.name}")
+    d = DeviceInputs(make_inputs(wl))
+    h1, y1, r1 = run_block(d)
+    h2, y2, r2 = run_block(d)
+    assert torch.equal(h1.view(torch.int16), h2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(r1, r2)
+    # out_h == R: the residual stream updated in place
+    Rc = d.R.clone()
+    h3, y3, _ = run_block(d, out_h=Rc, R=Rc)
+    assert torch.equal(h3.view(torch.int16), h1.view(torch.int16))
+    assert torch.equal(y3.view(torch.int16), y1.view(torch.int16))
+
+
+def test_steps_one_by_one():
+    """The three entry points of the steps, each against the oracle's definition of that step."""
+    wl = SMALL[4]
+    _say(f"[gpu] steps {wl.name}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    T = wl.D // 256
+    h = torch.full((wl.M, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    part = torch.full((T, wl.M), float("nan"), dtype=torch.float32, device="cuda")
+    cb.coda_gemm1_residual_partial_rms(d.X, d.W1, d.R, h, part)
+    torch.cuda.synchronize()
+    oh = oracle.gemm_residual(f64(inp.X), f64(inp.W1), f64(inp.R))
+    check_h(f64(h), oh)
+    opart = np.stack([np.sum(oh[:, 256 * t: 256 * (t + 1)] ** 2, axis=1) for t in range(T)])
+    np.testing.assert_allclose(f64(part), opart, rtol=1e-4)
+    # step 2 on the GPU's own partials, against the oracle's reduction of the same partials
+    r = torch.full((wl.M,), float("nan"), dtype=torch.float32, device="cuda")
+    cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(f64(r), oracle.rms_from_partials(f64(part), wl.D, wl.eps), rtol=3e-7)
+    # step 3 on the GPU's h and r: y = epi(r * (h diag(gamma) W2)) against the oracle on the same h
+    y = torch.full((wl.M, wl.n_out), float("nan"), dtype=torch.bfloat16, device="cuda")
+    cb.coda_gemm2_rowscale(h, d.W2, d.gamma, r, wl.epi, y)
+    torch.cuda.synchronize()
+    z = (f64(h) @ (f64(inp.gamma)[:, None] * f64(inp.W2))) * f64(r)[:, None]
+    half = wl.N2 // 2
+    oy = np.array([[oracle.silu(v) for v in row] for row in z[:, :half]]) * z[:, half:]
+    check_y(f64(y), oy)
+
+
+def test_partial_reduce_synthetic():
+    """Step 2 alone on synthetic partials: fixed-order fp32 sum, within a few fp32 ulps of the fp64 value."""
+    _say("[gpu] partial reduce synthetic")
+    g = torch.Generator().manual_seed(5)
+    for T, M, D in [(1, 5, 256), (8, 8192, 2048), (16, 1000, 4096), (3, 257, 768)]:
+        part = (torch.rand(T, M, generator=g) * 400).to(torch.float32)
+        r = torch.empty(M, dtype=torch.float32, device="cuda")
+        cb.coda_partial_rms_reduce(part.cuda(), D, 1e-5, r)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(f64(r), oracle.rms_from_partials(f64(part), D, 1e-5), rtol=4e-7)
+
+
+def test_unit_gamma_identity_w2_property():
+    """gamma = 1, W2 = I: RMS(y_i) = 1/sqrt(1 + eps/mean(h_i^2)) up to bf16 rounding, on every row."""
+    wl = Workload("unit", M=513, K1=256, D=512, N2=512, epi=EPI_IDENTITY, eps=0.25, seed=6)
+    _say(f"[gpu] unit-gamma property {wl.name}")
+    inp = make_inputs(wl)
+    inp.gamma = torch.ones(wl.D)
+    inp.W2 = torch.eye(wl.D, dtype=torch.bfloat16)
+    d = DeviceInputs(inp)
+    h, y, _ = run_block(d)
+    hf, yf = f64(h), f64(y)
+    oh = oracle.gemm_residual(f64(inp.X), f64(inp.W1), f64(inp.R))
+    want = 1 / np.sqrt(1 + wl.eps / np.mean(oh ** 2, axis=1))
+    got = np.sqrt(np.mean(yf ** 2, axis=1))
+    np.testing.assert_allclose(got, want, rtol=8e-3)
+
+
+FULL = ["1b_attn_out_mlp_in", "1b_mlp_out_qkv", "8b_attn_out_mlp_in"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    """Full-size workloads in the benchmark's launch configuration, checked on sampled rows (first, last,
+    ragged tail and a seeded spread); also checks every output is finite."""
+    wl = WORKLOADS[name]
+    _say(f"[gpu] full size {wl}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h, y, r = run_block(d)
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(h).all()), "unwritten or non-finite output"
+    rows = sample_rows(wl.M, n=40)
+    oh, orr, oy = oracle_rows(inp, rows)
+    check_h(f64(h[rows]), oh)
+    check_y(f64(y[rows]), oy)
+    np.testing.assert_allclose(f64(r[rows]), orr, rtol=2e-5)
