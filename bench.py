@@ -52,7 +52,7 @@ def algorithmic_bytes(wl, fused: bool) -> int:
     if fused:
         T = D // 256
         b += 2 * 4 * T * M + 2 * 4 * M                    # part written + read, r written + read
-        b += 2 * M * D                                    # GEMM2 reads h back
+        b += 2 * 2 * M * D                                # h * gamma written, read back by GEMM2
     else:
         b += 2 * 2 * M * D                                # T written + read
         b += 2 * 2 * M * D + 4 * M                        # n written + read, r written
@@ -164,10 +164,11 @@ def main() -> int:
     T = wl.D // 256
     part = torch.empty(T, wl.M, dtype=torch.float32, device=dev)
     r = torch.empty(wl.M, dtype=torch.float32, device=dev)
+    hg = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
     n_ev = max(20, args.steps // 2)
-    k1 = lambda: cb.coda_gemm1_residual_partial_rms(X, W1, R, h, part)
+    k1 = lambda: cb.coda_gemm1_residual_partial_rms(X, W1, R, g, h, hg, part)
     k2 = lambda: cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r)
-    k3 = lambda: cb.coda_gemm2_rowscale(h, W2, g, r, wl.epi, y)
+    k3 = lambda: cb.coda_gemm2_rowscale(hg, W2, r, wl.epi, y)
     for fn in (k1, k2, k3):
         fn()
     torch.cuda.synchronize()
@@ -184,7 +185,7 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(k3_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(k3_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "kernel": "gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU, FOLD_GAMMA> (GEMM2)",
+                "kernel": "gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU> (GEMM2 + row scale + SwiGLU)",
                 "kernel_ms": round(k3_ms, 4), "algorithmic_flops_per_launch": k3_flops}
 
     fb, ub = algorithmic_bytes(wl, True), algorithmic_bytes(wl, False)

@@ -57,11 +57,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("coda_block_fwd", "coda_block_unfused"):
         getattr(lib, name).argtypes = block
         getattr(lib, name).restype = i32
-    lib.coda_gemm1_residual_partial_rms.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.coda_gemm1_residual_partial_rms.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.coda_gemm1_residual_partial_rms.restype = i32
     lib.coda_partial_rms_reduce.argtypes = [vp, i64, i64, i64, f32, vp, vp]
     lib.coda_partial_rms_reduce.restype = i32
-    lib.coda_gemm2_rowscale.argtypes = [vp, vp, vp, vp, i32, vp, i64, i64, i64, vp]
+    lib.coda_gemm2_rowscale.argtypes = [vp, vp, vp, i32, vp, i64, i64, i64, vp]
     lib.coda_gemm2_rowscale.restype = i32
     _lib = lib
     return lib
@@ -138,12 +138,14 @@ def coda_block_unfused(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, ou
     _block("coda_block_unfused", X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspace, stream)
 
 
-def coda_gemm1_residual_partial_rms(X, W1, R, out_h, part, stream=None):
+def coda_gemm1_residual_partial_rms(X, W1, R, gamma, out_h, out_hg, part, stream=None):
+    """Step 1: out_h = bf16(X W1 + R), out_hg = bf16((X W1 + R) * gamma), part [D/256, M] partial sums of squares."""
     M, K1 = X.shape
     D = W1.shape[1]
     st = load().coda_gemm1_residual_partial_rms(
         _dev(X, "X", torch.bfloat16, (M, K1)), _dev(W1, "W1", torch.bfloat16, (K1, D)),
-        _dev(R, "R", torch.bfloat16, (M, D)), _dev(out_h, "out_h", torch.bfloat16, (M, D)),
+        _dev(R, "R", torch.bfloat16, (M, D)), _dev(gamma, "gamma", torch.float32, (D,)),
+        _dev(out_h, "out_h", torch.bfloat16, (M, D)), _dev(out_hg, "out_hg", torch.bfloat16, (M, D)),
         _dev(part, "part", torch.float32, (D // 256, M)), M, K1, D, _stream(stream))
     _check(st, "coda_gemm1_residual_partial_rms")
 
@@ -155,14 +157,15 @@ def coda_partial_rms_reduce(part, D: int, eps: float, r, stream=None):
     _check(st, "coda_partial_rms_reduce")
 
 
-def coda_gemm2_rowscale(h, W2, gamma, r, epi_kind: int, out_y, stream=None):
-    M, D = h.shape
+def coda_gemm2_rowscale(hg, W2, r, epi_kind: int, out_y, stream=None):
+    """Step 3: out_y = bf16(epi(r * (hg W2)))."""
+    M, D = hg.shape
     N2 = W2.shape[1]
     ny = N2 if epi_kind == EPI_IDENTITY else N2 // 2
     st = load().coda_gemm2_rowscale(
-        _dev(h, "h", torch.bfloat16, (M, D)), _dev(W2, "W2", torch.bfloat16, (D, N2)),
-        _dev(gamma, "gamma", torch.float32, (D,)), _dev(r, "r", torch.float32, (M,)), int(epi_kind),
-        _dev(out_y, "out_y", torch.bfloat16, (M, ny)), M, D, N2, _stream(stream))
+        _dev(hg, "hg", torch.bfloat16, (M, D)), _dev(W2, "W2", torch.bfloat16, (D, N2)),
+        _dev(r, "r", torch.float32, (M,)), int(epi_kind), _dev(out_y, "out_y", torch.bfloat16, (M, ny)),
+        M, D, N2, _stream(stream))
     _check(st, "coda_gemm2_rowscale")
 
 

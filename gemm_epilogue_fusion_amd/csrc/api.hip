@@ -64,7 +64,7 @@ int check_dims(int64_t M, int64_t K1, int64_t D, int64_t N2) {
   if (M > kMaxDim || K1 > kMaxDim || D > kMaxDim || N2 > kMaxDim || M * K1 > kMaxDim * 2 ||
       M * D > kMaxDim * 2 || M * N2 > kMaxDim * 2 || D * N2 > kMaxDim * 2 || K1 * D > kMaxDim * 2)
     return fail(CODA_ERR_UNSUPPORTED, "dimensions too large");
-  if (K1 % 64) return fail(CODA_ERR_UNSUPPORTED, "K1=%lld is not a multiple of 64", (long long)K1);
+  if (K1 % 128) return fail(CODA_ERR_UNSUPPORTED, "K1=%lld is not a multiple of 128", (long long)K1);
   if (D % 256) return fail(CODA_ERR_UNSUPPORTED, "D=%lld is not a multiple of 256", (long long)D);
   if (N2 % 256) return fail(CODA_ERR_UNSUPPORTED, "N2=%lld is not a multiple of 256", (long long)N2);
   return CODA_OK;
@@ -96,8 +96,9 @@ int check_alias(const Range* in, int nin, const Range* out, int nout, const void
 struct Workspace {
   float* part;
   float* r;
-  uint16_t* t;  // unfused: T = X W1
-  uint16_t* n;  // unfused: normalised rows
+  uint16_t* hg;  // fused: h * gamma, the second GEMM's A operand
+  uint16_t* t;   // unfused: T = X W1
+  uint16_t* n;   // unfused: normalised rows
 };
 
 size_t ws_part_bytes(int64_t M, int64_t D) { return align256((size_t)(D / 256) * (size_t)M * 4); }
@@ -105,9 +106,7 @@ size_t ws_r_bytes(int64_t M) { return align256((size_t)M * 4); }
 size_t ws_mat_bytes(int64_t M, int64_t D) { return align256((size_t)M * (size_t)D * 2); }
 
 size_t ws_bytes(int64_t M, int64_t D, int unfused) {
-  size_t b = ws_part_bytes(M, D) + ws_r_bytes(M);
-  if (unfused) b += 2 * ws_mat_bytes(M, D);
-  return b;
+  return ws_part_bytes(M, D) + ws_r_bytes(M) + (unfused ? 2 : 1) * ws_mat_bytes(M, D);
 }
 
 Workspace carve(void* ws, int64_t M, int64_t D, int unfused) {
@@ -121,6 +120,8 @@ Workspace carve(void* ws, int64_t M, int64_t D, int unfused) {
     w.t = (uint16_t*)p;
     p += ws_mat_bytes(M, D);
     w.n = (uint16_t*)p;
+  } else {
+    w.hg = (uint16_t*)p;
   }
   return w;
 }
@@ -192,15 +193,15 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
     hipStream_t st = (hipStream_t)stream;
     Workspace w = carve(workspace, M, D, 0);
     if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
-                                                   (uint16_t*)out_h, w.part, (int)M, (int)K1, (int)D, st),
+                                                   gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
+                                                   st),
                        "gemm1_res_prms launch")))
       return s;
     if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                        "prms_reduce launch")))
       return s;
-    return hip_check(coda::launch_gemm2_rowscale((const uint16_t*)out_h, (const uint16_t*)W2, gamma, w.r,
-                                                 epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
-                                                 (int)N2, st),
+    return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, epi_kind == CODA_EPI_SWIGLU,
+                                                 (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
                      "gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -224,29 +225,30 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
                                                 (int)M, (int)D, eps, st),
                        "add_rmsnorm launch")))
       return s;
-    return hip_check(coda::launch_gemm2_rowscale(w.n, (const uint16_t*)W2, nullptr, nullptr,
-                                                 epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
-                                                 (int)N2, st),
+    return hip_check(coda::launch_gemm2_rowscale(w.n, (const uint16_t*)W2, nullptr, epi_kind == CODA_EPI_SWIGLU,
+                                                 (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
                      "unfused gemm2 launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }
 }
 
-int coda_gemm1_residual_partial_rms(const void* X, const void* W1, const void* R, void* out_h, float* part,
-                                    int64_t M, int64_t K1, int64_t D, void* stream) {
+int coda_gemm1_residual_partial_rms(const void* X, const void* W1, const void* R, const float* gamma, void* out_h,
+                                    void* out_hg, float* part, int64_t M, int64_t K1, int64_t D, void* stream) {
   try {
     int s;
     if ((s = check_ptr(X, "X")) || (s = check_ptr(W1, "W1")) || (s = check_ptr(R, "R")) ||
-        (s = check_ptr(out_h, "out_h")) || (s = check_ptr(part, "part")))
+        (s = check_ptr(gamma, "gamma")) || (s = check_ptr(out_h, "out_h")) || (s = check_ptr(out_hg, "out_hg")) ||
+        (s = check_ptr(part, "part")))
       return s;
     if ((s = check_dims(M, K1, D, 256))) return s;
-    const Range in[3] = {rng("X", X, (size_t)(M * K1 * 2)), rng("W1", W1, (size_t)(K1 * D * 2)),
-                         rng("R", R, (size_t)(M * D * 2))};
-    const Range out[2] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("part", part, (size_t)(D / 256 * M * 4))};
-    if ((s = check_alias(in, 3, out, 2, out_h, R))) return s;
-    return hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
-                                                 (uint16_t*)out_h, part, (int)M, (int)K1, (int)D,
+    const Range in[4] = {rng("X", X, (size_t)(M * K1 * 2)), rng("W1", W1, (size_t)(K1 * D * 2)),
+                         rng("R", R, (size_t)(M * D * 2)), rng("gamma", gamma, (size_t)D * 4)};
+    const Range out[3] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("out_hg", out_hg, (size_t)(M * D * 2)),
+                          rng("part", part, (size_t)(D / 256 * M * 4))};
+    if ((s = check_alias(in, 4, out, 3, out_h, R))) return s;
+    return hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R, gamma,
+                                                 (uint16_t*)out_h, (uint16_t*)out_hg, part, (int)M, (int)K1, (int)D,
                                                  (hipStream_t)stream),
                      "gemm1_res_prms launch");
   } catch (...) {
@@ -272,21 +274,21 @@ int coda_partial_rms_reduce(const float* part, int64_t T, int64_t M, int64_t D, 
   }
 }
 
-int coda_gemm2_rowscale(const void* h, const void* W2, const float* gamma, const float* r, int epi_kind,
-                        void* out_y, int64_t M, int64_t D, int64_t N2, void* stream) {
+int coda_gemm2_rowscale(const void* hg, const void* W2, const float* r, int epi_kind, void* out_y, int64_t M,
+                        int64_t D, int64_t N2, void* stream) {
   try {
     int s;
-    if ((s = check_ptr(h, "h")) || (s = check_ptr(W2, "W2")) || (s = check_ptr(gamma, "gamma")) ||
-        (s = check_ptr(r, "r")) || (s = check_ptr(out_y, "out_y")))
+    if ((s = check_ptr(hg, "hg")) || (s = check_ptr(W2, "W2")) || (s = check_ptr(r, "r")) ||
+        (s = check_ptr(out_y, "out_y")))
       return s;
-    if ((s = check_dims(M, 64, D, N2))) return s;
+    if ((s = check_dims(M, 128, D, N2))) return s;
     if ((s = check_epi_eps(epi_kind, 0.0f))) return s;
     const int64_t ny = epi_kind == CODA_EPI_SWIGLU ? N2 / 2 : N2;
-    const Range in[4] = {rng("h", h, (size_t)(M * D * 2)), rng("W2", W2, (size_t)(D * N2 * 2)),
-                         rng("gamma", gamma, (size_t)D * 4), rng("r", r, (size_t)M * 4)};
+    const Range in[3] = {rng("hg", hg, (size_t)(M * D * 2)), rng("W2", W2, (size_t)(D * N2 * 2)),
+                         rng("r", r, (size_t)M * 4)};
     const Range out[1] = {rng("out_y", out_y, (size_t)(M * ny * 2))};
-    if ((s = check_alias(in, 4, out, 1, nullptr, nullptr))) return s;
-    return hip_check(coda::launch_gemm2_rowscale((const uint16_t*)h, (const uint16_t*)W2, gamma, r,
+    if ((s = check_alias(in, 3, out, 1, nullptr, nullptr))) return s;
+    return hip_check(coda::launch_gemm2_rowscale((const uint16_t*)hg, (const uint16_t*)W2, r,
                                                  epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
                                                  (int)N2, (hipStream_t)stream),
                      "gemm2_rowscale launch");

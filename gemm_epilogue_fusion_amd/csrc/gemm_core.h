@@ -1,30 +1,41 @@
-// gemm_core.h -- bf16 MFMA GEMM mainloop for gfx950 (CDNA4) shared by the block's two GEMMs.
+// gemm_core.h -- bf16 MFMA GEMM mainloop for gfx950 (CDNA4) shared by the block's GEMMs.
 //
 // The CODA write-up ("CODA: new research optimizes Transformer training with GEMM-epilogue programming",
 // section "CODA: the treasure hidden in the epilogue") splits a GEMM into a mainloop (tiled
 // multiply-accumulate) and an epilogue (finishing work done while the output tile is still in registers).
 // This file is the mainloop; the epilogues live with the kernels.
 //
-// Tiling (one workgroup = 4 waves of 64 lanes):
-//   macro tile 256 (M) x 256 (N), K step 64, each wave owns a 128 x 128 sub-tile held as 4 x 4 blocks of
-//   32 x 32 fp32 accumulators (256 accumulator registers per lane).
-//   Operands: A [M,K] row-major (K contiguous); B [K,N] row-major (N contiguous), as weights are stored.
-//   Both tiles are staged global -> VGPR -> LDS with 16-byte loads, double-buffered in LDS (128 KiB of the
-//   160 KiB a CU has).  B stays N-contiguous in LDS and is read K-contiguous with ds_read_b64_tr_b16, the
-//   gfx950 transposing LDS read, so no transpose pass over the weights is needed.
-//   The MFMA is v_mfma_f32_32x32x16_bf16 with the B fragment as its first operand and the A fragment as
-//   its second, which computes the transposed tile: every lane then owns one output row (4 groups of 4
-//   consecutive columns per 32 x 32 block), so row-wise epilogue work (sums of squares, the row scale)
-//   stays inside a lane.
+// Tiling: one workgroup of 8 waves (512 lanes, two waves per SIMD) computes a 256 x 256 tile.  Wave w owns
+// rows 128 (w % 2) .. +128 and columns 64 (w / 2) .. +64 as 4 x 2 blocks of 32 x 32 fp32 accumulators
+// (128 registers per lane).
+//
+// Operands: A [M,K] row-major (K contiguous); B [K,N] row-major (N contiguous), the layout weights are
+// stored in.  K advances 32 at a time through a ring of 4 LDS stages (4 x 32 KiB): stage k+3 is fetched
+// while stage k is multiplied, with global_load_lds_dwordx4 (global memory straight into LDS, no VGPR
+// staging), so each tile's loads have three K steps of latency budget.  One barrier per K step, placed
+// half-way so that the next step's first fragments are read from LDS while the current step's last
+// MFMAs run.  The barrier carries no memory fence: the wait is an explicit vmcnt for the stage about to be
+// read, which keeps the later stages' loads in flight.
+//
+// B stays N-contiguous in LDS and is read K-contiguous with ds_read_b64_tr_b16 (the gfx950 transposing
+// LDS read), so the weights need no transpose pass.  The MFMA (v_mfma_f32_32x32x16_bf16) takes the B
+// fragment as its first operand and the A fragment as its second, which yields the transposed tile: each
+// lane owns output rows, so row-wise epilogue work (sums of squares, the row scale) stays inside a lane.
+//
+// LDS swizzles (verified conflict-free with the SQ_LDS_BANK_CONFLICT counter): A rows are 64 bytes, chunk
+// c of row r sits at slot c ^ ((r / 4) % 4); B rows are 512 bytes, chunk c of row k at c ^ 4 (k % 4).
 //
 // Lane layouts (verified on the device):
 //   v_mfma_f32_32x32x16_bf16(a, b, c): a lane l holds a[row l%32][k 8(l/32)+e], b lane l holds
 //   b[k 8(l/32)+e][col l%32]; result register r of lane l is c[row 8(r/4)+4(l/32)+r%4][col l%32].
 //   ds_read_b64_tr_b16: inside each group of 16 lanes, element e of lane i is element i%4 of the 8 bytes
 //   addressed by lane 4e + i/4 of the group.
+//   global_load_lds_dwordx4: lane i's 16 bytes land at the wave-uniform LDS base + 16 i.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace coda {
 
@@ -33,20 +44,25 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256;
-constexpr int BN = 256;
-constexpr int BK = 64;
-constexpr int NTHREADS = 256;
-constexpr int A_TILE_BYTES = BM * BK * 2;  // 32 KiB
-constexpr int B_TILE_BYTES = BK * BN * 2;  // 32 KiB
-constexpr int STAGE_BYTES = A_TILE_BYTES + B_TILE_BYTES;
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;  // 128 KiB
+constexpr int BM = 256;            // rows of a workgroup tile
+constexpr int BN = 256;            // accumulator columns of a workgroup tile
+constexpr int BK = 32;             // K per stage
+constexpr int NSTAGE = 4;          // LDS ring depth
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int NB = 2;              // 32-column accumulator blocks per wave
+constexpr int A_BYTES = BM * BK * 2;      // 16 KiB
+constexpr int B_BYTES = BK * BN * 2;      // 16 KiB
+constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;  // 128 KiB
+constexpr int K_MULTIPLE = BK * NSTAGE;           // K must be a multiple of this
 
-// ---- small conversions --------------------------------------------------------------------------------
+// ---- small conversions ------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 // two fp32 -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), lo in the low half
@@ -55,130 +71,184 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// ---- LDS layouts ------------------------------------------------------------------------------------
-// A tile: 256 rows of 128 bytes (8 chunks of 16 B); chunk c of row m sits at slot c ^ (m % 8), so the 8
-// rows a 16-byte fragment read touches at once fall in 8 different bank groups.
-__device__ __forceinline__ int a_off(int m, int c) { return m * 128 + ((c ^ (m & 7)) << 4); }
-// B tile: 64 rows of 512 bytes (32 chunks of 16 B); chunk c of row k sits at slot c ^ (2 (k % 4)), so the
-// 4 rows x 32 bytes one transposing read of 16 lanes touches fall in 8 different bank groups.  Rows k and
-// k + 4 share a swizzle, which lets the second half of a fragment reuse the first half's address + 2 KiB.
-__device__ __forceinline__ int b_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 1)) << 4); }
+// ---- LDS layout -------------------------------------------------------------------------------------
+__device__ __forceinline__ int a_off(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+__device__ __forceinline__ int b_off(int k, int c) { return k * 512 + ((c ^ ((k & 3) << 2)) << 4); }
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
+// 16 bytes per lane from global memory into LDS at the wave-uniform base + 16 * lane
+__device__ __forceinline__ void g2lds16(const void* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
 
-// One K step of 64 from the LDS stage (sA, sB) into the wave's 4 x 4 accumulator blocks.
-// wm, wn: the wave's position (0/1) in the 2 x 2 wave grid; lane: 0..63.
-__device__ __forceinline__ void mma_stage(const char* sA, const char* sB, int wm, int wn, int lane,
-                                          f32x16 (&acc)[4][4]) {
-  const int q = lane >> 4;  // 16-lane group
-  const int j = lane & 15;
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8]),
+// then a workgroup barrier the compiler may not move memory operations across.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+struct Frags {
+  s16x8 a[4];   // A rows mb*32 .. +32 of the wave, 8 K values per lane
+  s16x8 b[NB];  // B columns nb*32 .. +32 of the wave, 8 K values per lane
+};
+
+// Per-lane LDS offsets of the fragments inside a stage (sub-step s of 16 K values adds immediates).
+struct LaneOffs {
+  int a[2];
+  int b[NB];
+};
+
+__device__ __forceinline__ void lane_offsets(int wm, int wn, int lane, LaneOffs& o) {
+  const int q = lane >> 4, j = lane & 15;
 #pragma unroll
-  for (int s = 0; s < BK / 16; ++s) {
-    s16x8 bfr[4], afr[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      // lane j of group q points at row k0 + j/4, columns n0 + 4 (j%4) .. +3 of the tile, so that after the
-      // transposing read lane i of the group holds rows k0..k0+3 of column n0 + i.
-      const int n0 = wn * 128 + nb * 32 + 16 * (q & 1);
-      const int krow = 16 * s + 8 * (q >> 1) + (j >> 2);
-      const int piece = (n0 >> 2) + (j & 3);  // 8-byte piece within the 512-byte row
-      const char* p = sB + b_off(krow, piece >> 1) + ((piece & 1) << 3);
-      s16x4 lo = lds_read_tr16(p);
-      s16x4 hi = lds_read_tr16(p + 4 * 512);  // rows k0+4..k0+7, same swizzle
-      bfr[nb] = (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = wm * 128 + mb * 32 + (lane & 31);
-      afr[mb] = *(const s16x8*)(sA + a_off(m, 2 * s + (lane >> 5)));
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bfr[nb]),
-                                                             __builtin_bit_cast(bf16x8, afr[mb]),
-                                                             acc[mb][nb], 0, 0, 0);
+  for (int nb = 0; nb < NB; ++nb) {
+    // lane j of 16-lane group q points at row k0 + j/4, columns n0 + 4 (j%4) .. +3, so that after the
+    // transposing read lane i of the group holds rows k0..k0+3 of column n0 + i
+    const int n0 = wn * (32 * NB) + nb * 32 + 16 * (q & 1);
+    const int krow = 8 * (q >> 1) + (j >> 2);
+    const int piece = (n0 >> 2) + (j & 3);  // 8-byte piece within the 512-byte row
+    o.b[nb] = A_BYTES + b_off(krow, piece >> 1) + ((piece & 1) << 3);
   }
-}
-
-// 8 bf16 scaled by one fp32 factor and rounded back to bf16 (round to nearest even).
-__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 v, float g) {
-  u32x4 o;
+  const int m = wm * 128 + (lane & 31);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = pack_bf16(bf16_lo(v[i]) * g, bf16_hi(v[i]) * g);
-  return o;
+  for (int s = 0; s < 2; ++s) o.a[s] = a_off(m, 2 * s + (lane >> 5));
 }
 
-// The mainloop.  acc += A[m0:m0+256, :] * B[:, tile columns] over the full K.
-//   A: [M,K] bf16 with row stride lda; rows >= M are read as row M-1 (their results are never stored).
-//   B: [K,*] bf16 with row stride ldb; bcol = global column of the 8 tile columns this thread stages
-//      (tile column chunk t % 32), which lets a tile gather column segments (gate | up halves).
-//   gamma: if non-null, B row k is multiplied by gamma[k] while staged (W2' = diag(gamma) W2).
-__device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
-                                              const uint16_t* __restrict__ B, int64_t ldb, int64_t bcol,
-                                              const float* __restrict__ gamma, int K, char* smem,
-                                              f32x16 (&acc)[4][4]) {
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+__device__ __forceinline__ void read_frags(const char* st, const LaneOffs& o, int s, Frags& f) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const char* p = st + o.b[nb] + s * (16 * 512);
+    const s16x4 lo = lds_read_tr16(p);
+    const s16x4 hi = lds_read_tr16(p + 4 * 512);  // rows k0+4..k0+7 share the swizzle of rows k0..k0+3
+    f.b[nb] = (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) f.a[mb] = *(const s16x8*)(st + o.a[s] + mb * 32 * 64);
+}
 
+__device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[4][NB]) {
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = (f32x16){};
+    for (int nb = 0; nb < NB; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.b[nb]),
+                                                           __builtin_bit_cast(bf16x8, f.a[mb]), acc[mb][nb], 0, 0, 0);
+}
 
-  // per-thread global pointers: A row t/8 + 32p (chunk t%8), B row t/32 + 8p (chunk t%32)
-  const uint16_t* aptr[8];
+// Interleave the 8 MFMAs of a sub-step one-to-one with the 8 LDS reads of the next fragments.
+__device__ __forceinline__ void interleave_mma_reads() {
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    int row = m0 + (t >> 3) + 32 * p;
-    row = row < M ? row : M - 1;
-    aptr[p] = A + (int64_t)row * lda + (t & 7) * 8;
+  for (int i = 0; i < 4 + 2 * NB; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
   }
-  const uint16_t* bptr = B + (int64_t)(t >> 5) * ldb + bcol;
-  const int64_t bstep = 8 * ldb;
+}
 
-  u32x4 ra[8], rb[8];
-  float g[8];
+// The mainloop: acc = A[m0:m0+256, :] * B[:, tile columns] over the full K (K % K_MULTIPLE == 0).
+//   A: [M,K] bf16, row stride lda; rows >= M are read as row M-1 (their results are never stored).
+//   B: [K,*] bf16, row stride ldb.  bcol(c) gives the global column of the tile's 8-column chunk c
+//      (0..31), which lets a tile gather column segments (the gate | up halves of SwiGLU).
+template <class BCol>
+__device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
+                                              const uint16_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
+                                              char* smem, f32x16 (&acc)[4][NB]) {
+  constexpr int LPW = 16 / NWAVES;              // 1 KiB direct loads per wave per operand per stage
+  constexpr int PER = 2 * LPW;  // VMEM instructions per wave per stage
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = (f32x16){};
+
+  // Direct-load unit q (1 KiB) of a stage: A rows 16q .. 16q+15 (lane -> row 16q + lane/4, slot lane%4),
+  // B rows 2q, 2q+1 (lane -> row 2q + lane/32, slot lane%32).  Each lane fetches the logical chunk that
+  // the swizzle places in its slot.
+  const uint16_t* aptr[LPW];
+  const uint16_t* bptr[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int q = LPW * wave + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    int row = m0 + r;
+    row = row < M ? row : M - 1;
+    aptr[i] = A + (int64_t)row * lda + 8 * c;
+    const int kr = 2 * q + (lane >> 5);
+    const int cb = (lane & 31) ^ ((kr & 3) << 2);
+    bptr[i] = B + (int64_t)kr * ldb + bcol(cb);
+  }
+  LaneOffs lo;
+  lane_offsets(wm, wn, lane, lo);
   const int nk = K / BK;
 
-  auto load = [&](int kt) {
+  auto issue = [&](int kt, int stage) {
+    char* st = smem + stage * STAGE_BYTES;
     const int k0 = kt * BK;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) ra[p] = *(const u32x4*)(aptr[p] + k0);
+    for (int i = 0; i < LPW; ++i) g2lds16(aptr[i] + k0, st + (LPW * wave + i) * 1024);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) rb[p] = *(const u32x4*)(bptr + (int64_t)k0 * ldb + p * bstep);
-    if (gamma) {
-#pragma unroll
-      for (int p = 0; p < 8; ++p) g[p] = gamma[k0 + (t >> 5) + 8 * p];
-    }
-  };
-  auto store = [&](char* stage) {
-    char* sA = stage;
-    char* sB = stage + A_TILE_BYTES;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) *(u32x4*)(sA + a_off((t >> 3) + 32 * p, t & 7)) = ra[p];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      u32x4 v = gamma ? scale_bf16x8(rb[p], g[p]) : rb[p];
-      *(u32x4*)(sB + b_off((t >> 5) + 8 * p, t & 31)) = v;
-    }
+    for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + (int64_t)k0 * ldb, st + A_BYTES + (LPW * wave + i) * 1024);
   };
 
-  load(0);
-  store(smem);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE_BYTES;
-    if (kt + 1 < nk) load(kt + 1);
-    mma_stage(cur, cur + A_TILE_BYTES, wm, wn, lane, acc);
-    if (kt + 1 < nk) store(smem + ((kt + 1) & 1) * STAGE_BYTES);
-    __syncthreads();
+  Frags f0, f1;
+  // One K step on stage U.  ISSUE: fetch tile kt+3 into the stage tile kt-1 used (every wave has passed
+  // the barrier that followed its last read of it).  WAIT >= 0: the vmcnt that guarantees tile kt+1 has
+  // landed, then the barrier and the first fragments of tile kt+1; WAIT < 0: the last tile.
+  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c) {
+    constexpr int U = decltype(U_c)::value;
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr int WAIT = decltype(wait_c)::value;
+    const char* cur = smem + U * STAGE_BYTES;
+    if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
+    read_frags(cur, lo, 1, f1);
+    mma(f0, acc);
+    interleave_mma_reads();
+    if (WAIT >= 0) {
+      wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
+      read_frags(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, lo, 0, f0);
+    }
+    mma(f1, acc);
+    interleave_mma_reads();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using Yes = std::true_type;
+  using No = std::false_type;
+  using WaitFull = std::integral_constant<int, 2 * PER>;
+  static_assert(NSTAGE == 4, "the step sequence below is written for four stages");
+
+  // prologue: tiles 0..2 in flight, wait for tile 0
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
+  wait_barrier<2 * PER>();
+  read_frags(smem, lo, 0, f0);
+
+  const int nblk = nk / NSTAGE;
+  for (int bi = 0; bi < nblk - 1; ++bi) {
+    const int kt = bi * NSTAGE;
+    step(kt + 0, S0{}, Yes{}, WaitFull{});
+    step(kt + 1, S1{}, Yes{}, WaitFull{});
+    step(kt + 2, S2{}, Yes{}, WaitFull{});
+    step(kt + 3, S3{}, Yes{}, WaitFull{});
   }
+  // last block: only its first step fetches (the last tile); the waits shrink as the ring drains
+  const int kt = (nblk - 1) * NSTAGE;
+  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{});
+  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER>{});
+  step(kt + 2, S2{}, No{}, std::integral_constant<int, 0>{});
+  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
 }
 
 // Maps the linear workgroup id to a (row tile, column tile) pair.

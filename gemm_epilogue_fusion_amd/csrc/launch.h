@@ -6,14 +6,15 @@
 
 namespace coda {
 
-// K1: H = bf16(X W1 + R) and part[t][m] = sum over tile t's 256 columns of the fp32 (X W1 + R)^2.
-hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, uint16_t* H,
-                                 float* part, int M, int K1, int D, hipStream_t stream);
+// K1: H = bf16(X W1 + R), HG = bf16((X W1 + R) * gamma) and part[t][m] = sum over tile t's 256 columns of
+// the fp32 (X W1 + R)^2.
+hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, const float* gamma,
+                                 uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream);
 // K2: r[m] = 1 / sqrt(sum_t part[t][m] / D + eps).
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream);
-// K3 (gamma, r non-null) and U3 (both null): Y = bf16(epi(r * (H diag(gamma) W2))).
-hipError_t launch_gemm2_rowscale(const uint16_t* H, const uint16_t* W2, const float* gamma, const float* r,
-                                 int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream);
+// K3 (r non-null; A = h * gamma) and U3 (r null; A = the normalised rows): Y = bf16(epi(r * (A W2))).
+hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
+                                 int M, int D, int N2, hipStream_t stream);
 // U1: T = bf16(X W).
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
                              hipStream_t stream);

@@ -7,14 +7,18 @@
  *                                      still in registers; h is stored (it is the residual stream and the
  *                                      activation kept for backward, section "Five blocks and a Lego
  *                                      language": tiled matrix store)
+ *   hg = h * gamma                     the RMSNorm weight broadcast along the rows in the same epilogue
+ *                                      (vector-load primitive, same section), stored in the workspace
  *   part[t][i] = sum_{j in tile t} h_ij^2   per-row, per-column-tile partial sums from the same epilogue
  *                                      (block reduction primitive: "local RMS")
  *   r_i = 1 / sqrt(sum_t part[t][i] / D + eps)   a light reduction kernel
- *   y  = epi(r_i * (h W2'))  with W2' = diag(gamma) W2: the per-row scale commutes with the second GEMM,
- *                                      so the second mainloop runs on h itself and r is applied in its
- *                                      epilogue, optionally followed by SwiGLU on a fused gate|up product
- *                                      (the same section: SwiGLU admits the same rewrite).
- * No normalised tensor is ever written to or read from HBM.
+ *   y  = epi(r_i * (hg W2)) = epi(r_i * (h diag(gamma) W2)): the per-row scale commutes with the second
+ *                                      GEMM, so r is applied in its epilogue, optionally followed by SwiGLU
+ *                                      on a fused gate|up product (the same section: SwiGLU admits the same
+ *                                      rewrite).
+ * No normalised tensor is ever written to or read from HBM.  gamma is applied on the h side rather than
+ * folded into W2's tiles: on gfx950 scaling the W2 tiles in the second GEMM costs 13-19% of its time (the
+ * scaling work does not overlap the matrix cores), while writing hg costs one [M,D] bf16 store.
  *
  * Conventions shared by every entry point
  *   - All matrices are dense and row-major with no padding: X [M,K1], W1 [K1,D] (weights are [in,out]),
@@ -31,7 +35,7 @@
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the default stream) and is asynchronous: buffers
  *     must stay alive until the stream has passed the call.  Calls on distinct streams with distinct
  *     workspaces may run concurrently; calls sharing a workspace must be ordered by the caller.
- *   - Shape rules: M >= 1 (any value; the last row tile is masked); K1 a multiple of 64; D and N2
+ *   - Shape rules: M >= 1 (any value; the last row tile is masked); K1 a multiple of 128; D and N2
  *     multiples of 256 (for SwiGLU N2/2 is then a multiple of 128).  Other shapes return
  *     CODA_ERR_UNSUPPORTED.  eps must be finite and >= 0.
  *   - Aliasing: no output may overlap an input or another output, except the exact in-place residual
@@ -77,17 +81,17 @@ const char* coda_last_error(void);
 /* Workspace bytes an entry point needs for these dimensions.
  *   fp8:     0 for the bf16 entry points, 1 for the *_fp8 ones
  *   unfused: 0 for coda_block_fwd*, 1 for coda_block_unfused*
- * Layout (fused): part [D/256][M] fp32 partial sums of squares, then r [M] fp32, each 256-byte aligned;
- * the unfused path adds its two [M,D] bf16 intermediates T and n.  fp8 must be 0 (bf16 operands). */
+ * Layout: part [D/256][M] fp32 partial sums of squares, then r [M] fp32, then (fused) hg [M,D] bf16 or
+ * (unfused) the two [M,D] bf16 intermediates T and n, each 256-byte aligned.  fp8 must be 0. */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
 /* The fused block, bf16 operands.
  *   X [M,K1] bf16, W1 [K1,D] bf16, R [M,D] bf16, gamma [D] fp32, W2 [D,N2] bf16  (inputs)
  *   out_h [M,D] bf16 = bf16(X W1 + R) (the fp32 sum rounded once)                   (output)
  *   out_y [M,N2 or N2/2] bf16 = bf16(epi(r * (h W2')))                               (output)
- * Three kernels on `stream`: GEMM1 + residual + partial sums of squares, the row-scale reduction, and
- * GEMM2 (gamma folded into W2 while its tiles are staged) + row scale (+ SwiGLU).  After the call the
- * workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D). */
+ * Three kernels on `stream`: GEMM1 + residual + gamma + partial sums of squares, the row-scale reduction,
+ * and GEMM2 on hg + row scale (+ SwiGLU).  After the call the workspace holds r [M] (fp32) at byte offset
+ * coda_workspace_r_offset(M, D). */
 int coda_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
                    float eps, int epi_kind, void* out_h, void* out_y,
                    int64_t M, int64_t K1, int64_t D, int64_t N2,
@@ -106,20 +110,22 @@ size_t coda_workspace_r_offset(int64_t M, int64_t D);
 
 /* ---- the three steps of coda_block_fwd, exposed one by one (same conventions) ---- */
 
-/* Step 1: out_h = bf16(X W1 + R); part[t][i] = sum over the 256 columns of tile t of the fp32 h_ij^2.
- * part is [D/256][M] fp32 (device). */
-int coda_gemm1_residual_partial_rms(const void* X, const void* W1, const void* R, void* out_h, float* part,
-                                    int64_t M, int64_t K1, int64_t D, void* stream);
+/* Step 1: out_h = bf16(X W1 + R); out_hg = bf16((X W1 + R) * gamma) (the fp32 sum times gamma, rounded
+ * once); part[t][i] = sum over the 256 columns of tile t of the fp32 (X W1 + R)_ij^2.
+ * X [M,K1] bf16, W1 [K1,D] bf16, R [M,D] bf16, gamma [D] fp32 (inputs); out_h, out_hg [M,D] bf16 and
+ * part [D/256][M] fp32 (outputs; out_h == R is allowed). */
+int coda_gemm1_residual_partial_rms(const void* X, const void* W1, const void* R, const float* gamma, void* out_h,
+                                    void* out_hg, float* part, int64_t M, int64_t K1, int64_t D, void* stream);
 
 /* Step 2: r[i] = 1 / sqrt((sum_{t=0..T-1} part[t][i]) / D + eps), summed in t order.  part [T][M] fp32,
  * r [M] fp32 (device). */
 int coda_partial_rms_reduce(const float* part, int64_t T, int64_t M, int64_t D, float eps, float* r,
                             void* stream);
 
-/* Step 3: out_y = bf16(epi(r_i * (h W2'))) with W2'[k][n] = bf16(fp32(gamma_k * W2_kn)) formed while the
- * W2 tiles are staged.  h [M,D] bf16, W2 [D,N2] bf16, gamma [D] fp32, r [M] fp32 (device). */
-int coda_gemm2_rowscale(const void* h, const void* W2, const float* gamma, const float* r, int epi_kind,
-                        void* out_y, int64_t M, int64_t D, int64_t N2, void* stream);
+/* Step 3: out_y = bf16(epi(r_i * (hg W2))).  hg [M,D] bf16 (h * gamma from step 1), W2 [D,N2] bf16,
+ * r [M] fp32 (device). */
+int coda_gemm2_rowscale(const void* hg, const void* W2, const float* r, int epi_kind, void* out_y, int64_t M,
+                        int64_t D, int64_t N2, void* stream);
 
 #ifdef __cplusplus
 }

@@ -260,11 +260,15 @@ static void block_row(void* p, int64_t i, double* scratch) {
     /* normalise first: n_j = h_j * r * gamma_j, then z = n W2 */
     for (int64_t j = 0; j < D; ++j) arow[j] = hrow[j] * r * c->gamma[j];
     w2 = c->W2;
-  } else {
-    /* reparameterised: the product runs on h itself (bf16-rounded in the round-points form) against
-     * W2' = diag(gamma) W2, and r scales the product's row afterwards */
-    for (int64_t j = 0; j < D; ++j) arow[j] = c->form == FORM_ROUNDPTS ? oracle_bf16_round(hrow[j]) : hrow[j];
+  } else if (c->form == FORM_FUSED) {
+    /* reparameterised: the product runs on h itself against W2' = diag(gamma) W2, and r scales the
+     * product's row afterwards */
+    for (int64_t j = 0; j < D; ++j) arow[j] = hrow[j];
     w2 = c->W2g;
+  } else {
+    /* round-points form: gamma broadcast onto h and rounded once to bf16, (h * gamma) W2, then r */
+    for (int64_t j = 0; j < D; ++j) arow[j] = oracle_bf16_round(hrow[j] * c->gamma[j]);
+    w2 = c->W2;
   }
   for (int64_t n = 0; n < N2; ++n) z[n] = 0.0;
   for (int64_t j = 0; j < D; ++j) {
@@ -304,17 +308,12 @@ static int run_block(int form, int64_t M, int64_t K1, int64_t D, int64_t N2, con
   if (!(eps >= 0.0)) return -1;
 
   double* W2g = NULL;
-  if (form != FORM_UNFUSED) {
-    /* W2'_jn = gamma_j * W2_jn.  The round-points form rounds the product to fp32 and then to bf16,
-     * the two roundings a bf16 kernel makes when it scales a bf16 weight by an fp32 gamma. */
+  if (form == FORM_FUSED) {
+    /* W2'_jn = gamma_j * W2_jn */
     W2g = (double*)malloc((size_t)D * (size_t)N2 * sizeof(double));
     if (!W2g) return -2;
     for (int64_t j = 0; j < D; ++j)
-      for (int64_t n = 0; n < N2; ++n) {
-        double v = gamma[j] * W2[j * N2 + n];
-        if (form == FORM_ROUNDPTS) v = oracle_bf16_round((double)(float)v);
-        W2g[j * N2 + n] = v;
-      }
+      for (int64_t n = 0; n < N2; ++n) W2g[j * N2 + n] = gamma[j] * W2[j * N2 + n];
   }
   block_ctx c = {form, K1, D, N2, X, W1, R, gamma, W2, W2g, eps, epi, out_h, out_r, out_y};
   int rc = for_each_row(M, nthreads, (size_t)(2 * D + N2), block_row, &c);

@@ -64,9 +64,9 @@ int oracle_block_fused_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const d
                            double eps, int epi, double* out_h, double* out_r, double* out_y,
                            int nthreads);
 
-/* Diagnostic: the reparameterised order with the storage roundings a bf16 implementation makes:
- * h is rounded to bf16 before the second product (r still comes from the unrounded h),
- * W2' = bf16(fp32(gamma_k * W2_kn)), and y is rounded to bf16.  Not the contract; a sharp bug detector. */
+/* Diagnostic: the reparameterised order with the storage roundings a bf16 implementation makes when it
+ * broadcasts gamma onto h in the first GEMM's epilogue: a_ij = bf16(h_ij * gamma_j) (r still comes from the
+ * unrounded h), z = r_i * (a W2), y = bf16(epi(z)).  Not the contract; a sharp bug detector. */
 int oracle_block_roundpts_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const double* X,
                               const double* W1, const double* R, const double* gamma, const double* W2,
                               double eps, int epi, double* out_h, double* out_r, double* out_y,

@@ -69,7 +69,7 @@ def _call(lib, a, fn="coda_block_fwd"):
     ("misaligned_W2", dict(W2=BASE + 4 * GB + 8), INVALID),
     ("M_zero", dict(M=0), INVALID),
     ("K1_negative", dict(K1=-64), INVALID),
-    ("K1_not_64", dict(K1=96), UNSUPPORTED),
+    ("K1_not_128", dict(K1=192), UNSUPPORTED),
     ("D_not_256", dict(D=320), UNSUPPORTED),
     ("N2_not_256", dict(N2=384), UNSUPPORTED),
     ("bad_epi", dict(epi=7), INVALID),
@@ -102,10 +102,10 @@ def test_unfused_hidden_limit(lib):
 
 
 def test_workspace_bytes(lib):
-    # part [D/256][M] + r [M], each 256-byte aligned; the unfused path adds two [M, D] bf16 matrices
-    assert lib.coda_workspace_bytes(8192, 2048, 2048, 16384, 1, 0, 0) == 8 * 8192 * 4 + 8192 * 4
+    # part [D/256][M] + r [M], each 256-byte aligned; then h*gamma [M, D] bf16 (fused) or T and n (unfused)
+    assert lib.coda_workspace_bytes(8192, 2048, 2048, 16384, 1, 0, 0) == 8 * 8192 * 4 + 8192 * 4 + 8192 * 2048 * 2
     assert lib.coda_workspace_bytes(8192, 2048, 2048, 16384, 1, 0, 1) == 8 * 8192 * 4 + 8192 * 4 + 2 * 8192 * 2048 * 2
-    assert lib.coda_workspace_bytes(5, 64, 256, 256, 0, 0, 0) == 256 + 256
+    assert lib.coda_workspace_bytes(5, 128, 256, 256, 0, 0, 0) == 256 + 256 + 5 * 256 * 2
     assert lib.coda_workspace_r_offset(8192, 2048) == 8 * 8192 * 4
     assert lib.coda_workspace_bytes(0, 64, 256, 256, 0, 0, 0) == 0
 
@@ -115,12 +115,15 @@ def test_step_entry_points_validate(lib):
     assert lib.coda_partial_rms_reduce(BASE, 0, 100, 2048, 1e-5, BASE + GB, None) == INVALID
     assert lib.coda_partial_rms_reduce(BASE, 8, 100, 2048, -1.0, BASE + GB, None) == INVALID
     assert lib.coda_partial_rms_reduce(BASE, 8, 100, 2048, 1e-5, BASE + 256, None) == ALIAS
-    assert lib.coda_gemm1_residual_partial_rms(BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB,
-                                               100, 96, 256, None) == UNSUPPORTED
-    assert lib.coda_gemm2_rowscale(BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, 2, BASE + 4 * GB,
-                                   100, 256, 512, None) == INVALID
-    assert lib.coda_gemm2_rowscale(BASE, BASE + GB, BASE + 2 * GB, BASE + 3 * GB, 0, BASE + 16,
-                                   100, 256, 512, None) == ALIAS
+    g1 = lambda **o: lib.coda_gemm1_residual_partial_rms(
+        o.get("X", BASE), BASE + GB, BASE + 2 * GB, BASE + 3 * GB, o.get("h", BASE + 4 * GB), o.get("hg", BASE + 5 * GB),
+        BASE + 6 * GB, 100, o.get("K1", 256), 256, None)
+    assert g1(K1=192) == UNSUPPORTED
+    assert g1(X=0) == INVALID
+    assert g1(hg=BASE + 4 * GB + 512) == ALIAS   # out_hg overlapping out_h
+    assert g1(hg=BASE + 2 * GB) == ALIAS         # out_hg on R (only out_h may alias R)
+    assert lib.coda_gemm2_rowscale(BASE, BASE + GB, BASE + 2 * GB, 2, BASE + 4 * GB, 100, 256, 512, None) == INVALID
+    assert lib.coda_gemm2_rowscale(BASE, BASE + GB, BASE + 2 * GB, 0, BASE + 16, 100, 256, 512, None) == ALIAS
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")

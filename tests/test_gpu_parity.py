@@ -36,10 +36,10 @@ def _need_gpu():
 SMALL = [
     WORKLOADS["tiny"],
     Workload("ragged_swiglu", M=300, K1=512, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, x_std=1.0, seed=1),
-    Workload("ragged_identity", M=300, K1=320, D=768, N2=768, epi=EPI_IDENTITY, eps=1e-5, seed=2),
-    Workload("one_row", M=1, K1=64, D=256, N2=256, epi=EPI_SWIGLU, eps=1e-6, seed=3),
+    Workload("ragged_identity", M=300, K1=384, D=768, N2=768, epi=EPI_IDENTITY, eps=1e-5, seed=2),
+    Workload("one_row", M=1, K1=128, D=256, N2=256, epi=EPI_SWIGLU, eps=1e-6, seed=3),
     Workload("many_tiles", M=777, K1=1024, D=1024, N2=2048, epi=EPI_SWIGLU, eps=1e-5, seed=4),
-    Workload("k64_tail", M=257, K1=64, D=256, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=5),
+    Workload("k128_tail", M=257, K1=128, D=256, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=5),
 ]
 
 
@@ -95,11 +95,14 @@ def test_steps_one_by_one():
     d = DeviceInputs(inp)
     T = wl.D // 256
     h = torch.full((wl.M, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    hg = torch.full((wl.M, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
     part = torch.full((T, wl.M), float("nan"), dtype=torch.float32, device="cuda")
-    cb.coda_gemm1_residual_partial_rms(d.X, d.W1, d.R, h, part)
+    cb.coda_gemm1_residual_partial_rms(d.X, d.W1, d.R, d.gamma, h, hg, part)
     torch.cuda.synchronize()
     oh = oracle.gemm_residual(f64(inp.X), f64(inp.W1), f64(inp.R))
     check_h(f64(h), oh)
+    # h * gamma with the same rule as h (gamma broadcast along the rows)
+    check_h(f64(hg), oh * f64(inp.gamma)[None, :])
     opart = np.stack([np.sum(oh[:, 256 * t: 256 * (t + 1)] ** 2, axis=1) for t in range(T)])
     np.testing.assert_allclose(f64(part), opart, rtol=1e-4)
     # step 2 on the GPU's own partials, against the oracle's reduction of the same partials
@@ -107,11 +110,11 @@ def test_steps_one_by_one():
     cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r)
     torch.cuda.synchronize()
     np.testing.assert_allclose(f64(r), oracle.rms_from_partials(f64(part), wl.D, wl.eps), rtol=3e-7)
-    # step 3 on the GPU's h and r: y = epi(r * (h diag(gamma) W2)) against the oracle on the same h
+    # step 3 on the GPU's hg and r: y = epi(r * (hg W2)) against the oracle's silu on the same operands
     y = torch.full((wl.M, wl.n_out), float("nan"), dtype=torch.bfloat16, device="cuda")
-    cb.coda_gemm2_rowscale(h, d.W2, d.gamma, r, wl.epi, y)
+    cb.coda_gemm2_rowscale(hg, d.W2, r, wl.epi, y)
     torch.cuda.synchronize()
-    z = (f64(h) @ (f64(inp.gamma)[:, None] * f64(inp.W2))) * f64(r)[:, None]
+    z = (f64(hg) @ f64(inp.W2)) * f64(r)[:, None]
     half = wl.N2 // 2
     oy = np.array([[oracle.silu(v) for v in row] for row in z[:, :half]]) * z[:, half:]
     check_y(f64(y), oy)
