@@ -24,7 +24,7 @@ MUTANTS = [
     ("row_scale_twice", "z[n] *= r;", "z[n] *= r * r;"),
     ("gamma_dropped", "arow[j] = hrow[j] * r * c->gamma[j];", "arow[j] = hrow[j] * r;"),
     ("mean_denominator", "return 1.0 / sqrt(ss / (double)D + eps);", "return 1.0 / sqrt(ss / (double)(D - 1) + eps);"),
-    ("gamma_wrong_index", "double v = gamma[j] * W2[j * N2 + n];", "double v = gamma[n % D] * W2[j * N2 + n];"),
+    ("gamma_wrong_index", "W2g[j * N2 + n] = gamma[j] * W2[j * N2 + n];", "W2g[j * N2 + n] = gamma[n % D] * W2[j * N2 + n];"),
     ("silu_sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
     ("e4m3_subnormal", "v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
 ]
