@@ -7,5 +7,6 @@ library is opened on first use and a missing library raises instead of falling b
 from . import inputs  # noqa: F401
 from .binding import (  # noqa: F401
     EPI_IDENTITY, EPI_SWIGLU, CodaError, alloc_workspace, coda_abi_version, coda_block_fwd, coda_block_unfused,
+    coda_block_fwd_fp8, coda_block_unfused_fp8,
     coda_gemm1_residual_partial_rms, coda_gemm2_rowscale, coda_partial_rms_reduce, coda_workspace_bytes,
     coda_workspace_r_offset, load, workspace_r)

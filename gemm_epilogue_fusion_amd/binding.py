@@ -25,7 +25,8 @@ STATUS = {0: "CODA_OK", 1: "CODA_ERR_INVALID_ARG", 2: "CODA_ERR_UNSUPPORTED", 3:
 
 # every symbol include/coda.h declares
 EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_workspace_bytes",
-           "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused",
+           "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused", "coda_block_fwd_fp8",
+           "coda_block_unfused_fp8",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale")
 
 
@@ -56,6 +57,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     block = [vp, vp, vp, vp, vp, f32, i32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
     for name in ("coda_block_fwd", "coda_block_unfused"):
         getattr(lib, name).argtypes = block
+        getattr(lib, name).restype = i32
+    block8 = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+    for name in ("coda_block_fwd_fp8", "coda_block_unfused_fp8"):
+        getattr(lib, name).argtypes = block8
         getattr(lib, name).restype = i32
     lib.coda_gemm1_residual_partial_rms.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
     lib.coda_gemm1_residual_partial_rms.restype = i32
@@ -105,8 +110,8 @@ def coda_workspace_r_offset(M: int, D: int) -> int:
     return load().coda_workspace_r_offset(M, D)
 
 
-def alloc_workspace(M: int, K1: int, D: int, N2: int, epi_kind: int, unfused: int = 0, device="cuda"):
-    n = coda_workspace_bytes(M, K1, D, N2, epi_kind, 0, unfused)
+def alloc_workspace(M: int, K1: int, D: int, N2: int, epi_kind: int, unfused: int = 0, device="cuda", fp8: int = 0):
+    n = coda_workspace_bytes(M, K1, D, N2, epi_kind, fp8, unfused)
     if n == 0:
         raise ValueError("no workspace size for these dimensions")
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -136,6 +141,38 @@ def coda_block_fwd(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y,
 def coda_block_unfused(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y, workspace, stream=None):
     """Unfused three-kernel baseline with the same outputs."""
     _block("coda_block_unfused", X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspace, stream)
+
+
+def _block_fp8(name: str, Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, workspace, stream):
+    M, K1 = Xq.shape
+    D = W1q.shape[1]
+    N2 = W2q.shape[1]
+    ny = N2 if epi_kind == EPI_IDENTITY else N2 // 2
+    e4 = torch.float8_e4m3fn
+    args = (_dev(Xq, "Xq", e4, (M, K1)), _dev(sx, "sx", torch.float32, (M,)),
+            _dev(W1q, "W1q", e4, (K1, D)), _dev(sw1, "sw1", torch.float32, (D,)),
+            _dev(R, "R", torch.bfloat16, (M, D)), _dev(gamma, "gamma", torch.float32, (D,)),
+            _dev(W2q, "W2q", e4, (D, N2)), _dev(sw2, "sw2", torch.float32, (N2,)))
+    h = _dev(out_h, "out_h", torch.bfloat16, (M, D))
+    y = _dev(out_y, "out_y", torch.bfloat16, (M, ny))
+    ws = _dev(workspace, "workspace", torch.uint8)
+    st = getattr(load(), name)(*args, float(eps), int(epi_kind), h, y, M, K1, D, N2, ws, workspace.numel(),
+                               _stream(stream))
+    _check(st, name)
+
+
+def coda_block_fwd_fp8(Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps: float, epi_kind: int, out_h, out_y, workspace,
+                       stream=None):
+    """Fused block with e4m3 operands (dequantised value = code * scale; sx per row, sw1 / sw2 per column)."""
+    _block_fp8("coda_block_fwd_fp8", Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, workspace,
+               stream)
+
+
+def coda_block_unfused_fp8(Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps: float, epi_kind: int, out_h, out_y, workspace,
+                           stream=None):
+    """Unfused three-kernel baseline with e4m3 operands."""
+    _block_fp8("coda_block_unfused_fp8", Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y,
+               workspace, stream)
 
 
 def coda_gemm1_residual_partial_rms(X, W1, R, gamma, out_h, out_hg, part, stream=None):

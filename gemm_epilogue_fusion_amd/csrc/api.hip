@@ -94,62 +94,84 @@ int check_alias(const Range* in, int nin, const Range* out, int nout, const void
 }
 
 struct Workspace {
-  float* part;
-  float* r;
-  uint16_t* hg;  // fused: h * gamma, the second GEMM's A operand
-  uint16_t* t;   // unfused: T = X W1
-  uint16_t* n;   // unfused: normalised rows
+  float* part;    // [D/256][M] partial sums of squares
+  float* r;       // [M] row scale
+  uint16_t* hg;   // fused: h * gamma [M,D] bf16, the second GEMM's A operand (bf16) or its quantiser input (fp8)
+  uint16_t* t;    // unfused: T = X W1 [M,D] bf16
+  uint16_t* n;    // unfused bf16: normalised rows [M,D]
+  uint8_t* q;     // fp8: the second GEMM's e4m3 A operand [M,D] (fused: h*gamma quantised; unfused: n quantised)
+  float* qs;      // fp8: its per-row scale [M]
+  float* rs2;     // fp8 fused: the second GEMM's epilogue row scale qs * r [M]
 };
 
 size_t ws_part_bytes(int64_t M, int64_t D) { return align256((size_t)(D / 256) * (size_t)M * 4); }
-size_t ws_r_bytes(int64_t M) { return align256((size_t)M * 4); }
-size_t ws_mat_bytes(int64_t M, int64_t D) { return align256((size_t)M * (size_t)D * 2); }
+size_t ws_vec_bytes(int64_t M) { return align256((size_t)M * 4); }
+size_t ws_mat_bytes(int64_t M, int64_t D, int elem) { return align256((size_t)M * (size_t)D * elem); }
 
-size_t ws_bytes(int64_t M, int64_t D, int unfused) {
-  return ws_part_bytes(M, D) + ws_r_bytes(M) + (unfused ? 2 : 1) * ws_mat_bytes(M, D);
-}
-
-Workspace carve(void* ws, int64_t M, int64_t D, int unfused) {
-  char* p = (char*)ws;
-  Workspace w{};
-  w.part = (float*)p;
-  p += ws_part_bytes(M, D);
-  w.r = (float*)p;
-  p += ws_r_bytes(M);
+// Lays the workspace out (or, with ws == nullptr, only measures it).
+size_t carve(void* ws, int64_t M, int64_t D, int fp8, int unfused, Workspace* w) {
+  char* base = (char*)ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  Workspace x{};
+  x.part = (float*)take(ws_part_bytes(M, D));
+  x.r = (float*)take(ws_vec_bytes(M));
   if (unfused) {
-    w.t = (uint16_t*)p;
-    p += ws_mat_bytes(M, D);
-    w.n = (uint16_t*)p;
+    x.t = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+    if (fp8) {
+      x.q = (uint8_t*)take(ws_mat_bytes(M, D, 1));
+      x.qs = (float*)take(ws_vec_bytes(M));
+    } else {
+      x.n = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+    }
   } else {
-    w.hg = (uint16_t*)p;
+    x.hg = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+    if (fp8) {
+      x.q = (uint8_t*)take(ws_mat_bytes(M, D, 1));
+      x.qs = (float*)take(ws_vec_bytes(M));
+      x.rs2 = (float*)take(ws_vec_bytes(M));
+    }
   }
-  return w;
+  if (w) *w = x;
+  return off;
 }
 
-// Validation shared by coda_block_fwd and coda_block_unfused.
-int validate_block(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
-                   int epi, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2,
-                   void* workspace, size_t workspace_bytes, int unfused) {
+size_t ws_bytes(int64_t M, int64_t D, int fp8, int unfused) { return carve(nullptr, M, D, fp8, unfused, nullptr); }
+
+// Validation shared by the block entry points.  fp8: X, W1, W2 are e4m3 bytes and sx, sw1, sw2 their
+// scales (ignored, and may be NULL, for bf16).
+int validate_block(const void* X, const float* sx, const void* W1, const float* sw1, const void* R,
+                   const float* gamma, const void* W2, const float* sw2, float eps, int epi, void* out_h, void* out_y,
+                   int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace, size_t workspace_bytes, int fp8,
+                   int unfused) {
   int s;
   if ((s = check_ptr(X, "X")) || (s = check_ptr(W1, "W1")) || (s = check_ptr(R, "R")) ||
       (s = check_ptr(gamma, "gamma")) || (s = check_ptr(W2, "W2")) || (s = check_ptr(out_h, "out_h")) ||
       (s = check_ptr(out_y, "out_y")))
     return s;
+  if (fp8 && ((s = check_ptr(sx, "sx")) || (s = check_ptr(sw1, "sw1")) || (s = check_ptr(sw2, "sw2")))) return s;
   if ((s = check_dims(M, K1, D, N2))) return s;
+  if (fp8 && K1 % 256) return fail(CODA_ERR_UNSUPPORTED, "fp8: K1=%lld is not a multiple of 256", (long long)K1);
   if ((s = check_epi_eps(epi, eps))) return s;
   if (unfused && D > 8192) return fail(CODA_ERR_UNSUPPORTED, "unfused path supports D <= 8192");
-  const size_t need = ws_bytes(M, D, unfused);
+  const size_t need = ws_bytes(M, D, fp8, unfused);
   if (!workspace) return fail(CODA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if ((uintptr_t)workspace & 255) return fail(CODA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (workspace_bytes < need)
     return fail(CODA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   const int64_t ny = epi == CODA_EPI_SWIGLU ? N2 / 2 : N2;
-  const Range in[5] = {rng("X", X, (size_t)(M * K1 * 2)), rng("W1", W1, (size_t)(K1 * D * 2)),
+  const size_t el = fp8 ? 1 : 2;
+  const Range in[8] = {rng("X", X, (size_t)(M * K1) * el), rng("W1", W1, (size_t)(K1 * D) * el),
                        rng("R", R, (size_t)(M * D * 2)), rng("gamma", gamma, (size_t)D * 4),
-                       rng("W2", W2, (size_t)(D * N2 * 2))};
+                       rng("W2", W2, (size_t)(D * N2) * el), rng("sx", sx, fp8 ? (size_t)M * 4 : 0),
+                       rng("sw1", sw1, fp8 ? (size_t)D * 4 : 0), rng("sw2", sw2, fp8 ? (size_t)N2 * 4 : 0)};
   const Range out[3] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("out_y", out_y, (size_t)(M * ny * 2)),
                         rng("workspace", workspace, need)};
-  return check_alias(in, 5, out, 3, out_h, R);
+  return check_alias(in, 8, out, 3, out_h, R);
 }
 
 }  // namespace
@@ -177,8 +199,8 @@ size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int ep
   (void)K1;
   (void)N2;
   (void)epi_kind;
-  if (fp8 || M < 1 || D < 256) return 0;
-  return ws_bytes(M, D, unfused);
+  if (M < 1 || D < 256 || M > kMaxDim || D > kMaxDim) return 0;
+  return ws_bytes(M, D, fp8 ? 1 : 0, unfused ? 1 : 0);
 }
 
 size_t coda_workspace_r_offset(int64_t M, int64_t D) { return ws_part_bytes(M, D); }
@@ -187,11 +209,12 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
                    int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2,
                    void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    int s = validate_block(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
-                           workspace_bytes, 0);
+    int s = validate_block(X, nullptr, W1, nullptr, R, gamma, W2, nullptr, eps, epi_kind, out_h, out_y, M, K1, D, N2,
+                           workspace, workspace_bytes, 0, 0);
     if (s) return s;
     hipStream_t st = (hipStream_t)stream;
-    Workspace w = carve(workspace, M, D, 0);
+    Workspace w;
+    carve(workspace, M, D, 0, 0, &w);
     if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
                                                    gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
                                                    st),
@@ -212,11 +235,12 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
                        float eps, int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D,
                        int64_t N2, void* workspace, size_t workspace_bytes, void* stream) {
   try {
-    int s = validate_block(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
-                           workspace_bytes, 1);
+    int s = validate_block(X, nullptr, W1, nullptr, R, gamma, W2, nullptr, eps, epi_kind, out_h, out_y, M, K1, D, N2,
+                           workspace, workspace_bytes, 0, 1);
     if (s) return s;
     hipStream_t st = (hipStream_t)stream;
-    Workspace w = carve(workspace, M, D, 1);
+    Workspace w;
+    carve(workspace, M, D, 0, 1, &w);
     if ((s = hip_check(coda::launch_gemm_store((const uint16_t*)X, (const uint16_t*)W1, w.t, (int)M, (int)K1,
                                                (int)D, st),
                        "gemm_store launch")))
@@ -228,6 +252,61 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
     return hip_check(coda::launch_gemm2_rowscale(w.n, (const uint16_t*)W2, nullptr, epi_kind == CODA_EPI_SWIGLU,
                                                  (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
                      "unfused gemm2 launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
+                       const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
+                       void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  try {
+    int s = validate_block(Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
+                           workspace_bytes, 1, 0);
+    if (s) return s;
+    hipStream_t st = (hipStream_t)stream;
+    Workspace w;
+    carve(workspace, M, D, 1, 0, &w);
+    if ((s = hip_check(coda::launch_gemm1_res_prms_fp8((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1,
+                                                       (const uint16_t*)R, gamma, (uint16_t*)out_h, w.hg, w.part,
+                                                       (int)M, (int)K1, (int)D, st),
+                       "fp8 gemm1_res_prms launch")))
+      return s;
+    if ((s = hip_check(coda::launch_prms_reduce_quant(w.part, (int)(D / 256), (int)M, (int)D, eps, w.hg, w.q, w.r,
+                                                      w.qs, w.rs2, st),
+                       "prms_reduce_quant launch")))
+      return s;
+    return hip_check(coda::launch_gemm2_rowscale_fp8(w.q, (const uint8_t*)W2q, w.rs2, sw2, epi_kind == CODA_EPI_SWIGLU,
+                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                     "fp8 gemm2_rowscale launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_block_unfused_fp8(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
+                           const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
+                           void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  try {
+    int s = validate_block(Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
+                           workspace_bytes, 1, 1);
+    if (s) return s;
+    hipStream_t st = (hipStream_t)stream;
+    Workspace w;
+    carve(workspace, M, D, 1, 1, &w);
+    if ((s = hip_check(coda::launch_gemm_store_fp8((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1, w.t, (int)M,
+                                                   (int)K1, (int)D, st),
+                       "fp8 gemm_store launch")))
+      return s;
+    if ((s = hip_check(coda::launch_add_rmsnorm_quant(w.t, (const uint16_t*)R, gamma, (uint16_t*)out_h, w.q, w.r, w.qs,
+                                                      (int)M, (int)D, eps, st),
+                       "add_rmsnorm_quant launch")))
+      return s;
+    return hip_check(coda::launch_gemm2_rowscale_fp8(w.q, (const uint8_t*)W2q, w.qs, sw2, epi_kind == CODA_EPI_SWIGLU,
+                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                     "unfused fp8 gemm2 launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }

@@ -251,6 +251,169 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
   step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
 }
 
+// ======================================================================================================
+// fp8 (OCP e4m3fn) mainloop: same tile, ring and barrier structure; K advances 64 values (64 bytes) per
+// stage, so the A stage has the bf16 A stage's byte layout (256 rows x 64 B).  The B stage is 64 rows x
+// 256 B (chunk c of row k at slot c ^ 2 (k % 8)) and is read K-contiguous with ds_read_b64_tr_b8.  One
+// v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 block and stage (lane l holds A/B bytes k = 32 (l/32) .. +31).
+//   ds_read_b64_tr_b8: inside each group of 16 lanes, byte e of lane i is byte i%8 of the 8 bytes addressed
+//   by lane 2e + i/8 of the group (verified on the device).
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+constexpr int BK8 = 64;                         // e4m3 values of K per stage
+constexpr int K8_MULTIPLE = BK8 * NSTAGE;       // K must be a multiple of this
+
+__device__ __forceinline__ int b8_off(int k, int c) { return k * 256 + ((c ^ ((k & 7) << 1)) << 4); }
+
+__device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
+}
+
+struct Frags8 {
+  i32x8 a[4];
+  i32x8 b[NB];
+};
+
+struct LaneOffs8 {
+  int a;      // A fragment (rows mb*32 add 2 KiB each; the second 16 bytes sit at the next slot)
+  int a2;
+  int b[NB];  // B fragment, n-block nb (read r = 0..3 adds 2 KiB each)
+};
+
+__device__ __forceinline__ void lane_offsets8(int wm, int wn, int lane, LaneOffs8& o) {
+  const int q = lane >> 4, j = lane & 15;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    // lane j of 16-lane group q points at row k0 + j/2, bytes n0 + 8 (j%2) .. +7; after the transposing
+    // read lane i of the group holds rows k0..k0+7 of column n0 + i
+    const int n0 = wn * (32 * NB) + nb * 32 + 16 * (q & 1);
+    const int krow = 32 * (q >> 1) + (j >> 1);
+    o.b[nb] = A_BYTES + b8_off(krow, n0 >> 4) + ((j & 1) << 3);
+  }
+  const int m = wm * 128 + (lane & 31);
+  o.a = a_off(m, 2 * (lane >> 5));
+  o.a2 = a_off(m, 2 * (lane >> 5) + 1);
+}
+
+__device__ __forceinline__ void read_frags8(const char* st, const LaneOffs8& o, Frags8& f) {
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const char* p = st + o.b[nb];
+    const i32x2 r0 = lds_read_tr8(p);
+    const i32x2 r1 = lds_read_tr8(p + 8 * 256);
+    const i32x2 r2 = lds_read_tr8(p + 16 * 256);
+    const i32x2 r3 = lds_read_tr8(p + 24 * 256);
+    f.b[nb] = (i32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const u32x4 lo = *(const u32x4*)(st + o.a + mb * 32 * 64);
+    const u32x4 hi = *(const u32x4*)(st + o.a2 + mb * 32 * 64);
+    f.a[mb] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+}
+
+__device__ __forceinline__ void mma8(const Frags8& f, f32x16 (&acc)[4][NB]) {
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      // operand formats 0 = e4m3 (cbsz for the first operand, blgp for the second); E8M0 scales 127 = 1.0
+      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0, 127, 0, 127);
+}
+
+// acc = A[m0:m0+256, :] * B[:, tile columns], e4m3 operands, fp32 accumulation (K % K8_MULTIPLE == 0).
+//   A: [M,K] bytes, row stride lda bytes; B: [K,*] bytes, row stride ldb bytes; bcol(c) = global column of
+//   the tile's 16-column chunk c (0..15).
+template <class BCol>
+__device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A, int64_t lda, int M, int m0,
+                                                  const uint8_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
+                                                  char* smem, f32x16 (&acc)[4][NB]) {
+  constexpr int LPW = 16 / NWAVES;
+  constexpr int PER = 2 * LPW;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = (f32x16){};
+
+  // direct-load unit q: A rows 16q .. 16q+15 (as the bf16 A stage); B rows 4q .. 4q+3 (lane -> row
+  // 4q + lane/16, slot lane%16)
+  const uint8_t* aptr[LPW];
+  const uint8_t* bptr[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int q = LPW * wave + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    int row = m0 + r;
+    row = row < M ? row : M - 1;
+    aptr[i] = A + (int64_t)row * lda + 16 * c;
+    const int kr = 4 * q + (lane >> 4);
+    const int cb = (lane & 15) ^ ((kr & 7) << 1);
+    bptr[i] = B + (int64_t)kr * ldb + bcol(cb);
+  }
+  LaneOffs8 lo;
+  lane_offsets8(wm, wn, lane, lo);
+  const int nk = K / BK8;
+
+  auto issue = [&](int kt, int stage) {
+    char* st = smem + stage * STAGE_BYTES;
+    const int k0 = kt * BK8;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) g2lds16(aptr[i] + k0, st + (LPW * wave + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + (int64_t)k0 * ldb, st + A_BYTES + (LPW * wave + i) * 1024);
+  };
+
+  Frags8 f;
+  // one K step on stage U: the fragments of tile kt are in f on entry
+  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c) {
+    constexpr int U = decltype(U_c)::value;
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr int WAIT = decltype(wait_c)::value;
+    if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
+    mma8(f, acc);
+    // keep the step's shape (MFMAs, barrier, next fragments into the same registers): letting the
+    // scheduler overlap steps needs a second fragment set, which does not fit next to the accumulators
+    __builtin_amdgcn_sched_barrier(0);
+    if (WAIT >= 0) {
+      wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
+      read_frags8(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, lo, f);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using Yes = std::true_type;
+  using No = std::false_type;
+  using WaitFull = std::integral_constant<int, 2 * PER>;
+
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
+  wait_barrier<2 * PER>();
+  read_frags8(smem, lo, f);
+
+  const int nblk = nk / NSTAGE;
+  for (int bi = 0; bi < nblk - 1; ++bi) {
+    const int kt = bi * NSTAGE;
+    step(kt + 0, S0{}, Yes{}, WaitFull{});
+    step(kt + 1, S1{}, Yes{}, WaitFull{});
+    step(kt + 2, S2{}, Yes{}, WaitFull{});
+    step(kt + 3, S3{}, Yes{}, WaitFull{});
+  }
+  const int kt = (nblk - 1) * NSTAGE;
+  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{});
+  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER>{});
+  step(kt + 2, S2{}, No{}, std::integral_constant<int, 0>{});
+  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
+}
+
 // Maps the linear workgroup id to a (row tile, column tile) pair.
 // Workgroups are dealt to the 8 XCDs round-robin (id % 8), each XCD with its own L2.  The id is first
 // remapped so that XCD x receives a contiguous range of the tile order, then tiles are ordered in groups of

@@ -30,34 +30,38 @@ __device__ __forceinline__ float silu_f32(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Global column of a tile's 8-column chunk c (0..31) when the tile's 256 accumulator columns are one
-// contiguous range starting at n0.
+// Global column of the tile's column chunk c when the tile's 256 accumulator columns are one contiguous
+// range starting at n0 (W columns per chunk: 8 for bf16, 16 for e4m3).
+template <int W>
 struct ContiguousCols {
   int64_t n0;
-  __device__ int64_t operator()(int c) const { return n0 + 8 * c; }
+  __device__ int64_t operator()(int c) const { return n0 + W * c; }
 };
 // SwiGLU tiles: wave column group w (64 accumulator columns) holds 32 gate columns c0 + 32 w .. +32 followed
 // by the matching 32 up columns half + c0 + 32 w .. +32, so gate and up of one output share a lane.
+template <int W>
 struct GateUpCols {
   int64_t c0, half;
   __device__ int64_t operator()(int c) const {
-    const int nl = 8 * c, w = nl >> 6, within = nl & 63;
+    const int nl = W * c, w = nl >> 6, within = nl & 63;
     return within < 32 ? c0 + 32 * w + within : half + c0 + 32 * w + (within - 32);
   }
 };
 
-// One GEMM with a programmable epilogue.
-//   A [M,K] bf16 (row stride K), B [K,Nb] bf16 (row stride Nb); the accumulator tile covers 256 columns.
-//   MODE_RES_PRMS:  out [M,Nb] = bf16(acc + R); out2 [M,Nb] = bf16((acc + R) * gamma[n]);
-//                   part[tn][m] = sum over the tile's columns of (acc + R)^2
-//   MODE_STORE:     out [M,Nb] = bf16(acc)
-//   MODE_ROWSCALE:  out [M,Nb] = bf16(rs[m] * acc)            (rs == nullptr: scale 1)
+// One GEMM with a programmable epilogue.  The accumulator tile covers 256 columns of B; A [M,K] and B
+// [K,Nb] are bf16 (FP8 = false) or e4m3 bytes (FP8 = true), row-major.  In the epilogue the accumulator is
+// first multiplied by rowsc[m] * colsc[n] where those are given (dequantisation scales and / or the row
+// scale r), giving v:
+//   MODE_RES_PRMS:  out [M,Nb] = bf16(v + R); out2 [M,Nb] = bf16((v + R) * gamma[n]);
+//                   part[tn][m] = sum over the tile's columns of (v + R)^2
+//   MODE_STORE:     out [M,Nb] = bf16(v)
+//   MODE_ROWSCALE:  out [M,Nb] = bf16(v)
 //   MODE_ROWSCALE_SWIGLU: the tile's columns are 128 gate columns [tn*128, +128) and the matching 128 up
-//                   columns [Nb/2 + tn*128, +128); out [M,Nb/2] = bf16(silu(rs*gate) * (rs*up))
-template <int MODE>
+//                   columns [Nb/2 + tn*128, +128); out [M,Nb/2] = bf16(silu(v_gate) * v_up)
+template <int MODE, bool FP8>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, const float* __restrict__ gamma,
-    const uint16_t* R, const float* __restrict__ rs, uint16_t* out, uint16_t* __restrict__ out2,
+    const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
+    const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
     float* __restrict__ part, int M, int K, int Nb, int group_m) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const int tiles_m = (M + BM - 1) / BM;
@@ -67,10 +71,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   const int m0 = tm * BM;
 
   f32x16 acc[4][NB];
-  if (MODE == MODE_ROWSCALE_SWIGLU)
-    gemm_mainloop(A, K, M, m0, B, Nb, GateUpCols{(int64_t)tn * 128, Nb / 2}, K, smem, acc);
-  else
-    gemm_mainloop(A, K, M, m0, B, Nb, ContiguousCols{(int64_t)tn * BN}, K, smem, acc);
+  if (FP8) {
+    const uint8_t* A8 = (const uint8_t*)A;
+    const uint8_t* B8 = (const uint8_t*)B;
+    if (MODE == MODE_ROWSCALE_SWIGLU)
+      gemm_mainloop_fp8(A8, K, M, m0, B8, Nb, GateUpCols<16>{(int64_t)tn * 128, Nb / 2}, K, smem, acc);
+    else
+      gemm_mainloop_fp8(A8, K, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc);
+  } else {
+    const uint16_t* A16 = (const uint16_t*)A;
+    const uint16_t* B16 = (const uint16_t*)B;
+    if (MODE == MODE_ROWSCALE_SWIGLU)
+      gemm_mainloop(A16, K, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, K, smem, acc);
+    else
+      gemm_mainloop(A16, K, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc);
+  }
+
+  // Materialise the accumulators here: otherwise the compiler may sink the last MFMAs into the epilogue's
+  // row-masked store blocks, which keeps every operand fragment alive into the epilogue.
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(acc[mb][nb]));
 
   // ---- epilogue: the accumulator tile is still in registers ----
   // acc[mb][nb][r] is row m0 + 128 wm + 32 mb + lane%32, column 64 wn + 32 nb + 8 (r/4) + 4 (lane/32) + r%4
@@ -80,43 +102,52 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   const int wm = wave & 1, wn = wave >> 1;
   const int half = lane >> 5;
 
-  if (MODE == MODE_RES_PRMS || MODE == MODE_STORE) {
+  // per-row scales of this lane's four rows (rows past M read row M-1; they are never stored)
+  float rsv[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+    rsv[mb] = rowsc ? rowsc[m < M ? m : M - 1] : 1.0f;
+  }
+
+  if (MODE == MODE_RES_PRMS || MODE == MODE_STORE || MODE == MODE_ROWSCALE) {
     const int n_base = tn * BN + wn * 64 + 4 * half;
-    // the tile's residual values first, as one batch of loads (rows past M read row M-1, never stored)
-    u32x2 rr[4][NB][4];
-    if (MODE == MODE_RES_PRMS) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-        const int mr = m < M ? m : M - 1;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) rr[mb][nb][gq] = *(const u32x2*)(R + (int64_t)mr * Nb + n_base + nb * 32 + 8 * gq);
-      }
-    }
-    // gamma of this lane's columns: the same 4-column groups for every row
+    // gamma of this lane's 4-column groups (the same for every row)
     f32x4 gv[NB][4];
-    if (MODE == MODE_RES_PRMS) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) gv[nb][gq] = *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq);
-    }
+      for (int gq = 0; gq < 4; ++gq)
+        gv[nb][gq] = MODE == MODE_RES_PRMS ? *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
     float ss[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+      const int mr = m < M ? m : M - 1;
+      // this row block's residual values and column scales as one batch of loads (the column scales are
+      // re-read per row block from L1 rather than held: registers are the scarce resource here)
+      u32x2 rr[NB][4];
+      f32x4 cv[NB][4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int n = n_base + nb * 32 + 8 * gq;
+          if (MODE == MODE_RES_PRMS) rr[nb][gq] = *(const u32x2*)(R + (int64_t)mr * Nb + n);
+          cv[nb][gq] = colsc ? *(const f32x4*)(colsc + n) : (f32x4){1.f, 1.f, 1.f, 1.f};
+        }
       float s = 0.0f;
       u32x2 hv[NB][4], gvv[NB][4];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          float v0 = acc[mb][nb][4 * gq + 0], v1 = acc[mb][nb][4 * gq + 1];
-          float v2 = acc[mb][nb][4 * gq + 2], v3 = acc[mb][nb][4 * gq + 3];
+          const f32x4 c = cv[nb][gq];
+          const float sc = rsv[mb];
+          float v0 = acc[mb][nb][4 * gq + 0] * sc * c[0], v1 = acc[mb][nb][4 * gq + 1] * sc * c[1];
+          float v2 = acc[mb][nb][4 * gq + 2] * sc * c[2], v3 = acc[mb][nb][4 * gq + 3] * sc * c[3];
           if (MODE == MODE_RES_PRMS) {
-            const u32x2 r2 = rr[mb][nb][gq];
+            const u32x2 r2 = rr[nb][gq];
             v0 += bf16_lo(r2[0]);
             v1 += bf16_hi(r2[0]);
             v2 += bf16_lo(r2[1]);
@@ -163,51 +194,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         }
       }
     }
-  } else if (MODE == MODE_ROWSCALE) {
-    const int n_base = tn * BN + wn * 64 + 4 * half;
-    float scs[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-      scs[mb] = rs ? rs[m < M ? m : M - 1] : 1.0f;
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-      if (m >= M) continue;
-      const float sc = scs[mb];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n_base + nb * 32 + 8 * gq;
-          const f32x16& a = acc[mb][nb];
-          *(u32x2*)(out + (int64_t)m * Nb + n) =
-              (u32x2){pack_bf16(sc * a[4 * gq + 0], sc * a[4 * gq + 1]), pack_bf16(sc * a[4 * gq + 2], sc * a[4 * gq + 3])};
-        }
-    }
   } else {  // MODE_ROWSCALE_SWIGLU: accumulator block 0 holds gate columns, block 1 the matching up columns
     const int ny = Nb / 2;
     const int c_base = tn * 128 + wn * 32 + 4 * half;
-    float scs[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-      scs[mb] = rs ? rs[m < M ? m : M - 1] : 1.0f;
-    }
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
       if (m >= M) continue;
-      const float sc = scs[mb];
+      const float sc = rsv[mb];
+      f32x4 cg[4], cu[4];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        cg[gq] = colsc ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+        cu[gq] = colsc ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+      }
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int c = c_base + 8 * gq;
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float gate = sc * acc[mb][0][4 * gq + e];
-          const float up = sc * acc[mb][1][4 * gq + e];
+          const float gate = acc[mb][0][4 * gq + e] * sc * cg[gq][e];
+          const float up = acc[mb][1][4 * gq + e] * sc * cu[gq][e];
           y[e] = silu_f32(gate) * up;
         }
         *(u32x2*)(out + (int64_t)m * ny + c) = (u32x2){pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
@@ -226,12 +234,76 @@ __global__ __launch_bounds__(256) void prms_reduce_kernel(const float* __restric
   r[i] = 1.0f / sqrtf(s / D + eps);
 }
 
+// ---- e4m3 quantisation ----------------------------------------------------------------------------------
+constexpr float E4M3_MAX = 448.0f;
+
+// Four fp32 values -> four OCP e4m3fn bytes, round to nearest even (v_cvt_pk_fp8_f32; gfx950 uses the OCP
+// encoding).  Values are clamped to +-448 first, so the conversion never sees an out-of-range input.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -E4M3_MAX), E4M3_MAX);
+  b = fminf(fmaxf(b, -E4M3_MAX), E4M3_MAX);
+  c = fminf(fmaxf(c, -E4M3_MAX), E4M3_MAX);
+  d = fminf(fmaxf(d, -E4M3_MAX), E4M3_MAX);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// wave-wide maximum (butterfly over the 64 lanes; every lane ends with the same value)
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// K2 for e4m3 operands: one wave per row i.
+//   r[i]    = 1 / sqrt((sum_t part[t][i]) / D + eps)     (t summed in order, as in prms_reduce_kernel)
+//   s_a[i]  = amax_j |hg[i][j]| / 448  (1 for an all-zero row)
+//   hq[i][j] = e4m3(hg[i][j] / s_a[i])                     (the second GEMM's A operand)
+//   rs2[i]  = s_a[i] * r[i]                                (the second GEMM's epilogue row scale)
+__global__ __launch_bounds__(256) void prms_reduce_quant_kernel(const float* __restrict__ part, int T, int M, int D,
+                                                                float eps, const uint16_t* __restrict__ hg,
+                                                                uint8_t* __restrict__ hq, float* __restrict__ r,
+                                                                float* __restrict__ sa, float* __restrict__ rs2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (i >= M) return;  // whole waves only: the row index is uniform across the wave
+  float ss = 0.0f;
+  for (int t = 0; t < T; ++t) ss += part[(int64_t)t * M + i];
+  const float ri = 1.0f / sqrtf(ss / (float)D + eps);
+  const uint16_t* row = hg + i * D;
+  float amax = 0.0f;
+  for (int c = lane; c < D / 8; c += 64) {
+    const u32x4 v = *(const u32x4*)(row + 8 * c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[q])), fabsf(bf16_hi(v[q]))));
+  }
+  amax = wave_max(amax);
+  const float s = amax > 0.0f ? amax / E4M3_MAX : 1.0f;
+  uint8_t* qrow = hq + i * D;
+  for (int c = lane; c < D / 8; c += 64) {
+    const u32x4 v = *(const u32x4*)(row + 8 * c);
+    u32x2 o;
+    o[0] = pack_e4m3x4(bf16_lo(v[0]) / s, bf16_hi(v[0]) / s, bf16_lo(v[1]) / s, bf16_hi(v[1]) / s);
+    o[1] = pack_e4m3x4(bf16_lo(v[2]) / s, bf16_hi(v[2]) / s, bf16_lo(v[3]) / s, bf16_hi(v[3]) / s);
+    *(u32x2*)(qrow + 8 * c) = o;
+  }
+  if (lane == 0) {
+    r[i] = ri;
+    sa[i] = s;
+    rs2[i] = s * ri;
+  }
+}
+
 // U2: one workgroup per row.  hf = T + R (fp32); h = bf16(hf); r = 1/sqrt(mean(hf^2) + eps);
-// n = bf16(hf * r * gamma).  Each thread keeps up to 4 chunks of 8 columns in registers (D <= 8192).
+// n = hf * r * gamma, stored as bf16 (QUANT = false) or, for e4m3 operands, quantised per row to
+// e4m3(n / s_n) with s_n = amax |n| / 448 (QUANT = true; s_n goes to sn).  Each thread keeps up to 4
+// chunks of 8 columns in registers (D <= 8192).
+template <bool QUANT>
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* __restrict__ Tm, const uint16_t* R,
                                                           const float* __restrict__ gamma, uint16_t* H,
-                                                          uint16_t* __restrict__ Nout, float* __restrict__ rout,
-                                                          int D, float eps) {
+                                                          void* __restrict__ Nout, float* __restrict__ rout,
+                                                          float* __restrict__ sn, int D, float eps) {
   constexpr int MAXC = 4;
   __shared__ float red[4];
   const int64_t row = blockIdx.x;
@@ -262,21 +334,51 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* __rest
   const float tot = ((red[0] + red[1]) + red[2]) + red[3];
   const float r = 1.0f / sqrtf(tot / (float)D + eps);
   if (t == 0 && rout) rout[row] = r;
+  float nv[MAXC][8];
+  float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
     const int c = t + 256 * i;
     if (c < nchunks) {
-      u32x4 ho, no;
+      u32x4 ho;
       const float4 g0 = *(const float4*)(gamma + 8 * c);
       const float4 g1 = *(const float4*)(gamma + 8 * c + 4);
       const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ho[q] = pack_bf16(hv[i][2 * q], hv[i][2 * q + 1]);
-        no[q] = pack_bf16(hv[i][2 * q] * r * gg[2 * q], hv[i][2 * q + 1] * r * gg[2 * q + 1]);
+      for (int q = 0; q < 4; ++q) ho[q] = pack_bf16(hv[i][2 * q], hv[i][2 * q + 1]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        nv[i][e] = hv[i][e] * r * gg[e];
+        amax = fmaxf(amax, fabsf(nv[i][e]));
       }
       *(u32x4*)(H + row * D + 8 * c) = ho;
-      *(u32x4*)(Nout + row * D + 8 * c) = no;
+    }
+  }
+  float qs = 1.0f;
+  if (QUANT) {
+    __syncthreads();  // red[] is reused
+    amax = wave_max(amax);
+    if ((t & 63) == 0) red[t >> 6] = amax;
+    __syncthreads();
+    const float m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    qs = m > 0.0f ? m / E4M3_MAX : 1.0f;
+    if (t == 0) sn[row] = qs;
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = t + 256 * i;
+    if (c < nchunks) {
+      if (QUANT) {
+        u32x2 o;
+        o[0] = pack_e4m3x4(nv[i][0] / qs, nv[i][1] / qs, nv[i][2] / qs, nv[i][3] / qs);
+        o[1] = pack_e4m3x4(nv[i][4] / qs, nv[i][5] / qs, nv[i][6] / qs, nv[i][7] / qs);
+        *(u32x2*)((uint8_t*)Nout + row * D + 8 * c) = o;
+      } else {
+        u32x4 no;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) no[q] = pack_bf16(nv[i][2 * q], nv[i][2 * q + 1]);
+        *(u32x4*)((uint16_t*)Nout + row * D + 8 * c) = no;
+      }
     }
   }
 }
@@ -286,21 +388,27 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* __rest
 
 static int group_m_for(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 
-template <int MODE>
-static hipError_t launch_gemm(const uint16_t* A, const uint16_t* B, const float* gamma, const uint16_t* R,
-                              const float* rs, uint16_t* out, uint16_t* out2, float* part, int M, int K, int Nb,
+template <int MODE, bool FP8>
+static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, const uint16_t* R, const float* rowsc,
+                              const float* colsc, uint16_t* out, uint16_t* out2, float* part, int M, int K, int Nb,
                               hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   dim3 grid(tiles_m * tiles_n), block(NTHREADS);
-  hipLaunchKernelGGL((gemm_epilogue_kernel<MODE>), grid, block, 0, stream, A, B, gamma, R, rs, out, out2, part, M,
-                     K, Nb, group_m_for(tiles_m));
+  hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
+                     out2, part, M, K, Nb, group_m_for(tiles_m));
   return hipGetLastError();
 }
 
 hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, const float* gamma,
                                  uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream) {
-  return launch_gemm<MODE_RES_PRMS>(X, W1, gamma, R, nullptr, H, HG, part, M, K1, D, stream);
+  return launch_gemm<MODE_RES_PRMS, false>(X, W1, gamma, R, nullptr, nullptr, H, HG, part, M, K1, D, stream);
+}
+
+hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
+                                     const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* HG, float* part,
+                                     int M, int K1, int D, hipStream_t stream) {
+  return launch_gemm<MODE_RES_PRMS, true>(Xq, W1q, gamma, R, sx, sw1, H, HG, part, M, K1, D, stream);
 }
 
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream) {
@@ -309,21 +417,51 @@ hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps,
   return hipGetLastError();
 }
 
+hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* HG, uint8_t* HQ,
+                                    float* r, float* sa, float* rs2, hipStream_t stream) {
+  dim3 grid((M + 3) / 4), block(256);
+  hipLaunchKernelGGL(prms_reduce_quant_kernel, grid, block, 0, stream, part, T, M, D, eps, HG, HQ, r, sa, rs2);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
                                  int M, int D, int N2, hipStream_t stream) {
-  if (swiglu) return launch_gemm<MODE_ROWSCALE_SWIGLU>(A, W2, nullptr, nullptr, r, Y, nullptr, nullptr, M, D, N2, stream);
-  return launch_gemm<MODE_ROWSCALE>(A, W2, nullptr, nullptr, r, Y, nullptr, nullptr, M, D, N2, stream);
+  if (swiglu)
+    return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2,
+                                                    stream);
+  return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2, stream);
+}
+
+hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,
+                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+  if (swiglu)
+    return launch_gemm<MODE_ROWSCALE_SWIGLU, true>(Aq, W2q, nullptr, nullptr, rowsc, sw2, Y, nullptr, nullptr, M, D,
+                                                   N2, stream);
+  return launch_gemm<MODE_ROWSCALE, true>(Aq, W2q, nullptr, nullptr, rowsc, sw2, Y, nullptr, nullptr, M, D, N2, stream);
 }
 
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
                              hipStream_t stream) {
-  return launch_gemm<MODE_STORE>(X, W, nullptr, nullptr, nullptr, T, nullptr, nullptr, M, K, N, stream);
+  return launch_gemm<MODE_STORE, false>(X, W, nullptr, nullptr, nullptr, nullptr, T, nullptr, nullptr, M, K, N, stream);
+}
+
+hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,
+                                 int M, int K, int N, hipStream_t stream) {
+  return launch_gemm<MODE_STORE, true>(Xq, Wq, nullptr, nullptr, sx, sw, T, nullptr, nullptr, M, K, N, stream);
 }
 
 hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* N,
                               float* r, int M, int D, float eps, hipStream_t stream) {
   dim3 grid(M), block(256);
-  hipLaunchKernelGGL(add_rmsnorm_kernel, grid, block, 0, stream, T, R, gamma, H, N, r, D, eps);
+  hipLaunchKernelGGL(add_rmsnorm_kernel<false>, grid, block, 0, stream, T, R, gamma, H, (void*)N, r, (float*)nullptr,
+                     D, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_rmsnorm_quant(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H,
+                                    uint8_t* NQ, float* r, float* sn, int M, int D, float eps, hipStream_t stream) {
+  dim3 grid(M), block(256);
+  hipLaunchKernelGGL(add_rmsnorm_kernel<true>, grid, block, 0, stream, T, R, gamma, H, (void*)NQ, r, sn, D, eps);
   return hipGetLastError();
 }
 

@@ -22,4 +22,22 @@ hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, 
 hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* N,
                               float* r, int M, int D, float eps, hipStream_t stream);
 
+// ---- e4m3 operands (scales: dequantised value = code * scale) ----
+// K1: as launch_gemm1_res_prms with X W1 = (Xq W1q) * sx[m] * sw1[n].
+hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
+                                     const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* HG, float* part,
+                                     int M, int K1, int D, hipStream_t stream);
+// K2: r from the partial sums; HQ = e4m3(HG / sa) per row with sa = amax|HG row| / 448; rs2 = sa * r.
+hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* HG, uint8_t* HQ,
+                                    float* r, float* sa, float* rs2, hipStream_t stream);
+// K3 / U3: Y = bf16(epi((Aq W2q) * rowsc[m] * sw2[n])).
+hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,
+                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream);
+// U1: T = bf16((Xq Wq) * sx[m] * sw[n]).
+hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,
+                                 int M, int K, int N, hipStream_t stream);
+// U2: H = bf16(T + R); NQ = e4m3(n / sn) per row with n = (T + R) r gamma and sn = amax|n row| / 448.
+hipError_t launch_add_rmsnorm_quant(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H,
+                                    uint8_t* NQ, float* r, float* sn, int M, int D, float eps, hipStream_t stream);
+
 }  // namespace coda

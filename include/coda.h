@@ -81,8 +81,9 @@ const char* coda_last_error(void);
 /* Workspace bytes an entry point needs for these dimensions.
  *   fp8:     0 for the bf16 entry points, 1 for the *_fp8 ones
  *   unfused: 0 for coda_block_fwd*, 1 for coda_block_unfused*
- * Layout: part [D/256][M] fp32 partial sums of squares, then r [M] fp32, then (fused) hg [M,D] bf16 or
- * (unfused) the two [M,D] bf16 intermediates T and n, each 256-byte aligned.  fp8 must be 0. */
+ * Layout (each piece 256-byte aligned): part [D/256][M] fp32 partial sums of squares, r [M] fp32, then
+ *   fused:   hg = h * gamma [M,D] bf16 (+ fp8: its e4m3 quantisation [M,D], the row scales [M], s_a*r [M])
+ *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]). */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
 /* The fused block, bf16 operands.
@@ -97,6 +98,19 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
                    int64_t M, int64_t K1, int64_t D, int64_t N2,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* The fused block with fp8 (OCP e4m3fn) operands and fp32 accumulation.
+ *   Xq [M,K1] e4m3 with per-row scales sx [M]; W1q [K1,D] e4m3 with per-column scales sw1 [D];
+ *   W2q [D,N2] e4m3 with per-column scales sw2 [N2]; R [M,D] bf16; gamma [D] fp32.
+ *   out_h = bf16(dequant(Xq) dequant(W1q) + R); out_y as coda_block_fwd.
+ * The second product's A operand is h * gamma quantised per row to e4m3 with scale
+ * s_a = amax_j |bf16(h_ij gamma_j)| / 448 (1 for an all-zero row) by the reduction kernel, which has the
+ * whole row; y = bf16(epi(acc * s_a_i * r_i * sw2_n)).  Shape rules as coda_block_fwd, and K1 a multiple
+ * of 256.  Workspace: coda_workspace_bytes(..., fp8 = 1, unfused = 0). */
+int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
+                       const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
+                       void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* The unfused three-kernel baseline, kept to measure the HBM traffic the fusion saves:
  *   T = bf16(X W1)  ->  h = bf16(T + R), r from the fp32 T + R, n = bf16(h * r * gamma)  ->  y = epi(n W2).
  * T and n live in the workspace.  Same arguments and outputs as coda_block_fwd. */
@@ -105,7 +119,15 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
                        int64_t M, int64_t K1, int64_t D, int64_t N2,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Byte offset of r [M] (fp32) inside the workspace of coda_block_fwd and coda_block_unfused. */
+/* The unfused baseline with e4m3 operands: T = bf16(dequant(Xq) dequant(W1q)) -> h = bf16(T + R),
+ * n = (T + R) r gamma quantised per row to e4m3 (scale amax|n row| / 448) -> y = epi(dequant(nq) dequant(W2q)).
+ * Same arguments as coda_block_fwd_fp8; workspace: coda_workspace_bytes(..., fp8 = 1, unfused = 1). */
+int coda_block_unfused_fp8(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
+                           const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
+                           void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Byte offset of r [M] (fp32) inside the workspace of every block entry point. */
 size_t coda_workspace_r_offset(int64_t M, int64_t D);
 
 /* ---- the three steps of coda_block_fwd, exposed one by one (same conventions) ---- */

@@ -144,3 +144,28 @@ def test_binding_rejects_host_tensors():
                           torch.ones(256), torch.zeros(256, 256, dtype=torch.bfloat16), 1e-5, 0,
                           torch.zeros(4, 256, dtype=torch.bfloat16), torch.zeros(4, 256, dtype=torch.bfloat16),
                           torch.zeros(1024, dtype=torch.uint8))
+
+
+def _call8(lib, a, fn="coda_block_fwd_fp8", sx=BASE + 8 * GB, sw1=BASE + 9 * GB, sw2=BASE + 10 * GB):
+    return getattr(lib, fn)(a["X"], sx, a["W1"], sw1, a["R"], a["gamma"], a["W2"], sw2, a["eps"], a["epi"],
+                            a["out_h"], a["out_y"], a["M"], a["K1"], a["D"], a["N2"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("fn", ["coda_block_fwd_fp8", "coda_block_unfused_fp8"])
+def test_fp8_validation(lib, fn):
+    a = _args(M=512, K1=256, D=256, N2=512)
+    assert _call8(lib, a, fn, sx=0) == INVALID
+    assert _call8(lib, a, fn, sw2=BASE + 10 * GB + 4) == INVALID          # misaligned scale
+    assert _call8(lib, _args(K1=384), fn) == UNSUPPORTED                  # e4m3 K step is 256
+    assert _call8(lib, a, fn, sw1=BASE + 5 * GB) == ALIAS                  # a scale vector under out_h
+    small = dict(a)
+    small["ws_bytes"] = 1024
+    assert _call8(lib, small, fn) == WORKSPACE
+
+
+def test_fp8_workspace_bytes(lib):
+    M, D = 8192, 2048
+    a = lambda x: (x + 255) // 256 * 256
+    base = a(8 * M * 4) + a(M * 4)
+    assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 1, 0) == base + a(M * D * 2) + a(M * D) + 2 * a(M * 4)
+    assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 1, 1) == base + a(M * D * 2) + a(M * D) + a(M * 4)

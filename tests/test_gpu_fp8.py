@@ -1,0 +1,126 @@
+"""GPU parity of the fused block with OCP e4m3 operands (and its unfused baseline) against the fp64 oracle.
+
+The oracle runs on the dequantised inputs (code * scale, exact in fp64); the contract tolerance for e4m3 is
+a normwise max relative error of 6e-2 on y (h keeps the bf16 rule).  The method-internal quantiser (h * gamma
+per row to e4m3) is checked code for code against the oracle's e4m3 encoder, both sides computing x / s in
+fp32.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gemm_epilogue_fusion_amd import binding as cb
+from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, EPI_SWIGLU, WORKLOADS, Workload, make_inputs
+
+from parity import check_h, check_y, f64, sample_rows
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cb.load()
+
+
+def _u8(t):
+    return t.view(torch.uint8).numpy()
+
+
+def _oracle_fp8(inp, rows=None, form="fused"):
+    wl = inp.wl
+    Xq, sx, R = inp.Xq, inp.sx, inp.R
+    if rows is not None:
+        idx = torch.as_tensor(rows, dtype=torch.long)
+        Xq, sx, R = Xq[idx], sx[idx], R[idx]
+    X = oracle.dequant_rows_e4m3(_u8(Xq), sx.numpy())
+    W1 = oracle.dequant_cols_e4m3(_u8(inp.W1q), inp.sw1.numpy())
+    W2 = oracle.dequant_cols_e4m3(_u8(inp.W2q), inp.sw2.numpy())
+    fn = oracle.block_fused if form == "fused" else oracle.block_unfused
+    return fn(X, W1, f64(R), f64(inp.gamma), W2, wl.eps, wl.epi)
+
+
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+def _run_fp8(inp, unfused=False):
+    wl = inp.wl
+    dev = "cuda"
+    args = [t.to(dev) for t in (inp.Xq, inp.sx, inp.W1q, inp.sw1, inp.R, inp.gamma, inp.W2q, inp.sw2)]
+    h = torch.full((wl.M, wl.D), float("nan"), dtype=torch.bfloat16, device=dev)
+    y = torch.full((wl.M, wl.n_out), float("nan"), dtype=torch.bfloat16, device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=int(unfused), device=dev, fp8=1)
+    ws.fill_(0xFF)
+    fn = cb.coda_block_unfused_fp8 if unfused else cb.coda_block_fwd_fp8
+    fn(*args, wl.eps, wl.epi, h, y, ws)
+    torch.cuda.synchronize()
+    return h, y, ws
+
+
+FP8_SMALL = [
+    Workload("fp8_ragged_swiglu", M=300, K1=512, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, fp8=True, seed=7),
+    Workload("fp8_identity", M=257, K1=256, D=768, N2=512, epi=EPI_IDENTITY, eps=1e-5, fp8=True, seed=8),
+    Workload("fp8_one_row", M=1, K1=256, D=256, N2=256, epi=EPI_SWIGLU, eps=1e-6, fp8=True, seed=9),
+]
+
+
+@pytest.mark.parametrize("wl", FP8_SMALL, ids=[w.name for w in FP8_SMALL])
+def test_fp8_fused_small(wl):
+    _say(f"[gpu] fp8 fused {wl}")
+    inp = make_inputs(wl)
+    h, y, ws = _run_fp8(inp)
+    oh, orr, oy = _oracle_fp8(inp)
+    check_h(f64(h), oh)
+    check_y(f64(y), oy, fp8=True)
+    # the workspace after the call: part, r, hg [M,D] bf16, hq [M,D] e4m3, s_a [M], s_a * r [M]
+    M, D = wl.M, wl.D
+    off_r = _align256((D // 256) * M * 4)
+    off_hg = off_r + _align256(M * 4)
+    off_q = off_hg + _align256(M * D * 2)
+    off_s = off_q + _align256(M * D)
+    wsc = ws.cpu()
+    r = wsc[off_r: off_r + 4 * M].view(torch.float32).numpy()
+    np.testing.assert_allclose(r, orr, rtol=2e-5)
+    hg = wsc[off_hg: off_hg + 2 * M * D].view(torch.bfloat16).view(M, D).float().numpy()
+    q = wsc[off_q: off_q + M * D].view(M, D).numpy()
+    s = wsc[off_s: off_s + 4 * M].view(torch.float32).numpy()
+    # per-row scale: amax of the stored bf16 h * gamma over 448, computed in fp32 on both sides
+    amax = np.max(np.abs(hg), axis=1).astype(np.float32)
+    want_s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    assert np.array_equal(s, want_s)
+    # codes: the oracle's e4m3 encoder on the same fp32 quotient, code for code
+    quot = (hg.astype(np.float32) / s[:, None]).astype(np.float32)
+    assert np.array_equal(q, oracle.e4m3_encode(quot.astype(np.float64)))
+
+
+@pytest.mark.parametrize("wl", FP8_SMALL[:2], ids=[w.name for w in FP8_SMALL[:2]])
+def test_fp8_unfused_small(wl):
+    _say(f"[gpu] fp8 unfused {wl}")
+    inp = make_inputs(wl)
+    h, y, _ = _run_fp8(inp, unfused=True)
+    oh, _, oy = _oracle_fp8(inp, form="unfused")
+    check_h(f64(h), oh)
+    check_y(f64(y), oy, fp8=True)
+
+
+def test_fp8_full_size_sampled_rows():
+    wl = WORKLOADS["1b_attn_out_mlp_in_fp8"]
+    _say(f"[gpu] fp8 full size {wl}")
+    inp = make_inputs(wl)
+    h, y, _ = _run_fp8(inp)
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(h).all()), "unwritten or non-finite output"
+    rows = sample_rows(wl.M, n=40)
+    oh, _, oy = _oracle_fp8(inp, rows)
+    check_h(f64(h[rows]), oh)
+    check_y(f64(y[rows]), oy, fp8=True)
