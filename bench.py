@@ -112,6 +112,9 @@ def main() -> int:
     ap.add_argument("--workload", default="1b_attn_out_mlp_in")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
+                         "reference that scales the HBM byte counters of a profiling run)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -157,6 +160,13 @@ def main() -> int:
     ms = elapsed * 1e3 / args.steps
     tflops = wl.flops / (ms * 1e-3) / 1e12
     if args.only_fused:
+        if args.copy_calibration_mib:
+            n = args.copy_calibration_mib * (1 << 20)
+            src = torch.ones(n, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
         print(json.dumps({"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": ms}))
         return 0
 
