@@ -48,6 +48,46 @@ struct GateUpCols {
   }
 };
 
+// ---- output tile staging in LDS -----------------------------------------------------------------------
+// A bf16 tile of 256 rows x 8 CH columns: row r is 16 CH bytes, its 16-byte chunk c at slot c ^ (r % CH), so
+// both the lanes that write 32 rows of one chunk and the lanes that read one row's chunks spread over the
+// banks.
+template <int CH>
+__device__ __forceinline__ int tile_off(int r, int c) { return r * (16 * CH) + ((c ^ (r & (CH - 1))) << 4); }
+
+// Whole rows of the staged tile to dst[(m0 + r) * ld + n0 ...], 16 bytes per lane; rows >= M are skipped.
+template <int CH>
+__device__ __forceinline__ void store_tile_rows(const char* smem, uint16_t* dst, int ld, int m0, int n0, int M) {
+  constexpr int ROWS_PER_PASS = NTHREADS / CH;
+  const int t = threadIdx.x;
+  const int c = t % CH;
+#pragma unroll
+  for (int p = 0; p < BM / ROWS_PER_PASS; ++p) {
+    const int r = p * ROWS_PER_PASS + t / CH;
+    const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, c));
+    const int m = m0 + r;
+    if (m < M) *(u32x4*)(dst + (int64_t)m * ld + n0 + 8 * c) = v;
+  }
+}
+
+// Rows m0 .. m0+255 of src (columns n0 .. n0 + 8 CH) into the staged-tile layout with direct global -> LDS
+// loads (rows past M read row M-1).  The caller waits for the loads (vmcnt) and synchronises the workgroup.
+template <int CH>
+__device__ __forceinline__ void load_tile_rows(const uint16_t* src, int ld, int m0, int n0, int M, char* smem) {
+  constexpr int ROWS_PER_INST = 64 / CH;  // one wave instruction fills 1 KiB
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < BM / (NWAVES * ROWS_PER_INST); ++j) {
+    const int r0 = (wave * (BM / NWAVES)) + j * ROWS_PER_INST;
+    const int r = r0 + lane / CH;
+    const int slot = lane % CH;
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    g2lds16(src + (int64_t)m * ld + n0 + 8 * (slot ^ (r & (CH - 1))), smem + r0 * (16 * CH));
+  }
+}
+
 // One GEMM with a programmable epilogue.  The accumulator tile covers 256 columns of B; A [M,K] and B
 // [K,Nb] are bf16 (FP8 = false) or e4m3 bytes (FP8 = true), row-major.  In the epilogue the accumulator is
 // first multiplied by rowsc[m] * colsc[n] where those are given (dequantisation scales and / or the row
@@ -63,7 +103,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
     float* __restrict__ part, int M, int K, int Nb, int group_m) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
+  // the mainloop ring (reused as the output staging area), plus the row-sum exchange of MODE_RES_PRMS
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 : 0)];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   int tm, tn;
@@ -95,7 +136,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(acc[mb][nb]));
 
   // ---- epilogue: the accumulator tile is still in registers ----
-  // acc[mb][nb][r] is row m0 + 128 wm + 32 mb + lane%32, column 64 wn + 32 nb + 8 (r/4) + 4 (lane/32) + r%4
+  // acc[mb][nb][r] is row m0 + 128 wm + 32 mb + lane%32, column 64 wn + 32 nb + 8 (r/4) + 4 (lane/32) + r%4.
+  // Each lane owns 4-column pieces of its rows, so the results are first staged as a bf16 tile in LDS
+  // (the mainloop's ring is free by then) and written out as whole rows: stores of 8 scattered bytes per
+  // lane would cost the memory system a request per 16 bytes.
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
@@ -109,9 +153,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
     rsv[mb] = rowsc ? rowsc[m < M ? m : M - 1] : 1.0f;
   }
+  __syncthreads();  // every wave is done with the mainloop's LDS stages
 
   if (MODE == MODE_RES_PRMS || MODE == MODE_STORE || MODE == MODE_ROWSCALE) {
     const int n_base = tn * BN + wn * 64 + 4 * half;
+    if (MODE == MODE_RES_PRMS) {
+      // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows)
+      load_tile_rows<32>(R, Nb, m0, tn * BN, M, smem);
+      wait_barrier<0>();
+    }
     // gamma of this lane's 4-column groups (the same for every row)
     f32x4 gv[NB][4];
 #pragma unroll
@@ -120,34 +170,31 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       for (int gq = 0; gq < 4; ++gq)
         gv[nb][gq] = MODE == MODE_RES_PRMS ? *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
     float ss[4];
+    u32x2 hgv[4][NB][4];  // bf16(h * gamma), staged after h has been written out
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-      const int mr = m < M ? m : M - 1;
-      // this row block's residual values and column scales as one batch of loads (the column scales are
-      // re-read per row block from L1 rather than held: registers are the scarce resource here)
-      u32x2 rr[NB][4];
+      const int r = wm * 128 + mb * 32 + (lane & 31);
+      // this row block's column scales as one batch of loads (re-read per row block from L1 rather than
+      // held: registers are the scarce resource here)
       f32x4 cv[NB][4];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int n = n_base + nb * 32 + 8 * gq;
-          if (MODE == MODE_RES_PRMS) rr[nb][gq] = *(const u32x2*)(R + (int64_t)mr * Nb + n);
-          cv[nb][gq] = colsc ? *(const f32x4*)(colsc + n) : (f32x4){1.f, 1.f, 1.f, 1.f};
-        }
+        for (int gq = 0; gq < 4; ++gq)
+          cv[nb][gq] = colsc ? *(const f32x4*)(colsc + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
       float s = 0.0f;
-      u32x2 hv[NB][4], gvv[NB][4];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
+          char* slot = smem + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half;
           const f32x4 c = cv[nb][gq];
           const float sc = rsv[mb];
           float v0 = acc[mb][nb][4 * gq + 0] * sc * c[0], v1 = acc[mb][nb][4 * gq + 1] * sc * c[1];
           float v2 = acc[mb][nb][4 * gq + 2] * sc * c[2], v3 = acc[mb][nb][4 * gq + 3] * sc * c[3];
           if (MODE == MODE_RES_PRMS) {
-            const u32x2 r2 = rr[nb][gq];
+            // the slot holds this lane's residual values; h replaces them in place
+            const u32x2 r2 = *(const u32x2*)slot;
             v0 += bf16_lo(r2[0]);
             v1 += bf16_hi(r2[0]);
             v2 += bf16_lo(r2[1]);
@@ -157,34 +204,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
             s += v2 * v2;
             s += v3 * v3;
             const f32x4 g = gv[nb][gq];
-            gvv[nb][gq] = (u32x2){pack_bf16(v0 * g[0], v1 * g[1]), pack_bf16(v2 * g[2], v3 * g[3])};
+            hgv[mb][nb][gq] = (u32x2){pack_bf16(v0 * g[0], v1 * g[1]), pack_bf16(v2 * g[2], v3 * g[3])};
           }
-          hv[nb][gq] = (u32x2){pack_bf16(v0, v1), pack_bf16(v2, v3)};
+          *(u32x2*)slot = (u32x2){pack_bf16(v0, v1), pack_bf16(v2, v3)};
         }
       ss[mb] = s;
-      if (m < M) {
+    }
+    __syncthreads();
+    store_tile_rows<32>(smem, out, Nb, m0, tn * BN, M);
+    if (MODE == MODE_RES_PRMS) {
+      __syncthreads();
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int r = wm * 128 + mb * 32 + (lane & 31);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int64_t o = (int64_t)m * Nb + n_base + nb * 32 + 8 * gq;
-            *(u32x2*)(out + o) = hv[nb][gq];
-            if (MODE == MODE_RES_PRMS) *(u32x2*)(out2 + o) = gvv[nb][gq];
-          }
+          for (int gq = 0; gq < 4; ++gq)
+            *(u32x2*)(smem + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half) = hgv[mb][nb][gq];
       }
-    }
-    if (MODE == MODE_RES_PRMS) {
       // lanes l and l+32 hold the same row: add their halves, then the four waves sharing the rows, in a
       // fixed order (no atomics: the partial sums are reproducible bit for bit)
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) ss[mb] += __shfl_xor(ss[mb], 32);
-      __syncthreads();  // every wave is done with the mainloop's LDS stages
-      float* red = (float*)smem;  // [4 wn][256 rows]
+      float* red = (float*)(smem + LDS_BYTES);  // [4 wn][256 rows], outside the staging area
       if (lane < 32) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) red[wn * 256 + wm * 128 + mb * 32 + lane] = ss[mb];
       }
       __syncthreads();
+      store_tile_rows<32>(smem, out2, Nb, m0, tn * BN, M);
       if (wn == 0 && lane < 32) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -199,8 +248,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const int c_base = tn * 128 + wn * 32 + 4 * half;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-      if (m >= M) continue;
+      const int r = wm * 128 + mb * 32 + (lane & 31);
       const float sc = rsv[mb];
       f32x4 cg[4], cu[4];
 #pragma unroll
@@ -210,7 +258,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       }
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int c = c_base + 8 * gq;
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -218,9 +265,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
           const float up = acc[mb][1][4 * gq + e] * sc * cu[gq][e];
           y[e] = silu_f32(gate) * up;
         }
-        *(u32x2*)(out + (int64_t)m * ny + c) = (u32x2){pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
+        *(u32x2*)(smem + tile_off<16>(r, wn * 4 + gq) + 8 * half) =
+            (u32x2){pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3])};
       }
     }
+    __syncthreads();
+    store_tile_rows<16>(smem, out, ny, m0, tn * 128, M);
   }
 }
 
