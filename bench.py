@@ -4,7 +4,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
 A step is one coda_block_fwd call (all three kernels: GEMM1 + residual + partial sums of squares, the
-row-scale reduction, GEMM2 with the gamma fold, row scale and SwiGLU) on inputs already resident in HBM.
+row-scale reduction, GEMM2 on h * gamma with the row scale and SwiGLU) on inputs already resident in HBM.
 W untimed steps, then K timed steps between two device synchronisations.  Prints ONE JSON line.
 
 Besides the headline the line carries:
@@ -15,6 +15,8 @@ Besides the headline the line carries:
   cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the same workload (rows are
                 independent), scaled to TFLOP/s
   unfused       the three-kernel baseline timed the same way, and the algorithmic HBM bytes both paths move
+  fp8           the same block with e4m3 X / W1 / W2 (per-row and per-column fp32 scales), fused and unfused,
+                timed with HIP events, against the dense fp8 MFMA peak (5 PFLOP/s)
 """
 from __future__ import annotations
 
@@ -29,6 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 MFMA peak
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X published dense fp8 MFMA peak
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused block TFLOP/s + % bf16 MFMA peak at 1B shape M=8192; HBM bytes saved"
 KERNEL_SOURCES = ["gemm_epilogue_fusion_amd/csrc/gemm_core.h", "gemm_epilogue_fusion_amd/csrc/kernels.hip"]
@@ -94,6 +97,32 @@ def cpu_baseline(wl, inp, target_s: float = 15.0) -> dict:
                       f"rows are independent so the rate scales to the full block"}
 
 
+def time_fp8(dev, n_ev: int, warmup: int, torch, cb) -> dict:
+    """The e4m3 version of the headline block: fused and unfused, average ms per call by HIP events."""
+    from gemm_epilogue_fusion_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["1b_attn_out_mlp_in_fp8"]
+    inp = make_inputs(wl)
+    a = [t.to(dev) for t in (inp.Xq, inp.sx, inp.W1q, inp.sw1, inp.R, inp.gamma, inp.W2q, inp.sw2)]
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev, fp8=1)
+    wsu = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=1, device=dev, fp8=1)
+    fused = lambda: cb.coda_block_fwd_fp8(*a, wl.eps, wl.epi, h, y, ws)
+    unfused = lambda: cb.coda_block_unfused_fp8(*a, wl.eps, wl.epi, h, y, wsu)
+    for _ in range(warmup):
+        fused()
+        unfused()
+    torch.cuda.synchronize()
+    f_ms = time_loop(fused, n_ev, torch)
+    u_ms = time_loop(unfused, n_ev, torch)
+    tf = wl.flops / (f_ms * 1e-3) / 1e12
+    return {"workload": wl.name, "dtype": "e4m3 operands, fp32 accumulate, bf16 h/y",
+            "fused_ms": round(f_ms, 4), "tflops": round(tf, 2),
+            "pct_fp8_mfma_peak": round(100 * tf / MFMA_FP8_PEAK_TFLOPS, 2), "unfused_ms": round(u_ms, 4),
+            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4)}
+
+
 def traffic_record(src_hash: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -111,6 +140,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="1b_attn_out_mlp_in")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the e4m3 block timing")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
@@ -214,6 +244,8 @@ def main() -> int:
         "hbm_bytes": {"fused_algorithmic": fb, "unfused_algorithmic": ub, "saved_algorithmic": ub - fb},
         "kernel_source_hash": src_hash,
     }
+    if not args.no_fp8:
+        line["fp8"] = time_fp8(dev, n_ev, args.warmup, torch, cb)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(line))
