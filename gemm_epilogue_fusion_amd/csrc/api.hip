@@ -96,10 +96,10 @@ int check_alias(const Range* in, int nin, const Range* out, int nout, const void
 struct Workspace {
   float* part;    // [D/256][M] partial sums of squares
   float* r;       // [M] row scale
-  uint16_t* hg;   // fused: h * gamma [M,D] bf16, the second GEMM's A operand (bf16) or its quantiser input (fp8)
+  uint16_t* hg;   // fused bf16: h * gamma [M,D] bf16, the second GEMM's A operand
   uint16_t* t;    // unfused: T = X W1 [M,D] bf16
   uint16_t* n;    // unfused bf16: normalised rows [M,D]
-  uint8_t* q;     // fp8: the second GEMM's e4m3 A operand [M,D] (fused: h*gamma quantised; unfused: n quantised)
+  uint8_t* q;     // fp8: the second GEMM's e4m3 A operand [M,D] (fused: h * gamma quantised; unfused: n quantised)
   float* qs;      // fp8: its per-row scale [M]
   float* rs2;     // fp8 fused: the second GEMM's epilogue row scale qs * r [M]
 };
@@ -128,13 +128,12 @@ size_t carve(void* ws, int64_t M, int64_t D, int fp8, int unfused, Workspace* w)
     } else {
       x.n = (uint16_t*)take(ws_mat_bytes(M, D, 2));
     }
+  } else if (fp8) {
+    x.q = (uint8_t*)take(ws_mat_bytes(M, D, 1));
+    x.qs = (float*)take(ws_vec_bytes(M));
+    x.rs2 = (float*)take(ws_vec_bytes(M));
   } else {
     x.hg = (uint16_t*)take(ws_mat_bytes(M, D, 2));
-    if (fp8) {
-      x.q = (uint8_t*)take(ws_mat_bytes(M, D, 1));
-      x.qs = (float*)take(ws_vec_bytes(M));
-      x.rs2 = (float*)take(ws_vec_bytes(M));
-    }
   }
   if (w) *w = x;
   return off;
@@ -269,12 +268,12 @@ int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const f
     Workspace w;
     carve(workspace, M, D, 1, 0, &w);
     if ((s = hip_check(coda::launch_gemm1_res_prms_fp8((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1,
-                                                       (const uint16_t*)R, gamma, (uint16_t*)out_h, w.hg, w.part,
-                                                       (int)M, (int)K1, (int)D, st),
+                                                       (const uint16_t*)R, (uint16_t*)out_h, w.part, (int)M,
+                                                       (int)K1, (int)D, st),
                        "fp8 gemm1_res_prms launch")))
       return s;
-    if ((s = hip_check(coda::launch_prms_reduce_quant(w.part, (int)(D / 256), (int)M, (int)D, eps, w.hg, w.q, w.r,
-                                                      w.qs, w.rs2, st),
+    if ((s = hip_check(coda::launch_prms_reduce_quant(w.part, (int)(D / 256), (int)M, (int)D, eps,
+                                                      (const uint16_t*)out_h, gamma, w.q, w.r, w.qs, w.rs2, st),
                        "prms_reduce_quant launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale_fp8(w.q, (const uint8_t*)W2q, w.rs2, sw2, epi_kind == CODA_EPI_SWIGLU,

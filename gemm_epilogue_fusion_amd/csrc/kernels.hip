@@ -8,6 +8,8 @@
 //   K2 prms_reduce    : the light reduction, r = 1 / sqrt(sum_t part / D + eps)
 //   K3 gemm2_rowscale : mainloop on h * gamma against W2, i.e. h (diag(gamma) W2); the epilogue applies r
 //                       (a per-row scalar commutes with the product) and SwiGLU
+// With e4m3 operands K1 stores h only, and K2 (prms_reduce_quant) forms h * gamma from the stored h and
+// quantises it per row for K3.
 // Unfused baseline (three operators whose intermediates round-trip HBM, the pattern the same section
 // describes as the conventional one):
 //   U1 gemm_store     : T = bf16(X W1)
@@ -92,7 +94,7 @@ __device__ __forceinline__ void load_tile_rows(const uint16_t* src, int ld, int 
 // [K,Nb] are bf16 (FP8 = false) or e4m3 bytes (FP8 = true), row-major.  In the epilogue the accumulator is
 // first multiplied by rowsc[m] * colsc[n] where those are given (dequantisation scales and / or the row
 // scale r), giving v:
-//   MODE_RES_PRMS:  out [M,Nb] = bf16(v + R); out2 [M,Nb] = bf16((v + R) * gamma[n]);
+//   MODE_RES_PRMS:  out [M,Nb] = bf16(v + R); out2 [M,Nb] = bf16((v + R) * gamma[n]) (bf16 operands only);
 //                   part[tn][m] = sum over the tile's columns of (v + R)^2
 //   MODE_STORE:     out [M,Nb] = bf16(v)
 //   MODE_ROWSCALE:  out [M,Nb] = bf16(v)
@@ -156,6 +158,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   __syncthreads();  // every wave is done with the mainloop's LDS stages
 
   if (MODE == MODE_RES_PRMS || MODE == MODE_STORE || MODE == MODE_ROWSCALE) {
+    // h * gamma is written by the bf16 K1 only (the e4m3 path forms it in K2 from the stored h)
+    constexpr bool WRITE_HG = MODE == MODE_RES_PRMS && !FP8;
     const int n_base = tn * BN + wn * 64 + 4 * half;
     if (MODE == MODE_RES_PRMS) {
       // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows)
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq)
-        gv[nb][gq] = MODE == MODE_RES_PRMS ? *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+        gv[nb][gq] = WRITE_HG ? *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
     float ss[4];
     u32x2 hgv[4][NB][4];  // bf16(h * gamma), staged after h has been written out
 #pragma unroll
@@ -203,8 +207,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
             s += v1 * v1;
             s += v2 * v2;
             s += v3 * v3;
-            const f32x4 g = gv[nb][gq];
-            hgv[mb][nb][gq] = (u32x2){pack_bf16(v0 * g[0], v1 * g[1]), pack_bf16(v2 * g[2], v3 * g[3])};
+            if (WRITE_HG) {
+              const f32x4 g = gv[nb][gq];
+              hgv[mb][nb][gq] = (u32x2){pack_bf16(v0 * g[0], v1 * g[1]), pack_bf16(v2 * g[2], v3 * g[3])};
+            }
           }
           *(u32x2*)slot = (u32x2){pack_bf16(v0, v1), pack_bf16(v2, v3)};
         }
@@ -213,15 +219,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     __syncthreads();
     store_tile_rows<32>(smem, out, Nb, m0, tn * BN, M);
     if (MODE == MODE_RES_PRMS) {
-      __syncthreads();
+      if (WRITE_HG) {
+        __syncthreads();
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int r = wm * 128 + mb * 32 + (lane & 31);
+        for (int mb = 0; mb < 4; ++mb) {
+          const int r = wm * 128 + mb * 32 + (lane & 31);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq)
-            *(u32x2*)(smem + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half) = hgv[mb][nb][gq];
+            for (int gq = 0; gq < 4; ++gq)
+              *(u32x2*)(smem + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half) = hgv[mb][nb][gq];
+        }
       }
       // lanes l and l+32 hold the same row: add their halves, then the four waves sharing the rows, in a
       // fixed order (no atomics: the partial sums are reproducible bit for bit)
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         for (int mb = 0; mb < 4; ++mb) red[wn * 256 + wm * 128 + mb * 32 + lane] = ss[mb];
       }
       __syncthreads();
-      store_tile_rows<32>(smem, out2, Nb, m0, tn * BN, M);
+      if (WRITE_HG) store_tile_rows<32>(smem, out2, Nb, m0, tn * BN, M);
       if (wn == 0 && lane < 32) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -307,36 +315,77 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // K2 for e4m3 operands: one wave per row i.
-//   r[i]    = 1 / sqrt((sum_t part[t][i]) / D + eps)     (t summed in order, as in prms_reduce_kernel)
-//   s_a[i]  = amax_j |hg[i][j]| / 448  (1 for an all-zero row)
-//   hq[i][j] = e4m3(hg[i][j] / s_a[i])                     (the second GEMM's A operand)
-//   rs2[i]  = s_a[i] * r[i]                                (the second GEMM's epilogue row scale)
+//   r[i]     = 1 / sqrt((sum_t part[t][i]) / D + eps)    (t summed in order, as in prms_reduce_kernel)
+//   a[i][j]  = h[i][j] * gamma[j] in fp32, h the stored bf16 value
+//   s_a[i]   = amax_j |a[i][j]| / 448  (1 for an all-zero row)
+//   hq[i][j] = e4m3(a[i][j] * (1 / s_a[i]))               (the second GEMM's A operand; the reciprocal is
+//                                                          rounded to fp32 once per row)
+//   rs2[i]   = s_a[i] * r[i]                               (the second GEMM's epilogue row scale)
+// Each lane keeps up to CACHED 8-column chunks of a[i] in registers between the amax and the quantisation
+// (D <= 4096 reads h and gamma once); wider rows recompute the rest.
 __global__ __launch_bounds__(256) void prms_reduce_quant_kernel(const float* __restrict__ part, int T, int M, int D,
-                                                                float eps, const uint16_t* __restrict__ hg,
+                                                                float eps, const uint16_t* __restrict__ h,
+                                                                const float* __restrict__ gamma,
                                                                 uint8_t* __restrict__ hq, float* __restrict__ r,
                                                                 float* __restrict__ sa, float* __restrict__ rs2) {
+  constexpr int CACHED = 8;
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (i >= M) return;  // whole waves only: the row index is uniform across the wave
+  const uint16_t* row = h + i * D;
+  const int nch = D / 8;
+  auto scaled = [&](int c, float (&a)[8]) {
+    const u32x4 v = *(const u32x4*)(row + 8 * c);
+    const f32x4 g0 = *(const f32x4*)(gamma + 8 * c);
+    const f32x4 g1 = *(const f32x4*)(gamma + 8 * c + 4);
+    a[0] = bf16_lo(v[0]) * g0[0];
+    a[1] = bf16_hi(v[0]) * g0[1];
+    a[2] = bf16_lo(v[1]) * g0[2];
+    a[3] = bf16_hi(v[1]) * g0[3];
+    a[4] = bf16_lo(v[2]) * g1[0];
+    a[5] = bf16_hi(v[2]) * g1[1];
+    a[6] = bf16_lo(v[3]) * g1[2];
+    a[7] = bf16_hi(v[3]) * g1[3];
+  };
+  float av[CACHED][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < CACHED; ++k) {
+    const int c = lane + 64 * k;
+    if (c < nch) {
+      scaled(c, av[k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(av[k][e]));
+    }
+  }
+  for (int c = lane + 64 * CACHED; c < nch; c += 64) {
+    float a[8];
+    scaled(c, a);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(a[e]));
+  }
   float ss = 0.0f;
   for (int t = 0; t < T; ++t) ss += part[(int64_t)t * M + i];
   const float ri = 1.0f / sqrtf(ss / (float)D + eps);
-  const uint16_t* row = hg + i * D;
-  float amax = 0.0f;
-  for (int c = lane; c < D / 8; c += 64) {
-    const u32x4 v = *(const u32x4*)(row + 8 * c);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[q])), fabsf(bf16_hi(v[q]))));
-  }
   amax = wave_max(amax);
   const float s = amax > 0.0f ? amax / E4M3_MAX : 1.0f;
+  const float inv = 1.0f / s;
   uint8_t* qrow = hq + i * D;
-  for (int c = lane; c < D / 8; c += 64) {
-    const u32x4 v = *(const u32x4*)(row + 8 * c);
+  auto quant = [&](const float (&a)[8], int c) {
     u32x2 o;
-    o[0] = pack_e4m3x4(bf16_lo(v[0]) / s, bf16_hi(v[0]) / s, bf16_lo(v[1]) / s, bf16_hi(v[1]) / s);
-    o[1] = pack_e4m3x4(bf16_lo(v[2]) / s, bf16_hi(v[2]) / s, bf16_lo(v[3]) / s, bf16_hi(v[3]) / s);
+    o[0] = pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+    o[1] = pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
     *(u32x2*)(qrow + 8 * c) = o;
+  };
+#pragma unroll
+  for (int k = 0; k < CACHED; ++k) {
+    const int c = lane + 64 * k;
+    if (c < nch) quant(av[k], c);
+  }
+  for (int c = lane + 64 * CACHED; c < nch; c += 64) {
+    float a[8];
+    scaled(c, a);
+    quant(a, c);
   }
   if (lane == 0) {
     r[i] = ri;
@@ -456,9 +505,9 @@ hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const ui
 }
 
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
-                                     const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* HG, float* part,
-                                     int M, int K1, int D, hipStream_t stream) {
-  return launch_gemm<MODE_RES_PRMS, true>(Xq, W1q, gamma, R, sx, sw1, H, HG, part, M, K1, D, stream);
+                                     const uint16_t* R, uint16_t* H, float* part, int M, int K1, int D,
+                                     hipStream_t stream) {
+  return launch_gemm<MODE_RES_PRMS, true>(Xq, W1q, nullptr, R, sx, sw1, H, nullptr, part, M, K1, D, stream);
 }
 
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream) {
@@ -467,10 +516,11 @@ hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps,
   return hipGetLastError();
 }
 
-hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* HG, uint8_t* HQ,
-                                    float* r, float* sa, float* rs2, hipStream_t stream) {
+hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* H,
+                                    const float* gamma, uint8_t* HQ, float* r, float* sa, float* rs2,
+                                    hipStream_t stream) {
   dim3 grid((M + 3) / 4), block(256);
-  hipLaunchKernelGGL(prms_reduce_quant_kernel, grid, block, 0, stream, part, T, M, D, eps, HG, HQ, r, sa, rs2);
+  hipLaunchKernelGGL(prms_reduce_quant_kernel, grid, block, 0, stream, part, T, M, D, eps, H, gamma, HQ, r, sa, rs2);
   return hipGetLastError();
 }
 

@@ -25,11 +25,13 @@ hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float*
 // ---- e4m3 operands (scales: dequantised value = code * scale) ----
 // K1: as launch_gemm1_res_prms with X W1 = (Xq W1q) * sx[m] * sw1[n].
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
-                                     const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* HG, float* part,
-                                     int M, int K1, int D, hipStream_t stream);
-// K2: r from the partial sums; HQ = e4m3(HG / sa) per row with sa = amax|HG row| / 448; rs2 = sa * r.
-hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* HG, uint8_t* HQ,
-                                    float* r, float* sa, float* rs2, hipStream_t stream);
+                                     const uint16_t* R, uint16_t* H, float* part, int M, int K1, int D,
+                                     hipStream_t stream);
+// K2: r from the partial sums; with a = H * gamma (fp32), HQ = e4m3(a * (1 / sa)) per row, sa = amax|a row| / 448;
+// rs2 = sa * r.
+hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* H,
+                                    const float* gamma, uint8_t* HQ, float* r, float* sa, float* rs2,
+                                    hipStream_t stream);
 // K3 / U3: Y = bf16(epi((Aq W2q) * rowsc[m] * sw2[n])).
 hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,
                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream);

@@ -82,7 +82,8 @@ const char* coda_last_error(void);
  *   fp8:     0 for the bf16 entry points, 1 for the *_fp8 ones
  *   unfused: 0 for coda_block_fwd*, 1 for coda_block_unfused*
  * Layout (each piece 256-byte aligned): part [D/256][M] fp32 partial sums of squares, r [M] fp32, then
- *   fused:   hg = h * gamma [M,D] bf16 (+ fp8: its e4m3 quantisation [M,D], the row scales [M], s_a*r [M])
+ *   fused:   bf16: hg = h * gamma [M,D] bf16; fp8: the e4m3 quantisation of h * gamma [M,D], its row scales
+ *            s_a [M] and s_a * r [M]
  *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]). */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
@@ -102,9 +103,9 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
  *   Xq [M,K1] e4m3 with per-row scales sx [M]; W1q [K1,D] e4m3 with per-column scales sw1 [D];
  *   W2q [D,N2] e4m3 with per-column scales sw2 [N2]; R [M,D] bf16; gamma [D] fp32.
  *   out_h = bf16(dequant(Xq) dequant(W1q) + R); out_y as coda_block_fwd.
- * The second product's A operand is h * gamma quantised per row to e4m3 with scale
- * s_a = amax_j |bf16(h_ij gamma_j)| / 448 (1 for an all-zero row) by the reduction kernel, which has the
- * whole row; y = bf16(epi(acc * s_a_i * r_i * sw2_n)).  Shape rules as coda_block_fwd, and K1 a multiple
+ * The second product's A operand is a = h * gamma (fp32, h the stored bf16 out_h) quantised per row to
+ * e4m3(a * (1 / s_a)) with s_a = amax_j |a_ij| / 448 (1 for an all-zero row; 1 / s_a rounded to fp32 once)
+ * by the reduction kernel, which has the whole row; y = bf16(epi(acc * s_a_i * r_i * sw2_n)).  Shape rules as coda_block_fwd, and K1 a multiple
  * of 256.  Workspace: coda_workspace_bytes(..., fp8 = 1, unfused = 0). */
 int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
                        const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
