@@ -269,11 +269,6 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)(p));
 }
 
-struct Frags8 {
-  i32x8 a[4];
-  i32x8 b[NB];
-};
-
 struct LaneOffs8 {
   int a;      // A fragment (rows mb*32 add 2 KiB each; the second 16 bytes sit at the next slot)
   int a2;
@@ -295,7 +290,8 @@ __device__ __forceinline__ void lane_offsets8(int wm, int wn, int lane, LaneOffs
   o.a2 = a_off(m, 2 * (lane >> 5) + 1);
 }
 
-__device__ __forceinline__ void read_frags8(const char* st, const LaneOffs8& o, Frags8& f) {
+// Fragment reads: B for both 32-column blocks (four transposing reads each), A for one 32-row block.
+__device__ __forceinline__ void read_b8(const char* st, const LaneOffs8& o, i32x8 (&b)[NB]) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const char* p = st + o.b[nb];
@@ -303,28 +299,33 @@ __device__ __forceinline__ void read_frags8(const char* st, const LaneOffs8& o, 
     const i32x2 r1 = lds_read_tr8(p + 8 * 256);
     const i32x2 r2 = lds_read_tr8(p + 16 * 256);
     const i32x2 r3 = lds_read_tr8(p + 24 * 256);
-    f.b[nb] = (i32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
-  }
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const u32x4 lo = *(const u32x4*)(st + o.a + mb * 32 * 64);
-    const u32x4 hi = *(const u32x4*)(st + o.a2 + mb * 32 * 64);
-    f.a[mb] = (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    b[nb] = (i32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
   }
 }
+__device__ __forceinline__ i32x8 read_a8(const char* st, const LaneOffs8& o, int mb) {
+  const u32x4 lo = *(const u32x4*)(st + o.a + mb * 32 * 64);
+  const u32x4 hi = *(const u32x4*)(st + o.a2 + mb * 32 * 64);
+  return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
 
-__device__ __forceinline__ void mma8(const Frags8& f, f32x16 (&acc)[4][NB]) {
+// Row blocks mb0 and mb0+1 times both column blocks.  Operand formats 0 = e4m3 (cbsz for the first operand,
+// blgp for the second); E8M0 block scales 127 = 1.0 (the real scales are applied in the epilogue).
+__device__ __forceinline__ void mma8_rows(const i32x8 (&b)[NB], const i32x8& a0, const i32x8& a1, int mb0,
+                                          f32x16 (&acc)[4][NB]) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int nb = 0; nb < NB; ++nb)
+    acc[mb0][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[nb], a0, acc[mb0][nb], 0, 0, 0, 127, 0, 127);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      // operand formats 0 = e4m3 (cbsz for the first operand, blgp for the second); E8M0 scales 127 = 1.0
-      acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[nb], f.a[mb], acc[mb][nb], 0, 0, 0, 127, 0, 127);
+  for (int nb = 0; nb < NB; ++nb)
+    acc[mb0 + 1][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[nb], a1, acc[mb0 + 1][nb], 0, 0, 0, 127, 0, 127);
 }
 
 // acc = A[m0:m0+256, :] * B[:, tile columns], e4m3 operands, fp32 accumulation (K % K8_MULTIPLE == 0).
 //   A: [M,K] bytes, row stride lda bytes; B: [K,*] bytes, row stride ldb bytes; bcol(c) = global column of
 //   the tile's 16-column chunk c (0..15).
+// A step's fragments are split into X = {B blocks, A row blocks 0,1}, double-buffered across steps, and
+// Y = {A row blocks 2,3}: the first half multiplies row blocks 0,1 while Y is read; after the barrier the
+// second half multiplies row blocks 2,3 while the next stage's X is read into the other buffer.
 template <class BCol>
 __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A, int64_t lda, int M, int m0,
                                                   const uint8_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
@@ -369,22 +370,36 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
     for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + (int64_t)k0 * ldb, st + A_BYTES + (LPW * wave + i) * 1024);
   };
 
-  Frags8 f;
-  // one K step on stage U: the fragments of tile kt are in f on entry
+  i32x8 xb[2][NB], xa[2][2], ya[2];
+  // one K step on stage U; X[U % 2] holds the stage's B and A row blocks 0,1 on entry
   auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c) {
     constexpr int U = decltype(U_c)::value;
+    constexpr int P = U & 1;
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr int WAIT = decltype(wait_c)::value;
+    const char* cur = smem + U * STAGE_BYTES;
     if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
-    mma8(f, acc);
-    // keep the step's shape (MFMAs, barrier, next fragments into the same registers): letting the
-    // scheduler overlap steps needs a second fragment set, which does not fit next to the accumulators
-    __builtin_amdgcn_sched_barrier(0);
+    ya[0] = read_a8(cur, lo, 2);
+    ya[1] = read_a8(cur, lo, 3);
+    mma8_rows(xb[P], xa[P][0], xa[P][1], 0, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
     if (WAIT >= 0) {
       wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
-      read_frags8(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, lo, f);
+      const char* nxt = smem + ((U + 1) % NSTAGE) * STAGE_BYTES;
+      read_b8(nxt, lo, xb[1 - P]);
+      xa[1 - P][0] = read_a8(nxt, lo, 0);
+      xa[1 - P][1] = read_a8(nxt, lo, 1);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    mma8_rows(xb[P], ya[0], ya[1], 2, acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -397,7 +412,9 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
 #pragma unroll
   for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
   wait_barrier<2 * PER>();
-  read_frags8(smem, lo, f);
+  read_b8(smem, lo, xb[0]);
+  xa[0][0] = read_a8(smem, lo, 0);
+  xa[0][1] = read_a8(smem, lo, 1);
 
   const int nblk = nk / NSTAGE;
   for (int bi = 0; bi < nblk - 1; ++bi) {
