@@ -73,6 +73,9 @@ def _load():
     for name in ("oracle_dequant_rows_e4m3", "oracle_dequant_cols_e4m3"):
         getattr(lib, name).argtypes = [i64, i64, u8p, fp, dp]
         getattr(lib, name).restype = ctypes.c_int
+    lib.oracle_block_bwd_f64.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, dp, f, dp, dp, dp, dp, dp, dp, dp,
+                                         ctypes.c_int]
+    lib.oracle_block_bwd_f64.restype = ctypes.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ctypes.c_int
     _lib = lib
@@ -123,6 +126,35 @@ def block_fused(X, W1, R, gamma, W2, eps, epi, nthreads=0):
 def block_roundpts(X, W1, R, gamma, W2, eps, epi, nthreads=0):
     """Reparameterised order with bf16 storage roundings of h, diag(gamma) W2 and y (diagnostic)."""
     return _block("oracle_block_roundpts_f64", X, W1, R, gamma, W2, eps, epi, nthreads)
+
+
+def block_bwd(X, W1, R, gamma, W2, eps, dz, dh_out=None, nthreads=0):
+    """Backward of the block given dz [M,N2] (gradient of z = (h r gamma) W2, before the epilogue) and dh_out
+    [M,D] (gradient arriving at h; None for none).  Returns (dX, dW1, dR, dgamma, dW2) in fp64."""
+    lib = _load()
+    X, W1, R, gamma, W2, dz = (_f64(a) for a in (X, W1, R, gamma, W2, dz))
+    M, K1 = X.shape
+    K1b, D = W1.shape
+    Db, N2 = W2.shape
+    if K1b != K1 or Db != D or R.shape != (M, D) or gamma.shape != (D,) or dz.shape != (M, N2):
+        raise ValueError("oracle: inconsistent shapes")
+    dhp = None
+    if dh_out is not None:
+        dh_out = _f64(dh_out)
+        if dh_out.shape != (M, D):
+            raise ValueError("oracle: inconsistent shapes")
+        dhp = _ptr(dh_out)
+    dX = np.empty((M, K1), np.float64)
+    dW1 = np.empty((K1, D), np.float64)
+    dR = np.empty((M, D), np.float64)
+    dgamma = np.empty((D,), np.float64)
+    dW2 = np.empty((D, N2), np.float64)
+    rc = lib.oracle_block_bwd_f64(M, K1, D, N2, _ptr(X), _ptr(W1), _ptr(R), _ptr(gamma), _ptr(W2), float(eps),
+                                  _ptr(dz), dhp, _ptr(dX), _ptr(dW1), _ptr(dR), _ptr(dgamma), _ptr(dW2),
+                                  int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_block_bwd_f64 failed with {rc}")
+    return dX, dW1, dR, dgamma, dW2
 
 
 def gemm_residual(X, W1, R=None, nthreads=0):

@@ -341,3 +341,132 @@ int oracle_block_roundpts_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, cons
                               int nthreads) {
   return run_block(FORM_ROUNDPTS, M, K1, D, N2, X, W1, R, gamma, W2, eps, epi, out_h, out_r, out_y, nthreads);
 }
+
+/* ------------------------------------------------------------------------------------------------ */
+/* backward of the block                                                                            */
+/*
+ * The CODA write-up (section "CODA: the treasure hidden in the epilogue", and its results section on the
+ * backward kernels) applies the same epilogue programming to back-propagation.  The reference here is the
+ * textbook chain rule of the forward definition above, in the unfused order, with the gradient dz of the
+ * second product's output (before any epilogue) and the gradient dh_out arriving at h from downstream
+ * (h is the residual stream):
+ *   h = X W1 + R;  r_i = 1/sqrt(mean_j h_ij^2 + eps);  n = r h;  u = n * gamma;  z = u W2
+ *   du = dz W2^T;  dW2 = u^T dz;  dgamma_j = sum_i du_ij n_ij;  dn = du * gamma
+ *   dh_ij = r_i (dn_ij - n_ij mean_j'(dn_ij' n_ij')) + dh_out_ij;  dR = dh;  dX = dh W1^T;  dW1 = X^T dh
+ * Sums over rows run in row order, sums over columns in column order.
+ */
+
+typedef struct {
+  int64_t K1, D, N2;
+  const double *X, *W1, *R, *gamma, *W2, *dz, *dh_out;
+  double eps;
+  double *u, *n, *du, *dh, *dX;
+} bwd_ctx;
+
+/* scratch per thread: h row (D) */
+static void bwd_row(void* p, int64_t i, double* scratch) {
+  bwd_ctx* c = (bwd_ctx*)p;
+  const int64_t K1 = c->K1, D = c->D, N2 = c->N2;
+  double* hrow = scratch;
+  for (int64_t j = 0; j < D; ++j) hrow[j] = 0.0;
+  for (int64_t k = 0; k < K1; ++k) {
+    double x = c->X[i * K1 + k];
+    const double* w = c->W1 + k * D;
+    for (int64_t j = 0; j < D; ++j) hrow[j] += x * w[j];
+  }
+  for (int64_t j = 0; j < D; ++j) hrow[j] += c->R[i * D + j];
+  const double r = rms_scale_of_row(hrow, D, c->eps);
+  double* n = c->n + i * D;
+  double* u = c->u + i * D;
+  double* du = c->du + i * D;
+  double* dh = c->dh + i * D;
+  for (int64_t j = 0; j < D; ++j) {
+    n[j] = r * hrow[j];
+    u[j] = n[j] * c->gamma[j];
+  }
+  /* du_ij = sum_n dz_in W2_jn */
+  const double* dzi = c->dz + i * N2;
+  for (int64_t j = 0; j < D; ++j) {
+    const double* w = c->W2 + j * N2;
+    double s = 0.0;
+    for (int64_t q = 0; q < N2; ++q) s += dzi[q] * w[q];
+    du[j] = s;
+  }
+  /* RMSNorm backward: dn = du * gamma; dh = r (dn - n mean(dn n)) (+ dh_out) */
+  double dot = 0.0;
+  for (int64_t j = 0; j < D; ++j) dot += du[j] * c->gamma[j] * n[j];
+  const double mean = dot / (double)D;
+  for (int64_t j = 0; j < D; ++j) {
+    double v = r * (du[j] * c->gamma[j] - n[j] * mean);
+    if (c->dh_out) v += c->dh_out[i * D + j];
+    dh[j] = v;
+  }
+  /* dX_ik = sum_j dh_ij W1_kj */
+  for (int64_t k = 0; k < K1; ++k) {
+    const double* w = c->W1 + k * D;
+    double s = 0.0;
+    for (int64_t j = 0; j < D; ++j) s += dh[j] * w[j];
+    c->dX[i * K1 + k] = s;
+  }
+}
+
+typedef struct {
+  int64_t M, K1, D, N2;
+  const double *X, *dz;
+  const double *u, *n, *du, *dh;
+  double *dW1, *dgamma, *dW2;
+} bwd_w_ctx;
+
+/* one row j of dW2 [D,N2] and dgamma_j; sums over the data rows i in order */
+static void bwd_w2_row(void* p, int64_t j, double* scratch) {
+  bwd_w_ctx* c = (bwd_w_ctx*)p;
+  (void)scratch;
+  const int64_t D = c->D, N2 = c->N2;
+  double* out = c->dW2 + j * N2;
+  for (int64_t q = 0; q < N2; ++q) out[q] = 0.0;
+  double g = 0.0;
+  for (int64_t i = 0; i < c->M; ++i) {
+    const double a = c->u[i * D + j];
+    const double* dzi = c->dz + i * N2;
+    for (int64_t q = 0; q < N2; ++q) out[q] += a * dzi[q];
+    g += c->du[i * D + j] * c->n[i * D + j];
+  }
+  c->dgamma[j] = g;
+}
+
+/* one row k of dW1 [K1,D]: dW1_kj = sum_i X_ik dh_ij */
+static void bwd_w1_row(void* p, int64_t k, double* scratch) {
+  bwd_w_ctx* c = (bwd_w_ctx*)p;
+  (void)scratch;
+  const int64_t K1 = c->K1, D = c->D;
+  double* out = c->dW1 + k * D;
+  for (int64_t j = 0; j < D; ++j) out[j] = 0.0;
+  for (int64_t i = 0; i < c->M; ++i) {
+    const double x = c->X[i * K1 + k];
+    const double* d = c->dh + i * D;
+    for (int64_t j = 0; j < D; ++j) out[j] += x * d[j];
+  }
+}
+
+int oracle_block_bwd_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const double* X, const double* W1,
+                         const double* R, const double* gamma, const double* W2, double eps, const double* dz,
+                         const double* dh_out, double* out_dX, double* out_dW1, double* out_dR,
+                         double* out_dgamma, double* out_dW2, int nthreads) {
+  if (M < 0 || K1 <= 0 || D <= 0 || N2 <= 0) return -1;
+  if (!X || !W1 || !R || !gamma || !W2 || !dz || !out_dX || !out_dW1 || !out_dR || !out_dgamma || !out_dW2)
+    return -1;
+  if (!(eps >= 0.0)) return -1;
+  const size_t md = (size_t)M * (size_t)D;
+  double* buf = (double*)malloc(3 * md * sizeof(double) + 1);
+  if (!buf) return -2;
+  double *u = buf, *n = buf + md, *du = buf + 2 * md;
+  bwd_ctx c = {K1, D, N2, X, W1, R, gamma, W2, dz, dh_out, eps, u, n, du, out_dR, out_dX};
+  int rc = for_each_row(M, nthreads, (size_t)D, bwd_row, &c);
+  if (rc == 0) {
+    bwd_w_ctx w = {M, K1, D, N2, X, dz, u, n, du, out_dR, out_dW1, out_dgamma, out_dW2};
+    rc = for_each_row(D, nthreads, 0, bwd_w2_row, &w);
+    if (rc == 0) rc = for_each_row(K1, nthreads, 0, bwd_w1_row, &w);
+  }
+  free(buf);
+  return rc;
+}

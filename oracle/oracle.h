@@ -72,6 +72,15 @@ int oracle_block_roundpts_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, cons
                               double eps, int epi, double* out_h, double* out_r, double* out_y,
                               int nthreads);
 
+/* Backward of the block (chain rule of the unfused order; see oracle.c): given dz [M,N2], the gradient of
+ * z = (h * r * gamma) W2 (the second product's output before the epilogue), and dh_out [M,D] (the gradient
+ * arriving at h from downstream, NULL for none), computes dX [M,K1], dW1 [K1,D], dR [M,D] (= dh),
+ * dgamma [D] and dW2 [D,N2].  h and r are recomputed from X, W1, R. */
+int oracle_block_bwd_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const double* X, const double* W1,
+                         const double* R, const double* gamma, const double* W2, double eps, const double* dz,
+                         const double* dh_out, double* out_dX, double* out_dW1, double* out_dR,
+                         double* out_dgamma, double* out_dW2, int nthreads);
+
 /* silu(x) = x / (1 + exp(-x)) */
 double oracle_silu(double x);
 

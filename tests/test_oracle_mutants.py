@@ -3,8 +3,8 @@
 Each case copies the oracle's C source, plants one plausible mistake (eps outside the square root, a
 dropped residual, a transposed operand, gate and up swapped, r applied twice, gamma dropped, a wrong
 mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent in the fp8
-decoder), rebuilds it in a temporary directory and runs the pin tests against it.  Every mutant must fail
-at least one pin; the unmodified oracle is never touched.
+decoder, and seven mistakes in the backward), rebuilds it in a temporary directory and runs the pin tests
+against it.  Every mutant must fail at least one pin; the unmodified oracle is never touched.
 """
 import os
 import shutil
@@ -28,6 +28,41 @@ MUTANTS = [
     ("silu_sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
     ("e4m3_subnormal", "v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
 ]
+
+
+# mistakes in the backward: the RMS correction term dropped, its sign flipped, r applied twice, dh_out
+# dropped, W1 untransposed in dX, u replaced by n in dW2, gamma dropped from dgamma's product
+MUTANTS_BWD = [
+    ("bwd_no_correction", "double v = r * (du[j] * c->gamma[j] - n[j] * mean);", "double v = r * (du[j] * c->gamma[j]);"),
+    ("bwd_correction_sign", "double v = r * (du[j] * c->gamma[j] - n[j] * mean);",
+     "double v = r * (du[j] * c->gamma[j] + n[j] * mean);"),
+    ("bwd_r_twice", "double v = r * (du[j] * c->gamma[j] - n[j] * mean);",
+     "double v = r * r * (du[j] * c->gamma[j] - n[j] * mean);"),
+    ("bwd_dh_out_dropped", "if (c->dh_out) v += c->dh_out[i * D + j];", ";"),
+    ("bwd_dx_w1_index", "for (int64_t j = 0; j < D; ++j) s += dh[j] * w[j];",
+     "for (int64_t j = 0; j < D; ++j) s += dh[j] * c->W1[(j % K1) * D + k % D];"),
+    ("bwd_dw2_uses_n", "const double a = c->u[i * D + j];", "const double a = c->n[i * D + j];"),
+    ("bwd_dgamma_uses_u", "g += c->du[i * D + j] * c->n[i * D + j];", "g += c->du[i * D + j] * c->u[i * D + j];"),
+]
+
+
+def _run_pins(tmp_path, name, before, after, pins):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert before in src, f"mutation site for {name} no longer exists"
+    shutil.copytree(os.path.join(ROOT, "oracle"), tmp_path / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tmp_path / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py"))
+    (tmp_path / "oracle" / "oracle.c").write_text(src.replace(before, after, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", pins, "-q", "-x", "-p", "no:cacheprovider"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 1, f"mutant {name} was not caught:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout
+
+
+@pytest.mark.parametrize("name,before,after", MUTANTS_BWD, ids=[m[0] for m in MUTANTS_BWD])
+def test_backward_pins_catch_planted_mistake(tmp_path, name, before, after):
+    _run_pins(tmp_path, name, before, after, "tests/test_oracle_bwd_pins.py")
 
 
 @pytest.mark.parametrize("name,before,after", MUTANTS, ids=[m[0] for m in MUTANTS])
