@@ -27,7 +27,8 @@ STATUS = {0: "CODA_OK", 1: "CODA_ERR_INVALID_ARG", 2: "CODA_ERR_UNSUPPORTED", 3:
 EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_workspace_bytes",
            "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused", "coda_block_fwd_fp8",
            "coda_block_unfused_fp8",
-           "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale")
+           "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
+           "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused")
 
 
 class CodaError(RuntimeError):
@@ -68,6 +69,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.coda_partial_rms_reduce.restype = i32
     lib.coda_gemm2_rowscale.argtypes = [vp, vp, vp, i32, vp, i64, i64, i64, vp]
     lib.coda_gemm2_rowscale.restype = i32
+    lib.coda_bwd_workspace_bytes.argtypes, lib.coda_bwd_workspace_bytes.restype = [i64, i64, i64, i64, i32], sz
+    bwd = [vp] * 13 + [i64, i64, i64, i64, vp, sz, vp]
+    for name in ("coda_block_bwd", "coda_block_bwd_unfused"):
+        getattr(lib, name).argtypes = bwd
+        getattr(lib, name).restype = i32
     _lib = lib
     return lib
 
@@ -210,3 +216,47 @@ def workspace_r(workspace: torch.Tensor, M: int, D: int) -> torch.Tensor:
     """View of r [M] fp32 inside a workspace after coda_block_fwd / coda_block_unfused."""
     off = coda_workspace_r_offset(M, D)
     return workspace[off: off + 4 * M].view(torch.float32)
+
+
+def coda_bwd_workspace_bytes(M: int, K1: int, D: int, N2: int, unfused: int = 0) -> int:
+    return load().coda_bwd_workspace_bytes(M, K1, D, N2, unfused)
+
+
+def alloc_bwd_workspace(M: int, K1: int, D: int, N2: int, unfused: int = 0, device="cuda"):
+    n = coda_bwd_workspace_bytes(M, K1, D, N2, unfused)
+    if n == 0:
+        raise ValueError("no workspace size for these dimensions")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _block_bwd(name, X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, workspace,
+               stream):
+    M, K1 = X.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    bf = torch.bfloat16
+    args = (_dev(X, "X", bf, (M, K1)), _dev(W1, "W1", bf, (K1, D)), _dev(h, "h", bf, (M, D)),
+            _dev(r, "r", torch.float32, (M,)), _dev(gamma, "gamma", torch.float32, (D,)),
+            _dev(W2, "W2", bf, (D, N2)), _dev(dz, "dz", bf, (M, N2)),
+            None if dh_out is None else _dev(dh_out, "dh_out", bf, (M, D)),
+            _dev(out_dX, "out_dX", bf, (M, K1)), _dev(out_dW1, "out_dW1", torch.float32, (K1, D)),
+            _dev(out_dR, "out_dR", bf, (M, D)), _dev(out_dgamma, "out_dgamma", torch.float32, (D,)),
+            _dev(out_dW2, "out_dW2", torch.float32, (D, N2)))
+    ws = _dev(workspace, "workspace", torch.uint8)
+    st = getattr(load(), name)(*args, M, K1, D, N2, ws, workspace.numel(), _stream(stream))
+    _check(st, name)
+
+
+def coda_block_bwd(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, workspace,
+                   stream=None):
+    """Backward of the block (fused path): dX, dW1, dR (= dh), dgamma, dW2 from dz (gradient of the second
+    product's output) and dh_out (gradient arriving at h; None for none), with h and r from the forward."""
+    _block_bwd("coda_block_bwd", X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2,
+               workspace, stream)
+
+
+def coda_block_bwd_unfused(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2,
+                           workspace, stream=None):
+    """Unfused backward baseline with the same outputs."""
+    _block_bwd("coda_block_bwd_unfused", X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma,
+               out_dW2, workspace, stream)

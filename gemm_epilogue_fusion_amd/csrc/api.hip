@@ -173,6 +173,65 @@ int validate_block(const void* X, const float* sx, const void* W1, const float* 
   return check_alias(in, 8, out, 3, out_h, R);
 }
 
+// ---- backward ----
+struct BwdWorkspace {
+  uint16_t* G;    // r gamma P [M,D] bf16 (unfused: after P itself)
+  float* part;    // row partials [D/256][M]
+  float* part2;   // column partials [ceil(M/256)][D]
+  float* a;       // [M]
+  uint16_t* dhT;  // [D,M] bf16
+  uint16_t* nT;   // [D,M] bf16
+  uint16_t* P;    // unfused: P = dz W2^T [M,D] bf16
+};
+
+size_t carve_bwd(void* ws, int64_t M, int64_t D, int unfused, BwdWorkspace* w) {
+  char* base = (char*)ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  BwdWorkspace x{};
+  x.G = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+  x.part = (float*)take(ws_part_bytes(M, D));
+  x.part2 = (float*)take(align256((size_t)((M + 255) / 256) * (size_t)D * 4));
+  x.a = (float*)take(ws_vec_bytes(M));
+  x.dhT = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+  x.nT = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+  if (unfused) x.P = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+  if (w) *w = x;
+  return off;
+}
+
+int validate_bwd(const void* X, const void* W1, const void* h, const float* r, const float* gamma, const void* W2,
+                 const void* dz, const void* dh_out, void* dX, float* dW1, void* dR, float* dgamma, float* dW2,
+                 int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace, size_t workspace_bytes, int unfused) {
+  int s;
+  if ((s = check_ptr(X, "X")) || (s = check_ptr(W1, "W1")) || (s = check_ptr(h, "h")) || (s = check_ptr(r, "r")) ||
+      (s = check_ptr(gamma, "gamma")) || (s = check_ptr(W2, "W2")) || (s = check_ptr(dz, "dz")) ||
+      (s = check_ptr(dX, "out_dX")) || (s = check_ptr(dW1, "out_dW1")) || (s = check_ptr(dR, "out_dR")) ||
+      (s = check_ptr(dgamma, "out_dgamma")) || (s = check_ptr(dW2, "out_dW2")))
+    return s;
+  if (dh_out && (s = check_ptr(dh_out, "dh_out"))) return s;
+  if ((s = check_dims(M, K1, D, N2))) return s;
+  if (M % 128) return fail(CODA_ERR_UNSUPPORTED, "backward: M=%lld is not a multiple of 128", (long long)M);
+  if (K1 % 256) return fail(CODA_ERR_UNSUPPORTED, "backward: K1=%lld is not a multiple of 256", (long long)K1);
+  const size_t need = carve_bwd(nullptr, M, D, unfused, nullptr);
+  if (!workspace) return fail(CODA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)workspace & 255) return fail(CODA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(CODA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  const Range in[8] = {rng("X", X, (size_t)(M * K1) * 2), rng("W1", W1, (size_t)(K1 * D) * 2),
+                       rng("h", h, (size_t)(M * D) * 2),  rng("r", r, (size_t)M * 4),
+                       rng("gamma", gamma, (size_t)D * 4), rng("W2", W2, (size_t)(D * N2) * 2),
+                       rng("dz", dz, (size_t)(M * N2) * 2), rng("dh_out", dh_out, dh_out ? (size_t)(M * D) * 2 : 0)};
+  const Range out[6] = {rng("out_dX", dX, (size_t)(M * K1) * 2),     rng("out_dW1", dW1, (size_t)(K1 * D) * 4),
+                        rng("out_dR", dR, (size_t)(M * D) * 2),      rng("out_dgamma", dgamma, (size_t)D * 4),
+                        rng("out_dW2", dW2, (size_t)(D * N2) * 4),   rng("workspace", workspace, need)};
+  return check_alias(in, 8, out, 6, nullptr, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -373,6 +432,83 @@ int coda_gemm2_rowscale(const void* hg, const void* W2, const float* r, int epi_
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t coda_bwd_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused) {
+  (void)K1;
+  (void)N2;
+  if (M < 1 || D < 1) return 0;
+  return carve_bwd(nullptr, M, D, unfused ? 1 : 0, nullptr);
+}
+
+static int block_bwd(const void* X, const void* W1, const void* h, const float* r, const float* gamma, const void* W2,
+                     const void* dz, const void* dh_out, void* out_dX, float* out_dW1, void* out_dR,
+                     float* out_dgamma, float* out_dW2, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                     void* workspace, size_t workspace_bytes, void* stream, int unfused) {
+  try {
+    int s = validate_bwd(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, M, K1, D,
+                         N2, workspace, workspace_bytes, unfused);
+    if (s) return s;
+    hipStream_t st = (hipStream_t)stream;
+    BwdWorkspace w;
+    carve_bwd(workspace, M, D, unfused, &w);
+    const uint16_t* hh = (const uint16_t*)h;
+    if (unfused) {
+      // P = dz W2^T stored, then its row and column statistics in a separate pass
+      if ((s = hip_check(coda::launch_gemm_nt_store((const uint16_t*)dz, (const uint16_t*)W2, w.P, (int)M, (int)N2,
+                                                    (int)D, st),
+                         "bwd P launch")))
+        return s;
+      if ((s = hip_check(coda::launch_bwd_p_from_mem(w.P, hh, r, gamma, w.G, w.part, w.part2, (int)M, (int)D, st),
+                         "bwd P statistics launch")))
+        return s;
+    } else {
+      if ((s = hip_check(coda::launch_bwd_p((const uint16_t*)dz, (const uint16_t*)W2, hh, r, gamma, w.G, w.part,
+                                            w.part2, (int)M, (int)D, (int)N2, st),
+                         "bwd P launch")))
+        return s;
+    }
+    if ((s = hip_check(coda::launch_bwd_reduce(w.part, (int)(D / 256), w.part2, (int)((M + 255) / 256), r, (int)M,
+                                               (int)D, w.a, out_dgamma, st),
+                       "bwd reduce launch")))
+      return s;
+    if ((s = hip_check(coda::launch_bwd_dh(w.G, hh, (const uint16_t*)dh_out, r, w.a, (int)M, (int)D,
+                                           (uint16_t*)out_dR, w.dhT, w.nT, st),
+                       "bwd dh launch")))
+      return s;
+    if ((s = hip_check(coda::launch_gemm_nt_store((const uint16_t*)out_dR, (const uint16_t*)W1, (uint16_t*)out_dX,
+                                                  (int)M, (int)D, (int)K1, st),
+                       "bwd dX launch")))
+      return s;
+    if ((s = hip_check(coda::launch_gemm_f32_trans(w.dhT, (const uint16_t*)X, out_dW1, (int)D, (int)M, (int)K1, st),
+                       "bwd dW1 launch")))
+      return s;
+    return hip_check(coda::launch_gemm_f32_rowscale(w.nT, (const uint16_t*)dz, gamma, out_dW2, (int)D, (int)M,
+                                                    (int)N2, st),
+                     "bwd dW2 launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_block_bwd(const void* X, const void* W1, const void* h, const float* r, const float* gamma, const void* W2,
+                   const void* dz, const void* dh_out, void* out_dX, float* out_dW1, void* out_dR, float* out_dgamma,
+                   float* out_dW2, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return block_bwd(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, M, K1, D, N2,
+                   workspace, workspace_bytes, stream, 0);
+}
+
+int coda_block_bwd_unfused(const void* X, const void* W1, const void* h, const float* r, const float* gamma,
+                           const void* W2, const void* dz, const void* dh_out, void* out_dX, float* out_dW1,
+                           void* out_dR, float* out_dgamma, float* out_dW2, int64_t M, int64_t K1, int64_t D,
+                           int64_t N2, void* workspace, size_t workspace_bytes, void* stream) {
+  return block_bwd(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, M, K1, D, N2,
+                   workspace, workspace_bytes, stream, 1);
 }
 
 }  // extern "C"

@@ -1,0 +1,408 @@
+// bwd_kernels.hip -- backward of the GEMM -> residual -> RMSNorm -> GEMM block for gfx950.
+//
+// The CODA write-up ("CODA: new research optimizes Transformer training with GEMM-epilogue programming",
+// sections "CODA: the treasure hidden in the epilogue" and "Experimental results") applies the epilogue
+// rewrite to back-propagation as well.  Forward: h = X W1 + R, r_i = 1/sqrt(mean_j h_ij^2 + eps), n = r h,
+// u = n * gamma, z = u W2.  Given dz (the gradient of z) and dh_out (the gradient arriving at the residual
+// stream h), the textbook backward is
+//   du = dz W2^T;  dgamma_j = sum_i du_ij n_ij;  dh = r (du gamma - n mean_j(du_ij gamma_j n_ij)) + dh_out
+//   dR = dh;  dX = dh W1^T;  dW1 = X^T dh;  dW2 = u^T dz.
+// With P = dz W2^T the per-row pieces become
+//   dh_ij = r_i gamma_j P_ij - a_i h_ij + dh_out_ij,   a_i = r_i^3 S_i / D,   S_i = sum_j gamma_j P_ij h_ij
+//   dgamma_j = sum_i P_ij r_i h_ij,                    dW2 = diag(gamma) (n^T dz)
+// so the kernels are
+//   B1 bwd_p      : P = dz W2^T (W2 read as its own [D,N2] rows, K = N2); the epilogue, with the tile's h, r
+//                   and gamma, stores G = r gamma P (bf16), per-row partial sums of gamma P h (one slot per
+//                   column tile) and per-column partial sums of P r h (one slot per row tile)
+//   B2 bwd_reduce : a_i from the row partials (summed in tile order), dgamma from the column partials
+//   B3 bwd_dh     : dh = G - a h + dh_out -> dR (bf16), and the transposes dh^T, n^T [D,M] (bf16)
+//   B4 dX  = dh W1^T        (W1 read as its own [K1,D] rows)
+//   B5 dW1 = (dh^T X)^T     (fp32, the tile stored transposed)
+//   B6 dW2 = diag(gamma) (n^T dz)   (fp32, gamma as the output row scale)
+// The unfused baseline replaces B1 by a GEMM that stores du = P (bf16) and a separate pass over du and h
+// that computes what B1's epilogue computes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm_core.h"
+#include "launch.h"
+
+namespace coda {
+
+enum BwdMode { BWD_P = 0, BWD_P_FROM_MEM = 1, BWD_STORE_BF16 = 2, BWD_F32_ROWSCALE = 3, BWD_F32_TRANS = 4 };
+
+struct BwdArgs {
+  const uint16_t* A;   // [M, K] row-major
+  const uint16_t* B;   // [K, Nb] row-major, or (BT) [Nb, K] row-major
+  const uint16_t* h;   // BWD_P*: h [M, Nb]
+  const float* r;      // BWD_P*: r [M]
+  const float* gamma;  // BWD_P*: gamma [Nb];  BWD_F32_ROWSCALE: the output row scale [M]
+  uint16_t* out;       // bf16 output [M, Nb] (G or the plain product)
+  float* outf;         // fp32 output: [M, Nb], or [Nb, M] (BWD_F32_TRANS)
+  float* part;         // BWD_P*: row partials [Nb/256][M]
+  float* part2;        // BWD_P*: column partials [ceil(M/256)][Nb]
+  int M, K, Nb, group_m;
+};
+
+struct RowsFrom {
+  int64_t n0;
+  __device__ int64_t operator()(int r) const { return n0 + r; }
+};
+
+// fp32 tile staging: 128 rows x 256 columns, row pitch 1 KiB, 16-byte chunk c of row r at c ^ (r % 64)
+__device__ __forceinline__ int f32_off(int r, int c) { return r * 1024 + ((c ^ (r & 63)) << 4); }
+// transposed fp32 staging: 256 rows (the tile's columns) x 128 columns (the tile's rows), pitch 512 B,
+// 4-byte word w of row q at word (w ^ 32 (q % 2)) so that the two lane halves use different banks
+__device__ __forceinline__ int f32t_off(int q, int w) { return q * 512 + ((w ^ ((q & 1) << 5)) << 2); }
+
+template <int MODE, bool BT>
+__global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
+  constexpr bool PMODE = MODE == BWD_P || MODE == BWD_P_FROM_MEM;
+  // the mainloop ring (reused as the staging area), plus the row / column partial-sum exchanges
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (PMODE ? 6144 : 0)];
+  const int M = args.M, Nb = args.Nb;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = Nb / BN;
+  int tm, tn;
+  tile_coords(tiles_m, tiles_n, args.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int half = lane >> 5;
+
+  f32x16 acc[4][NB];
+  if (MODE == BWD_P_FROM_MEM) {
+    // the product was stored by an earlier kernel (bf16 [M, Nb]): bring the tile into the accumulator layout
+    load_tile_rows<32>(args.A, Nb, m0, n0, M, smem);
+    wait_barrier<0>();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int rr = wm * 128 + mb * 32 + (lane & 31);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const u32x2 v = *(const u32x2*)(smem + tile_off<32>(rr, wn * 8 + nb * 4 + gq) + 8 * half);
+          acc[mb][nb][4 * gq + 0] = bf16_lo(v[0]);
+          acc[mb][nb][4 * gq + 1] = bf16_hi(v[0]);
+          acc[mb][nb][4 * gq + 2] = bf16_lo(v[1]);
+          acc[mb][nb][4 * gq + 3] = bf16_hi(v[1]);
+        }
+    }
+  } else if (BT) {
+    gemm_mainloop_nt(args.A, args.K, M, m0, args.B, args.K, RowsFrom{n0}, args.K, smem, acc);
+  } else {
+    gemm_mainloop(args.A, args.K, M, m0, args.B, Nb, ContiguousCols<8>{n0}, args.K, smem, acc);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(acc[mb][nb]));
+  __syncthreads();  // every wave is done with the LDS (ring or tile)
+
+  // acc[mb][nb][e] is row m0 + 128 wm + 32 mb + lane%32, column n0 + 64 wn + 32 nb + 8 (e/4) + 4 half + e%4
+  if (PMODE) {
+    load_tile_rows<32>(args.h, Nb, m0, n0, M, smem);
+    float rv[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+      rv[mb] = args.r[m < M ? m : M - 1];
+    }
+    const int c_base = n0 + wn * 64 + 4 * half;
+    f32x4 gv[NB][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) gv[nb][gq] = *(const f32x4*)(args.gamma + c_base + nb * 32 + 8 * gq);
+    wait_barrier<0>();
+    float srow[4];
+    float tcol[NB][4][4];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tcol[nb][gq][e] = 0.0f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int rr = wm * 128 + mb * 32 + (lane & 31);
+      const bool live = m0 + rr < M;
+      const float ri = rv[mb];
+      float s = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          char* slot = smem + tile_off<32>(rr, wn * 8 + nb * 4 + gq) + 8 * half;
+          const u32x2 hv = *(const u32x2*)slot;
+          const float hf[4] = {bf16_lo(hv[0]), bf16_hi(hv[0]), bf16_lo(hv[1]), bf16_hi(hv[1])};
+          float g[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p = acc[mb][nb][4 * gq + e];
+            const float gp = gv[nb][gq][e] * p;
+            s += gp * hf[e];
+            if (live) tcol[nb][gq][e] += p * ri * hf[e];
+            g[e] = ri * gp;
+          }
+          *(u32x2*)slot = (u32x2){pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
+        }
+      srow[mb] = s;
+    }
+    // column partials: the 32 lanes of each half hold the same columns for different rows
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v = tcol[nb][gq][e];
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) v += __shfl_xor(v, off);
+          tcol[nb][gq][e] = v;
+        }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) srow[mb] += __shfl_xor(srow[mb], 32);
+    float* red = (float*)(smem + LDS_BYTES);          // [4 wn][256 rows]
+    float* red2 = (float*)(smem + LDS_BYTES + 4096);  // [2 wm][256 columns]
+    if (lane < 32) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) red[wn * 256 + wm * 128 + mb * 32 + lane] = srow[mb];
+    }
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) red2[wm * 256 + wn * 64 + nb * 32 + 8 * gq + 4 * half + e] = tcol[nb][gq][e];
+    }
+    __syncthreads();
+    store_tile_rows<32>(smem, args.out, Nb, m0, n0, M);
+    if (wn == 0 && lane < 32) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = wm * 128 + mb * 32 + lane;
+        const int m = m0 + row;
+        if (m < M) args.part[(int64_t)tn * M + m] = ((red[row] + red[256 + row]) + red[512 + row]) + red[768 + row];
+      }
+    }
+    if (t < 256) args.part2[(int64_t)tm * Nb + n0 + t] = red2[t] + red2[256 + t];
+  } else if (MODE == BWD_STORE_BF16) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int rr = wm * 128 + mb * 32 + (lane & 31);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x16& a = acc[mb][nb];
+          *(u32x2*)(smem + tile_off<32>(rr, wn * 8 + nb * 4 + gq) + 8 * half) =
+              (u32x2){pack_bf16(a[4 * gq], a[4 * gq + 1]), pack_bf16(a[4 * gq + 2], a[4 * gq + 3])};
+        }
+    }
+    __syncthreads();
+    store_tile_rows<32>(smem, args.out, Nb, m0, n0, M);
+  } else if (MODE == BWD_F32_ROWSCALE) {
+    // fp32 [M, Nb] with a row scale, staged 128 rows at a time
+    float rs[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+      rs[mb] = args.gamma ? args.gamma[m < M ? m : M - 1] : 1.0f;
+    }
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (wm == hh) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int rr = mb * 32 + (lane & 31);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const f32x16& a = acc[mb][nb];
+              const float sc = rs[mb];
+              *(f32x4*)(smem + f32_off(rr, (wn * 64 + nb * 32 + 8 * gq + 4 * half) >> 2)) =
+                  (f32x4){a[4 * gq] * sc, a[4 * gq + 1] * sc, a[4 * gq + 2] * sc, a[4 * gq + 3] * sc};
+            }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int rr = p * 8 + (t >> 6);
+        const int c = t & 63;
+        const f32x4 v = *(const f32x4*)(smem + f32_off(rr, c));
+        const int m = m0 + hh * 128 + rr;
+        if (m < M) *(f32x4*)(args.outf + (int64_t)m * Nb + n0 + 4 * c) = v;
+      }
+      __syncthreads();
+    }
+  } else {  // BWD_F32_TRANS: outf [Nb, M] = the tile transposed, fp32, staged 128 tile rows at a time
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      if (wm == hh) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int w = mb * 32 + (lane & 31);  // tile row within the half = output column
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int q = wn * 64 + nb * 32 + 8 * gq + 4 * half + e;  // tile column = output row
+                *(float*)(smem + f32t_off(q, w)) = acc[mb][nb][4 * gq + e];
+              }
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < 16; ++p) {
+        const int q = p * 16 + (t >> 5);
+        const int c = t & 31;  // 4 words = 4 output columns
+        const float* src = (const float*)(smem + q * 512);
+        const int sw = (q & 1) << 5;
+        const f32x4 v = {src[(4 * c) ^ sw], src[(4 * c + 1) ^ sw], src[(4 * c + 2) ^ sw], src[(4 * c + 3) ^ sw]};
+        const int col = m0 + hh * 128 + 4 * c;
+        if (col < M) *(f32x4*)(args.outf + (int64_t)(n0 + q) * M + col) = v;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// B2: a_i = r_i^3 / D * sum_t part[t][i] (t in order), dgamma_j = sum_q part2[q][j] (q in order).
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, int T, const float* __restrict__ part2,
+                                                         int Q, const float* __restrict__ r, int M, int D,
+                                                         float* __restrict__ a, float* __restrict__ dgamma) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < M) {
+    float s = 0.0f;
+    for (int t = 0; t < T; ++t) s += part[(int64_t)t * M + i];
+    const float ri = r[i];
+    a[i] = ri * ri * ri * s / (float)D;
+  }
+  if (i < D) {
+    float g = 0.0f;
+    for (int q = 0; q < Q; ++q) g += part2[(int64_t)q * D + i];
+    dgamma[i] = g;
+  }
+}
+
+// B3: one 64 x 64 tile of [M, D] per workgroup.  dh = G - a_i h + dh_out (fp32, then bf16) -> dR; the same
+// dh and n = bf16(r_i h) are written transposed, [D, M], through LDS.
+__global__ __launch_bounds__(256) void bwd_dh_kernel(const uint16_t* __restrict__ G, const uint16_t* __restrict__ h,
+                                                     const uint16_t* __restrict__ dh_out, const float* __restrict__ r,
+                                                     const float* __restrict__ a, int M, int D,
+                                                     uint16_t* __restrict__ dR, uint16_t* __restrict__ dhT,
+                                                     uint16_t* __restrict__ nT) {
+  __shared__ uint16_t tdh[64][64 + 2];
+  __shared__ uint16_t tn[64][64 + 2];
+  const int t = threadIdx.x;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int ri_ = t >> 2;          // tile row
+  const int cj = (t & 3) * 16;     // 16 columns
+  const int64_t i = i0 + ri_;
+  const float rr = r[i], ai = a[i];
+#pragma unroll
+  for (int hlf = 0; hlf < 2; ++hlf) {
+    const int j = j0 + cj + 8 * hlf;
+    const u32x4 gv = *(const u32x4*)(G + i * D + j);
+    const u32x4 hv = *(const u32x4*)(h + i * D + j);
+    const u32x4 ov = dh_out ? *(const u32x4*)(dh_out + i * D + j) : (u32x4){0u, 0u, 0u, 0u};
+    u32x4 dv, nv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float h0 = bf16_lo(hv[q]), h1 = bf16_hi(hv[q]);
+      const float d0 = bf16_lo(gv[q]) - ai * h0 + bf16_lo(ov[q]);
+      const float d1 = bf16_hi(gv[q]) - ai * h1 + bf16_hi(ov[q]);
+      dv[q] = pack_bf16(d0, d1);
+      nv[q] = pack_bf16(rr * h0, rr * h1);
+      const int c = cj + 8 * hlf + 2 * q;
+      tdh[c][ri_] = (uint16_t)(dv[q] & 0xffff);
+      tdh[c + 1][ri_] = (uint16_t)(dv[q] >> 16);
+      tn[c][ri_] = (uint16_t)(nv[q] & 0xffff);
+      tn[c + 1][ri_] = (uint16_t)(nv[q] >> 16);
+    }
+    *(u32x4*)(dR + i * D + j) = dv;
+  }
+  __syncthreads();
+  // transposed rows: row j of the tile holds 64 values of i; 8 per thread-chunk, 512 chunks per tensor
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int ch = t + 256 * p;
+    const int jr = ch >> 3, ic = (ch & 7) * 8;
+    u32x4 o1, o2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o1[q] = (uint32_t)tdh[jr][ic + 2 * q] | ((uint32_t)tdh[jr][ic + 2 * q + 1] << 16);
+      o2[q] = (uint32_t)tn[jr][ic + 2 * q] | ((uint32_t)tn[jr][ic + 2 * q + 1] << 16);
+    }
+    *(u32x4*)(dhT + (int64_t)(j0 + jr) * M + i0 + ic) = o1;
+    *(u32x4*)(nT + (int64_t)(j0 + jr) * M + i0 + ic) = o2;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------------
+// launchers (host)
+
+template <int MODE, bool BT>
+static hipError_t launch_bwd(const BwdArgs& a0, hipStream_t stream) {
+  BwdArgs a = a0;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  const int tiles_n = a.Nb / BN;
+  a.group_m = tiles_m < 4 ? tiles_m : 4;
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, BT>), dim3(tiles_m * tiles_n), dim3(NTHREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_p(const uint16_t* dz, const uint16_t* W2, const uint16_t* h, const float* r, const float* gamma,
+                        uint16_t* G, float* part, float* part2, int M, int D, int N2, hipStream_t stream) {
+  BwdArgs a{dz, W2, h, r, gamma, G, nullptr, part, part2, M, N2, D, 0};
+  return launch_bwd<BWD_P, true>(a, stream);
+}
+
+hipError_t launch_bwd_p_from_mem(const uint16_t* P, const uint16_t* h, const float* r, const float* gamma, uint16_t* G,
+                                 float* part, float* part2, int M, int D, hipStream_t stream) {
+  BwdArgs a{P, nullptr, h, r, gamma, G, nullptr, part, part2, M, 0, D, 0};
+  return launch_bwd<BWD_P_FROM_MEM, false>(a, stream);
+}
+
+hipError_t launch_gemm_nt_store(const uint16_t* A, const uint16_t* Bt, uint16_t* C, int M, int K, int N,
+                                hipStream_t stream) {
+  BwdArgs a{A, Bt, nullptr, nullptr, nullptr, C, nullptr, nullptr, nullptr, M, K, N, 0};
+  return launch_bwd<BWD_STORE_BF16, true>(a, stream);
+}
+
+hipError_t launch_gemm_f32_rowscale(const uint16_t* A, const uint16_t* B, const float* rowsc, float* C, int M, int K,
+                                    int N, hipStream_t stream) {
+  BwdArgs a{A, B, nullptr, nullptr, rowsc, nullptr, C, nullptr, nullptr, M, K, N, 0};
+  return launch_bwd<BWD_F32_ROWSCALE, false>(a, stream);
+}
+
+hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N,
+                                 hipStream_t stream) {
+  BwdArgs a{A, B, nullptr, nullptr, nullptr, nullptr, Ct, nullptr, nullptr, M, K, N, 0};
+  return launch_bwd<BWD_F32_TRANS, false>(a, stream);
+}
+
+hipError_t launch_bwd_reduce(const float* part, int T, const float* part2, int Q, const float* r, int M, int D,
+                             float* a, float* dgamma, hipStream_t stream) {
+  const int n = M > D ? M : D;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, part, T, part2, Q, r, M, D, a,
+                     dgamma);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dh(const uint16_t* G, const uint16_t* h, const uint16_t* dh_out, const float* r, const float* a,
+                         int M, int D, uint16_t* dR, uint16_t* dhT, uint16_t* nT, hipStream_t stream) {
+  hipLaunchKernelGGL(bwd_dh_kernel, dim3(D / 64, M / 64), dim3(256), 0, stream, G, h, dh_out, r, a, M, D, dR, dhT, nT);
+  return hipGetLastError();
+}
+
+}  // namespace coda

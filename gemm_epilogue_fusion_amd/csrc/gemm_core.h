@@ -251,6 +251,107 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
   step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
 }
 
+// The same mainloop with B given transposed: Bt [N,K] with K contiguous (a weight read as [out,in], or W^T of
+// an [in,out] weight).  The B stage then has the A stage's layout (tile row = output column, 64-byte rows,
+// the same swizzle) and is read with ds_read_b128 like A.  brow(r) = global row of Bt that feeds tile-local
+// output column r (0..255).
+template <class BRow>
+__device__ __forceinline__ void gemm_mainloop_nt(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
+                                                 const uint16_t* __restrict__ Bt, int64_t ldbt, BRow brow, int K,
+                                                 char* smem, f32x16 (&acc)[4][NB]) {
+  constexpr int LPW = 16 / NWAVES;
+  constexpr int PER = 2 * LPW;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = (f32x16){};
+  // direct-load unit q: rows 16q .. 16q+15 of both stages (lane -> row 16q + lane/4, slot lane%4)
+  const uint16_t* aptr[LPW];
+  const uint16_t* bptr[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int q = LPW * wave + i;
+    const int r = 16 * q + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    int row = m0 + r;
+    row = row < M ? row : M - 1;
+    aptr[i] = A + (int64_t)row * lda + 8 * c;
+    bptr[i] = Bt + brow(r) * ldbt + 8 * c;
+  }
+  // per-lane fragment offsets: sub-step s reads chunk 2 s + lane/32 of its row
+  int oa[2], ob[2][NB];
+  {
+    const int m = wm * 128 + (lane & 31);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      oa[s] = a_off(m, 2 * s + (lane >> 5));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        ob[s][nb] = A_BYTES + a_off(wn * (32 * NB) + nb * 32 + (lane & 31), 2 * s + (lane >> 5));
+    }
+  }
+  auto rd = [&](const char* st, int s, Frags& f) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) f.b[nb] = *(const s16x8*)(st + ob[s][nb]);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) f.a[mb] = *(const s16x8*)(st + oa[s] + mb * 32 * 64);
+  };
+  const int nk = K / BK;
+  auto issue = [&](int kt, int stage) {
+    char* st = smem + stage * STAGE_BYTES;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) g2lds16(aptr[i] + k0, st + (LPW * wave + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + k0, st + A_BYTES + (LPW * wave + i) * 1024);
+  };
+  Frags f0, f1;
+  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c) {
+    constexpr int U = decltype(U_c)::value;
+    constexpr bool ISSUE = decltype(issue_c)::value;
+    constexpr int WAIT = decltype(wait_c)::value;
+    const char* cur = smem + U * STAGE_BYTES;
+    if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
+    rd(cur, 1, f1);
+    mma(f0, acc);
+    interleave_mma_reads();
+    if (WAIT >= 0) {
+      wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
+      rd(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, 0, f0);
+    }
+    mma(f1, acc);
+    interleave_mma_reads();
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using Yes = std::true_type;
+  using No = std::false_type;
+  using WaitFull = std::integral_constant<int, 2 * PER>;
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
+  wait_barrier<2 * PER>();
+  rd(smem, 0, f0);
+  const int nblk = nk / NSTAGE;
+  for (int bi = 0; bi < nblk - 1; ++bi) {
+    const int kt = bi * NSTAGE;
+    step(kt + 0, S0{}, Yes{}, WaitFull{});
+    step(kt + 1, S1{}, Yes{}, WaitFull{});
+    step(kt + 2, S2{}, Yes{}, WaitFull{});
+    step(kt + 3, S3{}, Yes{}, WaitFull{});
+  }
+  const int kt = (nblk - 1) * NSTAGE;
+  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{});
+  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER>{});
+  step(kt + 2, S2{}, No{}, std::integral_constant<int, 0>{});
+  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
+}
+
 // ======================================================================================================
 // fp8 (OCP e4m3fn) mainloop: same tile, ring and barrier structure; K advances 64 values (64 bytes) per
 // stage, so the A stage has the bf16 A stage's byte layout (256 rows x 64 B).  The B stage is 64 rows x
@@ -429,6 +530,54 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
   step(kt + 1, S1{}, No{}, std::integral_constant<int, PER>{});
   step(kt + 2, S2{}, No{}, std::integral_constant<int, 0>{});
   step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
+}
+
+// Global column of the tile's column chunk c when the tile's 256 accumulator columns are one contiguous
+// range starting at n0 (W columns per chunk: 8 for bf16, 16 for e4m3).
+template <int W>
+struct ContiguousCols {
+  int64_t n0;
+  __device__ int64_t operator()(int c) const { return n0 + W * c; }
+};
+
+// ---- output tile staging in LDS -----------------------------------------------------------------------
+// A bf16 tile of 256 rows x 8 CH columns: row r is 16 CH bytes, its 16-byte chunk c at slot c ^ (r % CH), so
+// both the lanes that write 32 rows of one chunk and the lanes that read one row's chunks spread over the
+// banks.
+template <int CH>
+__device__ __forceinline__ int tile_off(int r, int c) { return r * (16 * CH) + ((c ^ (r & (CH - 1))) << 4); }
+
+// Whole rows of the staged tile to dst[(m0 + r) * ld + n0 ...], 16 bytes per lane; rows >= M are skipped.
+template <int CH>
+__device__ __forceinline__ void store_tile_rows(const char* smem, uint16_t* dst, int ld, int m0, int n0, int M) {
+  constexpr int ROWS_PER_PASS = NTHREADS / CH;
+  const int t = threadIdx.x;
+  const int c = t % CH;
+#pragma unroll
+  for (int p = 0; p < BM / ROWS_PER_PASS; ++p) {
+    const int r = p * ROWS_PER_PASS + t / CH;
+    const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, c));
+    const int m = m0 + r;
+    if (m < M) *(u32x4*)(dst + (int64_t)m * ld + n0 + 8 * c) = v;
+  }
+}
+
+// Rows m0 .. m0+255 of src (columns n0 .. n0 + 8 CH) into the staged-tile layout with direct global -> LDS
+// loads (rows past M read row M-1).  The caller waits for the loads (vmcnt) and synchronises the workgroup.
+template <int CH>
+__device__ __forceinline__ void load_tile_rows(const uint16_t* src, int ld, int m0, int n0, int M, char* smem) {
+  constexpr int ROWS_PER_INST = 64 / CH;  // one wave instruction fills 1 KiB
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < BM / (NWAVES * ROWS_PER_INST); ++j) {
+    const int r0 = (wave * (BM / NWAVES)) + j * ROWS_PER_INST;
+    const int r = r0 + lane / CH;
+    const int slot = lane % CH;
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    g2lds16(src + (int64_t)m * ld + n0 + 8 * (slot ^ (r & (CH - 1))), smem + r0 * (16 * CH));
+  }
 }
 
 // Maps the linear workgroup id to a (row tile, column tile) pair.

@@ -32,13 +32,6 @@ __device__ __forceinline__ float silu_f32(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// Global column of the tile's column chunk c when the tile's 256 accumulator columns are one contiguous
-// range starting at n0 (W columns per chunk: 8 for bf16, 16 for e4m3).
-template <int W>
-struct ContiguousCols {
-  int64_t n0;
-  __device__ int64_t operator()(int c) const { return n0 + W * c; }
-};
 // SwiGLU tiles: wave column group w (64 accumulator columns) holds 32 gate columns c0 + 32 w .. +32 followed
 // by the matching 32 up columns half + c0 + 32 w .. +32, so gate and up of one output share a lane.
 template <int W>
@@ -49,46 +42,6 @@ struct GateUpCols {
     return within < 32 ? c0 + 32 * w + within : half + c0 + 32 * w + (within - 32);
   }
 };
-
-// ---- output tile staging in LDS -----------------------------------------------------------------------
-// A bf16 tile of 256 rows x 8 CH columns: row r is 16 CH bytes, its 16-byte chunk c at slot c ^ (r % CH), so
-// both the lanes that write 32 rows of one chunk and the lanes that read one row's chunks spread over the
-// banks.
-template <int CH>
-__device__ __forceinline__ int tile_off(int r, int c) { return r * (16 * CH) + ((c ^ (r & (CH - 1))) << 4); }
-
-// Whole rows of the staged tile to dst[(m0 + r) * ld + n0 ...], 16 bytes per lane; rows >= M are skipped.
-template <int CH>
-__device__ __forceinline__ void store_tile_rows(const char* smem, uint16_t* dst, int ld, int m0, int n0, int M) {
-  constexpr int ROWS_PER_PASS = NTHREADS / CH;
-  const int t = threadIdx.x;
-  const int c = t % CH;
-#pragma unroll
-  for (int p = 0; p < BM / ROWS_PER_PASS; ++p) {
-    const int r = p * ROWS_PER_PASS + t / CH;
-    const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, c));
-    const int m = m0 + r;
-    if (m < M) *(u32x4*)(dst + (int64_t)m * ld + n0 + 8 * c) = v;
-  }
-}
-
-// Rows m0 .. m0+255 of src (columns n0 .. n0 + 8 CH) into the staged-tile layout with direct global -> LDS
-// loads (rows past M read row M-1).  The caller waits for the loads (vmcnt) and synchronises the workgroup.
-template <int CH>
-__device__ __forceinline__ void load_tile_rows(const uint16_t* src, int ld, int m0, int n0, int M, char* smem) {
-  constexpr int ROWS_PER_INST = 64 / CH;  // one wave instruction fills 1 KiB
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int j = 0; j < BM / (NWAVES * ROWS_PER_INST); ++j) {
-    const int r0 = (wave * (BM / NWAVES)) + j * ROWS_PER_INST;
-    const int r = r0 + lane / CH;
-    const int slot = lane % CH;
-    int m = m0 + r;
-    m = m < M ? m : M - 1;
-    g2lds16(src + (int64_t)m * ld + n0 + 8 * (slot ^ (r & (CH - 1))), smem + r0 * (16 * CH));
-  }
-}
 
 // One GEMM with a programmable epilogue.  The accumulator tile covers 256 columns of B; A [M,K] and B
 // [K,Nb] are bf16 (FP8 = false) or e4m3 bytes (FP8 = true), row-major.  In the epilogue the accumulator is

@@ -42,4 +42,28 @@ hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8
 hipError_t launch_add_rmsnorm_quant(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H,
                                     uint8_t* NQ, float* r, float* sn, int M, int D, float eps, hipStream_t stream);
 
+// ---- backward (bwd_kernels.hip) ----
+// B1: P = dz W2^T (W2 [D,N2] read as rows); G = bf16(r gamma P) [M,D]; part[D/256][M] row partials of
+// gamma P h; part2[ceil(M/256)][D] column partials of P r h.
+hipError_t launch_bwd_p(const uint16_t* dz, const uint16_t* W2, const uint16_t* h, const float* r, const float* gamma,
+                        uint16_t* G, float* part, float* part2, int M, int D, int N2, hipStream_t stream);
+// The unfused counterpart of B1's epilogue: the same outputs from a stored P [M,D] (bf16).
+hipError_t launch_bwd_p_from_mem(const uint16_t* P, const uint16_t* h, const float* r, const float* gamma, uint16_t* G,
+                                 float* part, float* part2, int M, int D, hipStream_t stream);
+// C [M,N] = bf16(A Bt^T), A [M,K], Bt [N,K].
+hipError_t launch_gemm_nt_store(const uint16_t* A, const uint16_t* Bt, uint16_t* C, int M, int K, int N,
+                                hipStream_t stream);
+// C [M,N] = fp32 rowsc[m] * (A B), A [M,K], B [K,N] (rowsc may be null).
+hipError_t launch_gemm_f32_rowscale(const uint16_t* A, const uint16_t* B, const float* rowsc, float* C, int M, int K,
+                                    int N, hipStream_t stream);
+// Ct [N,M] = fp32 (A B)^T, A [M,K], B [K,N].
+hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N,
+                                 hipStream_t stream);
+// B2: a[i] = r_i^3 / D * sum_t part[t][i]; dgamma[j] = sum_q part2[q][j].
+hipError_t launch_bwd_reduce(const float* part, int T, const float* part2, int Q, const float* r, int M, int D,
+                             float* a, float* dgamma, hipStream_t stream);
+// B3: dR = bf16(G - a h + dh_out) [M,D]; dhT, nT [D,M] = dR and bf16(r h), transposed.  M, D multiples of 64.
+hipError_t launch_bwd_dh(const uint16_t* G, const uint16_t* h, const uint16_t* dh_out, const float* r, const float* a,
+                         int M, int D, uint16_t* dR, uint16_t* dhT, uint16_t* nT, hipStream_t stream);
+
 }  // namespace coda

@@ -127,3 +127,14 @@ def make_inputs(wl: Workload) -> BlockInputs:
         out.W1q, out.sw1 = _quantize_e4m3(W1f, dim=0)
         out.W2q, out.sw2 = _quantize_e4m3(W2f, dim=0)
     return out
+
+
+def make_grads(wl: Workload, dz_std: float = 1.0, dh_std: float = 1.0):
+    """Incoming gradients for the backward of workload ``wl``: dz [M, N2] (gradient of the second product's
+    output) and dh_out [M, D] (gradient arriving at the residual stream), seeded Gaussians rounded to bf16
+    (idx 5 and 6 of the same seeding scheme).  The real ones come from the layers above; their scale only
+    sets the scale of every output gradient."""
+    s = wl.seed
+    dz = _normal((wl.M, wl.N2), dz_std, s, 5).to(torch.bfloat16)
+    dh = _normal((wl.M, wl.D), dh_std, s, 6).to(torch.bfloat16)
+    return dz, dh

@@ -150,6 +150,37 @@ int coda_partial_rms_reduce(const float* part, int64_t T, int64_t M, int64_t D, 
 int coda_gemm2_rowscale(const void* hg, const void* W2, const float* r, int epi_kind, void* out_y, int64_t M,
                         int64_t D, int64_t N2, void* stream);
 
+/* ---- backward of the block ----
+ * The CODA write-up (section "CODA: the treasure hidden in the epilogue"; section "Experimental results"
+ * reports the backward kernels) applies the same epilogue rewrite to back-propagation.  With the forward
+ * h = X W1 + R, r_i = 1/sqrt(mean_j h_ij^2 + eps), n = r h, u = n * gamma, z = u W2, and given dz (the
+ * gradient of z, the second product's output before any epilogue) and dh_out (the gradient arriving at the
+ * residual stream h from downstream; NULL for none):
+ *   dR = dh = r (du gamma - n mean_j(du_ij gamma_j n_ij)) + dh_out,   du = dz W2^T
+ *   dX = dh W1^T,  dW1 = X^T dh,  dgamma_j = sum_i du_ij n_ij,  dW2 = u^T dz
+ * Inputs: X [M,K1] bf16, W1 [K1,D] bf16, h [M,D] bf16 and r [M] fp32 as the forward left them (out_h and
+ * the workspace's r), gamma [D] fp32, W2 [D,N2] bf16, dz [M,N2] bf16, dh_out [M,D] bf16 or NULL.
+ * Outputs: out_dX [M,K1] bf16, out_dW1 [K1,D] fp32, out_dR [M,D] bf16, out_dgamma [D] fp32, out_dW2 [D,N2]
+ * fp32.  Six kernels on `stream` (the fused path): P = dz W2^T with the RMSNorm-backward row and column
+ * statistics in its epilogue, a light reduction, dh (and its transpose and n's), then the dX, dW1 and dW2
+ * products.  Shape rules: M a multiple of 128, K1 a multiple of 256, D and N2 multiples of 256.  No output
+ * may overlap an input or another output.  Workspace: coda_bwd_workspace_bytes(..., unfused = 0); other
+ * conventions as the forward entry points. */
+size_t coda_bwd_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused);
+
+int coda_block_bwd(const void* X, const void* W1, const void* h, const float* r, const float* gamma, const void* W2,
+                   const void* dz, const void* dh_out, void* out_dX, float* out_dW1, void* out_dR, float* out_dgamma,
+                   float* out_dW2, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* The unfused backward baseline: P = dz W2^T is stored (bf16) and its RMSNorm-backward statistics are
+ * computed by a separate pass over P and h; the remaining kernels are shared.  Same arguments and outputs;
+ * workspace: coda_bwd_workspace_bytes(..., unfused = 1). */
+int coda_block_bwd_unfused(const void* X, const void* W1, const void* h, const float* r, const float* gamma,
+                           const void* W2, const void* dz, const void* dh_out, void* out_dX, float* out_dW1,
+                           void* out_dR, float* out_dgamma, float* out_dW2, int64_t M, int64_t K1, int64_t D,
+                           int64_t N2, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

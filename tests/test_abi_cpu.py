@@ -169,3 +169,55 @@ def test_fp8_workspace_bytes(lib):
     base = a(8 * M * 4) + a(M * 4)
     assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 1, 0) == base + a(M * D) + 2 * a(M * 4)
     assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 1, 1) == base + a(M * D * 2) + a(M * D) + a(M * 4)
+
+
+# ---- backward entry points ----
+def _bargs(M=256, K1=256, D=256, N2=512, unfused=0, **over):
+    a = dict(X=BASE, W1=BASE + GB, h=BASE + 2 * GB, r=BASE + 3 * GB, gamma=BASE + 3 * GB + (1 << 20),
+             W2=BASE + 4 * GB, dz=BASE + 5 * GB, dh_out=BASE + 6 * GB, dX=BASE + 7 * GB, dW1=BASE + 8 * GB,
+             dR=BASE + 9 * GB, dgamma=BASE + 10 * GB, dW2=BASE + 11 * GB, M=M, K1=K1, D=D, N2=N2,
+             ws=BASE + 12 * GB)
+    a.update(over)
+    a["ws_bytes"] = cb.load().coda_bwd_workspace_bytes(a["M"], a["K1"], a["D"], a["N2"], 1)  # fits both paths
+    return a
+
+
+def _bcall(lib, a, fn="coda_block_bwd"):
+    return getattr(lib, fn)(a["X"], a["W1"], a["h"], a["r"], a["gamma"], a["W2"], a["dz"], a["dh_out"], a["dX"],
+                            a["dW1"], a["dR"], a["dgamma"], a["dW2"], a["M"], a["K1"], a["D"], a["N2"], a["ws"],
+                            a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("fn", ["coda_block_bwd", "coda_block_bwd_unfused"])
+@pytest.mark.parametrize("case,over,want", [
+    ("null_dz", dict(dz=0), INVALID),
+    ("null_out_dW2", dict(dW2=0), INVALID),
+    ("misaligned_r", dict(r=BASE + 3 * GB + 4), INVALID),
+    ("M_not_128", dict(M=320), UNSUPPORTED),
+    ("K1_not_256", dict(K1=384), UNSUPPORTED),
+    ("D_not_256", dict(D=320), UNSUPPORTED),
+    ("out_dR_on_h", dict(dR=BASE + 2 * GB), ALIAS),
+    ("out_dX_on_out_dR", dict(dX=BASE + 9 * GB + 512), ALIAS),
+    ("ws_on_dz", dict(ws=BASE + 5 * GB), ALIAS),
+    ("null_workspace", dict(ws=0), WORKSPACE),
+])
+def test_bwd_validation(lib, fn, case, over, want):
+    a = _bargs(**over)
+    assert _bcall(lib, a, fn) == want, lib.coda_last_error()
+    assert lib.coda_last_error() != b""
+
+
+def test_bwd_workspace_bytes(lib):
+    al = lambda x: (x + 255) // 256 * 256
+    M, D = 8192, 2048
+    fused = al(M * D * 2) + al((D // 256) * M * 4) + al((M // 256) * D * 4) + al(M * 4) + 2 * al(M * D * 2)
+    assert lib.coda_bwd_workspace_bytes(M, 2048, D, 16384, 0) == fused
+    assert lib.coda_bwd_workspace_bytes(M, 2048, D, 16384, 1) == fused + al(M * D * 2)
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_bwd_no_gpu_reports_hip_error(lib):
+    a = _bargs()
+    assert _bcall(lib, a) == HIP
+    a = _bargs(dh_out=0)  # dh_out is optional
+    assert _bcall(lib, a) == HIP

@@ -1,0 +1,116 @@
+"""GPU parity of the block's backward (fused and unfused paths) against the fp64 oracle.
+
+Each case runs the forward on the GPU (for h and r, as a caller would keep them), then the backward on the
+GPU, and compares dX, dW1, dR, dgamma and dW2 with oracle.block_bwd on the same bf16-valued inputs (the
+oracle recomputes h and r in fp64 from X, W1, R).  Bar: the bf16 contract of the forward, normwise max
+relative error <= 2e-2 and mean absolute error <= 1e-3 of max|o|.  At the 1B shape the row-local outputs
+(dX, dR) are compared on sampled rows; the weight gradients are covered by the smaller cases, which span
+several tiles in every dimension and a half-filled last row tile.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gemm_epilogue_fusion_amd import binding as cb
+from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, EPI_SWIGLU, WORKLOADS, Workload, make_grads, make_inputs
+
+from parity import f64, sample_rows
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+NORMWISE = 2e-2
+MAE_REL = 1e-3
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cb.load()
+
+
+def _check(name, got, want):
+    want = np.asarray(want, np.float64)
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    scale = np.max(np.abs(want))
+    err = np.max(np.abs(got - want)) / scale
+    mae = np.mean(np.abs(got - want)) / scale
+    assert err <= NORMWISE, f"{name}: normwise max relative error {err:.3e}"
+    assert mae <= MAE_REL, f"{name}: mean absolute error / max|o| {mae:.3e}"
+    return err
+
+
+def _run(wl, unfused=False, with_dh_out=True):
+    inp = make_inputs(wl)
+    dz, dho = make_grads(wl)
+    dev = "cuda"
+    X, W1, R, g, W2 = (t.to(dev) for t in (inp.X, inp.W1, inp.R, inp.gamma, inp.W2))
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev)
+    cb.coda_block_fwd(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws)
+    r = cb.workspace_r(ws, wl.M, wl.D)
+    dzd = dz.to(dev)
+    dhd = dho.to(dev) if with_dh_out else None
+    outs = dict(dX=torch.full((wl.M, wl.K1), float("nan"), dtype=torch.bfloat16, device=dev),
+                dW1=torch.full((wl.K1, wl.D), float("nan"), dtype=torch.float32, device=dev),
+                dR=torch.full((wl.M, wl.D), float("nan"), dtype=torch.bfloat16, device=dev),
+                dgamma=torch.full((wl.D,), float("nan"), dtype=torch.float32, device=dev),
+                dW2=torch.full((wl.D, wl.N2), float("nan"), dtype=torch.float32, device=dev))
+    wsb = cb.alloc_bwd_workspace(wl.M, wl.K1, wl.D, wl.N2, unfused=int(unfused), device=dev)
+    wsb.fill_(0xFF)
+    fn = cb.coda_block_bwd_unfused if unfused else cb.coda_block_bwd
+    fn(X, W1, h, r, g, W2, dzd, dhd, outs["dX"], outs["dW1"], outs["dR"], outs["dgamma"], outs["dW2"], wsb)
+    torch.cuda.synchronize()
+    return inp, dz, (dho if with_dh_out else None), {k: v.float().cpu().numpy() for k, v in outs.items()}
+
+
+SMALL = [
+    Workload("bwd_one_tile", M=256, K1=256, D=256, N2=512, epi=EPI_SWIGLU, eps=1e-5, w1_std=1 / 16, w2_std=1 / 16, seed=21),
+    Workload("bwd_half_row_tile", M=384, K1=512, D=512, N2=768, epi=EPI_IDENTITY, eps=1e-5, w1_std=0.05, w2_std=0.05, seed=22),
+    Workload("bwd_wide_d", M=128, K1=256, D=768, N2=256, epi=EPI_SWIGLU, eps=1e-6, w1_std=0.06, w2_std=0.04, seed=23),
+]
+
+
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_bwd_small(wl, unfused):
+    _say(f"[gpu] bwd {'unfused' if unfused else 'fused'} {wl}")
+    inp, dz, dho, got = _run(wl, unfused=unfused)
+    want = oracle.block_bwd(f64(inp.X), f64(inp.W1), f64(inp.R), f64(inp.gamma), f64(inp.W2), wl.eps, f64(dz),
+                            f64(dho))
+    for name, w in zip(("dX", "dW1", "dR", "dgamma", "dW2"), want):
+        _check(name, got[name], w)
+
+
+def test_bwd_without_dh_out():
+    wl = SMALL[1]
+    _say(f"[gpu] bwd without dh_out {wl}")
+    inp, dz, _, got = _run(wl, with_dh_out=False)
+    want = oracle.block_bwd(f64(inp.X), f64(inp.W1), f64(inp.R), f64(inp.gamma), f64(inp.W2), wl.eps, f64(dz), None)
+    for name, w in zip(("dX", "dW1", "dR", "dgamma", "dW2"), want):
+        _check(name, got[name], w)
+
+
+def test_bwd_full_size_sampled_rows():
+    wl = WORKLOADS["1b_attn_out_mlp_in"]
+    _say(f"[gpu] bwd full size {wl}")
+    inp, dz, dho, got = _run(wl)
+    for name in ("dW1", "dgamma", "dW2"):
+        assert np.all(np.isfinite(got[name])), name
+    rows = sample_rows(wl.M, n=24)
+    idx = torch.as_tensor(rows, dtype=torch.long)
+    want = oracle.block_bwd(f64(inp.X[idx]), f64(inp.W1), f64(inp.R[idx]), f64(inp.gamma), f64(inp.W2), wl.eps,
+                            f64(dz[idx]), f64(dho[idx]))
+    _check("dX", got["dX"][rows], want[0])
+    _check("dR", got["dR"][rows], want[2])
