@@ -17,6 +17,8 @@ Besides the headline the line carries:
   unfused       the three-kernel baseline timed the same way, and the algorithmic HBM bytes both paths move
   fp8           the same block with e4m3 X / W1 / W2 (per-row and per-column fp32 scales), fused and unfused,
                 timed with HIP events, against the dense fp8 MFMA peak (5 PFLOP/s)
+  backward      the block's backward (dX, dW1, dR, dgamma, dW2 from dz and dh_out; four products of the
+                forward's sizes, 2x its flops), fused and unfused, timed with HIP events
 """
 from __future__ import annotations
 
@@ -123,6 +125,35 @@ def time_fp8(dev, n_ev: int, warmup: int, torch, cb) -> dict:
             "speedup_fused_vs_unfused": round(u_ms / f_ms, 4)}
 
 
+def time_bwd(wl, X, W1, g, W2, h, ws, n_ev: int, warmup: int, torch, cb) -> dict:
+    """The backward of the headline block (h and r as the forward left them), fused and unfused."""
+    from gemm_epilogue_fusion_amd.inputs import make_grads
+
+    dev = X.device
+    dz, dho = (t.to(dev) for t in make_grads(wl))
+    r = cb.workspace_r(ws, wl.M, wl.D)
+    outs = (torch.empty(wl.M, wl.K1, dtype=torch.bfloat16, device=dev),
+            torch.empty(wl.K1, wl.D, dtype=torch.float32, device=dev),
+            torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev),
+            torch.empty(wl.D, dtype=torch.float32, device=dev),
+            torch.empty(wl.D, wl.N2, dtype=torch.float32, device=dev))
+    wsf = cb.alloc_bwd_workspace(wl.M, wl.K1, wl.D, wl.N2, device=dev)
+    wsu = cb.alloc_bwd_workspace(wl.M, wl.K1, wl.D, wl.N2, unfused=1, device=dev)
+    fused = lambda: cb.coda_block_bwd(X, W1, h, r, g, W2, dz, dho, *outs, wsf)
+    unfused = lambda: cb.coda_block_bwd_unfused(X, W1, h, r, g, W2, dz, dho, *outs, wsu)
+    for _ in range(warmup):
+        fused()
+        unfused()
+    torch.cuda.synchronize()
+    f_ms = time_loop(fused, n_ev, torch)
+    u_ms = time_loop(unfused, n_ev, torch)
+    flops = 2 * wl.flops
+    tf = flops / (f_ms * 1e-3) / 1e12
+    return {"what": "dX, dW1, dR, dgamma, dW2 from dz and dh_out", "flops_per_call": flops, "fused_ms": round(f_ms, 4),
+            "tflops": round(tf, 2), "pct_bf16_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2),
+            "unfused_ms": round(u_ms, 4), "speedup_fused_vs_unfused": round(u_ms / f_ms, 4)}
+
+
 def traffic_record(src_hash: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -141,6 +172,7 @@ def main() -> int:
     ap.add_argument("--workload", default="1b_attn_out_mlp_in")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the e4m3 block timing")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
@@ -244,6 +276,8 @@ def main() -> int:
         "hbm_bytes": {"fused_algorithmic": fb, "unfused_algorithmic": ub, "saved_algorithmic": ub - fb},
         "kernel_source_hash": src_hash,
     }
+    if not args.no_bwd:
+        line["backward"] = time_bwd(wl, X, W1, g, W2, h, ws, n_ev, args.warmup, torch, cb)
     if not args.no_fp8:
         line["fp8"] = time_fp8(dev, n_ev, args.warmup, torch, cb)
     if not args.no_cpu_baseline:

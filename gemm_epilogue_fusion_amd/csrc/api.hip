@@ -182,9 +182,10 @@ struct BwdWorkspace {
   uint16_t* dhT;  // [D,M] bf16
   uint16_t* nT;   // [D,M] bf16
   uint16_t* P;    // unfused: P = dz W2^T [M,D] bf16
+  float* slabs;   // split-K partial products of dW1 and dW2 (whichever needs more; none when neither splits)
 };
 
-size_t carve_bwd(void* ws, int64_t M, int64_t D, int unfused, BwdWorkspace* w) {
+size_t carve_bwd(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused, BwdWorkspace* w) {
   char* base = (char*)ws;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -200,6 +201,11 @@ size_t carve_bwd(void* ws, int64_t M, int64_t D, int unfused, BwdWorkspace* w) {
   x.dhT = (uint16_t*)take(ws_mat_bytes(M, D, 2));
   x.nT = (uint16_t*)take(ws_mat_bytes(M, D, 2));
   if (unfused) x.P = (uint16_t*)take(ws_mat_bytes(M, D, 2));
+  // dW1 = (dh^T X)^T: a [D,K1] product over K = M; dW2 = n^T dz: a [D,N2] product over K = M
+  const int s1 = coda::gemm_ksplit((int)D, (int)K1, (int)M), s2 = coda::gemm_ksplit((int)D, (int)N2, (int)M);
+  const size_t b1 = s1 > 1 ? (size_t)s1 * (size_t)D * (size_t)K1 * 4 : 0;
+  const size_t b2 = s2 > 1 ? (size_t)s2 * (size_t)D * (size_t)N2 * 4 : 0;
+  if (b1 || b2) x.slabs = (float*)take(align256(b1 > b2 ? b1 : b2));
   if (w) *w = x;
   return off;
 }
@@ -217,7 +223,7 @@ int validate_bwd(const void* X, const void* W1, const void* h, const float* r, c
   if ((s = check_dims(M, K1, D, N2))) return s;
   if (M % 128) return fail(CODA_ERR_UNSUPPORTED, "backward: M=%lld is not a multiple of 128", (long long)M);
   if (K1 % 256) return fail(CODA_ERR_UNSUPPORTED, "backward: K1=%lld is not a multiple of 256", (long long)K1);
-  const size_t need = carve_bwd(nullptr, M, D, unfused, nullptr);
+  const size_t need = carve_bwd(nullptr, M, K1, D, N2, unfused, nullptr);
   if (!workspace) return fail(CODA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if ((uintptr_t)workspace & 255) return fail(CODA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   if (workspace_bytes < need)
@@ -439,10 +445,8 @@ int coda_gemm2_rowscale(const void* hg, const void* W2, const float* r, int epi_
 extern "C" {
 
 size_t coda_bwd_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused) {
-  (void)K1;
-  (void)N2;
-  if (M < 1 || D < 1) return 0;
-  return carve_bwd(nullptr, M, D, unfused ? 1 : 0, nullptr);
+  if (M < 1 || K1 < 1 || D < 1 || N2 < 1 || M > kMaxDim || K1 > kMaxDim || D > kMaxDim || N2 > kMaxDim) return 0;
+  return carve_bwd(nullptr, M, K1, D, N2, unfused ? 1 : 0, nullptr);
 }
 
 static int block_bwd(const void* X, const void* W1, const void* h, const float* r, const float* gamma, const void* W2,
@@ -455,7 +459,7 @@ static int block_bwd(const void* X, const void* W1, const void* h, const float* 
     if (s) return s;
     hipStream_t st = (hipStream_t)stream;
     BwdWorkspace w;
-    carve_bwd(workspace, M, D, unfused, &w);
+    carve_bwd(workspace, M, K1, D, N2, unfused, &w);
     const uint16_t* hh = (const uint16_t*)h;
     if (unfused) {
       // P = dz W2^T stored, then its row and column statistics in a separate pass
@@ -484,11 +488,12 @@ static int block_bwd(const void* X, const void* W1, const void* h, const float* 
                                                   (int)M, (int)D, (int)K1, st),
                        "bwd dX launch")))
       return s;
-    if ((s = hip_check(coda::launch_gemm_f32_trans(w.dhT, (const uint16_t*)X, out_dW1, (int)D, (int)M, (int)K1, st),
+    if ((s = hip_check(coda::launch_gemm_f32_trans(w.dhT, (const uint16_t*)X, out_dW1, (int)D, (int)M, (int)K1,
+                                                   w.slabs, st),
                        "bwd dW1 launch")))
       return s;
     return hip_check(coda::launch_gemm_f32_rowscale(w.nT, (const uint16_t*)dz, gamma, out_dW2, (int)D, (int)M,
-                                                    (int)N2, st),
+                                                    (int)N2, w.slabs, st),
                      "bwd dW2 launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");

@@ -42,6 +42,7 @@ struct BwdArgs {
   float* part;         // BWD_P*: row partials [Nb/256][M]
   float* part2;        // BWD_P*: column partials [ceil(M/256)][Nb]
   int M, K, Nb, group_m;
+  int64_t slab;        // BWD_F32_*: split-K partial products go to outf + blockIdx.y * slab (K per split = K)
 };
 
 struct RowsFrom {
@@ -94,7 +95,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
   } else if (BT) {
     gemm_mainloop_nt(args.A, args.K, M, m0, args.B, args.K, RowsFrom{n0}, args.K, smem, acc);
   } else {
-    gemm_mainloop(args.A, args.K, M, m0, args.B, Nb, ContiguousCols<8>{n0}, args.K, smem, acc);
+    // split K: workgroup row blockIdx.y multiplies K range [y K, (y + 1) K) of the gridDim.y K ranges
+    const int64_t k0 = (int64_t)blockIdx.y * args.K;
+    const int64_t lda = (int64_t)args.K * gridDim.y;
+    gemm_mainloop(args.A + k0, lda, M, m0, args.B + k0 * Nb, Nb, ContiguousCols<8>{n0}, args.K, smem, acc);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -238,7 +242,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
         const int c = t & 63;
         const f32x4 v = *(const f32x4*)(smem + f32_off(rr, c));
         const int m = m0 + hh * 128 + rr;
-        if (m < M) *(f32x4*)(args.outf + (int64_t)m * Nb + n0 + 4 * c) = v;
+        if (m < M) *(f32x4*)(args.outf + blockIdx.y * args.slab + (int64_t)m * Nb + n0 + 4 * c) = v;
       }
       __syncthreads();
     }
@@ -269,29 +273,50 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
         const int sw = (q & 1) << 5;
         const f32x4 v = {src[(4 * c) ^ sw], src[(4 * c + 1) ^ sw], src[(4 * c + 2) ^ sw], src[(4 * c + 3) ^ sw]};
         const int col = m0 + hh * 128 + 4 * c;
-        if (col < M) *(f32x4*)(args.outf + (int64_t)(n0 + q) * M + col) = v;
+        if (col < M) *(f32x4*)(args.outf + blockIdx.y * args.slab + (int64_t)(n0 + q) * M + col) = v;
       }
       __syncthreads();
     }
   }
 }
 
-// B2: a_i = r_i^3 / D * sum_t part[t][i] (t in order), dgamma_j = sum_q part2[q][j] (q in order).
+// B2: a_i = r_i^3 / D * sum_t part[t][i] (t in order), one thread per row; dgamma_j = sum_q part2[q][j], 32
+// lanes per column (each lane sums q = lane, lane + 32, ... in order, then a fixed butterfly).
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, int T, const float* __restrict__ part2,
                                                          int Q, const float* __restrict__ r, int M, int D,
                                                          float* __restrict__ a, float* __restrict__ dgamma) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < M) {
-    float s = 0.0f;
-    for (int t = 0; t < T; ++t) s += part[(int64_t)t * M + i];
-    const float ri = r[i];
-    a[i] = ri * ri * ri * s / (float)D;
+  const int row_blocks = (M + 255) / 256;
+  if ((int)blockIdx.x < row_blocks) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < M) {
+      float s = 0.0f;
+#pragma unroll 8
+      for (int t = 0; t < T; ++t) s += part[(int64_t)t * M + i];
+      const float ri = r[i];
+      a[i] = ri * ri * ri * s / (float)D;
+    }
+    return;
   }
-  if (i < D) {
-    float g = 0.0f;
-    for (int q = 0; q < Q; ++q) g += part2[(int64_t)q * D + i];
-    dgamma[i] = g;
-  }
+  const int j = ((int)blockIdx.x - row_blocks) * 8 + (threadIdx.x >> 5);
+  const int lane = threadIdx.x & 31;
+  float g = 0.0f;
+  if (j < D)
+    for (int q = lane; q < Q; q += 32) g += part2[(int64_t)q * D + j];
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) g += __shfl_xor(g, off, 32);
+  if (j < D && lane == 0) dgamma[j] = g;
+}
+
+// Sum of S split-K slabs of n floats (slab s at src + s * n), in slab order, times an optional row scale
+// (rows of `cols` floats).  n and cols multiples of 4.
+__global__ __launch_bounds__(256) void slab_sum_kernel(const float* __restrict__ src, int S, int64_t n, int cols,
+                                                       const float* __restrict__ rowsc, float* __restrict__ dst) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= n) return;
+  f32x4 v = *(const f32x4*)(src + e);
+  for (int s = 1; s < S; ++s) v += *(const f32x4*)(src + (int64_t)s * n + e);
+  if (rowsc) v *= rowsc[e / cols];
+  *(f32x4*)(dst + e) = v;
 }
 
 // B3: one 64 x 64 tile of [M, D] per workgroup.  dh = G - a_i h + dh_out (fp32, then bf16) -> dR; the same
@@ -352,50 +377,73 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const uint16_t* __restrict_
 // launchers (host)
 
 template <int MODE, bool BT>
-static hipError_t launch_bwd(const BwdArgs& a0, hipStream_t stream) {
+static hipError_t launch_bwd(const BwdArgs& a0, hipStream_t stream, int ksplit = 1) {
   BwdArgs a = a0;
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = a.Nb / BN;
   a.group_m = tiles_m < 4 ? tiles_m : 4;
-  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, BT>), dim3(tiles_m * tiles_n), dim3(NTHREADS), 0, stream, a);
+  a.K /= ksplit;
+  hipLaunchKernelGGL((bwd_gemm_kernel<MODE, BT>), dim3(tiles_m * tiles_n, ksplit), dim3(NTHREADS), 0, stream, a);
   return hipGetLastError();
+}
+
+int gemm_ksplit(int M, int N, int K) {
+  const int tiles = ((M + BM - 1) / BM) * (N / BN);
+  int s = 1;
+  while (s < 8 && tiles * s < 256 && K % (K_MULTIPLE * s * 2) == 0) s *= 2;
+  return s;
 }
 
 hipError_t launch_bwd_p(const uint16_t* dz, const uint16_t* W2, const uint16_t* h, const float* r, const float* gamma,
                         uint16_t* G, float* part, float* part2, int M, int D, int N2, hipStream_t stream) {
-  BwdArgs a{dz, W2, h, r, gamma, G, nullptr, part, part2, M, N2, D, 0};
+  BwdArgs a{dz, W2, h, r, gamma, G, nullptr, part, part2, M, N2, D, 0, 0};
   return launch_bwd<BWD_P, true>(a, stream);
 }
 
 hipError_t launch_bwd_p_from_mem(const uint16_t* P, const uint16_t* h, const float* r, const float* gamma, uint16_t* G,
                                  float* part, float* part2, int M, int D, hipStream_t stream) {
-  BwdArgs a{P, nullptr, h, r, gamma, G, nullptr, part, part2, M, 0, D, 0};
+  BwdArgs a{P, nullptr, h, r, gamma, G, nullptr, part, part2, M, 0, D, 0, 0};
   return launch_bwd<BWD_P_FROM_MEM, false>(a, stream);
 }
 
 hipError_t launch_gemm_nt_store(const uint16_t* A, const uint16_t* Bt, uint16_t* C, int M, int K, int N,
                                 hipStream_t stream) {
-  BwdArgs a{A, Bt, nullptr, nullptr, nullptr, C, nullptr, nullptr, nullptr, M, K, N, 0};
+  BwdArgs a{A, Bt, nullptr, nullptr, nullptr, C, nullptr, nullptr, nullptr, M, K, N, 0, 0};
   return launch_bwd<BWD_STORE_BF16, true>(a, stream);
 }
 
-hipError_t launch_gemm_f32_rowscale(const uint16_t* A, const uint16_t* B, const float* rowsc, float* C, int M, int K,
-                                    int N, hipStream_t stream) {
-  BwdArgs a{A, B, nullptr, nullptr, rowsc, nullptr, C, nullptr, nullptr, M, K, N, 0};
-  return launch_bwd<BWD_F32_ROWSCALE, false>(a, stream);
+static hipError_t slab_sum(const float* slabs, int S, int64_t n, int cols, const float* rowsc, float* dst,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(slab_sum_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, stream, slabs, S, n, cols,
+                     rowsc, dst);
+  return hipGetLastError();
 }
 
-hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N,
+hipError_t launch_gemm_f32_rowscale(const uint16_t* A, const uint16_t* B, const float* rowsc, float* C, int M, int K,
+                                    int N, float* slabs, hipStream_t stream) {
+  const int S = gemm_ksplit(M, N, K);
+  const int64_t n = (int64_t)M * N;
+  BwdArgs a{A, B, nullptr, nullptr, S > 1 ? nullptr : rowsc, nullptr, S > 1 ? slabs : C, nullptr, nullptr, M, K, N,
+            0, n};
+  hipError_t e = launch_bwd<BWD_F32_ROWSCALE, false>(a, stream, S);
+  if (e != hipSuccess || S == 1) return e;
+  return slab_sum(slabs, S, n, N, rowsc, C, stream);
+}
+
+hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N, float* slabs,
                                  hipStream_t stream) {
-  BwdArgs a{A, B, nullptr, nullptr, nullptr, nullptr, Ct, nullptr, nullptr, M, K, N, 0};
-  return launch_bwd<BWD_F32_TRANS, false>(a, stream);
+  const int S = gemm_ksplit(M, N, K);
+  const int64_t n = (int64_t)M * N;
+  BwdArgs a{A, B, nullptr, nullptr, nullptr, nullptr, S > 1 ? slabs : Ct, nullptr, nullptr, M, K, N, 0, n};
+  hipError_t e = launch_bwd<BWD_F32_TRANS, false>(a, stream, S);
+  if (e != hipSuccess || S == 1) return e;
+  return slab_sum(slabs, S, n, M, nullptr, Ct, stream);
 }
 
 hipError_t launch_bwd_reduce(const float* part, int T, const float* part2, int Q, const float* r, int M, int D,
                              float* a, float* dgamma, hipStream_t stream) {
-  const int n = M > D ? M : D;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, part, T, part2, Q, r, M, D, a,
-                     dgamma);
+  const int blocks = (M + 255) / 256 + (D + 7) / 8;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(blocks), dim3(256), 0, stream, part, T, part2, Q, r, M, D, a, dgamma);
   return hipGetLastError();
 }
 

@@ -53,11 +53,15 @@ hipError_t launch_bwd_p_from_mem(const uint16_t* P, const uint16_t* h, const flo
 // C [M,N] = bf16(A Bt^T), A [M,K], Bt [N,K].
 hipError_t launch_gemm_nt_store(const uint16_t* A, const uint16_t* Bt, uint16_t* C, int M, int K, int N,
                                 hipStream_t stream);
+// Number of K ranges the fp32 products below split K into (1, 2, 4 or 8): enough workgroups to cover the
+// CUs when the output has few tiles.  The partial products go to `slabs` (gemm_ksplit(...) * M * N floats,
+// unused when it is 1) and are summed in order by a second kernel.
+int gemm_ksplit(int M, int N, int K);
 // C [M,N] = fp32 rowsc[m] * (A B), A [M,K], B [K,N] (rowsc may be null).
 hipError_t launch_gemm_f32_rowscale(const uint16_t* A, const uint16_t* B, const float* rowsc, float* C, int M, int K,
-                                    int N, hipStream_t stream);
+                                    int N, float* slabs, hipStream_t stream);
 // Ct [N,M] = fp32 (A B)^T, A [M,K], B [K,N].
-hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N,
+hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N, float* slabs,
                                  hipStream_t stream);
 // B2: a[i] = r_i^3 / D * sum_t part[t][i]; dgamma[j] = sum_q part2[q][j].
 hipError_t launch_bwd_reduce(const float* part, int T, const float* part2, int Q, const float* r, int M, int D,

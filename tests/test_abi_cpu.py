@@ -207,12 +207,24 @@ def test_bwd_validation(lib, fn, case, over, want):
     assert lib.coda_last_error() != b""
 
 
-def test_bwd_workspace_bytes(lib):
+def _ksplit(rows, cols, k):
+    # the fp32 weight-gradient products split K until they have >= 256 workgroups (at most 8 ranges, each
+    # range a multiple of 128)
+    tiles = -(-rows // 256) * (cols // 256)
+    s = 1
+    while s < 8 and tiles * s < 256 and k % (128 * s * 2) == 0:
+        s *= 2
+    return s
+
+
+@pytest.mark.parametrize("M,K1,D,N2", [(8192, 2048, 2048, 16384), (8192, 8192, 2048, 3072), (256, 256, 256, 512)])
+def test_bwd_workspace_bytes(lib, M, K1, D, N2):
     al = lambda x: (x + 255) // 256 * 256
-    M, D = 8192, 2048
-    fused = al(M * D * 2) + al((D // 256) * M * 4) + al((M // 256) * D * 4) + al(M * 4) + 2 * al(M * D * 2)
-    assert lib.coda_bwd_workspace_bytes(M, 2048, D, 16384, 0) == fused
-    assert lib.coda_bwd_workspace_bytes(M, 2048, D, 16384, 1) == fused + al(M * D * 2)
+    fused = al(M * D * 2) + al((D // 256) * M * 4) + al(-(-M // 256) * D * 4) + al(M * 4) + 2 * al(M * D * 2)
+    s1, s2 = _ksplit(D, K1, M), _ksplit(D, N2, M)
+    slabs = max(s1 * D * K1 * 4 if s1 > 1 else 0, s2 * D * N2 * 4 if s2 > 1 else 0)
+    assert lib.coda_bwd_workspace_bytes(M, K1, D, N2, 0) == fused + al(slabs)
+    assert lib.coda_bwd_workspace_bytes(M, K1, D, N2, 1) == fused + al(M * D * 2) + al(slabs)
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
