@@ -76,6 +76,8 @@ def _load():
     lib.oracle_block_bwd_f64.argtypes = [i64, i64, i64, i64, dp, dp, dp, dp, dp, f, dp, dp, dp, dp, dp, dp, dp,
                                          ctypes.c_int]
     lib.oracle_block_bwd_f64.restype = ctypes.c_int
+    lib.oracle_rope_rows_f64.argtypes = [i64, i64, dp, i64, i64, i64, f]
+    lib.oracle_rope_rows_f64.restype = ctypes.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ctypes.c_int
     _lib = lib
@@ -155,6 +157,18 @@ def block_bwd(X, W1, R, gamma, W2, eps, dz, dh_out=None, nthreads=0):
     if rc != 0:
         raise RuntimeError(f"oracle_block_bwd_f64 failed with {rc}")
     return dX, dW1, dR, dgamma, dW2
+
+
+def rope_rows(y, head_dim, n_rot, seq_len, base):
+    """Rotary position embedding of the rows of y [M,N] (a copy is returned): the first n_rot columns, heads of
+    head_dim, pair (i, i + head_dim/2) rotated by (row mod seq_len) * base^(-2 i / head_dim)."""
+    lib = _load()
+    out = np.array(_f64(y), copy=True)
+    M, N = out.shape
+    rc = lib.oracle_rope_rows_f64(M, N, _ptr(out), int(head_dim), int(n_rot), int(seq_len), float(base))
+    if rc != 0:
+        raise RuntimeError(f"oracle_rope_rows_f64 failed with {rc}")
+    return out
 
 
 def gemm_residual(X, W1, R=None, nthreads=0):

@@ -470,3 +470,35 @@ int oracle_block_bwd_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const dou
   free(buf);
   return rc;
 }
+
+/* ------------------------------------------------------------------------------------------------ */
+/* rotary position embedding on the rows of a product                                               */
+/*
+ * The CODA write-up (section "CODA: the treasure hidden in the epilogue"; section "Five blocks and a Lego
+ * language": elementwise transforms) lists RoPE among the operations that run in a GEMM epilogue.  The pages
+ * fix no convention; this one is the "rotate half" form used by LLaMA-family checkpoints: for each head of
+ * head_dim columns among the first n_rot columns, the pair (i, i + head_dim/2), i < head_dim/2, is rotated by
+ * theta = pos * base^(-2 i / head_dim) with pos = row mod seq_len:
+ *   (a, b) -> (a cos theta - b sin theta, b cos theta + a sin theta).
+ */
+int oracle_rope_rows_f64(int64_t M, int64_t N, double* y, int64_t head_dim, int64_t n_rot, int64_t seq_len,
+                         double base) {
+  if (M < 0 || N <= 0 || !y || head_dim <= 0 || (head_dim % 2) != 0 || n_rot < 0 || n_rot > N ||
+      (n_rot % head_dim) != 0 || seq_len <= 0 || !(base > 0.0))
+    return -1;
+  const int64_t half = head_dim / 2;
+  for (int64_t m = 0; m < M; ++m) {
+    const double pos = (double)(m % seq_len);
+    double* row = y + m * N;
+    for (int64_t h0 = 0; h0 < n_rot; h0 += head_dim) {
+      for (int64_t i = 0; i < half; ++i) {
+        const double theta = pos * pow(base, -2.0 * (double)i / (double)head_dim);
+        const double c = cos(theta), s = sin(theta);
+        const double a = row[h0 + i], b = row[h0 + i + half];
+        row[h0 + i] = a * c - b * s;
+        row[h0 + i + half] = b * c + a * s;
+      }
+    }
+  }
+  return 0;
+}

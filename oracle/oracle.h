@@ -81,6 +81,12 @@ int oracle_block_bwd_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const dou
                          const double* dh_out, double* out_dX, double* out_dW1, double* out_dR,
                          double* out_dgamma, double* out_dW2, int nthreads);
 
+/* Rotary position embedding, in place on y [M,N] ("rotate half" pairing; see oracle.c): for each head of
+ * head_dim columns among the first n_rot, the pair (i, i + head_dim/2) is rotated by
+ * (row mod seq_len) * base^(-2 i / head_dim). */
+int oracle_rope_rows_f64(int64_t M, int64_t N, double* y, int64_t head_dim, int64_t n_rot, int64_t seq_len,
+                         double base);
+
 /* silu(x) = x / (1 + exp(-x)) */
 double oracle_silu(double x);
 

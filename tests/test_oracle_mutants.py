@@ -3,7 +3,7 @@
 Each case copies the oracle's C source, plants one plausible mistake (eps outside the square root, a
 dropped residual, a transposed operand, gate and up swapped, r applied twice, gamma dropped, a wrong
 mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent in the fp8
-decoder, and seven mistakes in the backward), rebuilds it in a temporary directory and runs the pin tests
+decoder, seven mistakes in the backward and four in the rotary embedding), rebuilds it in a temporary directory and runs the pin tests
 against it.  Every mutant must fail at least one pin; the unmodified oracle is never touched.
 """
 import os
@@ -46,6 +46,17 @@ MUTANTS_BWD = [
 ]
 
 
+# mistakes in the rotary embedding: a sign of the rotation flipped, the exponent's factor 2 dropped, the
+# position not wrapped at the sequence length, neighbours paired instead of halves
+MUTANTS_ROPE = [
+    ("rope_sin_sign", "row[h0 + i] = a * c - b * s;", "row[h0 + i] = a * c + b * s;"),
+    ("rope_exponent", "pow(base, -2.0 * (double)i / (double)head_dim)", "pow(base, -1.0 * (double)i / (double)head_dim)"),
+    ("rope_no_wrap", "const double pos = (double)(m % seq_len);", "const double pos = (double)m;"),
+    ("rope_pairing", "const double a = row[h0 + i], b = row[h0 + i + half];",
+     "const double a = row[h0 + i], b = row[h0 + (i ^ 1) + half];"),
+]
+
+
 def _run_pins(tmp_path, name, before, after, pins):
     src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
     assert before in src, f"mutation site for {name} no longer exists"
@@ -58,6 +69,11 @@ def _run_pins(tmp_path, name, before, after, pins):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, f"mutant {name} was not caught:\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout
+
+
+@pytest.mark.parametrize("name,before,after", MUTANTS_ROPE, ids=[m[0] for m in MUTANTS_ROPE])
+def test_rope_pins_catch_planted_mistake(tmp_path, name, before, after):
+    _run_pins(tmp_path, name, before, after, "tests/test_oracle_rope_pins.py")
 
 
 @pytest.mark.parametrize("name,before,after", MUTANTS_BWD, ids=[m[0] for m in MUTANTS_BWD])
