@@ -19,6 +19,8 @@ Besides the headline the line carries:
                 timed with HIP events, against the dense fp8 MFMA peak (5 PFLOP/s)
   backward      the block's backward (dX, dW1, dR, dgamma, dW2 from dz and dh_out; four products of the
                 forward's sizes, 2x its flops), fused and unfused, timed with HIP events
+  rope          the 1B MLP-out -> QKV block with a rotary embedding of the q and k heads: in GEMM2's epilogue,
+                against the plain block and the plain block followed by a separate rotation pass
 """
 from __future__ import annotations
 
@@ -154,6 +156,39 @@ def time_bwd(wl, X, W1, g, W2, h, ws, n_ev: int, warmup: int, torch, cb) -> dict
             "unfused_ms": round(u_ms, 4), "speedup_fused_vs_unfused": round(u_ms / f_ms, 4)}
 
 
+def time_rope(dev, n_ev: int, warmup: int, torch, cb) -> dict:
+    """The QKV block with RoPE on the q and k heads (32 + 8 heads of 64 of the 48), seq_len 2048, base 5e5:
+    fused into GEMM2's epilogue, against the plain block alone and the plain block + a separate pass."""
+    from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, WORKLOADS, make_inputs
+
+    wl = WORKLOADS["1b_mlp_out_qkv"]
+    seq_len, n_rot, base = 2048, 2560, 500000.0
+    inp = make_inputs(wl)
+    X, W1, R, g, W2 = (t.to(dev) for t in (inp.X, inp.W1, inp.R, inp.gamma, inp.W2))
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(wl.M, wl.N2, dtype=torch.bfloat16, device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, EPI_IDENTITY, device=dev)
+    plain = lambda: cb.coda_block_fwd(X, W1, R, g, W2, wl.eps, EPI_IDENTITY, h, y, ws)
+    fused = lambda: cb.coda_block_fwd_rope(X, W1, R, g, W2, wl.eps, seq_len, n_rot, base, h, y, ws)
+
+    def separate():
+        plain()
+        cb.coda_rope_rows(y, seq_len, n_rot, base)
+
+    for _ in range(warmup):
+        plain()
+        fused()
+        separate()
+    torch.cuda.synchronize()
+    p_ms, f_ms, s_ms = (time_loop(fn, n_ev, torch) for fn in (plain, fused, separate))
+    return {"workload": wl.name, "seq_len": seq_len, "n_rope_cols": n_rot, "rope_base": base,
+            "fused_ms": round(f_ms, 4), "tflops": round(wl.flops / (f_ms * 1e-3) / 1e12, 2),
+            "plain_block_ms": round(p_ms, 4), "separate_pass_ms": round(s_ms, 4),
+            "fused_overhead_vs_plain_pct": round(100 * (f_ms / p_ms - 1), 2),
+            "speedup_fused_vs_separate": round(s_ms / f_ms, 4),
+            "hbm_bytes_saved_algorithmic": 2 * 2 * wl.M * n_rot}
+
+
 def traffic_record(src_hash: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -173,6 +208,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true", help="skip the e4m3 block timing")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding block timing")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
@@ -280,6 +316,8 @@ def main() -> int:
         line["backward"] = time_bwd(wl, X, W1, g, W2, h, ws, n_ev, args.warmup, torch, cb)
     if not args.no_fp8:
         line["fp8"] = time_fp8(dev, n_ev, args.warmup, torch, cb)
+    if not args.no_rope:
+        line["rope"] = time_rope(dev, n_ev, args.warmup, torch, cb)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(line))

@@ -28,7 +28,8 @@ EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_wo
            "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused", "coda_block_fwd_fp8",
            "coda_block_unfused_fp8",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
-           "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused")
+           "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_fwd_rope",
+           "coda_rope_rows")
 
 
 class CodaError(RuntimeError):
@@ -69,6 +70,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.coda_partial_rms_reduce.restype = i32
     lib.coda_gemm2_rowscale.argtypes = [vp, vp, vp, i32, vp, i64, i64, i64, vp]
     lib.coda_gemm2_rowscale.restype = i32
+    lib.coda_block_fwd_rope.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, f32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+    lib.coda_block_fwd_rope.restype = i32
+    lib.coda_rope_rows.argtypes, lib.coda_rope_rows.restype = [vp, i64, i64, i64, i64, f32, vp], i32
     lib.coda_bwd_workspace_bytes.argtypes, lib.coda_bwd_workspace_bytes.restype = [i64, i64, i64, i64, i32], sz
     bwd = [vp] * 13 + [i64, i64, i64, i64, vp, sz, vp]
     for name in ("coda_block_bwd", "coda_block_bwd_unfused"):
@@ -147,6 +151,30 @@ def coda_block_fwd(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y,
 def coda_block_unfused(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y, workspace, stream=None):
     """Unfused three-kernel baseline with the same outputs."""
     _block("coda_block_unfused", X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspace, stream)
+
+
+def coda_block_fwd_rope(X, W1, R, gamma, W2, eps: float, seq_len: int, n_rope_cols: int, rope_base: float, out_h,
+                        out_y, workspace, stream=None):
+    """Fused block (identity epilogue) with a rotary embedding of the first n_rope_cols output columns."""
+    M, K1 = X.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    args = (_dev(X, "X", torch.bfloat16, (M, K1)), _dev(W1, "W1", torch.bfloat16, (K1, D)),
+            _dev(R, "R", torch.bfloat16, (M, D)), _dev(gamma, "gamma", torch.float32, (D,)),
+            _dev(W2, "W2", torch.bfloat16, (D, N2)))
+    st = load().coda_block_fwd_rope(*args, float(eps), int(seq_len), int(n_rope_cols), float(rope_base),
+                                    _dev(out_h, "out_h", torch.bfloat16, (M, D)),
+                                    _dev(out_y, "out_y", torch.bfloat16, (M, N2)), M, K1, D, N2,
+                                    _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(st, "coda_block_fwd_rope")
+
+
+def coda_rope_rows(y, seq_len: int, n_rope_cols: int, rope_base: float, stream=None):
+    """In-place rotary embedding of bf16 y [M,N] (the separate-pass counterpart)."""
+    M, N = y.shape
+    st = load().coda_rope_rows(_dev(y, "y", torch.bfloat16), M, N, int(seq_len), int(n_rope_cols), float(rope_base),
+                               _stream(stream))
+    _check(st, "coda_rope_rows")
 
 
 def _block_fp8(name: str, Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, workspace, stream):

@@ -173,6 +173,15 @@ int validate_block(const void* X, const float* sx, const void* W1, const float* 
   return check_alias(in, 8, out, 3, out_h, R);
 }
 
+int check_rope(int64_t N, int64_t seq_len, int64_t n_rot, float base) {
+  if (seq_len < 1 || seq_len > kMaxDim) return fail(CODA_ERR_INVALID_ARG, "seq_len must be >= 1");
+  if (n_rot < 0 || n_rot > N || n_rot % 64)
+    return fail(CODA_ERR_INVALID_ARG, "n_rope_cols=%lld must be a multiple of 64 in [0, %lld]", (long long)n_rot,
+                (long long)N);
+  if (!std::isfinite(base) || !(base > 0.0f)) return fail(CODA_ERR_INVALID_ARG, "rope_base must be finite and > 0");
+  return CODA_OK;
+}
+
 // ---- backward ----
 struct BwdWorkspace {
   uint16_t* G;    // r gamma P [M,D] bf16 (unfused: after P itself)
@@ -290,6 +299,49 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
     return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, epi_kind == CODA_EPI_SWIGLU,
                                                  (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
                      "gemm2_rowscale launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_block_fwd_rope(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                        int64_t seq_len, int64_t n_rope_cols, float rope_base, void* out_h, void* out_y, int64_t M,
+                        int64_t K1, int64_t D, int64_t N2, void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    int s = validate_block(X, nullptr, W1, nullptr, R, gamma, W2, nullptr, eps, CODA_EPI_IDENTITY, out_h, out_y, M,
+                           K1, D, N2, workspace, workspace_bytes, 0, 0);
+    if (s) return s;
+    if ((s = check_rope(N2, seq_len, n_rope_cols, rope_base))) return s;
+    hipStream_t st = (hipStream_t)stream;
+    Workspace w;
+    carve(workspace, M, D, 0, 0, &w);
+    if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
+                                                   gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
+                                                   st),
+                       "gemm1_res_prms launch")))
+      return s;
+    if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
+                       "prms_reduce launch")))
+      return s;
+    return hip_check(coda::launch_gemm2_rowscale_rope(w.hg, (const uint16_t*)W2, w.r, (int)seq_len, (int)n_rope_cols,
+                                                      rope_base, (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                     "gemm2_rowscale_rope launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_rope_rows(void* y, int64_t M, int64_t N, int64_t seq_len, int64_t n_rope_cols, float rope_base,
+                   void* stream) {
+  try {
+    int s;
+    if ((s = check_ptr(y, "y"))) return s;
+    if (M < 1 || N < 1 || M > kMaxDim || N > kMaxDim || M * N > kMaxDim * 2)
+      return fail(CODA_ERR_INVALID_ARG, "bad dimensions M=%lld N=%lld", (long long)M, (long long)N);
+    if ((s = check_rope(N, seq_len, n_rope_cols, rope_base))) return s;
+    return hip_check(coda::launch_rope_rows((uint16_t*)y, (int)M, (int)N, (int)seq_len, (int)n_rope_cols, rope_base,
+                                            (hipStream_t)stream),
+                     "rope_rows launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }

@@ -23,7 +23,23 @@
 
 namespace coda {
 
-enum EpiMode { MODE_RES_PRMS = 0, MODE_STORE = 1, MODE_ROWSCALE = 2, MODE_ROWSCALE_SWIGLU = 3 };
+enum EpiMode { MODE_RES_PRMS = 0, MODE_STORE = 1, MODE_ROWSCALE = 2, MODE_ROWSCALE_SWIGLU = 3, MODE_ROWSCALE_ROPE = 4 };
+
+// Rotary position embedding applied in MODE_ROWSCALE_ROPE's epilogue: the first n_rot output columns form
+// heads of 64; in each, the pair (i, i + 32) is rotated by pos * base^(-2 i / 64), pos = row mod seq_len.
+// rev[i] = base^(-2 i / 64) / (2 pi) is built on the host in double: the angle is taken in revolutions, reduced
+// to [0, 1) and fed to the hardware sine and cosine, whose input is in revolutions over a limited range.
+struct RopeParams {
+  int seq_len;
+  int n_rot;
+  float rev[32];
+};
+
+__device__ __forceinline__ void rope_sincos(float pos, float rev, float& c, float& s) {
+  const float t = __builtin_amdgcn_fractf(pos * rev);
+  c = __builtin_amdgcn_cosf(t);
+  s = __builtin_amdgcn_sinf(t);
+}
 
 // silu(x) = x / (1 + exp(-x)) in fp32 with the hardware exp2 and reciprocal (each about 1 ulp; the result
 // is rounded to bf16 afterwards).
@@ -51,13 +67,14 @@ struct GateUpCols {
 //                   part[tn][m] = sum over the tile's columns of (v + R)^2
 //   MODE_STORE:     out [M,Nb] = bf16(v)
 //   MODE_ROWSCALE:  out [M,Nb] = bf16(v)
+//   MODE_ROWSCALE_ROPE: out [M,Nb] = bf16(rope(v)) (bf16 operands; see RopeParams)
 //   MODE_ROWSCALE_SWIGLU: the tile's columns are 128 gate columns [tn*128, +128) and the matching 128 up
 //                   columns [Nb/2 + tn*128, +128); out [M,Nb/2] = bf16(silu(v_gate) * v_up)
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
-    float* __restrict__ part, int M, int K, int Nb, int group_m) {
+    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope) {
   // the mainloop ring (reused as the output staging area), plus the row-sum exchange of MODE_RES_PRMS
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 : 0)];
   const int tiles_m = (M + BM - 1) / BM;
@@ -204,6 +221,44 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         }
       }
     }
+  } else if (MODE == MODE_ROWSCALE_ROPE) {
+    // a wave's 64 accumulator columns are one head: block 0 holds head columns 0..31, block 1 columns 32..63,
+    // so the rotated pairs (i, i + 32) share a lane and a register index
+    const int head0 = tn * BN + wn * 64;
+    const bool rotate = head0 < rope.n_rot;
+    float rev[4][4];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rev[gq][e] = half ? rope.rev[8 * gq + 4 + e] : rope.rev[8 * gq + e];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const int r = wm * 128 + mb * 32 + (lane & 31);
+      const int m = m0 + r;
+      const float pos = (float)((m < M ? m : M - 1) % rope.seq_len);
+      const float sc = rsv[mb];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float lo[4], hi[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = acc[mb][0][4 * gq + e] * sc, b = acc[mb][1][4 * gq + e] * sc;
+          if (rotate) {
+            float c, sn;
+            rope_sincos(pos, rev[gq][e], c, sn);
+            lo[e] = a * c - b * sn;
+            hi[e] = b * c + a * sn;
+          } else {
+            lo[e] = a;
+            hi[e] = b;
+          }
+        }
+        *(u32x2*)(smem + tile_off<32>(r, wn * 8 + gq) + 8 * half) = (u32x2){pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])};
+        *(u32x2*)(smem + tile_off<32>(r, wn * 8 + 4 + gq) + 8 * half) = (u32x2){pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])};
+      }
+    }
+    __syncthreads();
+    store_tile_rows<32>(smem, out, Nb, m0, tn * BN, M);
   } else {  // MODE_ROWSCALE_SWIGLU: accumulator block 0 holds gate columns, block 1 the matching up columns
     const int ny = Nb / 2;
     const int c_base = tn * 128 + wn * 32 + 4 * half;
@@ -443,12 +498,12 @@ static int group_m_for(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 template <int MODE, bool FP8>
 static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, const uint16_t* R, const float* rowsc,
                               const float* colsc, uint16_t* out, uint16_t* out2, float* part, int M, int K, int Nb,
-                              hipStream_t stream) {
+                              hipStream_t stream, RopeParams rope = RopeParams{}) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   dim3 grid(tiles_m * tiles_n), block(NTHREADS);
   hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
-                     out2, part, M, K, Nb, group_m_for(tiles_m));
+                     out2, part, M, K, Nb, group_m_for(tiles_m), rope);
   return hipGetLastError();
 }
 
@@ -483,6 +538,44 @@ hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const fl
     return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2,
                                                     stream);
   return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2, stream);
+}
+
+static RopeParams rope_params(int seq_len, int n_rot, float base) {
+  RopeParams p;
+  p.seq_len = seq_len;
+  p.n_rot = n_rot;
+  for (int i = 0; i < 32; ++i) p.rev[i] = (float)(pow((double)base, -(double)(2 * i) / 64.0) / (2.0 * M_PI));
+  return p;
+}
+
+hipError_t launch_gemm2_rowscale_rope(const uint16_t* A, const uint16_t* W2, const float* r, int seq_len, int n_rot,
+                                      float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+  return launch_gemm<MODE_ROWSCALE_ROPE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2,
+                                                stream, rope_params(seq_len, n_rot, base));
+}
+
+// Standalone rotary embedding, in place on bf16 Y [M,N] (the unfused counterpart): one thread per pair.
+__global__ __launch_bounds__(256) void rope_rows_kernel(uint16_t* Y, int M, int N, RopeParams rope) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int pairs = rope.n_rot / 2;
+  if (idx >= (int64_t)M * pairs) return;
+  const int m = (int)(idx / pairs), p = (int)(idx % pairs);
+  const int head = p / 32, i = p % 32;
+  float c, sn;
+  rope_sincos((float)(m % rope.seq_len), rope.rev[i], c, sn);
+  uint16_t* row = Y + (int64_t)m * N + head * 64;
+  const float a = __uint_as_float((uint32_t)row[i] << 16), b = __uint_as_float((uint32_t)row[i + 32] << 16);
+  const uint32_t o = pack_bf16(a * c - b * sn, b * c + a * sn);
+  row[i] = (uint16_t)(o & 0xffff);
+  row[i + 32] = (uint16_t)(o >> 16);
+}
+
+hipError_t launch_rope_rows(uint16_t* Y, int M, int N, int seq_len, int n_rot, float base, hipStream_t stream) {
+  const int64_t n = (int64_t)M * (n_rot / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, Y, M, N,
+                     rope_params(seq_len, n_rot, base));
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,

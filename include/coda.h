@@ -128,6 +128,24 @@ int coda_block_unfused_fp8(const void* Xq, const float* sx, const void* W1q, con
                            void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
                            size_t workspace_bytes, void* stream);
 
+/* The fused block with a rotary position embedding after the row scale (identity epilogue), for a block that
+ * feeds attention (QKV projection).  The write-up lists RoPE among the epilogue-fusable operations (section
+ * "CODA: the treasure hidden in the epilogue"; section "Five blocks and a Lego language": elementwise
+ * transforms).  Convention (the pages fix none; this is the LLaMA-family "rotate half" form): the first
+ * n_rope_cols columns of y form heads of 64 columns; in each, the pair (i, i + 32) is rotated by
+ * theta = pos * rope_base^(-2 i / 64) with pos = row mod seq_len:
+ *   (a, b) -> (a cos theta - b sin theta, b cos theta + a sin theta),  a, b = r * (h W2') in fp32;
+ * y = bf16 of the result; columns >= n_rope_cols are y = bf16(r * (h W2')).  Arguments, outputs, shape rules
+ * and workspace as coda_block_fwd with CODA_EPI_IDENTITY; n_rope_cols a multiple of 64 in [0, N2],
+ * seq_len >= 1, rope_base finite and > 0 (else CODA_ERR_INVALID_ARG). */
+int coda_block_fwd_rope(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                        int64_t seq_len, int64_t n_rope_cols, float rope_base, void* out_h, void* out_y, int64_t M,
+                        int64_t K1, int64_t D, int64_t N2, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same rotation as a separate pass, in place on bf16 y [M,N] (the unfused counterpart of
+ * coda_block_fwd_rope, used to measure what the epilogue saves).  Same convention and argument rules. */
+int coda_rope_rows(void* y, int64_t M, int64_t N, int64_t seq_len, int64_t n_rope_cols, float rope_base, void* stream);
+
 /* Byte offset of r [M] (fp32) inside the workspace of every block entry point. */
 size_t coda_workspace_r_offset(int64_t M, int64_t D);
 

@@ -233,3 +233,44 @@ def test_bwd_no_gpu_reports_hip_error(lib):
     assert _bcall(lib, a) == HIP
     a = _bargs(dh_out=0)  # dh_out is optional
     assert _bcall(lib, a) == HIP
+
+
+def _rcall(lib, a, seq_len=2048, n_rot=256, base=10000.0):
+    return lib.coda_block_fwd_rope(a["X"], a["W1"], a["R"], a["gamma"], a["W2"], a["eps"], seq_len, n_rot, base,
+                                   a["out_h"], a["out_y"], a["M"], a["K1"], a["D"], a["N2"], a["ws"], a["ws_bytes"],
+                                   None)
+
+
+@pytest.mark.parametrize("case,kw,want", [
+    ("seq_len_zero", dict(seq_len=0), INVALID),
+    ("n_rot_not_64", dict(n_rot=96), INVALID),
+    ("n_rot_negative", dict(n_rot=-64), INVALID),
+    ("n_rot_past_N2", dict(n_rot=576), INVALID),
+    ("base_zero", dict(base=0.0), INVALID),
+    ("base_negative", dict(base=-1.0), INVALID),
+    ("base_nan", dict(base=float("nan")), INVALID),
+    ("base_inf", dict(base=float("inf")), INVALID),
+])
+def test_rope_validation(lib, case, kw, want):
+    assert _rcall(lib, _args(), **kw) == want, lib.coda_last_error()
+    y = BASE + 6 * GB
+    assert lib.coda_rope_rows(y, 100, 512, kw.get("seq_len", 2048), kw.get("n_rot", 256), kw.get("base", 1e4),
+                              None) == want
+
+
+def test_rope_block_rules(lib):
+    # the block's own rules come first, and only the identity epilogue's workspace is needed
+    assert _rcall(lib, _args(N2=384)) == UNSUPPORTED
+    assert _rcall(lib, _args(out_y=BASE + 16)) == ALIAS
+    a = _args()
+    a["ws_bytes"] = lib.coda_workspace_bytes(a["M"], a["K1"], a["D"], a["N2"], 0, 0, 0) - 1
+    assert _rcall(lib, a) == WORKSPACE
+    assert lib.coda_rope_rows(0, 100, 512, 2048, 256, 1e4, None) == INVALID
+    assert lib.coda_rope_rows(BASE, 0, 512, 2048, 256, 1e4, None) == INVALID
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_rope_no_gpu_reports_hip_error(lib):
+    assert _rcall(lib, _args()) == HIP
+    assert _rcall(lib, _args(), n_rot=0) == HIP
+    assert lib.coda_rope_rows(BASE, 100, 512, 2048, 256, 1e4, None) == HIP
