@@ -3,11 +3,14 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one coda_block_fwd call (all three kernels: GEMM1 + residual + partial sums of squares, the
-row-scale reduction, GEMM2 on h * gamma with the row scale and SwiGLU) on inputs already resident in HBM.
+A step is one coda_block_fwd call (GEMM1 + residual + partial sums of squares, then GEMM2 on h * gamma whose
+workgroups reduce their rows' partial sums to the row scale and apply it and SwiGLU in the epilogue) on inputs
+already resident in HBM.
 W untimed steps, then K timed steps between two device synchronisations.  Prints ONE JSON line.
 
 Besides the headline the line carries:
+  kernels_ms    each step entry point timed alone (GEMM1, the stand-alone reduce, GEMM2 with a given row
+                scale), the block, and the three step kernels back to back (the block before the fold)
   roofline      the dominant kernel (GEMM2) timed alone with HIP events on the stream it runs on, its
                 algorithmic flops (2 M D N2) per launch divided by the average launch time, against the
                 published bf16 dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3 counter
@@ -281,6 +284,12 @@ def main() -> int:
         fn()
     torch.cuda.synchronize()
     k1_ms, k2_ms, k3_ms = (time_loop(fn, n_ev, torch) for fn in (k1, k2, k3))
+    def three_steps():  # the same fused path with the reduce as its own kernel between the two GEMMs
+        k1()
+        k2()
+        k3()
+
+    three_ms = time_loop(three_steps, n_ev, torch)
     for _ in range(args.warmup):
         step_unfused()
     unf_ms = time_loop(step_unfused, n_ev, torch)
@@ -306,7 +315,8 @@ def main() -> int:
         "pct_bf16_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "roofline": roofline,
         "kernels_ms": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
-                       "gemm2_rowscale": round(k3_ms, 4), "fused_block_events": round(fused_ev_ms, 4)},
+                       "gemm2_rowscale": round(k3_ms, 4), "fused_block_events": round(fused_ev_ms, 4),
+                       "three_step_kernels_events": round(three_ms, 4)},
         "unfused": {"ms_per_step": round(unf_ms, 4), "tflops": round(wl.flops / (unf_ms * 1e-3) / 1e12, 2),
                     "speedup_fused_vs_unfused": round(unf_ms / fused_ev_ms, 4)},
         "hbm_bytes": {"fused_algorithmic": fb, "unfused_algorithmic": ub, "saved_algorithmic": ub - fb},

@@ -293,6 +293,11 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
                                                    st),
                        "gemm1_res_prms launch")))
       return s;
+    if (coda::fold_supported((int)D))  // the reduce runs inside K3's workgroups
+      return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
+                                                        epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M,
+                                                        (int)D, (int)N2, st),
+                       "gemm2_rowscale_fold launch");
     if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                        "prms_reduce launch")))
       return s;
@@ -320,6 +325,11 @@ int coda_block_fwd_rope(const void* X, const void* W1, const void* R, const floa
                                                    st),
                        "gemm1_res_prms launch")))
       return s;
+    if (coda::fold_supported((int)D))
+      return hip_check(coda::launch_gemm2_rowscale_rope_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
+                                                             (int)seq_len, (int)n_rope_cols, rope_base,
+                                                             (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                       "gemm2_rowscale_rope_fold launch");
     if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                        "prms_reduce launch")))
       return s;

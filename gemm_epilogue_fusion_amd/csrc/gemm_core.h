@@ -155,10 +155,16 @@ __device__ __forceinline__ void interleave_mma_reads() {
 //   A: [M,K] bf16, row stride lda; rows >= M are read as row M-1 (their results are never stored).
 //   B: [K,*] bf16, row stride ldb.  bcol(c) gives the global column of the tile's 8-column chunk c
 //      (0..31), which lets a tile gather column segments (the gate | up halves of SwiGLU).
-template <class BCol>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// hook() runs once, after the first stage has landed (its loads issued before the mainloop have had the
+// first stage's latency to complete); it must issue no memory operation of its own.
+template <class BCol, class Hook = NoHook>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
                                               const uint16_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
-                                              char* smem, f32x16 (&acc)[4][NB]) {
+                                              char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{}) {
   constexpr int LPW = 16 / NWAVES;              // 1 KiB direct loads per wave per operand per stage
   constexpr int PER = 2 * LPW;  // VMEM instructions per wave per stage
   const int t = threadIdx.x;
@@ -233,6 +239,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
 #pragma unroll
   for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
   wait_barrier<2 * PER>();
+  hook();
   read_frags(smem, lo, 0, f0);
 
   const int nblk = nk / NSTAGE;

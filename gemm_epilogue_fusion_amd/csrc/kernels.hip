@@ -35,6 +35,18 @@ struct RopeParams {
   float rev[32];
 };
 
+// The partial-RMS reduce folded into the second GEMM (T > 0): the workgroup forms the row scales of its own
+// rows from the first GEMM's partial sums, r = 1 / sqrt((sum_t part[t][m]) / D + eps) with t summed in order
+// 0..T-1 (the expression of prms_reduce_kernel, so the values are the same), and the tiles of column 0 write
+// r out for the backward.
+constexpr int FOLD_MAX_T = 16;  // D <= 4096
+struct RowFold {
+  int T;
+  float D;
+  float eps;
+  float* r;
+};
+
 __device__ __forceinline__ void rope_sincos(float pos, float rev, float& c, float& s) {
   const float t = __builtin_amdgcn_fractf(pos * rev);
   c = __builtin_amdgcn_cosf(t);
@@ -74,14 +86,40 @@ template <int MODE, bool FP8>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
-    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope) {
-  // the mainloop ring (reused as the output staging area), plus the row-sum exchange of MODE_RES_PRMS
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 : 0)];
+    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold) {
+  // row-scale modes of the bf16 second GEMM can fold the partial-RMS reduce in (see RowFold)
+  constexpr bool CAN_FOLD = !FP8 && (MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE);
+  // the mainloop ring (reused as the output staging area), plus the row-sum exchange of MODE_RES_PRMS or the
+  // folded row scales
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 : CAN_FOLD ? 1024 : 0)];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM;
+
+  // folded reduce: thread t < 256 fetches the partial sums of row m0 + t before the mainloop and forms its
+  // r once the first stage has landed; indexes past T re-read part[T-1] and are not summed
+  const bool folding = CAN_FOLD && fold.T > 0;
+  float pv[FOLD_MAX_T];
+  float rfold = 1.0f;
+  if (CAN_FOLD && folding && threadIdx.x < BM) {
+    const int row = m0 + (int)threadIdx.x < M ? m0 + (int)threadIdx.x : M - 1;
+#pragma unroll
+    for (int i = 0; i < FOLD_MAX_T; ++i) pv[i] = part[(int64_t)(i < fold.T ? i : fold.T - 1) * M + row];
+  }
+  auto fold_hook = [&]() {
+    if (CAN_FOLD && folding && threadIdx.x < BM) {
+      // pin the sum here: hoisted above the mainloop's first loads, it would wait out the fetch alone
+#pragma unroll
+      for (int i = 0; i < FOLD_MAX_T; ++i) asm volatile("" : "+v"(pv[i]));
+      float s = 0.0f;
+#pragma unroll
+      for (int i = 0; i < FOLD_MAX_T; ++i)
+        if (i < fold.T) s += pv[i];
+      rfold = 1.0f / sqrtf(s / fold.D + fold.eps);
+    }
+  };
 
   f32x16 acc[4][NB];
   if (FP8) {
@@ -95,9 +133,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const uint16_t* A16 = (const uint16_t*)A;
     const uint16_t* B16 = (const uint16_t*)B;
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop(A16, K, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, K, smem, acc);
+      gemm_mainloop(A16, K, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, K, smem, acc, fold_hook);
     else
-      gemm_mainloop(A16, K, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc);
+      gemm_mainloop(A16, K, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook);
   }
 
   // Materialise the accumulators here: otherwise the compiler may sink the last MFMAs into the epilogue's
@@ -120,12 +158,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
 
   // per-row scales of this lane's four rows (rows past M read row M-1; they are never stored)
   float rsv[4];
+  float* fold_r = (float*)(smem + LDS_BYTES);
+  if (CAN_FOLD && folding) {
+    if (t < BM) {
+      fold_r[t] = rfold;
+      if (tn == 0 && m0 + t < M) fold.r[m0 + t] = rfold;
+    }
+  } else {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
-    const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-    rsv[mb] = rowsc ? rowsc[m < M ? m : M - 1] : 1.0f;
+    for (int mb = 0; mb < 4; ++mb) {
+      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+      rsv[mb] = rowsc ? rowsc[m < M ? m : M - 1] : 1.0f;
+    }
   }
-  __syncthreads();  // every wave is done with the mainloop's LDS stages
+  __syncthreads();  // every wave is done with the mainloop's LDS stages (and the folded row scales are in)
+  if (CAN_FOLD && folding) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) rsv[mb] = fold_r[wm * 128 + mb * 32 + (lane & 31)];
+  }
 
   if (MODE == MODE_RES_PRMS || MODE == MODE_STORE || MODE == MODE_ROWSCALE) {
     // h * gamma is written by the bf16 K1 only (the e4m3 path forms it in K2 from the stored h)
@@ -498,12 +548,12 @@ static int group_m_for(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 template <int MODE, bool FP8>
 static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, const uint16_t* R, const float* rowsc,
                               const float* colsc, uint16_t* out, uint16_t* out2, float* part, int M, int K, int Nb,
-                              hipStream_t stream, RopeParams rope = RopeParams{}) {
+                              hipStream_t stream, RopeParams rope = RopeParams{}, RowFold fold = RowFold{}) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   dim3 grid(tiles_m * tiles_n), block(NTHREADS);
   hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
-                     out2, part, M, K, Nb, group_m_for(tiles_m), rope);
+                     out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold);
   return hipGetLastError();
 }
 
@@ -540,6 +590,18 @@ hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const fl
   return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2, stream);
 }
 
+int fold_supported(int D) { return D / BN <= FOLD_MAX_T; }
+
+hipError_t launch_gemm2_rowscale_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps, float* r,
+                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+  const RowFold f{D / BN, (float)D, eps, r};
+  if (swiglu)
+    return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr,
+                                                    (float*)part, M, D, N2, stream, RopeParams{}, f);
+  return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr, (float*)part, M, D,
+                                           N2, stream, RopeParams{}, f);
+}
+
 static RopeParams rope_params(int seq_len, int n_rot, float base) {
   RopeParams p;
   p.seq_len = seq_len;
@@ -552,6 +614,14 @@ hipError_t launch_gemm2_rowscale_rope(const uint16_t* A, const uint16_t* W2, con
                                       float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
   return launch_gemm<MODE_ROWSCALE_ROPE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2,
                                                 stream, rope_params(seq_len, n_rot, base));
+}
+
+hipError_t launch_gemm2_rowscale_rope_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps,
+                                           float* r, int seq_len, int n_rot, float base, uint16_t* Y, int M, int D,
+                                           int N2, hipStream_t stream) {
+  return launch_gemm<MODE_ROWSCALE_ROPE, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr, (float*)part,
+                                                M, D, N2, stream, rope_params(seq_len, n_rot, base),
+                                                RowFold{D / BN, (float)D, eps, r});
 }
 
 // Standalone rotary embedding, in place on bf16 Y [M,N] (the unfused counterpart): one thread per pair.

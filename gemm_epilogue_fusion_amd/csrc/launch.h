@@ -15,10 +15,18 @@ hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps,
 // K3 (r non-null; A = h * gamma) and U3 (r null; A = the normalised rows): Y = bf16(epi(r * (A W2))).
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
                                  int M, int D, int N2, hipStream_t stream);
+// K2 folded into K3 (D / 256 <= 16, see fold_supported): the row scales come from the partial sums of K1, are
+// formed per workgroup as launch_prms_reduce forms them, and are written to r by the tiles of column 0.
+int fold_supported(int D);
+hipError_t launch_gemm2_rowscale_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps, float* r,
+                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream);
 // K3 with a rotary embedding after the row scale (identity epilogue): Y = bf16(rope(r * (A W2))); the first n_rot
 // columns form heads of 64 rotated at position row mod seq_len with frequencies base^(-2i/64).
 hipError_t launch_gemm2_rowscale_rope(const uint16_t* A, const uint16_t* W2, const float* r, int seq_len, int n_rot,
                                       float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream);
+hipError_t launch_gemm2_rowscale_rope_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps,
+                                           float* r, int seq_len, int n_rot, float base, uint16_t* Y, int M, int D,
+                                           int N2, hipStream_t stream);
 // The same rotation as a separate in-place pass over bf16 Y [M,N] (the unfused counterpart).
 hipError_t launch_rope_rows(uint16_t* Y, int M, int N, int seq_len, int n_rot, float base, hipStream_t stream);
 // U1: T = bf16(X W).

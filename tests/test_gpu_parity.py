@@ -120,6 +120,34 @@ def test_steps_one_by_one():
     check_y(f64(y), oy)
 
 
+FOLD = [SMALL[1], SMALL[3], SMALL[4],
+        Workload("fold_t16", M=300, K1=256, D=4096, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=7),
+        Workload("no_fold_t17", M=130, K1=128, D=4352, N2=256, epi=EPI_SWIGLU, eps=1e-5, seed=8)]
+
+
+@pytest.mark.parametrize("wl", FOLD, ids=[w.name for w in FOLD])
+def test_block_equals_its_three_steps(wl):
+    """coda_block_fwd (the partial-RMS reduce folded into the second GEMM where D / 256 <= 16, the separate
+    reduce kernel otherwise) gives the same h, r and y, bit for bit, as the three step entry points run one
+    after another: the fold forms r with the reduce kernel's own expression and summation order."""
+    _say(f"[gpu] block vs its steps {wl.name}")
+    d = DeviceInputs(make_inputs(wl))
+    h, y, r = run_block(d)
+    T = wl.D // 256
+    h2 = torch.empty_like(h)
+    hg = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device="cuda")
+    part = torch.empty(T, wl.M, dtype=torch.float32, device="cuda")
+    r2 = torch.empty(wl.M, dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y)
+    cb.coda_gemm1_residual_partial_rms(d.X, d.W1, d.R, d.gamma, h2, hg, part)
+    cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r2)
+    cb.coda_gemm2_rowscale(hg, d.W2, r2, wl.epi, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(h.view(torch.int16), h2.view(torch.int16))
+    assert torch.equal(r.view(torch.int32), r2.view(torch.int32))
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 def test_partial_reduce_synthetic():
     """Step 2 alone on synthetic partials: fixed-order fp32 sum, within a few fp32 ulps of the fp64 value."""
     _say("[gpu] partial reduce synthetic")
