@@ -78,6 +78,9 @@ def _load():
     lib.oracle_block_bwd_f64.restype = ctypes.c_int
     lib.oracle_rope_rows_f64.argtypes = [i64, i64, dp, i64, i64, i64, f]
     lib.oracle_rope_rows_f64.restype = ctypes.c_int
+    lib.oracle_cross_entropy_f64.argtypes = [i64, i64, i64, dp, dp, ctypes.POINTER(ctypes.c_int64), dp, dp,
+                                             ctypes.c_int]
+    lib.oracle_cross_entropy_f64.restype = ctypes.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ctypes.c_int
     _lib = lib
@@ -169,6 +172,25 @@ def rope_rows(y, head_dim, n_rot, seq_len, base):
     if rc != 0:
         raise RuntimeError(f"oracle_rope_rows_f64 failed with {rc}")
     return out
+
+
+def cross_entropy(H, W, labels, nthreads=0):
+    """Per-row cross-entropy of the logits H W (H [M,D], W [D,V]) against integer labels [M] (negative =
+    ignored, loss 0).  Returns (loss [M], lse [M]) in fp64."""
+    lib = _load()
+    H, W = _f64(H), _f64(W)
+    M, D = H.shape
+    Db, V = W.shape
+    lab = np.ascontiguousarray(np.asarray(labels, dtype=np.int64).reshape(-1))
+    if Db != D or lab.shape != (M,):
+        raise ValueError("oracle: inconsistent shapes")
+    loss = np.empty(M, np.float64)
+    lse = np.empty(M, np.float64)
+    rc = lib.oracle_cross_entropy_f64(M, D, V, _ptr(H), _ptr(W), lab.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                      _ptr(loss), _ptr(lse), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_cross_entropy_f64 failed with {rc}")
+    return loss, lse
 
 
 def gemm_residual(X, W1, R=None, nthreads=0):

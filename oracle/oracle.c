@@ -502,3 +502,48 @@ int oracle_rope_rows_f64(int64_t M, int64_t N, double* y, int64_t head_dim, int6
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------------ */
+/* cross-entropy of a vocabulary projection                                                         */
+/*
+ * The CODA write-up names cross-entropy among the operations its epilogue programming covers (section "CODA:
+ * the treasure hidden in the epilogue"), with reductions done inside the epilogue and merged by a light
+ * kernel afterwards (section "Five blocks and a Lego language").  What is computed is the plain definition:
+ * logits z = H W (H [M,D], W [D,V]); lse_i = log sum_j exp(z_ij), evaluated as m_i + log sum_j exp(z_ij - m_i)
+ * with m_i = max_j z_ij so that no exponential overflows; loss_i = lse_i - z_{i,label_i}.  A negative label
+ * marks an ignored position: its loss is 0 (its lse is still produced).
+ */
+typedef struct {
+  int64_t D, V;
+  const double *H, *W;
+  const int64_t* labels;
+  double *loss, *lse;
+} ce_ctx;
+
+static void ce_row(void* p, int64_t i, double* z) {
+  ce_ctx* c = (ce_ctx*)p;
+  for (int64_t j = 0; j < c->V; ++j) z[j] = 0.0;
+  for (int64_t k = 0; k < c->D; ++k) {
+    const double h = c->H[i * c->D + k];
+    const double* w = c->W + k * c->V;
+    for (int64_t j = 0; j < c->V; ++j) z[j] += h * w[j];
+  }
+  double m = -INFINITY;
+  for (int64_t j = 0; j < c->V; ++j)
+    if (z[j] > m) m = z[j];
+  double s = 0.0;
+  for (int64_t j = 0; j < c->V; ++j) s += exp(z[j] - m);
+  const double l = m + log(s);
+  const int64_t label = c->labels[i];
+  c->lse[i] = l;
+  c->loss[i] = label < 0 ? 0.0 : l - z[label];
+}
+
+int oracle_cross_entropy_f64(int64_t M, int64_t D, int64_t V, const double* H, const double* W,
+                             const int64_t* labels, double* out_loss, double* out_lse, int nthreads) {
+  if (M < 0 || D < 0 || V < 1 || !H || !W || !labels || !out_loss || !out_lse) return -1;
+  for (int64_t i = 0; i < M; ++i)
+    if (labels[i] >= V) return -1;
+  ce_ctx c = {D, V, H, W, labels, out_loss, out_lse};
+  return for_each_row(M, nthreads, (size_t)V, ce_row, &c);
+}

@@ -87,6 +87,12 @@ int oracle_block_bwd_f64(int64_t M, int64_t K1, int64_t D, int64_t N2, const dou
 int oracle_rope_rows_f64(int64_t M, int64_t N, double* y, int64_t head_dim, int64_t n_rot, int64_t seq_len,
                          double base);
 
+/* Cross-entropy of a vocabulary projection (see oracle.c): logits z = H W with H [M,D], W [D,V];
+ * out_lse[i] = log sum_j exp(z_ij) (max-shifted); out_loss[i] = out_lse[i] - z[i][labels[i]], or 0 where
+ * labels[i] < 0 (ignored).  Labels must be < V. */
+int oracle_cross_entropy_f64(int64_t M, int64_t D, int64_t V, const double* H, const double* W,
+                             const int64_t* labels, double* out_loss, double* out_lse, int nthreads);
+
 /* silu(x) = x / (1 + exp(-x)) */
 double oracle_silu(double x);
 

@@ -3,7 +3,7 @@
 Each case copies the oracle's C source, plants one plausible mistake (eps outside the square root, a
 dropped residual, a transposed operand, gate and up swapped, r applied twice, gamma dropped, a wrong
 mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent in the fp8
-decoder, seven mistakes in the backward and four in the rotary embedding), rebuilds it in a temporary directory and runs the pin tests
+decoder, seven mistakes in the backward, four in the rotary embedding and five in the cross-entropy), rebuilds it in a temporary directory and runs the pin tests
 against it.  Every mutant must fail at least one pin; the unmodified oracle is never touched.
 """
 import os
@@ -57,6 +57,20 @@ MUTANTS_ROPE = [
 ]
 
 
+# mistakes in the cross-entropy: the label's neighbour picked, the log dropped, the first logit left out of
+# the sum, an ignored row given the full lse as its loss, the max shift not added back
+MUTANTS_CE = [
+    ("ce_label_neighbour", "c->loss[i] = label < 0 ? 0.0 : l - z[label];",
+     "c->loss[i] = label < 0 ? 0.0 : l - z[(label + 1) % c->V];"),
+    ("ce_no_log", "const double l = m + log(s);", "const double l = m + s;"),
+    ("ce_sum_skips_first", "for (int64_t j = 0; j < c->V; ++j) s += exp(z[j] - m);",
+     "for (int64_t j = 1; j < c->V; ++j) s += exp(z[j] - m);"),
+    ("ce_ignored_row_loss", "c->loss[i] = label < 0 ? 0.0 : l - z[label];",
+     "c->loss[i] = label < 0 ? l : l - z[label];"),
+    ("ce_shift_not_restored", "const double l = m + log(s);", "const double l = log(s);"),
+]
+
+
 def _run_pins(tmp_path, name, before, after, pins):
     src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
     assert before in src, f"mutation site for {name} no longer exists"
@@ -69,6 +83,11 @@ def _run_pins(tmp_path, name, before, after, pins):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, f"mutant {name} was not caught:\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout
+
+
+@pytest.mark.parametrize("name,before,after", MUTANTS_CE, ids=[m[0] for m in MUTANTS_CE])
+def test_ce_pins_catch_planted_mistake(tmp_path, name, before, after):
+    _run_pins(tmp_path, name, before, after, "tests/test_oracle_ce_pins.py")
 
 
 @pytest.mark.parametrize("name,before,after", MUTANTS_ROPE, ids=[m[0] for m in MUTANTS_ROPE])
