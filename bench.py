@@ -24,6 +24,8 @@ Besides the headline the line carries:
                 forward's sizes, 2x its flops), fused and unfused, timed with HIP events
   rope          the 1B MLP-out -> QKV block with a rotary embedding of the q and k heads: in GEMM2's epilogue,
                 against the plain block and the plain block followed by a separate rotation pass
+  ce            cross-entropy of the 1B LM head (V = 128256) with the logits reduced in the GEMM's epilogue,
+                against storing bf16 logits and reading them back
 """
 from __future__ import annotations
 
@@ -192,6 +194,34 @@ def time_rope(dev, n_ev: int, warmup: int, torch, cb) -> dict:
             "hbm_bytes_saved_algorithmic": 2 * 2 * wl.M * n_rot}
 
 
+def time_ce(dev, n_ev: int, warmup: int, torch, cb) -> dict:
+    """Cross-entropy of the 1B LM head (M=8192, D=2048, V=128256) with the logits never stored, against the
+    baseline that stores bf16 logits and reads them back."""
+    from gemm_epilogue_fusion_amd.inputs import CE_WORKLOADS, make_ce_inputs
+
+    wl = CE_WORKLOADS["1b_lm_head"]
+    H, W, labels = (t.to(dev) for t in make_ce_inputs(wl))
+    loss = torch.empty(wl.M, dtype=torch.float32, device=dev)
+    lse = torch.empty(wl.M, dtype=torch.float32, device=dev)
+    ws = cb.alloc_ce_workspace(wl.M, wl.V, device=dev)
+    wsu = cb.alloc_ce_workspace(wl.M, wl.V, unfused=1, device=dev)
+    fused = lambda: cb.coda_ce_fwd(H, W, labels, loss, lse, ws)
+    unfused = lambda: cb.coda_ce_unfused(H, W, labels, loss, lse, wsu)
+    for _ in range(warmup):
+        fused()
+        unfused()
+    torch.cuda.synchronize()
+    n = max(5, n_ev // 4)
+    f_ms = time_loop(fused, n, torch)
+    u_ms = time_loop(unfused, n, torch)
+    tf = wl.flops / (f_ms * 1e-3) / 1e12
+    T = wl.V // 256
+    saved = 2 * 2 * wl.M * wl.V - 2 * (2 * 4 * T * wl.M + 4 * wl.M)  # logits written + read, minus partials
+    return {"workload": wl.name, "M": wl.M, "D": wl.D, "V": wl.V, "fused_ms": round(f_ms, 4), "tflops": round(tf, 2),
+            "pct_bf16_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2), "unfused_ms": round(u_ms, 4),
+            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4), "hbm_bytes_saved_algorithmic": saved}
+
+
 def traffic_record(src_hash: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -212,6 +242,7 @@ def main() -> int:
     ap.add_argument("--no-fp8", action="store_true", help="skip the e4m3 block timing")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding block timing")
+    ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy timing")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
@@ -328,6 +359,8 @@ def main() -> int:
         line["fp8"] = time_fp8(dev, n_ev, args.warmup, torch, cb)
     if not args.no_rope:
         line["rope"] = time_rope(dev, n_ev, args.warmup, torch, cb)
+    if not args.no_ce:
+        line["ce"] = time_ce(dev, n_ev, args.warmup, torch, cb)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(line))

@@ -29,7 +29,7 @@ EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_wo
            "coda_block_unfused_fp8",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
            "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_fwd_rope",
-           "coda_rope_rows")
+           "coda_rope_rows", "coda_ce_workspace_bytes", "coda_ce_fwd", "coda_ce_unfused")
 
 
 class CodaError(RuntimeError):
@@ -77,6 +77,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     bwd = [vp] * 13 + [i64, i64, i64, i64, vp, sz, vp]
     for name in ("coda_block_bwd", "coda_block_bwd_unfused"):
         getattr(lib, name).argtypes = bwd
+        getattr(lib, name).restype = i32
+    lib.coda_ce_workspace_bytes.argtypes, lib.coda_ce_workspace_bytes.restype = [i64, i64, i32], sz
+    for name in ("coda_ce_fwd", "coda_ce_unfused"):
+        getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -288,3 +292,32 @@ def coda_block_bwd_unfused(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, 
     """Unfused backward baseline with the same outputs."""
     _block_bwd("coda_block_bwd_unfused", X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma,
                out_dW2, workspace, stream)
+
+
+def coda_ce_workspace_bytes(M: int, V: int, unfused: int = 0) -> int:
+    return int(load().coda_ce_workspace_bytes(M, V, unfused))
+
+
+def alloc_ce_workspace(M: int, V: int, unfused: int = 0, device="cuda"):
+    n = coda_ce_workspace_bytes(M, V, unfused)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def _ce(name, H, W, labels, out_loss, out_lse, workspace, stream):
+    M, D = H.shape
+    V = W.shape[1]
+    st = getattr(load(), name)(_dev(H, "H", torch.bfloat16, (M, D)), _dev(W, "W", torch.bfloat16, (D, V)),
+                               _dev(labels, "labels", torch.int32, (M,)), _dev(out_loss, "out_loss", torch.float32, (M,)),
+                               _dev(out_lse, "out_lse", torch.float32, (M,)), M, D, V,
+                               _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(st, name)
+
+
+def coda_ce_fwd(H, W, labels, out_loss, out_lse, workspace, stream=None):
+    """Per-row cross-entropy of H W against labels (int32; negative = ignored) with the logits never stored."""
+    _ce("coda_ce_fwd", H, W, labels, out_loss, out_lse, workspace, stream)
+
+
+def coda_ce_unfused(H, W, labels, out_loss, out_lse, workspace, stream=None):
+    """The same through stored bf16 logits (the baseline)."""
+    _ce("coda_ce_unfused", H, W, labels, out_loss, out_lse, workspace, stream)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcoda.so")
-SOURCES = ["kernels.hip", "bwd_kernels.hip", "api.hip"]
+SOURCES = ["kernels.hip", "bwd_kernels.hip", "ce_kernels.hip", "api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 (v_pk_*_f32) instructions.

@@ -579,3 +579,101 @@ int coda_block_bwd_unfused(const void* X, const void* W1, const void* h, const f
 }
 
 }  // extern "C"
+
+// ---- cross-entropy of a vocabulary projection ----
+namespace {
+
+struct CeWorkspace {
+  float* part_m;  // [V/256][M] per-tile row maxima
+  float* part_s;  // [V/256][M] per-tile row sums of exp(z - max)
+  float* zlab;    // [M] the label's logit
+  uint16_t* z;    // unfused: the bf16 logits [M,V]
+};
+
+size_t carve_ce(void* ws, int64_t M, int64_t V, int unfused, CeWorkspace* w) {
+  char* base = (char*)ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  CeWorkspace x{};
+  if (unfused) {
+    x.z = (uint16_t*)take(ws_mat_bytes(M, V, 2));
+  } else {
+    x.part_m = (float*)take(ws_part_bytes(M, V));
+    x.part_s = (float*)take(ws_part_bytes(M, V));
+    x.zlab = (float*)take(ws_vec_bytes(M));
+  }
+  if (w) *w = x;
+  return off;
+}
+
+int ce(const void* H, const void* W, const int* labels, float* out_loss, float* out_lse, int64_t M, int64_t D,
+       int64_t V, void* workspace, size_t workspace_bytes, void* stream, int unfused) {
+  try {
+    int s;
+    if ((s = check_ptr(H, "H")) || (s = check_ptr(W, "W")) || (s = check_ptr(labels, "labels")) ||
+        (s = check_ptr(out_loss, "out_loss")) || (s = check_ptr(out_lse, "out_lse")))
+      return s;
+    if (M < 1 || D < 1 || V < 1)
+      return fail(CODA_ERR_INVALID_ARG, "dimensions must be >= 1 (M=%lld D=%lld V=%lld)", (long long)M,
+                  (long long)D, (long long)V);
+    if (M > kMaxDim || D > kMaxDim || V > kMaxDim || M * D > kMaxDim * 2 || D * V > kMaxDim * 2 ||
+        M * V > kMaxDim * 8)
+      return fail(CODA_ERR_UNSUPPORTED, "dimensions too large");
+    if (D % 128) return fail(CODA_ERR_UNSUPPORTED, "D=%lld is not a multiple of 128", (long long)D);
+    if (V % 256) return fail(CODA_ERR_UNSUPPORTED, "V=%lld is not a multiple of 256", (long long)V);
+    const size_t need = carve_ce(nullptr, M, V, unfused, nullptr);
+    if (!workspace) return fail(CODA_ERR_WORKSPACE, "workspace is NULL");
+    if ((uintptr_t)workspace & 255) return fail(CODA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(CODA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    const Range in[3] = {rng("H", H, (size_t)M * D * 2), rng("W", W, (size_t)D * V * 2),
+                         rng("labels", labels, (size_t)M * 4)};
+    const Range out[3] = {rng("out_loss", out_loss, (size_t)M * 4), rng("out_lse", out_lse, (size_t)M * 4),
+                          rng("workspace", workspace, need)};
+    if ((s = check_alias(in, 3, out, 3, nullptr, nullptr))) return s;
+    hipStream_t st = (hipStream_t)stream;
+    CeWorkspace w;
+    carve_ce(workspace, M, V, unfused, &w);
+    if (unfused) {
+      if ((s = hip_check(coda::launch_gemm_store((const uint16_t*)H, (const uint16_t*)W, w.z, (int)M, (int)D, (int)V,
+                                                 st),
+                         "ce logits launch")))
+        return s;
+      return hip_check(coda::launch_ce_rows(w.z, labels, (int)M, (int)V, out_loss, out_lse, st), "ce rows launch");
+    }
+    if ((s = hip_check(coda::launch_ce_gemm((const uint16_t*)H, (const uint16_t*)W, labels, w.part_m, w.part_s,
+                                            w.zlab, (int)M, (int)D, (int)V, st),
+                       "ce gemm launch")))
+      return s;
+    return hip_check(coda::launch_ce_reduce(w.part_m, w.part_s, w.zlab, labels, (int)(V / 256), (int)M, (int)V,
+                                            out_loss, out_lse, st),
+                     "ce reduce launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t coda_ce_workspace_bytes(int64_t M, int64_t V, int unfused) {
+  if (M < 1 || V < 256 || M > kMaxDim || V > kMaxDim) return 0;
+  return carve_ce(nullptr, M, V, unfused, nullptr);
+}
+
+int coda_ce_fwd(const void* H, const void* W, const int32_t* labels, float* out_loss, float* out_lse, int64_t M,
+                int64_t D, int64_t V, void* workspace, size_t workspace_bytes, void* stream) {
+  return ce(H, W, labels, out_loss, out_lse, M, D, V, workspace, workspace_bytes, stream, 0);
+}
+
+int coda_ce_unfused(const void* H, const void* W, const int32_t* labels, float* out_loss, float* out_lse, int64_t M,
+                    int64_t D, int64_t V, void* workspace, size_t workspace_bytes, void* stream) {
+  return ce(H, W, labels, out_loss, out_lse, M, D, V, workspace, workspace_bytes, stream, 1);
+}
+
+}  // extern "C"

@@ -84,4 +84,17 @@ hipError_t launch_bwd_reduce(const float* part, int T, const float* part2, int Q
 hipError_t launch_bwd_dh(const uint16_t* G, const uint16_t* h, const uint16_t* dh_out, const float* r, const float* a,
                          int M, int D, uint16_t* dR, uint16_t* dhT, uint16_t* nT, hipStream_t stream);
 
+// ---- cross-entropy of a vocabulary projection (ce_kernels.hip) ----
+// C1: logits z = H W by 256 x 256 tiles; per tile t and row i, part_m[t][i] = max z, part_s[t][i] = sum exp(z -
+// max); zlab[i] = z[i][labels[i]] from the tile holding that column.  D % 128 == 0, V % 256 == 0.
+hipError_t launch_ce_gemm(const uint16_t* H, const uint16_t* W, const int* labels, float* part_m, float* part_s,
+                          float* zlab, int M, int D, int V, hipStream_t stream);
+// C2: lse[i] = merge of the T pairs of row i in tile order; loss[i] = lse[i] - zlab[i] (0 for a negative label,
+// NaN for a label >= V).
+hipError_t launch_ce_reduce(const float* part_m, const float* part_s, const float* zlab, const int* labels, int T,
+                            int M, int V, float* loss, float* lse, hipStream_t stream);
+// CU: the same from stored bf16 logits Z [M,V] (the unfused baseline).
+hipError_t launch_ce_rows(const uint16_t* Z, const int* labels, int M, int V, float* loss, float* lse,
+                          hipStream_t stream);
+
 }  // namespace coda

@@ -138,3 +138,41 @@ def make_grads(wl: Workload, dz_std: float = 1.0, dh_std: float = 1.0):
     dz = _normal((wl.M, wl.N2), dz_std, s, 5).to(torch.bfloat16)
     dh = _normal((wl.M, wl.D), dh_std, s, 6).to(torch.bfloat16)
     return dz, dh
+
+
+# ---- cross-entropy of a vocabulary projection ----
+@dataclass(frozen=True)
+class CeWorkload:
+    """Per-row cross-entropy of H W against labels: H [M,D] (the final normalised hidden states), W [D,V] (the
+    vocabulary projection, [in,out]), labels [M] int32."""
+    name: str
+    M: int
+    D: int
+    V: int
+    h_std: float = 1.0
+    w_std: float = 0.02
+    ignore_every: int = 0   # every n-th row (from row 0) gets the ignored label -100 (0: none)
+    seed: int = 0
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.D * self.V
+
+
+# LLaMA-3-style LM head at the 1B size: hidden 2048, vocabulary 128256 (= 501 x 256), 4 sequences of 2048 tokens.
+# The write-up fixes no vocabulary; labels are uniform over it (a real corpus is Zipf-like, which changes
+# nothing in the arithmetic).
+CE_WORKLOADS: Dict[str, CeWorkload] = {
+    "1b_lm_head": CeWorkload("1b_lm_head", M=8192, D=2048, V=128256, ignore_every=64),
+}
+
+
+def make_ce_inputs(wl: CeWorkload):
+    """Draw (H bf16, W bf16, labels int32) on the CPU with idx H=8, W=9, labels=10 of the seeding scheme."""
+    s = wl.seed
+    H = _normal((wl.M, wl.D), wl.h_std, s, 8).to(torch.bfloat16)
+    W = _normal((wl.D, wl.V), wl.w_std, s, 9).to(torch.bfloat16)
+    labels = torch.randint(0, wl.V, (wl.M,), generator=_gen(s, 10), dtype=torch.int64).to(torch.int32)
+    if wl.ignore_every:
+        labels[::wl.ignore_every] = -100
+    return H, W, labels

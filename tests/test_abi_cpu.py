@@ -274,3 +274,42 @@ def test_rope_no_gpu_reports_hip_error(lib):
     assert _rcall(lib, _args()) == HIP
     assert _rcall(lib, _args(), n_rot=0) == HIP
     assert lib.coda_rope_rows(BASE, 100, 512, 2048, 256, 1e4, None) == HIP
+
+
+def _ccall(lib, fn="coda_ce_fwd", M=300, D=256, V=768, H=BASE, W=BASE + GB, labels=BASE + 2 * GB,
+           loss=BASE + 3 * GB, lse=BASE + 4 * GB, ws=BASE + 5 * GB, ws_bytes=None, unfused=0):
+    if ws_bytes is None:
+        ws_bytes = lib.coda_ce_workspace_bytes(M, V, unfused) if M >= 1 and V >= 256 else 1 << 20
+    return getattr(lib, fn)(H, W, labels, loss, lse, M, D, V, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn,unfused", [("coda_ce_fwd", 0), ("coda_ce_unfused", 1)])
+@pytest.mark.parametrize("case,kw,want", [
+    ("null_H", dict(H=0), INVALID),
+    ("null_labels", dict(labels=0), INVALID),
+    ("misaligned_loss", dict(loss=BASE + 3 * GB + 4), INVALID),
+    ("M_zero", dict(M=0), INVALID),
+    ("D_not_128", dict(D=192), UNSUPPORTED),
+    ("V_not_256", dict(V=1000), UNSUPPORTED),
+    ("loss_on_H", dict(loss=BASE + 64), ALIAS),
+    ("lse_on_loss", dict(lse=BASE + 3 * GB + 256), ALIAS),
+    ("ws_on_labels", dict(ws=BASE + 2 * GB), ALIAS),
+    ("null_workspace", dict(ws=0), WORKSPACE),
+    ("small_workspace", dict(ws_bytes=100), WORKSPACE),
+])
+def test_ce_validation(lib, fn, unfused, case, kw, want):
+    assert _ccall(lib, fn, unfused=unfused, **kw) == want, lib.coda_last_error()
+
+
+def test_ce_workspace_bytes(lib):
+    al = lambda x: (x + 255) // 256 * 256
+    M, V = 8192, 128256
+    assert lib.coda_ce_workspace_bytes(M, V, 0) == 2 * al(V // 256 * M * 4) + al(M * 4)
+    assert lib.coda_ce_workspace_bytes(M, V, 1) == al(M * V * 2)
+    assert lib.coda_ce_workspace_bytes(0, V, 0) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_ce_no_gpu_reports_hip_error(lib):
+    assert _ccall(lib) == HIP
+    assert _ccall(lib, "coda_ce_unfused", unfused=1) == HIP
