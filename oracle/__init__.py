@@ -81,6 +81,10 @@ def _load():
     lib.oracle_cross_entropy_f64.argtypes = [i64, i64, i64, dp, dp, ctypes.POINTER(ctypes.c_int64), dp, dp,
                                              ctypes.c_int]
     lib.oracle_cross_entropy_f64.restype = ctypes.c_int
+    lib.oracle_mx_scale_exp.argtypes, lib.oracle_mx_scale_exp.restype = [f], ctypes.c_int
+    lib.oracle_mx_quant_rows_e4m3.argtypes = [i64, i64, i64, dp, ctypes.POINTER(ctypes.c_uint8),
+                                              ctypes.POINTER(ctypes.c_int32)]
+    lib.oracle_mx_quant_rows_e4m3.restype = ctypes.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ctypes.c_int
     _lib = lib
@@ -277,3 +281,23 @@ def dequant_cols_e4m3(q, s) -> np.ndarray:
     if lib.oracle_dequant_cols_e4m3(rows, cols, _ptr(q, ctypes.c_uint8), _ptr(s, ctypes.c_float), _ptr(out)) != 0:
         raise RuntimeError("oracle_dequant_cols_e4m3 failed")
     return out
+
+
+def mx_scale_exp(amax: float) -> int:
+    """Scale exponent of an MX-style e4m3 block whose largest magnitude is amax."""
+    return int(_load().oracle_mx_scale_exp(float(amax)))
+
+
+def mx_quant_rows_e4m3(x, block: int = 32):
+    """Block-scaled e4m3 of the rows of x [rows, cols]: returns (codes uint8 [rows, cols], exps int32
+    [rows, cols / block]); value = decode(code) * 2^exp of its block."""
+    lib = _load()
+    x = _f64(x)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), np.uint8)
+    exps = np.empty((rows, cols // block), np.int32)
+    rc = lib.oracle_mx_quant_rows_e4m3(rows, cols, int(block), _ptr(x), _ptr(codes, ctypes.c_uint8),
+                                       _ptr(exps, ctypes.c_int32))
+    if rc != 0:
+        raise RuntimeError(f"oracle_mx_quant_rows_e4m3 failed with {rc}")
+    return codes, exps

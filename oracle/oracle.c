@@ -547,3 +547,44 @@ int oracle_cross_entropy_f64(int64_t M, int64_t D, int64_t V, const double* H, c
   ce_ctx c = {D, V, H, W, labels, out_loss, out_lse};
   return for_each_row(M, nthreads, (size_t)V, ce_row, &c);
 }
+
+/* ------------------------------------------------------------------------------------------------ */
+/* block-scaled (MX-style) e4m3 quantisation of rows                                                */
+/*
+ * A variant of the e4m3 path in which the second product's A operand carries one power-of-two scale per 32
+ * consecutive values of a row instead of one scale per row, so that the first product's epilogue can
+ * quantise its own tile with no cross-tile amax (the pages give no quantisation granularity; they name fp8
+ * operands and per-row activation scales among the epilogue's vector loads, section "Five blocks and a Lego
+ * language").  Reading: the scale of a block is 2^e with e the smallest integer such that
+ * amax_block <= 448 * 2^e (so no value needs saturating), e = 0 for an all-zero block, e limited to
+ * [-127, 127] (the range of an 8-bit power-of-two scale); code = e4m3(x / 2^e), rounded to nearest even.
+ */
+int oracle_mx_scale_exp(double amax) {
+  if (!(amax > 0.0)) return 0;
+  if (isinf(amax)) return 127;
+  int e2;
+  const double m = frexp(amax, &e2); /* amax = m 2^e2, 0.5 <= m < 1 */
+  /* amax <= 448 2^e  <=>  m 2^e2 <= 1.75 2^(e + 8)  <=>  e >= e2 - 9 when 2m <= 1.75, else e >= e2 - 8 */
+  int e = (2.0 * m <= 1.75) ? e2 - 9 : e2 - 8;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e;
+}
+
+int oracle_mx_quant_rows_e4m3(int64_t rows, int64_t cols, int64_t block, const double* x, uint8_t* codes,
+                              int32_t* exps) {
+  if (rows < 0 || cols < 0 || block <= 0 || (cols % block) != 0 || !x || !codes || !exps) return -1;
+  const int64_t nb = cols / block;
+  for (int64_t i = 0; i < rows; ++i) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const double* v = x + i * cols + b * block;
+      double amax = 0.0;
+      for (int64_t j = 0; j < block; ++j)
+        if (fabs(v[j]) > amax) amax = fabs(v[j]);
+      const int e = oracle_mx_scale_exp(amax);
+      exps[i * nb + b] = e;
+      for (int64_t j = 0; j < block; ++j) codes[i * cols + b * block + j] = oracle_e4m3_encode(ldexp(v[j], -e));
+    }
+  }
+  return 0;
+}

@@ -93,6 +93,14 @@ int oracle_rope_rows_f64(int64_t M, int64_t N, double* y, int64_t head_dim, int6
 int oracle_cross_entropy_f64(int64_t M, int64_t D, int64_t V, const double* H, const double* W,
                              const int64_t* labels, double* out_loss, double* out_lse, int nthreads);
 
+/* Block-scaled (MX-style) e4m3 (see oracle.c): the scale exponent of a block with largest magnitude amax is the
+ * smallest e with amax <= 448 * 2^e (0 for amax = 0; limited to [-127, 127]). */
+int oracle_mx_scale_exp(double amax);
+/* Quantise x [rows, cols] in blocks of `block` consecutive values of a row: exps[i][b] = the block's scale
+ * exponent, codes[i][j] = e4m3(x[i][j] / 2^exps[i][j / block]).  cols must be a multiple of block. */
+int oracle_mx_quant_rows_e4m3(int64_t rows, int64_t cols, int64_t block, const double* x, uint8_t* codes,
+                              int32_t* exps);
+
 /* silu(x) = x / (1 + exp(-x)) */
 double oracle_silu(double x);
 

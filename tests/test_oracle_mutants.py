@@ -3,7 +3,7 @@
 Each case copies the oracle's C source, plants one plausible mistake (eps outside the square root, a
 dropped residual, a transposed operand, gate and up swapped, r applied twice, gamma dropped, a wrong
 mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent in the fp8
-decoder, seven mistakes in the backward, four in the rotary embedding and five in the cross-entropy), rebuilds it in a temporary directory and runs the pin tests
+decoder, seven mistakes in the backward, four in the rotary embedding, five in the cross-entropy and three in the block-scaled quantiser), rebuilds it in a temporary directory and runs the pin tests
 against it.  Every mutant must fail at least one pin; the unmodified oracle is never touched.
 """
 import os
@@ -71,6 +71,15 @@ MUTANTS_CE = [
 ]
 
 
+# mistakes in the block-scaled quantiser: the scale exponent taken one binade low (values above 448 would
+# saturate), the block boundary shifted, the scale multiplied instead of divided
+MUTANTS_MX = [
+    ("mx_exponent_low", "int e = (2.0 * m <= 1.75) ? e2 - 9 : e2 - 8;", "int e = e2 - 9;"),
+    ("mx_block_shift", "const double* v = x + i * cols + b * block;", "const double* v = x + i * cols + b * block + (b > 0);"),
+    ("mx_scale_multiplied", "oracle_e4m3_encode(ldexp(v[j], -e));", "oracle_e4m3_encode(ldexp(v[j], e));"),
+]
+
+
 def _run_pins(tmp_path, name, before, after, pins):
     src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
     assert before in src, f"mutation site for {name} no longer exists"
@@ -83,6 +92,11 @@ def _run_pins(tmp_path, name, before, after, pins):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, f"mutant {name} was not caught:\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout
+
+
+@pytest.mark.parametrize("name,before,after", MUTANTS_MX, ids=[m[0] for m in MUTANTS_MX])
+def test_mx_pins_catch_planted_mistake(tmp_path, name, before, after):
+    _run_pins(tmp_path, name, before, after, "tests/test_oracle_mx_pins.py")
 
 
 @pytest.mark.parametrize("name,before,after", MUTANTS_CE, ids=[m[0] for m in MUTANTS_CE])
