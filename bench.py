@@ -19,7 +19,7 @@ Besides the headline the line carries:
                 independent), scaled to TFLOP/s
   unfused       the three-kernel baseline timed the same way, and the algorithmic HBM bytes both paths move
   fp8           the same block with e4m3 X / W1 / W2 (per-row and per-column fp32 scales), fused and unfused,
-                timed with HIP events, against the dense fp8 MFMA peak (5 PFLOP/s)
+                and the block-scaled variant, timed with HIP events, against the dense fp8 MFMA peak (5 PFLOP/s)
   backward      the block's backward (dX, dW1, dR, dgamma, dW2 from dz and dh_out; four products of the
                 forward's sizes, 2x its flops), fused and unfused, timed with HIP events
   rope          the 1B MLP-out -> QKV block with a rotary embedding of the q and k heads: in GEMM2's epilogue,
@@ -117,19 +117,29 @@ def time_fp8(dev, n_ev: int, warmup: int, torch, cb) -> dict:
     y = torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)
     ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev, fp8=1)
     wsu = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=1, device=dev, fp8=1)
+    wsm = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev, fp8=2)
     fused = lambda: cb.coda_block_fwd_fp8(*a, wl.eps, wl.epi, h, y, ws)
     unfused = lambda: cb.coda_block_unfused_fp8(*a, wl.eps, wl.epi, h, y, wsu)
+    mx = lambda: cb.coda_block_fwd_fp8_mx(*a, wl.eps, wl.epi, h, y, wsm)
     for _ in range(warmup):
         fused()
         unfused()
+        mx()
     torch.cuda.synchronize()
     f_ms = time_loop(fused, n_ev, torch)
     u_ms = time_loop(unfused, n_ev, torch)
+    m_ms = time_loop(mx, n_ev, torch)
     tf = wl.flops / (f_ms * 1e-3) / 1e12
+    tm = wl.flops / (m_ms * 1e-3) / 1e12
     return {"workload": wl.name, "dtype": "e4m3 operands, fp32 accumulate, bf16 h/y",
             "fused_ms": round(f_ms, 4), "tflops": round(tf, 2),
             "pct_fp8_mfma_peak": round(100 * tf / MFMA_FP8_PEAK_TFLOPS, 2), "unfused_ms": round(u_ms, 4),
-            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4)}
+            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4),
+            "block_scaled": {"what": "second GEMM's A operand quantised in the first GEMM's epilogue, one "
+                                     "power-of-two scale per 32 values; the reduce folded in (2 kernels)",
+                             "fused_ms": round(m_ms, 4), "tflops": round(tm, 2),
+                             "pct_fp8_mfma_peak": round(100 * tm / MFMA_FP8_PEAK_TFLOPS, 2),
+                             "speedup_vs_unfused": round(u_ms / m_ms, 4)}}
 
 
 def time_bwd(wl, X, W1, g, W2, h, ws, n_ev: int, warmup: int, torch, cb) -> dict:

@@ -26,7 +26,7 @@ STATUS = {0: "CODA_OK", 1: "CODA_ERR_INVALID_ARG", 2: "CODA_ERR_UNSUPPORTED", 3:
 # every symbol include/coda.h declares
 EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_workspace_bytes",
            "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused", "coda_block_fwd_fp8",
-           "coda_block_unfused_fp8",
+           "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
            "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_fwd_rope",
            "coda_rope_rows", "coda_ce_workspace_bytes", "coda_ce_fwd", "coda_ce_unfused")
@@ -61,7 +61,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         getattr(lib, name).argtypes = block
         getattr(lib, name).restype = i32
     block8 = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
-    for name in ("coda_block_fwd_fp8", "coda_block_unfused_fp8"):
+    for name in ("coda_block_fwd_fp8", "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx"):
         getattr(lib, name).argtypes = block8
         getattr(lib, name).restype = i32
     lib.coda_gemm1_residual_partial_rms.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
@@ -203,6 +203,14 @@ def coda_block_fwd_fp8(Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps: float, epi_kin
                        stream=None):
     """Fused block with e4m3 operands (dequantised value = code * scale; sx per row, sw1 / sw2 per column)."""
     _block_fp8("coda_block_fwd_fp8", Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, workspace,
+               stream)
+
+
+def coda_block_fwd_fp8_mx(Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps: float, epi_kind: int, out_h, out_y, workspace,
+                          stream=None):
+    """Fused e4m3 block whose second GEMM takes a block-scaled (32 values per power-of-two scale) A operand
+    quantised in the first GEMM's epilogue; workspace from alloc_workspace(..., fp8=2)."""
+    _block_fp8("coda_block_fwd_fp8_mx", Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, workspace,
                stream)
 
 

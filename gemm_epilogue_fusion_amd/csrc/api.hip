@@ -102,6 +102,7 @@ struct Workspace {
   uint8_t* q;     // fp8: the second GEMM's e4m3 A operand [M,D] (fused: h * gamma quantised; unfused: n quantised)
   float* qs;      // fp8: its per-row scale [M]
   float* rs2;     // fp8 fused: the second GEMM's epilogue row scale qs * r [M]
+  uint8_t* mxs;   // fp8 fused, block-scaled: the block scales of q, (D/64) * ceil(M/256)*256 * 2 bytes
 };
 
 size_t ws_part_bytes(int64_t M, int64_t D) { return align256((size_t)(D / 256) * (size_t)M * 4); }
@@ -128,6 +129,9 @@ size_t carve(void* ws, int64_t M, int64_t D, int fp8, int unfused, Workspace* w)
     } else {
       x.n = (uint16_t*)take(ws_mat_bytes(M, D, 2));
     }
+  } else if (fp8 == 2) {  // block-scaled (MX-style) A operand of the second GEMM
+    x.q = (uint8_t*)take(ws_mat_bytes(M, D, 1));
+    x.mxs = (uint8_t*)take(align256((size_t)(D / 64) * (size_t)((M + 255) / 256 * 256) * 2));
   } else if (fp8) {
     x.q = (uint8_t*)take(ws_mat_bytes(M, D, 1));
     x.qs = (float*)take(ws_vec_bytes(M));
@@ -272,8 +276,8 @@ size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int ep
   (void)K1;
   (void)N2;
   (void)epi_kind;
-  if (M < 1 || D < 256 || M > kMaxDim || D > kMaxDim) return 0;
-  return ws_bytes(M, D, fp8 ? 1 : 0, unfused ? 1 : 0);
+  if (M < 1 || D < 256 || M > kMaxDim || D > kMaxDim || fp8 < 0 || fp8 > 2 || (fp8 == 2 && unfused)) return 0;
+  return ws_bytes(M, D, fp8, unfused ? 1 : 0);
 }
 
 size_t coda_workspace_r_offset(int64_t M, int64_t D) { return ws_part_bytes(M, D); }
@@ -406,6 +410,36 @@ int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const f
     return hip_check(coda::launch_gemm2_rowscale_fp8(w.q, (const uint8_t*)W2q, w.rs2, sw2, epi_kind == CODA_EPI_SWIGLU,
                                                      (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
                      "fp8 gemm2_rowscale launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_block_fwd_fp8_mx(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
+                          const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
+                          void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  try {
+    int s = validate_block(Xq, sx, W1q, sw1, R, gamma, W2q, sw2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
+                           workspace_bytes, 2, 0);
+    if (s) return s;
+    hipStream_t st = (hipStream_t)stream;
+    Workspace w;
+    carve(workspace, M, D, 2, 0, &w);
+    if ((s = hip_check(coda::launch_gemm1_res_prms_fp8_mx((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1,
+                                                          (const uint16_t*)R, gamma, (uint16_t*)out_h, w.q, w.mxs,
+                                                          w.part, (int)M, (int)K1, (int)D, st),
+                       "fp8 block-scaled gemm1_res_prms launch")))
+      return s;
+    const bool fold = coda::fold_supported((int)D);
+    if (!fold && (s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
+                                "prms_reduce launch")))
+      return s;
+    return hip_check(coda::launch_gemm2_rowscale_fp8_mx(w.q, w.mxs, (const uint8_t*)W2q, sw2, w.r,
+                                                        fold ? w.part : nullptr, eps, w.r,
+                                                        epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M,
+                                                        (int)D, (int)N2, st),
+                     "fp8 block-scaled gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }

@@ -159,8 +159,9 @@ struct NoHook {
   __device__ void operator()() const {}
 };
 
-// hook() runs once, after the first stage has landed (its loads issued before the mainloop have had the
-// first stage's latency to complete); it must issue no memory operation of its own.
+// hook() runs once, after the first stage has landed and every wave has passed the barrier: global loads (or
+// global -> LDS loads) issued before the mainloop have completed by then.  It must issue no global memory
+// operation of its own (the mainloop's wait counts assume its own loads only).
 template <class BCol, class Hook = NoHook>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
                                               const uint16_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
@@ -363,7 +364,11 @@ __device__ __forceinline__ void gemm_mainloop_nt(const uint16_t* __restrict__ A,
 // fp8 (OCP e4m3fn) mainloop: same tile, ring and barrier structure; K advances 64 values (64 bytes) per
 // stage, so the A stage has the bf16 A stage's byte layout (256 rows x 64 B).  The B stage is 64 rows x
 // 256 B (chunk c of row k at slot c ^ 2 (k % 8)) and is read K-contiguous with ds_read_b64_tr_b8.  One
-// v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 block and stage (lane l holds A/B bytes k = 32 (l/32) .. +31).
+// v_mfma_f32_32x32x64_f8f6f4 per 32 x 32 block and stage.  Operand layout of that instruction (measured on the
+// device with per-lane block scales, which expose it): lane l, h = l/32, holds in bytes 0..15 the K values
+// 16h .. 16h+15 and in bytes 16..31 the K values 32+16h .. 32+16h+15 of its row / column; the scale of lane l
+// covers K block h, i.e. K 32h .. 32h+31, half of which sits in each lane half.  Both fragments are gathered
+// in that order, so the block scales line up with 32 consecutive K values.
 //   ds_read_b64_tr_b8: inside each group of 16 lanes, byte e of lane i is byte i%8 of the 8 bytes addressed
 //   by lane 2e + i/8 of the group (verified on the device).
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -378,8 +383,7 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const char* p) {
 }
 
 struct LaneOffs8 {
-  int a;      // A fragment (rows mb*32 add 2 KiB each; the second 16 bytes sit at the next slot)
-  int a2;
+  int a;      // A fragment (rows mb*32 add 2 KiB each; the second 16 bytes sit two chunks on, a ^ 32)
   int b[NB];  // B fragment, n-block nb (read r = 0..3 adds 2 KiB each)
 };
 
@@ -388,14 +392,16 @@ __device__ __forceinline__ void lane_offsets8(int wm, int wn, int lane, LaneOffs
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     // lane j of 16-lane group q points at row k0 + j/2, bytes n0 + 8 (j%2) .. +7; after the transposing
-    // read lane i of the group holds rows k0..k0+7 of column n0 + i
+    // read lane i of the group holds rows k0..k0+7 of column n0 + i.  Lane half h = q/2 reads rows 16h ..
+    // 16h+15 and 32+16h .. 32+16h+15 (four reads of 8 rows, see read_b8)
     const int n0 = wn * (32 * NB) + nb * 32 + 16 * (q & 1);
-    const int krow = 32 * (q >> 1) + (j >> 1);
+    const int krow = 16 * (q >> 1) + (j >> 1);
     o.b[nb] = A_BYTES + b8_off(krow, n0 >> 4) + ((j & 1) << 3);
   }
   const int m = wm * 128 + (lane & 31);
-  o.a = a_off(m, 2 * (lane >> 5));
-  o.a2 = a_off(m, 2 * (lane >> 5) + 1);
+  // lane half h takes chunks h and h + 2 of its row (K 16h.. and 32+16h..); chunk h + 2 = h ^ 2 sits at
+  // a_off(m, h) ^ 32 (the swizzle is an XOR)
+  o.a = a_off(m, lane >> 5);
 }
 
 // Fragment reads: B for both 32-column blocks (four transposing reads each), A for one 32-row block.
@@ -403,29 +409,47 @@ __device__ __forceinline__ void read_b8(const char* st, const LaneOffs8& o, i32x
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const char* p = st + o.b[nb];
-    const i32x2 r0 = lds_read_tr8(p);
-    const i32x2 r1 = lds_read_tr8(p + 8 * 256);
-    const i32x2 r2 = lds_read_tr8(p + 16 * 256);
-    const i32x2 r3 = lds_read_tr8(p + 24 * 256);
+    const i32x2 r0 = lds_read_tr8(p);              // rows 16h + 0..7
+    const i32x2 r1 = lds_read_tr8(p + 8 * 256);    // rows 16h + 8..15
+    const i32x2 r2 = lds_read_tr8(p + 32 * 256);   // rows 32 + 16h + 0..7
+    const i32x2 r3 = lds_read_tr8(p + 40 * 256);   // rows 32 + 16h + 8..15
     b[nb] = (i32x8){r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
   }
 }
 __device__ __forceinline__ i32x8 read_a8(const char* st, const LaneOffs8& o, int mb) {
   const u32x4 lo = *(const u32x4*)(st + o.a + mb * 32 * 64);
-  const u32x4 hi = *(const u32x4*)(st + o.a2 + mb * 32 * 64);
+  const u32x4 hi = *(const u32x4*)(st + (o.a ^ 32) + mb * 32 * 64);
   return (i32x8){(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
 // Row blocks mb0 and mb0+1 times both column blocks.  Operand formats 0 = e4m3 (cbsz for the first operand,
-// blgp for the second); E8M0 block scales 127 = 1.0 (the real scales are applied in the epilogue).
-__device__ __forceinline__ void mma8_rows(const i32x8 (&b)[NB], const i32x8& a0, const i32x8& a1, int mb0,
+// blgp for the second).  E8M0 block scales: the B side always 127 = 1.0 (its per-column scales go to the
+// epilogue); the A side 127 too, or (MX) byte mb of asc: the scale of the 32 K values this lane holds of its
+// row in row block mb.
+template <bool MX, int mb0>
+__device__ __forceinline__ void mma8_rows(const i32x8 (&b)[NB], const i32x8& a0, const i32x8& a1, int asc,
                                           f32x16 (&acc)[4][NB]) {
+  const int s = MX ? asc : 127;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
-    acc[mb0][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[nb], a0, acc[mb0][nb], 0, 0, 0, 127, 0, 127);
+    acc[mb0][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[nb], a0, acc[mb0][nb], 0, 0, 0, 127,
+                                                                   MX ? mb0 : 0, s);
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb)
-    acc[mb0 + 1][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[nb], a1, acc[mb0 + 1][nb], 0, 0, 0, 127, 0, 127);
+    acc[mb0 + 1][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(b[nb], a1, acc[mb0 + 1][nb], 0, 0, 0, 127,
+                                                                       MX ? mb0 + 1 : 0, s);
+}
+
+// MX scales of the A operand, staged per K step next to the ring: MX_STAGE_BYTES per stage, 256 bytes per
+// wave.  In global memory they are laid out so that each wave's 256 bytes for a K step are contiguous and
+// lane l of the wave reads its four row blocks' bytes as one word:
+//   byte (((kt * tiles_m + tm) * 2 + wm) * 64 + 32 h + j) * 4 + mb
+// is the scale of row tm*256 + wm*128 + mb*32 + j, K values 64 kt + 32 h .. +31 (lane l = 32 h + j supplies
+// the scale of that K block of that row in row block mb).
+constexpr int MX_STAGE_BYTES = NWAVES * 256;
+__device__ __forceinline__ int64_t mx_scale_index(int kt, int tiles_m, int m, int h) {
+  const int tm = m >> 8, r = m & 255;
+  return ((((int64_t)kt * tiles_m + tm) * 2 + (r >> 7)) * 64 + 32 * h + (r & 31)) * 4 + ((r >> 5) & 3);
 }
 
 // acc = A[m0:m0+256, :] * B[:, tile columns], e4m3 operands, fp32 accumulation (K % K8_MULTIPLE == 0).
@@ -434,12 +458,16 @@ __device__ __forceinline__ void mma8_rows(const i32x8 (&b)[NB], const i32x8& a0,
 // A step's fragments are split into X = {B blocks, A row blocks 0,1}, double-buffered across steps, and
 // Y = {A row blocks 2,3}: the first half multiplies row blocks 0,1 while Y is read; after the barrier the
 // second half multiplies row blocks 2,3 while the next stage's X is read into the other buffer.
-template <class BCol>
+// MX: asc_g is the A operand's scale array (layout above, tiles_m row tiles) and mx_smem the MX_STAGE_BYTES x
+// NSTAGE staging area; each wave adds one 4-byte-per-lane direct load per stage.  hook() as in gemm_mainloop.
+template <bool MX = false, class BCol, class Hook = NoHook>
 __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A, int64_t lda, int M, int m0,
                                                   const uint8_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
-                                                  char* smem, f32x16 (&acc)[4][NB]) {
+                                                  char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{},
+                                                  const uint8_t* __restrict__ asc_g = nullptr,
+                                                  char* mx_smem = nullptr) {
   constexpr int LPW = 16 / NWAVES;
-  constexpr int PER = 2 * LPW;
+  constexpr int PER = 2 * LPW + (MX ? 1 : 0);
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -451,8 +479,9 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
 
   // direct-load unit q: A rows 16q .. 16q+15 (as the bf16 A stage); B rows 4q .. 4q+3 (lane -> row
   // 4q + lane/16, slot lane%16)
-  const uint8_t* aptr[LPW];
-  const uint8_t* bptr[LPW];
+  // 32-bit byte offsets from the operand bases (every e4m3 operand is below 2^31 bytes): half the registers
+  // of per-lane pointers
+  uint32_t aoff[LPW], boff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int q = LPW * wave + i;
@@ -460,22 +489,34 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     int row = m0 + r;
     row = row < M ? row : M - 1;
-    aptr[i] = A + (int64_t)row * lda + 16 * c;
+    aoff[i] = (uint32_t)((int64_t)row * lda + 16 * c);
     const int kr = 4 * q + (lane >> 4);
     const int cb = (lane & 15) ^ ((kr & 7) << 1);
-    bptr[i] = B + (int64_t)kr * ldb + bcol(cb);
+    boff[i] = (uint32_t)((int64_t)kr * ldb + bcol(cb));
   }
   LaneOffs8 lo;
   lane_offsets8(wm, wn, lane, lo);
   const int nk = K / BK8;
+  // MX: this wave's 256 scale bytes of K step kt start at asc_g + ((kt * tiles_m + tm) * 2 + wm) * 256
+  // (wave-uniform; only the lane's 4-byte offset is per lane)
+  const int tiles_m = (M + BM - 1) / BM;
+  const uint8_t* asc_w = MX ? asc_g + ((int64_t)(m0 >> 8) * 2 + wm) * 256 : nullptr;
+  const int64_t asc_step = (int64_t)tiles_m * 512;
 
   auto issue = [&](int kt, int stage) {
     char* st = smem + stage * STAGE_BYTES;
     const int k0 = kt * BK8;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) g2lds16(aptr[i] + k0, st + (LPW * wave + i) * 1024);
+    for (int i = 0; i < LPW; ++i) g2lds16(A + k0 + aoff[i], st + (LPW * wave + i) * 1024);
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + (int64_t)k0 * ldb, st + A_BYTES + (LPW * wave + i) * 1024);
+    for (int i = 0; i < LPW; ++i) g2lds16(B + (int64_t)k0 * ldb + boff[i], st + A_BYTES + (LPW * wave + i) * 1024);
+    if (MX)
+      __builtin_amdgcn_global_load_lds(asc_w + kt * asc_step + 4 * lane,
+                                       (lds_void*)(mx_smem + stage * MX_STAGE_BYTES + wave * 256), 4, 0, 0);
+  };
+  // MX: lane l's word of the stage: the scales of its four row blocks
+  auto read_asc = [&](int stage) {
+    return MX ? *(const int*)(mx_smem + stage * MX_STAGE_BYTES + wave * 256 + 4 * lane) : 127;
   };
 
   i32x8 xb[2][NB], xa[2][2], ya[2];
@@ -487,9 +528,12 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
     constexpr int WAIT = decltype(wait_c)::value;
     const char* cur = smem + U * STAGE_BYTES;
     if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
+    // MX: this stage's scale word, read first so that the first MFMAs wait for it alone (one register: a
+    // prefetched copy per buffer would not fit)
+    const int sc = read_asc(U);
     ya[0] = read_a8(cur, lo, 2);
     ya[1] = read_a8(cur, lo, 3);
-    mma8_rows(xb[P], xa[P][0], xa[P][1], 0, acc);
+    mma8_rows<MX, 0>(xb[P], xa[P][0], xa[P][1], sc, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -502,7 +546,7 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
       xa[1 - P][0] = read_a8(nxt, lo, 0);
       xa[1 - P][1] = read_a8(nxt, lo, 1);
     }
-    mma8_rows(xb[P], ya[0], ya[1], 2, acc);
+    mma8_rows<MX, 2>(xb[P], ya[0], ya[1], sc, acc);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
@@ -520,6 +564,7 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
 #pragma unroll
   for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
   wait_barrier<2 * PER>();
+  hook();
   read_b8(smem, lo, xb[0]);
   xa[0][0] = read_a8(smem, lo, 0);
   xa[0][1] = read_a8(smem, lo, 1);

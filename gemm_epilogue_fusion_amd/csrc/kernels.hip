@@ -53,6 +53,35 @@ __device__ __forceinline__ void rope_sincos(float pos, float rev, float& c, floa
   s = __builtin_amdgcn_sinf(t);
 }
 
+// ---- e4m3 quantisation ----------------------------------------------------------------------------------
+constexpr float E4M3_MAX = 448.0f;
+
+// Four fp32 values -> four OCP e4m3fn bytes, round to nearest even (v_cvt_pk_fp8_f32; gfx950 uses the OCP
+// encoding).  Values are clamped to +-448 first, so the conversion never sees an out-of-range input.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -E4M3_MAX), E4M3_MAX);
+  b = fminf(fmaxf(b, -E4M3_MAX), E4M3_MAX);
+  c = fminf(fmaxf(c, -E4M3_MAX), E4M3_MAX);
+  d = fminf(fmaxf(d, -E4M3_MAX), E4M3_MAX);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// Power-of-two scale of a block of 32 values (MX-style e4m3): the smallest e with amax <= 448 * 2^e, 0 for
+// amax = 0 (or NaN), limited to [-127, 127].  Exact: with amax = m 2^e2 (0.5 <= m < 1), the test
+// 2m <= 1.75 on the mantissa bits decides between e2 - 9 and e2 - 8.
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const uint32_t u = __float_as_uint(amax);
+  const int ef = (int)((u >> 23) & 0xff);
+  if (ef == 0) return -127;  // below 2^-126: under every scale the 8-bit exponent can hold
+  if (ef == 255) return 127;
+  const int e2 = ef - 126;
+  const int e = (u & 0x7fffffu) <= 0x600000u ? e2 - 9 : e2 - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // silu(x) = x / (1 + exp(-x)) in fp32 with the hardware exp2 and reciprocal (each about 1 ulp; the result
 // is rounded to bf16 afterwards).
 __device__ __forceinline__ float silu_f32(float x) {
@@ -82,41 +111,50 @@ struct GateUpCols {
 //   MODE_ROWSCALE_ROPE: out [M,Nb] = bf16(rope(v)) (bf16 operands; see RopeParams)
 //   MODE_ROWSCALE_SWIGLU: the tile's columns are 128 gate columns [tn*128, +128) and the matching 128 up
 //                   columns [Nb/2 + tn*128, +128); out [M,Nb/2] = bf16(silu(v_gate) * v_up)
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, bool MX = false>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
-    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold) {
-  // row-scale modes of the bf16 second GEMM can fold the partial-RMS reduce in (see RowFold)
-  constexpr bool CAN_FOLD = !FP8 && (MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE);
+    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs) {
+  constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
+  // MX (e4m3 only): K1 (MODE_RES_PRMS) also quantises h * gamma in blocks of 32 columns with power-of-two
+  // scales (codes to out2, scales to mxs); K3 (row-scale modes) reads its A operand's block scales from mxs
+  constexpr bool MX_A = FP8 && MX && ROWSCALE_MODE;
+  // row-scale modes of the second GEMM can fold the partial-RMS reduce in (see RowFold), except the e4m3 path
+  // with per-row A scales, whose reduce kernel also quantises
+  constexpr bool CAN_FOLD = (!FP8 || MX) && ROWSCALE_MODE;
   // the mainloop ring (reused as the output staging area), plus the row-sum exchange of MODE_RES_PRMS or the
-  // folded row scales
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 : CAN_FOLD ? 1024 : 0)];
+  // folded row scales, plus the MX scale stages
+  constexpr int FOLD_LDS = CAN_FOLD ? 1024 + FOLD_MAX_T * BM * 4 : 0;  // row scales, then the partial sums
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 : FOLD_LDS) +
+                                                    (MX_A ? NSTAGE * MX_STAGE_BYTES : 0)];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   int tm, tn;
   tile_coords(tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM;
 
-  // folded reduce: thread t < 256 fetches the partial sums of row m0 + t before the mainloop and forms its
-  // r once the first stage has landed; indexes past T re-read part[T-1] and are not summed
+  // folded reduce: before the mainloop the partial sums of the tile's rows go global -> LDS (4 bytes per lane,
+  // 64 rows per load, rows past M read row M-1), older than every stage load, so the mainloop's first wait
+  // covers them; once the first stage has landed thread t < 256 sums row t's T values in order and forms r
   const bool folding = CAN_FOLD && fold.T > 0;
-  float pv[FOLD_MAX_T];
+  float* fold_r = (float*)(smem + LDS_BYTES);                 // [256] the row scales
+  float* fold_part = (float*)(smem + LDS_BYTES + 1024);       // [T][256] the partial sums
   float rfold = 1.0f;
-  if (CAN_FOLD && folding && threadIdx.x < BM) {
-    const int row = m0 + (int)threadIdx.x < M ? m0 + (int)threadIdx.x : M - 1;
-#pragma unroll
-    for (int i = 0; i < FOLD_MAX_T; ++i) pv[i] = part[(int64_t)(i < fold.T ? i : fold.T - 1) * M + row];
+  if (CAN_FOLD && folding) {
+    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int ln = (int)threadIdx.x & 63;
+    for (int u = wv; u < fold.T * 4; u += NWAVES) {
+      const int tt = u >> 2, r = (u & 3) * 64 + ln;
+      const int row = m0 + r < M ? m0 + r : M - 1;
+      __builtin_amdgcn_global_load_lds(part + (int64_t)tt * M + row, (lds_void*)(fold_part + tt * BM + (u & 3) * 64),
+                                       4, 0, 0);
+    }
   }
   auto fold_hook = [&]() {
     if (CAN_FOLD && folding && threadIdx.x < BM) {
-      // pin the sum here: hoisted above the mainloop's first loads, it would wait out the fetch alone
-#pragma unroll
-      for (int i = 0; i < FOLD_MAX_T; ++i) asm volatile("" : "+v"(pv[i]));
       float s = 0.0f;
-#pragma unroll
-      for (int i = 0; i < FOLD_MAX_T; ++i)
-        if (i < fold.T) s += pv[i];
+      for (int i = 0; i < fold.T; ++i) s += fold_part[i * BM + threadIdx.x];
       rfold = 1.0f / sqrtf(s / fold.D + fold.eps);
     }
   };
@@ -125,10 +163,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   if (FP8) {
     const uint8_t* A8 = (const uint8_t*)A;
     const uint8_t* B8 = (const uint8_t*)B;
+    char* mx_smem = smem + LDS_BYTES + FOLD_LDS;
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop_fp8(A8, K, M, m0, B8, Nb, GateUpCols<16>{(int64_t)tn * 128, Nb / 2}, K, smem, acc);
+      gemm_mainloop_fp8<MX_A>(A8, K, M, m0, B8, Nb, GateUpCols<16>{(int64_t)tn * 128, Nb / 2}, K, smem, acc,
+                              fold_hook, mxs, mx_smem);
     else
-      gemm_mainloop_fp8(A8, K, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc);
+      gemm_mainloop_fp8<MX_A>(A8, K, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
+                              mxs, mx_smem);
   } else {
     const uint16_t* A16 = (const uint16_t*)A;
     const uint16_t* B16 = (const uint16_t*)B;
@@ -158,7 +199,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
 
   // per-row scales of this lane's four rows (rows past M read row M-1; they are never stored)
   float rsv[4];
-  float* fold_r = (float*)(smem + LDS_BYTES);
   if (CAN_FOLD && folding) {
     if (t < BM) {
       fold_r[t] = rfold;
@@ -270,6 +310,57 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
           if (m < M) part[(int64_t)tn * M + m] = ((red[row] + red[256 + row]) + red[512 + row]) + red[768 + row];
         }
       }
+      if (FP8 && MX) {
+        // a = bf16(h) * gamma in fp32 from the h tile still staged in LDS, quantised per 32-column block:
+        // thread t takes block t % 8 of rows t / 8 + 64 p; codes (32 bytes) to out2 = hq [M, Nb], the block's
+        // scale byte e + 127 to mxs (mx_scale_index layout)
+        const int b = t & 7;
+        const int col0 = tn * BN + 32 * b;
+        float g[32];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const f32x4 v = *(const f32x4*)(gamma + col0 + 4 * i);
+          g[4 * i] = v[0];
+          g[4 * i + 1] = v[1];
+          g[4 * i + 2] = v[2];
+          g[4 * i + 3] = v[3];
+        }
+        uint8_t* hq = (uint8_t*)out2;
+        const int tiles_m_k3 = (M + BM - 1) / BM;
+#pragma unroll 1
+        for (int p = 0; p < 4; ++p) {
+          const int r = p * 64 + (t >> 3);
+          const int m = m0 + r;
+          float a[32];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4 w = *(const u32x4*)(smem + tile_off<32>(r, 4 * b + c));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              a[8 * c + 2 * e] = bf16_lo(w[e]) * g[8 * c + 2 * e];
+              a[8 * c + 2 * e + 1] = bf16_hi(w[e]) * g[8 * c + 2 * e + 1];
+            }
+          }
+          float amax = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(a[i]));
+          const int e = mx_scale_exp(amax);
+          const float inv = ldexpf(1.0f, -e);
+          if (m < M) {
+            u32x4 q[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const float* v = a + 16 * h2 + 4 * w;
+                q[h2][w] = pack_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+              }
+            *(u32x4*)(hq + (int64_t)m * Nb + col0) = q[0];
+            *(u32x4*)(hq + (int64_t)m * Nb + col0 + 16) = q[1];
+            mxs[mx_scale_index(col0 >> 6, tiles_m_k3, m, (col0 >> 5) & 1)] = (uint8_t)(e + 127);
+          }
+        }
+      }
     }
   } else if (MODE == MODE_ROWSCALE_ROPE) {
     // a wave's 64 accumulator columns are one head: block 0 holds head columns 0..31, block 1 columns 32..63,
@@ -350,20 +441,6 @@ __global__ __launch_bounds__(256) void prms_reduce_kernel(const float* __restric
   r[i] = 1.0f / sqrtf(s / D + eps);
 }
 
-// ---- e4m3 quantisation ----------------------------------------------------------------------------------
-constexpr float E4M3_MAX = 448.0f;
-
-// Four fp32 values -> four OCP e4m3fn bytes, round to nearest even (v_cvt_pk_fp8_f32; gfx950 uses the OCP
-// encoding).  Values are clamped to +-448 first, so the conversion never sees an out-of-range input.
-__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
-  a = fminf(fmaxf(a, -E4M3_MAX), E4M3_MAX);
-  b = fminf(fmaxf(b, -E4M3_MAX), E4M3_MAX);
-  c = fminf(fmaxf(c, -E4M3_MAX), E4M3_MAX);
-  d = fminf(fmaxf(d, -E4M3_MAX), E4M3_MAX);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
-}
 
 // wave-wide maximum (butterfly over the 64 lanes; every lane ends with the same value)
 __device__ __forceinline__ float wave_max(float v) {
@@ -545,15 +622,16 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* __rest
 
 static int group_m_for(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 
-template <int MODE, bool FP8>
+template <int MODE, bool FP8, bool MX = false>
 static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, const uint16_t* R, const float* rowsc,
                               const float* colsc, uint16_t* out, uint16_t* out2, float* part, int M, int K, int Nb,
-                              hipStream_t stream, RopeParams rope = RopeParams{}, RowFold fold = RowFold{}) {
+                              hipStream_t stream, RopeParams rope = RopeParams{}, RowFold fold = RowFold{},
+                              uint8_t* mxs = nullptr) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   dim3 grid(tiles_m * tiles_n), block(NTHREADS);
-  hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
-                     out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold);
+  hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8, MX>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
+                     out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs);
   return hipGetLastError();
 }
 
@@ -566,6 +644,25 @@ hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const u
                                      const uint16_t* R, uint16_t* H, float* part, int M, int K1, int D,
                                      hipStream_t stream) {
   return launch_gemm<MODE_RES_PRMS, true>(Xq, W1q, nullptr, R, sx, sw1, H, nullptr, part, M, K1, D, stream);
+}
+
+hipError_t launch_gemm1_res_prms_fp8_mx(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
+                                        const uint16_t* R, const float* gamma, uint16_t* H, uint8_t* HQ, uint8_t* HS,
+                                        float* part, int M, int K1, int D, hipStream_t stream) {
+  return launch_gemm<MODE_RES_PRMS, true, true>(Xq, W1q, gamma, R, sx, sw1, H, (uint16_t*)HQ, part, M, K1, D, stream,
+                                                RopeParams{}, RowFold{}, HS);
+}
+
+hipError_t launch_gemm2_rowscale_fp8_mx(const uint8_t* HQ, const uint8_t* HS, const uint8_t* W2q, const float* sw2,
+                                        const float* r_in, const float* part, float eps, float* r_out, int swiglu,
+                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+  const RowFold f = part ? RowFold{D / BN, (float)D, eps, r_out} : RowFold{};
+  if (swiglu)
+    return launch_gemm<MODE_ROWSCALE_SWIGLU, true, true>(HQ, W2q, nullptr, nullptr, part ? nullptr : r_in, sw2, Y,
+                                                         nullptr, (float*)part, M, D, N2, stream, RopeParams{}, f,
+                                                         (uint8_t*)HS);
+  return launch_gemm<MODE_ROWSCALE, true, true>(HQ, W2q, nullptr, nullptr, part ? nullptr : r_in, sw2, Y, nullptr,
+                                                (float*)part, M, D, N2, stream, RopeParams{}, f, (uint8_t*)HS);
 }
 
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream) {

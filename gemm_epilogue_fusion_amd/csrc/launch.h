@@ -41,6 +41,17 @@ hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float*
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
                                      const uint16_t* R, uint16_t* H, float* part, int M, int K1, int D,
                                      hipStream_t stream);
+// MX variant of K1: also HQ = e4m3 codes of a = bf16(H) * gamma in blocks of 32 columns with power-of-two scales
+// (HS: one byte e + 127 per block, laid out as mx_scale_index in gemm_core.h; ceil(M / 256) * 256 rows * D / 32
+// bytes).  D % 256 == 0.
+hipError_t launch_gemm1_res_prms_fp8_mx(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
+                                        const uint16_t* R, const float* gamma, uint16_t* H, uint8_t* HQ, uint8_t* HS,
+                                        float* part, int M, int K1, int D, hipStream_t stream);
+// MX variant of K3: Y = bf16(epi(r * (HQ W2q) * sw2[n])) with HQ's block scales inside the MFMA.  With part
+// non-null the reduce is folded in (D / 256 <= 16; r written to r_out), else the row scale is r_in.
+hipError_t launch_gemm2_rowscale_fp8_mx(const uint8_t* HQ, const uint8_t* HS, const uint8_t* W2q, const float* sw2,
+                                        const float* r_in, const float* part, float eps, float* r_out, int swiglu,
+                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream);
 // K2: r from the partial sums; with a = H * gamma (fp32), HQ = e4m3(a * (1 / sa)) per row, sa = amax|a row| / 448;
 // rs2 = sa * r.
 hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* H,

@@ -78,12 +78,13 @@ const char* coda_status_string(int status);
 /* Detail of the last failure on the calling thread ("" if none).  Valid until the next call. */
 const char* coda_last_error(void);
 
-/* Workspace bytes an entry point needs for these dimensions.
- *   fp8:     0 for the bf16 entry points, 1 for the *_fp8 ones
- *   unfused: 0 for coda_block_fwd*, 1 for coda_block_unfused*
+/* Workspace bytes an entry point needs for these dimensions (0 for invalid arguments).
+ *   fp8:     0 for the bf16 entry points, 1 for the *_fp8 ones, 2 for coda_block_fwd_fp8_mx
+ *   unfused: 0 for coda_block_fwd*, 1 for coda_block_unfused* (fp8 = 2 has no unfused form)
  * Layout (each piece 256-byte aligned): part [D/256][M] fp32 partial sums of squares, r [M] fp32, then
  *   fused:   bf16: hg = h * gamma [M,D] bf16; fp8: the e4m3 quantisation of h * gamma [M,D], its row scales
- *            s_a [M] and s_a * r [M]
+ *            s_a [M] and s_a * r [M]; fp8 = 2: the block-scaled e4m3 codes [M,D] and their power-of-two scales,
+ *            one byte per 32 values ((D/64) * ceil(M/256) * 512 bytes)
  *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]). */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
@@ -127,6 +128,22 @@ int coda_block_unfused_fp8(const void* Xq, const float* sx, const void* W1q, con
                            const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
                            void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
                            size_t workspace_bytes, void* stream);
+
+/* The fused e4m3 block with a block-scaled (MX-style) A operand for the second GEMM, a variant that needs no
+ * cross-tile amax: the first GEMM's epilogue quantises a = bf16(h) * gamma (fp32) itself, in blocks of 32
+ * consecutive columns of a row, each with a power-of-two scale 2^e, e the smallest integer with
+ * amax_block <= 448 * 2^e (e = 0 for an all-zero block; e limited to [-127, 127]), codes e4m3(a / 2^e) rounded to
+ * nearest even; the second GEMM feeds the scales to the scaled MFMA and applies r (the partial-RMS reduce folded
+ * in where D <= 4096) and sw2 in its epilogue:
+ *   y = bf16(epi(r[i] * sw2[n] * sum_k dec(q[i][k]) 2^e(i, k/32) dec(W2q[k][n]))).
+ * Two kernels (three where D > 4096).  The pages fix no quantisation granularity (they list per-row activation
+ * scales among the epilogue's vector loads, section "Five blocks and a Lego language"); this is a variant of
+ * coda_block_fwd_fp8 with the same arguments, outputs, shape rules and errors; workspace:
+ * coda_workspace_bytes(..., fp8 = 2, unfused = 0), which also holds r at coda_workspace_r_offset. */
+int coda_block_fwd_fp8_mx(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
+                          const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
+                          void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* The fused block with a rotary position embedding after the row scale (identity epilogue), for a block that
  * feeds attention (QKV projection).  The write-up lists RoPE among the epilogue-fusable operations (section

@@ -151,7 +151,7 @@ def _call8(lib, a, fn="coda_block_fwd_fp8", sx=BASE + 8 * GB, sw1=BASE + 9 * GB,
                             a["out_h"], a["out_y"], a["M"], a["K1"], a["D"], a["N2"], a["ws"], a["ws_bytes"], None)
 
 
-@pytest.mark.parametrize("fn", ["coda_block_fwd_fp8", "coda_block_unfused_fp8"])
+@pytest.mark.parametrize("fn", ["coda_block_fwd_fp8", "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx"])
 def test_fp8_validation(lib, fn):
     a = _args(M=512, K1=256, D=256, N2=512)
     assert _call8(lib, a, fn, sx=0) == INVALID
@@ -169,6 +169,17 @@ def test_fp8_workspace_bytes(lib):
     base = a(8 * M * 4) + a(M * 4)
     assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 1, 0) == base + a(M * D) + 2 * a(M * 4)
     assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 1, 1) == base + a(M * D * 2) + a(M * D) + a(M * 4)
+    # block-scaled: the codes and one scale byte per 32 values, rows padded to the 256-row tile
+    assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 2, 0) == base + a(M * D) + a(D // 32 * M)
+    assert lib.coda_workspace_bytes(300, 256, 512, 512, 0, 2, 0) == a(2 * 300 * 4) + a(300 * 4) + a(300 * 512) + a(16 * 512)
+    assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 2, 1) == 0   # no unfused block-scaled form
+    assert lib.coda_workspace_bytes(M, 2048, D, 16384, 1, 3, 0) == 0
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_fp8_mx_no_gpu_reports_hip_error(lib):
+    a = _args(M=512, K1=256, D=256, N2=512)
+    assert _call8(lib, a, "coda_block_fwd_fp8_mx") == HIP
 
 
 # ---- backward entry points ----
