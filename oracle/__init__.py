@@ -82,6 +82,8 @@ def _load():
                                              ctypes.c_int]
     lib.oracle_cross_entropy_f64.restype = ctypes.c_int
     lib.oracle_mx_scale_exp.argtypes, lib.oracle_mx_scale_exp.restype = [f], ctypes.c_int
+    lib.oracle_swiglu_bwd_f64.argtypes = [i64, i64, i64, dp, dp, dp, dp, ctypes.c_int]
+    lib.oracle_swiglu_bwd_f64.restype = ctypes.c_int
     lib.oracle_mx_quant_rows_e4m3.argtypes = [i64, i64, i64, dp, ctypes.POINTER(ctypes.c_uint8),
                                               ctypes.POINTER(ctypes.c_int32)]
     lib.oracle_mx_quant_rows_e4m3.restype = ctypes.c_int
@@ -301,3 +303,19 @@ def mx_quant_rows_e4m3(x, block: int = 32):
     if rc != 0:
         raise RuntimeError(f"oracle_mx_quant_rows_e4m3 failed with {rc}")
     return codes, exps
+
+
+def swiglu_bwd(dout, Wd, z, nthreads=0):
+    """dz [M, 2F] of y = silu(g) * u, z = [g | u], given the gradient dout [M,D] of the next product
+    out = y Wd (Wd [F,D]): dy = dout Wd^T, dz = [dy u silu'(g) | dy silu(g)]."""
+    lib = _load()
+    dout, Wd, z = _f64(dout), _f64(Wd), _f64(z)
+    M, D = dout.shape
+    F, Db = Wd.shape
+    if Db != D or z.shape != (M, 2 * F):
+        raise ValueError("oracle: inconsistent shapes")
+    dz = np.empty((M, 2 * F), np.float64)
+    rc = lib.oracle_swiglu_bwd_f64(M, F, D, _ptr(dout), _ptr(Wd), _ptr(z), _ptr(dz), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_swiglu_bwd_f64 failed with {rc}")
+    return dz

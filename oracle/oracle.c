@@ -588,3 +588,33 @@ int oracle_mx_quant_rows_e4m3(int64_t rows, int64_t cols, int64_t block, const d
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------------ */
+/* backward of the SwiGLU epilogue                                                                  */
+/*
+ * The write-up reports the backward of the SwiGLU block among its largest gains (section "Experimental
+ * results") and says a forward epilogue has a backward with the same structure (section "CODA: the treasure
+ * hidden in the epilogue"); it gives no formulas.  What is computed is the chain rule of y = silu(g) * u with
+ * z = [g | u] (the gate and up halves of the second product's output, F columns each):
+ *   dy = dout Wd^T            (dout [M,D], Wd [F,D]: the gradient reaching y through the next product, whose
+ *                             weight maps the F columns of y to D; Wd is stored [in = F, out = D])
+ *   dg = dy * u * silu'(g),   silu'(g) = s (1 + g (1 - s)),  s = 1 / (1 + exp(-g))
+ *   du = dy * silu(g)
+ * and dz = [dg | du] [M, 2F].
+ */
+int oracle_swiglu_bwd_f64(int64_t M, int64_t F, int64_t D, const double* dout, const double* Wd, const double* z,
+                          double* out_dz, int nthreads) {
+  (void)nthreads;
+  if (M < 0 || F <= 0 || D <= 0 || !dout || !Wd || !z || !out_dz) return -1;
+  for (int64_t i = 0; i < M; ++i) {
+    for (int64_t f = 0; f < F; ++f) {
+      double dy = 0.0;
+      for (int64_t d = 0; d < D; ++d) dy += dout[i * D + d] * Wd[f * D + d];
+      const double g = z[i * 2 * F + f], u = z[i * 2 * F + F + f];
+      const double s = 1.0 / (1.0 + exp(-g));
+      out_dz[i * 2 * F + f] = dy * u * s * (1.0 + g * (1.0 - s));
+      out_dz[i * 2 * F + F + f] = dy * g * s;
+    }
+  }
+  return 0;
+}

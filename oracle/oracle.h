@@ -101,6 +101,11 @@ int oracle_mx_scale_exp(double amax);
 int oracle_mx_quant_rows_e4m3(int64_t rows, int64_t cols, int64_t block, const double* x, uint8_t* codes,
                               int32_t* exps);
 
+/* Backward of y = silu(g) * u (see oracle.c): z [M, 2F] = [g | u], dout [M,D], Wd [F,D] (the next product's
+ * weight, stored [in = F, out = D]); dy = dout Wd^T; out_dz [M, 2F] = [dy u silu'(g) | dy silu(g)]. */
+int oracle_swiglu_bwd_f64(int64_t M, int64_t F, int64_t D, const double* dout, const double* Wd, const double* z,
+                          double* out_dz, int nthreads);
+
 /* silu(x) = x / (1 + exp(-x)) */
 double oracle_silu(double x);
 

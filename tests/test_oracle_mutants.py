@@ -3,7 +3,7 @@
 Each case copies the oracle's C source, plants one plausible mistake (eps outside the square root, a
 dropped residual, a transposed operand, gate and up swapped, r applied twice, gamma dropped, a wrong
 mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent in the fp8
-decoder, seven mistakes in the backward, four in the rotary embedding, five in the cross-entropy and three in the block-scaled quantiser), rebuilds it in a temporary directory and runs the pin tests
+decoder, seven mistakes in the backward, four in the rotary embedding, five in the cross-entropy, three in the block-scaled quantiser and three in the SwiGLU backward), rebuilds it in a temporary directory and runs the pin tests
 against it.  Every mutant must fail at least one pin; the unmodified oracle is never touched.
 """
 import os
@@ -80,6 +80,17 @@ MUTANTS_MX = [
 ]
 
 
+# mistakes in the SwiGLU backward: silu' without its correction term, Wd not transposed, gate and up swapped
+# in the up-gradient
+MUTANTS_SWIGLU_BWD = [
+    ("swiglu_bwd_no_correction", "out_dz[i * 2 * F + f] = dy * u * s * (1.0 + g * (1.0 - s));",
+     "out_dz[i * 2 * F + f] = dy * u * s;"),
+    ("swiglu_bwd_wd_untransposed", "for (int64_t d = 0; d < D; ++d) dy += dout[i * D + d] * Wd[f * D + d];",
+     "for (int64_t d = 0; d < D; ++d) dy += dout[i * D + d] * Wd[(d % F) * D + f % D];"),
+    ("swiglu_bwd_up_uses_u", "out_dz[i * 2 * F + F + f] = dy * g * s;", "out_dz[i * 2 * F + F + f] = dy * u * s;"),
+]
+
+
 def _run_pins(tmp_path, name, before, after, pins):
     src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
     assert before in src, f"mutation site for {name} no longer exists"
@@ -92,6 +103,11 @@ def _run_pins(tmp_path, name, before, after, pins):
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, f"mutant {name} was not caught:\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout
+
+
+@pytest.mark.parametrize("name,before,after", MUTANTS_SWIGLU_BWD, ids=[m[0] for m in MUTANTS_SWIGLU_BWD])
+def test_swiglu_bwd_pins_catch_planted_mistake(tmp_path, name, before, after):
+    _run_pins(tmp_path, name, before, after, "tests/test_oracle_swiglu_bwd_pins.py")
 
 
 @pytest.mark.parametrize("name,before,after", MUTANTS_MX, ids=[m[0] for m in MUTANTS_MX])
