@@ -26,6 +26,9 @@ Besides the headline the line carries:
                 against the plain block and the plain block followed by a separate rotation pass
   ce            cross-entropy of the 1B LM head (V = 128256) with the logits reduced in the GEMM's epilogue,
                 against storing bf16 logits and reading them back
+  swiglu        the forward that also stores the SwiGLU pre-activation z (against the plain forward), and the
+                SwiGLU backward at the 1B down-projection shape, fused into the dgrad product's epilogue and
+                unfused (dy stored, then an elementwise pass)
 """
 from __future__ import annotations
 
@@ -232,6 +235,38 @@ def time_ce(dev, n_ev: int, warmup: int, torch, cb) -> dict:
             "speedup_fused_vs_unfused": round(u_ms / f_ms, 4), "hbm_bytes_saved_algorithmic": saved}
 
 
+def time_swiglu(wl, X, W1, R, g, W2, dev, n_ev: int, warmup: int, torch, cb) -> dict:
+    """The SwiGLU pieces of training: the forward that also stores z (against the plain forward), and the
+    SwiGLU backward at the 1B down-projection shape, fused (dy reduced into dz in the epilogue) and unfused."""
+    from gemm_epilogue_fusion_amd.inputs import EPI_SWIGLU, SWIGLU_BWD_WORKLOADS, make_swiglu_bwd_inputs
+
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(wl.M, wl.N2 // 2, dtype=torch.bfloat16, device=dev)
+    z = torch.empty(wl.M, wl.N2, dtype=torch.bfloat16, device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, EPI_SWIGLU, device=dev)
+    plain = lambda: cb.coda_block_fwd(X, W1, R, g, W2, wl.eps, EPI_SWIGLU, h, y, ws)
+    savez = lambda: cb.coda_block_fwd_save_z(X, W1, R, g, W2, wl.eps, h, y, z, ws)
+    bw = SWIGLU_BWD_WORKLOADS["1b_mlp_down_dgrad"]
+    dout, Wd, zz = (t.to(dev) for t in make_swiglu_bwd_inputs(bw))
+    dz = torch.empty(bw.M, 2 * bw.F, dtype=torch.bfloat16, device=dev)
+    wsu = torch.empty(cb.coda_swiglu_bwd_workspace_bytes(bw.M, bw.F, 1), dtype=torch.uint8, device=dev)
+    fused = lambda: cb.coda_swiglu_bwd(dout, Wd, zz, dz)
+    unfused = lambda: cb.coda_swiglu_bwd_unfused(dout, Wd, zz, dz, wsu)
+    for _ in range(warmup):
+        plain()
+        savez()
+        fused()
+        unfused()
+    torch.cuda.synchronize()
+    p_ms, z_ms, f_ms, u_ms = (time_loop(fn, n_ev, torch) for fn in (plain, savez, fused, unfused))
+    return {"forward_save_z": {"workload": wl.name, "ms": round(z_ms, 4), "plain_forward_ms": round(p_ms, 4),
+                               "z_bytes_written": 2 * wl.M * wl.N2},
+            "backward": {"workload": bw.name, "M": bw.M, "D": bw.D, "F": bw.F, "fused_ms": round(f_ms, 4),
+                         "tflops": round(bw.flops / (f_ms * 1e-3) / 1e12, 2), "unfused_ms": round(u_ms, 4),
+                         "speedup_fused_vs_unfused": round(u_ms / f_ms, 4),
+                         "hbm_bytes_saved_algorithmic": 2 * 2 * bw.M * bw.F}}
+
+
 def traffic_record(src_hash: str):
     if not os.path.exists(TRAFFIC_FILE):
         return None
@@ -253,6 +288,7 @@ def main() -> int:
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding block timing")
     ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy timing")
+    ap.add_argument("--no-swiglu", action="store_true", help="skip the SwiGLU forward-with-z / backward timing")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
@@ -371,6 +407,8 @@ def main() -> int:
         line["rope"] = time_rope(dev, n_ev, args.warmup, torch, cb)
     if not args.no_ce:
         line["ce"] = time_ce(dev, n_ev, args.warmup, torch, cb)
+    if not args.no_swiglu and wl.epi == 1:
+        line["swiglu"] = time_swiglu(wl, X, W1, R, g, W2, dev, n_ev, args.warmup, torch, cb)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(line))

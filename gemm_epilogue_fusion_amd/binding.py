@@ -29,7 +29,8 @@ EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_wo
            "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
            "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_fwd_rope",
-           "coda_rope_rows", "coda_ce_workspace_bytes", "coda_ce_fwd", "coda_ce_unfused")
+           "coda_rope_rows", "coda_ce_workspace_bytes", "coda_ce_fwd", "coda_ce_unfused",
+           "coda_block_fwd_save_z", "coda_swiglu_bwd_workspace_bytes", "coda_swiglu_bwd", "coda_swiglu_bwd_unfused")
 
 
 class CodaError(RuntimeError):
@@ -81,6 +82,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.coda_ce_workspace_bytes.argtypes, lib.coda_ce_workspace_bytes.restype = [i64, i64, i32], sz
     for name in ("coda_ce_fwd", "coda_ce_unfused"):
         getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
+        getattr(lib, name).restype = i32
+    lib.coda_block_fwd_save_z.argtypes = [vp, vp, vp, vp, vp, f32, vp, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+    lib.coda_block_fwd_save_z.restype = i32
+    lib.coda_swiglu_bwd_workspace_bytes.argtypes, lib.coda_swiglu_bwd_workspace_bytes.restype = [i64, i64, i32], sz
+    for name in ("coda_swiglu_bwd", "coda_swiglu_bwd_unfused"):
+        getattr(lib, name).argtypes = [vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -329,3 +336,41 @@ def coda_ce_fwd(H, W, labels, out_loss, out_lse, workspace, stream=None):
 def coda_ce_unfused(H, W, labels, out_loss, out_lse, workspace, stream=None):
     """The same through stored bf16 logits (the baseline)."""
     _ce("coda_ce_unfused", H, W, labels, out_loss, out_lse, workspace, stream)
+
+
+def coda_block_fwd_save_z(X, W1, R, gamma, W2, eps: float, out_h, out_y, out_z, workspace, stream=None):
+    """Fused block with the SwiGLU epilogue that also stores the pre-activation z [M, N2] (gate | up)."""
+    M, K1 = X.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    st = load().coda_block_fwd_save_z(
+        _dev(X, "X", torch.bfloat16, (M, K1)), _dev(W1, "W1", torch.bfloat16, (K1, D)),
+        _dev(R, "R", torch.bfloat16, (M, D)), _dev(gamma, "gamma", torch.float32, (D,)),
+        _dev(W2, "W2", torch.bfloat16, (D, N2)), float(eps), _dev(out_h, "out_h", torch.bfloat16, (M, D)),
+        _dev(out_y, "out_y", torch.bfloat16, (M, N2 // 2)), _dev(out_z, "out_z", torch.bfloat16, (M, N2)), M, K1, D, N2,
+        _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream(stream))
+    _check(st, "coda_block_fwd_save_z")
+
+
+def coda_swiglu_bwd_workspace_bytes(M: int, F: int, unfused: int = 0) -> int:
+    return int(load().coda_swiglu_bwd_workspace_bytes(M, F, unfused))
+
+
+def _swiglu_bwd(name, dout, Wd, z, out_dz, workspace, stream):
+    M, D = dout.shape
+    F = Wd.shape[0]
+    ws = _dev(workspace, "workspace", torch.uint8) if workspace is not None else None
+    st = getattr(load(), name)(_dev(dout, "dout", torch.bfloat16, (M, D)), _dev(Wd, "Wd", torch.bfloat16, (F, D)),
+                               _dev(z, "z", torch.bfloat16, (M, 2 * F)), _dev(out_dz, "out_dz", torch.bfloat16, (M, 2 * F)),
+                               M, D, F, ws, workspace.numel() if workspace is not None else 0, _stream(stream))
+    _check(st, name)
+
+
+def coda_swiglu_bwd(dout, Wd, z, out_dz, workspace=None, stream=None):
+    """dz of the SwiGLU epilogue from the gradient of the next product (dy never stored)."""
+    _swiglu_bwd("coda_swiglu_bwd", dout, Wd, z, out_dz, workspace, stream)
+
+
+def coda_swiglu_bwd_unfused(dout, Wd, z, out_dz, workspace, stream=None):
+    """The same through a stored dy (workspace of coda_swiglu_bwd_workspace_bytes(M, F, 1) bytes)."""
+    _swiglu_bwd("coda_swiglu_bwd_unfused", dout, Wd, z, out_dz, workspace, stream)

@@ -711,3 +711,114 @@ int coda_ce_unfused(const void* H, const void* W, const int32_t* labels, float* 
 }
 
 }  // extern "C"
+
+// ---- SwiGLU: the forward that keeps z, and the backward of the SwiGLU epilogue ----
+extern "C" {
+
+int coda_block_fwd_save_z(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                          void* out_h, void* out_y, void* out_z, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    int s = validate_block(X, nullptr, W1, nullptr, R, gamma, W2, nullptr, eps, CODA_EPI_SWIGLU, out_h, out_y, M, K1,
+                           D, N2, workspace, workspace_bytes, 0, 0);
+    if (s) return s;
+    if ((s = check_ptr(out_z, "out_z"))) return s;
+    const Range zr = rng("out_z", out_z, (size_t)(M * N2) * 2);
+    const Range others[8] = {rng("X", X, (size_t)(M * K1) * 2), rng("W1", W1, (size_t)(K1 * D) * 2),
+                             rng("R", R, (size_t)(M * D) * 2),  rng("gamma", gamma, (size_t)D * 4),
+                             rng("W2", W2, (size_t)(D * N2) * 2), rng("out_h", out_h, (size_t)(M * D) * 2),
+                             rng("out_y", out_y, (size_t)(M * (N2 / 2)) * 2),
+                             rng("workspace", workspace, ws_bytes(M, D, 0, 0))};
+    for (int i = 0; i < 8; ++i)
+      if (overlap(zr, others[i])) return fail(CODA_ERR_ALIAS, "out_z overlaps %s", others[i].name);
+    hipStream_t st = (hipStream_t)stream;
+    Workspace w;
+    carve(workspace, M, D, 0, 0, &w);
+    if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
+                                                   gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
+                                                   st),
+                       "gemm1_res_prms launch")))
+      return s;
+    if (coda::fold_supported((int)D))
+      return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r, 1,
+                                                        (uint16_t*)out_y, (int)M, (int)D, (int)N2, st,
+                                                        (uint16_t*)out_z),
+                       "gemm2_rowscale_fold launch");
+    if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
+                       "prms_reduce launch")))
+      return s;
+    return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, 1, (uint16_t*)out_y, (int)M, (int)D,
+                                                 (int)N2, st, (uint16_t*)out_z),
+                     "gemm2_rowscale launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+size_t coda_swiglu_bwd_workspace_bytes(int64_t M, int64_t F, int unfused) {
+  if (M < 1 || F < 1 || M > kMaxDim || F > kMaxDim) return 0;
+  return unfused ? align256((size_t)M * (size_t)F * 2) : 0;
+}
+
+}  // extern "C"
+
+namespace {
+
+int swiglu_bwd(const void* dout, const void* Wd, const void* z, void* out_dz, int64_t M, int64_t D, int64_t F,
+               void* workspace, size_t workspace_bytes, void* stream, int unfused) {
+  try {
+    int s;
+    if ((s = check_ptr(dout, "dout")) || (s = check_ptr(Wd, "Wd")) || (s = check_ptr(z, "z")) ||
+        (s = check_ptr(out_dz, "out_dz")))
+      return s;
+    if (M < 1 || D < 1 || F < 1)
+      return fail(CODA_ERR_INVALID_ARG, "dimensions must be >= 1 (M=%lld D=%lld F=%lld)", (long long)M, (long long)D,
+                  (long long)F);
+    if (M > kMaxDim || D > kMaxDim || F > kMaxDim || M * D > kMaxDim * 2 || F * D > kMaxDim * 2 ||
+        M * F > kMaxDim)
+      return fail(CODA_ERR_UNSUPPORTED, "dimensions too large");
+    if (D % 128) return fail(CODA_ERR_UNSUPPORTED, "D=%lld is not a multiple of 128", (long long)D);
+    if (F % 256) return fail(CODA_ERR_UNSUPPORTED, "F=%lld is not a multiple of 256", (long long)F);
+    const size_t need = coda_swiglu_bwd_workspace_bytes(M, F, unfused);
+    if (need) {
+      if (!workspace) return fail(CODA_ERR_WORKSPACE, "workspace is NULL");
+      if ((uintptr_t)workspace & 255) return fail(CODA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+      if (workspace_bytes < need)
+        return fail(CODA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    }
+    const Range in[3] = {rng("dout", dout, (size_t)(M * D) * 2), rng("Wd", Wd, (size_t)(F * D) * 2),
+                         rng("z", z, (size_t)(M * 2 * F) * 2)};
+    const Range out[2] = {rng("out_dz", out_dz, (size_t)(M * 2 * F) * 2), rng("workspace", workspace, need)};
+    if ((s = check_alias(in, 3, out, need ? 2 : 1, nullptr, nullptr))) return s;
+    hipStream_t st = (hipStream_t)stream;
+    if (!unfused)
+      return hip_check(coda::launch_swiglu_bwd((const uint16_t*)dout, (const uint16_t*)Wd, (const uint16_t*)z,
+                                               (uint16_t*)out_dz, (int)M, (int)D, (int)F, st),
+                       "swiglu_bwd launch");
+    uint16_t* dy = (uint16_t*)workspace;
+    if ((s = hip_check(coda::launch_gemm_nt_store((const uint16_t*)dout, (const uint16_t*)Wd, dy, (int)M, (int)D,
+                                                  (int)F, st),
+                       "swiglu_bwd dy launch")))
+      return s;
+    return hip_check(coda::launch_swiglu_bwd_rows(dy, (const uint16_t*)z, (uint16_t*)out_dz, (int)M, (int)F, st),
+                     "swiglu_bwd rows launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int coda_swiglu_bwd(const void* dout, const void* Wd, const void* z, void* out_dz, int64_t M, int64_t D, int64_t F,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return swiglu_bwd(dout, Wd, z, out_dz, M, D, F, workspace, workspace_bytes, stream, 0);
+}
+
+int coda_swiglu_bwd_unfused(const void* dout, const void* Wd, const void* z, void* out_dz, int64_t M, int64_t D,
+                            int64_t F, void* workspace, size_t workspace_bytes, void* stream) {
+  return swiglu_bwd(dout, Wd, z, out_dz, M, D, F, workspace, workspace_bytes, stream, 1);
+}
+
+}  // extern "C"

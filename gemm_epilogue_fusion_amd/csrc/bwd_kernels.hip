@@ -29,7 +29,8 @@
 
 namespace coda {
 
-enum BwdMode { BWD_P = 0, BWD_P_FROM_MEM = 1, BWD_STORE_BF16 = 2, BWD_F32_ROWSCALE = 3, BWD_F32_TRANS = 4 };
+enum BwdMode { BWD_P = 0, BWD_P_FROM_MEM = 1, BWD_STORE_BF16 = 2, BWD_F32_ROWSCALE = 3, BWD_F32_TRANS = 4,
+               BWD_SWIGLU = 5 };
 
 struct BwdArgs {
   const uint16_t* A;   // [M, K] row-major
@@ -43,7 +44,52 @@ struct BwdArgs {
   float* part2;        // BWD_P*: column partials [ceil(M/256)][Nb]
   int M, K, Nb, group_m;
   int64_t slab;        // BWD_F32_*: split-K partial products go to outf + blockIdx.y * slab (K per split = K)
+                       // BWD_SWIGLU: h = z [M, 2 Nb] (gate | up), out = dz [M, 2 Nb]
 };
+
+// silu(x) = x s(x) and its derivative s(x) (1 + x (1 - s(x))), s the logistic function, in fp32 with the
+// hardware exp2 and reciprocal (each about 1 ulp)
+__device__ __forceinline__ float logistic_f32(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
+// SwiGLU backward of four values: dg = dy u silu'(g), du = dy silu(g)
+__device__ __forceinline__ void swiglu_bwd4(const float (&dy)[4], const float (&g)[4], const float (&u)[4],
+                                            float (&dg)[4], float (&du)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float sg = logistic_f32(g[e]);
+    dg[e] = dy[e] * u[e] * (sg * (1.0f + g[e] * (1.0f - sg)));
+    du[e] = dy[e] * (g[e] * sg);
+  }
+}
+
+// rows r0 .. r0+127 of a bf16 tile of 256 columns between global memory (row stride ld) and LDS (tile_off<32>
+// layout relative to row r0); rows past M read row M-1 and are not written
+__device__ __forceinline__ void load_half_tile(const uint16_t* src, int ld, int m0, int n0, int M, char* dst) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int r0 = wave * 16 + 2 * j;  // 2 rows of 512 bytes per wave instruction
+    const int r = r0 + lane / 32;
+    const int slot = lane % 32;
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    g2lds16(src + (int64_t)m * ld + n0 + 8 * (slot ^ (r & 31)), dst + r0 * 512);
+  }
+}
+__device__ __forceinline__ void store_half_tile(const char* srcl, uint16_t* dst, int ld, int m0, int n0, int M) {
+  const int t = threadIdx.x;
+  const int c = t % 32;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = p * 16 + t / 32;
+    const u32x4 v = *(const u32x4*)(srcl + tile_off<32>(r, c));
+    const int m = m0 + r;
+    if (m < M) *(u32x4*)(dst + (int64_t)m * ld + n0 + 8 * c) = v;
+  }
+}
 
 struct RowsFrom {
   int64_t n0;
@@ -246,6 +292,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
       }
       __syncthreads();
     }
+  } else if (MODE == BWD_SWIGLU) {
+    // the tile is dy for columns n0 .. n0+255 of F = Nb; the gate and up tiles of z come into LDS 128 rows at a
+    // time (gate in the first 64 KiB, up in the second), the waves owning those rows replace them in place by
+    // dg and du, and both go out as whole rows
+    const int ldz = 2 * Nb;
+#pragma unroll 1
+    for (int hh = 0; hh < 2; ++hh) {
+      load_half_tile(args.h, ldz, m0 + 128 * hh, n0, M, smem);
+      load_half_tile(args.h, ldz, m0 + 128 * hh, Nb + n0, M, smem + 65536);
+      wait_barrier<0>();
+      if (wm == hh) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int rr = mb * 32 + (lane & 31);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              char* sg = smem + tile_off<32>(rr, wn * 8 + nb * 4 + gq) + 8 * half;
+              char* su = sg + 65536;
+              const u32x2 gv = *(const u32x2*)sg, uv = *(const u32x2*)su;
+              const float g[4] = {bf16_lo(gv[0]), bf16_hi(gv[0]), bf16_lo(gv[1]), bf16_hi(gv[1])};
+              const float u[4] = {bf16_lo(uv[0]), bf16_hi(uv[0]), bf16_lo(uv[1]), bf16_hi(uv[1])};
+              const float dy[4] = {acc[mb][nb][4 * gq], acc[mb][nb][4 * gq + 1], acc[mb][nb][4 * gq + 2],
+                                   acc[mb][nb][4 * gq + 3]};
+              float dg[4], du[4];
+              swiglu_bwd4(dy, g, u, dg, du);
+              *(u32x2*)sg = (u32x2){pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3])};
+              *(u32x2*)su = (u32x2){pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3])};
+            }
+        }
+      }
+      __syncthreads();
+      store_half_tile(smem, args.out, ldz, m0 + 128 * hh, n0, M);
+      store_half_tile(smem + 65536, args.out, ldz, m0 + 128 * hh, Nb + n0, M);
+      __syncthreads();
+    }
   } else {  // BWD_F32_TRANS: outf [Nb, M] = the tile transposed, fp32, staged 128 tile rows at a time
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -394,6 +477,19 @@ int gemm_ksplit(int M, int N, int K) {
   return s;
 }
 
+hipError_t launch_swiglu_bwd(const uint16_t* dout, const uint16_t* Wd, const uint16_t* z, uint16_t* dz, int M, int D,
+                             int F, hipStream_t stream) {
+  BwdArgs a{};
+  a.A = dout;
+  a.B = Wd;
+  a.h = z;
+  a.out = dz;
+  a.M = M;
+  a.K = D;
+  a.Nb = F;
+  return launch_bwd<BWD_SWIGLU, true>(a, stream);
+}
+
 hipError_t launch_bwd_p(const uint16_t* dz, const uint16_t* W2, const uint16_t* h, const float* r, const float* gamma,
                         uint16_t* G, float* part, float* part2, int M, int D, int N2, hipStream_t stream) {
   BwdArgs a{dz, W2, h, r, gamma, G, nullptr, part, part2, M, N2, D, 0, 0};
@@ -404,6 +500,34 @@ hipError_t launch_bwd_p_from_mem(const uint16_t* P, const uint16_t* h, const flo
                                  float* part, float* part2, int M, int D, hipStream_t stream) {
   BwdArgs a{P, nullptr, h, r, gamma, G, nullptr, part, part2, M, 0, D, 0, 0};
   return launch_bwd<BWD_P_FROM_MEM, false>(a, stream);
+}
+
+// The unfused counterpart of S1's epilogue: one thread per 4 consecutive columns of dy [M,F].
+__global__ __launch_bounds__(256) void swiglu_bwd_rows_kernel(const uint16_t* __restrict__ dy,
+                                                              const uint16_t* __restrict__ z, uint16_t* __restrict__ dz,
+                                                              int M, int F) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 4-column group
+  const int64_t groups = (int64_t)M * (F / 4);
+  if (q >= groups) return;
+  const int64_t m = q / (F / 4), f = 4 * (q % (F / 4));
+  const u32x2 dv = *(const u32x2*)(dy + m * F + f);
+  const u32x2 gv = *(const u32x2*)(z + m * 2 * F + f);
+  const u32x2 uv = *(const u32x2*)(z + m * 2 * F + F + f);
+  const float d[4] = {bf16_lo(dv[0]), bf16_hi(dv[0]), bf16_lo(dv[1]), bf16_hi(dv[1])};
+  const float g[4] = {bf16_lo(gv[0]), bf16_hi(gv[0]), bf16_lo(gv[1]), bf16_hi(gv[1])};
+  const float u[4] = {bf16_lo(uv[0]), bf16_hi(uv[0]), bf16_lo(uv[1]), bf16_hi(uv[1])};
+  float dg[4], du[4];
+  swiglu_bwd4(d, g, u, dg, du);
+  *(u32x2*)(dz + m * 2 * F + f) = (u32x2){pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3])};
+  *(u32x2*)(dz + m * 2 * F + F + f) = (u32x2){pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3])};
+}
+
+hipError_t launch_swiglu_bwd_rows(const uint16_t* dy, const uint16_t* z, uint16_t* dz, int M, int F,
+                                  hipStream_t stream) {
+  const int64_t groups = (int64_t)M * (F / 4);
+  hipLaunchKernelGGL(swiglu_bwd_rows_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, stream, dy, z, dz,
+                     M, F);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_nt_store(const uint16_t* A, const uint16_t* Bt, uint16_t* C, int M, int K, int N,

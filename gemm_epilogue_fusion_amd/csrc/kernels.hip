@@ -428,6 +428,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     }
     __syncthreads();
     store_tile_rows<16>(smem, out, ny, m0, tn * 128, M);
+    if (out2) {
+      // the pre-activation z = [gate | up] (bf16 [M, Nb]) for the backward: the tile's gate columns, then its up
+      // columns, staged side by side once the y tile has left the staging area
+      __syncthreads();
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int r = wm * 128 + mb * 32 + (lane & 31);
+        const float sc = rsv[mb];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const f32x4 cg = colsc ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+          const f32x4 cu = colsc ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+          float g[4], u[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            g[e] = acc[mb][0][4 * gq + e] * sc * cg[e];
+            u[e] = acc[mb][1][4 * gq + e] * sc * cu[e];
+          }
+          *(u32x2*)(smem + tile_off<16>(r, wn * 4 + gq) + 8 * half) = (u32x2){pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
+          *(u32x2*)(smem + 65536 + tile_off<16>(r, wn * 4 + gq) + 8 * half) =
+              (u32x2){pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
+        }
+      }
+      __syncthreads();
+      store_tile_rows<16>(smem, out2, Nb, m0, tn * 128, M);
+      store_tile_rows<16>(smem + 65536, out2, Nb, m0, ny + tn * 128, M);
+    }
   }
 }
 
@@ -680,9 +707,9 @@ hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, floa
 }
 
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
-                                 int M, int D, int N2, hipStream_t stream) {
+                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z) {
   if (swiglu)
-    return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2,
+    return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, r, nullptr, Y, Z, nullptr, M, D, N2,
                                                     stream);
   return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2, stream);
 }
@@ -690,10 +717,11 @@ hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const fl
 int fold_supported(int D) { return D / BN <= FOLD_MAX_T; }
 
 hipError_t launch_gemm2_rowscale_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps, float* r,
-                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
+                                      uint16_t* Z) {
   const RowFold f{D / BN, (float)D, eps, r};
   if (swiglu)
-    return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr,
+    return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, Z,
                                                     (float*)part, M, D, N2, stream, RopeParams{}, f);
   return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr, (float*)part, M, D,
                                            N2, stream, RopeParams{}, f);

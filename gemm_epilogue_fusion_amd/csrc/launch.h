@@ -13,13 +13,15 @@ hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const ui
 // K2: r[m] = 1 / sqrt(sum_t part[t][m] / D + eps).
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream);
 // K3 (r non-null; A = h * gamma) and U3 (r null; A = the normalised rows): Y = bf16(epi(r * (A W2))).
+// Z (SwiGLU only, may be null): also store the pre-activation z = [gate | up] = r (A W2) as bf16 [M, N2].
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
-                                 int M, int D, int N2, hipStream_t stream);
+                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z = nullptr);
 // K2 folded into K3 (D / 256 <= 16, see fold_supported): the row scales come from the partial sums of K1, are
 // formed per workgroup as launch_prms_reduce forms them, and are written to r by the tiles of column 0.
 int fold_supported(int D);
 hipError_t launch_gemm2_rowscale_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps, float* r,
-                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream);
+                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
+                                      uint16_t* Z = nullptr);
 // K3 with a rotary embedding after the row scale (identity epilogue): Y = bf16(rope(r * (A W2))); the first n_rot
 // columns form heads of 64 rotated at position row mod seq_len with frequencies base^(-2i/64).
 hipError_t launch_gemm2_rowscale_rope(const uint16_t* A, const uint16_t* W2, const float* r, int seq_len, int n_rot,
@@ -107,5 +109,15 @@ hipError_t launch_ce_reduce(const float* part_m, const float* part_s, const floa
 // CU: the same from stored bf16 logits Z [M,V] (the unfused baseline).
 hipError_t launch_ce_rows(const uint16_t* Z, const int* labels, int M, int V, float* loss, float* lse,
                           hipStream_t stream);
+
+// ---- backward of the SwiGLU epilogue (bwd_kernels.hip) ----
+// S1: dy = dout Wd^T (dout [M,D], Wd [F,D] read as its own rows; D % 128 == 0, F % 256 == 0) with the SwiGLU
+// backward in the epilogue: dz[:, f] = dy u silu'(g), dz[:, F + f] = dy silu(g), g = z[:, f], u = z[:, F + f];
+// dy is never stored.
+hipError_t launch_swiglu_bwd(const uint16_t* dout, const uint16_t* Wd, const uint16_t* z, uint16_t* dz, int M, int D,
+                             int F, hipStream_t stream);
+// The baseline's second kernel: the same from a stored dy [M,F] bf16.
+hipError_t launch_swiglu_bwd_rows(const uint16_t* dy, const uint16_t* z, uint16_t* dz, int M, int F,
+                                  hipStream_t stream);
 
 }  // namespace coda

@@ -176,3 +176,37 @@ def make_ce_inputs(wl: CeWorkload):
     if wl.ignore_every:
         labels[::wl.ignore_every] = -100
     return H, W, labels
+
+
+# ---- backward of the SwiGLU epilogue ----
+@dataclass(frozen=True)
+class SwigluBwdWorkload:
+    """dz [M, 2F] of y = silu(g) * u from z = [g | u] [M, 2F] and the gradient dout [M, D] of the next product
+    out = y Wd, Wd [F, D] (stored [in = F, out = D])."""
+    name: str
+    M: int
+    D: int
+    F: int
+    z_std: float = 1.0
+    dout_std: float = 1.0
+    w_std: float = 0.02
+    seed: int = 0
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.D * self.F
+
+
+# The 1B MLP (hidden 2048, intermediate 8192): the gradient comes back through the down projection.
+SWIGLU_BWD_WORKLOADS: Dict[str, SwigluBwdWorkload] = {
+    "1b_mlp_down_dgrad": SwigluBwdWorkload("1b_mlp_down_dgrad", M=8192, D=2048, F=8192),
+}
+
+
+def make_swiglu_bwd_inputs(wl: SwigluBwdWorkload):
+    """Draw (dout bf16 [M,D], Wd bf16 [F,D], z bf16 [M,2F]) with idx dout=11, Wd=12, z=13 of the seeding scheme."""
+    s = wl.seed
+    dout = _normal((wl.M, wl.D), wl.dout_std, s, 11).to(torch.bfloat16)
+    Wd = _normal((wl.F, wl.D), wl.w_std, s, 12).to(torch.bfloat16)
+    z = _normal((wl.M, 2 * wl.F), wl.z_std, s, 13).to(torch.bfloat16)
+    return dout, Wd, z

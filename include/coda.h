@@ -238,6 +238,34 @@ int coda_ce_fwd(const void* H, const void* W, const int32_t* labels, float* out_
 int coda_ce_unfused(const void* H, const void* W, const int32_t* labels, float* out_loss, float* out_lse, int64_t M,
                     int64_t D, int64_t V, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The fused block with the SwiGLU epilogue (as coda_block_fwd with CODA_EPI_SWIGLU) that also stores the
+ * pre-activation out_z = [gate | up] = r * (h W2') as bf16 [M, N2], written from GEMM2's epilogue, for the
+ * backward of the SwiGLU (coda_swiglu_bwd).  Arguments, shape rules, workspace and errors as coda_block_fwd;
+ * out_z may not overlap any other buffer. */
+int coda_block_fwd_save_z(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                          void* out_h, void* out_y, void* out_z, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward of the SwiGLU epilogue y = silu(g) * u, z = [g | u] (F = N2/2 columns each), fused into the epilogue
+ * of the product that brings the gradient back to y.  The write-up reports the SwiGLU backward among its
+ * largest gains (section "Experimental results"; section "CODA: the treasure hidden in the epilogue" for the
+ * backward's structure).  Inputs: dout [M,D] bf16, the gradient of out = y Wd; Wd [F,D] bf16, that product's
+ * weight stored [in = F, out = D]; z [M, 2F] bf16 from coda_block_fwd_save_z.  Output: out_dz [M, 2F] bf16,
+ *   dy = dout Wd^T (fp32 accumulation, never stored),
+ *   out_dz[:, f] = bf16(dy u silu'(g)), out_dz[:, F + f] = bf16(dy silu(g)),  silu'(g) = s (1 + g (1 - s)),
+ * s = 1 / (1 + exp(-g)); out_dz is the dz that coda_block_bwd takes.  One kernel on `stream`; no workspace
+ * (coda_swiglu_bwd_workspace_bytes(M, F, 0) = 0; workspace may be NULL).  Shape rules: D a multiple of 128,
+ * F a multiple of 256 (else CODA_ERR_UNSUPPORTED), M >= 1.  out_dz may not overlap an input. */
+size_t coda_swiglu_bwd_workspace_bytes(int64_t M, int64_t F, int unfused);
+
+int coda_swiglu_bwd(const void* dout, const void* Wd, const void* z, void* out_dz, int64_t M, int64_t D, int64_t F,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* The unfused baseline: dy is stored (bf16 [M,F] in the workspace, coda_swiglu_bwd_workspace_bytes(M, F, 1)
+ * bytes) and a second kernel reads it back with z.  Same arguments and outputs (dy rounded to bf16 first). */
+int coda_swiglu_bwd_unfused(const void* dout, const void* Wd, const void* z, void* out_dz, int64_t M, int64_t D,
+                            int64_t F, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -324,3 +324,47 @@ def test_ce_workspace_bytes(lib):
 def test_ce_no_gpu_reports_hip_error(lib):
     assert _ccall(lib) == HIP
     assert _ccall(lib, "coda_ce_unfused", unfused=1) == HIP
+
+
+def _scall(lib, fn="coda_swiglu_bwd", M=300, D=256, F=512, dout=BASE, Wd=BASE + GB, z=BASE + 2 * GB,
+           dz=BASE + 3 * GB, ws=BASE + 4 * GB, ws_bytes=1 << 30):
+    return getattr(lib, fn)(dout, Wd, z, dz, M, D, F, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["coda_swiglu_bwd", "coda_swiglu_bwd_unfused"])
+@pytest.mark.parametrize("case,kw,want", [
+    ("null_dout", dict(dout=0), INVALID),
+    ("misaligned_z", dict(z=BASE + 2 * GB + 8), INVALID),
+    ("M_zero", dict(M=0), INVALID),
+    ("D_not_128", dict(D=192), UNSUPPORTED),
+    ("F_not_256", dict(F=640), UNSUPPORTED),
+    ("dz_on_z", dict(dz=BASE + 2 * GB + 256), ALIAS),
+])
+def test_swiglu_bwd_validation(lib, fn, case, kw, want):
+    assert _scall(lib, fn, **kw) == want, lib.coda_last_error()
+
+
+def test_swiglu_bwd_workspace(lib):
+    assert lib.coda_swiglu_bwd_workspace_bytes(8192, 8192, 0) == 0
+    assert lib.coda_swiglu_bwd_workspace_bytes(8192, 8192, 1) == 8192 * 8192 * 2
+    assert _scall(lib, "coda_swiglu_bwd_unfused", ws=0) == WORKSPACE
+    assert _scall(lib, "coda_swiglu_bwd_unfused", ws_bytes=100) == WORKSPACE
+    assert _scall(lib, "coda_swiglu_bwd_unfused", ws=BASE + 2 * GB) == ALIAS  # workspace on z
+
+
+@pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
+def test_swiglu_bwd_no_gpu_reports_hip_error(lib):
+    assert _scall(lib, "coda_swiglu_bwd", ws=0, ws_bytes=0) == HIP  # the fused form needs no workspace
+    assert _scall(lib, "coda_swiglu_bwd_unfused") == HIP
+
+
+def test_save_z_validation(lib):
+    a = _args(epi=1)
+    z = BASE + 8 * GB
+    call = lambda **o: lib.coda_block_fwd_save_z(a["X"], a["W1"], a["R"], a["gamma"], a["W2"], a["eps"], a["out_h"],
+                                                 a["out_y"], o.get("z", z), a["M"], a["K1"], a["D"], o.get("N2", a["N2"]),
+                                                 a["ws"], a["ws_bytes"], None)
+    assert call(z=0) == INVALID
+    assert call(z=BASE + 16) == ALIAS            # on X
+    assert call(z=BASE + 6 * GB + 64) == ALIAS   # on out_y
+    assert call(N2=384) == UNSUPPORTED

@@ -1,0 +1,102 @@
+"""GPU parity of the SwiGLU pieces of the training path against the fp64 oracle.
+
+- coda_block_fwd_save_z: y bit for bit equal to coda_block_fwd's, and z = r (h W2') against the oracle block
+  with the identity epilogue (its output is exactly that pre-activation), to the block's bf16 bar.
+- coda_swiglu_bwd (dy = dout Wd^T reduced into dz in the epilogue) and coda_swiglu_bwd_unfused (dy stored in
+  bf16, then an elementwise pass) against oracle.swiglu_bwd on the same bf16-valued inputs, to the bf16 bar
+  (normwise 2e-2, MAE 1e-3 of max|o|): one tile, ragged rows over several tiles, wide gates, and the 1B
+  down-projection shape on sampled rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gemm_epilogue_fusion_amd import binding as cb
+from gemm_epilogue_fusion_amd.inputs import (EPI_IDENTITY, EPI_SWIGLU, SWIGLU_BWD_WORKLOADS, SwigluBwdWorkload, Workload,
+                                             make_inputs, make_swiglu_bwd_inputs)
+
+from parity import DeviceInputs, check_y, f64, oracle_rows, run_block, sample_rows
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cb.load()
+
+
+FWD = [
+    Workload("savez_ragged", M=300, K1=512, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=51),
+    Workload("savez_wide_d", M=256, K1=256, D=4352, N2=512, epi=EPI_SWIGLU, eps=1e-5, seed=52),  # D > 4096
+]
+
+
+@pytest.mark.parametrize("wl", FWD, ids=[w.name for w in FWD])
+def test_fwd_save_z(wl):
+    _say(f"[gpu] fwd save z {wl.name}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    _, y_plain, _ = run_block(d)
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((wl.M, wl.N2 // 2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    z = torch.full((wl.M, wl.N2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, EPI_SWIGLU, device="cuda")
+    cb.coda_block_fwd_save_z(d.X, d.W1, d.R, d.gamma, d.W2, wl.eps, h, y, z, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
+    _, _, oz = oracle_rows(make_inputs(wl.with_(epi=EPI_IDENTITY)))
+    check_y(f64(z), oz, what="z")
+
+
+def _run(dout, Wd, z, unfused):
+    M, F = dout.shape[0], Wd.shape[0]
+    dev = "cuda"
+    dz = torch.full((M, 2 * F), float("nan"), dtype=torch.bfloat16, device=dev)
+    ws = None
+    if unfused:
+        ws = torch.full((cb.coda_swiglu_bwd_workspace_bytes(M, F, 1),), 0xFF, dtype=torch.uint8, device=dev)
+    fn = cb.coda_swiglu_bwd_unfused if unfused else cb.coda_swiglu_bwd
+    fn(dout.to(dev), Wd.to(dev), z.to(dev), dz, ws)
+    torch.cuda.synchronize()
+    return f64(dz)
+
+
+BWD = [
+    SwigluBwdWorkload("one_tile", M=64, D=128, F=256, seed=61),
+    SwigluBwdWorkload("ragged", M=300, D=384, F=768, seed=62),
+    SwigluBwdWorkload("wide_gates", M=257, D=256, F=512, z_std=4.0, seed=63),
+]
+
+
+@pytest.mark.parametrize("wl", BWD, ids=[w.name for w in BWD])
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_swiglu_bwd_small(wl, unfused):
+    _say(f"[gpu] swiglu bwd {'unfused' if unfused else 'fused'} {wl}")
+    dout, Wd, z = make_swiglu_bwd_inputs(wl)
+    got = _run(dout, Wd, z, unfused)
+    want = oracle.swiglu_bwd(f64(dout), f64(Wd), f64(z))
+    check_y(got[:, :wl.F], want[:, :wl.F], what="dgate")
+    check_y(got[:, wl.F:], want[:, wl.F:], what="dup")
+
+
+def test_swiglu_bwd_full_size_sampled_rows():
+    wl = SWIGLU_BWD_WORKLOADS["1b_mlp_down_dgrad"]
+    _say(f"[gpu] swiglu bwd full size {wl}")
+    dout, Wd, z = make_swiglu_bwd_inputs(wl)
+    got = _run(dout, Wd, z, False)
+    assert np.all(np.isfinite(got))
+    rows = sample_rows(wl.M, n=24, seed=5)
+    want = oracle.swiglu_bwd(f64(dout[rows]), f64(Wd), f64(z[rows]))
+    check_y(got[rows][:, :wl.F], want[:, :wl.F], what="dgate")
+    check_y(got[rows][:, wl.F:], want[:, wl.F:], what="dup")
