@@ -195,7 +195,8 @@ struct BwdWorkspace {
   uint16_t* dhT;  // [D,M] bf16
   uint16_t* nT;   // [D,M] bf16
   uint16_t* P;    // unfused: P = dz W2^T [M,D] bf16
-  float* slabs;   // split-K partial products of dW1 and dW2 (whichever needs more; none when neither splits)
+  float* slabs;   // split-K partial products of dW1 and dW2 (whichever needs more)
+  uint16_t* W2T;  // W2^T [N2,D] bf16 for the first product; shares its bytes with slabs (used later in the stream)
 };
 
 size_t carve_bwd(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused, BwdWorkspace* w) {
@@ -218,7 +219,12 @@ size_t carve_bwd(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int unf
   const int s1 = coda::gemm_ksplit((int)D, (int)K1, (int)M), s2 = coda::gemm_ksplit((int)D, (int)N2, (int)M);
   const size_t b1 = s1 > 1 ? (size_t)s1 * (size_t)D * (size_t)K1 * 4 : 0;
   const size_t b2 = s2 > 1 ? (size_t)s2 * (size_t)D * (size_t)N2 * 4 : 0;
-  if (b1 || b2) x.slabs = (float*)take(align256(b1 > b2 ? b1 : b2));
+  const size_t bt = (size_t)D * (size_t)N2 * 2;
+  size_t region = b1 > b2 ? b1 : b2;
+  region = region > bt ? region : bt;
+  char* shared = take(align256(region));
+  x.slabs = (float*)shared;
+  x.W2T = (uint16_t*)shared;
   if (w) *w = x;
   return off;
 }
@@ -557,18 +563,22 @@ static int block_bwd(const void* X, const void* W1, const void* h, const float* 
     BwdWorkspace w;
     carve_bwd(workspace, M, K1, D, N2, unfused, &w);
     const uint16_t* hh = (const uint16_t*)h;
+    // the first product reads W2 K-major: transpose it once (a [D,N2] -> [N2,D] pass, HBM-bound) so that the
+    // product runs on the NN mainloop, which fetches whole 512-byte weight rows per stage
+    if ((s = hip_check(coda::launch_transpose_bf16((const uint16_t*)W2, (int)D, (int)N2, w.W2T, st),
+                       "bwd W2 transpose launch")))
+      return s;
     if (unfused) {
       // P = dz W2^T stored, then its row and column statistics in a separate pass
-      if ((s = hip_check(coda::launch_gemm_nt_store((const uint16_t*)dz, (const uint16_t*)W2, w.P, (int)M, (int)N2,
-                                                    (int)D, st),
+      if ((s = hip_check(coda::launch_gemm_nn_store((const uint16_t*)dz, w.W2T, w.P, (int)M, (int)N2, (int)D, st),
                          "bwd P launch")))
         return s;
       if ((s = hip_check(coda::launch_bwd_p_from_mem(w.P, hh, r, gamma, w.G, w.part, w.part2, (int)M, (int)D, st),
                          "bwd P statistics launch")))
         return s;
     } else {
-      if ((s = hip_check(coda::launch_bwd_p((const uint16_t*)dz, (const uint16_t*)W2, hh, r, gamma, w.G, w.part,
-                                            w.part2, (int)M, (int)D, (int)N2, st),
+      if ((s = hip_check(coda::launch_bwd_p_nn((const uint16_t*)dz, w.W2T, hh, r, gamma, w.G, w.part, w.part2,
+                                               (int)M, (int)D, (int)N2, st),
                          "bwd P launch")))
         return s;
     }

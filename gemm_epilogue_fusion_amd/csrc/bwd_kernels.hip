@@ -496,6 +496,39 @@ hipError_t launch_bwd_p(const uint16_t* dz, const uint16_t* W2, const uint16_t* 
   return launch_bwd<BWD_P, true>(a, stream);
 }
 
+// B1 on the NN mainloop: W2T = W2^T [N2, D] is read K-major like any [in,out] weight.
+hipError_t launch_bwd_p_nn(const uint16_t* dz, const uint16_t* W2T, const uint16_t* h, const float* r,
+                           const float* gamma, uint16_t* G, float* part, float* part2, int M, int D, int N2,
+                           hipStream_t stream) {
+  BwdArgs a{dz, W2T, h, r, gamma, G, nullptr, part, part2, M, N2, D, 0, 0};
+  return launch_bwd<BWD_P, false>(a, stream);
+}
+
+hipError_t launch_gemm_nn_store(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int K, int N,
+                                hipStream_t stream) {
+  BwdArgs a{A, B, nullptr, nullptr, nullptr, C, nullptr, nullptr, nullptr, M, K, N, 0, 0};
+  return launch_bwd<BWD_STORE_BF16, false>(a, stream);
+}
+
+// dst [C, R] = src [R, C]^T (bf16), 64 x 64 tiles through LDS (rows of 66 elements: the column reads of the
+// second phase fall in different banks); R and C multiples of 64.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ src, int R, int C,
+                                                             uint16_t* __restrict__ dst) {
+  __shared__ uint16_t tile[64][66];
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = ty; i < 64; i += 4) tile[i][tx] = src[(int64_t)(r0 + i) * C + c0 + tx];
+  __syncthreads();
+#pragma unroll
+  for (int i = ty; i < 64; i += 4) dst[(int64_t)(c0 + i) * R + r0 + tx] = tile[tx][i];
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, uint16_t* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(C / 64, R / 64), dim3(256), 0, stream, src, R, C, dst);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_p_from_mem(const uint16_t* P, const uint16_t* h, const float* r, const float* gamma, uint16_t* G,
                                  float* part, float* part2, int M, int D, hipStream_t stream) {
   BwdArgs a{P, nullptr, h, r, gamma, G, nullptr, part, part2, M, 0, D, 0, 0};

@@ -78,6 +78,15 @@ hipError_t launch_bwd_p(const uint16_t* dz, const uint16_t* W2, const uint16_t* 
 hipError_t launch_bwd_p_from_mem(const uint16_t* P, const uint16_t* h, const float* r, const float* gamma, uint16_t* G,
                                  float* part, float* part2, int M, int D, hipStream_t stream);
 // C [M,N] = bf16(A Bt^T), A [M,K], Bt [N,K].
+// B1 with the NN mainloop on W2T = W2^T [N2, D] (same outputs as launch_bwd_p).
+hipError_t launch_bwd_p_nn(const uint16_t* dz, const uint16_t* W2T, const uint16_t* h, const float* r,
+                           const float* gamma, uint16_t* G, float* part, float* part2, int M, int D, int N2,
+                           hipStream_t stream);
+// C [M,N] = bf16(A [M,K] B [K,N]) on the NN mainloop.
+hipError_t launch_gemm_nn_store(const uint16_t* A, const uint16_t* B, uint16_t* C, int M, int K, int N,
+                                hipStream_t stream);
+// dst [C, R] = src [R, C]^T, bf16; R and C multiples of 64.
+hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, uint16_t* dst, hipStream_t stream);
 hipError_t launch_gemm_nt_store(const uint16_t* A, const uint16_t* Bt, uint16_t* C, int M, int K, int N,
                                 hipStream_t stream);
 // Number of K ranges the fp32 products below split K into (1, 2, 4 or 8): enough workgroups to cover the
