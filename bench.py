@@ -10,7 +10,10 @@ W untimed steps, then K timed steps between two device synchronisations.  Prints
 
 Besides the headline the line carries:
   kernels_ms    each step entry point timed alone (GEMM1, the stand-alone reduce, GEMM2 with a given row
-                scale), the block, and the three step kernels back to back (the block before the fold)
+                scale), the block, the three step kernels back to back (the block before the fold), and as
+                context GEMM2's product alone through torch.matmul (hipBLASLt, no epilogue)
+  block_per_call  the block timed call by call: median, p10 and p90, warm (back to back) and cold (a 512 MiB
+                write before each call pushes the operands out of the 256 MB MALL)
   roofline      the dominant kernel (GEMM2) timed alone with HIP events on the stream it runs on, its
                 algorithmic flops (2 M D N2) per launch divided by the average launch time, against the
                 published bf16 dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3 counter
@@ -84,6 +87,23 @@ def time_loop(fn, n: int, torch) -> float:
     end.record()
     end.synchronize()
     return start.elapsed_time(end) / n
+
+
+def step_distribution(fn, n: int, torch, scrub=None) -> dict:
+    """Per-call ms of fn over n calls, each between its own pair of HIP events: median, p10 and p90.  With
+    scrub, scrub() runs before each call outside its events (a write larger than the 256 MB MALL, so the
+    call starts with its operands out of the cache)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        if scrub is not None:
+            scrub()
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in evs)
+    q = lambda p: round(t[min(n - 1, int(round(p * (n - 1))))], 4)
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "n": n}
 
 
 def cpu_baseline(wl, inp, target_s: float = 15.0) -> dict:
@@ -372,6 +392,21 @@ def main() -> int:
     unf_ms = time_loop(step_unfused, n_ev, torch)
     fused_ev_ms = time_loop(step, n_ev, torch)
 
+    # per-call spread, warm (back to back) and cold (a 512 MiB write between calls evicts the MALL)
+    scrub_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    n_dist = min(100, n_ev)
+    dist = {"warm_ms": step_distribution(step, n_dist, torch),
+            "cold_ms": step_distribution(step, n_dist, torch, scrub=lambda: scrub_buf.fill_(1))}
+    del scrub_buf
+    # context: the GEMM2 product alone through torch.matmul (hipBLASLt), no epilogue
+    mm_out = torch.empty(wl.M, wl.N2, dtype=torch.bfloat16, device=dev)
+    mm = lambda: torch.matmul(hg, W2, out=mm_out)
+    for _ in range(3):
+        mm()
+    torch.cuda.synchronize()
+    mm_ms = time_loop(mm, n_ev, torch)
+    del mm_out
+
     k3_flops = 2 * wl.M * wl.D * wl.N2
     k3_tflops = k3_flops / (k3_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
@@ -393,7 +428,9 @@ def main() -> int:
         "roofline": roofline,
         "kernels_ms": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
                        "gemm2_rowscale": round(k3_ms, 4), "fused_block_events": round(fused_ev_ms, 4),
-                       "three_step_kernels_events": round(three_ms, 4)},
+                       "three_step_kernels_events": round(three_ms, 4),
+                       "torch_matmul_gemm2_product_only": round(mm_ms, 4)},
+        "block_per_call": dist,
         "unfused": {"ms_per_step": round(unf_ms, 4), "tflops": round(wl.flops / (unf_ms * 1e-3) / 1e12, 2),
                     "speedup_fused_vs_unfused": round(unf_ms / fused_ev_ms, 4)},
         "hbm_bytes": {"fused_algorithmic": fb, "unfused_algorithmic": ub, "saved_algorithmic": ub - fb},
