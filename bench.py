@@ -9,15 +9,16 @@ already resident in HBM.
 W untimed steps, then K timed steps between two device synchronisations.  Prints ONE JSON line.
 
 Besides the headline the line carries:
-  kernels_ms    each step entry point timed alone (GEMM1, the stand-alone reduce, GEMM2 with a given row
-                scale), the block, the three step kernels back to back (the block before the fold), and as
-                context GEMM2's product alone through torch.matmul (hipBLASLt, no epilogue)
+  kernels_ms    the block's two kernels timed alone (GEMM1 writing h * gamma in K panels; GEMM2 reading them
+                with the reduce folded in), the block, the row-major step entry points (GEMM1, the stand-alone
+                reduce, GEMM2 with a given row scale) alone and back to back (the block before the fold and the
+                panel layout), and as context GEMM2's product alone through torch.matmul (hipBLASLt, no epilogue)
   block_per_call  the block timed call by call: median, p10 and p90, warm (back to back) and cold (a 512 MiB
                 write before each call pushes the operands out of the 256 MB MALL)
-  roofline      the dominant kernel (GEMM2) timed alone with HIP events on the stream it runs on, its
-                algorithmic flops (2 M D N2) per launch divided by the average launch time, against the
-                published bf16 dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3 counter
-                summary if it was taken on the current kernel sources, else null
+  roofline      the dominant kernel (GEMM2 as the block launches it) timed alone with HIP events on the stream
+                it runs on, its algorithmic flops (2 M D N2) per launch divided by the average launch time,
+                against the published bf16 dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3
+                counter summary if it was taken on the current kernel sources, else null
   cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the same workload (rows are
                 independent), scaled to TFLOP/s
   unfused       the three-kernel baseline timed the same way, and the algorithmic HBM bytes both paths move
@@ -368,20 +369,26 @@ def main() -> int:
         print(json.dumps({"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": ms}))
         return 0
 
-    # per-step kernels timed alone with HIP events (same stream as the launches: torch's current stream)
+    # per-step kernels timed alone with HIP events (same stream as the launches: torch's current stream).
+    # The block's own kernels: K1 writing h * gamma in K panels, and K3 reading them with the reduce folded in
+    # (the dominant kernel).  The row-major step entry points (K1, the reduce kernel, K3) are timed too: the
+    # three back to back are the block before the fold and the panel layout.
     T = wl.D // 256
     part = torch.empty(T, wl.M, dtype=torch.float32, device=dev)
     r = torch.empty(wl.M, dtype=torch.float32, device=dev)
     hg = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+    hgp = torch.empty(wl.D // 32, wl.M, 32, dtype=torch.bfloat16, device=dev)
     n_ev = max(20, args.steps // 2)
+    k1p = lambda: cb.coda_gemm1_residual_partial_rms_panels(X, W1, R, g, h, hgp, part)
+    k3p = lambda: cb.coda_gemm2_rowscale_panels(hgp, W2, part, wl.eps, r, wl.epi, y)
     k1 = lambda: cb.coda_gemm1_residual_partial_rms(X, W1, R, g, h, hg, part)
     k2 = lambda: cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r)
     k3 = lambda: cb.coda_gemm2_rowscale(hg, W2, r, wl.epi, y)
-    for fn in (k1, k2, k3):
+    for fn in (k1p, k3p, k1, k2, k3):
         fn()
     torch.cuda.synchronize()
-    k1_ms, k2_ms, k3_ms = (time_loop(fn, n_ev, torch) for fn in (k1, k2, k3))
-    def three_steps():  # the same fused path with the reduce as its own kernel between the two GEMMs
+    k1p_ms, k3_ms, k1_ms, k2_ms, k3r_ms = (time_loop(fn, n_ev, torch) for fn in (k1p, k3p, k1, k2, k3))
+    def three_steps():  # the row-major steps, with the reduce as its own kernel between the two GEMMs
         k1()
         k2()
         k3()
@@ -414,7 +421,8 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(k3_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(k3_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "kernel": "gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU> (GEMM2 + row scale + SwiGLU)",
+                "kernel": "gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU> as the block launches it (GEMM2 on h * gamma "
+                          "in K panels, partial-RMS reduce folded in, row scale + SwiGLU)",
                 "kernel_ms": round(k3_ms, 4), "algorithmic_flops_per_launch": k3_flops}
 
     fb, ub = algorithmic_bytes(wl, True), algorithmic_bytes(wl, False)
@@ -426,9 +434,11 @@ def main() -> int:
                    "epilogue": "swiglu" if wl.epi else "identity", "eps": wl.eps},
         "pct_bf16_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "roofline": roofline,
-        "kernels_ms": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
-                       "gemm2_rowscale": round(k3_ms, 4), "fused_block_events": round(fused_ev_ms, 4),
-                       "three_step_kernels_events": round(three_ms, 4),
+        "kernels_ms": {"gemm1_res_prms": round(k1p_ms, 4), "gemm2_rowscale_fold": round(k3_ms, 4),
+                       "fused_block_events": round(fused_ev_ms, 4),
+                       "row_major_steps": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
+                                           "gemm2_rowscale": round(k3r_ms, 4),
+                                           "three_back_to_back": round(three_ms, 4)},
                        "torch_matmul_gemm2_product_only": round(mm_ms, 4)},
         "block_per_call": dist,
         "unfused": {"ms_per_step": round(unf_ms, 4), "tflops": round(wl.flops / (unf_ms * 1e-3) / 1e12, 2),

@@ -28,6 +28,7 @@ EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_wo
            "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused", "coda_block_fwd_fp8",
            "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
+           "coda_gemm1_residual_partial_rms_panels", "coda_gemm2_rowscale_panels",
            "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_fwd_rope",
            "coda_rope_rows", "coda_ce_workspace_bytes", "coda_ce_fwd", "coda_ce_unfused",
            "coda_block_fwd_save_z", "coda_swiglu_bwd_workspace_bytes", "coda_swiglu_bwd", "coda_swiglu_bwd_unfused")
@@ -71,6 +72,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.coda_partial_rms_reduce.restype = i32
     lib.coda_gemm2_rowscale.argtypes = [vp, vp, vp, i32, vp, i64, i64, i64, vp]
     lib.coda_gemm2_rowscale.restype = i32
+    lib.coda_gemm1_residual_partial_rms_panels.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.coda_gemm1_residual_partial_rms_panels.restype = i32
+    lib.coda_gemm2_rowscale_panels.argtypes = [vp, vp, vp, f32, vp, i32, vp, i64, i64, i64, vp]
+    lib.coda_gemm2_rowscale_panels.restype = i32
     lib.coda_block_fwd_rope.argtypes = [vp, vp, vp, vp, vp, f32, i64, i64, f32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
     lib.coda_block_fwd_rope.restype = i32
     lib.coda_rope_rows.argtypes, lib.coda_rope_rows.restype = [vp, i64, i64, i64, i64, f32, vp], i32
@@ -257,6 +262,34 @@ def coda_gemm2_rowscale(hg, W2, r, epi_kind: int, out_y, stream=None):
         _dev(r, "r", torch.float32, (M,)), int(epi_kind), _dev(out_y, "out_y", torch.bfloat16, (M, ny)),
         M, D, N2, _stream(stream))
     _check(st, "coda_gemm2_rowscale")
+
+
+def coda_gemm1_residual_partial_rms_panels(X, W1, R, gamma, out_h, out_hg_panels, part, stream=None):
+    """Step 1 with hg written in K panels: out_hg_panels [D/32, M, 32] holds hg[m, 32 p + j] at [p, m, j]."""
+    M, K1 = X.shape
+    D = W1.shape[1]
+    st = load().coda_gemm1_residual_partial_rms_panels(
+        _dev(X, "X", torch.bfloat16, (M, K1)), _dev(W1, "W1", torch.bfloat16, (K1, D)),
+        _dev(R, "R", torch.bfloat16, (M, D)), _dev(gamma, "gamma", torch.float32, (D,)),
+        _dev(out_h, "out_h", torch.bfloat16, (M, D)),
+        _dev(out_hg_panels, "out_hg_panels", torch.bfloat16, (D // 32, M, 32)),
+        _dev(part, "part", torch.float32, (D // 256, M)), M, K1, D, _stream(stream))
+    _check(st, "coda_gemm1_residual_partial_rms_panels")
+
+
+def coda_gemm2_rowscale_panels(hg_panels, W2, part, eps: float, r, epi_kind: int, out_y, stream=None):
+    """Step 3 on hg in K panels [D/32, M, 32].  With part [D/256, M] the reduce is folded in and r [M] is
+    written; with part None r is read (eps unused)."""
+    P, M, _ = hg_panels.shape
+    D = 32 * P
+    N2 = W2.shape[1]
+    ny = N2 if epi_kind == EPI_IDENTITY else N2 // 2
+    st = load().coda_gemm2_rowscale_panels(
+        _dev(hg_panels, "hg_panels", torch.bfloat16, (P, M, 32)), _dev(W2, "W2", torch.bfloat16, (D, N2)),
+        None if part is None else _dev(part, "part", torch.float32, (D // 256, M)), float(eps),
+        _dev(r, "r", torch.float32, (M,)), int(epi_kind), _dev(out_y, "out_y", torch.bfloat16, (M, ny)),
+        M, D, N2, _stream(stream))
+    _check(st, "coda_gemm2_rowscale_panels")
 
 
 def workspace_r(workspace: torch.Tensor, M: int, D: int) -> torch.Tensor:

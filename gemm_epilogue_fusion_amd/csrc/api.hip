@@ -37,6 +37,11 @@ int hip_check(hipError_t e, const char* what) {
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every row index and per-matrix element count in range
 
+// The fused paths keep the second GEMM's A operand (h * gamma, or its e4m3 codes) in the workspace as K panels
+// of the mainloop's stage width: it is private to the block, and whole-line direct loads shorten GEMM2 (see
+// ALayout in gemm_core.h).  The step entry points, whose tensors the caller sees, stay row-major.
+constexpr int kPanels = 1;
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Range {
@@ -300,19 +305,19 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
     carve(workspace, M, D, 0, 0, &w);
     if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
                                                    gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
-                                                   st),
+                                                   st, kPanels),
                        "gemm1_res_prms launch")))
       return s;
     if (coda::fold_supported((int)D))  // the reduce runs inside K3's workgroups
       return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
                                                         epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M,
-                                                        (int)D, (int)N2, st),
+                                                        (int)D, (int)N2, st, nullptr, kPanels),
                        "gemm2_rowscale_fold launch");
     if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                        "prms_reduce launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, epi_kind == CODA_EPI_SWIGLU,
-                                                 (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                                                 (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, nullptr, kPanels),
                      "gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -332,19 +337,21 @@ int coda_block_fwd_rope(const void* X, const void* W1, const void* R, const floa
     carve(workspace, M, D, 0, 0, &w);
     if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
                                                    gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
-                                                   st),
+                                                   st, kPanels),
                        "gemm1_res_prms launch")))
       return s;
     if (coda::fold_supported((int)D))
       return hip_check(coda::launch_gemm2_rowscale_rope_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
                                                              (int)seq_len, (int)n_rope_cols, rope_base,
-                                                             (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                                                             (uint16_t*)out_y, (int)M, (int)D, (int)N2, st,
+                                                             kPanels),
                        "gemm2_rowscale_rope_fold launch");
     if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                        "prms_reduce launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale_rope(w.hg, (const uint16_t*)W2, w.r, (int)seq_len, (int)n_rope_cols,
-                                                      rope_base, (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                                                      rope_base, (uint16_t*)out_y, (int)M, (int)D, (int)N2, st,
+                                                      kPanels),
                      "gemm2_rowscale_rope launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -410,11 +417,12 @@ int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const f
                        "fp8 gemm1_res_prms launch")))
       return s;
     if ((s = hip_check(coda::launch_prms_reduce_quant(w.part, (int)(D / 256), (int)M, (int)D, eps,
-                                                      (const uint16_t*)out_h, gamma, w.q, w.r, w.qs, w.rs2, st),
+                                                      (const uint16_t*)out_h, gamma, w.q, w.r, w.qs, w.rs2, st,
+                                                      kPanels),
                        "prms_reduce_quant launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale_fp8(w.q, (const uint8_t*)W2q, w.rs2, sw2, epi_kind == CODA_EPI_SWIGLU,
-                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, kPanels),
                      "fp8 gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -434,7 +442,7 @@ int coda_block_fwd_fp8_mx(const void* Xq, const float* sx, const void* W1q, cons
     carve(workspace, M, D, 2, 0, &w);
     if ((s = hip_check(coda::launch_gemm1_res_prms_fp8_mx((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1,
                                                           (const uint16_t*)R, gamma, (uint16_t*)out_h, w.q, w.mxs,
-                                                          w.part, (int)M, (int)K1, (int)D, st),
+                                                          w.part, (int)M, (int)K1, (int)D, st, kPanels),
                        "fp8 block-scaled gemm1_res_prms launch")))
       return s;
     const bool fold = coda::fold_supported((int)D);
@@ -444,7 +452,7 @@ int coda_block_fwd_fp8_mx(const void* Xq, const float* sx, const void* W1q, cons
     return hip_check(coda::launch_gemm2_rowscale_fp8_mx(w.q, w.mxs, (const uint8_t*)W2q, sw2, w.r,
                                                         fold ? w.part : nullptr, eps, w.r,
                                                         epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M,
-                                                        (int)D, (int)N2, st),
+                                                        (int)D, (int)N2, st, kPanels),
                      "fp8 block-scaled gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -536,6 +544,67 @@ int coda_gemm2_rowscale(const void* hg, const void* W2, const float* r, int epi_
     return hip_check(coda::launch_gemm2_rowscale((const uint16_t*)hg, (const uint16_t*)W2, r,
                                                  epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
                                                  (int)N2, (hipStream_t)stream),
+                     "gemm2_rowscale launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_gemm1_residual_partial_rms_panels(const void* X, const void* W1, const void* R, const float* gamma,
+                                           void* out_h, void* out_hg, float* part, int64_t M, int64_t K1, int64_t D,
+                                           void* stream) {
+  try {
+    int s;
+    if ((s = check_ptr(X, "X")) || (s = check_ptr(W1, "W1")) || (s = check_ptr(R, "R")) ||
+        (s = check_ptr(gamma, "gamma")) || (s = check_ptr(out_h, "out_h")) || (s = check_ptr(out_hg, "out_hg")) ||
+        (s = check_ptr(part, "part")))
+      return s;
+    if ((s = check_dims(M, K1, D, 256))) return s;
+    const Range in[4] = {rng("X", X, (size_t)(M * K1 * 2)), rng("W1", W1, (size_t)(K1 * D * 2)),
+                         rng("R", R, (size_t)(M * D * 2)), rng("gamma", gamma, (size_t)D * 4)};
+    const Range out[3] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("out_hg", out_hg, (size_t)(M * D * 2)),
+                          rng("part", part, (size_t)(D / 256 * M * 4))};
+    if ((s = check_alias(in, 4, out, 3, out_h, R))) return s;
+    return hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R, gamma,
+                                                 (uint16_t*)out_h, (uint16_t*)out_hg, part, (int)M, (int)K1, (int)D,
+                                                 (hipStream_t)stream, kPanels),
+                     "gemm1_res_prms launch");
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_gemm2_rowscale_panels(const void* hg, const void* W2, const float* part, float eps, float* r, int epi_kind,
+                               void* out_y, int64_t M, int64_t D, int64_t N2, void* stream) {
+  try {
+    int s;
+    if ((s = check_ptr(hg, "hg")) || (s = check_ptr(W2, "W2")) || (s = check_ptr(r, "r")) ||
+        (s = check_ptr(out_y, "out_y")))
+      return s;
+    if (part && (s = check_ptr(part, "part"))) return s;
+    if ((s = check_dims(M, 128, D, N2))) return s;
+    if ((s = check_epi_eps(epi_kind, part ? eps : 0.0f))) return s;
+    if (part && !coda::fold_supported((int)D))
+      return fail(CODA_ERR_UNSUPPORTED, "the folded reduce takes D <= 4096 (D = %lld)", (long long)D);
+    const int64_t ny = epi_kind == CODA_EPI_SWIGLU ? N2 / 2 : N2;
+    const bool sw = epi_kind == CODA_EPI_SWIGLU;
+    const hipStream_t st = (hipStream_t)stream;
+    if (part) {
+      const Range in[3] = {rng("hg", hg, (size_t)(M * D * 2)), rng("W2", W2, (size_t)(D * N2 * 2)),
+                           rng("part", part, (size_t)(D / 256 * M * 4))};
+      const Range out[2] = {rng("out_y", out_y, (size_t)(M * ny * 2)), rng("r", r, (size_t)M * 4)};
+      if ((s = check_alias(in, 3, out, 2, nullptr, nullptr))) return s;
+      return hip_check(coda::launch_gemm2_rowscale_fold((const uint16_t*)hg, (const uint16_t*)W2, part, eps, r, sw,
+                                                        (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, nullptr,
+                                                        kPanels),
+                       "gemm2_rowscale_fold launch");
+    }
+    const Range in[3] = {rng("hg", hg, (size_t)(M * D * 2)), rng("W2", W2, (size_t)(D * N2 * 2)),
+                         rng("r", r, (size_t)M * 4)};
+    const Range out[1] = {rng("out_y", out_y, (size_t)(M * ny * 2))};
+    if ((s = check_alias(in, 3, out, 1, nullptr, nullptr))) return s;
+    return hip_check(coda::launch_gemm2_rowscale((const uint16_t*)hg, (const uint16_t*)W2, r, sw, (uint16_t*)out_y,
+                                                 (int)M, (int)D, (int)N2, st, nullptr, kPanels),
                      "gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -746,19 +815,19 @@ int coda_block_fwd_save_z(const void* X, const void* W1, const void* R, const fl
     carve(workspace, M, D, 0, 0, &w);
     if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
                                                    gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
-                                                   st),
+                                                   st, kPanels),
                        "gemm1_res_prms launch")))
       return s;
     if (coda::fold_supported((int)D))
       return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r, 1,
                                                         (uint16_t*)out_y, (int)M, (int)D, (int)N2, st,
-                                                        (uint16_t*)out_z),
+                                                        (uint16_t*)out_z, kPanels),
                        "gemm2_rowscale_fold launch");
     if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                        "prms_reduce launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, 1, (uint16_t*)out_y, (int)M, (int)D,
-                                                 (int)N2, st, (uint16_t*)out_z),
+                                                 (int)N2, st, (uint16_t*)out_z, kPanels),
                      "gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");

@@ -144,7 +144,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
     // split K: workgroup row blockIdx.y multiplies K range [y K, (y + 1) K) of the gridDim.y K ranges
     const int64_t k0 = (int64_t)blockIdx.y * args.K;
     const int64_t lda = (int64_t)args.K * gridDim.y;
-    gemm_mainloop(args.A + k0, lda, M, m0, args.B + k0 * Nb, Nb, ContiguousCols<8>{n0}, args.K, smem, acc);
+    gemm_mainloop(args.A + k0, ALayout{lda, BK}, M, m0, args.B + k0 * Nb, Nb, ContiguousCols<8>{n0}, args.K, smem,
+                  acc);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)

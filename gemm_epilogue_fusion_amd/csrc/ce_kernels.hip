@@ -65,7 +65,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_gemm_kernel(const uint16_t* __
   }
 
   f32x16 acc[4][NB];
-  gemm_mainloop(H, K, M, m0, W, V, ContiguousCols<8>{(int64_t)n0}, K, smem, acc);
+  gemm_mainloop(H, ALayout{K, BK}, M, m0, W, V, ContiguousCols<8>{(int64_t)n0}, K, smem, acc);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll

@@ -151,8 +151,19 @@ __device__ __forceinline__ void interleave_mma_reads() {
   }
 }
 
+// Where the A operand's K steps live.  Element (m, k) of A sits at m * row + (k / S) * step + k % S, S being
+// the mainloop's K per stage (32 bf16 values, 64 e4m3 bytes).  Row-major A [M,K] has row = its row stride and
+// step = S.  A written in K panels [K / S][M][S] has row = S and step = M * S: then a stage's A tile (256 rows
+// of one panel) is one contiguous block and every direct load covers whole 128-byte cache lines, where the
+// row-major tile's 64-byte row pieces each take a line of their own through the L1 (measured: 5-8% off the
+// product's time at the 1B GEMM2 shape).
+struct ALayout {
+  int64_t row;
+  int64_t step;
+};
+
 // The mainloop: acc = A[m0:m0+256, :] * B[:, tile columns] over the full K (K % K_MULTIPLE == 0).
-//   A: [M,K] bf16, row stride lda; rows >= M are read as row M-1 (their results are never stored).
+//   A: [M,K] bf16 laid out as `al` says; rows >= M are read as row M-1 (their results are never stored).
 //   B: [K,*] bf16, row stride ldb.  bcol(c) gives the global column of the tile's 8-column chunk c
 //      (0..31), which lets a tile gather column segments (the gate | up halves of SwiGLU).
 struct NoHook {
@@ -163,7 +174,7 @@ struct NoHook {
 // global -> LDS loads) issued before the mainloop have completed by then.  It must issue no global memory
 // operation of its own (the mainloop's wait counts assume its own loads only).
 template <class BCol, class Hook = NoHook>
-__device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
+__device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, ALayout al, int M, int m0,
                                               const uint16_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
                                               char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{}) {
   constexpr int LPW = 16 / NWAVES;              // 1 KiB direct loads per wave per operand per stage
@@ -189,7 +200,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     int row = m0 + r;
     row = row < M ? row : M - 1;
-    aptr[i] = A + (int64_t)row * lda + 8 * c;
+    aptr[i] = A + (int64_t)row * al.row + 8 * c;
     const int kr = 2 * q + (lane >> 5);
     const int cb = (lane & 31) ^ ((kr & 3) << 2);
     bptr[i] = B + (int64_t)kr * ldb + bcol(cb);
@@ -202,7 +213,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, in
     char* st = smem + stage * STAGE_BYTES;
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) g2lds16(aptr[i] + k0, st + (LPW * wave + i) * 1024);
+    for (int i = 0; i < LPW; ++i) g2lds16(aptr[i] + (int64_t)kt * al.step, st + (LPW * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + (int64_t)k0 * ldb, st + A_BYTES + (LPW * wave + i) * 1024);
   };
@@ -453,7 +464,7 @@ __device__ __forceinline__ int64_t mx_scale_index(int kt, int tiles_m, int m, in
 }
 
 // acc = A[m0:m0+256, :] * B[:, tile columns], e4m3 operands, fp32 accumulation (K % K8_MULTIPLE == 0).
-//   A: [M,K] bytes, row stride lda bytes; B: [K,*] bytes, row stride ldb bytes; bcol(c) = global column of
+//   A: [M,K] bytes laid out as `al` says (S = 64); B: [K,*] bytes, row stride ldb bytes; bcol(c) = global column of
 //   the tile's 16-column chunk c (0..15).
 // A step's fragments are split into X = {B blocks, A row blocks 0,1}, double-buffered across steps, and
 // Y = {A row blocks 2,3}: the first half multiplies row blocks 0,1 while Y is read; after the barrier the
@@ -461,7 +472,7 @@ __device__ __forceinline__ int64_t mx_scale_index(int kt, int tiles_m, int m, in
 // MX: asc_g is the A operand's scale array (layout above, tiles_m row tiles) and mx_smem the MX_STAGE_BYTES x
 // NSTAGE staging area; each wave adds one 4-byte-per-lane direct load per stage.  hook() as in gemm_mainloop.
 template <bool MX = false, class BCol, class Hook = NoHook>
-__device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A, int64_t lda, int M, int m0,
+__device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A, ALayout al, int M, int m0,
                                                   const uint8_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
                                                   char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{},
                                                   const uint8_t* __restrict__ asc_g = nullptr,
@@ -489,11 +500,12 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     int row = m0 + r;
     row = row < M ? row : M - 1;
-    aoff[i] = (uint32_t)((int64_t)row * lda + 16 * c);
+    aoff[i] = (uint32_t)((int64_t)row * al.row + 16 * c);
     const int kr = 4 * q + (lane >> 4);
     const int cb = (lane & 15) ^ ((kr & 7) << 1);
     boff[i] = (uint32_t)((int64_t)kr * ldb + bcol(cb));
   }
+  const uint32_t astep = (uint32_t)al.step;  // bytes per K step of A (below 2^31 as A is)
   LaneOffs8 lo;
   lane_offsets8(wm, wn, lane, lo);
   const int nk = K / BK8;
@@ -506,8 +518,9 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
   auto issue = [&](int kt, int stage) {
     char* st = smem + stage * STAGE_BYTES;
     const int k0 = kt * BK8;
+    const uint32_t ak = (uint32_t)kt * astep;  // wave-uniform
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) g2lds16(A + k0 + aoff[i], st + (LPW * wave + i) * 1024);
+    for (int i = 0; i < LPW; ++i) g2lds16(A + ak + aoff[i], st + (LPW * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) g2lds16(B + (int64_t)k0 * ldb + boff[i], st + A_BYTES + (LPW * wave + i) * 1024);
     if (MX)
@@ -611,6 +624,25 @@ __device__ __forceinline__ void store_tile_rows(const char* smem, uint16_t* dst,
     const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, c));
     const int m = m0 + r;
     if (m < M) *(u32x4*)(dst + (int64_t)m * ld + n0 + 8 * c) = v;
+  }
+}
+
+// The staged tile to K panels of 32 columns: column n0 + 32 p + j of row m0 + r goes to
+// dst[(n0 / 32 + p) * panel + (m0 + r) * 32 + j] (panel = rows * 32 elements, the panel stride); rows >= M are
+// skipped.  Each wave writes 1 KiB of one panel per pass (16 rows x 64 bytes, contiguous).
+template <int CH>
+__device__ __forceinline__ void store_tile_panels(const char* smem, uint16_t* dst, int64_t panel, int m0, int n0,
+                                                  int M) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < BM * CH / NTHREADS; ++p) {
+    const int g = p * NTHREADS + t;       // 16-byte chunk of the tile in panel order
+    const int pn = g / (BM * 4);          // panel (4 chunks of 16 bytes per row)
+    const int w = g % (BM * 4);
+    const int r = w >> 2, c4 = w & 3;
+    const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, 4 * pn + c4));
+    const int m = m0 + r;
+    if (m < M) *(u32x4*)(dst + (int64_t)(n0 / 32 + pn) * panel + (int64_t)m * 32 + 8 * c4) = v;
   }
 }
 

@@ -111,11 +111,15 @@ struct GateUpCols {
 //   MODE_ROWSCALE_ROPE: out [M,Nb] = bf16(rope(v)) (bf16 operands; see RopeParams)
 //   MODE_ROWSCALE_SWIGLU: the tile's columns are 128 gate columns [tn*128, +128) and the matching 128 up
 //                   columns [Nb/2 + tn*128, +128); out [M,Nb/2] = bf16(silu(v_gate) * v_up)
+// panels != 0: MODE_RES_PRMS writes out2 (h * gamma, or the MX codes) in K panels of the second GEMM's stage
+// width ([Nb / 32][M][32] bf16, [Nb / 64][M][64] bytes), and the row-scale modes read A from such panels (ALayout
+// in gemm_core.h); A of MODE_RES_PRMS and MODE_STORE is always row-major.
 template <int MODE, bool FP8, bool MX = false>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
-    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs) {
+    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs,
+    int panels) {
   constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
   // MX (e4m3 only): K1 (MODE_RES_PRMS) also quantises h * gamma in blocks of 32 columns with power-of-two
   // scales (codes to out2, scales to mxs); K3 (row-scale modes) reads its A operand's block scales from mxs
@@ -159,24 +163,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     }
   };
 
+  constexpr int KS = FP8 ? BK8 : BK;  // K per stage: the panel width
+  const ALayout al = (ROWSCALE_MODE && panels) ? ALayout{KS, (int64_t)M * KS} : ALayout{K, KS};
   f32x16 acc[4][NB];
   if (FP8) {
     const uint8_t* A8 = (const uint8_t*)A;
     const uint8_t* B8 = (const uint8_t*)B;
     char* mx_smem = smem + LDS_BYTES + FOLD_LDS;
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop_fp8<MX_A>(A8, K, M, m0, B8, Nb, GateUpCols<16>{(int64_t)tn * 128, Nb / 2}, K, smem, acc,
+      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, GateUpCols<16>{(int64_t)tn * 128, Nb / 2}, K, smem, acc,
                               fold_hook, mxs, mx_smem);
     else
-      gemm_mainloop_fp8<MX_A>(A8, K, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
+      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
                               mxs, mx_smem);
   } else {
     const uint16_t* A16 = (const uint16_t*)A;
     const uint16_t* B16 = (const uint16_t*)B;
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop(A16, K, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, K, smem, acc, fold_hook);
+      gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, K, smem, acc, fold_hook);
     else
-      gemm_mainloop(A16, K, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook);
+      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook);
   }
 
   // Materialise the accumulators here: otherwise the compiler may sink the last MFMAs into the epilogue's
@@ -301,7 +307,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         for (int mb = 0; mb < 4; ++mb) red[wn * 256 + wm * 128 + mb * 32 + lane] = ss[mb];
       }
       __syncthreads();
-      if (WRITE_HG) store_tile_rows<32>(smem, out2, Nb, m0, tn * BN, M);
+      if (WRITE_HG) {
+        if (panels)
+          store_tile_panels<32>(smem, out2, (int64_t)M * 32, m0, tn * BN, M);
+        else
+          store_tile_rows<32>(smem, out2, Nb, m0, tn * BN, M);
+      }
       if (wn == 0 && lane < 32) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -355,8 +366,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
                 const float* v = a + 16 * h2 + 4 * w;
                 q[h2][w] = pack_e4m3x4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
               }
-            *(u32x4*)(hq + (int64_t)m * Nb + col0) = q[0];
-            *(u32x4*)(hq + (int64_t)m * Nb + col0 + 16) = q[1];
+            uint8_t* dq = panels ? hq + (int64_t)(col0 >> 6) * M * 64 + (int64_t)m * 64 + (col0 & 63)
+                                 : hq + (int64_t)m * Nb + col0;
+            *(u32x4*)dq = q[0];
+            *(u32x4*)(dq + 16) = q[1];
             mxs[mx_scale_index(col0 >> 6, tiles_m_k3, m, (col0 >> 5) & 1)] = (uint8_t)(e + 127);
           }
         }
@@ -483,13 +496,15 @@ __device__ __forceinline__ float wave_max(float v) {
 //   hq[i][j] = e4m3(a[i][j] * (1 / s_a[i]))               (the second GEMM's A operand; the reciprocal is
 //                                                          rounded to fp32 once per row)
 //   rs2[i]   = s_a[i] * r[i]                               (the second GEMM's epilogue row scale)
+// hq is written row-major, or with panels != 0 in K panels of 64 bytes ([D / 64][M][64]).
 // Each lane keeps up to CACHED 8-column chunks of a[i] in registers between the amax and the quantisation
 // (D <= 4096 reads h and gamma once); wider rows recompute the rest.
 __global__ __launch_bounds__(256) void prms_reduce_quant_kernel(const float* __restrict__ part, int T, int M, int D,
                                                                 float eps, const uint16_t* __restrict__ h,
                                                                 const float* __restrict__ gamma,
                                                                 uint8_t* __restrict__ hq, float* __restrict__ r,
-                                                                float* __restrict__ sa, float* __restrict__ rs2) {
+                                                                float* __restrict__ sa, float* __restrict__ rs2,
+                                                                int panels) {
   constexpr int CACHED = 8;
   const int lane = threadIdx.x & 63;
   const int64_t i = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -537,7 +552,9 @@ __global__ __launch_bounds__(256) void prms_reduce_quant_kernel(const float* __r
     u32x2 o;
     o[0] = pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
     o[1] = pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
-    *(u32x2*)(qrow + 8 * c) = o;
+    // panels: [D / 64][M][64] bytes (the second GEMM's stage width), else row-major
+    uint8_t* dq = panels ? hq + (int64_t)((8 * c) >> 6) * M * 64 + i * 64 + ((8 * c) & 63) : qrow + 8 * c;
+    *(u32x2*)dq = o;
   };
 #pragma unroll
   for (int k = 0; k < CACHED; ++k) {
@@ -653,18 +670,20 @@ template <int MODE, bool FP8, bool MX = false>
 static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, const uint16_t* R, const float* rowsc,
                               const float* colsc, uint16_t* out, uint16_t* out2, float* part, int M, int K, int Nb,
                               hipStream_t stream, RopeParams rope = RopeParams{}, RowFold fold = RowFold{},
-                              uint8_t* mxs = nullptr) {
+                              uint8_t* mxs = nullptr, int panels = 0) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   dim3 grid(tiles_m * tiles_n), block(NTHREADS);
   hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8, MX>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
-                     out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs);
+                     out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, const float* gamma,
-                                 uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream) {
-  return launch_gemm<MODE_RES_PRMS, false>(X, W1, gamma, R, nullptr, nullptr, H, HG, part, M, K1, D, stream);
+                                 uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream,
+                                 int panels) {
+  return launch_gemm<MODE_RES_PRMS, false>(X, W1, gamma, R, nullptr, nullptr, H, HG, part, M, K1, D, stream,
+                                           RopeParams{}, RowFold{}, nullptr, panels);
 }
 
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
@@ -675,21 +694,21 @@ hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const u
 
 hipError_t launch_gemm1_res_prms_fp8_mx(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
                                         const uint16_t* R, const float* gamma, uint16_t* H, uint8_t* HQ, uint8_t* HS,
-                                        float* part, int M, int K1, int D, hipStream_t stream) {
+                                        float* part, int M, int K1, int D, hipStream_t stream, int panels) {
   return launch_gemm<MODE_RES_PRMS, true, true>(Xq, W1q, gamma, R, sx, sw1, H, (uint16_t*)HQ, part, M, K1, D, stream,
-                                                RopeParams{}, RowFold{}, HS);
+                                                RopeParams{}, RowFold{}, HS, panels);
 }
 
 hipError_t launch_gemm2_rowscale_fp8_mx(const uint8_t* HQ, const uint8_t* HS, const uint8_t* W2q, const float* sw2,
                                         const float* r_in, const float* part, float eps, float* r_out, int swiglu,
-                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels) {
   const RowFold f = part ? RowFold{D / BN, (float)D, eps, r_out} : RowFold{};
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, true, true>(HQ, W2q, nullptr, nullptr, part ? nullptr : r_in, sw2, Y,
                                                          nullptr, (float*)part, M, D, N2, stream, RopeParams{}, f,
-                                                         (uint8_t*)HS);
+                                                         (uint8_t*)HS, panels);
   return launch_gemm<MODE_ROWSCALE, true, true>(HQ, W2q, nullptr, nullptr, part ? nullptr : r_in, sw2, Y, nullptr,
-                                                (float*)part, M, D, N2, stream, RopeParams{}, f, (uint8_t*)HS);
+                                                (float*)part, M, D, N2, stream, RopeParams{}, f, (uint8_t*)HS, panels);
 }
 
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream) {
@@ -700,31 +719,33 @@ hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps,
 
 hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* H,
                                     const float* gamma, uint8_t* HQ, float* r, float* sa, float* rs2,
-                                    hipStream_t stream) {
+                                    hipStream_t stream, int panels) {
   dim3 grid((M + 3) / 4), block(256);
-  hipLaunchKernelGGL(prms_reduce_quant_kernel, grid, block, 0, stream, part, T, M, D, eps, H, gamma, HQ, r, sa, rs2);
+  hipLaunchKernelGGL(prms_reduce_quant_kernel, grid, block, 0, stream, part, T, M, D, eps, H, gamma, HQ, r, sa, rs2,
+                     panels);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
-                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z) {
+                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z, int panels) {
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, r, nullptr, Y, Z, nullptr, M, D, N2,
-                                                    stream);
-  return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2, stream);
+                                                    stream, RopeParams{}, RowFold{}, nullptr, panels);
+  return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2, stream,
+                                           RopeParams{}, RowFold{}, nullptr, panels);
 }
 
 int fold_supported(int D) { return D / BN <= FOLD_MAX_T; }
 
 hipError_t launch_gemm2_rowscale_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps, float* r,
                                       int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
-                                      uint16_t* Z) {
+                                      uint16_t* Z, int panels) {
   const RowFold f{D / BN, (float)D, eps, r};
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, Z,
-                                                    (float*)part, M, D, N2, stream, RopeParams{}, f);
+                                                    (float*)part, M, D, N2, stream, RopeParams{}, f, nullptr, panels);
   return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr, (float*)part, M, D,
-                                           N2, stream, RopeParams{}, f);
+                                           N2, stream, RopeParams{}, f, nullptr, panels);
 }
 
 static RopeParams rope_params(int seq_len, int n_rot, float base) {
@@ -736,17 +757,19 @@ static RopeParams rope_params(int seq_len, int n_rot, float base) {
 }
 
 hipError_t launch_gemm2_rowscale_rope(const uint16_t* A, const uint16_t* W2, const float* r, int seq_len, int n_rot,
-                                      float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+                                      float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
+                                      int panels) {
   return launch_gemm<MODE_ROWSCALE_ROPE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2,
-                                                stream, rope_params(seq_len, n_rot, base));
+                                                stream, rope_params(seq_len, n_rot, base), RowFold{}, nullptr,
+                                                panels);
 }
 
 hipError_t launch_gemm2_rowscale_rope_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps,
                                            float* r, int seq_len, int n_rot, float base, uint16_t* Y, int M, int D,
-                                           int N2, hipStream_t stream) {
+                                           int N2, hipStream_t stream, int panels) {
   return launch_gemm<MODE_ROWSCALE_ROPE, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr, (float*)part,
                                                 M, D, N2, stream, rope_params(seq_len, n_rot, base),
-                                                RowFold{D / BN, (float)D, eps, r});
+                                                RowFold{D / BN, (float)D, eps, r}, nullptr, panels);
 }
 
 // Standalone rotary embedding, in place on bf16 Y [M,N] (the unfused counterpart): one thread per pair.
@@ -774,11 +797,12 @@ hipError_t launch_rope_rows(uint16_t* Y, int M, int N, int seq_len, int n_rot, f
 }
 
 hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,
-                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream) {
+                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels) {
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, true>(Aq, W2q, nullptr, nullptr, rowsc, sw2, Y, nullptr, nullptr, M, D,
-                                                   N2, stream);
-  return launch_gemm<MODE_ROWSCALE, true>(Aq, W2q, nullptr, nullptr, rowsc, sw2, Y, nullptr, nullptr, M, D, N2, stream);
+                                                   N2, stream, RopeParams{}, RowFold{}, nullptr, panels);
+  return launch_gemm<MODE_ROWSCALE, true>(Aq, W2q, nullptr, nullptr, rowsc, sw2, Y, nullptr, nullptr, M, D, N2, stream,
+                                          RopeParams{}, RowFold{}, nullptr, panels);
 }
 
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,

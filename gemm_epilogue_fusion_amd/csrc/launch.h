@@ -8,27 +8,31 @@ namespace coda {
 
 // K1: H = bf16(X W1 + R), HG = bf16((X W1 + R) * gamma) and part[t][m] = sum over tile t's 256 columns of
 // the fp32 (X W1 + R)^2.
+// `panels` (here and below): HG / HQ are written, and the second GEMM's A operand is read, in K panels of the
+// mainloop's stage width ([D / 32][M][32] bf16, [D / 64][M][64] e4m3 bytes) instead of row-major [M, D].
 hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, const float* gamma,
-                                 uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream);
+                                 uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream,
+                                 int panels = 0);
 // K2: r[m] = 1 / sqrt(sum_t part[t][m] / D + eps).
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream);
 // K3 (r non-null; A = h * gamma) and U3 (r null; A = the normalised rows): Y = bf16(epi(r * (A W2))).
 // Z (SwiGLU only, may be null): also store the pre-activation z = [gate | up] = r (A W2) as bf16 [M, N2].
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
-                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z = nullptr);
+                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z = nullptr, int panels = 0);
 // K2 folded into K3 (D / 256 <= 16, see fold_supported): the row scales come from the partial sums of K1, are
 // formed per workgroup as launch_prms_reduce forms them, and are written to r by the tiles of column 0.
 int fold_supported(int D);
 hipError_t launch_gemm2_rowscale_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps, float* r,
                                       int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
-                                      uint16_t* Z = nullptr);
+                                      uint16_t* Z = nullptr, int panels = 0);
 // K3 with a rotary embedding after the row scale (identity epilogue): Y = bf16(rope(r * (A W2))); the first n_rot
 // columns form heads of 64 rotated at position row mod seq_len with frequencies base^(-2i/64).
 hipError_t launch_gemm2_rowscale_rope(const uint16_t* A, const uint16_t* W2, const float* r, int seq_len, int n_rot,
-                                      float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream);
+                                      float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
+                                      int panels = 0);
 hipError_t launch_gemm2_rowscale_rope_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps,
                                            float* r, int seq_len, int n_rot, float base, uint16_t* Y, int M, int D,
-                                           int N2, hipStream_t stream);
+                                           int N2, hipStream_t stream, int panels = 0);
 // The same rotation as a separate in-place pass over bf16 Y [M,N] (the unfused counterpart).
 hipError_t launch_rope_rows(uint16_t* Y, int M, int N, int seq_len, int n_rot, float base, hipStream_t stream);
 // U1: T = bf16(X W).
@@ -48,20 +52,21 @@ hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const u
 // bytes).  D % 256 == 0.
 hipError_t launch_gemm1_res_prms_fp8_mx(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
                                         const uint16_t* R, const float* gamma, uint16_t* H, uint8_t* HQ, uint8_t* HS,
-                                        float* part, int M, int K1, int D, hipStream_t stream);
+                                        float* part, int M, int K1, int D, hipStream_t stream, int panels = 0);
 // MX variant of K3: Y = bf16(epi(r * (HQ W2q) * sw2[n])) with HQ's block scales inside the MFMA.  With part
 // non-null the reduce is folded in (D / 256 <= 16; r written to r_out), else the row scale is r_in.
 hipError_t launch_gemm2_rowscale_fp8_mx(const uint8_t* HQ, const uint8_t* HS, const uint8_t* W2q, const float* sw2,
                                         const float* r_in, const float* part, float eps, float* r_out, int swiglu,
-                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream);
+                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels = 0);
 // K2: r from the partial sums; with a = H * gamma (fp32), HQ = e4m3(a * (1 / sa)) per row, sa = amax|a row| / 448;
 // rs2 = sa * r.
 hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* H,
                                     const float* gamma, uint8_t* HQ, float* r, float* sa, float* rs2,
-                                    hipStream_t stream);
+                                    hipStream_t stream, int panels = 0);
 // K3 / U3: Y = bf16(epi((Aq W2q) * rowsc[m] * sw2[n])).
 hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,
-                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream);
+                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
+                                     int panels = 0);
 // U1: T = bf16((Xq Wq) * sx[m] * sw[n]).
 hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,
                                  int M, int K, int N, hipStream_t stream);

@@ -82,10 +82,13 @@ const char* coda_last_error(void);
  *   fp8:     0 for the bf16 entry points, 1 for the *_fp8 ones, 2 for coda_block_fwd_fp8_mx
  *   unfused: 0 for coda_block_fwd*, 1 for coda_block_unfused* (fp8 = 2 has no unfused form)
  * Layout (each piece 256-byte aligned): part [D/256][M] fp32 partial sums of squares, r [M] fp32, then
- *   fused:   bf16: hg = h * gamma [M,D] bf16; fp8: the e4m3 quantisation of h * gamma [M,D], its row scales
- *            s_a [M] and s_a * r [M]; fp8 = 2: the block-scaled e4m3 codes [M,D] and their power-of-two scales,
- *            one byte per 32 values ((D/64) * ceil(M/256) * 512 bytes)
- *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]). */
+ *   fused:   bf16: hg = h * gamma, M * D bf16; fp8: the e4m3 quantisation of h * gamma, M * D bytes, its row
+ *            scales s_a [M] and s_a * r [M]; fp8 = 2: the block-scaled e4m3 codes, M * D bytes, and their
+ *            power-of-two scales, one byte per 32 values ((D/64) * ceil(M/256) * 512 bytes).  The fused paths
+ *            keep hg and the codes in K panels of the second product's stage width: element (m, k) at
+ *            ((k / P) * M + m) * P + k % P with P = 32 (bf16) or 64 (e4m3), so that the second product reads
+ *            whole cache lines
+ *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]), row-major. */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
 /* The fused block, bf16 operands.
@@ -184,6 +187,22 @@ int coda_partial_rms_reduce(const float* part, int64_t T, int64_t M, int64_t D, 
  * r [M] fp32 (device). */
 int coda_gemm2_rowscale(const void* hg, const void* W2, const float* r, int epi_kind, void* out_y, int64_t M,
                         int64_t D, int64_t N2, void* stream);
+
+/* Steps 1 and 3 in the layout coda_block_fwd uses between them (the same arithmetic, bit for bit).
+ * hg in K panels of 32 columns: element (m, k) of the logical [M,D] hg at ((k / 32) * M + m) * 32 + k % 32,
+ * so that the second product's direct loads cover whole 128-byte lines.
+ * _panels step 1: as coda_gemm1_residual_partial_rms with out_hg written in that layout (M * D bf16).
+ * _panels step 3: as coda_gemm2_rowscale on hg in that layout.  With part non-NULL (part [D/256][M] fp32 from
+ * step 1, D <= 4096, eps finite >= 0) step 2 is folded in: each workgroup sums its rows' partial sums in t order
+ * and forms r as coda_partial_rms_reduce does (the same r bit for bit), and the workgroups of the first column
+ * tile also write r [M] (output); with part NULL, r [M] is an input and eps is ignored.  Errors as
+ * coda_gemm2_rowscale, plus CODA_ERR_UNSUPPORTED for part with D > 4096 and CODA_ERR_ALIAS for r overlapping
+ * an input or out_y when it is an output. */
+int coda_gemm1_residual_partial_rms_panels(const void* X, const void* W1, const void* R, const float* gamma,
+                                           void* out_h, void* out_hg, float* part, int64_t M, int64_t K1, int64_t D,
+                                           void* stream);
+int coda_gemm2_rowscale_panels(const void* hg, const void* W2, const float* part, float eps, float* r, int epi_kind,
+                               void* out_y, int64_t M, int64_t D, int64_t N2, void* stream);
 
 /* ---- backward of the block ----
  * The CODA write-up (section "CODA: the treasure hidden in the epilogue"; section "Experimental results"

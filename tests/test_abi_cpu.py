@@ -126,6 +126,27 @@ def test_step_entry_points_validate(lib):
     assert lib.coda_gemm2_rowscale(BASE, BASE + GB, BASE + 2 * GB, 0, BASE + 16, 100, 256, 512, None) == ALIAS
 
 
+def test_panel_step_entry_points_validate(lib):
+    g1 = lambda **o: lib.coda_gemm1_residual_partial_rms_panels(
+        o.get("X", BASE), BASE + GB, BASE + 2 * GB, BASE + 3 * GB, o.get("h", BASE + 4 * GB), o.get("hg", BASE + 5 * GB),
+        BASE + 6 * GB, 100, o.get("K1", 256), 256, None)
+    assert g1(K1=192) == UNSUPPORTED
+    assert g1(X=0) == INVALID
+    assert g1(hg=BASE + 4 * GB + 512) == ALIAS
+    # step 3: hg, W2, part, eps, r, epi, y, M, D, N2
+    g3 = lambda **o: lib.coda_gemm2_rowscale_panels(
+        BASE, BASE + GB, o.get("part", BASE + 2 * GB), o.get("eps", 1e-5), o.get("r", BASE + 3 * GB), o.get("epi", 1),
+        o.get("y", BASE + 4 * GB), 100, o.get("D", 256), 512, None)
+    assert g3(epi=2) == INVALID
+    assert g3(eps=-1.0) == INVALID
+    assert g3(eps=float("nan")) == INVALID
+    assert g3(D=4352) == UNSUPPORTED                  # the folded reduce takes D <= 4096
+    assert g3(r=BASE + 2 * GB + 64) == ALIAS          # r (an output when folding) on part
+    assert g3(y=BASE + 3 * GB) == ALIAS               # out_y on r
+    assert g3(y=BASE + 16) == ALIAS                   # out_y on hg
+    assert g3(D=192) == UNSUPPORTED
+
+
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")
 def test_no_gpu_reports_hip_error(lib):
     """With no GPU, a call that passes validation fails at the launch with CODA_ERR_HIP (no crash)."""

@@ -63,6 +63,12 @@ def _oracle_a32(oh, gamma):
     return (hb * gamma.numpy().astype(np.float32)[None, :]).astype(np.float32)
 
 
+def _panels_to_rows(flat, M, D, P=64):
+    """The fused paths keep the e4m3 operand in the workspace as K panels [D / P][M][P] (element (m, k) at
+    ((k / P) * M + m) * P + k % P); this returns it as [M, D]."""
+    return flat.view(D // P, M, P).permute(1, 0, 2).reshape(M, D)
+
+
 def _run_fp8(inp, unfused=False):
     wl = inp.wl
     dev = "cuda"
@@ -94,7 +100,7 @@ def test_fp8_fused_small(wl):
     oh, orr, oy = _oracle_fp8(inp)
     check_h(f64(h), oh)
     check_y(f64(y), oy, fp8=True)
-    # the workspace after the call: part, r, hq [M,D] e4m3, s_a [M], s_a * r [M]
+    # the workspace after the call: part, r, hq (M * D e4m3 bytes in K panels of 64), s_a [M], s_a * r [M]
     M, D = wl.M, wl.D
     off_r = _align256((D // 256) * M * 4)
     off_q = off_r + _align256(M * 4)
@@ -102,7 +108,7 @@ def test_fp8_fused_small(wl):
     wsc = ws.cpu()
     r = wsc[off_r: off_r + 4 * M].view(torch.float32).numpy()
     np.testing.assert_allclose(r, orr, rtol=2e-5)
-    q = wsc[off_q: off_q + M * D].view(M, D).numpy()
+    q = _panels_to_rows(wsc[off_q: off_q + M * D], M, D).numpy()
     s = wsc[off_s: off_s + 4 * M].view(torch.float32).numpy()
     # the quantiser's input from the oracle's side: its h rounded to bf16, times gamma in fp32 (the kernels'
     # product), then the row scale amax / 448, its fp32 reciprocal and the scaled value in fp32
@@ -197,7 +203,7 @@ def test_fp8_mx_small(wl):
     np.testing.assert_allclose(wsc[off_r: off_r + 4 * M].view(torch.float32).numpy(), orr, rtol=2e-5)
     y_mx, codes, exps = _oracle_mx_y(inp, oh, orr)
     check_roundpts(f64(y), y_mx)
-    q = wsc[off_q: off_q + M * D].view(M, D).numpy()
+    q = _panels_to_rows(wsc[off_q: off_q + M * D], M, D).numpy()
     assert np.mean(q == codes) >= 0.99
     assert np.mean(_mx_scales_from_workspace(wsc, M, D, off_s) == exps) >= 0.99
 

@@ -148,6 +148,44 @@ def test_block_equals_its_three_steps(wl):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+PANEL = [FOLD[0], FOLD[1], FOLD[3]]
+
+
+@pytest.mark.parametrize("wl", PANEL, ids=[w.name for w in PANEL])
+def test_panel_steps_equal_row_major_steps(wl):
+    """The step entry points in the block's K-panel layout of hg give the row-major steps' h, part, hg (read
+    back through the panel index), r and y bit for bit: the layout moves bytes, not arithmetic.  Step 3 with
+    the folded reduce also writes the reduce kernel's r."""
+    _say(f"[gpu] panel steps vs row-major steps {wl.name}")
+    d = DeviceInputs(make_inputs(wl))
+    M, D, T = wl.M, wl.D, wl.D // 256
+    ny = wl.N2 // 2 if wl.epi == EPI_SWIGLU else wl.N2
+    dev = "cuda"
+    h = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    hg = torch.empty(M, D, dtype=torch.bfloat16, device=dev)
+    part = torch.empty(T, M, dtype=torch.float32, device=dev)
+    r = torch.empty(M, dtype=torch.float32, device=dev)
+    y = torch.empty(M, ny, dtype=torch.bfloat16, device=dev)
+    cb.coda_gemm1_residual_partial_rms(d.X, d.W1, d.R, d.gamma, h, hg, part)
+    cb.coda_partial_rms_reduce(part, D, wl.eps, r)
+    cb.coda_gemm2_rowscale(hg, d.W2, r, wl.epi, y)
+    h2 = torch.full_like(h, float("nan"))
+    hgp = torch.full((D // 32, M, 32), float("nan"), dtype=torch.bfloat16, device=dev)
+    part2 = torch.full_like(part, float("nan"))
+    r2 = torch.full_like(r, float("nan"))
+    y2 = torch.full_like(y, float("nan"))
+    y3 = torch.full_like(y, float("nan"))
+    cb.coda_gemm1_residual_partial_rms_panels(d.X, d.W1, d.R, d.gamma, h2, hgp, part2)
+    cb.coda_gemm2_rowscale_panels(hgp, d.W2, part2, wl.eps, r2, wl.epi, y2)   # reduce folded in
+    cb.coda_gemm2_rowscale_panels(hgp, d.W2, None, 0.0, r, wl.epi, y3)       # r given
+    torch.cuda.synchronize()
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+    assert torch.equal(bits(h2), bits(h)) and torch.equal(bits(part2), bits(part))
+    assert torch.equal(bits(hgp.permute(1, 0, 2).reshape(M, D)), bits(hg))
+    assert torch.equal(bits(r2), bits(r))
+    assert torch.equal(bits(y2), bits(y)) and torch.equal(bits(y3), bits(y))
+
+
 def test_partial_reduce_synthetic():
     """Step 2 alone on synthetic partials: fixed-order fp32 sum, within a few fp32 ulps of the fp64 value."""
     _say("[gpu] partial reduce synthetic")
