@@ -30,6 +30,8 @@ Besides the headline the line carries:
                 against the plain block and the plain block followed by a separate rotation pass
   ce            cross-entropy of the 1B LM head (V = 128256) with the logits reduced in the GEMM's epilogue,
                 against storing bf16 logits and reading them back
+  tiny          the 64-row block, launch-bound: microseconds per block called eagerly and replayed from a HIP
+                graph
   swiglu        the forward that also stores the SwiGLU pre-activation z (against the plain forward), and the
                 SwiGLU backward at the 1B down-projection shape, fused into the dgrad product's epilogue and
                 unfused (dy stored, then an elementwise pass)
@@ -195,6 +197,41 @@ def time_bwd(wl, X, W1, g, W2, h, ws, n_ev: int, warmup: int, torch, cb) -> dict
             "unfused_ms": round(u_ms, 4), "speedup_fused_vs_unfused": round(u_ms / f_ms, 4)}
 
 
+def time_tiny(dev, torch, cb) -> dict:
+    """The tiny block (M=64, K1=D=256, N2=512), launch-bound: microseconds per block called eagerly (two kernel
+    launches through the C ABI each) and replayed from a HIP graph holding 50 blocks."""
+    from gemm_epilogue_fusion_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS["tiny"]
+    inp = make_inputs(wl)
+    X, W1, R, g, W2 = (t.to(dev) for t in (inp.X, inp.W1, inp.R, inp.gamma, inp.W2))
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev)
+    call = lambda: cb.coda_block_fwd(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws)
+    for _ in range(20):
+        call()
+    torch.cuda.synchronize()
+    eager_ms = time_loop(call, 500, torch)
+    per_graph = 50
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_ms = time_loop(graph.replay, 20, torch) / per_graph
+    return {"workload": wl.name, "M": wl.M, "K1": wl.K1, "D": wl.D, "N2": wl.N2, "kernels_per_block": 2,
+            "eager_us_per_block": round(eager_ms * 1e3, 2), "graph_us_per_block": round(graph_ms * 1e3, 2),
+            "graph_blocks_per_replay": per_graph}
+
+
 def time_rope(dev, n_ev: int, warmup: int, torch, cb) -> dict:
     """The QKV block with RoPE on the q and k heads (32 + 8 heads of 64 of the 48), seq_len 2048, base 5e5:
     fused into GEMM2's epilogue, against the plain block alone and the plain block + a separate pass."""
@@ -310,6 +347,7 @@ def main() -> int:
     ap.add_argument("--no-rope", action="store_true", help="skip the rotary-embedding block timing")
     ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy timing")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the SwiGLU forward-with-z / backward timing")
+    ap.add_argument("--no-tiny", action="store_true", help="skip the launch-bound tiny block (eager and graph)")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
@@ -456,6 +494,8 @@ def main() -> int:
         line["ce"] = time_ce(dev, n_ev, args.warmup, torch, cb)
     if not args.no_swiglu and wl.epi == 1:
         line["swiglu"] = time_swiglu(wl, X, W1, R, g, W2, dev, n_ev, args.warmup, torch, cb)
+    if not args.no_tiny:
+        line["tiny"] = time_tiny(dev, torch, cb)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, inp)
     print(json.dumps(line))

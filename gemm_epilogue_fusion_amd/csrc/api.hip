@@ -39,7 +39,8 @@ constexpr int64_t kMaxDim = (int64_t)1 << 30;  // keeps every row index and per-
 
 // The fused paths keep the second GEMM's A operand (h * gamma, or its e4m3 codes) in the workspace as K panels
 // of the mainloop's stage width: it is private to the block, and whole-line direct loads shorten GEMM2 (see
-// ALayout in gemm_core.h).  The step entry points, whose tensors the caller sees, stay row-major.
+// ALayout in gemm_core.h).  The backward keeps dh^T and n^T, the A operands of the weight-gradient products,
+// the same way.  The step entry points, whose tensors the caller sees, stay row-major.
 constexpr int kPanels = 1;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -197,8 +198,8 @@ struct BwdWorkspace {
   float* part;    // row partials [D/256][M]
   float* part2;   // column partials [ceil(M/256)][D]
   float* a;       // [M]
-  uint16_t* dhT;  // [D,M] bf16
-  uint16_t* nT;   // [D,M] bf16
+  uint16_t* dhT;  // dh^T, M * D bf16 in K panels over M ([M/32][D][32])
+  uint16_t* nT;   // n^T, same layout
   uint16_t* P;    // unfused: P = dz W2^T [M,D] bf16
   float* slabs;   // split-K partial products of dW1 and dW2 (whichever needs more)
   uint16_t* W2T;  // W2^T [N2,D] bf16 for the first product; shares its bytes with slabs (used later in the stream)
@@ -656,7 +657,7 @@ static int block_bwd(const void* X, const void* W1, const void* h, const float* 
                        "bwd reduce launch")))
       return s;
     if ((s = hip_check(coda::launch_bwd_dh(w.G, hh, (const uint16_t*)dh_out, r, w.a, (int)M, (int)D,
-                                           (uint16_t*)out_dR, w.dhT, w.nT, st),
+                                           (uint16_t*)out_dR, w.dhT, w.nT, st, kPanels),
                        "bwd dh launch")))
       return s;
     if ((s = hip_check(coda::launch_gemm_nt_store((const uint16_t*)out_dR, (const uint16_t*)W1, (uint16_t*)out_dX,
@@ -664,11 +665,11 @@ static int block_bwd(const void* X, const void* W1, const void* h, const float* 
                        "bwd dX launch")))
       return s;
     if ((s = hip_check(coda::launch_gemm_f32_trans(w.dhT, (const uint16_t*)X, out_dW1, (int)D, (int)M, (int)K1,
-                                                   w.slabs, st),
+                                                   w.slabs, st, kPanels),
                        "bwd dW1 launch")))
       return s;
     return hip_check(coda::launch_gemm_f32_rowscale(w.nT, (const uint16_t*)dz, gamma, out_dW2, (int)D, (int)M,
-                                                    (int)N2, w.slabs, st),
+                                                    (int)N2, w.slabs, st, kPanels),
                      "bwd dW2 launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");

@@ -45,6 +45,7 @@ struct BwdArgs {
   int M, K, Nb, group_m;
   int64_t slab;        // BWD_F32_*: split-K partial products go to outf + blockIdx.y * slab (K per split = K)
                        // BWD_SWIGLU: h = z [M, 2 Nb] (gate | up), out = dz [M, 2 Nb]
+  int a_panels;        // non-transposed B: A in K panels [K_total / 32][M][32] (ALayout in gemm_core.h)
 };
 
 // silu(x) = x s(x) and its derivative s(x) (1 + x (1 - s(x))), s the logistic function, in fp32 with the
@@ -144,8 +145,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
     // split K: workgroup row blockIdx.y multiplies K range [y K, (y + 1) K) of the gridDim.y K ranges
     const int64_t k0 = (int64_t)blockIdx.y * args.K;
     const int64_t lda = (int64_t)args.K * gridDim.y;
-    gemm_mainloop(args.A + k0, ALayout{lda, BK}, M, m0, args.B + k0 * Nb, Nb, ContiguousCols<8>{n0}, args.K, smem,
-                  acc);
+    const int64_t pstep = (int64_t)M * BK;  // one K panel of A
+    const uint16_t* a0 = args.a_panels ? args.A + (k0 / BK) * pstep : args.A + k0;
+    gemm_mainloop(a0, args.a_panels ? ALayout{BK, pstep} : ALayout{lda, BK}, M, m0, args.B + k0 * Nb, Nb,
+                  ContiguousCols<8>{n0}, args.K, smem, acc);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -409,7 +412,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ dh_out, const float* __restrict__ r,
                                                      const float* __restrict__ a, int M, int D,
                                                      uint16_t* __restrict__ dR, uint16_t* __restrict__ dhT,
-                                                     uint16_t* __restrict__ nT) {
+                                                     uint16_t* __restrict__ nT, int panels) {
   __shared__ uint16_t tdh[64][64 + 2];
   __shared__ uint16_t tn[64][64 + 2];
   const int t = threadIdx.x;
@@ -452,8 +455,11 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const uint16_t* __restrict_
       o1[q] = (uint32_t)tdh[jr][ic + 2 * q] | ((uint32_t)tdh[jr][ic + 2 * q + 1] << 16);
       o2[q] = (uint32_t)tn[jr][ic + 2 * q] | ((uint32_t)tn[jr][ic + 2 * q + 1] << 16);
     }
-    *(u32x4*)(dhT + (int64_t)(j0 + jr) * M + i0 + ic) = o1;
-    *(u32x4*)(nT + (int64_t)(j0 + jr) * M + i0 + ic) = o2;
+    // [D, M] rows, or (panels) K panels over M of the weight-gradient products: ((m / 32) D + d) 32 + m % 32
+    const int64_t off = panels ? ((int64_t)((i0 + ic) >> 5) * D + j0 + jr) * 32 + ((i0 + ic) & 31)
+                               : (int64_t)(j0 + jr) * M + i0 + ic;
+    *(u32x4*)(dhT + off) = o1;
+    *(u32x4*)(nT + off) = o2;
   }
 }
 
@@ -578,21 +584,21 @@ static hipError_t slab_sum(const float* slabs, int S, int64_t n, int cols, const
 }
 
 hipError_t launch_gemm_f32_rowscale(const uint16_t* A, const uint16_t* B, const float* rowsc, float* C, int M, int K,
-                                    int N, float* slabs, hipStream_t stream) {
+                                    int N, float* slabs, hipStream_t stream, int a_panels) {
   const int S = gemm_ksplit(M, N, K);
   const int64_t n = (int64_t)M * N;
   BwdArgs a{A, B, nullptr, nullptr, S > 1 ? nullptr : rowsc, nullptr, S > 1 ? slabs : C, nullptr, nullptr, M, K, N,
-            0, n};
+            0, n, a_panels};
   hipError_t e = launch_bwd<BWD_F32_ROWSCALE, false>(a, stream, S);
   if (e != hipSuccess || S == 1) return e;
   return slab_sum(slabs, S, n, N, rowsc, C, stream);
 }
 
 hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N, float* slabs,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, int a_panels) {
   const int S = gemm_ksplit(M, N, K);
   const int64_t n = (int64_t)M * N;
-  BwdArgs a{A, B, nullptr, nullptr, nullptr, nullptr, S > 1 ? slabs : Ct, nullptr, nullptr, M, K, N, 0, n};
+  BwdArgs a{A, B, nullptr, nullptr, nullptr, nullptr, S > 1 ? slabs : Ct, nullptr, nullptr, M, K, N, 0, n, a_panels};
   hipError_t e = launch_bwd<BWD_F32_TRANS, false>(a, stream, S);
   if (e != hipSuccess || S == 1) return e;
   return slab_sum(slabs, S, n, M, nullptr, Ct, stream);
@@ -606,8 +612,9 @@ hipError_t launch_bwd_reduce(const float* part, int T, const float* part2, int Q
 }
 
 hipError_t launch_bwd_dh(const uint16_t* G, const uint16_t* h, const uint16_t* dh_out, const float* r, const float* a,
-                         int M, int D, uint16_t* dR, uint16_t* dhT, uint16_t* nT, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_dh_kernel, dim3(D / 64, M / 64), dim3(256), 0, stream, G, h, dh_out, r, a, M, D, dR, dhT, nT);
+                         int M, int D, uint16_t* dR, uint16_t* dhT, uint16_t* nT, hipStream_t stream, int panels) {
+  hipLaunchKernelGGL(bwd_dh_kernel, dim3(D / 64, M / 64), dim3(256), 0, stream, G, h, dh_out, r, a, M, D, dR, dhT, nT,
+                     panels);
   return hipGetLastError();
 }
 

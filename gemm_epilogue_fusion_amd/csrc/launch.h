@@ -98,18 +98,21 @@ hipError_t launch_gemm_nt_store(const uint16_t* A, const uint16_t* Bt, uint16_t*
 // CUs when the output has few tiles.  The partial products go to `slabs` (gemm_ksplit(...) * M * N floats,
 // unused when it is 1) and are summed in order by a second kernel.
 int gemm_ksplit(int M, int N, int K);
-// C [M,N] = fp32 rowsc[m] * (A B), A [M,K], B [K,N] (rowsc may be null).
+// C [M,N] = fp32 rowsc[m] * (A B), A [M,K], B [K,N] (rowsc may be null).  a_panels: A in K panels
+// [K/32][M][32] (as launch_bwd_dh writes dh^T and n^T with panels set), else row-major.
 hipError_t launch_gemm_f32_rowscale(const uint16_t* A, const uint16_t* B, const float* rowsc, float* C, int M, int K,
-                                    int N, float* slabs, hipStream_t stream);
-// Ct [N,M] = fp32 (A B)^T, A [M,K], B [K,N].
+                                    int N, float* slabs, hipStream_t stream, int a_panels = 0);
+// Ct [N,M] = fp32 (A B)^T, A [M,K], B [K,N]; a_panels as above.
 hipError_t launch_gemm_f32_trans(const uint16_t* A, const uint16_t* B, float* Ct, int M, int K, int N, float* slabs,
-                                 hipStream_t stream);
+                                 hipStream_t stream, int a_panels = 0);
 // B2: a[i] = r_i^3 / D * sum_t part[t][i]; dgamma[j] = sum_q part2[q][j].
 hipError_t launch_bwd_reduce(const float* part, int T, const float* part2, int Q, const float* r, int M, int D,
                              float* a, float* dgamma, hipStream_t stream);
 // B3: dR = bf16(G - a h + dh_out) [M,D]; dhT, nT [D,M] = dR and bf16(r h), transposed.  M, D multiples of 64.
+// panels: dhT and nT in K panels over M for the weight-gradient products ([M/32][D][32]), else [D,M] rows.
 hipError_t launch_bwd_dh(const uint16_t* G, const uint16_t* h, const uint16_t* dh_out, const float* r, const float* a,
-                         int M, int D, uint16_t* dR, uint16_t* dhT, uint16_t* nT, hipStream_t stream);
+                         int M, int D, uint16_t* dR, uint16_t* dhT, uint16_t* nT, hipStream_t stream,
+                         int panels = 0);
 
 // ---- cross-entropy of a vocabulary projection (ce_kernels.hip) ----
 // C1: logits z = H W by 256 x 256 tiles; per tile t and row i, part_m[t][i] = max z, part_s[t][i] = sum exp(z -
