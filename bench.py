@@ -274,8 +274,8 @@ def time_ce(dev, n_ev: int, warmup: int, torch, cb) -> dict:
     H, W, labels = (t.to(dev) for t in make_ce_inputs(wl))
     loss = torch.empty(wl.M, dtype=torch.float32, device=dev)
     lse = torch.empty(wl.M, dtype=torch.float32, device=dev)
-    ws = cb.alloc_ce_workspace(wl.M, wl.V, device=dev)
-    wsu = cb.alloc_ce_workspace(wl.M, wl.V, unfused=1, device=dev)
+    ws = cb.alloc_ce_workspace(wl.M, wl.D, wl.V, device=dev)
+    wsu = cb.alloc_ce_workspace(wl.M, wl.D, wl.V, unfused=1, device=dev)
     fused = lambda: cb.coda_ce_fwd(H, W, labels, loss, lse, ws)
     unfused = lambda: cb.coda_ce_unfused(H, W, labels, loss, lse, wsu)
     for _ in range(warmup):

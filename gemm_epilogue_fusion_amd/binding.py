@@ -84,7 +84,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("coda_block_bwd", "coda_block_bwd_unfused"):
         getattr(lib, name).argtypes = bwd
         getattr(lib, name).restype = i32
-    lib.coda_ce_workspace_bytes.argtypes, lib.coda_ce_workspace_bytes.restype = [i64, i64, i32], sz
+    lib.coda_ce_workspace_bytes.argtypes, lib.coda_ce_workspace_bytes.restype = [i64, i64, i64, i32], sz
     for name in ("coda_ce_fwd", "coda_ce_unfused"):
         getattr(lib, name).argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, sz, vp]
         getattr(lib, name).restype = i32
@@ -342,12 +342,12 @@ def coda_block_bwd_unfused(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, 
                out_dW2, workspace, stream)
 
 
-def coda_ce_workspace_bytes(M: int, V: int, unfused: int = 0) -> int:
-    return int(load().coda_ce_workspace_bytes(M, V, unfused))
+def coda_ce_workspace_bytes(M: int, D: int, V: int, unfused: int = 0) -> int:
+    return int(load().coda_ce_workspace_bytes(M, D, V, unfused))
 
 
-def alloc_ce_workspace(M: int, V: int, unfused: int = 0, device="cuda"):
-    n = coda_ce_workspace_bytes(M, V, unfused)
+def alloc_ce_workspace(M: int, D: int, V: int, unfused: int = 0, device="cuda"):
+    n = coda_ce_workspace_bytes(M, D, V, unfused)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 

@@ -702,9 +702,10 @@ struct CeWorkspace {
   float* part_s;  // [V/256][M] per-tile row sums of exp(z - max)
   float* zlab;    // [M] the label's logit
   uint16_t* z;    // unfused: the bf16 logits [M,V]
+  uint16_t* hp;   // H in K panels of 32 columns ([D/32][M][32]), the product's A operand on both paths
 };
 
-size_t carve_ce(void* ws, int64_t M, int64_t V, int unfused, CeWorkspace* w) {
+size_t carve_ce(void* ws, int64_t M, int64_t D, int64_t V, int unfused, CeWorkspace* w) {
   char* base = (char*)ws;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -713,6 +714,7 @@ size_t carve_ce(void* ws, int64_t M, int64_t V, int unfused, CeWorkspace* w) {
     return p;
   };
   CeWorkspace x{};
+  x.hp = (uint16_t*)take(ws_mat_bytes(M, D, 2));
   if (unfused) {
     x.z = (uint16_t*)take(ws_mat_bytes(M, V, 2));
   } else {
@@ -739,7 +741,7 @@ int ce(const void* H, const void* W, const int* labels, float* out_loss, float* 
       return fail(CODA_ERR_UNSUPPORTED, "dimensions too large");
     if (D % 128) return fail(CODA_ERR_UNSUPPORTED, "D=%lld is not a multiple of 128", (long long)D);
     if (V % 256) return fail(CODA_ERR_UNSUPPORTED, "V=%lld is not a multiple of 256", (long long)V);
-    const size_t need = carve_ce(nullptr, M, V, unfused, nullptr);
+    const size_t need = carve_ce(nullptr, M, D, V, unfused, nullptr);
     if (!workspace) return fail(CODA_ERR_WORKSPACE, "workspace is NULL");
     if ((uintptr_t)workspace & 255) return fail(CODA_ERR_WORKSPACE, "workspace is not 256-byte aligned");
     if (workspace_bytes < need)
@@ -751,16 +753,17 @@ int ce(const void* H, const void* W, const int* labels, float* out_loss, float* 
     if ((s = check_alias(in, 3, out, 3, nullptr, nullptr))) return s;
     hipStream_t st = (hipStream_t)stream;
     CeWorkspace w;
-    carve_ce(workspace, M, V, unfused, &w);
+    carve_ce(workspace, M, D, V, unfused, &w);
+    if ((s = hip_check(coda::launch_panelize_bf16((const uint16_t*)H, (int)M, (int)D, w.hp, st), "ce panel launch")))
+      return s;
     if (unfused) {
-      if ((s = hip_check(coda::launch_gemm_store((const uint16_t*)H, (const uint16_t*)W, w.z, (int)M, (int)D, (int)V,
-                                                 st),
+      if ((s = hip_check(coda::launch_gemm_store(w.hp, (const uint16_t*)W, w.z, (int)M, (int)D, (int)V, st, kPanels),
                          "ce logits launch")))
         return s;
       return hip_check(coda::launch_ce_rows(w.z, labels, (int)M, (int)V, out_loss, out_lse, st), "ce rows launch");
     }
-    if ((s = hip_check(coda::launch_ce_gemm((const uint16_t*)H, (const uint16_t*)W, labels, w.part_m, w.part_s,
-                                            w.zlab, (int)M, (int)D, (int)V, st),
+    if ((s = hip_check(coda::launch_ce_gemm(w.hp, (const uint16_t*)W, labels, w.part_m, w.part_s, w.zlab, (int)M,
+                                            (int)D, (int)V, st, kPanels),
                        "ce gemm launch")))
       return s;
     return hip_check(coda::launch_ce_reduce(w.part_m, w.part_s, w.zlab, labels, (int)(V / 256), (int)M, (int)V,
@@ -775,9 +778,9 @@ int ce(const void* H, const void* W, const int* labels, float* out_loss, float* 
 
 extern "C" {
 
-size_t coda_ce_workspace_bytes(int64_t M, int64_t V, int unfused) {
-  if (M < 1 || V < 256 || M > kMaxDim || V > kMaxDim) return 0;
-  return carve_ce(nullptr, M, V, unfused, nullptr);
+size_t coda_ce_workspace_bytes(int64_t M, int64_t D, int64_t V, int unfused) {
+  if (M < 1 || D < 1 || V < 256 || M > kMaxDim || D > kMaxDim || V > kMaxDim) return 0;
+  return carve_ce(nullptr, M, D, V, unfused, nullptr);
 }
 
 int coda_ce_fwd(const void* H, const void* W, const int32_t* labels, float* out_loss, float* out_lse, int64_t M,

@@ -12,6 +12,9 @@
 //                         negative label, NaN for a label >= V)
 // The unfused baseline stores the logits in bf16 (the first GEMM kernel's plain store) and reads them back:
 //   CU ce_rows_kernel   : one workgroup per row of the stored logits.
+// Both paths first copy H into K panels of 32 columns (panelize_bf16_kernel; ALayout in gemm_core.h): the
+// product re-reads each H row tile once per 256 vocabulary columns, and whole-line loads of it shorten the
+// product by more than the copy costs.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -43,7 +46,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_gemm_kernel(const uint16_t* __
                                                              const uint16_t* __restrict__ W,
                                                              const int* __restrict__ labels, float* __restrict__ part_m,
                                                              float* __restrict__ part_s, float* __restrict__ zlab, int M,
-                                                             int K, int V, int group_m) {
+                                                             int K, int V, int group_m, int a_panels) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = V / BN;
@@ -65,7 +68,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void ce_gemm_kernel(const uint16_t* __
   }
 
   f32x16 acc[4][NB];
-  gemm_mainloop(H, ALayout{K, BK}, M, m0, W, V, ContiguousCols<8>{(int64_t)n0}, K, smem, acc);
+  gemm_mainloop(H, a_panels ? ALayout{BK, (int64_t)M * BK} : ALayout{K, BK}, M, m0, W, V,
+                ContiguousCols<8>{(int64_t)n0}, K, smem, acc);
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -203,10 +207,27 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const uint16_t* __restrict
 static int ce_group_m(int tiles_m) { return tiles_m < 4 ? tiles_m : 4; }
 
 hipError_t launch_ce_gemm(const uint16_t* H, const uint16_t* W, const int* labels, float* part_m, float* part_s,
-                          float* zlab, int M, int D, int V, hipStream_t stream) {
+                          float* zlab, int M, int D, int V, hipStream_t stream, int a_panels) {
   const int tiles_m = (M + BM - 1) / BM;
   hipLaunchKernelGGL(ce_gemm_kernel, dim3(tiles_m * (V / BN)), dim3(NTHREADS), 0, stream, H, W, labels, part_m,
-                     part_s, zlab, M, D, V, ce_group_m(tiles_m));
+                     part_s, zlab, M, D, V, ce_group_m(tiles_m), a_panels);
+  return hipGetLastError();
+}
+
+// dst = src [M, D] bf16 in K panels of 32 columns: src[m][32 p + j] -> dst[(p M + m) 32 + j].  A workgroup moves
+// 64 rows of one panel: each lane one 16-byte piece, so a workgroup writes 4 KiB of the panel contiguously.
+__global__ __launch_bounds__(256) void panelize_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                            int M, int D) {
+  const int p = blockIdx.x;
+  const int r = blockIdx.y * 64 + (threadIdx.x >> 2);
+  const int c4 = threadIdx.x & 3;
+  if (r >= M) return;
+  const u32x4 v = *(const u32x4*)(src + (int64_t)r * D + 32 * p + 8 * c4);
+  *(u32x4*)(dst + ((int64_t)p * M + r) * 32 + 8 * c4) = v;
+}
+
+hipError_t launch_panelize_bf16(const uint16_t* src, int M, int D, uint16_t* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(panelize_bf16_kernel, dim3(D / 32, (M + 63) / 64), dim3(256), 0, stream, src, dst, M, D);
   return hipGetLastError();
 }
 

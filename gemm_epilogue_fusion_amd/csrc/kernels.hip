@@ -112,8 +112,8 @@ struct GateUpCols {
 //   MODE_ROWSCALE_SWIGLU: the tile's columns are 128 gate columns [tn*128, +128) and the matching 128 up
 //                   columns [Nb/2 + tn*128, +128); out [M,Nb/2] = bf16(silu(v_gate) * v_up)
 // panels != 0: MODE_RES_PRMS writes out2 (h * gamma, or the MX codes) in K panels of the second GEMM's stage
-// width ([Nb / 32][M][32] bf16, [Nb / 64][M][64] bytes), and the row-scale modes read A from such panels (ALayout
-// in gemm_core.h); A of MODE_RES_PRMS and MODE_STORE is always row-major.
+// width ([Nb / 32][M][32] bf16, [Nb / 64][M][64] bytes), and the row-scale modes and MODE_STORE read A from such
+// panels (ALayout in gemm_core.h); A of MODE_RES_PRMS is always row-major.
 template <int MODE, bool FP8, bool MX = false>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
@@ -164,7 +164,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   };
 
   constexpr int KS = FP8 ? BK8 : BK;  // K per stage: the panel width
-  const ALayout al = (ROWSCALE_MODE && panels) ? ALayout{KS, (int64_t)M * KS} : ALayout{K, KS};
+  const ALayout al = ((ROWSCALE_MODE || MODE == MODE_STORE) && panels) ? ALayout{KS, (int64_t)M * KS}
+                                                                        : ALayout{K, KS};
   f32x16 acc[4][NB];
   if (FP8) {
     const uint8_t* A8 = (const uint8_t*)A;
@@ -806,8 +807,9 @@ hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, cons
 }
 
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
-                             hipStream_t stream) {
-  return launch_gemm<MODE_STORE, false>(X, W, nullptr, nullptr, nullptr, nullptr, T, nullptr, nullptr, M, K, N, stream);
+                             hipStream_t stream, int a_panels) {
+  return launch_gemm<MODE_STORE, false>(X, W, nullptr, nullptr, nullptr, nullptr, T, nullptr, nullptr, M, K, N, stream,
+                                        RopeParams{}, RowFold{}, nullptr, a_panels);
 }
 
 hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,

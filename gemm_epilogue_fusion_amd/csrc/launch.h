@@ -35,9 +35,9 @@ hipError_t launch_gemm2_rowscale_rope_fold(const uint16_t* A, const uint16_t* W2
                                            int N2, hipStream_t stream, int panels = 0);
 // The same rotation as a separate in-place pass over bf16 Y [M,N] (the unfused counterpart).
 hipError_t launch_rope_rows(uint16_t* Y, int M, int N, int seq_len, int n_rot, float base, hipStream_t stream);
-// U1: T = bf16(X W).
+// U1: T = bf16(X W); a_panels: X given in K panels of 32 ([K/32][M][32], as launch_panelize_bf16 writes).
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
-                             hipStream_t stream);
+                             hipStream_t stream, int a_panels = 0);
 // U2: H = bf16(T + R), N = bf16((T + R) r gamma), r[m] (optional).  D <= 8192.
 hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* N,
                               float* r, int M, int D, float eps, hipStream_t stream);
@@ -118,7 +118,9 @@ hipError_t launch_bwd_dh(const uint16_t* G, const uint16_t* h, const uint16_t* d
 // C1: logits z = H W by 256 x 256 tiles; per tile t and row i, part_m[t][i] = max z, part_s[t][i] = sum exp(z -
 // max); zlab[i] = z[i][labels[i]] from the tile holding that column.  D % 128 == 0, V % 256 == 0.
 hipError_t launch_ce_gemm(const uint16_t* H, const uint16_t* W, const int* labels, float* part_m, float* part_s,
-                          float* zlab, int M, int D, int V, hipStream_t stream);
+                          float* zlab, int M, int D, int V, hipStream_t stream, int a_panels = 0);
+// dst = src [M,D] bf16 in K panels of 32 columns ([D/32][M][32]); D % 32 == 0.
+hipError_t launch_panelize_bf16(const uint16_t* src, int M, int D, uint16_t* dst, hipStream_t stream);
 // C2: lse[i] = merge of the T pairs of row i in tile order; loss[i] = lse[i] - zlab[i] (0 for a negative label,
 // NaN for a label >= V).
 hipError_t launch_ce_reduce(const float* part_m, const float* part_s, const float* zlab, const int* labels, int T,

@@ -241,19 +241,21 @@ int coda_block_bwd_unfused(const void* X, const void* W1, const void* h, const f
  * language").  Computes, per row i of H [M,D] (bf16) against W [D,V] (bf16, [in,out] like the other weights):
  *   z = H W (fp32 accumulation), out_lse[i] = log sum_j exp(z_ij), out_loss[i] = out_lse[i] - z[i][labels[i]];
  * labels [M] int32 on the device; a negative label marks an ignored row (loss 0, lse still written), a label
- * >= V gives a NaN loss.  Outputs fp32 [M].  Two kernels on `stream`: the product whose epilogue reduces each
- * 256-column tile of a row to (max, sum of exp(z - max)) and picks the label's logit, then the merge of those
- * pairs in tile order.  Shape rules: D a multiple of 128, V a multiple of 256 (else CODA_ERR_UNSUPPORTED),
- * M >= 1.  No output may overlap an input, another output or the workspace.  Workspace:
- * coda_ce_workspace_bytes(M, V, 0) bytes, 256-byte aligned; other conventions as coda_block_fwd. */
-size_t coda_ce_workspace_bytes(int64_t M, int64_t V, int unfused);
+ * >= V gives a NaN loss.  Outputs fp32 [M].  Three kernels on `stream`: a copy of H into K panels of 32 columns
+ * (the product's operand layout, see coda_workspace_bytes), the product whose epilogue reduces each 256-column
+ * tile of a row to (max, sum of exp(z - max)) and picks the label's logit, then the merge of those pairs in
+ * tile order.  Shape rules: D a multiple of 128, V a multiple of 256 (else CODA_ERR_UNSUPPORTED), M >= 1.  No
+ * output may overlap an input, another output or the workspace.  Workspace: coda_ce_workspace_bytes(M, D, V, 0)
+ * bytes, 256-byte aligned (the panel copy of H, M * D bf16, then the pairs and label logits); other conventions
+ * as coda_block_fwd. */
+size_t coda_ce_workspace_bytes(int64_t M, int64_t D, int64_t V, int unfused);
 
 int coda_ce_fwd(const void* H, const void* W, const int32_t* labels, float* out_loss, float* out_lse, int64_t M,
                 int64_t D, int64_t V, void* workspace, size_t workspace_bytes, void* stream);
 
-/* The unfused baseline: the logits are stored in bf16 (workspace: coda_ce_workspace_bytes(M, V, 1) = the M x V
- * bf16 logits) and a second kernel reads each row back.  Same arguments and outputs; the loss and lse come from
- * the bf16-rounded logits. */
+/* The unfused baseline: the logits are stored in bf16 (workspace: coda_ce_workspace_bytes(M, D, V, 1) = the panel
+ * copy of H and the M x V bf16 logits) and a second kernel reads each row back.  Same arguments and outputs; the
+ * loss and lse come from the bf16-rounded logits. */
 int coda_ce_unfused(const void* H, const void* W, const int32_t* labels, float* out_loss, float* out_lse, int64_t M,
                     int64_t D, int64_t V, void* workspace, size_t workspace_bytes, void* stream);
 

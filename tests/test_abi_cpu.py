@@ -312,7 +312,7 @@ def test_rope_no_gpu_reports_hip_error(lib):
 def _ccall(lib, fn="coda_ce_fwd", M=300, D=256, V=768, H=BASE, W=BASE + GB, labels=BASE + 2 * GB,
            loss=BASE + 3 * GB, lse=BASE + 4 * GB, ws=BASE + 5 * GB, ws_bytes=None, unfused=0):
     if ws_bytes is None:
-        ws_bytes = lib.coda_ce_workspace_bytes(M, V, unfused) if M >= 1 and V >= 256 else 1 << 20
+        ws_bytes = lib.coda_ce_workspace_bytes(M, D, V, unfused) if M >= 1 and V >= 256 else 1 << 20
     return getattr(lib, fn)(H, W, labels, loss, lse, M, D, V, ws, ws_bytes, None)
 
 
@@ -336,10 +336,12 @@ def test_ce_validation(lib, fn, unfused, case, kw, want):
 
 def test_ce_workspace_bytes(lib):
     al = lambda x: (x + 255) // 256 * 256
-    M, V = 8192, 128256
-    assert lib.coda_ce_workspace_bytes(M, V, 0) == 2 * al(V // 256 * M * 4) + al(M * 4)
-    assert lib.coda_ce_workspace_bytes(M, V, 1) == al(M * V * 2)
-    assert lib.coda_ce_workspace_bytes(0, V, 0) == 0
+    M, D, V = 8192, 2048, 128256
+    # the panel copy of H [M, D] bf16 first, then the per-tile pairs and label logits (or the bf16 logits)
+    assert lib.coda_ce_workspace_bytes(M, D, V, 0) == al(M * D * 2) + 2 * al(V // 256 * M * 4) + al(M * 4)
+    assert lib.coda_ce_workspace_bytes(M, D, V, 1) == al(M * D * 2) + al(M * V * 2)
+    assert lib.coda_ce_workspace_bytes(0, D, V, 0) == 0
+    assert lib.coda_ce_workspace_bytes(M, 0, V, 0) == 0
 
 
 @pytest.mark.skipif(torch.cuda.device_count() > 0, reason="would launch on fake pointers")

@@ -48,7 +48,7 @@ def _run(H, W, labels, unfused=False):
     dev = "cuda"
     loss = torch.full((M,), float("nan"), dtype=torch.float32, device=dev)
     lse = torch.full((M,), float("nan"), dtype=torch.float32, device=dev)
-    ws = cb.alloc_ce_workspace(M, V, unfused=int(unfused), device=dev)
+    ws = cb.alloc_ce_workspace(M, H.shape[1], V, unfused=int(unfused), device=dev)
     ws.fill_(0xFF)
     fn = cb.coda_ce_unfused if unfused else cb.coda_ce_fwd
     fn(H.to(dev), W.to(dev), labels.to(dev), loss, lse, ws)
