@@ -147,8 +147,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
     const int64_t lda = (int64_t)args.K * gridDim.y;
     const int64_t pstep = (int64_t)M * BK;  // one K panel of A
     const uint16_t* a0 = args.a_panels ? args.A + (k0 / BK) * pstep : args.A + k0;
-    gemm_mainloop(a0, args.a_panels ? ALayout{BK, pstep} : ALayout{lda, BK}, M, m0, args.B + k0 * Nb, Nb,
-                  ContiguousCols<8>{n0}, args.K, smem, acc);
+    const ALayout al = args.a_panels ? ALayout{BK, pstep} : ALayout{lda, BK};
+    if (MODE == BWD_P)  // the h tile's first 192 rows arrive as the ring drains
+      gemm_mainloop(a0, al, M, m0, args.B + k0 * Nb, Nb, ContiguousCols<8>{n0}, args.K, smem, acc, NoHook{},
+                    TileRowsDrain{args.h, Nb, m0, n0, M, smem});
+    else
+      gemm_mainloop(a0, al, M, m0, args.B + k0 * Nb, Nb, ContiguousCols<8>{n0}, args.K, smem, acc);
   }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -158,7 +162,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
 
   // acc[mb][nb][e] is row m0 + 128 wm + 32 mb + lane%32, column n0 + 64 wn + 32 nb + 8 (e/4) + 4 half + e%4
   if (PMODE) {
-    load_tile_rows<32>(args.h, Nb, m0, n0, M, smem);
+    if (MODE == BWD_P && !BT)
+      load_tile_rows64<32>(args.h, Nb, m0, n0, M, smem, 192);  // rows 0 .. 191 came with the mainloop's drain
+    else
+      load_tile_rows<32>(args.h, Nb, m0, n0, M, smem);
     float rv[4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {

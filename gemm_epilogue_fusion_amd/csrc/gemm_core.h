@@ -173,10 +173,21 @@ struct NoHook {
 // hook() runs once, after the first stage has landed and every wave has passed the barrier: global loads (or
 // global -> LDS loads) issued before the mainloop have completed by then.  It must issue no global memory
 // operation of its own (the mainloop's wait counts assume its own loads only).
-template <class BCol, class Hook = NoHook>
+//
+// drain(s) lets the epilogue's own operands start to arrive while the last K steps run: it is called for
+// s = 0, 1, 2 right after the barrier behind which every wave has finished reading ring stage s for the last
+// time (in the last four K steps), and may fill that stage's STAGE_BYTES with direct loads; it must issue
+// exactly Drain::LOADS vector memory instructions per wave, which the remaining waits count.  Stage 3 is read
+// until the mainloop returns; the caller waits for the drain's loads (vmcnt) and synchronises the workgroup.
+struct NoDrain {
+  static constexpr int LOADS = 0;
+  __device__ void operator()(int) const {}
+};
+template <class BCol, class Hook = NoHook, class Drain = NoDrain>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, ALayout al, int M, int m0,
                                               const uint16_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
-                                              char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{}) {
+                                              char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{},
+                                              Drain drain = Drain{}) {
   constexpr int LPW = 16 / NWAVES;              // 1 KiB direct loads per wave per operand per stage
   constexpr int PER = 2 * LPW;  // VMEM instructions per wave per stage
   const int t = threadIdx.x;
@@ -221,11 +232,13 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
   Frags f0, f1;
   // One K step on stage U.  ISSUE: fetch tile kt+3 into the stage tile kt-1 used (every wave has passed
   // the barrier that followed its last read of it).  WAIT >= 0: the vmcnt that guarantees tile kt+1 has
-  // landed, then the barrier and the first fragments of tile kt+1; WAIT < 0: the last tile.
-  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c) {
+  // landed, then the barrier and the first fragments of tile kt+1; WAIT < 0: the last tile.  DRAIN >= 0:
+  // drain(DRAIN) after the barrier (stage U is then free).
+  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c, auto drain_c) {
     constexpr int U = decltype(U_c)::value;
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr int WAIT = decltype(wait_c)::value;
+    constexpr int DRAIN = decltype(drain_c)::value;
     const char* cur = smem + U * STAGE_BYTES;
     if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
     read_frags(cur, lo, 1, f1);
@@ -233,6 +246,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
     interleave_mma_reads();
     if (WAIT >= 0) {
       wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
+      if (DRAIN >= 0 && Drain::LOADS > 0) drain(DRAIN);
       read_frags(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, lo, 0, f0);
     }
     mma(f1, acc);
@@ -254,20 +268,24 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
   hook();
   read_frags(smem, lo, 0, f0);
 
+  using NoD = std::integral_constant<int, -1>;
+  constexpr int DL = Drain::LOADS;
+  static_assert(PER + DL < 64 && 2 * DL < 64, "vmcnt range");
   const int nblk = nk / NSTAGE;
   for (int bi = 0; bi < nblk - 1; ++bi) {
     const int kt = bi * NSTAGE;
-    step(kt + 0, S0{}, Yes{}, WaitFull{});
-    step(kt + 1, S1{}, Yes{}, WaitFull{});
-    step(kt + 2, S2{}, Yes{}, WaitFull{});
-    step(kt + 3, S3{}, Yes{}, WaitFull{});
+    step(kt + 0, S0{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 1, S1{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 2, S2{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 3, S3{}, Yes{}, WaitFull{}, NoD{});
   }
-  // last block: only its first step fetches (the last tile); the waits shrink as the ring drains
+  // last block: only its first step fetches (the last tile); the waits shrink as the ring drains, and count
+  // the drain's loads issued after the stage loads they wait for
   const int kt = (nblk - 1) * NSTAGE;
-  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{});
-  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER>{});
-  step(kt + 2, S2{}, No{}, std::integral_constant<int, 0>{});
-  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
+  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{}, S0{});
+  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER + DL>{}, S1{});
+  step(kt + 2, S2{}, No{}, std::integral_constant<int, 2 * DL>{}, S2{});
+  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{}, NoD{});
 }
 
 // The same mainloop with B given transposed: Bt [N,K] with K contiguous (a weight read as [out,in], or W^T of
@@ -663,6 +681,35 @@ __device__ __forceinline__ void load_tile_rows(const uint16_t* src, int ld, int 
     g2lds16(src + (int64_t)m * ld + n0 + 8 * (slot ^ (r & (CH - 1))), smem + r0 * (16 * CH));
   }
 }
+
+// Rows row0 .. row0+63 of the staged-tile layout (as load_tile_rows), 64 / (NWAVES * 64 / CH) direct loads per
+// wave: with CH = 32 the 32 KiB of one ring stage, 4 loads per wave.
+template <int CH>
+__device__ __forceinline__ void load_tile_rows64(const uint16_t* src, int ld, int m0, int n0, int M, char* smem,
+                                                 int row0) {
+  constexpr int ROWS_PER_INST = 64 / CH;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int j = 0; j < 64 / (NWAVES * ROWS_PER_INST); ++j) {
+    const int r0 = row0 + wave * (64 / NWAVES) + j * ROWS_PER_INST;
+    const int r = r0 + lane / CH;
+    const int slot = lane % CH;
+    int m = m0 + r;
+    m = m < M ? m : M - 1;
+    g2lds16(src + (int64_t)m * ld + n0 + 8 * (slot ^ (r & (CH - 1))), smem + r0 * (16 * CH));
+  }
+}
+
+// The epilogue's 256 x 256 bf16 tile of a row-major [*, ld] operand (the residual, or h), rows 64 s .. 64 s + 63
+// into ring stage s as the ring drains (see NoDrain); the caller loads rows 192 .. 255 after the mainloop.
+struct TileRowsDrain {
+  static constexpr int LOADS = 4;
+  const uint16_t* src;
+  int ld, m0, n0, M;
+  char* smem;
+  __device__ void operator()(int s) const { load_tile_rows64<32>(src, ld, m0, n0, M, smem, 64 * s); }
+};
 
 // Maps the linear workgroup id to a (row tile, column tile) pair.
 // Workgroups are dealt to the 8 XCDs round-robin (id % 8), each XCD with its own L2.  The id is first

@@ -182,6 +182,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const uint16_t* B16 = (const uint16_t*)B;
     if (MODE == MODE_ROWSCALE_SWIGLU)
       gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, K, smem, acc, fold_hook);
+    else if (MODE == MODE_RES_PRMS)  // the residual tile's first 192 rows arrive as the ring drains
+      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
+                    TileRowsDrain{R, Nb, m0, tn * BN, M, smem});
     else
       gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook);
   }
@@ -229,8 +232,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     constexpr bool WRITE_HG = MODE == MODE_RES_PRMS && !FP8;
     const int n_base = tn * BN + wn * 64 + 4 * half;
     if (MODE == MODE_RES_PRMS) {
-      // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows)
-      load_tile_rows<32>(R, Nb, m0, tn * BN, M, smem);
+      // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows); the bf16
+      // mainloop has fetched rows 0 .. 191 as its ring drained
+      if (FP8)
+        load_tile_rows<32>(R, Nb, m0, tn * BN, M, smem);
+      else
+        load_tile_rows64<32>(R, Nb, m0, tn * BN, M, smem, 192);
       wait_barrier<0>();
     }
     // gamma of this lane's 4-column groups (the same for every row)
