@@ -92,6 +92,22 @@ __device__ __forceinline__ void store_half_tile(const char* srcl, uint16_t* dst,
   }
 }
 
+// The SwiGLU backward's first half tile of z (rows m0 .. m0+127): gate rows 0..63 and 64..127, then up rows
+// 0..63, into ring stages 0, 1, 2 as the mainloop drains (NoDrain in gemm_core.h); the staging layout is
+// load_half_tile's, gate at smem and up at smem + 64 KiB.
+struct SwigluDrain {
+  static constexpr int LOADS = 4;
+  const uint16_t* z;
+  int ldz, m0, n0, nb, M;
+  char* smem;
+  __device__ void operator()(int s) const {
+    if (s < 2)
+      load_tile_rows64<32>(z, ldz, m0, n0, M, smem, 64 * s);
+    else
+      load_tile_rows64<32>(z, ldz, m0, nb + n0, M, smem + 65536, 0);
+  }
+};
+
 struct RowsFrom {
   int64_t n0;
   __device__ int64_t operator()(int r) const { return n0 + r; }
@@ -140,7 +156,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
         }
     }
   } else if (BT) {
-    gemm_mainloop_nt(args.A, args.K, M, m0, args.B, args.K, RowsFrom{n0}, args.K, smem, acc);
+    if (MODE == BWD_SWIGLU)  // the first half tile of z arrives as the ring drains (SwigluDrain)
+      gemm_mainloop_nt(args.A, args.K, M, m0, args.B, args.K, RowsFrom{n0}, args.K, smem, acc,
+                       SwigluDrain{args.h, 2 * Nb, m0, n0, Nb, M, smem});
+    else
+      gemm_mainloop_nt(args.A, args.K, M, m0, args.B, args.K, RowsFrom{n0}, args.K, smem, acc);
   } else {
     // split K: workgroup row blockIdx.y multiplies K range [y K, (y + 1) K) of the gridDim.y K ranges
     const int64_t k0 = (int64_t)blockIdx.y * args.K;
@@ -310,8 +330,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
     const int ldz = 2 * Nb;
 #pragma unroll 1
     for (int hh = 0; hh < 2; ++hh) {
-      load_half_tile(args.h, ldz, m0 + 128 * hh, n0, M, smem);
-      load_half_tile(args.h, ldz, m0 + 128 * hh, Nb + n0, M, smem + 65536);
+      if (hh == 0) {  // the mainloop's drain has fetched gate rows 0 .. 127 and up rows 0 .. 63
+        load_tile_rows64<32>(args.h, ldz, m0, Nb + n0, M, smem + 65536, 64);
+      } else {
+        load_half_tile(args.h, ldz, m0 + 128 * hh, n0, M, smem);
+        load_half_tile(args.h, ldz, m0 + 128 * hh, Nb + n0, M, smem + 65536);
+      }
       wait_barrier<0>();
       if (wm == hh) {
 #pragma unroll

@@ -292,10 +292,10 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
 // an [in,out] weight).  The B stage then has the A stage's layout (tile row = output column, 64-byte rows,
 // the same swizzle) and is read with ds_read_b128 like A.  brow(r) = global row of Bt that feeds tile-local
 // output column r (0..255).
-template <class BRow>
+template <class BRow, class Drain = NoDrain>
 __device__ __forceinline__ void gemm_mainloop_nt(const uint16_t* __restrict__ A, int64_t lda, int M, int m0,
                                                  const uint16_t* __restrict__ Bt, int64_t ldbt, BRow brow, int K,
-                                                 char* smem, f32x16 (&acc)[4][NB]) {
+                                                 char* smem, f32x16 (&acc)[4][NB], Drain drain = Drain{}) {
   constexpr int LPW = 16 / NWAVES;
   constexpr int PER = 2 * LPW;
   const int t = threadIdx.x;
@@ -347,10 +347,11 @@ __device__ __forceinline__ void gemm_mainloop_nt(const uint16_t* __restrict__ A,
     for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + k0, st + A_BYTES + (LPW * wave + i) * 1024);
   };
   Frags f0, f1;
-  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c) {
+  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c, auto drain_c) {
     constexpr int U = decltype(U_c)::value;
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr int WAIT = decltype(wait_c)::value;
+    constexpr int DRAIN = decltype(drain_c)::value;
     const char* cur = smem + U * STAGE_BYTES;
     if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
     rd(cur, 1, f1);
@@ -358,6 +359,7 @@ __device__ __forceinline__ void gemm_mainloop_nt(const uint16_t* __restrict__ A,
     interleave_mma_reads();
     if (WAIT >= 0) {
       wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
+      if (DRAIN >= 0 && Drain::LOADS > 0) drain(DRAIN);
       rd(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, 0, f0);
     }
     mma(f1, acc);
@@ -374,19 +376,23 @@ __device__ __forceinline__ void gemm_mainloop_nt(const uint16_t* __restrict__ A,
   for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
   wait_barrier<2 * PER>();
   rd(smem, 0, f0);
+  using NoD = std::integral_constant<int, -1>;
+  constexpr int DL = Drain::LOADS;
+  static_assert(PER + DL < 64 && 2 * DL < 64, "vmcnt range");
   const int nblk = nk / NSTAGE;
   for (int bi = 0; bi < nblk - 1; ++bi) {
     const int kt = bi * NSTAGE;
-    step(kt + 0, S0{}, Yes{}, WaitFull{});
-    step(kt + 1, S1{}, Yes{}, WaitFull{});
-    step(kt + 2, S2{}, Yes{}, WaitFull{});
-    step(kt + 3, S3{}, Yes{}, WaitFull{});
+    step(kt + 0, S0{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 1, S1{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 2, S2{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 3, S3{}, Yes{}, WaitFull{}, NoD{});
   }
+  // the last block with the drain (as in gemm_mainloop)
   const int kt = (nblk - 1) * NSTAGE;
-  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{});
-  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER>{});
-  step(kt + 2, S2{}, No{}, std::integral_constant<int, 0>{});
-  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
+  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{}, S0{});
+  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER + DL>{}, S1{});
+  step(kt + 2, S2{}, No{}, std::integral_constant<int, 2 * DL>{}, S2{});
+  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{}, NoD{});
 }
 
 // ======================================================================================================
