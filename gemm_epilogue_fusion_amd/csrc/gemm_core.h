@@ -9,13 +9,15 @@
 // rows 128 (w % 2) .. +128 and columns 64 (w / 2) .. +64 as 4 x 2 blocks of 32 x 32 fp32 accumulators
 // (128 registers per lane).
 //
-// Operands: A [M,K] row-major (K contiguous); B [K,N] row-major (N contiguous), the layout weights are
-// stored in.  K advances 32 at a time through a ring of 4 LDS stages (4 x 32 KiB): stage k+3 is fetched
+// Operands: A [M,K] row-major (K contiguous), or in K panels of the stage width (ALayout below); B [K,N]
+// row-major (N contiguous), the layout weights are stored in.  K advances 32 at a time through a ring of 4 LDS
+// stages (4 x 32 KiB): stage k+3 is fetched
 // while stage k is multiplied, with global_load_lds_dwordx4 (global memory straight into LDS, no VGPR
 // staging), so each tile's loads have three K steps of latency budget.  One barrier per K step, placed
 // half-way so that the next step's first fragments are read from LDS while the current step's last
 // MFMAs run.  The barrier carries no memory fence: the wait is an explicit vmcnt for the stage about to be
-// read, which keeps the later stages' loads in flight.
+// read, which keeps the later stages' loads in flight.  As the ring drains in the last K steps, the freed
+// stages can take the epilogue's own operand tile (the drain hook).
 //
 // B stays N-contiguous in LDS and is read K-contiguous with ds_read_b64_tr_b16 (the gfx950 transposing
 // LDS read), so the weights need no transpose pass.  The MFMA (v_mfma_f32_32x32x16_bf16) takes the B

@@ -9,7 +9,8 @@
 //   K3 gemm2_rowscale : mainloop on h * gamma against W2, i.e. h (diag(gamma) W2); the epilogue applies r
 //                       (a per-row scalar commutes with the product) and SwiGLU
 // With e4m3 operands K1 stores h only, and K2 (prms_reduce_quant) forms h * gamma from the stored h and
-// quantises it per row for K3.
+// quantises it per row for K3.  Inside the block, h * gamma (or its codes) is written in K panels of K3's
+// stage width (ALayout in gemm_core.h) and K2 is folded into K3 where D <= 4096 (RowFold).
 // Unfused baseline (three operators whose intermediates round-trip HBM, the pattern the same section
 // describes as the conventional one):
 //   U1 gemm_store     : T = bf16(X W1)
