@@ -556,10 +556,16 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __r
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = ty; i < 64; i += 4) tile[i][tx] = src[(int64_t)(r0 + i) * C + c0 + tx];
+  for (int j = 0; j < 16; ++j) {
+    const int i = ty + 4 * j;
+    tile[i][tx] = src[(int64_t)(r0 + i) * C + c0 + tx];
+  }
   __syncthreads();
 #pragma unroll
-  for (int i = ty; i < 64; i += 4) dst[(int64_t)(c0 + i) * R + r0 + tx] = tile[tx][i];
+  for (int j = 0; j < 16; ++j) {
+    const int i = ty + 4 * j;
+    dst[(int64_t)(c0 + i) * R + r0 + tx] = tile[tx][i];
+  }
 }
 
 hipError_t launch_transpose_bf16(const uint16_t* src, int R, int C, uint16_t* dst, hipStream_t stream) {
