@@ -400,8 +400,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
 
 // B2: a_i = r_i^3 / D * sum_t part[t][i] (t in order), one thread per row; dgamma_j = sum_q part2[q][j], 32
 // lanes per column (each lane sums q = lane, lane + 32, ... in order, then a fixed butterfly).
-__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, int T, const float* __restrict__ part2,
-                                                         int Q, const float* __restrict__ r, int M, int D,
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(const float* __restrict__ part, int T,
+                                                         const float* __restrict__ part2, int Q,
+                                                         const float* __restrict__ r, int M, int D,
                                                          float* __restrict__ a, float* __restrict__ dgamma) {
   const int row_blocks = (M + 255) / 256;
   if ((int)blockIdx.x < row_blocks) {

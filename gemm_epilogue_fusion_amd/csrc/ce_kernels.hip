@@ -45,8 +45,8 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 __global__ __launch_bounds__(NTHREADS, 1) void ce_gemm_kernel(const uint16_t* __restrict__ H,
                                                              const uint16_t* __restrict__ W,
                                                              const int* __restrict__ labels, float* __restrict__ part_m,
-                                                             float* __restrict__ part_s, float* __restrict__ zlab, int M,
-                                                             int K, int V, int group_m, int a_panels) {
+                                                             float* __restrict__ part_s, float* __restrict__ zlab,
+                                                             int M, int K, int V, int group_m, int a_panels) {
   __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = V / BN;
@@ -216,8 +216,8 @@ hipError_t launch_ce_gemm(const uint16_t* H, const uint16_t* W, const int* label
 
 // dst = src [M, D] bf16 in K panels of 32 columns: src[m][32 p + j] -> dst[(p M + m) 32 + j].  A workgroup moves
 // 64 rows of one panel: each lane one 16-byte piece, so a workgroup writes 4 KiB of the panel contiguously.
-__global__ __launch_bounds__(256) void panelize_bf16_kernel(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
-                                                            int M, int D) {
+__global__ __launch_bounds__(256) void panelize_bf16_kernel(const uint16_t* __restrict__ src,
+                                                            uint16_t* __restrict__ dst, int M, int D) {
   const int p = blockIdx.x;
   const int r = blockIdx.y * 64 + (threadIdx.x >> 2);
   const int c4 = threadIdx.x & 3;

@@ -104,7 +104,7 @@ struct GateUpCols {
 // One GEMM with a programmable epilogue.  The accumulator tile covers 256 columns of B; A [M,K] and B
 // [K,Nb] are bf16 (FP8 = false) or e4m3 bytes (FP8 = true), row-major.  In the epilogue the accumulator is
 // first multiplied by rowsc[m] * colsc[n] where those are given (dequantisation scales and / or the row
-// scale r), giving v:
+// scale r; column scales exist for e4m3 operands only, so the bf16 kernels compile without them), giving v:
 //   MODE_RES_PRMS:  out [M,Nb] = bf16(v + R); out2 [M,Nb] = bf16((v + R) * gamma[n]) (bf16 operands only);
 //                   part[tn][m] = sum over the tile's columns of (v + R)^2
 //   MODE_STORE:     out [M,Nb] = bf16(v)
@@ -260,7 +260,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq)
-          cv[nb][gq] = colsc ? *(const f32x4*)(colsc + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+          cv[nb][gq] = (FP8 && colsc) ? *(const f32x4*)(colsc + n_base + nb * 32 + 8 * gq)
+                                      : (f32x4){1.f, 1.f, 1.f, 1.f};
       float s = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -416,8 +417,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
             hi[e] = b;
           }
         }
-        *(u32x2*)(smem + tile_off<32>(r, wn * 8 + gq) + 8 * half) = (u32x2){pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])};
-        *(u32x2*)(smem + tile_off<32>(r, wn * 8 + 4 + gq) + 8 * half) = (u32x2){pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])};
+        *(u32x2*)(smem + tile_off<32>(r, wn * 8 + gq) + 8 * half) =
+            (u32x2){pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3])};
+        *(u32x2*)(smem + tile_off<32>(r, wn * 8 + 4 + gq) + 8 * half) =
+            (u32x2){pack_bf16(hi[0], hi[1]), pack_bf16(hi[2], hi[3])};
       }
     }
     __syncthreads();
@@ -432,8 +435,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       f32x4 cg[4], cu[4];
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        cg[gq] = colsc ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
-        cu[gq] = colsc ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+        cg[gq] = (FP8 && colsc) ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+        cu[gq] = (FP8 && colsc) ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
       }
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
@@ -460,15 +463,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         const float sc = rsv[mb];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 cg = colsc ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
-          const f32x4 cu = colsc ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+          const f32x4 cg = (FP8 && colsc) ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+          const f32x4 cu = (FP8 && colsc) ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
           float g[4], u[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             g[e] = acc[mb][0][4 * gq + e] * sc * cg[e];
             u[e] = acc[mb][1][4 * gq + e] * sc * cu[e];
           }
-          *(u32x2*)(smem + tile_off<16>(r, wn * 4 + gq) + 8 * half) = (u32x2){pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
+          *(u32x2*)(smem + tile_off<16>(r, wn * 4 + gq) + 8 * half) =
+              (u32x2){pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3])};
           *(u32x2*)(smem + 65536 + tile_off<16>(r, wn * 4 + gq) + 8 * half) =
               (u32x2){pack_bf16(u[0], u[1]), pack_bf16(u[2], u[3])};
         }
