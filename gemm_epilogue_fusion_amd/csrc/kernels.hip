@@ -219,7 +219,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
-      rsv[mb] = rowsc ? rowsc[m < M ? m : M - 1] : 1.0f;
+      // row scales: the e4m3 dequantisation scales, or r in the row-scale modes (bf16 GEMM1 and plain stores
+      // have none, so their kernels compile without the load)
+      rsv[mb] = ((FP8 || ROWSCALE_MODE) && rowsc) ? rowsc[m < M ? m : M - 1] : 1.0f;
     }
   }
   __syncthreads();  // every wave is done with the mainloop's LDS stages (and the folded row scales are in)
