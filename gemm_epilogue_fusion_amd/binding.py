@@ -29,7 +29,8 @@ EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_wo
            "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
            "coda_gemm1_residual_partial_rms_panels", "coda_gemm2_rowscale_panels",
-           "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_fwd_rope",
+           "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_bwd_w2t",
+           "coda_block_fwd_rope",
            "coda_rope_rows", "coda_ce_workspace_bytes", "coda_ce_fwd", "coda_ce_unfused",
            "coda_block_fwd_save_z", "coda_swiglu_bwd_workspace_bytes", "coda_swiglu_bwd", "coda_swiglu_bwd_unfused")
 
@@ -81,7 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.coda_rope_rows.argtypes, lib.coda_rope_rows.restype = [vp, i64, i64, i64, i64, f32, vp], i32
     lib.coda_bwd_workspace_bytes.argtypes, lib.coda_bwd_workspace_bytes.restype = [i64, i64, i64, i64, i32], sz
     bwd = [vp] * 13 + [i64, i64, i64, i64, vp, sz, vp]
-    for name in ("coda_block_bwd", "coda_block_bwd_unfused"):
+    for name in ("coda_block_bwd", "coda_block_bwd_unfused", "coda_block_bwd_w2t"):
         getattr(lib, name).argtypes = bwd
         getattr(lib, name).restype = i32
     lib.coda_ce_workspace_bytes.argtypes, lib.coda_ce_workspace_bytes.restype = [i64, i64, i64, i32], sz
@@ -310,14 +311,14 @@ def alloc_bwd_workspace(M: int, K1: int, D: int, N2: int, unfused: int = 0, devi
 
 
 def _block_bwd(name, X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, workspace,
-               stream):
+               stream, w2_transposed=False):
     M, K1 = X.shape
     D = W1.shape[1]
-    N2 = W2.shape[1]
+    N2 = W2.shape[0] if w2_transposed else W2.shape[1]
     bf = torch.bfloat16
     args = (_dev(X, "X", bf, (M, K1)), _dev(W1, "W1", bf, (K1, D)), _dev(h, "h", bf, (M, D)),
             _dev(r, "r", torch.float32, (M,)), _dev(gamma, "gamma", torch.float32, (D,)),
-            _dev(W2, "W2", bf, (D, N2)), _dev(dz, "dz", bf, (M, N2)),
+            _dev(W2, "W2t", bf, (N2, D)) if w2_transposed else _dev(W2, "W2", bf, (D, N2)), _dev(dz, "dz", bf, (M, N2)),
             None if dh_out is None else _dev(dh_out, "dh_out", bf, (M, D)),
             _dev(out_dX, "out_dX", bf, (M, K1)), _dev(out_dW1, "out_dW1", torch.float32, (K1, D)),
             _dev(out_dR, "out_dR", bf, (M, D)), _dev(out_dgamma, "out_dgamma", torch.float32, (D,)),
@@ -333,6 +334,14 @@ def coda_block_bwd(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, 
     product's output) and dh_out (gradient arriving at h; None for none), with h and r from the forward."""
     _block_bwd("coda_block_bwd", X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2,
                workspace, stream)
+
+
+def coda_block_bwd_w2t(X, W1, h, r, gamma, W2t, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, workspace,
+                       stream=None):
+    """coda_block_bwd with W2 given transposed (W2t [N2, D], the [out, in] layout): the same results, without
+    the transpose pass over W2."""
+    _block_bwd("coda_block_bwd_w2t", X, W1, h, r, gamma, W2t, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma,
+               out_dW2, workspace, stream, w2_transposed=True)
 
 
 def coda_block_bwd_unfused(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2,

@@ -624,8 +624,9 @@ size_t coda_bwd_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, in
 static int block_bwd(const void* X, const void* W1, const void* h, const float* r, const float* gamma, const void* W2,
                      const void* dz, const void* dh_out, void* out_dX, float* out_dW1, void* out_dR,
                      float* out_dgamma, float* out_dW2, int64_t M, int64_t K1, int64_t D, int64_t N2,
-                     void* workspace, size_t workspace_bytes, void* stream, int unfused) {
+                     void* workspace, size_t workspace_bytes, void* stream, int unfused, int w2_transposed = 0) {
   try {
+    // w2_transposed: the caller passes W2^T [N2,D] in W2's place (same size, same checks) and B0 is skipped
     int s = validate_bwd(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, M, K1, D,
                          N2, workspace, workspace_bytes, unfused);
     if (s) return s;
@@ -634,20 +635,23 @@ static int block_bwd(const void* X, const void* W1, const void* h, const float* 
     carve_bwd(workspace, M, K1, D, N2, unfused, &w);
     const uint16_t* hh = (const uint16_t*)h;
     // the first product reads W2 K-major: transpose it once (a [D,N2] -> [N2,D] pass, HBM-bound) so that the
-    // product runs on the NN mainloop, which fetches whole 512-byte weight rows per stage
-    if ((s = hip_check(coda::launch_transpose_bf16((const uint16_t*)W2, (int)D, (int)N2, w.W2T, st),
+    // product runs on the NN mainloop, which fetches whole 512-byte weight rows per stage; a caller that holds
+    // W2^T already (weights kept [out,in]) passes it instead
+    const uint16_t* W2T = w2_transposed ? (const uint16_t*)W2 : w.W2T;
+    if (!w2_transposed &&
+        (s = hip_check(coda::launch_transpose_bf16((const uint16_t*)W2, (int)D, (int)N2, w.W2T, st),
                        "bwd W2 transpose launch")))
       return s;
     if (unfused) {
       // P = dz W2^T stored, then its row and column statistics in a separate pass
-      if ((s = hip_check(coda::launch_gemm_nn_store((const uint16_t*)dz, w.W2T, w.P, (int)M, (int)N2, (int)D, st),
+      if ((s = hip_check(coda::launch_gemm_nn_store((const uint16_t*)dz, W2T, w.P, (int)M, (int)N2, (int)D, st),
                          "bwd P launch")))
         return s;
       if ((s = hip_check(coda::launch_bwd_p_from_mem(w.P, hh, r, gamma, w.G, w.part, w.part2, (int)M, (int)D, st),
                          "bwd P statistics launch")))
         return s;
     } else {
-      if ((s = hip_check(coda::launch_bwd_p_nn((const uint16_t*)dz, w.W2T, hh, r, gamma, w.G, w.part, w.part2,
+      if ((s = hip_check(coda::launch_bwd_p_nn((const uint16_t*)dz, W2T, hh, r, gamma, w.G, w.part, w.part2,
                                                (int)M, (int)D, (int)N2, st),
                          "bwd P launch")))
         return s;
@@ -682,6 +686,14 @@ int coda_block_bwd(const void* X, const void* W1, const void* h, const float* r,
                    size_t workspace_bytes, void* stream) {
   return block_bwd(X, W1, h, r, gamma, W2, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, M, K1, D, N2,
                    workspace, workspace_bytes, stream, 0);
+}
+
+int coda_block_bwd_w2t(const void* X, const void* W1, const void* h, const float* r, const float* gamma,
+                       const void* W2t, const void* dz, const void* dh_out, void* out_dX, float* out_dW1, void* out_dR,
+                       float* out_dgamma, float* out_dW2, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return block_bwd(X, W1, h, r, gamma, W2t, dz, dh_out, out_dX, out_dW1, out_dR, out_dgamma, out_dW2, M, K1, D, N2,
+                   workspace, workspace_bytes, stream, 0, 1);
 }
 
 int coda_block_bwd_unfused(const void* X, const void* W1, const void* h, const float* r, const float* gamma,

@@ -227,6 +227,15 @@ int coda_block_bwd(const void* X, const void* W1, const void* h, const float* r,
                    float* out_dW2, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* coda_block_bwd with W2 given transposed: W2t is W2^T [N2,D] bf16 row-major (the [out,in] layout in which
+ * many frameworks keep their weights) in W2's place; the other arguments, the checks (W2t has W2's size), the
+ * workspace and the results are coda_block_bwd's, bit for bit.  The transpose pass over W2 that
+ * coda_block_bwd makes first (a read and a write of D * N2 * 2 bytes) is skipped. */
+int coda_block_bwd_w2t(const void* X, const void* W1, const void* h, const float* r, const float* gamma,
+                       const void* W2t, const void* dz, const void* dh_out, void* out_dX, float* out_dW1, void* out_dR,
+                       float* out_dgamma, float* out_dW2, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* The unfused backward baseline: P = dz W2^T is stored (bf16) and its RMSNorm-backward statistics are
  * computed by a separate pass over P and h; the remaining kernels are shared.  Same arguments and outputs;
  * workspace: coda_bwd_workspace_bytes(..., unfused = 1). */

@@ -220,7 +220,7 @@ def _bcall(lib, a, fn="coda_block_bwd"):
                             a["ws_bytes"], None)
 
 
-@pytest.mark.parametrize("fn", ["coda_block_bwd", "coda_block_bwd_unfused"])
+@pytest.mark.parametrize("fn", ["coda_block_bwd", "coda_block_bwd_unfused", "coda_block_bwd_w2t"])
 @pytest.mark.parametrize("case,over,want", [
     ("null_dz", dict(dz=0), INVALID),
     ("null_out_dW2", dict(dW2=0), INVALID),

@@ -50,7 +50,7 @@ def _check(name, got, want):
     return err
 
 
-def _run(wl, unfused=False, with_dh_out=True):
+def _run(wl, unfused=False, with_dh_out=True, w2t=False):
     inp = make_inputs(wl)
     dz, dho = make_grads(wl)
     dev = "cuda"
@@ -69,8 +69,12 @@ def _run(wl, unfused=False, with_dh_out=True):
                 dW2=torch.full((wl.D, wl.N2), float("nan"), dtype=torch.float32, device=dev))
     wsb = cb.alloc_bwd_workspace(wl.M, wl.K1, wl.D, wl.N2, unfused=int(unfused), device=dev)
     wsb.fill_(0xFF)
-    fn = cb.coda_block_bwd_unfused if unfused else cb.coda_block_bwd
-    fn(X, W1, h, r, g, W2, dzd, dhd, outs["dX"], outs["dW1"], outs["dR"], outs["dgamma"], outs["dW2"], wsb)
+    if w2t:  # W2 handed over as W2^T [N2, D]
+        cb.coda_block_bwd_w2t(X, W1, h, r, g, W2.t().contiguous(), dzd, dhd, outs["dX"], outs["dW1"], outs["dR"],
+                              outs["dgamma"], outs["dW2"], wsb)
+    else:
+        fn = cb.coda_block_bwd_unfused if unfused else cb.coda_block_bwd
+        fn(X, W1, h, r, g, W2, dzd, dhd, outs["dX"], outs["dW1"], outs["dR"], outs["dgamma"], outs["dW2"], wsb)
     torch.cuda.synchronize()
     return inp, dz, (dho if with_dh_out else None), {k: v.float().cpu().numpy() for k, v in outs.items()}
 
@@ -100,6 +104,17 @@ def test_bwd_without_dh_out():
     want = oracle.block_bwd(f64(inp.X), f64(inp.W1), f64(inp.R), f64(inp.gamma), f64(inp.W2), wl.eps, f64(dz), None)
     for name, w in zip(("dX", "dW1", "dR", "dgamma", "dW2"), want):
         _check(name, got[name], w)
+
+
+@pytest.mark.parametrize("wl", SMALL[:2], ids=[w.name for w in SMALL[:2]])
+def test_bwd_w2t_equals_bwd(wl):
+    """coda_block_bwd_w2t on W2^T gives coda_block_bwd's outputs bit for bit (the same kernels after the
+    transpose that it skips)."""
+    _say(f"[gpu] bwd with W2^T {wl}")
+    _, _, _, a = _run(wl)
+    _, _, _, b = _run(wl, w2t=True)
+    for name in ("dX", "dW1", "dR", "dgamma", "dW2"):
+        assert np.array_equal(a[name].view(np.uint32), b[name].view(np.uint32)), name
 
 
 def test_bwd_full_size_sampled_rows():
