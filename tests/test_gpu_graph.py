@@ -1,7 +1,8 @@
-"""The entry points under HIP graph capture (torch.cuda.CUDAGraph): a captured block, replayed several times
-with other eager GPU work and synchronisations in between, gives the eager result bit for bit on every
-replay, and follows new data copied into its static inputs.  The library enqueues only kernels (no memset,
-no allocation, no host synchronisation), which is what makes a call capturable.
+"""The entry points under HIP graph capture (torch.cuda.CUDAGraph) and on concurrent streams.  A captured
+block, replayed several times with other eager GPU work and synchronisations in between, gives the eager
+result bit for bit on every replay, and follows new data copied into its static inputs.  The library enqueues
+only kernels (no memset, no allocation, no host synchronisation), which is what makes a call capturable.  Two
+blocks in flight on two streams with their own workspaces give what each gives alone.
 """
 import sys
 
@@ -121,3 +122,33 @@ def test_backward_graph_replays_match_eager():
         torch.cuda.synchronize()
         for o, ref in zip(outs, refs):
             assert torch.equal(_bits(o), _bits(ref)), f"replay {i}: a gradient differs from the eager call"
+
+
+def test_concurrent_streams_distinct_workspaces():
+    """Two blocks in flight at once on two streams, each with its own workspace (the documented condition for
+    concurrent calls), give the results each gives alone, bit for bit."""
+    wls = [Workload("stream_a", M=513, K1=256, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=31),
+           Workload("stream_b", M=300, K1=384, D=768, N2=512, epi=0, eps=1e-5, seed=32)]
+    _say("[gpu] two streams " + ", ".join(w.name for w in wls))
+    runs = []
+    for wl in wls:
+        d = DeviceInputs(make_inputs(wl))
+        dev = d.X.device
+        ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev)
+        outs = [(torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev),
+                 torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)) for _ in range(2)]
+        runs.append((wl, d, ws, outs))
+    for wl, d, ws, outs in runs:  # alone, one after the other
+        cb.coda_block_fwd(d.X, d.W1, d.R, d.gamma, d.W2, wl.eps, wl.epi, outs[0][0], outs[0][1], ws)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in runs]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):  # interleaved launches on the two streams
+        for s, (wl, d, ws, outs) in zip(streams, runs):
+            with torch.cuda.stream(s):
+                cb.coda_block_fwd(d.X, d.W1, d.R, d.gamma, d.W2, wl.eps, wl.epi, outs[1][0], outs[1][1], ws)
+    torch.cuda.synchronize()
+    for wl, d, ws, outs in runs:
+        assert torch.equal(_bits(outs[0][0]), _bits(outs[1][0])), wl.name
+        assert torch.equal(_bits(outs[0][1]), _bits(outs[1][1])), wl.name
