@@ -215,9 +215,10 @@ int coda_gemm2_rowscale_panels(const void* hg, const void* W2, const float* part
  * Inputs: X [M,K1] bf16, W1 [K1,D] bf16, h [M,D] bf16 and r [M] fp32 as the forward left them (out_h and
  * the workspace's r), gamma [D] fp32, W2 [D,N2] bf16, dz [M,N2] bf16, dh_out [M,D] bf16 or NULL.
  * Outputs: out_dX [M,K1] bf16, out_dW1 [K1,D] fp32, out_dR [M,D] bf16, out_dgamma [D] fp32, out_dW2 [D,N2]
- * fp32.  Six kernels on `stream` (the fused path): P = dz W2^T with the RMSNorm-backward row and column
- * statistics in its epilogue, a light reduction, dh (and its transpose and n's), then the dX, dW1 and dW2
- * products.  Shape rules: M a multiple of 128, K1 a multiple of 256, D and N2 multiples of 256.  No output
+ * fp32.  Kernels on `stream` (the fused path): W2's transpose (see coda_block_bwd_w2t), P = dz W2^T with the
+ * RMSNorm-backward row and column statistics in its epilogue, a light reduction, dh (and its transpose and
+ * n's), then the dX, dW1 and dW2 products (the weight gradients split along M into fp32 slabs, summed by a
+ * small kernel, where their output has few tiles).  Shape rules: M a multiple of 128, K1 a multiple of 256, D and N2 multiples of 256.  No output
  * may overlap an input or another output.  Workspace: coda_bwd_workspace_bytes(..., unfused = 0); other
  * conventions as the forward entry points. */
 size_t coda_bwd_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused);
