@@ -489,20 +489,29 @@ def main() -> int:
         "hbm_bytes": {"fused_algorithmic": fb, "unfused_algorithmic": ub, "saved_algorithmic": ub - fb},
         "kernel_source_hash": src_hash,
     }
+    def extra(key, fn):
+        # the further measurements: a Python-level failure in one of them (an error status from the library,
+        # an allocation failure) is recorded under its key and the line is still printed with the headline
+        try:
+            line[key] = fn()
+        except Exception as e:  # noqa: BLE001
+            print(f"bench: {key} failed: {e!r}", file=sys.stderr, flush=True)
+            line[key] = {"error": repr(e)}
+
     if not args.no_bwd:
-        line["backward"] = time_bwd(wl, X, W1, g, W2, h, ws, n_ev, args.warmup, torch, cb)
+        extra("backward", lambda: time_bwd(wl, X, W1, g, W2, h, ws, n_ev, args.warmup, torch, cb))
     if not args.no_fp8:
-        line["fp8"] = time_fp8(dev, n_ev, args.warmup, torch, cb)
+        extra("fp8", lambda: time_fp8(dev, n_ev, args.warmup, torch, cb))
     if not args.no_rope:
-        line["rope"] = time_rope(dev, n_ev, args.warmup, torch, cb)
+        extra("rope", lambda: time_rope(dev, n_ev, args.warmup, torch, cb))
     if not args.no_ce:
-        line["ce"] = time_ce(dev, n_ev, args.warmup, torch, cb)
+        extra("ce", lambda: time_ce(dev, n_ev, args.warmup, torch, cb))
     if not args.no_swiglu and wl.epi == 1:
-        line["swiglu"] = time_swiglu(wl, X, W1, R, g, W2, dev, n_ev, args.warmup, torch, cb)
+        extra("swiglu", lambda: time_swiglu(wl, X, W1, R, g, W2, dev, n_ev, args.warmup, torch, cb))
     if not args.no_tiny:
-        line["tiny"] = time_tiny(dev, torch, cb)
+        extra("tiny", lambda: time_tiny(dev, torch, cb))
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, inp)
+        extra("cpu_baseline", lambda: cpu_baseline(wl, inp))
     print(json.dumps(line))
     return 0
 
