@@ -72,6 +72,11 @@ def _call(lib, a, fn="coda_block_fwd"):
     ("K1_not_128", dict(K1=192), UNSUPPORTED),
     ("D_not_256", dict(D=320), UNSUPPORTED),
     ("N2_not_256", dict(N2=384), UNSUPPORTED),
+    # largest sizes: each dimension at most 2^30, each matrix at most 2^31 elements (32-bit row and element
+    # indices in the kernels), checked before any pointer range is formed
+    ("M_above_2e30", dict(M=(1 << 30) + 1), UNSUPPORTED),
+    ("y_above_2e31_elements", dict(M=1 << 20, N2=1 << 12), UNSUPPORTED),
+    ("W2_above_2e31_elements", dict(D=1 << 16, N2=1 << 16), UNSUPPORTED),
     ("bad_epi", dict(epi=7), INVALID),
     ("eps_negative", dict(eps=-1.0), INVALID),
     ("eps_nan", dict(eps=float("nan")), INVALID),
