@@ -232,3 +232,22 @@ def test_full_size_sampled_rows(name):
     check_h(f64(h[rows]), oh)
     check_y(f64(y[rows]), oy)
     np.testing.assert_allclose(f64(r[rows]), orr, rtol=2e-5)
+
+
+def test_largest_output_sampled_rows():
+    """y at the largest size the ABI accepts, 2^31 elements (65536 x 32768 bf16, 4 GiB): byte offsets past
+    2^32 in the stores, 32768 second-GEMM tiles.  Checked against the oracle on sampled rows, the last ones
+    among them, and for finiteness everywhere."""
+    wl = Workload("largest_y", M=65536, K1=128, D=256, N2=32768, epi=EPI_IDENTITY, eps=1e-5, seed=12)
+    _say(f"[gpu] largest output {wl}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h, y, r = run_block(d)
+    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(h).all()), "unwritten or non-finite output"
+    rows = sample_rows(wl.M, n=16)
+    idx = torch.as_tensor(rows, dtype=torch.long, device=y.device)
+    oh, orr, oy = oracle_rows(inp, rows)
+    check_h(f64(h[idx]), oh)
+    check_y(f64(y[idx]), oy)
+    np.testing.assert_allclose(f64(r[rows]), orr, rtol=2e-5)
+
