@@ -235,9 +235,9 @@ def test_full_size_sampled_rows(name):
 
 
 def test_largest_output_sampled_rows():
-    """y at the largest size the ABI accepts, 2^31 elements (65536 x 32768 bf16, 4 GiB): byte offsets past
-    2^32 in the stores, 32768 second-GEMM tiles.  Checked against the oracle on sampled rows, the last ones
-    among them, and for finiteness everywhere."""
+    """y at the largest size the ABI accepts, 2^31 elements (65536 x 32768 bf16, 4 GiB): store offsets up to
+    2^32 - 2 bytes (past any signed 32-bit offset), 32768 second-GEMM tiles.  Checked against the oracle on
+    sampled rows, the last ones among them, and for finiteness everywhere."""
     wl = Workload("largest_y", M=65536, K1=128, D=256, N2=32768, epi=EPI_IDENTITY, eps=1e-5, seed=12)
     _say(f"[gpu] largest output {wl}")
     inp = make_inputs(wl)
