@@ -87,6 +87,11 @@ def _load():
     lib.oracle_mx_quant_rows_e4m3.argtypes = [i64, i64, i64, dp, ctypes.POINTER(ctypes.c_uint8),
                                               ctypes.POINTER(ctypes.c_int32)]
     lib.oracle_mx_quant_rows_e4m3.restype = ctypes.c_int
+    for name, argt in (("oracle_bf16_round_array", [i64, dp, dp]),
+                       ("oracle_e4m3_encode_array", [i64, dp, ctypes.POINTER(ctypes.c_uint8)]),
+                       ("oracle_e4m3_decode_array", [i64, ctypes.POINTER(ctypes.c_uint8), dp])):
+        getattr(lib, name).argtypes = argt
+        getattr(lib, name).restype = ctypes.c_int
     lib.oracle_default_threads.argtypes = []
     lib.oracle_default_threads.restype = ctypes.c_int
     _lib = lib
@@ -243,22 +248,28 @@ def silu(x: float) -> float:
 def bf16_round(x) -> np.ndarray:
     lib = _load()
     a = _f64(x)
-    out = np.fromiter((lib.oracle_bf16_round(float(v)) for v in a.ravel()), np.float64, a.size)
-    return out.reshape(a.shape)
+    out = np.empty(a.shape, np.float64)
+    if lib.oracle_bf16_round_array(a.size, _ptr(a), _ptr(out)) != 0:
+        raise RuntimeError("oracle_bf16_round_array failed")
+    return out
 
 
 def e4m3_decode(codes) -> np.ndarray:
     lib = _load()
-    c = np.asarray(codes, dtype=np.uint8)
-    out = np.fromiter((lib.oracle_e4m3_decode(int(v)) for v in c.ravel()), np.float64, c.size)
-    return out.reshape(c.shape)
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    if lib.oracle_e4m3_decode_array(c.size, _ptr(c, ctypes.c_uint8), _ptr(out)) != 0:
+        raise RuntimeError("oracle_e4m3_decode_array failed")
+    return out
 
 
 def e4m3_encode(x) -> np.ndarray:
     lib = _load()
     a = _f64(x)
-    out = np.fromiter((lib.oracle_e4m3_encode(float(v)) for v in a.ravel()), np.uint8, a.size)
-    return out.reshape(a.shape)
+    out = np.empty(a.shape, np.uint8)
+    if lib.oracle_e4m3_encode_array(a.size, _ptr(a), _ptr(out, ctypes.c_uint8)) != 0:
+        raise RuntimeError("oracle_e4m3_encode_array failed")
+    return out
 
 
 def dequant_rows_e4m3(q, s) -> np.ndarray:

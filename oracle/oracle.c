@@ -93,6 +93,25 @@ uint8_t oracle_e4m3_encode(double x) {
   return sign | (uint8_t)(((lead + 7) << 3) | mant);
 }
 
+/* The three codecs above applied element by element to arrays (the same scalar functions in a loop). */
+int oracle_bf16_round_array(int64_t n, const double* x, double* out) {
+  if (n < 0 || (n && (!x || !out))) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_round(x[i]);
+  return 0;
+}
+
+int oracle_e4m3_encode_array(int64_t n, const double* x, uint8_t* out) {
+  if (n < 0 || (n && (!x || !out))) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_encode(x[i]);
+  return 0;
+}
+
+int oracle_e4m3_decode_array(int64_t n, const uint8_t* q, double* out) {
+  if (n < 0 || (n && (!q || !out))) return -1;
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3_decode(q[i]);
+  return 0;
+}
+
 int oracle_dequant_rows_e4m3(int64_t rows, int64_t cols, const uint8_t* q, const float* s, double* out) {
   if (rows < 0 || cols < 0 || !q || !s || !out) return -1;
   for (int64_t i = 0; i < rows; ++i)
@@ -602,19 +621,29 @@ int oracle_mx_quant_rows_e4m3(int64_t rows, int64_t cols, int64_t block, const d
  *   du = dy * silu(g)
  * and dz = [dg | du] [M, 2F].
  */
+typedef struct {
+  int64_t F, D;
+  const double *dout, *Wd, *z;
+  double* dz;
+} swiglu_bwd_ctx;
+
+static void swiglu_bwd_row(void* p, int64_t i, double* scratch) {
+  swiglu_bwd_ctx* c = (swiglu_bwd_ctx*)p;
+  (void)scratch;
+  const int64_t F = c->F, D = c->D;
+  for (int64_t f = 0; f < F; ++f) {
+    double dy = 0.0;
+    for (int64_t d = 0; d < D; ++d) dy += c->dout[i * D + d] * c->Wd[f * D + d];
+    const double g = c->z[i * 2 * F + f], u = c->z[i * 2 * F + F + f];
+    const double s = 1.0 / (1.0 + exp(-g));
+    c->dz[i * 2 * F + f] = dy * u * s * (1.0 + g * (1.0 - s));
+    c->dz[i * 2 * F + F + f] = dy * g * s;
+  }
+}
+
 int oracle_swiglu_bwd_f64(int64_t M, int64_t F, int64_t D, const double* dout, const double* Wd, const double* z,
                           double* out_dz, int nthreads) {
-  (void)nthreads;
   if (M < 0 || F <= 0 || D <= 0 || !dout || !Wd || !z || !out_dz) return -1;
-  for (int64_t i = 0; i < M; ++i) {
-    for (int64_t f = 0; f < F; ++f) {
-      double dy = 0.0;
-      for (int64_t d = 0; d < D; ++d) dy += dout[i * D + d] * Wd[f * D + d];
-      const double g = z[i * 2 * F + f], u = z[i * 2 * F + F + f];
-      const double s = 1.0 / (1.0 + exp(-g));
-      out_dz[i * 2 * F + f] = dy * u * s * (1.0 + g * (1.0 - s));
-      out_dz[i * 2 * F + F + f] = dy * g * s;
-    }
-  }
-  return 0;
+  swiglu_bwd_ctx c = {F, D, dout, Wd, z, out_dz};
+  return for_each_row(M, nthreads, 0, swiglu_bwd_row, &c);
 }

@@ -119,6 +119,11 @@ double oracle_e4m3_decode(uint8_t code);
 /* Round to nearest e4m3fn, ties to even, saturating to +-448; NaN -> 0x7F. */
 uint8_t oracle_e4m3_encode(double x);
 
+/* The codecs above applied element by element to arrays of n values. */
+int oracle_bf16_round_array(int64_t n, const double* x, double* out);
+int oracle_e4m3_encode_array(int64_t n, const double* x, uint8_t* out);
+int oracle_e4m3_decode_array(int64_t n, const uint8_t* q, double* out);
+
 /* Dequantise e4m3 codes: per-row scales  out[i][k] = decode(q[i][k]) * s[i]   (activations)
  *                        per-column       out[k][n] = decode(q[k][n]) * s[n]   (weights)      */
 int oracle_dequant_rows_e4m3(int64_t rows, int64_t cols, const uint8_t* q, const float* s, double* out);

@@ -118,3 +118,111 @@ def sample_rows(M: int, n: int = 48, seed: int = 0) -> np.ndarray:
     picks = set(range(min(8, M))) | set(range(max(0, M - 8), M))
     picks |= set(int(v) for v in rng.choice(M, size=min(n, M), replace=False))
     return np.array(sorted(picks))
+
+
+def sample_rows_covering(M: int, n: int = 48, seed: int = 0) -> np.ndarray:
+    """sample_rows plus, for every 256-row tile, one row in each 128-row half, chosen so that the sample covers
+    every value of row % 32 (a lane's row inside a 32-row accumulator block) and every 32-row block of each half:
+    a tile placed wrongly, or a row mapping wrong inside a tile, cannot hide in unsampled rows."""
+    picks = set(int(v) for v in sample_rows(M, n, seed))
+    tiles = (M + 255) // 256
+    for t in range(tiles):
+        for half in (0, 1):
+            off = 128 * half + 32 * ((t + half) % 4) + (t + 16 * half) % 32
+            row = 256 * t + off
+            if row < M:
+                picks.add(row)
+    for res in range(32):  # every residue mod 32 at least once, whatever the tile count
+        if not any(p % 32 == res for p in picks):
+            cand = [m for m in range(res, M, 32)]
+            if cand:
+                picks.add(cand[(res * 7919) % len(cand)])
+    return np.array(sorted(picks))
+
+
+class Gauge:
+    """Running normwise and mean absolute errors of a result compared chunk by chunk of rows, so that every row
+    of a full-size output can be checked without holding the oracle's whole fp64 output at once."""
+
+    def __init__(self, what: str):
+        self.what = what
+        self.max_err = 0.0
+        self.max_ref = 0.0
+        self.sum_err = 0.0
+        self.n = 0
+
+    def add(self, g: np.ndarray, o: np.ndarray) -> None:
+        assert np.all(np.isfinite(g)), f"{self.what}: non-finite values"
+        d = np.abs(g - o)
+        if d.size:
+            self.max_err = max(self.max_err, float(d.max()))
+            self.max_ref = max(self.max_ref, float(np.abs(o).max()))
+            self.sum_err += float(d.sum())
+            self.n += d.size
+
+    def normwise(self) -> float:
+        return self.max_err / max(self.max_ref, 1e-30)
+
+    def mae_rel(self) -> float:
+        return self.sum_err / max(self.n, 1) / max(self.max_ref, 1e-30)
+
+
+def check_h_local(g: np.ndarray, o: np.ndarray) -> None:
+    """The elementwise half of check_h (|dh| <= 1e-2 |h| + 1e-2 rms(h_row)): a property of each row alone."""
+    rms = np.sqrt(np.mean(o * o, axis=1, keepdims=True))
+    bad = np.abs(g - o) > H_ELEM_REL * np.abs(o) + H_ELEM_REL * rms
+    assert not bad.any(), f"h: {int(bad.sum())} elements outside |dh| <= 1e-2|h| + 1e-2 rms(h_row)"
+
+
+def check_all_rows(M: int, h: torch.Tensor, y: torch.Tensor, r, oracle_chunk, fp8: bool = False,
+                   chunk: int = 1024, say=print, r_rtol: float = 2e-5) -> dict:
+    """Every row of a GPU result against the oracle, chunk by chunk (rows are independent, so the oracle can run
+    on row ranges).  h, y (bf16) and r (fp32, or None) are the GPU's results; oracle_chunk(a, b) returns a dict
+    with the oracle's 'h', 'y' (fp64) and optionally 'r' and 'y_rp' (the storage-rounding form) for rows a..b-1.
+    Applies the contract of check_h / check_y / check_roundpts to the whole output, and prints one progress line
+    per chunk."""
+    hc, yc = h.detach().cpu(), y.detach().cpu()
+    rc = r.detach().cpu() if r is not None else None
+    gh, gy, grp = Gauge("h"), Gauge("y"), Gauge("y vs storage-rounding oracle")
+    for a in range(0, M, chunk):
+        b = min(M, a + chunk)
+        o = oracle_chunk(a, b)
+        hg = f64(hc[a:b])
+        gh.add(hg, o["h"])
+        check_h_local(hg, o["h"])
+        yg = f64(yc[a:b])
+        gy.add(yg, o["y"])
+        if "y_rp" in o:
+            grp.add(yg, o["y_rp"])
+        if rc is not None and "r" in o:
+            np.testing.assert_allclose(f64(rc[a:b]), o["r"], rtol=r_rtol)
+        say(f"    rows {a}..{b - 1} of {M}: y normwise so far {gy.normwise():.3e}")
+    out = {"h_normwise": gh.normwise(), "y_normwise": gy.normwise(), "y_mae_rel": gy.mae_rel()}
+    assert out["h_normwise"] <= H_NORMWISE, f"h: normwise {out['h_normwise']:.3e} > {H_NORMWISE}"
+    lim = Y_NORMWISE_FP8 if fp8 else Y_NORMWISE
+    assert out["y_normwise"] <= lim, f"y: normwise max rel error {out['y_normwise']:.3e} > {lim}"
+    if not fp8:
+        assert out["y_mae_rel"] <= Y_MAE_REL, f"y: MAE/max|o| {out['y_mae_rel']:.3e} > {Y_MAE_REL}"
+    if grp.n:
+        out["rp_normwise"], out["rp_mae_rel"] = grp.normwise(), grp.mae_rel()
+        assert out["rp_normwise"] <= RP_NORMWISE, f"y vs storage-rounding oracle: normwise {out['rp_normwise']:.3e}"
+        assert out["rp_mae_rel"] <= RP_MAE_REL, f"y vs storage-rounding oracle: MAE/max {out['rp_mae_rel']:.3e}"
+    say("    all rows: " + ", ".join(f"{k} {v:.3e}" for k, v in out.items()))
+    return out
+
+
+def oracle_chunk_fn(inp: BlockInputs, roundpts: bool = True):
+    """oracle_chunk for check_all_rows on a bf16 workload: the fused fp64 form (h, r, y) and, if asked, the
+    storage-rounding form's y, for a row range."""
+    wl = inp.wl
+    W1, g, W2 = f64(inp.W1), f64(inp.gamma), f64(inp.W2)
+
+    def fn(a, b):
+        X, R = f64(inp.X[a:b]), f64(inp.R[a:b])
+        oh, orr, oy = oracle.block_fused(X, W1, R, g, W2, wl.eps, wl.epi)
+        out = {"h": oh, "r": orr, "y": oy}
+        if roundpts:
+            out["y_rp"] = oracle.block_roundpts(X, W1, R, g, W2, wl.eps, wl.epi)[2]
+        return out
+
+    return fn

@@ -3,9 +3,14 @@
 Each case runs the forward on the GPU (for h and r, as a caller would keep them), then the backward on the
 GPU, and compares dX, dW1, dR, dgamma and dW2 with oracle.block_bwd on the same bf16-valued inputs (the
 oracle recomputes h and r in fp64 from X, W1, R).  Bar: the bf16 contract of the forward, normwise max
-relative error <= 2e-2 and mean absolute error <= 1e-3 of max|o|.  At the 1B shape the row-local outputs
-(dX, dR) are compared on sampled rows; the weight gradients are covered by the smaller cases, which span
-several tiles in every dimension and a half-filled last row tile.
+relative error <= 2e-2 and mean absolute error <= 1e-3 of max|o|.
+
+The weight-gradient products split their K (= M) across workgroups when their output has few tiles, and sum
+the split parts in a second kernel; small cases reach splits of 2, 4 and 8.  At the 1B shape (dW1 split in 4)
+the weight gradients are compared element by element with a row mask: dz and dh_out are zero outside 256
+rows spread over every row tile, so those rows contribute nothing, the GPU still runs the full-size launch, and
+the oracle needs only the 256 rows.  The row-local outputs dX and dR are compared on sampled rows of the
+unmasked 1B backward.
 """
 import sys
 
@@ -16,7 +21,7 @@ import torch
 from gemm_epilogue_fusion_amd import binding as cb
 from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, EPI_SWIGLU, WORKLOADS, Workload, make_grads, make_inputs
 
-from parity import f64, sample_rows
+from parity import f64, sample_rows_covering
 
 import oracle
 
@@ -50,9 +55,14 @@ def _check(name, got, want):
     return err
 
 
-def _run(wl, unfused=False, with_dh_out=True, w2t=False):
+def _run(wl, unfused=False, with_dh_out=True, w2t=False, row_mask=None):
     inp = make_inputs(wl)
     dz, dho = make_grads(wl)
+    if row_mask is not None:  # rows outside the mask get no incoming gradient
+        keep = torch.zeros(wl.M, dtype=torch.bool)
+        keep[torch.as_tensor(row_mask, dtype=torch.long)] = True
+        dz = torch.where(keep[:, None], dz, torch.zeros((), dtype=dz.dtype))
+        dho = torch.where(keep[:, None], dho, torch.zeros((), dtype=dho.dtype))
     dev = "cuda"
     X, W1, R, g, W2 = (t.to(dev) for t in (inp.X, inp.W1, inp.R, inp.gamma, inp.W2))
     h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
@@ -83,7 +93,31 @@ SMALL = [
     Workload("bwd_one_tile", M=256, K1=256, D=256, N2=512, epi=EPI_SWIGLU, eps=1e-5, w1_std=1 / 16, w2_std=1 / 16, seed=21),
     Workload("bwd_half_row_tile", M=384, K1=512, D=512, N2=768, epi=EPI_IDENTITY, eps=1e-5, w1_std=0.05, w2_std=0.05, seed=22),
     Workload("bwd_wide_d", M=128, K1=256, D=768, N2=256, epi=EPI_SWIGLU, eps=1e-6, w1_std=0.06, w2_std=0.04, seed=23),
+    # the weight-gradient products split K = M in 4 (M = 512) and in 8 (M = 1024): one output tile for dW1,
+    # two for dW2
+    Workload("bwd_split4", M=512, K1=256, D=256, N2=512, epi=EPI_IDENTITY, eps=1e-5, w1_std=1 / 16, w2_std=1 / 16, seed=24),
+    Workload("bwd_split8", M=1024, K1=256, D=256, N2=512, epi=EPI_SWIGLU, eps=1e-5, w1_std=1 / 16, w2_std=1 / 16, seed=25),
 ]
+
+
+def _split(rows, cols, k):
+    """The split count of a weight-gradient product with a [rows, cols] output over K = k: doubled (up to 8)
+    while the parts' workgroups stay under one per compute unit (256) and each part keeps K a multiple of 128."""
+    tiles = ((rows + 255) // 256) * (cols // 256)
+    s = 1
+    while s < 8 and tiles * s < 256 and k % (128 * s * 2) == 0:
+        s *= 2
+    return s
+
+
+def test_split_counts_reached():
+    """The small cases reach the split counts they are meant to: 1, 2, 4 and 8 parts for dW1 / dW2, and dW1
+    splits in 4 at the 1B shape."""
+    got = {w.name: (_split(w.D, w.K1, w.M), _split(w.D, w.N2, w.M)) for w in SMALL}
+    assert got["bwd_split4"] == (4, 4) and got["bwd_split8"] == (8, 8)
+    full = WORKLOADS["1b_attn_out_mlp_in"]
+    assert _split(full.D, full.K1, full.M) == 4
+    assert {s for pair in got.values() for s in pair} >= {1, 2, 4, 8}
 
 
 @pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
@@ -123,9 +157,43 @@ def test_bwd_full_size_sampled_rows():
     inp, dz, dho, got = _run(wl)
     for name in ("dW1", "dgamma", "dW2"):
         assert np.all(np.isfinite(got[name])), name
-    rows = sample_rows(wl.M, n=24)
+    rows = sample_rows_covering(wl.M, n=24)
     idx = torch.as_tensor(rows, dtype=torch.long)
     want = oracle.block_bwd(f64(inp.X[idx]), f64(inp.W1), f64(inp.R[idx]), f64(inp.gamma), f64(inp.W2), wl.eps,
                             f64(dz[idx]), f64(dho[idx]))
     _check("dX", got["dX"][rows], want[0])
     _check("dR", got["dR"][rows], want[2])
+
+
+def _mask_rows(M, per_tile=8):
+    """per_tile rows in every 256-row tile, at positions that move from tile to tile (row % 32 and the 32-row
+    block both vary)."""
+    rows = []
+    for t in range((M + 255) // 256):
+        for j in range(per_tile):
+            off = (32 * j + 5 * t + 3 * j * j) % 256
+            if 256 * t + off < M:
+                rows.append(256 * t + off)
+    return np.array(sorted(set(rows)))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_bwd_full_size_weight_grads_masked_rows(unfused):
+    """dW1 (K split in 4 at this shape), dW2 and dgamma at the 1B shape, every element, with the incoming
+    gradients zero outside 256 rows; dX and dR are zero outside them and checked against the oracle inside."""
+    wl = WORKLOADS["1b_attn_out_mlp_in"]
+    rows = _mask_rows(wl.M)
+    _say(f"[gpu] bwd {'unfused' if unfused else 'fused'} full size, weight gradients, {len(rows)} live rows {wl}")
+    inp, dz, dho, got = _run(wl, unfused=unfused, row_mask=rows)
+    idx = torch.as_tensor(rows, dtype=torch.long)
+    want = oracle.block_bwd(f64(inp.X[idx]), f64(inp.W1), f64(inp.R[idx]), f64(inp.gamma), f64(inp.W2), wl.eps,
+                            f64(dz[idx]), f64(dho[idx]))
+    dead = np.ones(wl.M, dtype=bool)
+    dead[rows] = False
+    assert not np.any(got["dX"][dead]) and not np.any(got["dR"][dead]), "gradient in rows with no incoming gradient"
+    _check("dX", got["dX"][rows], want[0])
+    _check("dR", got["dR"][rows], want[2])
+    for name, w in (("dW1", want[1]), ("dgamma", want[3]), ("dW2", want[4])):
+        err = _check(name, got[name], w)
+        _say(f"    {name}: normwise {err:.3e}")

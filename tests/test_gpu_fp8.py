@@ -1,12 +1,15 @@
 """GPU parity of the fused block with OCP e4m3 operands (and its unfused baseline) against the fp64 oracle.
 
 The oracle runs on the dequantised inputs (code * scale, exact in fp64); the contract tolerance for e4m3 is
-a normwise max relative error of 6e-2 on y (h keeps the bf16 rule).  The method-internal quantisers are checked
-against the oracle's encoders applied to the oracle's own h (rounded to bf16 as the kernels store it): the
-per-row one (row scale amax/448, codes of h * gamma / scale) and the block-scaled one of coda_block_fwd_fp8_mx
-(one power-of-two scale per 32 values).  Where the GPU's fp32-accumulated h lands one bf16 step away from the
-oracle's, a code may differ, so codes and scales must agree on at least 99% of the entries, and the block-scaled
-y must match the oracle's y computed through its own quantised operand to the storage-rounding bar.
+a normwise max relative error of 6e-2 on y (h keeps the bf16 rule).  The method-internal quantisers are byte
+work and are checked bit for bit: given the h the GPU stored (bf16) and gamma, the kernels' steps are fully
+determined in fp32 (a = h * gamma; per row: amax, s = amax / 448, its reciprocal, a times it, clamp to +-448,
+round to nearest even e4m3; block-scaled: the power-of-two exponent of each 32-value block and a / 2^e), so an
+fp32 emulation of those steps in numpy, with the oracle's e4m3 encoder for the last rounding, must reproduce
+every code and every scale.  As an end-to-end check the same quantisers applied to the oracle's own h (rounded
+to bf16 as stored) must agree on at least 99% of the codes (the rest sit where the GPU's fp32-accumulated h is
+one bf16 step from the oracle's), and the block-scaled y must match the oracle's y computed through its own
+quantised operand to the storage-rounding bar.  The full-size workload is compared on every row.
 """
 import sys
 
@@ -17,7 +20,7 @@ import torch
 from gemm_epilogue_fusion_amd import binding as cb
 from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, EPI_SWIGLU, WORKLOADS, Workload, make_inputs
 
-from parity import check_h, check_roundpts, check_y, f64, sample_rows
+from parity import check_all_rows, check_h, check_roundpts, check_y, f64
 
 import oracle
 
@@ -69,6 +72,46 @@ def _panels_to_rows(flat, M, D, P=64):
     return flat.view(D // P, M, P).permute(1, 0, 2).reshape(M, D)
 
 
+def _gpu_a32(h, gamma):
+    """a = h * gamma in fp32 from the GPU's stored bf16 h: the quantisers' input exactly as the kernels form it
+    (bf16 -> fp32 is exact, the product is one fp32 rounding)."""
+    hb = h.detach().cpu().float().numpy()
+    return hb * gamma.numpy().astype(np.float32)[None, :]
+
+
+def _rowq_fp32(a):
+    """The per-row quantiser's steps in fp32: s = amax / 448 (1 for an all-zero row), inv = 1 / s, q = e4m3 of
+    a * inv clamped to +-448 (the last rounding by the oracle's encoder; the fp32 value is exact in fp64)."""
+    amax = np.max(np.abs(a), axis=1).astype(np.float32)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    inv = (np.float32(1.0) / s).astype(np.float32)
+    quot = np.clip(a * inv[:, None], np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+    return oracle.e4m3_encode(quot.astype(np.float64)), s
+
+
+def _ws_rowq(ws, M, D):
+    """The per-row e4m3 path's workspace after a call: part, r, the codes (K panels of 64), s_a [M], s_a * r [M]."""
+    off_r = _align256((D // 256) * M * 4)
+    off_q = off_r + _align256(M * 4)
+    off_s = off_q + _align256(M * D)
+    off_rs = off_s + _align256(M * 4)
+    wsc = ws.cpu()
+    f32 = lambda off: wsc[off: off + 4 * M].view(torch.float32).numpy()
+    return {"r": f32(off_r), "q": _panels_to_rows(wsc[off_q: off_q + M * D], M, D).numpy(), "s": f32(off_s),
+            "rs": f32(off_rs)}
+
+
+def _check_rowq_exact(w, h, gamma):
+    """Codes, scales and the epilogue row scale s * r of the per-row quantiser, bit for bit from the GPU's h."""
+    want_q, want_s = _rowq_fp32(_gpu_a32(h, gamma))
+    assert np.array_equal(w["s"].view(np.uint32), want_s.view(np.uint32)), \
+        f"row scales: {int(np.sum(w['s'] != want_s))} differ"
+    bad = w["q"] != want_q
+    assert not bad.any(), f"codes: {int(bad.sum())} of {bad.size} differ (first at {np.argwhere(bad)[0]})"
+    rs = (w["s"] * w["r"]).astype(np.float32)
+    assert np.array_equal(w["rs"].view(np.uint32), rs.view(np.uint32)), "s_a * r differs from its fp32 product"
+
+
 def _run_fp8(inp, unfused=False):
     wl = inp.wl
     dev = "cuda"
@@ -100,25 +143,13 @@ def test_fp8_fused_small(wl):
     oh, orr, oy = _oracle_fp8(inp)
     check_h(f64(h), oh)
     check_y(f64(y), oy, fp8=True)
-    # the workspace after the call: part, r, hq (M * D e4m3 bytes in K panels of 64), s_a [M], s_a * r [M]
-    M, D = wl.M, wl.D
-    off_r = _align256((D // 256) * M * 4)
-    off_q = off_r + _align256(M * 4)
-    off_s = off_q + _align256(M * D)
-    wsc = ws.cpu()
-    r = wsc[off_r: off_r + 4 * M].view(torch.float32).numpy()
-    np.testing.assert_allclose(r, orr, rtol=2e-5)
-    q = _panels_to_rows(wsc[off_q: off_q + M * D], M, D).numpy()
-    s = wsc[off_s: off_s + 4 * M].view(torch.float32).numpy()
-    # the quantiser's input from the oracle's side: its h rounded to bf16, times gamma in fp32 (the kernels'
-    # product), then the row scale amax / 448, its fp32 reciprocal and the scaled value in fp32
-    a = _oracle_a32(oh, inp.gamma)
-    amax = np.max(np.abs(a), axis=1).astype(np.float32)
-    want_s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
-    np.testing.assert_allclose(s, want_s, rtol=2.0 ** -7)
-    inv = (np.float32(1.0) / want_s).astype(np.float32)
-    quot = (a * inv[:, None]).astype(np.float32)
-    assert np.mean(q == oracle.e4m3_encode(quot.astype(np.float64))) >= 0.99
+    w = _ws_rowq(ws, wl.M, wl.D)
+    np.testing.assert_allclose(w["r"], orr, rtol=2e-5)
+    _check_rowq_exact(w, h, inp.gamma)
+    # end to end: the same quantiser applied to the oracle's own h (rounded to bf16 as stored)
+    q_oracle, s_oracle = _rowq_fp32(_oracle_a32(oh, inp.gamma))
+    np.testing.assert_allclose(w["s"], s_oracle, rtol=2.0 ** -7)
+    assert np.mean(w["q"] == q_oracle) >= 0.99
 
 
 @pytest.mark.parametrize("wl", FP8_SMALL[:2], ids=[w.name for w in FP8_SMALL[:2]])
@@ -131,16 +162,30 @@ def test_fp8_unfused_small(wl):
     check_y(f64(y), oy, fp8=True)
 
 
-def test_fp8_full_size_sampled_rows():
+def _oracle_fp8_chunks(inp):
+    """oracle_chunk for check_all_rows: the fused fp64 form on the dequantised inputs, for a row range."""
+    wl = inp.wl
+    W1 = oracle.dequant_cols_e4m3(_u8(inp.W1q), inp.sw1.numpy())
+    W2 = oracle.dequant_cols_e4m3(_u8(inp.W2q), inp.sw2.numpy())
+    g = f64(inp.gamma)
+
+    def fn(a, b):
+        X = oracle.dequant_rows_e4m3(_u8(inp.Xq[a:b]), inp.sx[a:b].numpy())
+        oh, orr, oy = oracle.block_fused(X, W1, f64(inp.R[a:b]), g, W2, wl.eps, wl.epi)
+        return {"h": oh, "r": orr, "y": oy}
+
+    return fn
+
+
+@pytest.mark.timeout(600)
+def test_fp8_full_size_all_rows():
     wl = WORKLOADS["1b_attn_out_mlp_in_fp8"]
-    _say(f"[gpu] fp8 full size {wl}")
+    _say(f"[gpu] fp8 full size, all rows {wl}")
     inp = make_inputs(wl)
-    h, y, _ = _run_fp8(inp)
-    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(h).all()), "unwritten or non-finite output"
-    rows = sample_rows(wl.M, n=40)
-    oh, _, oy = _oracle_fp8(inp, rows)
-    check_h(f64(h[rows]), oh)
-    check_y(f64(y[rows]), oy, fp8=True)
+    h, y, ws = _run_fp8(inp)
+    w = _ws_rowq(ws, wl.M, wl.D)
+    _check_rowq_exact(w, h, inp.gamma)
+    check_all_rows(wl.M, h, y, torch.from_numpy(w["r"]), _oracle_fp8_chunks(inp), fp8=True, say=_say)
 
 
 # ---- block-scaled (MX-style) A operand of the second GEMM: coda_block_fwd_fp8_mx ----
@@ -169,6 +214,16 @@ def _mx_scales_from_workspace(wsc, M, D, off):
     tm, r = m // 256, m % 256
     idx = ((((kt * tiles_m + tm) * 2 + r // 128) * 64 + 32 * h + r % 32) * 4 + (r // 32) % 4)
     return raw[idx].astype(np.int32) - 127
+
+
+def _check_mx_exact(q, e, h, gamma):
+    """Codes and block exponents of the block-scaled quantiser, bit for bit: the oracle's block quantiser applied
+    to a = h * gamma formed in fp32 from the GPU's stored h (a / 2^e is exact in fp32 and in fp64 alike)."""
+    want_q, want_e = oracle.mx_quant_rows_e4m3(_gpu_a32(h, gamma).astype(np.float64), 32)
+    bad_e = e != want_e
+    assert not bad_e.any(), f"block exponents: {int(bad_e.sum())} of {bad_e.size} differ"
+    bad = q != want_q
+    assert not bad.any(), f"codes: {int(bad.sum())} of {bad.size} differ (first at {np.argwhere(bad)[0]})"
 
 
 def _oracle_mx_y(inp, oh, orr, rows=None):
@@ -204,19 +259,32 @@ def test_fp8_mx_small(wl):
     y_mx, codes, exps = _oracle_mx_y(inp, oh, orr)
     check_roundpts(f64(y), y_mx)
     q = _panels_to_rows(wsc[off_q: off_q + M * D], M, D).numpy()
+    e = _mx_scales_from_workspace(wsc, M, D, off_s)
+    _check_mx_exact(q, e, h, inp.gamma)
+    # end to end: the oracle's quantiser on the oracle's own h
     assert np.mean(q == codes) >= 0.99
-    assert np.mean(_mx_scales_from_workspace(wsc, M, D, off_s) == exps) >= 0.99
+    assert np.mean(e == exps) >= 0.99
 
 
-def test_fp8_mx_full_size_sampled_rows():
+@pytest.mark.timeout(600)
+def test_fp8_mx_full_size_all_rows():
     wl = WORKLOADS["1b_attn_out_mlp_in_fp8"]
-    _say(f"[gpu] fp8 block-scaled full size {wl}")
+    _say(f"[gpu] fp8 block-scaled full size, all rows {wl}")
     inp = make_inputs(wl)
-    h, y, _ = _run_fp8_mx(inp)
-    assert bool(torch.isfinite(y).all()) and bool(torch.isfinite(h).all()), "unwritten or non-finite output"
-    rows = sample_rows(wl.M, n=40)
-    oh, orr, oy = _oracle_fp8(inp, rows)
-    check_h(f64(h[rows]), oh)
-    check_y(f64(y[rows]), oy, fp8=True)
-    y_mx, _, _ = _oracle_mx_y(inp, oh, orr)
-    check_roundpts(f64(y[rows]), y_mx)
+    h, y, ws = _run_fp8_mx(inp)
+    M, D = wl.M, wl.D
+    off_r = _align256((D // 256) * M * 4)
+    off_q = off_r + _align256(M * 4)
+    off_s = off_q + _align256(M * D)
+    wsc = ws.cpu()
+    q = _panels_to_rows(wsc[off_q: off_q + M * D], M, D).numpy()
+    _check_mx_exact(q, _mx_scales_from_workspace(wsc, M, D, off_s), h, inp.gamma)
+    base = _oracle_fp8_chunks(inp)
+
+    def chunk(a, b):
+        o = base(a, b)
+        o["y_rp"] = _oracle_mx_y(inp, o["h"], o["r"])[0]
+        return o
+
+    r = wsc[off_r: off_r + 4 * M].view(torch.float32)
+    check_all_rows(M, h, y, r, chunk, fp8=True, say=_say)

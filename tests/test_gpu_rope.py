@@ -6,7 +6,7 @@ same bf16-valued inputs, to the bf16 contract of the block (normwise 2e-2, MAE 1
 row and column tiles with a ragged last row tile, a rotated span that ends inside a tile, a sequence length that
 is not a multiple of the row tile (positions wrap inside tiles), the degenerate cases (no rotated columns:
 bit-identical to coda_block_fwd; seq_len 1: every position is 0, the rotation is the identity), and the
-1B QKV shape (q and k heads rotated, v heads not) on sampled rows.
+1B QKV shape (q and k heads rotated, v heads not) on every row.
 """
 import sys
 
@@ -17,7 +17,7 @@ import torch
 from gemm_epilogue_fusion_amd import binding as cb
 from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, WORKLOADS, Workload, make_inputs
 
-from parity import DeviceInputs, check_h, check_y, f64, oracle_rows, run_block, sample_rows
+from parity import DeviceInputs, check_all_rows, check_h, check_y, f64, oracle_chunk_fn, oracle_rows, run_block
 
 import oracle
 
@@ -121,23 +121,26 @@ def test_rope_fused_matches_separate_pass():
     assert np.max(np.abs(a - b) / rowmax) <= 4 * 2.0 ** -8
 
 
-def _oracle_rope_row(y_row, pos, n_rot, base):
-    """Rotary embedding of one row at position pos: the row is placed at index pos of a zero array whose
-    sequence length exceeds pos, so the oracle's position rule (row index mod seq_len) gives pos."""
-    buf = np.zeros((pos + 1, y_row.shape[0]), np.float64)
-    buf[pos] = y_row
-    return oracle.rope_rows(buf, HEAD, n_rot, pos + 1, base)[pos]
-
-
-def test_rope_full_size_sampled_rows():
+@pytest.mark.timeout(600)
+def test_rope_full_size_all_rows():
+    """The 1B QKV shape (q and k heads rotated, v heads not), every row: the oracle block and its rotation
+    chunk by chunk of rows, each chunk's rows at their own positions (row index mod seq_len)."""
     wl = WORKLOADS["1b_mlp_out_qkv"]
     seq_len, n_rot, base = 2048, 2560, 500000.0
-    _say(f"rope fused full size {wl.name} seq={seq_len} n_rot={n_rot}")
+    _say(f"rope fused full size, all rows {wl.name} seq={seq_len} n_rot={n_rot}")
     inp = make_inputs(wl)
     d = DeviceInputs(inp)
     h, y = _run_rope(d, seq_len, n_rot, base)
-    rows = sample_rows(wl.M, n=24, seed=7)
-    oh, _, oy = oracle_rows(inp, rows)
-    oy = np.stack([_oracle_rope_row(oy[j], int(m) % seq_len, n_rot, base) for j, m in enumerate(rows)])
-    check_h(f64(h[torch.as_tensor(rows, device=h.device)]), oh)
-    check_y(f64(y[torch.as_tensor(rows, device=y.device)]), oy)
+    base_chunk = oracle_chunk_fn(inp, roundpts=False)
+
+    def chunk(a, b):
+        o = base_chunk(a, b)
+        # row a + k sits at position (a + k) mod seq_len = (p0 + k) mod seq_len: rotate a block whose row index
+        # starts p0 rows in and keep those rows
+        p0 = a % seq_len
+        buf = np.zeros((p0 + (b - a), o["y"].shape[1]), np.float64)
+        buf[p0:] = o["y"]
+        o["y"] = oracle.rope_rows(buf, HEAD, n_rot, seq_len, base)[p0:]
+        return o
+
+    check_all_rows(wl.M, h, y, None, chunk, say=_say)

@@ -83,11 +83,11 @@ MUTANTS_MX = [
 # mistakes in the SwiGLU backward: silu' without its correction term, Wd not transposed, gate and up swapped
 # in the up-gradient
 MUTANTS_SWIGLU_BWD = [
-    ("swiglu_bwd_no_correction", "out_dz[i * 2 * F + f] = dy * u * s * (1.0 + g * (1.0 - s));",
-     "out_dz[i * 2 * F + f] = dy * u * s;"),
-    ("swiglu_bwd_wd_untransposed", "for (int64_t d = 0; d < D; ++d) dy += dout[i * D + d] * Wd[f * D + d];",
-     "for (int64_t d = 0; d < D; ++d) dy += dout[i * D + d] * Wd[(d % F) * D + f % D];"),
-    ("swiglu_bwd_up_uses_u", "out_dz[i * 2 * F + F + f] = dy * g * s;", "out_dz[i * 2 * F + F + f] = dy * u * s;"),
+    ("swiglu_bwd_no_correction", "c->dz[i * 2 * F + f] = dy * u * s * (1.0 + g * (1.0 - s));",
+     "c->dz[i * 2 * F + f] = dy * u * s;"),
+    ("swiglu_bwd_wd_untransposed", "for (int64_t d = 0; d < D; ++d) dy += c->dout[i * D + d] * c->Wd[f * D + d];",
+     "for (int64_t d = 0; d < D; ++d) dy += c->dout[i * D + d] * c->Wd[(d % F) * D + f % D];"),
+    ("swiglu_bwd_up_uses_u", "c->dz[i * 2 * F + F + f] = dy * g * s;", "c->dz[i * 2 * F + F + f] = dy * u * s;"),
 ]
 
 
