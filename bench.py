@@ -80,6 +80,118 @@ def algorithmic_bytes(wl, fused: bool) -> int:
     return b
 
 
+HBM_FILE = os.path.join(ROOT, "profiles", "hbm_bytes_1b_attn_out_mlp_in.json")
+
+
+def kernel_algorithmic_bytes(wl) -> dict:
+    """(read, write) compulsory bytes of each kernel of both paths (bf16): every operand read once, every result
+    written once."""
+    M, K1, D, N2, ny, T = wl.M, wl.K1, wl.D, wl.N2, wl.n_out, wl.D // 256
+    return {"K1": (2 * (M * K1 + K1 * D + M * D) + 4 * D, 2 * 2 * M * D + 4 * T * M),
+            "K3": (2 * M * D + 2 * D * N2 + 4 * T * M, 2 * M * ny + 4 * M),
+            "U1": (2 * (M * K1 + K1 * D), 2 * M * D),
+            "U2": (2 * 2 * M * D + 4 * D, 2 * 2 * M * D + 4 * M),
+            "U3": (2 * M * D + 2 * D * N2, 2 * M * ny)}
+
+
+def hbm_bytes_record(wl, fused_alg: int, unfused_alg: int, src_hash: str) -> dict:
+    """Algorithmic bytes of both paths, and the counter-measured bytes from the committed summary when it was
+    taken on the current kernel sources at this workload (else null, with the reason)."""
+    M, D = wl.M, wl.D
+    rec = {"fused_algorithmic": fused_alg, "unfused_algorithmic": unfused_alg,
+           "saved_algorithmic": unfused_alg - fused_alg,
+           # gamma folded into W2's tiles instead (no h * gamma copy written and read back): what the saving
+           # would be; the copy is kept because scaling W2's tiles costs the second GEMM 13-19% of its time
+           "saved_algorithmic_if_gamma_folded_into_w2": unfused_alg - fused_alg + 2 * 2 * M * D,
+           "measured": None}
+    if wl.name != "1b_attn_out_mlp_in" or not os.path.exists(HBM_FILE):
+        rec["measured_note"] = "no counter summary for this workload"
+        return rec
+    with open(HBM_FILE) as f:
+        m = json.load(f)
+    if m.get("kernel_source_hash") != src_hash:
+        rec["measured_note"] = f"counter summary taken on other kernel sources ({m.get('kernel_source_hash')})"
+        return rec
+    rec["measured"] = {k: m[k] for k in ("fused", "unfused", "saved") if k in m}
+    rec["measured"]["source"] = os.path.relpath(HBM_FILE, ROOT)
+    rec["measured"]["what"] = m.get("what_short")
+    return rec
+
+
+def summarize_hbm_counters(dirs: list, out: str, wl) -> dict:
+    """Writes the measured-bytes summary from rocprofv3 --pmc runs of
+    `bench.py --only-fused --profile-unfused --copy-calibration-mib 1024` (one counter set per run).  Dispatches
+    are attributed by kernel name and order: GEMM1 and GEMM2 of the fused block until the first plain-store GEMM,
+    then U1, U2, U3 of the unfused block; the last copy kernel is the calibration copy.  Each kernel's value is
+    the mean over its dispatches after the first."""
+    import csv
+    import glob
+
+    vals = {}   # counter -> role -> [values]
+    calib = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise FileNotFoundError(f"no counter_collection.csv under {d}")
+        rows = sorted(csv.DictReader(open(files[0])), key=lambda r: int(r["Dispatch_Id"]))
+        seen_store = False
+        for r in rows:
+            k, c, v = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if "gemm_epilogue_kernel<1," in k:
+                seen_store = True
+            role = None
+            if "gemm_epilogue_kernel<0, false, false>" in k:
+                role = "K1"
+            elif "gemm_epilogue_kernel<3, false, false>" in k:
+                role = "U3" if seen_store else "K3"
+            elif "gemm_epilogue_kernel<1, false, false>" in k:
+                role = "U1"
+            elif "add_rmsnorm_kernel<false>" in k:
+                role = "U2"
+            elif "copy" in k.lower():
+                calib[c] = v  # the last copy dispatch wins: the calibration copy comes last
+            if role:
+                vals.setdefault(c, {}).setdefault(role, []).append(v)
+    mean = lambda xs: sum(xs[1:]) / len(xs[1:]) if len(xs) > 1 else xs[0]
+    copy_bytes = 1 << 30
+    fscale = copy_bytes / (calib["FETCH_SIZE"] * 1024)
+    wscale = copy_bytes / (calib["WRITE_SIZE"] * 1024)
+    alg = kernel_algorithmic_bytes(wl)
+    kern = {}
+    for role in ("K1", "K3", "U1", "U2", "U3"):
+        e = {"read_bytes": round(mean(vals["FETCH_SIZE"][role]) * 1024 * fscale),
+             "write_bytes": round(mean(vals["WRITE_SIZE"][role]) * 1024 * wscale),
+             "algorithmic_read_bytes": alg[role][0], "algorithmic_write_bytes": alg[role][1]}
+        for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_DRAM_sum"):
+            if c in vals and role in vals[c]:
+                e[c] = round(mean(vals[c][role]))
+        kern[role] = e
+    paths = {"fused": ("K1", "K3"), "unfused": ("U1", "U2", "U3")}
+    rec = {"what_short": "rocprofv3 FETCH_SIZE + WRITE_SIZE per kernel, scaled by a 1 GiB copy's readings: bytes at "
+                         "the L2's memory side (Infinity Cache hits included)",
+           "kernel_source_hash": kernel_source_hash(), "workload": wl.name,
+           "calibration": {"copy_bytes": copy_bytes, **{k: v for k, v in calib.items()}, "fetch_scale": round(fscale, 4),
+                           "write_scale": round(wscale, 4)},
+           "kernels": kern}
+    for name, roles in paths.items():
+        rd = sum(kern[r]["read_bytes"] for r in roles)
+        wr = sum(kern[r]["write_bytes"] for r in roles)
+        rec[name] = {"read_bytes": rd, "write_bytes": wr, "total_bytes": rd + wr,
+                     "algorithmic_total_bytes": sum(sum(alg[r]) for r in roles)}
+        if all("TCC_EA0_RDREQ_DRAM_sum" in kern[r] and "TCC_EA0_RDREQ_sum" in kern[r] for r in roles):
+            rec[name]["dram_share_of_read_requests"] = round(
+                sum(kern[r]["TCC_EA0_RDREQ_DRAM_sum"] for r in roles) / sum(kern[r]["TCC_EA0_RDREQ_sum"] for r in roles), 4)
+        if all("TCC_EA0_WRREQ_DRAM_sum" in kern[r] and "TCC_EA0_WRREQ_sum" in kern[r] for r in roles):
+            rec[name]["dram_share_of_write_requests"] = round(
+                sum(kern[r]["TCC_EA0_WRREQ_DRAM_sum"] for r in roles) / sum(kern[r]["TCC_EA0_WRREQ_sum"] for r in roles), 4)
+    rec["saved"] = {"total_bytes": rec["unfused"]["total_bytes"] - rec["fused"]["total_bytes"],
+                    "write_bytes": rec["unfused"]["write_bytes"] - rec["fused"]["write_bytes"],
+                    "algorithmic_bytes": rec["unfused"]["algorithmic_total_bytes"] - rec["fused"]["algorithmic_total_bytes"]}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    return rec
+
+
 def time_loop(fn, n: int, torch) -> float:
     """Average ms per call of fn over n back-to-back calls, with HIP events on the current stream."""
     start = torch.cuda.Event(enable_timing=True)
@@ -90,6 +202,149 @@ def time_loop(fn, n: int, torch) -> float:
     end.record()
     end.synchronize()
     return start.elapsed_time(end) / n
+
+
+def timed_steps(fn, steps: int, warmup: int, torch, settle_ms: float = 0.0):
+    """The contract's timing: untimed calls for at least settle_ms of wall time (0: none), then `warmup` untimed
+    calls, then exactly `steps` calls timed by the host clock between two device synchronisations.  A HIP event
+    is recorded on the calls' stream before each timed call and after the last, which splits the same wall-clock
+    window into per-call times without adding a synchronisation.  Returns (wall ms per call, [event ms per call],
+    settle calls made)."""
+    settled = 0
+    if settle_ms > 0:
+        t_end = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(10):
+                fn()
+            settled += 10
+            torch.cuda.synchronize()
+    for _ in range(warmup):
+        fn()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i].record()
+        fn()
+    evs[steps].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)], settled
+
+
+def per_step_summary(per: list) -> dict:
+    t = sorted(per)
+    n = len(t)
+    q = lambda p: round(t[min(n - 1, int(round(p * (n - 1))))], 4)
+    return {"mean": round(sum(per) / n, 4), "first": round(per[0], 4), "last": round(per[-1], 4), "median": q(0.5),
+            "p10": q(0.1), "p90": q(0.9), "max": round(t[-1], 4), "first_third_mean": round(
+                sum(per[: max(1, n // 3)]) / max(1, n // 3), 4), "last_third_mean": round(
+                sum(per[n - max(1, n // 3):]) / max(1, n // 3), 4)}
+
+
+def environment(torch) -> dict:
+    """What ran: the source revision, the software stack and the device."""
+    import subprocess
+
+    env = {"commit": None, "csrc_hash": None, "torch": torch.__version__, "hip_runtime": torch.version.hip}
+    try:
+        env["commit"] = subprocess.run(["git", "rev-parse", "--short=12", "HEAD"], cwd=ROOT, capture_output=True,
+                                       text=True, timeout=10).stdout.strip() or None
+    except Exception:  # noqa: BLE001 -- a copy of the tree without its history
+        pass
+    if not env["commit"]:  # the revision recorded when the library was built (build() writes it)
+        try:
+            with open(os.path.join(ROOT, "gemm_epilogue_fusion_amd", "build_info.json")) as f:
+                env["commit"] = json.load(f).get("commit")
+            env["commit_from"] = "build_info.json"
+        except (OSError, ValueError):
+            pass
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_epilogue_fusion_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    env["csrc_hash"] = h.hexdigest()[:16]
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    p = torch.cuda.get_device_properties(0)
+    env.update({"gpu": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+                "memory_gib": round(p.total_memory / 2**30, 1)})
+    return env
+
+
+def _find_sclk(obj):
+    """The first value under a key that names the shader clock ("sclk") in rocm-smi's JSON, in MHz."""
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            if "sclk" in str(k).lower() and not isinstance(v, (dict, list)):
+                txt = str(v).lower().replace("mhz", "").strip(" ()")
+                try:
+                    return float(txt)
+                except ValueError:
+                    continue
+            r = _find_sclk(v)
+            if r is not None:
+                return r
+    elif isinstance(obj, list):
+        for v in obj:
+            r = _find_sclk(v)
+            if r is not None:
+                return r
+    return None
+
+
+def _read_sclk_mhz(raw: list):
+    """The current shader clock of the device from rocm-smi (MHz), or None; the first raw answers are kept."""
+    import subprocess
+
+    p = subprocess.run(["rocm-smi", "--showgpuclocks", "--json"], capture_output=True, text=True, timeout=20)
+    if len(raw) < 2:
+        raw.append((p.returncode, p.stdout[-600:], p.stderr[-300:]))
+    try:
+        return _find_sclk(json.loads(p.stdout))
+    except ValueError:
+        return None
+
+
+def clock_under_load(fn, torch, seconds: float = 1.5) -> dict:
+    """Shader clock read from rocm-smi a few times while fn runs back to back on the device (the clock the
+    block actually runs at: MFMA-bound kernels on random data run below the 2.4 GHz peak clock)."""
+    import threading
+
+    samples, raw, stop = [], [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                v = _read_sclk_mhz(raw)
+                if v:
+                    samples.append(v)
+            except Exception as e:  # noqa: BLE001 -- no rocm-smi: no reading
+                raw.append(repr(e))
+                return
+            time.sleep(0.05)
+
+    th = threading.Thread(target=poll, daemon=True)
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=30)
+    out = {"sclk_mhz_samples": samples, "sclk_mhz_median": sorted(samples)[len(samples) // 2] if samples else None,
+           "how": "rocm-smi --showgpuclocks while the fused block runs back to back"}
+    if not samples:
+        out["rocm_smi_answers"] = raw[:2]
+    return out
 
 
 def step_distribution(fn, n: int, torch, scrub=None) -> dict:
@@ -353,11 +608,27 @@ def main() -> int:
     ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy timing")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the SwiGLU forward-with-z / backward timing")
     ap.add_argument("--no-tiny", action="store_true", help="skip the launch-bound tiny block (eager and graph)")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed calls for at least this many ms before the warm-up calls of each timed window: the "
+                         "device's clock settles under sustained load only after some milliseconds (0: none)")
+    ap.add_argument("--no-clock", action="store_true", help="skip the shader-clock reading under load")
     ap.add_argument("--only-fused", action="store_true", help="time the fused block only (for profiling runs)")
+    ap.add_argument("--profile-unfused", action="store_true",
+                    help="with --only-fused: after the fused steps run the unfused block `steps` times (counter runs "
+                         "attribute dispatches to the two paths by their order)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB once (a plain copy of known size, the "
                          "reference that scales the HBM byte counters of a profiling run)")
+    ap.add_argument("--summarize-hbm-counters", nargs="+", metavar="DIR",
+                    help="write the measured-bytes summary (profiles/) from these rocprofv3 --pmc output folders and "
+                         "exit (no GPU needed)")
     args = ap.parse_args()
+
+    if args.summarize_hbm_counters:
+        from gemm_epilogue_fusion_amd.inputs import WORKLOADS as _W
+        rec = summarize_hbm_counters(args.summarize_hbm_counters, HBM_FILE, _W[args.workload])
+        print(json.dumps({k: rec[k] for k in ("fused", "unfused", "saved")}))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this block runs on one GPU; multi-GPU runs are not part of it "
@@ -391,17 +662,15 @@ def main() -> int:
     def step_unfused():
         cb.coda_block_unfused(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws_u)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed * 1e3 / args.steps
+    # the headline: the contract's timing (host clock around exactly K calls after W warm-up calls), with a HIP
+    # event before each call splitting the same window; the unfused baseline is timed the same way right after
+    ms, per_fused, settled = timed_steps(step, args.steps, args.warmup, torch, args.settle_ms)
     tflops = wl.flops / (ms * 1e-3) / 1e12
     if args.only_fused:
+        if args.profile_unfused:
+            for _ in range(args.steps):
+                step_unfused()
+            torch.cuda.synchronize()
         if args.copy_calibration_mib:
             n = args.copy_calibration_mib * (1 << 20)
             src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -411,6 +680,7 @@ def main() -> int:
             torch.cuda.synchronize()
         print(json.dumps({"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": ms}))
         return 0
+    unf_ms, per_unfused, _ = timed_steps(step_unfused, args.steps, args.warmup, torch, args.settle_ms)
 
     # per-step kernels timed alone with HIP events (same stream as the launches: torch's current stream).
     # The block's own kernels: K1 writing h * gamma in K panels, and K3 reading them with the reduce folded in
@@ -439,7 +709,7 @@ def main() -> int:
     three_ms = time_loop(three_steps, n_ev, torch)
     for _ in range(args.warmup):
         step_unfused()
-    unf_ms = time_loop(step_unfused, n_ev, torch)
+    unf_ev_ms = time_loop(step_unfused, n_ev, torch)
     fused_ev_ms = time_loop(step, n_ev, torch)
 
     # per-call spread, warm (back to back) and cold (a 512 MiB write between calls evicts the MALL)
@@ -469,6 +739,7 @@ def main() -> int:
                 "kernel_ms": round(k3_ms, 4), "algorithmic_flops_per_launch": k3_flops}
 
     fb, ub = algorithmic_bytes(wl, True), algorithmic_bytes(wl, False)
+    ev_f, ev_u = sum(per_fused) / len(per_fused), sum(per_unfused) / len(per_unfused)
     line = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -477,6 +748,20 @@ def main() -> int:
                    "epilogue": "swiglu" if wl.epi else "identity", "eps": wl.eps},
         "pct_bf16_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "roofline": roofline,
+        "timing": {
+            "ms_per_step": "host clock around exactly `steps` calls after `warmup` warm-up calls (and settle_ms of "
+                           "untimed calls before them), between two device synchronisations",
+            "settle_ms": args.settle_ms, "settle_calls": settled,
+            "fused_per_step_events_ms": per_step_summary(per_fused),
+            "events_ms": "HIP events on the calls' stream: in the timed window one event before each call "
+                         "(per_step), elsewhere one pair around n back-to-back calls (mean per call)",
+        },
+        "unfused": {"ms_per_step_wall": round(unf_ms, 4), "per_step_events_ms": per_step_summary(per_unfused),
+                    "tflops_wall": round(wl.flops / (unf_ms * 1e-3) / 1e12, 2),
+                    "speedup_fused_vs_unfused_wall": round(unf_ms / ms, 4),
+                    "speedup_fused_vs_unfused_events_same_window": round(ev_u / ev_f, 4),
+                    "ms_per_call_events": round(unf_ev_ms, 4), "fused_ms_per_call_events": round(fused_ev_ms, 4),
+                    "speedup_fused_vs_unfused_events": round(unf_ev_ms / fused_ev_ms, 4)},
         "kernels_ms": {"gemm1_res_prms": round(k1p_ms, 4), "gemm2_rowscale_fold": round(k3_ms, 4),
                        "fused_block_events": round(fused_ev_ms, 4),
                        "row_major_steps": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
@@ -484,9 +769,7 @@ def main() -> int:
                                            "three_back_to_back": round(three_ms, 4)},
                        "torch_matmul_gemm2_product_only": round(mm_ms, 4)},
         "block_per_call": dist,
-        "unfused": {"ms_per_step": round(unf_ms, 4), "tflops": round(wl.flops / (unf_ms * 1e-3) / 1e12, 2),
-                    "speedup_fused_vs_unfused": round(unf_ms / fused_ev_ms, 4)},
-        "hbm_bytes": {"fused_algorithmic": fb, "unfused_algorithmic": ub, "saved_algorithmic": ub - fb},
+        "hbm_bytes": hbm_bytes_record(wl, fb, ub, src_hash),
         "kernel_source_hash": src_hash,
     }
     def extra(key, fn):
@@ -510,6 +793,9 @@ def main() -> int:
         extra("swiglu", lambda: time_swiglu(wl, X, W1, R, g, W2, dev, n_ev, args.warmup, torch, cb))
     if not args.no_tiny:
         extra("tiny", lambda: time_tiny(dev, torch, cb))
+    extra("env", lambda: environment(torch))
+    if not args.no_clock:
+        extra("clock", lambda: clock_under_load(step, torch))
     if not args.no_cpu_baseline:
         extra("cpu_baseline", lambda: cpu_baseline(wl, inp))
     print(json.dumps(line))

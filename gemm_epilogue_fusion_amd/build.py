@@ -86,7 +86,25 @@ def build(verbose: bool = False) -> str:
             print(f"  {name}: VGPRs {u.get('VGPRs')}, scratch {u.get('ScratchSize')}, LDS {u.get('LDS')}",
                   file=sys.stderr)
     os.replace(tmp, LIB)
+    write_build_info()
     return LIB
+
+
+def write_build_info() -> None:
+    """Records the source revision the library was built from (build_info.json, not tracked): a copy of the tree
+    without its history (a benchmark machine) can still name it."""
+    import json
+    import time
+
+    info = {"commit": None, "dirty": None, "built_unix": int(time.time())}
+    try:
+        git = lambda *a: subprocess.run(["git", *a], cwd=ROOT, capture_output=True, text=True, timeout=10).stdout
+        info["commit"] = git("rev-parse", "--short=12", "HEAD").strip() or None
+        info["dirty"] = bool(git("status", "--porcelain", "--untracked-files=no").strip())
+    except Exception:  # noqa: BLE001 -- no git: nothing to record
+        pass
+    with open(os.path.join(PKG, "build_info.json"), "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":

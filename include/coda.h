@@ -91,19 +91,28 @@ const char* coda_last_error(void);
  *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]), row-major. */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
-/* The fused block, bf16 operands.
+/* The fused block, bf16 operands: the GEMM -> residual -> RMSNorm -> GEMM block of the write-up's section
+ * "CODA: the treasure hidden in the epilogue" (the residual added and the partial sums of squares taken in the
+ * first product's epilogue, the per-row RMS factor moved past the second product into its epilogue, SwiGLU
+ * admitting the same rewrite), with the section "Five blocks and a Lego language"'s primitives: tiled store
+ * of h, the RMSNorm weight as a broadcast vector, the block reduction for the local sums of squares.
  *   X [M,K1] bf16, W1 [K1,D] bf16, R [M,D] bf16, gamma [D] fp32, W2 [D,N2] bf16  (inputs)
  *   out_h [M,D] bf16 = bf16(X W1 + R) (the fp32 sum rounded once)                   (output)
- *   out_y [M,N2 or N2/2] bf16 = bf16(epi(r * (h W2')))                               (output)
- * Three kernels on `stream`: GEMM1 + residual + gamma + partial sums of squares, the row-scale reduction,
- * and GEMM2 on hg + row scale (+ SwiGLU).  After the call the workspace holds r [M] (fp32) at byte offset
- * coda_workspace_r_offset(M, D). */
+ *   out_y [M,N2 or N2/2] bf16 = bf16(epi(r * (hg W2))), hg = bf16(h * gamma)          (output)
+ * Two kernels on `stream` where D <= 4096: GEMM1 + residual + gamma + partial sums of squares, then GEMM2 on
+ * hg whose workgroups reduce their rows' partial sums to r themselves and apply r (+ SwiGLU) in the epilogue.
+ * Where D > 4096 the reduction runs as a kernel of its own between the two (three kernels).  After the call the
+ * workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D).  Ownership, errors and the
+ * asynchronous contract are the shared conventions above. */
 int coda_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
                    float eps, int epi_kind, void* out_h, void* out_y,
                    int64_t M, int64_t K1, int64_t D, int64_t N2,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* The fused block with fp8 (OCP e4m3fn) operands and fp32 accumulation.
+/* The fused block with fp8 (OCP e4m3fn) operands and fp32 accumulation: the same block (section "CODA: the
+ * treasure hidden in the epilogue"); the write-up's section "Where training time goes" reports that the
+ * non-GEMM share of training time grows once FP8 is introduced, and its section "Five blocks and a Lego
+ * language" lists per-row / per-column scale vectors among the epilogue's broadcast loads.
  *   Xq [M,K1] e4m3 with per-row scales sx [M]; W1q [K1,D] e4m3 with per-column scales sw1 [D];
  *   W2q [D,N2] e4m3 with per-column scales sw2 [N2]; R [M,D] bf16; gamma [D] fp32.
  *   out_h = bf16(dequant(Xq) dequant(W1q) + R); out_y as coda_block_fwd.
@@ -116,9 +125,13 @@ int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const f
                        void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* The unfused three-kernel baseline, kept to measure the HBM traffic the fusion saves:
- *   T = bf16(X W1)  ->  h = bf16(T + R), r from the fp32 T + R, n = bf16(h * r * gamma)  ->  y = epi(n W2).
- * T and n live in the workspace.  Same arguments and outputs as coda_block_fwd. */
+/* The unfused three-kernel baseline, kept to measure the HBM traffic the fusion saves: the conventional form
+ * the write-up's section "CODA: the treasure hidden in the epilogue" contrasts with the fused one (three
+ * operators, the intermediate written to and read back from memory twice):
+ *   T = bf16(X W1)  ->  hf = fp32(T) + fp32(R), h = bf16(hf), r = 1 / sqrt(mean(hf^2) + eps),
+ *   n = bf16(hf * r * gamma)  ->  y = bf16(epi(n W2)).
+ * T and n live in the workspace (row-major).  Same arguments, outputs, errors and conventions as
+ * coda_block_fwd; after the call the workspace holds r at coda_workspace_r_offset(M, D). */
 int coda_block_unfused(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
                        float eps, int epi_kind, void* out_h, void* out_y,
                        int64_t M, int64_t K1, int64_t D, int64_t N2,
