@@ -100,9 +100,10 @@ def hbm_bytes_record(wl, fused_alg: int, unfused_alg: int, src_hash: str) -> dic
     M, D = wl.M, wl.D
     rec = {"fused_algorithmic": fused_alg, "unfused_algorithmic": unfused_alg,
            "saved_algorithmic": unfused_alg - fused_alg,
-           # gamma folded into W2's tiles instead (no h * gamma copy written and read back): what the saving
-           # would be; the copy is kept because scaling W2's tiles costs the second GEMM 13-19% of its time
-           "saved_algorithmic_if_gamma_folded_into_w2": unfused_alg - fused_alg + 2 * 2 * M * D,
+           # gamma folded into W2's tiles instead, GEMM2 reading h itself: the h * gamma copy is not written (its
+           # read becomes a read of h), so the saving would be one [M,D] bf16 store larger; the copy is kept
+           # because scaling W2's tiles costs the second GEMM 13-19% of its time
+           "saved_algorithmic_if_gamma_folded_into_w2": unfused_alg - fused_alg + 2 * M * D,
            "measured": None}
     if wl.name != "1b_attn_out_mlp_in" or not os.path.exists(HBM_FILE):
         rec["measured_note"] = "no counter summary for this workload"
@@ -167,8 +168,22 @@ def summarize_hbm_counters(dirs: list, out: str, wl) -> dict:
                 e[c] = round(mean(vals[c][role]))
         kern[role] = e
     paths = {"fused": ("K1", "K3"), "unfused": ("U1", "U2", "U3")}
+    prof = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/hbm/{d} -o run -- python3 bench.py --only-fused "
+            "--profile-unfused --steps 10 --warmup 2 --settle-ms 0 --copy-calibration-mib 1024")
+    passes = [("FETCH_SIZE", "FETCH_SIZE"), ("WRITE_SIZE", "WRITE_SIZE"),
+              ("TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_DRAM_sum", "TCC_EA0_RDREQ_sum"),
+              ("TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_DRAM_sum", "TCC_EA0_WRREQ_sum")]
     rec = {"what_short": "rocprofv3 FETCH_SIZE + WRITE_SIZE per kernel, scaled by a 1 GiB copy's readings: bytes at "
                          "the L2's memory side (Infinity Cache hits included)",
+           "commands": ["cd /tmp && export TMPDIR=/tmp, then from the repository root, one counter set per run:"]
+                       + [prof.format(c=c, d=d) for c, d in passes]
+                       + ["python3 bench.py --summarize-hbm-counters " + " ".join(f"gpurun_out/hbm/{d}" for _, d in passes)],
+           "note": "The counters sit at the L2's side towards memory: every 128-byte request that misses an XCD's L2, "
+                   "served by the 256 MB Infinity Cache or by HBM (the L2 cannot tell them apart; every request is "
+                   "addressed to local memory, dram_share = 1).  The copy's FETCH_SIZE reads half the copied bytes (the "
+                   "derived counter prices a 128-byte request at 64 bytes) and its read-request count times 128 bytes "
+                   "equals the copy, hence fetch_scale 2.  The two GEMM2s read about 8x their operands: each XCD's L2 "
+                   "refills the tiles its 32 concurrent workgroups share, mostly from the Infinity Cache.",
            "kernel_source_hash": kernel_source_hash(), "workload": wl.name,
            "calibration": {"copy_bytes": copy_bytes, **{k: v for k, v in calib.items()}, "fetch_scale": round(fscale, 4),
                            "write_scale": round(wscale, 4)},
@@ -281,11 +296,12 @@ def _find_sclk(obj):
     if isinstance(obj, dict):
         for k, v in obj.items():
             if "sclk" in str(k).lower() and not isinstance(v, (dict, list)):
-                txt = str(v).lower().replace("mhz", "").strip(" ()")
-                try:
-                    return float(txt)
-                except ValueError:
-                    continue
+                # "1 (2100Mhz)" (level and clock) or "2100Mhz"
+                import re
+                m = re.search(r"(\d+(?:\.\d+)?)\s*mhz", str(v).lower())
+                if m:
+                    return float(m.group(1))
+                continue
             r = _find_sclk(v)
             if r is not None:
                 return r
