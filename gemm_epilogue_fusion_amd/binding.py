@@ -32,7 +32,8 @@ EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_wo
            "coda_bwd_workspace_bytes", "coda_block_bwd", "coda_block_bwd_unfused", "coda_block_bwd_w2t",
            "coda_block_fwd_rope",
            "coda_rope_rows", "coda_ce_workspace_bytes", "coda_ce_fwd", "coda_ce_unfused",
-           "coda_block_fwd_save_z", "coda_swiglu_bwd_workspace_bytes", "coda_swiglu_bwd", "coda_swiglu_bwd_unfused")
+           "coda_block_fwd_save_z", "coda_swiglu_bwd_workspace_bytes", "coda_swiglu_bwd", "coda_swiglu_bwd_unfused",
+           "coda_block_fwd_noalloc")
 
 
 class CodaError(RuntimeError):
@@ -63,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("coda_block_fwd", "coda_block_unfused"):
         getattr(lib, name).argtypes = block
         getattr(lib, name).restype = i32
+    lib.coda_block_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, f32, i32, vp, vp, i64, i64, i64, i64, vp]
+    lib.coda_block_fwd_noalloc.restype = i32
     block8 = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
     for name in ("coda_block_fwd_fp8", "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx"):
         getattr(lib, name).argtypes = block8
@@ -163,6 +166,25 @@ def _block(name: str, X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspac
 def coda_block_fwd(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y, workspace, stream=None):
     """Fused block: out_h = bf16(X W1 + R); out_y = bf16(epi(r * (h diag(gamma) W2)))."""
     _block("coda_block_fwd", X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, workspace, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # CODA_NOALLOC_SCRATCH_BYTES of include/coda.h
+
+
+def coda_block_fwd_noalloc(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y, stream=None):
+    """coda_block_fwd on the library's fixed per-device scratch (no workspace; nothing allocated); calls on one
+    device must not overlap."""
+    M, K1 = X.shape
+    D = W1.shape[1]
+    N2 = W2.shape[1]
+    ny = N2 if epi_kind == EPI_IDENTITY else N2 // 2
+    args = (_dev(X, "X", torch.bfloat16, (M, K1)), _dev(W1, "W1", torch.bfloat16, (K1, D)),
+            _dev(R, "R", torch.bfloat16, (M, D)), _dev(gamma, "gamma", torch.float32, (D,)),
+            _dev(W2, "W2", torch.bfloat16, (D, N2)))
+    h = _dev(out_h, "out_h", torch.bfloat16, (M, D))
+    y = _dev(out_y, "out_y", torch.bfloat16, (M, ny))
+    st = load().coda_block_fwd_noalloc(*args, float(eps), int(epi_kind), h, y, M, K1, D, N2, _stream(stream))
+    _check(st, "coda_block_fwd_noalloc")
 
 
 def coda_block_unfused(X, W1, R, gamma, W2, eps: float, epi_kind: int, out_h, out_y, workspace, stream=None):

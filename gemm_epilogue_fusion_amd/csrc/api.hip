@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <mutex>
 #include <string>
 
 #include "coda.h"
@@ -263,6 +264,64 @@ int validate_bwd(const void* X, const void* W1, const void* h, const float* r, c
   return check_alias(in, 8, out, 6, nullptr, nullptr);
 }
 
+// The fused block's launch sequence on an accepted argument set: coda_block_fwd on the caller's workspace,
+// coda_block_fwd_noalloc on the library's scratch.
+int launch_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                     int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                     void* workspace, hipStream_t st) {
+  int s;
+  Workspace w;
+  carve(workspace, M, D, 0, 0, &w);
+  if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R, gamma,
+                                                 (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D, st, kPanels),
+                     "gemm1_res_prms launch")))
+    return s;
+  if (coda::fold_supported((int)D))  // the reduce runs inside K3's workgroups
+    return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
+                                                      epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
+                                                      (int)N2, st, nullptr, kPanels),
+                     "gemm2_rowscale_fold launch");
+  if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
+                     "prms_reduce launch")))
+    return s;
+  return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, epi_kind == CODA_EPI_SWIGLU,
+                                               (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, nullptr, kPanels),
+                   "gemm2_rowscale launch");
+}
+
+}  // namespace
+
+// The fixed scratch of coda_block_fwd_noalloc: the fused block's workspace (partial sums, r, h * gamma in K panels)
+// for callers that cannot allocate.  Each device the library runs on holds its own copy from the moment the
+// library's code is loaded there until the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address comes from hipGetSymbolAddress, once per device (noalloc_scratch below), and
+// only that address is ever passed to a kernel.
+__device__ __align__(256) unsigned char scratch[CODA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, looked up on the first call on that device.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CODA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(CODA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(CODA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CODA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -301,25 +360,30 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
     int s = validate_block(X, nullptr, W1, nullptr, R, gamma, W2, nullptr, eps, epi_kind, out_h, out_y, M, K1, D, N2,
                            workspace, workspace_bytes, 0, 0);
     if (s) return s;
-    hipStream_t st = (hipStream_t)stream;
-    Workspace w;
-    carve(workspace, M, D, 0, 0, &w);
-    if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
-                                                   gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
-                                                   st, kPanels),
-                       "gemm1_res_prms launch")))
-      return s;
-    if (coda::fold_supported((int)D))  // the reduce runs inside K3's workgroups
-      return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
-                                                        epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M,
-                                                        (int)D, (int)N2, st, nullptr, kPanels),
-                       "gemm2_rowscale_fold launch");
-    if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
-                       "prms_reduce launch")))
-      return s;
-    return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, epi_kind == CODA_EPI_SWIGLU,
-                                                 (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, nullptr, kPanels),
-                     "gemm2_rowscale launch");
+    return launch_block_fwd(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
+                            (hipStream_t)stream);
+  } catch (...) {
+    return fail(CODA_ERR_INTERNAL, "unexpected exception");
+  }
+}
+
+int coda_block_fwd_noalloc(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
+                           float eps, int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D,
+                           int64_t N2, void* stream) {
+  try {
+    // the size limit first (plain arithmetic: nothing touches the device before the arguments are accepted)
+    if (M >= 1 && D >= 256 && M <= kMaxDim && D <= kMaxDim && ws_bytes(M, D, 0, 0) > (size_t)CODA_NOALLOC_SCRATCH_BYTES)
+      return fail(CODA_ERR_WORKSPACE,
+                  "coda_block_fwd_noalloc: M=%lld, D=%lld need %zu bytes of scratch; the library's fixed scratch holds "
+                  "%zu (use coda_block_fwd with a workspace)",
+                  (long long)M, (long long)D, ws_bytes(M, D, 0, 0), (size_t)CODA_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    int s = noalloc_scratch(&ws);
+    if (s) return s;
+    s = validate_block(X, nullptr, W1, nullptr, R, gamma, W2, nullptr, eps, epi_kind, out_h, out_y, M, K1, D, N2, ws,
+                       (size_t)CODA_NOALLOC_SCRATCH_BYTES, 0, 0);
+    if (s) return s;
+    return launch_block_fwd(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, ws, (hipStream_t)stream);
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }

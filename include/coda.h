@@ -109,6 +109,26 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
                    int64_t M, int64_t K1, int64_t D, int64_t N2,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the library's fixed scratch used by coda_block_fwd_noalloc (64 MiB per device). */
+#define CODA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* coda_block_fwd for callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments, outputs, shape rules, errors and kernels as
+ * coda_block_fwd, without the workspace: the block's workspace (partial sums, r, h * gamma) lives in a fixed
+ * array of CODA_NOALLOC_SCRATCH_BYTES in the library's device code, which each device the library runs on
+ * holds from the moment the library is loaded there until the process ends.  Nothing is allocated by this
+ * call (no hipMalloc, hipFree or allocating library routine); the first call on a device looks the array's
+ * address up once (hipGetSymbolAddress).  Limit: coda_workspace_bytes(M, K1, D, N2, epi_kind, 0, 0) must not
+ * exceed CODA_NOALLOC_SCRATCH_BYTES (M * D up to about 33 million: the 1B shapes fit, M = 16384 with D = 4096
+ * does not), else CODA_ERR_WORKSPACE before anything is enqueued.  Every call on one device shares that
+ * device's array and leaves its contents there (nothing in it needs clearing between calls: every byte the
+ * kernels read was written earlier in the same call), so calls that overlap on one device race: order them on
+ * one stream or otherwise.  r is not returned (it stays in the scratch); callers that need it use
+ * coda_block_fwd. */
+int coda_block_fwd_noalloc(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
+                           int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2,
+                           void* stream);
+
 /* The fused block with fp8 (OCP e4m3fn) operands and fp32 accumulation: the same block (section "CODA: the
  * treasure hidden in the epilogue"); the write-up's section "Where training time goes" reports that the
  * non-GEMM share of training time grows once FP8 is introduced, and its section "Five blocks and a Lego

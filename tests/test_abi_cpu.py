@@ -397,3 +397,17 @@ def test_save_z_validation(lib):
     assert call(z=BASE + 16) == ALIAS            # on X
     assert call(z=BASE + 6 * GB + 64) == ALIAS   # on out_y
     assert call(N2=384) == UNSUPPORTED
+
+
+def test_noalloc_limits(lib):
+    """coda_block_fwd_noalloc: a workspace beyond the library's fixed scratch is refused before anything touches the
+    device; bad arguments within the limit are refused with the block's own codes."""
+    f = lib.coda_block_fwd_noalloc
+    args = lambda M, D, N2=512, epi=0, **o: [o.get("X", BASE), BASE + GB, BASE + 2 * GB, BASE + 3 * GB, BASE + 4 * GB,
+                                             o.get("eps", 1e-5), epi, BASE + 5 * GB, BASE + 6 * GB, M, 256, D, N2, None]
+    assert lib.coda_workspace_bytes(16384, 256, 4096, 512, 0, 0, 0) > cb.NOALLOC_SCRATCH_BYTES
+    assert f(*args(16384, 4096)) == WORKSPACE
+    assert b"scratch" in lib.coda_last_error()
+    if torch.cuda.device_count() == 0:
+        # within the limit the scratch's address is looked up first: with no device that is a HIP error
+        assert f(*args(512, 256)) == HIP
