@@ -812,6 +812,13 @@ def main() -> int:
     extra("env", lambda: environment(torch))
     if not args.no_clock:
         extra("clock", lambda: clock_under_load(step, torch))
+        mhz = line.get("clock", {}).get("sclk_mhz_median")
+        if mhz:
+            # the same kernel against the peak at the shader clock it ran at (MFMA-bound kernels on random data run
+            # below the 2.4 GHz the published peak assumes)
+            peak_at_clock = MFMA_BF16_PEAK_TFLOPS * mhz / 2400.0
+            roofline["frac_at_measured_clock"] = round(k3_tflops / peak_at_clock, 4)
+            roofline["peak_at_measured_clock"] = round(peak_at_clock, 1)
     if not args.no_cpu_baseline:
         extra("cpu_baseline", lambda: cpu_baseline(wl, inp))
     print(json.dumps(line))
