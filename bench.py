@@ -32,6 +32,9 @@ Besides the headline the line carries:
                 against storing bf16 logits and reading them back
   tiny          the 64-row block, launch-bound: microseconds per block called eagerly and replayed from a HIP
                 graph
+  clock, mfma_ceiling  the shader clock under the block's load (rocm-smi), and what the matrix cores sustain on
+                random bf16 operands with no memory traffic (a probe build() compiles); the roofline adds K3's
+                fraction of each
   swiglu        the forward that also stores the SwiGLU pre-activation z (against the plain forward), and the
                 SwiGLU backward at the 1B down-projection shape, fused into the dgrad product's epilogue and
                 unfused (dy stored, then an elementwise pass)
@@ -324,6 +327,20 @@ def _read_sclk_mhz(raw: list):
         return _find_sclk(json.loads(p.stdout))
     except ValueError:
         return None
+
+
+def mfma_ceiling() -> dict:
+    """The device's MFMA-only rate on random bf16 operands (no memory traffic) and the shader clock it held, from
+    the probe build() compiles (gemm_epilogue_fusion_amd/csrc/mfma_ceiling.hip), run as a child process."""
+    import subprocess
+
+    exe = os.path.join(ROOT, "gemm_epilogue_fusion_amd", "mfma_ceiling")
+    if not os.path.exists(exe):
+        return {"error": "probe not built (build() compiles it)"}
+    p = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    rec = json.loads(p.stdout.strip().splitlines()[-1])
+    rec["source"] = "gemm_epilogue_fusion_amd/csrc/mfma_ceiling.hip"
+    return rec
 
 
 def clock_under_load(fn, torch, seconds: float = 1.5) -> dict:
@@ -819,6 +836,12 @@ def main() -> int:
             peak_at_clock = MFMA_BF16_PEAK_TFLOPS * mhz / 2400.0
             roofline["frac_at_measured_clock"] = round(k3_tflops / peak_at_clock, 4)
             roofline["peak_at_measured_clock"] = round(peak_at_clock, 1)
+    if not args.no_clock:
+        extra("mfma_ceiling", mfma_ceiling)
+        ceil = line.get("mfma_ceiling", {}).get("tflops")
+        if ceil:
+            # the same kernel against what the matrix cores sustain on random data with no memory traffic at all
+            roofline["frac_of_mfma_ceiling"] = round(k3_tflops / ceil, 4)
     if not args.no_cpu_baseline:
         extra("cpu_baseline", lambda: cpu_baseline(wl, inp))
     print(json.dumps(line))

@@ -87,7 +87,24 @@ def build(verbose: bool = False) -> str:
                   file=sys.stderr)
     os.replace(tmp, LIB)
     write_build_info()
+    build_mfma_ceiling()
     return LIB
+
+
+CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
+CEILING_EXE = os.path.join(PKG, "mfma_ceiling")
+
+
+def build_mfma_ceiling() -> str:
+    """The MFMA-only probe bench.py runs to measure the device's matrix-core ceiling (not part of the library)."""
+    tmp = CEILING_EXE + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-o", tmp, CEILING_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    os.replace(tmp, CEILING_EXE)
+    return CEILING_EXE
 
 
 def write_build_info() -> None:
