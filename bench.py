@@ -17,8 +17,9 @@ Besides the headline the line carries:
                 write before each call pushes the operands out of the 256 MB MALL)
   roofline      the dominant kernel (GEMM2 as the block launches it) timed alone with HIP events on the stream
                 it runs on, its algorithmic flops (2 M D N2) per launch divided by the average launch time,
-                against the published bf16 dense MFMA peak (2.5 PFLOP/s); traffic from the committed rocprofv3
-                counter summary if it was taken on the current kernel sources, else null
+                against the published bf16 dense MFMA peak (2.5 PFLOP/s); traffic (K3's bytes per launch at the L2's
+                memory side) from the committed rocprofv3 counter summary
+                (profiles/hbm_bytes_1b_attn_out_mlp_in.json) if it was taken on the current kernel sources, else null
   cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the same workload (rows are
                 independent), scaled to TFLOP/s
   unfused       the three-kernel baseline timed the same way, and the algorithmic HBM bytes both paths move
@@ -56,7 +57,6 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X published dense fp8 MFMA peak
 HBM_PEAK_GBS = 8000.0
 METRIC = "fused block TFLOP/s + % bf16 MFMA peak at 1B shape M=8192; HBM bytes saved"
 KERNEL_SOURCES = ["gemm_epilogue_fusion_amd/csrc/gemm_core.h", "gemm_epilogue_fusion_amd/csrc/kernels.hip"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm2_rowscale_1b_attn_out_mlp_in.json")
 
 
 def kernel_source_hash() -> str:
@@ -619,13 +619,16 @@ def time_swiglu(wl, X, W1, R, g, W2, dev, n_ev: int, warmup: int, torch, cb) -> 
 
 
 def traffic_record(src_hash: str):
-    if not os.path.exists(TRAFFIC_FILE):
+    """K3's measured bytes per launch (reads + writes at the L2's memory side) from the committed counter summary,
+    if it was taken on the current kernel sources."""
+    if not os.path.exists(HBM_FILE):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(HBM_FILE) as f:
         rec = json.load(f)
     if rec.get("kernel_source_hash") != src_hash:
         return None
-    return rec
+    k3 = rec["kernels"]["K3"]
+    return {"bytes_per_launch": k3["read_bytes"] + k3["write_bytes"]}
 
 
 def main() -> int:
@@ -842,6 +845,12 @@ def main() -> int:
         if ceil:
             # the same kernel against what the matrix cores sustain on random data with no memory traffic at all
             roofline["frac_of_mfma_ceiling"] = round(k3_tflops / ceil, 4)
+        ceil8 = line.get("mfma_ceiling", {}).get("fp8", {}).get("tflops")
+        f8 = line.get("fp8", {})
+        if ceil8 and "tflops" in f8:
+            f8["frac_of_fp8_mfma_ceiling"] = round(f8["tflops"] / ceil8, 4)
+            if "tflops" in f8.get("block_scaled", {}):
+                f8["block_scaled"]["frac_of_fp8_mfma_ceiling"] = round(f8["block_scaled"]["tflops"] / ceil8, 4)
     if not args.no_cpu_baseline:
         extra("cpu_baseline", lambda: cpu_baseline(wl, inp))
     print(json.dumps(line))

@@ -497,12 +497,12 @@ __device__ __forceinline__ int64_t mx_scale_index(int kt, int tiles_m, int m, in
 // second half multiplies row blocks 2,3 while the next stage's X is read into the other buffer.
 // MX: asc_g is the A operand's scale array (layout above, tiles_m row tiles) and mx_smem the MX_STAGE_BYTES x
 // NSTAGE staging area; each wave adds one 4-byte-per-lane direct load per stage.  hook() as in gemm_mainloop.
-template <bool MX = false, class BCol, class Hook = NoHook>
+template <bool MX = false, class BCol, class Hook = NoHook, class Drain = NoDrain>
 __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A, ALayout al, int M, int m0,
                                                   const uint8_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
                                                   char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{},
                                                   const uint8_t* __restrict__ asc_g = nullptr,
-                                                  char* mx_smem = nullptr) {
+                                                  char* mx_smem = nullptr, Drain drain = Drain{}) {
   constexpr int LPW = 16 / NWAVES;
   constexpr int PER = 2 * LPW + (MX ? 1 : 0);
   const int t = threadIdx.x;
@@ -559,12 +559,15 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
   };
 
   i32x8 xb[2][NB], xa[2][2], ya[2];
-  // one K step on stage U; X[U % 2] holds the stage's B and A row blocks 0,1 on entry
-  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c) {
+  // one K step on stage U; X[U % 2] holds the stage's B and A row blocks 0,1 on entry.  Every fragment of stage U
+  // is in registers by the mid-step barrier (B and A blocks 0,1 from the previous step, A blocks 2,3 read before
+  // the barrier), so DRAIN >= 0 hands the stage to drain(DRAIN) right after it, as in gemm_mainloop
+  auto step = [&](int kt, auto U_c, auto issue_c, auto wait_c, auto drain_c) {
     constexpr int U = decltype(U_c)::value;
     constexpr int P = U & 1;
     constexpr bool ISSUE = decltype(issue_c)::value;
     constexpr int WAIT = decltype(wait_c)::value;
+    constexpr int DRAIN = decltype(drain_c)::value;
     const char* cur = smem + U * STAGE_BYTES;
     if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
     // MX: this stage's scale word, read first so that the first MFMAs wait for it alone (one register: a
@@ -580,6 +583,7 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
     }
     if (WAIT >= 0) {
       wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
+      if (DRAIN >= 0 && Drain::LOADS > 0) drain(DRAIN);
       const char* nxt = smem + ((U + 1) % NSTAGE) * STAGE_BYTES;
       read_b8(nxt, lo, xb[1 - P]);
       xa[1 - P][0] = read_a8(nxt, lo, 0);
@@ -608,19 +612,23 @@ __device__ __forceinline__ void gemm_mainloop_fp8(const uint8_t* __restrict__ A,
   xa[0][0] = read_a8(smem, lo, 0);
   xa[0][1] = read_a8(smem, lo, 1);
 
+  using NoD = std::integral_constant<int, -1>;
+  constexpr int DL = Drain::LOADS;
+  static_assert(PER + DL < 64 && 2 * DL < 64, "vmcnt range");
   const int nblk = nk / NSTAGE;
   for (int bi = 0; bi < nblk - 1; ++bi) {
     const int kt = bi * NSTAGE;
-    step(kt + 0, S0{}, Yes{}, WaitFull{});
-    step(kt + 1, S1{}, Yes{}, WaitFull{});
-    step(kt + 2, S2{}, Yes{}, WaitFull{});
-    step(kt + 3, S3{}, Yes{}, WaitFull{});
+    step(kt + 0, S0{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 1, S1{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 2, S2{}, Yes{}, WaitFull{}, NoD{});
+    step(kt + 3, S3{}, Yes{}, WaitFull{}, NoD{});
   }
+  // the last block: the waits shrink as the ring drains and count the drain's loads issued after the stage loads
   const int kt = (nblk - 1) * NSTAGE;
-  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{});
-  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER>{});
-  step(kt + 2, S2{}, No{}, std::integral_constant<int, 0>{});
-  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{});
+  step(kt + 0, S0{}, Yes{}, std::integral_constant<int, 2 * PER>{}, S0{});
+  step(kt + 1, S1{}, No{}, std::integral_constant<int, PER + DL>{}, S1{});
+  step(kt + 2, S2{}, No{}, std::integral_constant<int, 2 * DL>{}, S2{});
+  step(kt + 3, S3{}, No{}, std::integral_constant<int, -1>{}, NoD{});
 }
 
 // Global column of the tile's column chunk c when the tile's 256 accumulator columns are one contiguous
