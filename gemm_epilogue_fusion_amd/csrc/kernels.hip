@@ -237,19 +237,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     // h * gamma is written by the bf16 K1 only (the e4m3 path forms it in K2 from the stored h)
     constexpr bool WRITE_HG = MODE == MODE_RES_PRMS && !FP8;
     const int n_base = tn * BN + wn * 64 + 4 * half;
-    if (MODE == MODE_RES_PRMS) {
-      // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows); the mainloop has
-      // fetched rows 0 .. 191 as its ring drained
-      load_tile_rows64<32>(R, Nb, m0, tn * BN, M, smem, 192);
-      wait_barrier<0>();
-    }
-    // gamma of this lane's 4-column groups (the same for every row)
+    // gamma of this lane's 4-column groups (the same for every row), loaded before the wait for the residual tile
+    // so that the two latencies overlap
     f32x4 gv[NB][4];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq)
         gv[nb][gq] = WRITE_HG ? *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+    if (MODE == MODE_RES_PRMS) {
+      // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows); the mainloop has
+      // fetched rows 0 .. 191 as its ring drained
+      load_tile_rows64<32>(R, Nb, m0, tn * BN, M, smem, 192);
+      wait_barrier<0>();
+    }
     float ss[4];
     u32x2 hgv[4][NB][4];  // bf16(h * gamma), staged after h has been written out
 #pragma unroll
