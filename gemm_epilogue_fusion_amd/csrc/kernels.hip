@@ -227,6 +227,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       rsv[mb] = ((FP8 || ROWSCALE_MODE) && rowsc) ? rowsc[m < M ? m : M - 1] : 1.0f;
     }
   }
+  // e4m3: this lane's column dequantisation scales, loaded once per tile (32 registers; the mainloop's fragments
+  // are dead by now) and before the barrier, so their latency overlaps it.  SwiGLU: csv[0..3] gate, csv[4..7] up
+  // columns; otherwise csv[4 nb + gq] for accumulator block nb, column group gq.
+  f32x4 csv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t col = MODE == MODE_ROWSCALE_SWIGLU
+                            ? (j < 4 ? 0 : Nb / 2) + tn * 128 + wn * 32 + 4 * half + 8 * (j & 3)
+                            : tn * BN + wn * 64 + 4 * half + (j >> 2) * 32 + 8 * (j & 3);
+    csv[j] = (FP8 && colsc) ? *(const f32x4*)(colsc + col) : (f32x4){1.f, 1.f, 1.f, 1.f};
+  }
   __syncthreads();  // every wave is done with the mainloop's LDS stages (and the folded row scales are in)
   if (CAN_FOLD && folding) {
 #pragma unroll
@@ -256,22 +267,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int r = wm * 128 + mb * 32 + (lane & 31);
-      // this row block's column scales as one batch of loads (re-read per row block from L1 rather than
-      // held: registers are the scarce resource here)
-      f32x4 cv[NB][4];
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          cv[nb][gq] = (FP8 && colsc) ? *(const f32x4*)(colsc + n_base + nb * 32 + 8 * gq)
-                                      : (f32x4){1.f, 1.f, 1.f, 1.f};
       float s = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           char* slot = smem + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half;
-          const f32x4 c = cv[nb][gq];
+          const f32x4 c = csv[nb * 4 + gq];
           const float sc = rsv[mb];
           float v0 = acc[mb][nb][4 * gq + 0] * sc * c[0], v1 = acc[mb][nb][4 * gq + 1] * sc * c[1];
           float v2 = acc[mb][nb][4 * gq + 2] * sc * c[2], v3 = acc[mb][nb][4 * gq + 3] * sc * c[3];
@@ -435,19 +437,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     for (int mb = 0; mb < 4; ++mb) {
       const int r = wm * 128 + mb * 32 + (lane & 31);
       const float sc = rsv[mb];
-      f32x4 cg[4], cu[4];
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        cg[gq] = (FP8 && colsc) ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
-        cu[gq] = (FP8 && colsc) ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
-      }
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         float y[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float gate = acc[mb][0][4 * gq + e] * sc * cg[gq][e];
-          const float up = acc[mb][1][4 * gq + e] * sc * cu[gq][e];
+          const float gate = acc[mb][0][4 * gq + e] * sc * csv[gq][e];
+          const float up = acc[mb][1][4 * gq + e] * sc * csv[4 + gq][e];
           y[e] = silu_f32(gate) * up;
         }
         *(u32x2*)(smem + tile_off<16>(r, wn * 4 + gq) + 8 * half) =
@@ -466,8 +462,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         const float sc = rsv[mb];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const f32x4 cg = (FP8 && colsc) ? *(const f32x4*)(colsc + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
-          const f32x4 cu = (FP8 && colsc) ? *(const f32x4*)(colsc + ny + c_base + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+          const f32x4 cg = csv[gq], cu = csv[4 + gq];
           float g[4], u[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
