@@ -21,7 +21,7 @@ Besides the headline the line carries:
                 memory side) from the committed rocprofv3 counter summary
                 (profiles/hbm_bytes_1b_attn_out_mlp_in.json) if it was taken on the current kernel sources, else null
   cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the same workload (rows are
-                independent), scaled to TFLOP/s
+                independent), scaled to TFLOP/s, and the GPU block's outputs on those rows compared with it
   unfused       the three-kernel baseline timed the same way, and the algorithmic HBM bytes both paths move
   fp8           the same block with e4m3 X / W1 / W2 (per-row and per-column fp32 scales), fused and unfused,
                 and the block-scaled variant, timed with HIP events, against the dense fp8 MFMA peak (5 PFLOP/s)
@@ -397,7 +397,10 @@ def step_distribution(fn, n: int, torch, scrub=None) -> dict:
     return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "n": n}
 
 
-def cpu_baseline(wl, inp, target_s: float = 15.0) -> dict:
+def cpu_baseline(wl, inp, gpu=None, target_s: float = 15.0) -> dict:
+    """The fp64 oracle (fused order) timed on the host on rows 0 .. n-1 of the workload, n sized to about target_s
+    seconds, scaled to TFLOP/s.  gpu = (h, y, r) of the GPU's block on the same inputs: the oracle's rows are then
+    also compared with the GPU's (normwise and mean errors), after the timing."""
     import numpy as np
     import torch
 
@@ -412,12 +415,22 @@ def cpu_baseline(wl, inp, target_s: float = 15.0) -> dict:
     dt = time.perf_counter() - t0
     rows2 = int(min(wl.M, max(rows, rows * target_s / max(dt, 1e-3))))
     t0 = time.perf_counter()
-    oracle.block_fused(f(inp.X[:rows2]), W1, f(inp.R[:rows2]), g, W2, wl.eps, wl.epi)
+    oh, orr, oy = oracle.block_fused(f(inp.X[:rows2]), W1, f(inp.R[:rows2]), g, W2, wl.eps, wl.epi)
     dt2 = time.perf_counter() - t0
-    return {"value": round(per_row * rows2 / dt2 / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.default_threads(),
-            "kind": "oracle",
-            "sample": f"fp64 oracle (fused order) on rows 0..{rows2 - 1} of the {wl.M}-row workload, {dt2:.1f} s; "
-                      f"rows are independent so the rate scales to the full block"}
+    rec = {"value": round(per_row * rows2 / dt2 / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.default_threads(),
+           "kind": "oracle",
+           "sample": f"fp64 oracle (fused order) on rows 0..{rows2 - 1} of the {wl.M}-row workload, {dt2:.1f} s; "
+                     f"rows are independent so the rate scales to the full block"}
+    if gpu is not None:
+        gh, gy, gr = (f(t[:rows2]) for t in gpu)
+        scale = lambda o: max(float(np.max(np.abs(o))), 1e-30)
+        rec["parity_on_these_rows"] = {
+            "rows": rows2, "y_normwise": float(np.max(np.abs(gy - oy)) / scale(oy)),
+            "y_mae_rel": float(np.mean(np.abs(gy - oy)) / scale(oy)),
+            "h_normwise": float(np.max(np.abs(gh - oh)) / scale(oh)),
+            "r_max_rel": float(np.max(np.abs(gr - orr) / np.abs(orr))),
+            "bars": "y normwise <= 2e-2, y MAE/max|o| <= 1e-3, h normwise <= 1e-2"}
+    return rec
 
 
 def time_fp8(dev, n_ev: int, warmup: int, torch, cb) -> dict:
@@ -852,7 +865,12 @@ def main() -> int:
             if "tflops" in f8.get("block_scaled", {}):
                 f8["block_scaled"]["frac_of_fp8_mfma_ceiling"] = round(f8["block_scaled"]["tflops"] / ceil8, 4)
     if not args.no_cpu_baseline:
-        extra("cpu_baseline", lambda: cpu_baseline(wl, inp))
+        def gpu_outputs():  # the block's outputs on these inputs, for the oracle leg's comparison
+            step()
+            torch.cuda.synchronize()
+            return h.clone(), y.clone(), cb.workspace_r(ws, wl.M, wl.D).clone()
+
+        extra("cpu_baseline", lambda: cpu_baseline(wl, inp, gpu_outputs()))
     print(json.dumps(line))
     return 0
 

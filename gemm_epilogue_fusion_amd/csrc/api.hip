@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdint>
+#include <cstdlib>
 #include <mutex>
 #include <string>
 
@@ -31,8 +32,22 @@ int ok() {
   return CODA_OK;
 }
 
+// CODA_SYNC_CHECK=1 in the environment (read at every launch, so a test can switch it): each launch is followed by
+// a device synchronisation and an error check, so that a device-side failure is reported by the entry point and
+// the launch that caused it rather than at the caller's next synchronisation.  A debugging aid: it serialises the
+// caller's streams, and it cannot be used under graph capture (the synchronisation fails there).
+bool sync_check() {
+  const char* v = std::getenv("CODA_SYNC_CHECK");
+  return v && *v && *v != '0';
+}
+
 int hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(CODA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  if (sync_check()) {
+    hipError_t s = hipDeviceSynchronize();
+    if (s == hipSuccess) s = hipGetLastError();
+    if (s != hipSuccess) return fail(CODA_ERR_HIP, "%s (CODA_SYNC_CHECK): %s", what, hipGetErrorString(s));
+  }
   return ok();
 }
 

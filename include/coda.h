@@ -44,6 +44,10 @@
  *     returns its code and enqueues nothing.  A launch failure returns CODA_ERR_HIP.  Device faults surface
  *     at the caller's next synchronisation.  No C++ exception crosses this boundary and nothing aborts.
  *     coda_last_error() gives a human-readable detail of the last failure on the calling thread.
+ *   - Debugging: with CODA_SYNC_CHECK=1 in the environment every launch is followed by a device synchronisation
+ *     and an error check, so a device-side failure is reported (CODA_ERR_HIP, the launch named in
+ *     coda_last_error()) by the call that caused it.  It serialises the caller's streams and fails under graph
+ *     capture; never set it for timing.
  */
 #ifndef CODA_H
 #define CODA_H

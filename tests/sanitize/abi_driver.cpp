@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 
 #include "coda.h"
 
@@ -123,6 +124,12 @@ int main() {
   EXPECT_EQ(g_launches - before, 4);
   EXPECT_EQ(coda_block_fwd_noalloc(P(1), P(2), P(3), F(4), P(5), -1.0f, 1, P(6), P(7), M, K1, D, N2, nullptr),
             CODA_ERR_INVALID_ARG);
+  // the debugging mode: every launch followed by a synchronisation and a check (stubbed here: it must still pass)
+  setenv("CODA_SYNC_CHECK", "1", 1);
+  before = g_launches;
+  EXPECT_EQ(coda_block_fwd(P(1), P(2), P(3), F(4), P(5), 1e-5f, 1, P(6), P(7), M, K1, D, N2, P(8), ws, nullptr), 0);
+  EXPECT_EQ(g_launches - before, 2);
+  unsetenv("CODA_SYNC_CHECK");
   if (failures) std::fprintf(stderr, "%d expectation(s) failed\n", failures);
   else std::printf("abi driver: %d launcher calls, every status as documented\n", g_launches);
   return failures ? 1 : 0;

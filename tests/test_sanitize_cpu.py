@@ -55,6 +55,8 @@ def _stub_source(fatbin_symbol: str) -> str:
     out.append("}  // namespace coda")
     out.append('extern "C" {')
     out.append("hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }")
+    out.append("hipError_t hipDeviceSynchronize() { return hipSuccess; }")
+    out.append("hipError_t hipGetLastError() { return hipSuccess; }")
     out.append('const char* hipGetErrorString(hipError_t) { return "stub"; }')
     out.append("hipError_t hipGetSymbolAddress(void** p, const void*) { *p = (void*)((uintptr_t)3 << 44); "
                "return hipSuccess; }")
