@@ -210,8 +210,20 @@ def summarize_hbm_counters(dirs: list, out: str, wl) -> dict:
     return rec
 
 
-def time_loop(fn, n: int, torch) -> float:
-    """Average ms per call of fn over n back-to-back calls, with HIP events on the current stream."""
+EXTRAS_SETTLE_MS = 200.0  # untimed calls before each secondary measurement (set from --settle-ms in main)
+
+
+def time_loop(fn, n: int, torch, settle_ms: float = None) -> float:
+    """Average ms per call of fn over n back-to-back calls, with HIP events on the current stream, after untimed
+    calls for settle_ms of wall time (default EXTRAS_SETTLE_MS; the device clock needs some milliseconds of a
+    steady load to settle, and a short window right after other work would otherwise inherit its state)."""
+    settle_ms = EXTRAS_SETTLE_MS if settle_ms is None else settle_ms
+    if settle_ms > 0:
+        t_end = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record()
@@ -693,6 +705,8 @@ def main() -> int:
         print("bench.py: no GPU", file=sys.stderr)
         return 2
     cb.load()
+    global EXTRAS_SETTLE_MS
+    EXTRAS_SETTLE_MS = min(args.settle_ms, 200.0)
     wl = WORKLOADS[args.workload]
     if wl.fp8:
         print("bench.py: fp8 workload is benchmarked with its own entry point", file=sys.stderr)
@@ -803,7 +817,9 @@ def main() -> int:
             "settle_ms": args.settle_ms, "settle_calls": settled,
             "fused_per_step_events_ms": per_step_summary(per_fused),
             "events_ms": "HIP events on the calls' stream: in the timed window one event before each call "
-                         "(per_step), elsewhere one pair around n back-to-back calls (mean per call)",
+                         "(per_step), elsewhere one pair around n back-to-back calls (mean per call) after "
+                         "extras_settle_ms of untimed calls of the same function",
+            "extras_settle_ms": EXTRAS_SETTLE_MS,
         },
         "unfused": {"ms_per_step_wall": round(unf_ms, 4), "per_step_events_ms": per_step_summary(per_unfused),
                     "tflops_wall": round(wl.flops / (unf_ms * 1e-3) / 1e12, 2),
