@@ -643,14 +643,14 @@ def time_swiglu(wl, X, W1, R, g, W2, dev, n_ev: int, warmup: int, torch, cb) -> 
                          "hbm_bytes_saved_algorithmic": 2 * 2 * bw.M * bw.F}}
 
 
-def traffic_record(src_hash: str):
+def traffic_record(src_hash: str, wl_name: str):
     """K3's measured bytes per launch (reads + writes at the L2's memory side) from the committed counter summary,
-    if it was taken on the current kernel sources."""
+    if it was taken on the current kernel sources at this workload."""
     if not os.path.exists(HBM_FILE):
         return None
     with open(HBM_FILE) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != src_hash:
+    if rec.get("kernel_source_hash") != src_hash or rec.get("workload") != wl_name:
         return None
     k3 = rec["kernels"]["K3"]
     return {"bytes_per_launch": k3["read_bytes"] + k3["write_bytes"]}
@@ -793,12 +793,14 @@ def main() -> int:
     k3_flops = 2 * wl.M * wl.D * wl.N2
     k3_tflops = k3_flops / (k3_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
-    traffic = traffic_record(src_hash)
+    traffic = traffic_record(src_hash, wl.name)
     roofline = {"bound": "mfma", "achieved": round(k3_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(k3_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "kernel": "gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU> as the block launches it (GEMM2 on h * gamma "
-                          "in K panels, partial-RMS reduce folded in, row scale + SwiGLU)",
+                "kernel": ("gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU> as the block launches it (GEMM2 on h * gamma "
+                           "in K panels, partial-RMS reduce folded in, row scale + SwiGLU)" if wl.epi == 1 else
+                           "gemm_epilogue_kernel<MODE_ROWSCALE> as the block launches it (GEMM2 on h * gamma in K "
+                           "panels, partial-RMS reduce folded in, row scale, identity epilogue)"),
                 "kernel_ms": round(k3_ms, 4), "algorithmic_flops_per_launch": k3_flops}
 
     fb, ub = algorithmic_bytes(wl, True), algorithmic_bytes(wl, False)
