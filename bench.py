@@ -755,8 +755,16 @@ def main() -> int:
     hg = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
     hgp = torch.empty(wl.D // 32, wl.M, 32, dtype=torch.bfloat16, device=dev)
     n_ev = max(20, args.steps // 2)
+    # the block folds the reduce into K3 where D / 256 <= 16 (D <= 4096); above that the reduce is a kernel of its
+    # own and K3 reads r
+    fold = wl.D // 256 <= 16
     k1p = lambda: cb.coda_gemm1_residual_partial_rms_panels(X, W1, R, g, h, hgp, part)
-    k3p = lambda: cb.coda_gemm2_rowscale_panels(hgp, W2, part, wl.eps, r, wl.epi, y)
+    if fold:
+        k3p = lambda: cb.coda_gemm2_rowscale_panels(hgp, W2, part, wl.eps, r, wl.epi, y)
+    else:
+        cb.coda_gemm1_residual_partial_rms_panels(X, W1, R, g, h, hgp, part)
+        cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r)
+        k3p = lambda: cb.coda_gemm2_rowscale_panels(hgp, W2, None, wl.eps, r, wl.epi, y)
     k1 = lambda: cb.coda_gemm1_residual_partial_rms(X, W1, R, g, h, hg, part)
     k2 = lambda: cb.coda_partial_rms_reduce(part, wl.D, wl.eps, r)
     k3 = lambda: cb.coda_gemm2_rowscale(hg, W2, r, wl.epi, y)
@@ -797,10 +805,10 @@ def main() -> int:
     roofline = {"bound": "mfma", "achieved": round(k3_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(k3_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                 "traffic": traffic["bytes_per_launch"] if traffic else None,
-                "kernel": ("gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU> as the block launches it (GEMM2 on h * gamma "
-                           "in K panels, partial-RMS reduce folded in, row scale + SwiGLU)" if wl.epi == 1 else
-                           "gemm_epilogue_kernel<MODE_ROWSCALE> as the block launches it (GEMM2 on h * gamma in K "
-                           "panels, partial-RMS reduce folded in, row scale, identity epilogue)"),
+                "kernel": ("gemm_epilogue_kernel<MODE_ROWSCALE_SWIGLU>" if wl.epi == 1 else
+                           "gemm_epilogue_kernel<MODE_ROWSCALE>") + " as the block launches it (GEMM2 on h * gamma in K "
+                          "panels, " + ("partial-RMS reduce folded in" if fold else "r from the reduce kernel") +
+                          ", row scale" + (" + SwiGLU)" if wl.epi == 1 else ", identity epilogue)"),
                 "kernel_ms": round(k3_ms, 4), "algorithmic_flops_per_launch": k3_flops}
 
     fb, ub = algorithmic_bytes(wl, True), algorithmic_bytes(wl, False)
@@ -829,7 +837,7 @@ def main() -> int:
                     "speedup_fused_vs_unfused_events_same_window": round(ev_u / ev_f, 4),
                     "ms_per_call_events": round(unf_ev_ms, 4), "fused_ms_per_call_events": round(fused_ev_ms, 4),
                     "speedup_fused_vs_unfused_events": round(unf_ev_ms / fused_ev_ms, 4)},
-        "kernels_ms": {"gemm1_res_prms": round(k1p_ms, 4), "gemm2_rowscale_fold": round(k3_ms, 4),
+        "kernels_ms": {"gemm1_res_prms": round(k1p_ms, 4), ("gemm2_rowscale_fold" if fold else "gemm2_rowscale"): round(k3_ms, 4),
                        "fused_block_events": round(fused_ev_ms, 4),
                        "row_major_steps": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
                                            "gemm2_rowscale": round(k3r_ms, 4),

@@ -55,8 +55,8 @@ class Workload:
         return replace(self, **kw)
 
 
-# The five workloads.  "tiny" is the case the oracle finishes in well under a second; the others are the
-# full-size shapes.
+# The workloads.  "tiny" is the case the oracle finishes in well under a second; the others are the full-size
+# shapes.
 WORKLOADS: Dict[str, Workload] = {
     "tiny": Workload("tiny", M=64, K1=256, D=256, N2=512, epi=EPI_IDENTITY, eps=1e-6,
                      w1_std=(1 / 256) ** 0.5, w2_std=(1 / 256) ** 0.5),
@@ -70,6 +70,10 @@ WORKLOADS: Dict[str, Workload] = {
     # attention output projection -> RMSNorm -> gate|up with SwiGLU, 8B-style (hidden 4096, inter 14336)
     "8b_attn_out_mlp_in": Workload("8b_attn_out_mlp_in", M=16384, K1=4096, D=4096, N2=28672,
                                    epi=EPI_SWIGLU, eps=1e-5),
+    # attention output projection -> RMSNorm -> gate|up with SwiGLU, 70B-style (hidden 8192, inter 28672): the
+    # largest hidden size the write-up's results name; D > 4096, so the partial-RMS reduce runs as its own kernel
+    "70b_attn_out_mlp_in": Workload("70b_attn_out_mlp_in", M=8192, K1=8192, D=8192, N2=57344,
+                                    epi=EPI_SWIGLU, eps=1e-5),
     # the 1B attention-out -> MLP-in block with e4m3 X / weights and per-row / per-column fp32 scales
     "1b_attn_out_mlp_in_fp8": Workload("1b_attn_out_mlp_in_fp8", M=8192, K1=2048, D=2048, N2=16384,
                                        epi=EPI_SWIGLU, eps=1e-5, fp8=True),

@@ -42,6 +42,8 @@ SMALL = [
     Workload("one_row", M=1, K1=128, D=256, N2=256, epi=EPI_SWIGLU, eps=1e-6, seed=3),
     Workload("many_tiles", M=777, K1=1024, D=1024, N2=2048, epi=EPI_SWIGLU, eps=1e-5, seed=4),
     Workload("k128_tail", M=257, K1=128, D=256, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=5),
+    # D / 256 = 17 > 16: the block runs the partial-RMS reduce as a kernel of its own instead of folding it
+    Workload("wide_d_unfolded", M=260, K1=128, D=4352, N2=256, epi=EPI_SWIGLU, eps=1e-5, seed=6),
 ]
 
 
@@ -59,7 +61,10 @@ def test_fused_block_small(wl):
     check_roundpts(f64(y), oy_rp)
 
 
-@pytest.mark.parametrize("wl", SMALL[:3], ids=[w.name for w in SMALL[:3]])
+UNFUSED_SMALL = SMALL[:3] + [SMALL[-1]]
+
+
+@pytest.mark.parametrize("wl", UNFUSED_SMALL, ids=[w.name for w in UNFUSED_SMALL])
 def test_unfused_block_small(wl):
     _say(f"[gpu] unfused block {wl}")
     inp = make_inputs(wl)
@@ -230,6 +235,35 @@ def test_full_size_all_rows(name):
     d = DeviceInputs(inp)
     h, y, r = run_block(d)
     check_all_rows(wl.M, h, y, r, oracle_chunk_fn(inp), say=_say)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_70b_hidden_sampled_rows(unfused):
+    """The 70B-style hidden size (D = 8192, SwiGLU over 2 x 28672 columns; the reduce as its own kernel) in the
+    benchmark's launch configuration, on rows that reach every row tile and every row position of an accumulator
+    block (every row would take the oracle minutes): h, y and r against the fused fp64 form, y against the
+    storage-rounding form; the unfused baseline against the oracle's unfused form."""
+    wl = WORKLOADS["70b_attn_out_mlp_in"]
+    _say(f"[gpu] 70B hidden, {'unfused' if unfused else 'fused'}, sampled rows {wl}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h, y, r = run_block(d, unfused=unfused)
+    rows = sample_rows_covering(wl.M, n=24)
+    idx = torch.as_tensor(rows, dtype=torch.long, device=y.device)
+    gh, gy = f64(h[idx]), f64(y[idx])
+    del h, y, d
+    torch.cuda.empty_cache()
+    oh, orr, oy = oracle_rows(inp, rows, form="unfused" if unfused else "fused")
+    check_h(gh, oh)
+    check_y(gy, oy)
+    if unfused:
+        # T = X W1 is stored in bf16 before the residual add (as in test_unfused_block_small)
+        np.testing.assert_allclose(f64(r[rows]), orr, rtol=2e-3)
+        return
+    np.testing.assert_allclose(f64(r[rows]), orr, rtol=2e-5)
+    _, _, oy_rp = oracle_rows(inp, rows, form="roundpts")
+    check_roundpts(gy, oy_rp)
 
 
 def test_largest_output_sampled_rows():
