@@ -445,6 +445,24 @@ def cpu_baseline(wl, inp, gpu=None, target_s: float = 15.0) -> dict:
     return rec
 
 
+def eager_block(X, W1, R, gamma, W2, wl, torch):
+    """The block as separate PyTorch operators on bf16 tensors, the kind of baseline the write-up measures
+    against (a vendor GEMM library plus framework operators): T = X W1 and z = n W2 through torch.matmul
+    (hipBLASLt on ROCm), the residual add, torch's RMSNorm and SwiGLU as operators of their own."""
+    import torch.nn.functional as F
+
+    g16 = gamma.to(torch.bfloat16)
+    half = wl.N2 // 2
+
+    def run():
+        hh = torch.matmul(X, W1) + R
+        n = F.rms_norm(hh, (wl.D,), g16, wl.eps)
+        z = torch.matmul(n, W2)
+        return F.silu(z[:, :half]) * z[:, half:] if wl.epi == 1 else z
+
+    return run
+
+
 def time_fp8(dev, n_ev: int, warmup: int, torch, cb) -> dict:
     """The e4m3 version of the headline block: fused and unfused, average ms per call by HIP events."""
     from gemm_epilogue_fusion_amd.inputs import WORKLOADS, make_inputs
@@ -744,6 +762,19 @@ def main() -> int:
         print(json.dumps({"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": ms}))
         return 0
     unf_ms, per_unfused, _ = timed_steps(step_unfused, args.steps, args.warmup, torch, args.settle_ms)
+    # context: the same block as PyTorch operators, timed the same way in a window of its own
+    eager = eager_block(X, W1, R, g, W2, wl, torch)
+    eager_ms, per_eager, _ = timed_steps(eager, args.steps, args.warmup, torch, args.settle_ms)
+    step()
+    y_eager = eager()
+    torch.cuda.synchronize()
+    eager_rec = {"what": "the block as PyTorch operators on bf16 tensors: torch.matmul (hipBLASLt) for both products, "
+                         "the residual add, torch.nn.functional.rms_norm and SwiGLU as separate operators",
+                 "ms_per_step_wall": round(eager_ms, 4), "per_step_events_ms": per_step_summary(per_eager),
+                 "speedup_fused_vs_eager_wall": round(eager_ms / ms, 4),
+                 "y_normwise_vs_fused": round(float((y_eager.float() - y.float()).abs().max()
+                                                    / y.float().abs().max().clamp_min(1e-30)), 5)}
+    del y_eager
 
     # per-step kernels timed alone with HIP events (same stream as the launches: torch's current stream).
     # The block's own kernels: K1 writing h * gamma in K panels, and K3 reading them with the reduce folded in
@@ -837,6 +868,7 @@ def main() -> int:
                     "speedup_fused_vs_unfused_events_same_window": round(ev_u / ev_f, 4),
                     "ms_per_call_events": round(unf_ev_ms, 4), "fused_ms_per_call_events": round(fused_ev_ms, 4),
                     "speedup_fused_vs_unfused_events": round(unf_ev_ms / fused_ev_ms, 4)},
+        "pytorch_eager": eager_rec,
         "kernels_ms": {"gemm1_res_prms": round(k1p_ms, 4), ("gemm2_rowscale_fold" if fold else "gemm2_rowscale"): round(k3_ms, 4),
                        "fused_block_events": round(fused_ev_ms, 4),
                        "row_major_steps": {"gemm1_res_prms": round(k1_ms, 4), "prms_reduce": round(k2_ms, 4),
