@@ -517,20 +517,39 @@ def time_bwd(wl, X, W1, g, W2, h, ws, n_ev: int, warmup: int, torch, cb) -> dict
     fused = lambda: cb.coda_block_bwd(X, W1, h, r, g, W2, dz, dho, *outs, wsf)
     fused_w2t = lambda: cb.coda_block_bwd_w2t(X, W1, h, r, g, W2t, dz, dho, *outs, wsf)
     unfused = lambda: cb.coda_block_bwd_unfused(X, W1, h, r, g, W2, dz, dho, *outs, wsu)
+    # context: the same gradients as PyTorch operators (bf16 products through torch.matmul, fp32 elementwise);
+    # the weights' transposes are made once outside the timing, the activations' (X^T, u^T) as copies inside it
+    W1t = W1.t().contiguous()
+    bf = torch.bfloat16
+    rc = r[:, None]
+
+    def eager():
+        n = h.float() * rc
+        u = (n * g).to(bf)
+        du = torch.matmul(dz, W2t).float()
+        dgamma = (du * n).sum(0)
+        dug = du * g
+        dh = (rc * (dug - n * (dug * n).mean(1, keepdim=True)) + dho.float()).to(bf)
+        return (torch.matmul(dh, W1t), torch.matmul(X.t().contiguous(), dh), dh, dgamma,
+                torch.matmul(u.t().contiguous(), dz))
+
     for _ in range(warmup):
         fused()
         fused_w2t()
         unfused()
+        eager()
     torch.cuda.synchronize()
     f_ms = time_loop(fused, n_ev, torch)
     t_ms = time_loop(fused_w2t, n_ev, torch)
     u_ms = time_loop(unfused, n_ev, torch)
+    e_ms = time_loop(eager, n_ev, torch)
     flops = 2 * wl.flops
     tf = flops / (f_ms * 1e-3) / 1e12
     return {"what": "dX, dW1, dR, dgamma, dW2 from dz and dh_out", "flops_per_call": flops, "fused_ms": round(f_ms, 4),
             "tflops": round(tf, 2), "pct_bf16_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2),
             "fused_w2t_ms": round(t_ms, 4), "unfused_ms": round(u_ms, 4),
-            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4)}
+            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4),
+            "pytorch_eager_ms": round(e_ms, 4), "speedup_fused_vs_pytorch_eager": round(e_ms / f_ms, 4)}
 
 
 def time_tiny(dev, torch, cb) -> dict:
@@ -614,19 +633,26 @@ def time_ce(dev, n_ev: int, warmup: int, torch, cb) -> dict:
     wsu = cb.alloc_ce_workspace(wl.M, wl.D, wl.V, unfused=1, device=dev)
     fused = lambda: cb.coda_ce_fwd(H, W, labels, loss, lse, ws)
     unfused = lambda: cb.coda_ce_unfused(H, W, labels, loss, lse, wsu)
+    # context: torch.matmul for the bf16 logits, then torch's cross-entropy over them in fp32 (labels < 0 ignored)
+    lab64 = labels.long()
+    eager = lambda: torch.nn.functional.cross_entropy(torch.matmul(H, W).float(), lab64, reduction="none",
+                                                       ignore_index=-100)
     for _ in range(warmup):
         fused()
         unfused()
+        eager()
     torch.cuda.synchronize()
     n = max(5, n_ev // 4)
     f_ms = time_loop(fused, n, torch)
     u_ms = time_loop(unfused, n, torch)
+    e_ms = time_loop(eager, n, torch)
     tf = wl.flops / (f_ms * 1e-3) / 1e12
     T = wl.V // 256
     saved = 2 * 2 * wl.M * wl.V - 2 * (2 * 4 * T * wl.M + 4 * wl.M)  # logits written + read, minus partials
     return {"workload": wl.name, "M": wl.M, "D": wl.D, "V": wl.V, "fused_ms": round(f_ms, 4), "tflops": round(tf, 2),
             "pct_bf16_mfma_peak": round(100 * tf / MFMA_BF16_PEAK_TFLOPS, 2), "unfused_ms": round(u_ms, 4),
-            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4), "hbm_bytes_saved_algorithmic": saved}
+            "speedup_fused_vs_unfused": round(u_ms / f_ms, 4), "pytorch_eager_ms": round(e_ms, 4),
+            "speedup_fused_vs_pytorch_eager": round(e_ms / f_ms, 4), "hbm_bytes_saved_algorithmic": saved}
 
 
 def time_swiglu(wl, X, W1, R, g, W2, dev, n_ev: int, warmup: int, torch, cb) -> dict:
@@ -646,18 +672,31 @@ def time_swiglu(wl, X, W1, R, g, W2, dev, n_ev: int, warmup: int, torch, cb) -> 
     wsu = torch.empty(cb.coda_swiglu_bwd_workspace_bytes(bw.M, bw.F, 1), dtype=torch.uint8, device=dev)
     fused = lambda: cb.coda_swiglu_bwd(dout, Wd, zz, dz)
     unfused = lambda: cb.coda_swiglu_bwd_unfused(dout, Wd, zz, dz, wsu)
+    # context: the same dz as PyTorch operators (dy through torch.matmul with Wd's transpose made once outside
+    # the timing, then silu's derivative in fp32)
+    WdT = Wd.t().contiguous()
+    F_ = bw.F
+
+    def eager():
+        dy = torch.matmul(dout, WdT).float()
+        gt, ut = zz[:, :F_].float(), zz[:, F_:].float()
+        sg = torch.sigmoid(gt)
+        return torch.cat(((dy * ut * sg * (1 + gt * (1 - sg))).to(torch.bfloat16), (dy * gt * sg).to(torch.bfloat16)), 1)
+
     for _ in range(warmup):
         plain()
         savez()
         fused()
         unfused()
+        eager()
     torch.cuda.synchronize()
-    p_ms, z_ms, f_ms, u_ms = (time_loop(fn, n_ev, torch) for fn in (plain, savez, fused, unfused))
+    p_ms, z_ms, f_ms, u_ms, e_ms = (time_loop(fn, n_ev, torch) for fn in (plain, savez, fused, unfused, eager))
     return {"forward_save_z": {"workload": wl.name, "ms": round(z_ms, 4), "plain_forward_ms": round(p_ms, 4),
                                "z_bytes_written": 2 * wl.M * wl.N2},
             "backward": {"workload": bw.name, "M": bw.M, "D": bw.D, "F": bw.F, "fused_ms": round(f_ms, 4),
                          "tflops": round(bw.flops / (f_ms * 1e-3) / 1e12, 2), "unfused_ms": round(u_ms, 4),
                          "speedup_fused_vs_unfused": round(u_ms / f_ms, 4),
+                         "pytorch_eager_ms": round(e_ms, 4), "speedup_fused_vs_pytorch_eager": round(e_ms / f_ms, 4),
                          "hbm_bytes_saved_algorithmic": 2 * 2 * bw.M * bw.F}}
 
 
