@@ -88,7 +88,7 @@ __device__ __forceinline__ void store_half_tile(const char* srcl, uint16_t* dst,
     const int r = p * 16 + t / 32;
     const u32x4 v = *(const u32x4*)(srcl + tile_off<32>(r, c));
     const int m = m0 + r;
-    if (m < M) *(u32x4*)(dst + (int64_t)m * ld + n0 + 8 * c) = v;
+    if (m < M) store_nt(dst + (int64_t)m * ld + n0 + 8 * c, v);
   }
 }
 
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
         const int c = t & 63;
         const f32x4 v = *(const f32x4*)(smem + f32_off(rr, c));
         const int m = m0 + hh * 128 + rr;
-        if (m < M) *(f32x4*)(args.outf + blockIdx.y * args.slab + (int64_t)m * Nb + n0 + 4 * c) = v;
+        if (m < M) store_nt(args.outf + blockIdx.y * args.slab + (int64_t)m * Nb + n0 + 4 * c, v);
       }
       __syncthreads();
     }
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_gemm_kernel(BwdArgs args) {
         const int sw = (q & 1) << 5;
         const f32x4 v = {src[(4 * c) ^ sw], src[(4 * c + 1) ^ sw], src[(4 * c + 2) ^ sw], src[(4 * c + 3) ^ sw]};
         const int col = m0 + hh * 128 + 4 * c;
-        if (col < M) *(f32x4*)(args.outf + blockIdx.y * args.slab + (int64_t)(n0 + q) * M + col) = v;
+        if (col < M) store_nt(args.outf + blockIdx.y * args.slab + (int64_t)(n0 + q) * M + col, v);
       }
       __syncthreads();
     }
@@ -435,7 +435,7 @@ __global__ __launch_bounds__(256) void slab_sum_kernel(const float* __restrict__
   f32x4 v = *(const f32x4*)(src + e);
   for (int s = 1; s < S; ++s) v += *(const f32x4*)(src + (int64_t)s * n + e);
   if (rowsc) v *= rowsc[e / cols];
-  *(f32x4*)(dst + e) = v;
+  store_nt(dst + e, v);
 }
 
 // B3: one 64 x 64 tile of [M, D] per workgroup.  dh = G - a_i h + dh_out (fp32, then bf16) -> dR; the same
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const uint16_t* __restrict_
       tn[c][ri_] = (uint16_t)(nv[q] & 0xffff);
       tn[c + 1][ri_] = (uint16_t)(nv[q] >> 16);
     }
-    *(u32x4*)(dR + i * D + j) = dv;
+    store_nt(dR + i * D + j, dv);
   }
   __syncthreads();
   // transposed rows: row j of the tile holds 64 values of i; 8 per thread-chunk, 512 chunks per tensor
@@ -490,8 +490,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(const uint16_t* __restrict_
     // [D, M] rows, or (panels) K panels over M of the weight-gradient products: ((m / 32) D + d) 32 + m % 32
     const int64_t off = panels ? ((int64_t)((i0 + ic) >> 5) * D + j0 + jr) * 32 + ((i0 + ic) & 31)
                                : (int64_t)(j0 + jr) * M + i0 + ic;
-    *(u32x4*)(dhT + off) = o1;
-    *(u32x4*)(nT + off) = o2;
+    store_nt(dhT + off, o1);
+    store_nt(nT + off, o2);
   }
 }
 
@@ -596,8 +596,8 @@ __global__ __launch_bounds__(256) void swiglu_bwd_rows_kernel(const uint16_t* __
   const float u[4] = {bf16_lo(uv[0]), bf16_hi(uv[0]), bf16_lo(uv[1]), bf16_hi(uv[1])};
   float dg[4], du[4];
   swiglu_bwd4(d, g, u, dg, du);
-  *(u32x2*)(dz + m * 2 * F + f) = (u32x2){pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3])};
-  *(u32x2*)(dz + m * 2 * F + F + f) = (u32x2){pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3])};
+  store_nt(dz + m * 2 * F + f, (u32x2){pack_bf16(dg[0], dg[1]), pack_bf16(dg[2], dg[3])});
+  store_nt(dz + m * 2 * F + F + f, (u32x2){pack_bf16(du[0], du[1]), pack_bf16(du[2], du[3])});
 }
 
 hipError_t launch_swiglu_bwd_rows(const uint16_t* dy, const uint16_t* z, uint16_t* dz, int M, int F,

@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void panelize_bf16_kernel(const uint16_t* __re
   const int c4 = threadIdx.x & 3;
   if (r >= M) return;
   const u32x4 v = *(const u32x4*)(src + (int64_t)r * D + 32 * p + 8 * c4);
-  *(u32x4*)(dst + ((int64_t)p * M + r) * 32 + 8 * c4) = v;
+  store_nt(dst + ((int64_t)p * M + r) * 32 + 8 * c4, v);
 }
 
 hipError_t launch_panelize_bf16(const uint16_t* src, int M, int D, uint16_t* dst, hipStream_t stream) {

@@ -640,6 +640,14 @@ struct ContiguousCols {
 };
 
 // ---- output tile staging in LDS -----------------------------------------------------------------------
+// Output tiles are written with the non-temporal hint (global_store ... nt).  Measured on the block's two GEMMs
+// back to back: with plain stores the pair took about 12 us more than the two kernels alone (the boundary
+// between them waits for the first kernel's written lines to leave the L2s); with the hint it takes their sum.
+__device__ __forceinline__ void store16_nt(uint16_t* p, u32x4 v) { __builtin_nontemporal_store(v, (u32x4*)p); }
+// The same hint for the other kernels' outputs (any vector type).
+template <class T>
+__device__ __forceinline__ void store_nt(void* p, T v) { __builtin_nontemporal_store(v, (T*)p); }
+
 // A bf16 tile of 256 rows x 8 CH columns: row r is 16 CH bytes, its 16-byte chunk c at slot c ^ (r % CH), so
 // both the lanes that write 32 rows of one chunk and the lanes that read one row's chunks spread over the
 // banks.
@@ -657,7 +665,7 @@ __device__ __forceinline__ void store_tile_rows(const char* smem, uint16_t* dst,
     const int r = p * ROWS_PER_PASS + t / CH;
     const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, c));
     const int m = m0 + r;
-    if (m < M) *(u32x4*)(dst + (int64_t)m * ld + n0 + 8 * c) = v;
+    if (m < M) store16_nt(dst + (int64_t)m * ld + n0 + 8 * c, v);
   }
 }
 
@@ -676,7 +684,7 @@ __device__ __forceinline__ void store_tile_panels(const char* smem, uint16_t* ds
     const int r = w >> 2, c4 = w & 3;
     const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, 4 * pn + c4));
     const int m = m0 + r;
-    if (m < M) *(u32x4*)(dst + (int64_t)(n0 / 32 + pn) * panel + (int64_t)m * 32 + 8 * c4) = v;
+    if (m < M) store16_nt(dst + (int64_t)(n0 / 32 + pn) * panel + (int64_t)m * 32 + 8 * c4, v);
   }
 }
 

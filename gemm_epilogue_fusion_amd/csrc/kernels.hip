@@ -383,8 +383,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
               }
             uint8_t* dq = panels ? hq + (int64_t)(col0 >> 6) * M * 64 + (int64_t)m * 64 + (col0 & 63)
                                  : hq + (int64_t)m * Nb + col0;
-            *(u32x4*)dq = q[0];
-            *(u32x4*)(dq + 16) = q[1];
+            store_nt(dq, q[0]);
+            store_nt(dq + 16, q[1]);
             mxs[mx_scale_index(col0 >> 6, tiles_m_k3, m, (col0 >> 5) & 1)] = (uint8_t)(e + 127);
           }
         }
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256) void prms_reduce_quant_kernel(const float* __r
     o[1] = pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv);
     // panels: [D / 64][M][64] bytes (the second GEMM's stage width), else row-major
     uint8_t* dq = panels ? hq + (int64_t)((8 * c) >> 6) * M * 64 + i * 64 + ((8 * c) & 63) : qrow + 8 * c;
-    *(u32x2*)dq = o;
+    store_nt(dq, o);
   };
 #pragma unroll
   for (int k = 0; k < CACHED; ++k) {
@@ -653,7 +653,7 @@ __global__ __launch_bounds__(256) void prms_reduce_quant_rows2_kernel(const floa
         o[0] = pack_e4m3x4(av[k][0] * inv, av[k][1] * inv, av[k][2] * inv, av[k][3] * inv);
         o[1] = pack_e4m3x4(av[k][4] * inv, av[k][5] * inv, av[k][6] * inv, av[k][7] * inv);
         uint8_t* dq = panels ? hq + (int64_t)((8 * c) >> 6) * M * 64 + i * 64 + ((8 * c) & 63) : hq + i * D + 8 * c;
-        *(u32x2*)dq = o;
+        store_nt(dq, o);
       }
     }
     if (lane == 0) {
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* __rest
         nv[i][e] = hv[i][e] * r * gg[e];
         amax = fmaxf(amax, fabsf(nv[i][e]));
       }
-      *(u32x4*)(H + row * D + 8 * c) = ho;
+      store_nt(H + row * D + 8 * c, ho);
     }
   }
   float qs = 1.0f;
@@ -741,12 +741,12 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(const uint16_t* __rest
         u32x2 o;
         o[0] = pack_e4m3x4(nv[i][0] / qs, nv[i][1] / qs, nv[i][2] / qs, nv[i][3] / qs);
         o[1] = pack_e4m3x4(nv[i][4] / qs, nv[i][5] / qs, nv[i][6] / qs, nv[i][7] / qs);
-        *(u32x2*)((uint8_t*)Nout + row * D + 8 * c) = o;
+        store_nt((uint8_t*)Nout + row * D + 8 * c, o);
       } else {
         u32x4 no;
 #pragma unroll
         for (int q = 0; q < 4; ++q) no[q] = pack_bf16(nv[i][2 * q], nv[i][2 * q + 1]);
-        *(u32x4*)((uint16_t*)Nout + row * D + 8 * c) = no;
+        store_nt((uint16_t*)Nout + row * D + 8 * c, no);
       }
     }
   }
