@@ -258,8 +258,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         gv[nb][gq] = WRITE_HG ? *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
     if (MODE == MODE_RES_PRMS) {
       // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows); the mainloop has
-      // fetched rows 0 .. 191 as its ring drained
-      load_tile_rows64<32>(R, Nb, m0, tn * BN, M, smem, 192);
+      // fetched rows 0 .. 191 as its ring drained.  A tile whose rows end before row 192 has nothing left to fetch
+      // (rows past M are never stored).
+      if (m0 + 192 < M) load_tile_rows64<32>(R, Nb, m0, tn * BN, M, smem, 192);
       wait_barrier<0>();
     }
     float ss[4];
