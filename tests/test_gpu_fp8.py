@@ -288,3 +288,54 @@ def test_fp8_mx_full_size_all_rows():
 
     r = wsc[off_r: off_r + 4 * M].view(torch.float32)
     check_all_rows(M, h, y, r, chunk, fp8=True, say=_say)
+
+
+# ---- seeded random shapes: the per-row, block-scaled and unfused e4m3 paths, each against the oracle ----
+
+def _fp8_random_shapes(n: int = 10, seed: int = 4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.choice([1, 3, 63, 65, 255, 257]) if i < 2 else rng.integers(1, 320))
+        K1 = 256 * int(rng.integers(1, 3))
+        D = 256 * int(rng.integers(1, 4))
+        N2 = 256 * int(rng.integers(1, 4))
+        epi = EPI_SWIGLU if rng.integers(0, 2) else EPI_IDENTITY
+        out.append(Workload(f"fp8rand{i}_M{M}_K{K1}_D{D}_N{N2}_{'swiglu' if epi else 'id'}", M=M, K1=K1, D=D,
+                            N2=N2, epi=epi, eps=1e-5, fp8=True, seed=200 + i))
+    return out
+
+
+FP8_RANDOM = _fp8_random_shapes()
+
+
+@pytest.mark.parametrize("wl", FP8_RANDOM, ids=[w.name for w in FP8_RANDOM])
+def test_fp8_random_shape(wl):
+    _say(f"[gpu] fp8 random shape {wl}")
+    inp = make_inputs(wl)
+    oh, orr, oy = _oracle_fp8(inp)
+    # per-row scales: end to end, r, and the quantiser bit for bit
+    h, y, ws = _run_fp8(inp)
+    check_h(f64(h), oh)
+    check_y(f64(y), oy, fp8=True)
+    w = _ws_rowq(ws, wl.M, wl.D)
+    np.testing.assert_allclose(w["r"], orr, rtol=2e-5)
+    _check_rowq_exact(w, h, inp.gamma)
+    # block-scaled A operand: end to end, the storage-rounding bar through the oracle's own quantiser, and the
+    # codes and exponents bit for bit
+    h, y, ws = _run_fp8_mx(inp)
+    check_h(f64(h), oh)
+    check_y(f64(y), oy, fp8=True)
+    M, D = wl.M, wl.D
+    off_r = _align256((D // 256) * M * 4)
+    off_q = off_r + _align256(M * 4)
+    off_s = off_q + _align256(M * D)
+    wsc = ws.cpu()
+    check_roundpts(f64(y), _oracle_mx_y(inp, oh, orr)[0])
+    q = _panels_to_rows(wsc[off_q: off_q + M * D], M, D).numpy()
+    _check_mx_exact(q, _mx_scales_from_workspace(wsc, M, D, off_s), h, inp.gamma)
+    # the unfused baseline against the oracle's unfused form
+    h, y, _ = _run_fp8(inp, unfused=True)
+    ouh, _, ouy = _oracle_fp8(inp, form="unfused")
+    check_h(f64(h), ouh)
+    check_y(f64(y), ouy, fp8=True)
