@@ -784,7 +784,8 @@ def main() -> int:
 
     # the headline: the contract's timing (host clock around exactly K calls after W warm-up calls), with a HIP
     # event before each call splitting the same window; the unfused baseline is timed the same way right after
-    ms, per_fused, settled = timed_steps(step, args.steps, args.warmup, torch, args.settle_ms)
+    with torch.cuda.nvtx.range("bench:headline_fused"):
+        ms, per_fused, settled = timed_steps(step, args.steps, args.warmup, torch, args.settle_ms)
     tflops = wl.flops / (ms * 1e-3) / 1e12
     if args.only_fused:
         if args.profile_unfused:
@@ -800,10 +801,12 @@ def main() -> int:
             torch.cuda.synchronize()
         print(json.dumps({"metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": ms}))
         return 0
-    unf_ms, per_unfused, _ = timed_steps(step_unfused, args.steps, args.warmup, torch, args.settle_ms)
+    with torch.cuda.nvtx.range("bench:headline_unfused"):
+        unf_ms, per_unfused, _ = timed_steps(step_unfused, args.steps, args.warmup, torch, args.settle_ms)
     # context: the same block as PyTorch operators, timed the same way in a window of its own
     eager = eager_block(X, W1, R, g, W2, wl, torch)
-    eager_ms, per_eager, _ = timed_steps(eager, args.steps, args.warmup, torch, args.settle_ms)
+    with torch.cuda.nvtx.range("bench:pytorch_eager"):
+        eager_ms, per_eager, _ = timed_steps(eager, args.steps, args.warmup, torch, args.settle_ms)
     step()
     y_eager = eager()
     torch.cuda.synchronize()
@@ -920,9 +923,12 @@ def main() -> int:
     }
     def extra(key, fn):
         # the further measurements: a Python-level failure in one of them (an error status from the library,
-        # an allocation failure) is recorded under its key and the line is still printed with the headline
+        # an allocation failure) is recorded under its key and the line is still printed with the headline.
+        # Each runs inside a named marker range (roctx through torch.cuda.nvtx), which a trace taken with
+        # rocprofv3 --marker-trace shows around the section's kernels.
         try:
-            line[key] = fn()
+            with torch.cuda.nvtx.range(f"bench:{key}"):
+                line[key] = fn()
         except Exception as e:  # noqa: BLE001
             print(f"bench: {key} failed: {e!r}", file=sys.stderr, flush=True)
             line[key] = {"error": repr(e)}
