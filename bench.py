@@ -409,10 +409,11 @@ def step_distribution(fn, n: int, torch, scrub=None) -> dict:
     return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "n": n}
 
 
-def cpu_baseline(wl, inp, gpu=None, target_s: float = 15.0) -> dict:
+def cpu_baseline(wl, inp, gpu=None, y_eager=None, target_s: float = 15.0) -> dict:
     """The fp64 oracle (fused order) timed on the host on rows 0 .. n-1 of the workload, n sized to about target_s
     seconds, scaled to TFLOP/s.  gpu = (h, y, r) of the GPU's block on the same inputs: the oracle's rows are then
-    also compared with the GPU's (normwise and mean errors), after the timing."""
+    also compared with the GPU's (normwise and mean errors), after the timing; y_eager (the block as PyTorch
+    operators) is compared on the same rows, so that the two errors can be set side by side."""
     import numpy as np
     import torch
 
@@ -442,6 +443,10 @@ def cpu_baseline(wl, inp, gpu=None, target_s: float = 15.0) -> dict:
             "h_normwise": float(np.max(np.abs(gh - oh)) / scale(oh)),
             "r_max_rel": float(np.max(np.abs(gr - orr) / np.abs(orr))),
             "bars": "y normwise <= 2e-2, y MAE/max|o| <= 1e-3, h normwise <= 1e-2"}
+        if y_eager is not None:
+            ey = f(y_eager[:rows2])
+            rec["parity_on_these_rows"]["pytorch_eager_y_normwise"] = float(np.max(np.abs(ey - oy)) / scale(oy))
+            rec["parity_on_these_rows"]["pytorch_eager_y_mae_rel"] = float(np.mean(np.abs(ey - oy)) / scale(oy))
     return rec
 
 
@@ -816,6 +821,7 @@ def main() -> int:
                  "speedup_fused_vs_eager_wall": round(eager_ms / ms, 4),
                  "y_normwise_vs_fused": round(float((y_eager.float() - y.float()).abs().max()
                                                     / y.float().abs().max().clamp_min(1e-30)), 5)}
+    y_eager_host = y_eager.cpu()  # for the oracle leg: the PyTorch operators' y against the oracle, same rows
     del y_eager
 
     # per-step kernels timed alone with HIP events (same stream as the launches: torch's current stream).
@@ -973,7 +979,7 @@ def main() -> int:
             torch.cuda.synchronize()
             return h.clone(), y.clone(), cb.workspace_r(ws, wl.M, wl.D).clone()
 
-        extra("cpu_baseline", lambda: cpu_baseline(wl, inp, gpu_outputs()))
+        extra("cpu_baseline", lambda: cpu_baseline(wl, inp, gpu_outputs(), y_eager_host))
     print(json.dumps(line))
     return 0
 
