@@ -197,3 +197,37 @@ def test_bwd_full_size_weight_grads_masked_rows(unfused):
     for name, w in (("dW1", want[1]), ("dgamma", want[3]), ("dW2", want[4])):
         err = _check(name, got[name], w)
         _say(f"    {name}: normwise {err:.3e}")
+
+
+def _random_shapes(n: int = 8, seed: int = 777):
+    """Seeded shapes within the backward's rules (M a multiple of 128, K1, D, N2 multiples of 256), both epilogues,
+    with and without dh_out, W2 given as is or transposed; small enough for the oracle to take well under a
+    second each."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = 128 * int(rng.integers(1, 9))
+        K1, D, N2 = (256 * int(rng.integers(1, 4)) for _ in range(3))
+        epi = EPI_SWIGLU if rng.integers(0, 2) else EPI_IDENTITY
+        dh, w2t = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+        wl = Workload(f"bwdrand{i}_M{M}_K{K1}_D{D}_N{N2}_{'swiglu' if epi else 'id'}{'_dh' if dh else ''}"
+                      f"{'_w2t' if w2t else ''}", M=M, K1=K1, D=D, N2=N2, epi=epi, eps=1e-5, w1_std=0.05,
+                      w2_std=0.05, seed=300 + i)
+        out.append((wl, dh, w2t))
+    return out
+
+
+# every shape on the fused path; the unfused path (which takes W2 as is) on the shapes without the transpose
+RANDOM = [(wl, dh, w2t, False) for wl, dh, w2t in _random_shapes()] + \
+         [(wl, dh, False, True) for wl, dh, w2t in _random_shapes() if not w2t]
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[f"{c[0].name}-{'unfused' if c[3] else 'fused'}" for c in RANDOM])
+def test_bwd_random_shape(case):
+    wl, dh, w2t, unfused = case
+    _say(f"[gpu] bwd random {'unfused' if unfused else 'fused'} {wl}")
+    inp, dz, dho, got = _run(wl, unfused=unfused, with_dh_out=dh, w2t=w2t)
+    want = oracle.block_bwd(f64(inp.X), f64(inp.W1), f64(inp.R), f64(inp.gamma), f64(inp.W2), wl.eps, f64(dz),
+                            f64(dho) if dh else None)
+    for name, w in zip(("dX", "dW1", "dR", "dgamma", "dW2"), want):
+        _check(name, got[name], w)

@@ -126,3 +126,36 @@ def test_ce_full_size_sampled_rows():
     Hs, Wd = f64(H[rows]), f64(W)
     oloss, olse = oracle.cross_entropy(Hs, Wd, labels[rows].numpy())
     _check_fused(loss[rows], lse[rows], oloss, olse, Hs, Wd)
+
+
+def _random_shapes(n: int = 8, seed: int = 555):
+    """Seeded shapes within the cross-entropy's rules (D a multiple of 128, V of 256, any M), some with ignored
+    labels."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.choice([1, 2, 255, 257]) if i < 2 else rng.integers(1, 700))
+        D = 128 * int(rng.integers(1, 5))
+        V = 256 * int(rng.integers(1, 13))
+        ign = int(rng.choice([0, 3, 11]))
+        out.append(CeWorkload(f"cerand{i}_M{M}_D{D}_V{V}_ign{ign}", M=M, D=D, V=V, ignore_every=ign, seed=500 + i))
+    return out
+
+
+RANDOM = _random_shapes()
+
+
+@pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_ce_random_shape(wl, unfused):
+    _say(f"[gpu] ce random {'unfused' if unfused else 'fused'} {wl}")
+    H, W, labels = make_ce_inputs(wl)
+    loss, lse = _run(H, W, labels, unfused)
+    oloss, olse = oracle.cross_entropy(f64(H), f64(W), labels.numpy())
+    assert np.all(np.isfinite(loss)) and np.all(np.isfinite(lse))
+    assert np.all(loss[labels.numpy() < 0] == 0.0)
+    if unfused:
+        bound = 2.0 ** -7 * np.max(np.abs(f64(H) @ f64(W)), axis=1) + ATOL
+        assert np.all(np.abs(loss - oloss) <= bound) and np.all(np.abs(lse - olse) <= bound)
+    else:
+        _check_fused(loss, lse, oloss, olse, f64(H), f64(W))

@@ -144,3 +144,40 @@ def test_rope_full_size_all_rows():
         return o
 
     check_all_rows(wl.M, h, y, None, chunk, say=_say)
+
+
+def _random_cases(n: int = 8, seed: int = 313):
+    """Seeded block shapes (identity epilogue) with a random rotated span (a multiple of the 64-column head, up to
+    all of N2), sequence length and base."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.integers(1, 600))
+        K1 = 128 * int(rng.integers(1, 5))
+        D = 256 * int(rng.integers(1, 3))
+        N2 = 256 * int(rng.integers(1, 5))
+        n_rot = 64 * int(rng.integers(0, N2 // 64 + 1))
+        seq = int(rng.choice([1, 7, 128, 333, 8192]))
+        base = float(rng.choice([10000.0, 500000.0]))
+        wl = Workload(f"roperand{i}_M{M}_K{K1}_D{D}_N{N2}_rot{n_rot}_seq{seq}", M=M, K1=K1, D=D, N2=N2,
+                      epi=EPI_IDENTITY, eps=1e-5, w1_std=0.05, w2_std=0.05, seed=330 + i)
+        out.append((wl, seq, n_rot, base))
+    return out
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=[c[0].name for c in RANDOM])
+@pytest.mark.parametrize("path", ["fused", "separate"])
+def test_rope_random_shape(case, path):
+    wl, seq_len, n_rot, base = case
+    _say(f"rope random {path} {wl.name}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    run = _run_rope if path == "fused" else _run_separate
+    h, y = run(d, seq_len, n_rot, base)
+    oh, _, oy = oracle_rows(inp)
+    oy = oracle.rope_rows(oy, HEAD, n_rot, seq_len, base)
+    check_h(f64(h), oh)
+    check_y(f64(y), oy)

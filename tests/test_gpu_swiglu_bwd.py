@@ -108,3 +108,30 @@ def test_swiglu_bwd_full_size_all_rows():
     for g in (gg, gu):
         _say(f"    {g.what}: normwise {g.normwise():.3e}, MAE/max {g.mae_rel():.3e}")
         assert g.normwise() <= Y_NORMWISE and g.mae_rel() <= Y_MAE_REL, g.what
+
+
+def _random_shapes(n: int = 8, seed: int = 616):
+    """Seeded shapes within the SwiGLU backward's rules (D a multiple of 128, F of 256, any M)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        M = int(rng.choice([1, 3, 256, 257]) if i < 2 else rng.integers(1, 600))
+        D = 128 * int(rng.integers(1, 5))
+        F = 256 * int(rng.integers(1, 4))
+        zs = float(rng.choice([1.0, 3.0]))
+        out.append(SwigluBwdWorkload(f"swbrand{i}_M{M}_D{D}_F{F}", M=M, D=D, F=F, z_std=zs, seed=600 + i))
+    return out
+
+
+RANDOM = _random_shapes()
+
+
+@pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_swiglu_bwd_random_shape(wl, unfused):
+    _say(f"[gpu] swiglu bwd random {'unfused' if unfused else 'fused'} {wl}")
+    dout, Wd, z = make_swiglu_bwd_inputs(wl)
+    got = _run(dout, Wd, z, unfused)
+    want = oracle.swiglu_bwd(f64(dout), f64(Wd), f64(z))
+    check_y(got[:, :wl.F], want[:, :wl.F], what="dgate")
+    check_y(got[:, wl.F:], want[:, wl.F:], what="dup")
