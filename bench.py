@@ -75,7 +75,9 @@ def algorithmic_bytes(wl, fused: bool) -> int:
     b += 2 * M * D + 2 * M * ny                          # h, y
     if fused:
         T = D // 256
-        b += 2 * 4 * T * M + 2 * 4 * M                    # part written + read, r written + read
+        b += 2 * 4 * T * M                                # part written + read
+        # r written; read back only where the reduce is a kernel of its own (D / 256 > 16), else GEMM2 forms it
+        b += 4 * M if T <= 16 else 2 * 4 * M
         b += 2 * 2 * M * D                                # h * gamma written, read back by GEMM2
     else:
         b += 2 * 2 * M * D                                # T written + read
@@ -263,10 +265,15 @@ def timed_steps(fn, steps: int, warmup: int, torch, settle_ms: float = 0.0):
 
 
 def per_step_summary(per: list) -> dict:
+    """Per-step times: mean, median, the nearest-rank 10th and 90th percentiles, first, last, max and the means of
+    the first and last thirds (a trend within the window shows as a difference between the two)."""
+    import statistics
+
     t = sorted(per)
     n = len(t)
     q = lambda p: round(t[min(n - 1, int(round(p * (n - 1))))], 4)
-    return {"mean": round(sum(per) / n, 4), "first": round(per[0], 4), "last": round(per[-1], 4), "median": q(0.5),
+    return {"mean": round(sum(per) / n, 4), "first": round(per[0], 4), "last": round(per[-1], 4),
+            "median": round(statistics.median(t), 4),
             "p10": q(0.1), "p90": q(0.9), "max": round(t[-1], 4), "first_third_mean": round(
                 sum(per[: max(1, n // 3)]) / max(1, n // 3), 4), "last_third_mean": round(
                 sum(per[n - max(1, n // 3):]) / max(1, n // 3), 4)}
