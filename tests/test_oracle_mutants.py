@@ -2,8 +2,10 @@
 
 Each case copies the oracle's C source, plants one plausible mistake (eps outside the square root, a
 dropped residual, a transposed operand, gate and up swapped, r applied twice, gamma dropped, a wrong
-mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent in the fp8
-decoder, seven mistakes in the backward, four in the rotary embedding, five in the cross-entropy, three in the block-scaled quantiser and three in the SwiGLU backward), rebuilds it in a temporary directory and runs the pin tests
+mean denominator, a wrong gamma index, a sign flip in silu, a wrong subnormal exponent or exponent bias in the fp8
+decoder, one significant bit too few in the fp8 and bf16 roundings, ties rounded away from zero, a wrong
+scale index in either dequantiser, the partial sums read transposed, either storage rounding of the
+round-points form left out, seven mistakes in the backward, four in the rotary embedding, five in the cross-entropy, three in the block-scaled quantiser and three in the SwiGLU backward), rebuilds it in a temporary directory and runs the pin tests
 against it.  Every mutant must fail at least one pin; the unmodified oracle is never touched.
 """
 import os
@@ -27,6 +29,19 @@ MUTANTS = [
     ("gamma_wrong_index", "W2g[j * N2 + n] = gamma[j] * W2[j * N2 + n];", "W2g[j * N2 + n] = gamma[n % D] * W2[j * N2 + n];"),
     ("silu_sign", "return x / (1.0 + exp(-x));", "return x / (1.0 + exp(x));"),
     ("e4m3_subnormal", "v = ldexp((double)mant, -9);", "v = ldexp((double)mant, -10);"),
+    ("e4m3_exponent_bias", "v = ldexp(1.0 + mant / 8.0, exp_bits - 7);", "v = ldexp(1.0 + mant / 8.0, exp_bits - 8);"),
+    ("e4m3_encode_three_bits", "round_to_grid(a, 4, -6);", "round_to_grid(a, 3, -6);"),
+    ("bf16_seven_bits", "round_to_grid(x, 8, -126);", "round_to_grid(x, 7, -126);"),
+    ("ties_away_from_zero", "return nearbyint(x / ulp) * ulp;", "return round(x / ulp) * ulp;"),
+    ("dequant_rows_scale_index", "oracle_e4m3_decode(q[i * cols + k]) * (double)s[i];",
+     "oracle_e4m3_decode(q[i * cols + k]) * (double)s[0];"),
+    ("dequant_cols_scale_index", "oracle_e4m3_decode(q[k * cols + n]) * (double)s[n];",
+     "oracle_e4m3_decode(q[k * cols + n]) * (double)s[k % cols];"),
+    ("partials_transposed", "ss += part[t * M + i];", "ss += part[i * T + t];"),
+    ("roundpts_operand_unrounded", "arow[j] = oracle_bf16_round(hrow[j] * c->gamma[j]);",
+     "arow[j] = hrow[j] * c->gamma[j];"),
+    ("roundpts_output_unrounded", "c->y[i * half + n] = c->form == FORM_ROUNDPTS ? oracle_bf16_round(v) : v;",
+     "c->y[i * half + n] = v;"),
 ]
 
 
