@@ -25,6 +25,7 @@ STATUS = {0: "CODA_OK", 1: "CODA_ERR_INVALID_ARG", 2: "CODA_ERR_UNSUPPORTED", 3:
 
 # every symbol include/coda.h declares
 EXPORTS = ("coda_abi_version", "coda_status_string", "coda_last_error", "coda_workspace_bytes",
+           "coda_workspace_split_bytes",
            "coda_workspace_r_offset", "coda_block_fwd", "coda_block_unfused", "coda_block_fwd_fp8",
            "coda_block_unfused_fp8", "coda_block_fwd_fp8_mx",
            "coda_gemm1_residual_partial_rms", "coda_partial_rms_reduce", "coda_gemm2_rowscale",
@@ -59,6 +60,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.coda_last_error.argtypes, lib.coda_last_error.restype = [], ctypes.c_char_p
     lib.coda_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32, i32]
     lib.coda_workspace_bytes.restype = sz
+    lib.coda_workspace_split_bytes.argtypes = [i64, i64, i64, i64, i32, i32, i32]
+    lib.coda_workspace_split_bytes.restype = sz
     lib.coda_workspace_r_offset.argtypes, lib.coda_workspace_r_offset.restype = [i64, i64], sz
     block = [vp, vp, vp, vp, vp, f32, i32, vp, vp, i64, i64, i64, i64, vp, sz, vp]
     for name in ("coda_block_fwd", "coda_block_unfused"):
@@ -140,10 +143,20 @@ def coda_workspace_r_offset(M: int, D: int) -> int:
     return load().coda_workspace_r_offset(M, D)
 
 
-def alloc_workspace(M: int, K1: int, D: int, N2: int, epi_kind: int, unfused: int = 0, device="cuda", fp8: int = 0):
+def coda_workspace_split_bytes(M: int, K1: int, D: int, N2: int, epi_kind: int, fp8: int = 0,
+                               unfused: int = 0) -> int:
+    return load().coda_workspace_split_bytes(M, K1, D, N2, epi_kind, fp8, unfused)
+
+
+def alloc_workspace(M: int, K1: int, D: int, N2: int, epi_kind: int, unfused: int = 0, device="cuda", fp8: int = 0,
+                    split: bool = True):
+    """The workspace of a block entry point; split=False leaves out the room for splitting the second product's
+    last wave (the block then runs that wave as whole tiles)."""
     n = coda_workspace_bytes(M, K1, D, N2, epi_kind, fp8, unfused)
     if n == 0:
         raise ValueError("no workspace size for these dimensions")
+    if not split:
+        n -= coda_workspace_split_bytes(M, K1, D, N2, epi_kind, fp8, unfused)
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 

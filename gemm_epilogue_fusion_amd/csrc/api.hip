@@ -2,6 +2,7 @@
 // and the launch sequences of the fused block and of the unfused baseline.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -167,6 +168,62 @@ size_t carve(void* ws, int64_t M, int64_t D, int fp8, int unfused, Workspace* w)
 
 size_t ws_bytes(int64_t M, int64_t D, int fp8, int unfused) { return carve(nullptr, M, D, fp8, unfused, nullptr); }
 
+// After those bytes the bf16 blocks keep the split of the second GEMM's last wave of tiles (coda::KSplit): the
+// tickets (align256(tail * 4) bytes), then two accumulator slots per split tile.  Its size is planned for 256 CUs
+// (MI355X); coda_workspace_bytes includes it, and a block uses the split only where the workspace it is given has
+// that room (with less, from the base size on, its second GEMM runs whole tiles).
+constexpr int kPlanCus = 256;
+
+int64_t gemm2_tiles(int64_t M, int64_t N2) { return (M + 255) / 256 * (N2 / 256); }
+
+size_t ws_split_bytes(int64_t M, int64_t D, int64_t N2, int fp8, int cus) {
+  if (fp8 || M < 1 || N2 < 256) return 0;
+  const int64_t nt = gemm2_tiles(M, N2);
+  const int64_t tail = nt - coda::ksplit_full(nt, D, cus);
+  if (tail <= 0) return 0;
+  return align256((size_t)tail * 4) + (size_t)(2 * tail) * coda::KSPLIT_SLOT_FLOATS * 4;
+}
+
+// The split room a block validated with `workspace_bytes` may use: the planned region when it fits, else none.
+size_t ws_split_room(int64_t M, int64_t D, int64_t N2, int fp8, int unfused, size_t workspace_bytes) {
+  const size_t base = ws_bytes(M, D, fp8, unfused);
+  const size_t b = ws_split_bytes(M, D, N2, fp8, kPlanCus);
+  return (b && workspace_bytes >= base + b) ? b : 0;
+}
+
+// CU count of the current device (cached per device; 0 when it cannot be read).
+int device_cus() {
+  constexpr int kDevs = 64;
+  static std::atomic<int> cache[kDevs];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kDevs) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = -1;
+    cache[dev].store(v, std::memory_order_relaxed);
+    c = v;
+  }
+  return c > 0 ? c : 0;
+}
+
+// The split the block's second GEMM runs with on this device, inside the validated room (none if it does not fit).
+coda::KSplit split_plan(void* ws, int64_t M, int64_t D, int64_t N2, int unfused, size_t room) {
+  coda::KSplit ks;
+  if (!room) return ks;
+  const int cus = device_cus();
+  const size_t need = ws_split_bytes(M, D, N2, 0, cus);
+  if (!need || need > room) return ks;
+  const int64_t nt = gemm2_tiles(M, N2);
+  const int full = coda::ksplit_full(nt, D, cus);
+  char* base = (char*)ws + ws_bytes(M, D, 0, unfused);
+  ks.full = full;
+  ks.ncnt = (int)(nt - full);
+  ks.cnt = (int*)base;
+  ks.part = (float*)(base + align256((size_t)(nt - full) * 4));
+  return ks;
+}
+
 // Validation shared by the block entry points.  fp8: X, W1, W2 are e4m3 bytes and sx, sw1, sw2 their
 // scales (ignored, and may be NULL, for bf16).
 int validate_block(const void* X, const float* sx, const void* W1, const float* sw1, const void* R,
@@ -195,7 +252,7 @@ int validate_block(const void* X, const float* sx, const void* W1, const float* 
                        rng("W2", W2, (size_t)(D * N2) * el), rng("sx", sx, fp8 ? (size_t)M * 4 : 0),
                        rng("sw1", sw1, fp8 ? (size_t)D * 4 : 0), rng("sw2", sw2, fp8 ? (size_t)N2 * 4 : 0)};
   const Range out[3] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("out_y", out_y, (size_t)(M * ny * 2)),
-                        rng("workspace", workspace, need)};
+                        rng("workspace", workspace, need + ws_split_room(M, D, N2, fp8, unfused, workspace_bytes))};
   return check_alias(in, 8, out, 3, out_h, R);
 }
 
@@ -283,24 +340,27 @@ int validate_bwd(const void* X, const void* W1, const void* h, const float* r, c
 // coda_block_fwd_noalloc on the library's scratch.
 int launch_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2, float eps,
                      int epi_kind, void* out_h, void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2,
-                     void* workspace, hipStream_t st) {
+                     void* workspace, size_t workspace_bytes, hipStream_t st, void* out_z = nullptr) {
   int s;
   Workspace w;
   carve(workspace, M, D, 0, 0, &w);
+  const coda::KSplit ks = split_plan(workspace, M, D, N2, 0, ws_split_room(M, D, N2, 0, 0, workspace_bytes));
   if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R, gamma,
-                                                 (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D, st, kPanels),
+                                                 (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D, st, kPanels,
+                                                 ks),
                      "gemm1_res_prms launch")))
     return s;
   if (coda::fold_supported((int)D))  // the reduce runs inside K3's workgroups
     return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
                                                       epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
-                                                      (int)N2, st, nullptr, kPanels),
+                                                      (int)N2, st, (uint16_t*)out_z, kPanels, ks),
                      "gemm2_rowscale_fold launch");
   if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                      "prms_reduce launch")))
     return s;
   return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, epi_kind == CODA_EPI_SWIGLU,
-                                               (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, nullptr, kPanels),
+                                               (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, (uint16_t*)out_z,
+                                               kPanels, ks),
                    "gemm2_rowscale launch");
 }
 
@@ -363,7 +423,15 @@ size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int ep
   (void)N2;
   (void)epi_kind;
   if (M < 1 || D < 256 || M > kMaxDim || D > kMaxDim || fp8 < 0 || fp8 > 2 || (fp8 == 2 && unfused)) return 0;
-  return ws_bytes(M, D, fp8, unfused ? 1 : 0);
+  // the split room of the bf16 blocks (N2 outside the shape rules: none)
+  const size_t split = (N2 >= 256 && N2 <= kMaxDim && N2 % 256 == 0) ? ws_split_bytes(M, D, N2, fp8, kPlanCus) : 0;
+  return ws_bytes(M, D, fp8, unfused ? 1 : 0) + split;
+}
+
+size_t coda_workspace_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused) {
+  if (coda_workspace_bytes(M, K1, D, N2, epi_kind, fp8, unfused) == 0) return 0;
+  if (N2 < 256 || N2 > kMaxDim || N2 % 256) return 0;
+  return ws_split_bytes(M, D, N2, fp8, kPlanCus);
 }
 
 size_t coda_workspace_r_offset(int64_t M, int64_t D) { return ws_part_bytes(M, D); }
@@ -376,7 +444,7 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
                            workspace, workspace_bytes, 0, 0);
     if (s) return s;
     return launch_block_fwd(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, workspace,
-                            (hipStream_t)stream);
+                            workspace_bytes, (hipStream_t)stream);
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }
@@ -398,7 +466,8 @@ int coda_block_fwd_noalloc(const void* X, const void* W1, const void* R, const f
     s = validate_block(X, nullptr, W1, nullptr, R, gamma, W2, nullptr, eps, epi_kind, out_h, out_y, M, K1, D, N2, ws,
                        (size_t)CODA_NOALLOC_SCRATCH_BYTES, 0, 0);
     if (s) return s;
-    return launch_block_fwd(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, ws, (hipStream_t)stream);
+    return launch_block_fwd(X, W1, R, gamma, W2, eps, epi_kind, out_h, out_y, M, K1, D, N2, ws,
+                            (size_t)CODA_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream);
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }
@@ -415,23 +484,24 @@ int coda_block_fwd_rope(const void* X, const void* W1, const void* R, const floa
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 0, 0, &w);
+    const coda::KSplit ks = split_plan(workspace, M, D, N2, 0, ws_split_room(M, D, N2, 0, 0, workspace_bytes));
     if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
                                                    gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
-                                                   st, kPanels),
+                                                   st, kPanels, ks),
                        "gemm1_res_prms launch")))
       return s;
     if (coda::fold_supported((int)D))
       return hip_check(coda::launch_gemm2_rowscale_rope_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
                                                              (int)seq_len, (int)n_rope_cols, rope_base,
                                                              (uint16_t*)out_y, (int)M, (int)D, (int)N2, st,
-                                                             kPanels),
+                                                             kPanels, ks),
                        "gemm2_rowscale_rope_fold launch");
     if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
                        "prms_reduce launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale_rope(w.hg, (const uint16_t*)W2, w.r, (int)seq_len, (int)n_rope_cols,
                                                       rope_base, (uint16_t*)out_y, (int)M, (int)D, (int)N2, st,
-                                                      kPanels),
+                                                      kPanels, ks),
                      "gemm2_rowscale_rope launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -464,8 +534,10 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 0, 1, &w);
+    // the same split of GEMM2's last wave as the fused block (the same kernel family on the same tiles)
+    const coda::KSplit ks = split_plan(workspace, M, D, N2, 1, ws_split_room(M, D, N2, 0, 1, workspace_bytes));
     if ((s = hip_check(coda::launch_gemm_store((const uint16_t*)X, (const uint16_t*)W1, w.t, (int)M, (int)K1,
-                                               (int)D, st),
+                                               (int)D, st, 0, ks),
                        "gemm_store launch")))
       return s;
     if ((s = hip_check(coda::launch_add_rmsnorm(w.t, (const uint16_t*)R, gamma, (uint16_t*)out_h, w.n, w.r,
@@ -473,7 +545,7 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
                        "add_rmsnorm launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale(w.n, (const uint16_t*)W2, nullptr, epi_kind == CODA_EPI_SWIGLU,
-                                                 (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                                                 (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, nullptr, 0, ks),
                      "unfused gemm2 launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -902,28 +974,12 @@ int coda_block_fwd_save_z(const void* X, const void* W1, const void* R, const fl
                              rng("R", R, (size_t)(M * D) * 2),  rng("gamma", gamma, (size_t)D * 4),
                              rng("W2", W2, (size_t)(D * N2) * 2), rng("out_h", out_h, (size_t)(M * D) * 2),
                              rng("out_y", out_y, (size_t)(M * (N2 / 2)) * 2),
-                             rng("workspace", workspace, ws_bytes(M, D, 0, 0))};
+                             rng("workspace", workspace,
+                                 ws_bytes(M, D, 0, 0) + ws_split_room(M, D, N2, 0, 0, workspace_bytes))};
     for (int i = 0; i < 8; ++i)
       if (overlap(zr, others[i])) return fail(CODA_ERR_ALIAS, "out_z overlaps %s", others[i].name);
-    hipStream_t st = (hipStream_t)stream;
-    Workspace w;
-    carve(workspace, M, D, 0, 0, &w);
-    if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
-                                                   gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
-                                                   st, kPanels),
-                       "gemm1_res_prms launch")))
-      return s;
-    if (coda::fold_supported((int)D))
-      return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r, 1,
-                                                        (uint16_t*)out_y, (int)M, (int)D, (int)N2, st,
-                                                        (uint16_t*)out_z, kPanels),
-                       "gemm2_rowscale_fold launch");
-    if ((s = hip_check(coda::launch_prms_reduce(w.part, (int)(D / 256), (int)M, (int)D, eps, w.r, st),
-                       "prms_reduce launch")))
-      return s;
-    return hip_check(coda::launch_gemm2_rowscale(w.hg, (const uint16_t*)W2, w.r, 1, (uint16_t*)out_y, (int)M, (int)D,
-                                                 (int)N2, st, (uint16_t*)out_z, kPanels),
-                     "gemm2_rowscale launch");
+    return launch_block_fwd(X, W1, R, gamma, W2, eps, CODA_EPI_SWIGLU, out_h, out_y, M, K1, D, N2, workspace,
+                            workspace_bytes, (hipStream_t)stream, out_z);
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
   }

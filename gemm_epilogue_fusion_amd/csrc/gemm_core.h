@@ -740,10 +740,7 @@ struct TileRowsDrain {
 // remapped so that XCD x receives a contiguous range of the tile order, then tiles are ordered in groups of
 // `group_m` row tiles (row tile fastest inside a group), so the tiles one XCD runs together share A row
 // tiles and B column tiles in its L2.
-__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
-  int b = blockIdx.x;
-  const int ntiles = tiles_m * tiles_n;
-  if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
+__device__ __forceinline__ void tile_of_order(int b, int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
   const int group_size = group_m * tiles_n;
   const int group = b / group_size;
   const int first_m = group * group_m;
@@ -751,6 +748,36 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_
   const int in_group = b - group * group_size;
   tm = first_m + in_group % gm;
   tn = in_group / gm;
+}
+
+__device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_m, int& tm, int& tn) {
+  int b = blockIdx.x;
+  const int ntiles = tiles_m * tiles_n;
+  if ((ntiles & 7) == 0) b = (b & 7) * (ntiles >> 3) + (b >> 3);
+  tile_of_order(b, tiles_m, tiles_n, group_m, tm, tn);
+}
+
+// The same with the tiles from `full` on (in tile order) split in two pieces along K: workgroups 0 .. full-1 take
+// whole tiles as tile_coords deals them (over `full` tiles), the next 2 (ntiles - full) take pieces, XCD by XCD in
+// contiguous ranges of the piece order with both pieces of a tile on one XCD where the count allows.  Returns the
+// piece (0: the first half of K, 1: the second) or -1 for a whole tile; b_out is the tile's place in the tile order.
+__device__ __forceinline__ int tile_coords_split(int tiles_m, int tiles_n, int group_m, int full, int& tm, int& tn,
+                                                 int& b_out) {
+  const int ntiles = tiles_m * tiles_n;
+  int b = blockIdx.x;
+  int piece = -1;
+  if (b < full) {
+    if ((full & 7) == 0) b = (b & 7) * (full >> 3) + (b >> 3);
+  } else {
+    int p = b - full;
+    const int np = 2 * (ntiles - full);
+    if ((np & 15) == 0) p = (p & 7) * (np >> 3) + (p >> 3);  // np / 8 even: a pair never straddles two XCDs
+    piece = p & 1;
+    b = full + (p >> 1);
+  }
+  b_out = b;
+  tile_of_order(b, tiles_m, tiles_n, group_m, tm, tn);
+  return piece;
 }
 
 }  // namespace coda

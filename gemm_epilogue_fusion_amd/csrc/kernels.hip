@@ -120,7 +120,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
     float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs,
-    int panels) {
+    int panels, KSplit ks) {
   constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
   // MX (e4m3 only): K1 (MODE_RES_PRMS) also quantises h * gamma in blocks of 32 columns with power-of-two
   // scales (codes to out2, scales to mxs); K3 (row-scale modes) reads its A operand's block scales from mxs
@@ -135,9 +135,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
                                                     (MX_A ? NSTAGE * MX_STAGE_BYTES : 0)];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
-  int tm, tn;
-  tile_coords(tiles_m, tiles_n, group_m, tm, tn);
+  // the split of the last wave (KSplit) exists for the bf16 row-scale modes; the first GEMMs clear its counters
+  constexpr bool CAN_SPLIT = ROWSCALE_MODE && !FP8;
+  if ((MODE == MODE_RES_PRMS || MODE == MODE_STORE) && ks.cnt && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < ks.ncnt; i += NTHREADS) ks.cnt[i] = 0;
+  int tm, tn, piece = -1, tile_ord = 0;
+  if (CAN_SPLIT && ks.full >= 0)
+    piece = tile_coords_split(tiles_m, tiles_n, group_m, ks.full, tm, tn, tile_ord);
+  else
+    tile_coords(tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM;
+  // a piece multiplies over its half of K
+  const int kpart = piece >= 0 ? K / 2 : K;
+  const int kbeg = piece > 0 ? kpart : 0;
 
   // folded reduce: before the mainloop the partial sums of the tile's rows go global -> LDS (4 bytes per lane,
   // 64 rows per load, rows past M read row M-1), older than every stage load, so the mainloop's first wait
@@ -182,15 +192,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
                               mxs, mx_smem);
   } else {
-    const uint16_t* A16 = (const uint16_t*)A;
-    const uint16_t* B16 = (const uint16_t*)B;
+    const uint16_t* A16 = (const uint16_t*)A + (int64_t)(kbeg / KS) * al.step;
+    const uint16_t* B16 = (const uint16_t*)B + (int64_t)kbeg * Nb;
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, K, smem, acc, fold_hook);
+      gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, kpart, smem, acc, fold_hook);
     else if (MODE == MODE_RES_PRMS)  // the residual tile's first 192 rows arrive as the ring drains
       gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
                     TileRowsDrain{R, Nb, m0, tn * BN, M, smem});
     else
-      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook);
+      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook);
   }
 
   // Materialise the accumulators here: otherwise the compiler may sink the last MFMAs into the epilogue's
@@ -199,6 +209,55 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(acc[mb][nb]));
+
+  if (CAN_SPLIT && piece >= 0) {
+    // A piece of a split tile (KSplit): its accumulators go to its slot, lane-major (wave w's register group j at
+    // w * 8192 + j * 256 floats, lane l at 4 l: each store instruction writes 1 KiB), then it takes a ticket.  The
+    // workgroup that draws ticket 1 adds the other piece's slot, written in the same layout, to its accumulators.
+    // Ordering: every wave's slot stores have completed before the barrier (it waits for them), after which one wave
+    // makes them visible on every XCD (agent-scope release: the L2 writes its dirty lines back) and takes the ticket;
+    // on the other side one wave discards stale cached lines (agent-scope acquire) before the barrier that precedes
+    // the slot loads.  One wave per side is enough because the release and the acquire act on the whole L2 and on
+    // the CU's L1, which the workgroup's waves share; measured at the 1B MLP-out -> QKV shape, the same fences in
+    // every wave cost more than the split saved.
+    // The ticket is broadcast through the first word of the folded-reduce area (its partial sums were consumed by
+    // the hook long before); a __shared__ variable of its own would make the compiler wait for every in-flight
+    // direct load (vmcnt(0)) before each LDS read of the mainloop, unable to tell that the two objects do not
+    // overlap (measured: 40% on the product's time, whole tiles included).
+    static_assert(!CAN_SPLIT || FOLD_LDS > 0, "the split needs the folded-reduce area");
+    int& ticket = *(int*)(smem + LDS_BYTES + 1024);
+    const int64_t pair = tile_ord - ks.full;
+    const int lane_off = (int)(threadIdx.x >> 6) * 8192 + (int)(threadIdx.x & 63) * 4;
+    float* mine = ks.part + (pair * 2 + piece) * KSPLIT_SLOT_FLOATS + lane_off;
+    const float* other = ks.part + (pair * 2 + (piece ^ 1)) * KSPLIT_SLOT_FLOATS + lane_off;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& a = acc[mb][nb];
+          *(f32x4*)(mine + ((mb * NB + nb) * 4 + q) * 256) =
+              (f32x4){a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        }
+    __syncthreads();
+    if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(ks.cnt + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket == 0) return;  // the other piece finishes the tile
+    if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 o = *(const f32x4*)(other + ((mb * NB + nb) * 4 + q) * 256);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[mb][nb][4 * q + e] += o[e];
+        }
+  }
 
   // ---- epilogue: the accumulator tile is still in registers ----
   // acc[mb][nb][r] is row m0 + 128 wm + 32 mb + lane%32, column 64 wn + 32 nb + 8 (r/4) + 4 (lane/32) + r%4.
@@ -762,20 +821,38 @@ template <int MODE, bool FP8, bool MX = false>
 static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, const uint16_t* R, const float* rowsc,
                               const float* colsc, uint16_t* out, uint16_t* out2, float* part, int M, int K, int Nb,
                               hipStream_t stream, RopeParams rope = RopeParams{}, RowFold fold = RowFold{},
-                              uint8_t* mxs = nullptr, int panels = 0) {
+                              uint8_t* mxs = nullptr, int panels = 0, KSplit ks = KSplit{}) {
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
-  dim3 grid(tiles_m * tiles_n), block(NTHREADS);
+  const int ntiles = tiles_m * tiles_n;
+  constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
+  int nwg = ntiles;
+  if (ROWSCALE_MODE && !FP8 && ks.full >= 0) {
+    if (ks.full >= ntiles || !ks.part || !ks.cnt || K % 256 || K < 1024)
+      ks.full = -1;  // nothing to split, or a split this K cannot take: whole tiles
+    else
+      nwg = ks.full + 2 * (ntiles - ks.full);
+  } else if (ROWSCALE_MODE) {
+    ks.full = -1;
+  }
+  dim3 grid(nwg), block(NTHREADS);
   hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8, MX>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
-                     out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels);
+                     out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels, ks);
   return hipGetLastError();
+}
+
+int ksplit_full(int64_t ntiles, int64_t K, int cus) {
+  if (cus <= 0 || ntiles <= 0 || K < 1024 || K % 256) return (int)ntiles;
+  const int64_t rem = ntiles % cus;
+  if (rem == 0 || 4 * rem > cus) return (int)ntiles;
+  return (int)(ntiles - rem);
 }
 
 hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, const float* gamma,
                                  uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream,
-                                 int panels) {
+                                 int panels, KSplit clear) {
   return launch_gemm<MODE_RES_PRMS, false>(X, W1, gamma, R, nullptr, nullptr, H, HG, part, M, K1, D, stream,
-                                           RopeParams{}, RowFold{}, nullptr, panels);
+                                           RopeParams{}, RowFold{}, nullptr, panels, clear);
 }
 
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
@@ -831,25 +908,26 @@ hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, floa
 }
 
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
-                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z, int panels) {
+                                 int M, int D, int N2, hipStream_t stream, uint16_t* Z, int panels, KSplit ks) {
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, r, nullptr, Y, Z, nullptr, M, D, N2,
-                                                    stream, RopeParams{}, RowFold{}, nullptr, panels);
+                                                    stream, RopeParams{}, RowFold{}, nullptr, panels, ks);
   return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2, stream,
-                                           RopeParams{}, RowFold{}, nullptr, panels);
+                                           RopeParams{}, RowFold{}, nullptr, panels, ks);
 }
 
 int fold_supported(int D) { return D / BN <= FOLD_MAX_T; }
 
 hipError_t launch_gemm2_rowscale_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps, float* r,
                                       int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
-                                      uint16_t* Z, int panels) {
+                                      uint16_t* Z, int panels, KSplit ks) {
   const RowFold f{D / BN, (float)D, eps, r};
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, Z,
-                                                    (float*)part, M, D, N2, stream, RopeParams{}, f, nullptr, panels);
+                                                    (float*)part, M, D, N2, stream, RopeParams{}, f, nullptr, panels,
+                                                    ks);
   return launch_gemm<MODE_ROWSCALE, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr, (float*)part, M, D,
-                                           N2, stream, RopeParams{}, f, nullptr, panels);
+                                           N2, stream, RopeParams{}, f, nullptr, panels, ks);
 }
 
 static RopeParams rope_params(int seq_len, int n_rot, float base) {
@@ -862,18 +940,18 @@ static RopeParams rope_params(int seq_len, int n_rot, float base) {
 
 hipError_t launch_gemm2_rowscale_rope(const uint16_t* A, const uint16_t* W2, const float* r, int seq_len, int n_rot,
                                       float base, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
-                                      int panels) {
+                                      int panels, KSplit ks) {
   return launch_gemm<MODE_ROWSCALE_ROPE, false>(A, W2, nullptr, nullptr, r, nullptr, Y, nullptr, nullptr, M, D, N2,
                                                 stream, rope_params(seq_len, n_rot, base), RowFold{}, nullptr,
-                                                panels);
+                                                panels, ks);
 }
 
 hipError_t launch_gemm2_rowscale_rope_fold(const uint16_t* A, const uint16_t* W2, const float* part, float eps,
                                            float* r, int seq_len, int n_rot, float base, uint16_t* Y, int M, int D,
-                                           int N2, hipStream_t stream, int panels) {
+                                           int N2, hipStream_t stream, int panels, KSplit ks) {
   return launch_gemm<MODE_ROWSCALE_ROPE, false>(A, W2, nullptr, nullptr, nullptr, nullptr, Y, nullptr, (float*)part,
                                                 M, D, N2, stream, rope_params(seq_len, n_rot, base),
-                                                RowFold{D / BN, (float)D, eps, r}, nullptr, panels);
+                                                RowFold{D / BN, (float)D, eps, r}, nullptr, panels, ks);
 }
 
 // Standalone rotary embedding, in place on bf16 Y [M,N] (the unfused counterpart): one thread per pair.
@@ -910,9 +988,9 @@ hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, cons
 }
 
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
-                             hipStream_t stream, int a_panels) {
+                             hipStream_t stream, int a_panels, KSplit clear) {
   return launch_gemm<MODE_STORE, false>(X, W, nullptr, nullptr, nullptr, nullptr, T, nullptr, nullptr, M, K, N, stream,
-                                        RopeParams{}, RowFold{}, nullptr, a_panels);
+                                        RopeParams{}, RowFold{}, nullptr, a_panels, clear);
 }
 
 hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,

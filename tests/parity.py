@@ -82,13 +82,18 @@ class DeviceInputs:
         self.W2 = inp.W2.to(device)
 
 
-def run_block(d: DeviceInputs, unfused: bool = False, poison: bool = True, out_h=None, R=None):
-    """One call of coda_block_fwd (or coda_block_unfused) on fresh, NaN-poisoned outputs and workspace."""
+def run_block(d: DeviceInputs, unfused: bool = False, poison: bool = True, out_h=None, R=None, split: bool = True,
+              ws_out: list = None):
+    """One call of coda_block_fwd (or coda_block_unfused) on fresh, NaN-poisoned outputs and workspace.  split=False
+    gives the call a workspace without the room to split the second product's last wave (whole tiles only);
+    ws_out, if given, receives the workspace."""
     wl = d.wl
     dev = d.X.device
     h = out_h if out_h is not None else torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
     y = torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)
-    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=int(unfused), device=dev)
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=int(unfused), device=dev, split=split)
+    if ws_out is not None:
+        ws_out.append(ws)
     if poison:
         if out_h is None:
             h.fill_(float("nan"))

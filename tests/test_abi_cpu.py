@@ -189,6 +189,33 @@ def test_fp8_validation(lib, fn):
     assert _call8(lib, small, fn) == WORKSPACE
 
 
+def test_workspace_split_bytes(lib):
+    """The room to split the second product's last wave, planned for 256 CUs: none where the tiles fill whole
+    waves, the last wave fills more than a quarter of the CUs or K = D < 1024; else one int32 ticket per tile of the
+    last wave (256-byte aligned) and two 256 KiB fp32 slots per such tile.  coda_workspace_bytes includes it."""
+    al = lambda x: (x + 255) // 256 * 256
+    slot = 512 * 128 * 4
+    base = lambda M, D, unfused=0: al(D // 256 * M * 4) + al(M * 4) + (2 if unfused else 1) * al(M * D * 2)
+    f = lib.coda_workspace_split_bytes
+    assert f(8192, 2048, 2048, 16384, 1, 0, 0) == 0          # 32 x 64 tiles: whole waves
+    assert f(8192, 8192, 2048, 3072, 0, 0, 0) == 0           # 32 x 12 = 384 tiles: a last wave of 128, over a quarter
+    assert lib.coda_workspace_bytes(8192, 8192, 2048, 3072, 0, 0, 0) == base(8192, 2048)
+    tail32 = al(32 * 4) + 64 * slot                           # 32 x 9 = 288 tiles: a last wave of 32
+    assert f(8192, 2048, 2048, 2304, 0, 0, 0) == tail32
+    assert lib.coda_workspace_bytes(8192, 2048, 2048, 2304, 0, 0, 0) == base(8192, 2048) + tail32
+    assert f(8192, 2048, 2048, 2304, 0, 0, 1) == tail32       # the unfused bf16 block: the same room
+    assert lib.coda_workspace_bytes(8192, 2048, 2048, 2304, 0, 0, 1) == base(8192, 2048, 1) + tail32
+    assert f(8192, 2048, 2048, 2304, 0, 1, 0) == 0            # e4m3 blocks: none
+    assert f(8192, 2048, 2048, 2304, 0, 2, 0) == 0
+    assert f(256 * 65, 256, 1024, 256, 0, 0, 0) == 0            # 65 tiles: the last wave is over a quarter
+    assert f(256 * 64, 256, 1024, 256, 0, 0, 0) == al(64 * 4) + 128 * slot  # 64 tiles: exactly a quarter
+    assert f(300, 256, 768, 1024, 1, 0, 0) == 0                 # K = 768
+    assert f(300, 256, 1024, 1024, 1, 0, 0) == al(8 * 4) + 16 * slot
+    assert f(130, 128, 4352, 256, 0, 0, 0) == al(4) + 2 * slot  # one tile, K = 4352 (halves of 2176)
+    assert f(0, 256, 2048, 3072, 0, 0, 0) == 0                  # invalid dimensions
+    assert f(8192, 256, 2048, 3000, 0, 0, 0) == 0
+
+
 def test_fp8_workspace_bytes(lib):
     M, D = 8192, 2048
     a = lambda x: (x + 255) // 256 * 256

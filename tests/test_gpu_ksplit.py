@@ -1,0 +1,227 @@
+"""GPU tests of the split of the second product's last wave of tiles, through the C ABI.
+
+Where the second product's 256 x 256 output tiles leave a last wave that fills at most a quarter of the CUs, each tile
+of that wave is computed as two halves of K whose fp32 sums are added before the epilogue (coda_workspace_bytes
+in include/coda.h describes the room this takes in the workspace).  Checked here:
+- the split is taken where it is planned: after a call every tile of the last wave holds ticket 2 (both halves
+  ran and each took its ticket);
+- small shapes whose every tile is split (a ragged row tile, SwiGLU and identity epilogues, the path with the
+  reduce as a kernel of its own) and a shape with a whole wave plus a split tail, fused and unfused, against the
+  oracle (every element on the small shapes; rows covering every row tile on the tail shape), and against the
+  same block run on whole tiles (a workspace without the split room): h and r equal bit for bit, y within the
+  fp32 summation-order difference;
+- outputs bit-identical run to run, whichever half finishes second;
+- a full-size shape with a last wave of 32 tiles (a QKV projection with 2 key-value heads of 64 after the 1B
+  hidden size: 8192 rows, D = 2048, 2048 + 2 x 128 output columns, 288 tiles): tickets, run-to-run identity, a row
+  in every row tile against the oracle and every row against the whole-tile run; the 1B MLP-out -> QKV shape itself
+  (384 tiles, a last wave of 128) is not split, the rule written out here and in the CPU tests;
+- the block with the rotary embedding and the forward that keeps z take the same split.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from gemm_epilogue_fusion_amd import binding as cb
+from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, EPI_SWIGLU, WORKLOADS, Workload, make_inputs
+
+from parity import (DeviceInputs, check_h, check_roundpts, check_y, f64, mae_rel, normwise, oracle_rows, run_block,
+                    sample_rows_covering)
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+SLOT_BYTES = 512 * 128 * 4  # one workgroup's fp32 accumulators
+PLAN_CUS = 256              # the split room is planned for MI355X's CU count
+# y of the split and whole-tile runs: the same products summed in another fp32 order, then rounded to bf16
+CLOSE_NORMWISE = 1e-2
+CLOSE_MAE_REL = 1e-4
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cb.load()
+    if torch.cuda.get_device_properties(0).multi_processor_count != PLAN_CUS:
+        pytest.skip("the split room is planned for 256 CUs")
+
+
+def _tail(wl: Workload, unfused: bool = False) -> int:
+    """Tiles of the last wave the workspace has room to split (from the library's own size query)."""
+    split = cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
+    return split // (2 * SLOT_BYTES)
+
+
+def _expected_tail(wl: Workload) -> int:
+    """The plan written out: the tiles of a last wave that fills at most a quarter of the CUs, for K = D >= 1024."""
+    tiles = (wl.M + 255) // 256 * (wl.N2 // 256)
+    rem = tiles % PLAN_CUS
+    return rem if (wl.D >= 1024 and wl.D % 256 == 0 and 0 < rem and 4 * rem <= PLAN_CUS) else 0
+
+
+def _tickets(ws: torch.Tensor, wl: Workload, unfused: bool = False) -> torch.Tensor:
+    total = cb.coda_workspace_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
+    base = total - cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
+    n = _tail(wl, unfused)
+    return ws[base: base + 4 * n].view(torch.int32).cpu()
+
+
+def _run(d: DeviceInputs, unfused=False, split=True):
+    box = []
+    h, y, r = run_block(d, unfused=unfused, split=split, ws_out=box)
+    return h, y, r, box[0]
+
+
+# a QKV projection with 2 key-value heads of 64 at the 1B hidden size: 32 x 9 = 288 tiles, a last wave of 32
+QKV_2KV = Workload("1b_qkv_2kv", M=8192, K1=2048, D=2048, N2=2304, epi=EPI_IDENTITY, eps=1e-5, seed=65)
+
+SMALL = [
+    Workload("split_swiglu_ragged", M=300, K1=256, D=1024, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=61),
+    Workload("split_identity_one_row_tile", M=64, K1=128, D=2048, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=62),
+    # D / 256 = 17: the reduce is a kernel of its own, the second product reads r; halves of K = 2176
+    Workload("split_no_fold", M=130, K1=128, D=4352, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=63),
+]
+
+
+def test_plan_matches_the_written_rule():
+    for wl in SMALL + [WORKLOADS["1b_mlp_out_qkv"], WORKLOADS["1b_attn_out_mlp_in"], WORKLOADS["tiny"]]:
+        for unfused in (False, True):
+            assert _tail(wl, unfused) == _expected_tail(wl), (wl.name, unfused)
+    assert _expected_tail(WORKLOADS["1b_mlp_out_qkv"]) == 0   # a last wave of 128 tiles: over a quarter
+    assert _expected_tail(WORKLOADS["1b_attn_out_mlp_in"]) == 0
+    assert _expected_tail(QKV_2KV) == 32
+
+
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_split_small_against_oracle(wl, unfused):
+    _say(f"[gpu] split {'unfused' if unfused else 'fused'} {wl}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    n = _tail(wl, unfused)
+    assert n == (wl.M + 255) // 256 * (wl.N2 // 256) > 0  # every tile split
+    h, y, r, ws = _run(d, unfused)
+    assert bool((_tickets(ws, wl, unfused) == 2).all()), "a split tile did not take both tickets"
+    form = "unfused" if unfused else "fused"
+    oh, orr, oy = oracle_rows(inp, form=form)
+    check_h(f64(h), oh)
+    check_y(f64(y), oy)
+    if unfused:
+        np.testing.assert_allclose(f64(r), orr, rtol=2e-3)
+    else:
+        np.testing.assert_allclose(f64(r), orr, rtol=2e-5)
+        check_roundpts(f64(y), oracle_rows(inp, form="roundpts")[2])
+    # the same block on whole tiles: the first product and r are untouched by the split, y differs only by the
+    # order of the fp32 sums
+    h0, y0, r0, _ = _run(d, unfused, split=False)
+    assert torch.equal(h.view(torch.int16), h0.view(torch.int16))
+    assert torch.equal(r.view(torch.int32), r0.view(torch.int32))
+    g, w = f64(y), f64(y0)
+    assert normwise(g, w) <= CLOSE_NORMWISE and mae_rel(g, w) <= CLOSE_MAE_REL
+
+
+def test_split_is_deterministic():
+    """The half that finishes second adds the other's fp32 slot to its own accumulators; fp32 addition is
+    commutative, so the result does not depend on the order in which the halves finish."""
+    wl = SMALL[0]
+    _say(f"[gpu] split determinism {wl.name}")
+    d = DeviceInputs(make_inputs(wl))
+    ys = [_run(d)[1] for _ in range(4)]
+    for y in ys[1:]:
+        assert torch.equal(y.view(torch.int16), ys[0].view(torch.int16))
+
+
+def test_split_tail_after_a_whole_wave():
+    """264 tiles: 256 whole tiles, then the last 8 (in the tile order) split; rows covering every row tile
+    against the oracle, every row against the whole-tile run."""
+    wl = Workload("split_tail", M=2048, K1=256, D=1024, N2=8448, epi=EPI_IDENTITY, eps=1e-5, seed=64)
+    _say(f"[gpu] split tail {wl}")
+    assert _tail(wl) == 8
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h, y, r, ws = _run(d)
+    assert bool((_tickets(ws, wl) == 2).all())
+    rows = sample_rows_covering(wl.M, n=64, seed=5)
+    oh, orr, oy = oracle_rows(inp, rows)
+    hg, yg = f64(h), f64(y)
+    check_h(hg[rows], oh)
+    check_y(yg[rows], oy)
+    np.testing.assert_allclose(f64(r)[rows], orr, rtol=2e-5)
+    _, y0, _, _ = _run(d, split=False)
+    w = f64(y0)
+    assert normwise(yg, w) <= CLOSE_NORMWISE and mae_rel(yg, w) <= CLOSE_MAE_REL
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
+def test_split_full_size_tail(unfused):
+    wl = QKV_2KV
+    _say(f"[gpu] split full size {'unfused' if unfused else 'fused'} {wl}")
+    assert _tail(wl, unfused) == 32
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h1, y1, r1, ws = _run(d, unfused)
+    assert bool((_tickets(ws, wl, unfused) == 2).all())
+    del ws
+    _, y2, _, _ = _run(d, unfused)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    # a row in every row tile (the split tiles are the last in the tile order, in the last row tiles), the ends
+    rows = np.array(sorted({0, 1, 2, 3, wl.M - 2, wl.M - 1} | {256 * t + (37 * t) % 256 for t in range(wl.M // 256)}))
+    oh, orr, oy = oracle_rows(inp, rows, form="unfused" if unfused else "fused")
+    check_h(f64(h1)[rows], oh)
+    check_y(f64(y1)[rows], oy)
+    np.testing.assert_allclose(f64(r1)[rows], orr, rtol=2e-3 if unfused else 2e-5)
+    _, y0, _, _ = _run(d, unfused, split=False)
+    g, w = f64(y1), f64(y0)
+    assert normwise(g, w) <= CLOSE_NORMWISE and mae_rel(g, w) <= CLOSE_MAE_REL
+
+
+def test_split_rope_block():
+    """coda_block_fwd_rope on a split shape: ticket 2 on every tile, the rotation against the oracle's, the
+    columns past the rotated span equal to the plain (also split) block's bit for bit."""
+    wl = SMALL[1]
+    seq_len, n_rot, base = 48, 256, 10000.0
+    _say(f"[gpu] split rope {wl.name}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    h = torch.full((wl.M, wl.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = torch.full((wl.M, wl.N2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, EPI_IDENTITY, device="cuda")
+    ws.fill_(0xFF)
+    cb.coda_block_fwd_rope(d.X, d.W1, d.R, d.gamma, d.W2, wl.eps, seq_len, n_rot, base, h, y, ws)
+    torch.cuda.synchronize()
+    assert bool((_tickets(ws, wl) == 2).all())
+    oh, _, oy = oracle_rows(inp)
+    check_h(f64(h), oh)
+    check_y(f64(y), oracle.rope_rows(oy, 64, n_rot, seq_len, base))
+    _, y_plain, _ = run_block(d)
+    assert torch.equal(y[:, n_rot:].view(torch.int16), y_plain[:, n_rot:].view(torch.int16))
+
+
+def test_split_save_z():
+    """The forward that keeps z on a split shape: y equal to coda_block_fwd's, z equal to the identity-epilogue
+    block's y (the same tiles, split the same way), bit for bit."""
+    wl = SMALL[0]
+    _say(f"[gpu] split save z {wl.name}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    _, y_plain, _ = run_block(d)
+    _, z_plain, _ = run_block(DeviceInputs(make_inputs(wl.with_(epi=EPI_IDENTITY))))
+    h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((wl.M, wl.N2 // 2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    z = torch.full((wl.M, wl.N2), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, EPI_SWIGLU, device="cuda")
+    cb.coda_block_fwd_save_z(d.X, d.W1, d.R, d.gamma, d.W2, wl.eps, h, y, z, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y_plain.view(torch.int16))
+    # SwiGLU tiles hold 128 gate and the matching 128 up columns, identity tiles 256 contiguous columns: the tile
+    # grid is the same, the accumulation per column too, so z is the identity block's y bit for bit
+    assert torch.equal(z.view(torch.int16), z_plain.view(torch.int16))

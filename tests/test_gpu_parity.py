@@ -136,10 +136,11 @@ FOLD = [SMALL[1], SMALL[3], SMALL[4],
 def test_block_equals_its_three_steps(wl):
     """coda_block_fwd (the partial-RMS reduce folded into the second GEMM where D / 256 <= 16, the separate
     reduce kernel otherwise) gives the same h, r and y, bit for bit, as the three step entry points run one
-    after another: the fold forms r with the reduce kernel's own expression and summation order."""
+    after another: the fold forms r with the reduce kernel's own expression and summation order.  The block runs
+    whole tiles here (a workspace without the split room), as the step entry points do."""
     _say(f"[gpu] block vs its steps {wl.name}")
     d = DeviceInputs(make_inputs(wl))
-    h, y, r = run_block(d)
+    h, y, r = run_block(d, split=False)
     T = wl.D // 256
     h2 = torch.empty_like(h)
     hg = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device="cuda")

@@ -46,6 +46,10 @@ def _stub_source(fatbin_symbol: str) -> str:
         params = re.sub(r"\s*=\s*[^,]+", "", params)  # default arguments belong to the declaration only
         if name == "fold_supported":
             body = "return D / 256 <= 16;"
+        elif name == "ksplit_full":  # the split rule of the second product's last wave
+            body = ("if (cus <= 0 || ntiles <= 0 || K < 1024 || K % 256) return (int)ntiles; "
+                    "const int64_t rem = ntiles % cus; "
+                    "return (rem == 0 || 4 * rem > cus) ? (int)ntiles : (int)(ntiles - rem);")
         elif name == "gemm_ksplit":  # the split rule of the weight-gradient products
             body = ("const int tiles = ((M + 255) / 256) * (N / 256); int s = 1; "
                     "while (s < 8 && tiles * s < 256 && K % (128 * s * 2) == 0) s *= 2; return s;")
@@ -55,6 +59,7 @@ def _stub_source(fatbin_symbol: str) -> str:
     out.append("}  // namespace coda")
     out.append('extern "C" {')
     out.append("hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }")
+    out.append("hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = 256; return hipSuccess; }")
     out.append("hipError_t hipDeviceSynchronize() { return hipSuccess; }")
     out.append("hipError_t hipGetLastError() { return hipSuccess; }")
     out.append('const char* hipGetErrorString(hipError_t) { return "stub"; }')
