@@ -123,6 +123,8 @@ __device__ __forceinline__ void lane_offsets(int wm, int wn, int lane, LaneOffs&
   for (int s = 0; s < 2; ++s) o.a[s] = a_off(m, 2 * s + (lane >> 5));
 }
 
+// RB: the wave's 32-row blocks that are computed (4; 2 in the small-row form, see wave_pos)
+template <int RB = 4>
 __device__ __forceinline__ void read_frags(const char* st, const LaneOffs& o, int s, Frags& f) {
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -132,17 +134,29 @@ __device__ __forceinline__ void read_frags(const char* st, const LaneOffs& o, in
     f.b[nb] = (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) f.a[mb] = *(const s16x8*)(st + o.a[s] + mb * 32 * 64);
+  for (int mb = 0; mb < RB; ++mb) f.a[mb] = *(const s16x8*)(st + o.a[s] + mb * 32 * 64);
 }
 
+template <int RB = 4>
 __device__ __forceinline__ void mma(const Frags& f, f32x16 (&acc)[4][NB]) {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+  for (int mb = 0; mb < RB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.b[nb]),
                                                            __builtin_bit_cast(bf16x8, f.a[mb]), acc[mb][nb], 0, 0, 0);
 }
+
+// The wave's place in the tile: rows 128 wm .. +128, columns 64 wn .. +64.  The 2 x 4 layout puts the two waves of a
+// SIMD (waves w and w + 4) on the same rows.  The small-row form (tiles of at most 64 rows, SMALL) puts them on the
+// same columns instead, so that each SIMD holds one wave of rows 0 .. 127: those waves compute the tile's first two
+// 32-row blocks, the waves of rows 128 .. 255 no product at all, and each SIMD runs a quarter of the MFMAs.
+template <bool SMALL = false>
+__device__ __forceinline__ void wave_pos(int wave, int& wm, int& wn) {
+  wm = SMALL ? wave >> 2 : wave & 1;
+  wn = SMALL ? wave & 3 : wave >> 1;
+}
+constexpr int SMALL_MAX_ROWS = 64;
 
 // Interleave the 8 MFMAs of a sub-step one-to-one with the 8 LDS reads of the next fragments.
 __device__ __forceinline__ void interleave_mma_reads() {
@@ -185,17 +199,23 @@ struct NoDrain {
   static constexpr int LOADS = 0;
   __device__ void operator()(int) const {}
 };
-template <class BCol, class Hook = NoHook, class Drain = NoDrain>
+// SMALL: the small-row form (at most SMALL_MAX_ROWS rows; wave_pos): every wave fetches and waits as usual, the
+// waves of rows 128 .. 255 skip the fragment reads and MFMAs, the others compute their first two row blocks only
+// (the other accumulators stay zero).
+template <class BCol, class Hook = NoHook, class Drain = NoDrain, bool SMALL = false>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, ALayout al, int M, int m0,
                                               const uint16_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
                                               char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{},
-                                              Drain drain = Drain{}) {
+                                              Drain drain = Drain{}, std::integral_constant<bool, SMALL> = {}) {
   constexpr int LPW = 16 / NWAVES;              // 1 KiB direct loads per wave per operand per stage
   constexpr int PER = 2 * LPW;  // VMEM instructions per wave per stage
+  constexpr int RB = SMALL ? 2 : 4;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  int wm, wn;
+  wave_pos<SMALL>(wave, wm, wn);
+  const bool computes = !SMALL || wm == 0;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -243,16 +263,20 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
     constexpr int DRAIN = decltype(drain_c)::value;
     const char* cur = smem + U * STAGE_BYTES;
     if (ISSUE) issue(kt + NSTAGE - 1, (U + NSTAGE - 1) % NSTAGE);
-    read_frags(cur, lo, 1, f1);
-    mma(f0, acc);
-    interleave_mma_reads();
+    if (computes) {
+      read_frags<RB>(cur, lo, 1, f1);
+      mma<RB>(f0, acc);
+      if (!SMALL) interleave_mma_reads();
+    }
     if (WAIT >= 0) {
       wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
       if (DRAIN >= 0 && Drain::LOADS > 0) drain(DRAIN);
-      read_frags(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, lo, 0, f0);
+      if (computes) read_frags<RB>(smem + ((U + 1) % NSTAGE) * STAGE_BYTES, lo, 0, f0);
     }
-    mma(f1, acc);
-    interleave_mma_reads();
+    if (computes) {
+      mma<RB>(f1, acc);
+      if (!SMALL) interleave_mma_reads();
+    }
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
@@ -268,7 +292,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
   for (int p = 0; p < NSTAGE - 1; ++p) issue(p, p);
   wait_barrier<2 * PER>();
   hook();
-  read_frags(smem, lo, 0, f0);
+  if (computes) read_frags<RB>(smem, lo, 0, f0);
 
   using NoD = std::integral_constant<int, -1>;
   constexpr int DL = Drain::LOADS;

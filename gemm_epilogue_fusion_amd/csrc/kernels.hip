@@ -115,13 +115,15 @@ struct GateUpCols {
 // panels != 0: MODE_RES_PRMS writes out2 (h * gamma, or the MX codes) in K panels of the second GEMM's stage
 // width ([Nb / 32][M][32] bf16, [Nb / 64][M][64] bytes), and the row-scale modes and MODE_STORE read A from such
 // panels (ALayout in gemm_core.h); A of MODE_RES_PRMS is always row-major.
-template <int MODE, bool FP8, bool MX = false>
+// SMALL (bf16, M <= SMALL_MAX_ROWS): the mainloop's small-row form (wave_pos in gemm_core.h).
+template <int MODE, bool FP8, bool MX = false, bool SMALL = false>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
     float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs,
     int panels, KSplit ks) {
   constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
+  static_assert(!SMALL || !FP8, "the small-row form is bf16 only");
   // MX (e4m3 only): K1 (MODE_RES_PRMS) also quantises h * gamma in blocks of 32 columns with power-of-two
   // scales (codes to out2, scales to mxs); K3 (row-scale modes) reads its A operand's block scales from mxs
   constexpr bool MX_A = FP8 && MX && ROWSCALE_MODE;
@@ -194,13 +196,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   } else {
     const uint16_t* A16 = (const uint16_t*)A + (int64_t)(kbeg / KS) * al.step;
     const uint16_t* B16 = (const uint16_t*)B + (int64_t)kbeg * Nb;
+    constexpr std::integral_constant<bool, SMALL> small{};
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, kpart, smem, acc, fold_hook);
+      gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, kpart, smem, acc, fold_hook,
+                    NoDrain{}, small);
     else if (MODE == MODE_RES_PRMS)  // the residual tile's first 192 rows arrive as the ring drains
       gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
-                    TileRowsDrain{R, Nb, m0, tn * BN, M, smem});
+                    TileRowsDrain{R, Nb, m0, tn * BN, M, smem}, small);
     else
-      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook);
+      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook,
+                    NoDrain{}, small);
   }
 
   // Materialise the accumulators here: otherwise the compiler may sink the last MFMAs into the epilogue's
@@ -267,7 +272,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = t >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  int wm, wn;
+  wave_pos<SMALL>(wave, wm, wn);
   const int half = lane >> 5;
 
   // per-row scales of this lane's four rows (rows past M read row M-1; they are never stored)
@@ -836,6 +842,13 @@ static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, 
     ks.full = -1;
   }
   dim3 grid(nwg), block(NTHREADS);
+  if constexpr (!FP8) {
+    if (M <= SMALL_MAX_ROWS) {  // the small-row form: a quarter of the MFMAs per SIMD
+      hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8, MX, true>), grid, block, 0, stream, A, B, gamma, R, rowsc,
+                         colsc, out, out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels, ks);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8, MX>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
                      out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels, ks);
   return hipGetLastError();
