@@ -124,6 +124,13 @@ def hbm_bytes_record(wl, fused_alg: int, unfused_alg: int, src_hash: str) -> dic
     return rec
 
 
+def _bf16_gemm_kernel(name: str, mode: int) -> bool:
+    """Whether a kernel name is the general bf16 instantiation of gemm_epilogue_kernel for `mode` (the template's
+    FP8 and MX arguments false, and its small-row argument false where the name carries it)."""
+    head = f"gemm_epilogue_kernel<{mode}, false, false"
+    return head + ">" in name or head + ", false>" in name
+
+
 def summarize_hbm_counters(dirs: list, out: str, wl) -> dict:
     """Writes the measured-bytes summary from rocprofv3 --pmc runs of
     `bench.py --only-fused --profile-unfused --copy-calibration-mib 1024` (one counter set per run).  Dispatches
@@ -146,11 +153,11 @@ def summarize_hbm_counters(dirs: list, out: str, wl) -> dict:
             if "gemm_epilogue_kernel<1," in k:
                 seen_store = True
             role = None
-            if "gemm_epilogue_kernel<0, false, false>" in k:
+            if _bf16_gemm_kernel(k, 0):
                 role = "K1"
-            elif "gemm_epilogue_kernel<3, false, false>" in k:
+            elif _bf16_gemm_kernel(k, 3):
                 role = "U3" if seen_store else "K3"
-            elif "gemm_epilogue_kernel<1, false, false>" in k:
+            elif _bf16_gemm_kernel(k, 1):
                 role = "U1"
             elif "add_rmsnorm_kernel<false>" in k:
                 role = "U2"

@@ -59,11 +59,23 @@ def test_measured_bytes_gating(tmp_path, monkeypatch):
     assert bench.hbm_bytes_record(WORKLOADS["8b_attn_out_mlp_in"], 10, 20, "abc")["measured"] is None
 
 
+def test_kernel_name_matching():
+    """The general bf16 GEMM kernels by mode, with or without the small-row template argument; not the small-row,
+    e4m3 or block-scaled instantiations."""
+    f = bench._bf16_gemm_kernel
+    assert f("void coda::gemm_epilogue_kernel<3, false, false, false>(void const*)", 3)
+    assert f("void coda::gemm_epilogue_kernel<3, false, false>(void const*)", 3)
+    assert not f("void coda::gemm_epilogue_kernel<3, false, false, true>(void const*)", 3)
+    assert not f("void coda::gemm_epilogue_kernel<3, true, false, false>(void const*)", 3)
+    assert not f("void coda::gemm_epilogue_kernel<3, true, true, false>(void const*)", 3)
+    assert not f("void coda::gemm_epilogue_kernel<0, false, false, false>(void const*)", 3)
+
+
 def _counter_dir(base, counter, value_of):
     """A counter_collection.csv as rocprofv3 writes it for one pass: two fused blocks, two unfused blocks, a copy."""
-    seq = ["gemm_epilogue_kernel<0, false, false>", "gemm_epilogue_kernel<3, false, false>"] * 2 + \
-          ["gemm_epilogue_kernel<1, false, false>", "add_rmsnorm_kernel<false>",
-           "gemm_epilogue_kernel<3, false, false>"] * 2 + ["__amd_rocclr_copyBuffer"]
+    seq = ["gemm_epilogue_kernel<0, false, false, false>", "gemm_epilogue_kernel<3, false, false, false>"] * 2 + \
+          ["gemm_epilogue_kernel<1, false, false, false>", "add_rmsnorm_kernel<false>",
+           "gemm_epilogue_kernel<3, false, false, false>"] * 2 + ["__amd_rocclr_copyBuffer"]
     d = base / counter
     d.mkdir()
     with open(d / "run_counter_collection.csv", "w", newline="") as fh:
