@@ -49,7 +49,9 @@ def _capture(fn):
 
 
 CASES = [WORKLOADS["tiny"],
-         Workload("graph_ragged_swiglu", M=300, K1=512, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=21)]
+         Workload("graph_ragged_swiglu", M=300, K1=512, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=21),
+         # every tile of the second product split along K: the tickets are cleared by the first kernel of each replay
+         Workload("graph_split_swiglu", M=300, K1=256, D=1024, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=23)]
 
 
 @pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
@@ -128,7 +130,9 @@ def test_concurrent_streams_distinct_workspaces():
     """Two blocks in flight at once on two streams, each with its own workspace (the documented condition for
     concurrent calls), give the results each gives alone, bit for bit."""
     wls = [Workload("stream_a", M=513, K1=256, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=31),
-           Workload("stream_b", M=300, K1=384, D=768, N2=512, epi=0, eps=1e-5, seed=32)]
+           Workload("stream_b", M=300, K1=384, D=768, N2=512, epi=0, eps=1e-5, seed=32),
+           # the second product split along K: each call's tickets and slots live in its own workspace
+           Workload("stream_c_split", M=200, K1=256, D=2048, N2=512, epi=0, eps=1e-5, seed=33)]
     _say("[gpu] two streams " + ", ".join(w.name for w in wls))
     runs = []
     for wl in wls:
