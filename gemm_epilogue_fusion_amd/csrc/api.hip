@@ -168,26 +168,30 @@ size_t carve(void* ws, int64_t M, int64_t D, int fp8, int unfused, Workspace* w)
 
 size_t ws_bytes(int64_t M, int64_t D, int fp8, int unfused) { return carve(nullptr, M, D, fp8, unfused, nullptr); }
 
-// After those bytes the bf16 blocks keep the split of the second GEMM's last wave of tiles (coda::KSplit): the
-// tickets (align256(tail * 4) bytes), then two accumulator slots per split tile.  Its size is planned for 256 CUs
-// (MI355X); coda_workspace_bytes includes it, and a block uses the split only where the workspace it is given has
-// that room (with less, from the base size on, its second GEMM runs whole tiles).
+// After those bytes the bf16 blocks keep the splits of their GEMMs' last waves of tiles (coda::KSplit): for the
+// second GEMM, then for the first, the tickets (align256(tail * 4) bytes) and two accumulator slots per split tile.
+// The size is planned for 256 CUs (MI355X); coda_workspace_bytes includes it, and a block splits only where the
+// workspace it is given has that room (with less, from the base size on, its GEMMs run whole tiles).
 constexpr int kPlanCus = 256;
 
-int64_t gemm2_tiles(int64_t M, int64_t N2) { return (M + 255) / 256 * (N2 / 256); }
+int64_t gemm_tiles(int64_t M, int64_t N) { return (M + 255) / 256 * (N / 256); }
 
-size_t ws_split_bytes(int64_t M, int64_t D, int64_t N2, int fp8, int cus) {
-  if (fp8 || M < 1 || N2 < 256) return 0;
-  const int64_t nt = gemm2_tiles(M, N2);
-  const int64_t tail = nt - coda::ksplit_full(nt, D, cus);
+// One GEMM's split room for `ntiles` tiles over K on `cus` CUs (0: no split).
+size_t split_bytes_one(int64_t ntiles, int64_t K, int cus) {
+  const int64_t tail = ntiles - coda::ksplit_full(ntiles, K, cus);
   if (tail <= 0) return 0;
   return align256((size_t)tail * 4) + (size_t)(2 * tail) * coda::KSPLIT_SLOT_FLOATS * 4;
 }
 
+size_t ws_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int fp8, int cus) {
+  if (fp8 || M < 1 || D < 256 || N2 < 256) return 0;
+  return split_bytes_one(gemm_tiles(M, N2), D, cus) + split_bytes_one(gemm_tiles(M, D), K1, cus);
+}
+
 // The split room a block validated with `workspace_bytes` may use: the planned region when it fits, else none.
-size_t ws_split_room(int64_t M, int64_t D, int64_t N2, int fp8, int unfused, size_t workspace_bytes) {
+size_t ws_split_room(int64_t M, int64_t K1, int64_t D, int64_t N2, int fp8, int unfused, size_t workspace_bytes) {
   const size_t base = ws_bytes(M, D, fp8, unfused);
-  const size_t b = ws_split_bytes(M, D, N2, fp8, kPlanCus);
+  const size_t b = ws_split_bytes(M, K1, D, N2, fp8, kPlanCus);
   return (b && workspace_bytes >= base + b) ? b : 0;
 }
 
@@ -207,21 +211,41 @@ int device_cus() {
   return c > 0 ? c : 0;
 }
 
-// The split the block's second GEMM runs with on this device, inside the validated room (none if it does not fit).
-coda::KSplit split_plan(void* ws, int64_t M, int64_t D, int64_t N2, int unfused, size_t room) {
+// One GEMM's split laid out from `at` (which then moves past it); no split where the plan has none.
+coda::KSplit split_one(char*& at, int64_t ntiles, int64_t K, int cus) {
   coda::KSplit ks;
-  if (!room) return ks;
-  const int cus = device_cus();
-  const size_t need = ws_split_bytes(M, D, N2, 0, cus);
-  if (!need || need > room) return ks;
-  const int64_t nt = gemm2_tiles(M, N2);
-  const int full = coda::ksplit_full(nt, D, cus);
-  char* base = (char*)ws + ws_bytes(M, D, 0, unfused);
-  ks.full = full;
-  ks.ncnt = (int)(nt - full);
-  ks.cnt = (int*)base;
-  ks.part = (float*)(base + align256((size_t)(nt - full) * 4));
+  const int64_t full = coda::ksplit_full(ntiles, K, cus);
+  if (full >= ntiles) return ks;
+  const int64_t tail = ntiles - full;
+  ks.full = (int)full;
+  ks.cnt = (int*)at;
+  ks.part = (float*)(at + align256((size_t)tail * 4));
+  at += align256((size_t)tail * 4) + (size_t)(2 * tail) * coda::KSPLIT_SLOT_FLOATS * 4;
   return ks;
+}
+
+// The splits a block's GEMMs run with on this device, inside the validated room (none if they do not fit): g1 for
+// the first GEMM (K1 or U1, over K1), g2 for the second (K3 or U3, over D).  g1 carries g2's tickets to clear.
+struct SplitPlan {
+  coda::KSplit g1, g2;
+  int tickets1 = 0;  // the first GEMM's tickets, cleared before it runs
+};
+
+SplitPlan split_plan(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused, size_t room) {
+  SplitPlan p;
+  if (!room) return p;
+  const int cus = device_cus();
+  const size_t need = ws_split_bytes(M, K1, D, N2, 0, cus);
+  if (!need || need > room) return p;
+  char* at = (char*)ws + ws_bytes(M, D, 0, unfused);
+  p.g2 = split_one(at, gemm_tiles(M, N2), D, cus);
+  p.g1 = split_one(at, gemm_tiles(M, D), K1, cus);
+  if (p.g2.full >= 0) {
+    p.g1.clear = p.g2.cnt;
+    p.g1.nclear = (int)(gemm_tiles(M, N2) - p.g2.full);
+  }
+  if (p.g1.full >= 0) p.tickets1 = (int)(gemm_tiles(M, D) - p.g1.full);
+  return p;
 }
 
 // Validation shared by the block entry points.  fp8: X, W1, W2 are e4m3 bytes and sx, sw1, sw2 their
@@ -252,7 +276,7 @@ int validate_block(const void* X, const float* sx, const void* W1, const float* 
                        rng("W2", W2, (size_t)(D * N2) * el), rng("sx", sx, fp8 ? (size_t)M * 4 : 0),
                        rng("sw1", sw1, fp8 ? (size_t)D * 4 : 0), rng("sw2", sw2, fp8 ? (size_t)N2 * 4 : 0)};
   const Range out[3] = {rng("out_h", out_h, (size_t)(M * D * 2)), rng("out_y", out_y, (size_t)(M * ny * 2)),
-                        rng("workspace", workspace, need + ws_split_room(M, D, N2, fp8, unfused, workspace_bytes))};
+                        rng("workspace", workspace, need + ws_split_room(M, K1, D, N2, fp8, unfused, workspace_bytes))};
   return check_alias(in, 8, out, 3, out_h, R);
 }
 
@@ -344,12 +368,15 @@ int launch_block_fwd(const void* X, const void* W1, const void* R, const float* 
   int s;
   Workspace w;
   carve(workspace, M, D, 0, 0, &w);
-  const coda::KSplit ks = split_plan(workspace, M, D, N2, 0, ws_split_room(M, D, N2, 0, 0, workspace_bytes));
+  const SplitPlan sp = split_plan(workspace, M, K1, D, N2, 0, ws_split_room(M, K1, D, N2, 0, 0, workspace_bytes));
+  if (sp.tickets1 && (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
+    return s;
   if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R, gamma,
                                                  (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D, st, kPanels,
-                                                 ks),
+                                                 sp.g1),
                      "gemm1_res_prms launch")))
     return s;
+  const coda::KSplit& ks = sp.g2;
   if (coda::fold_supported((int)D))  // the reduce runs inside K3's workgroups
     return hip_check(coda::launch_gemm2_rowscale_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
                                                       epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M, (int)D,
@@ -419,19 +446,19 @@ const char* coda_status_string(int status) {
 const char* coda_last_error(void) { return g_last_error.c_str(); }
 
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused) {
-  (void)K1;
-  (void)N2;
   (void)epi_kind;
   if (M < 1 || D < 256 || M > kMaxDim || D > kMaxDim || fp8 < 0 || fp8 > 2 || (fp8 == 2 && unfused)) return 0;
   // the split room of the bf16 blocks (N2 outside the shape rules: none)
-  const size_t split = (N2 >= 256 && N2 <= kMaxDim && N2 % 256 == 0) ? ws_split_bytes(M, D, N2, fp8, kPlanCus) : 0;
+  const size_t split = (N2 >= 256 && N2 <= kMaxDim && N2 % 256 == 0 && K1 >= 1 && K1 <= kMaxDim)
+                           ? ws_split_bytes(M, K1, D, N2, fp8, kPlanCus)
+                           : 0;
   return ws_bytes(M, D, fp8, unfused ? 1 : 0) + split;
 }
 
 size_t coda_workspace_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused) {
   if (coda_workspace_bytes(M, K1, D, N2, epi_kind, fp8, unfused) == 0) return 0;
-  if (N2 < 256 || N2 > kMaxDim || N2 % 256) return 0;
-  return ws_split_bytes(M, D, N2, fp8, kPlanCus);
+  if (N2 < 256 || N2 > kMaxDim || N2 % 256 || K1 < 1 || K1 > kMaxDim) return 0;
+  return ws_split_bytes(M, K1, D, N2, fp8, kPlanCus);
 }
 
 size_t coda_workspace_r_offset(int64_t M, int64_t D) { return ws_part_bytes(M, D); }
@@ -484,12 +511,16 @@ int coda_block_fwd_rope(const void* X, const void* W1, const void* R, const floa
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 0, 0, &w);
-    const coda::KSplit ks = split_plan(workspace, M, D, N2, 0, ws_split_room(M, D, N2, 0, 0, workspace_bytes));
+    const SplitPlan sp = split_plan(workspace, M, K1, D, N2, 0, ws_split_room(M, K1, D, N2, 0, 0, workspace_bytes));
+    if (sp.tickets1 &&
+        (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
+      return s;
     if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R,
                                                    gamma, (uint16_t*)out_h, w.hg, w.part, (int)M, (int)K1, (int)D,
-                                                   st, kPanels, ks),
+                                                   st, kPanels, sp.g1),
                        "gemm1_res_prms launch")))
       return s;
+    const coda::KSplit& ks = sp.g2;
     if (coda::fold_supported((int)D))
       return hip_check(coda::launch_gemm2_rowscale_rope_fold(w.hg, (const uint16_t*)W2, w.part, eps, w.r,
                                                              (int)seq_len, (int)n_rope_cols, rope_base,
@@ -534,12 +565,16 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 0, 1, &w);
-    // the same split of GEMM2's last wave as the fused block (the same kernel family on the same tiles)
-    const coda::KSplit ks = split_plan(workspace, M, D, N2, 1, ws_split_room(M, D, N2, 0, 1, workspace_bytes));
+    // the same splits of the GEMMs' last waves as the fused block (the same kernel family on the same tiles)
+    const SplitPlan sp = split_plan(workspace, M, K1, D, N2, 1, ws_split_room(M, K1, D, N2, 0, 1, workspace_bytes));
+    if (sp.tickets1 &&
+        (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
+      return s;
     if ((s = hip_check(coda::launch_gemm_store((const uint16_t*)X, (const uint16_t*)W1, w.t, (int)M, (int)K1,
-                                               (int)D, st, 0, ks),
+                                               (int)D, st, 0, sp.g1),
                        "gemm_store launch")))
       return s;
+    const coda::KSplit& ks = sp.g2;
     if ((s = hip_check(coda::launch_add_rmsnorm(w.t, (const uint16_t*)R, gamma, (uint16_t*)out_h, w.n, w.r,
                                                 (int)M, (int)D, eps, st),
                        "add_rmsnorm launch")))
@@ -975,7 +1010,7 @@ int coda_block_fwd_save_z(const void* X, const void* W1, const void* R, const fl
                              rng("W2", W2, (size_t)(D * N2) * 2), rng("out_h", out_h, (size_t)(M * D) * 2),
                              rng("out_y", out_y, (size_t)(M * (N2 / 2)) * 2),
                              rng("workspace", workspace,
-                                 ws_bytes(M, D, 0, 0) + ws_split_room(M, D, N2, 0, 0, workspace_bytes))};
+                                 ws_bytes(M, D, 0, 0) + ws_split_room(M, K1, D, N2, 0, 0, workspace_bytes))};
     for (int i = 0; i < 8; ++i)
       if (overlap(zr, others[i])) return fail(CODA_ERR_ALIAS, "out_z overlaps %s", others[i].name);
     return launch_block_fwd(X, W1, R, gamma, W2, eps, CODA_EPI_SWIGLU, out_h, out_y, M, K1, D, N2, workspace,

@@ -137,10 +137,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
                                                     (MX_A ? NSTAGE * MX_STAGE_BYTES : 0)];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
-  // the split of the last wave (KSplit) exists for the bf16 row-scale modes; the first GEMMs clear its counters
-  constexpr bool CAN_SPLIT = ROWSCALE_MODE && !FP8;
-  if ((MODE == MODE_RES_PRMS || MODE == MODE_STORE) && ks.cnt && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < ks.ncnt; i += NTHREADS) ks.cnt[i] = 0;
+  // the split of the last wave (KSplit) exists for the bf16 kernels; the first GEMMs also clear the second GEMM's
+  // tickets
+  constexpr bool FIRST_GEMM = MODE == MODE_RES_PRMS || MODE == MODE_STORE;
+  constexpr bool CAN_SPLIT = (ROWSCALE_MODE || FIRST_GEMM) && !FP8;
+  if (FIRST_GEMM && ks.clear && blockIdx.x == 0)
+    for (int i = threadIdx.x; i < ks.nclear; i += NTHREADS) ks.clear[i] = 0;
   int tm, tn, piece = -1, tile_ord = 0;
   if (CAN_SPLIT && ks.full >= 0)
     piece = tile_coords_split(tiles_m, tiles_n, group_m, ks.full, tm, tn, tile_ord);
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, kpart, smem, acc, fold_hook,
                     NoDrain{}, small);
     else if (MODE == MODE_RES_PRMS)  // the residual tile's first 192 rows arrive as the ring drains
-      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
+      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook,
                     TileRowsDrain{R, Nb, m0, tn * BN, M, smem}, small);
     else
       gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook,
@@ -219,18 +221,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     // A piece of a split tile (KSplit): its accumulators go to its slot, lane-major (wave w's register group j at
     // w * 8192 + j * 256 floats, lane l at 4 l: each store instruction writes 1 KiB), then it takes a ticket.  The
     // workgroup that draws ticket 1 adds the other piece's slot, written in the same layout, to its accumulators.
-    // Ordering: every wave's slot stores have completed before the barrier (it waits for them), after which one wave
-    // makes them visible on every XCD (agent-scope release: the L2 writes its dirty lines back) and takes the ticket;
-    // on the other side one wave discards stale cached lines (agent-scope acquire) before the barrier that precedes
-    // the slot loads.  One wave per side is enough because the release and the acquire act on the whole L2 and on
-    // the CU's L1, which the workgroup's waves share; measured at the 1B MLP-out -> QKV shape, the same fences in
-    // every wave cost more than the split saved.
-    // The ticket is broadcast through the first word of the folded-reduce area (its partial sums were consumed by
-    // the hook long before); a __shared__ variable of its own would make the compiler wait for every in-flight
-    // direct load (vmcnt(0)) before each LDS read of the mainloop, unable to tell that the two objects do not
-    // overlap (measured: 40% on the product's time, whole tiles included).
-    static_assert(!CAN_SPLIT || FOLD_LDS > 0, "the split needs the folded-reduce area");
-    int& ticket = *(int*)(smem + LDS_BYTES + 1024);
+    // Ordering: every wave waits for its own slot stores to complete (vmcnt(0); a workgroup barrier alone does not
+    // wait for other waves' global stores), then after the barrier one wave makes them visible on every XCD
+    // (agent-scope release: the L2 writes its dirty lines back, whichever wave wrote them) and takes the ticket.  On
+    // the other side each wave discards stale cached lines (agent-scope acquire) before its own slot loads.  The
+    // release runs in one wave only: it acts on the whole L2, and in all eight waves (as seq_cst fences) it made the
+    // 1B MLP-out -> QKV GEMM2 2.4x slower; the acquire in every wave cost 0.2-3 us per block against one wave's.
+    // The ticket is broadcast through a word of the kernel's LDS array that nothing reads or writes at this point:
+    // the first word of the folded-reduce area (its partial sums were consumed by the hook long before), of the row
+    // sums' exchange area (used later in the epilogue), or of ring stage 0 (free after the mainloop where no drain
+    // refills it).  A __shared__ variable of its own would make the compiler wait for every in-flight direct load
+    // (vmcnt(0)) before each LDS read of the mainloop, unable to tell that the two objects do not overlap
+    // (measured: 40% on the product's time, whole tiles included).
+    static_assert(!CAN_SPLIT || !ROWSCALE_MODE || FOLD_LDS > 0, "the split needs the folded-reduce area");
+    int& ticket = *(int*)(MODE == MODE_RES_PRMS ? smem + LDS_BYTES : ROWSCALE_MODE ? smem + LDS_BYTES + 1024 : smem);
     const int64_t pair = tile_ord - ks.full;
     const int lane_off = (int)(threadIdx.x >> 6) * 8192 + (int)(threadIdx.x & 63) * 4;
     float* mine = ks.part + (pair * 2 + piece) * KSPLIT_SLOT_FLOATS + lane_off;
@@ -245,13 +249,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
           *(f32x4*)(mine + ((mb * NB + nb) * 4 + q) * 256) =
               (f32x4){a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
         }
-    __syncthreads();
+    wait_barrier<0>();  // every wave's slot stores have completed (a workgroup barrier alone does not wait for them)
     if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(ks.cnt + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (ticket == 0) return;  // the other piece finishes the tile
-    if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // each wave, before its own slot loads
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -832,15 +835,12 @@ static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, 
   const int tiles_n = Nb / BN;
   const int ntiles = tiles_m * tiles_n;
   constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
+  constexpr bool CAN_SPLIT = (ROWSCALE_MODE || MODE == MODE_RES_PRMS || MODE == MODE_STORE) && !FP8;
   int nwg = ntiles;
-  if (ROWSCALE_MODE && !FP8 && ks.full >= 0) {
-    if (ks.full >= ntiles || !ks.part || !ks.cnt || K % 256 || K < 1024)
-      ks.full = -1;  // nothing to split, or a split this K cannot take: whole tiles
-    else
-      nwg = ks.full + 2 * (ntiles - ks.full);
-  } else if (ROWSCALE_MODE) {
-    ks.full = -1;
-  }
+  if (CAN_SPLIT && ks.full >= 0 && ks.full < ntiles && ks.part && ks.cnt && K % 256 == 0 && K >= 1024)
+    nwg = ks.full + 2 * (ntiles - ks.full);
+  else
+    ks.full = -1;  // nothing to split, or a split this kernel or K cannot take: whole tiles
   dim3 grid(nwg), block(NTHREADS);
   if constexpr (!FP8) {
     if (M <= SMALL_MAX_ROWS) {  // the small-row form: a quarter of the MFMAs per SIMD
@@ -854,6 +854,17 @@ static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, 
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void clear_tickets_kernel(int* __restrict__ cnt, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) cnt[i] = 0;
+}
+
+hipError_t launch_clear_tickets(int* cnt, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(clear_tickets_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cnt, n);
+  return hipGetLastError();
+}
+
 int ksplit_full(int64_t ntiles, int64_t K, int cus) {
   if (cus <= 0 || ntiles <= 0 || K < 1024 || K % 256) return (int)ntiles;
   const int64_t rem = ntiles % cus;
@@ -863,9 +874,9 @@ int ksplit_full(int64_t ntiles, int64_t K, int cus) {
 
 hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, const float* gamma,
                                  uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream,
-                                 int panels, KSplit clear) {
+                                 int panels, KSplit ks) {
   return launch_gemm<MODE_RES_PRMS, false>(X, W1, gamma, R, nullptr, nullptr, H, HG, part, M, K1, D, stream,
-                                           RopeParams{}, RowFold{}, nullptr, panels, clear);
+                                           RopeParams{}, RowFold{}, nullptr, panels, ks);
 }
 
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
@@ -1001,9 +1012,9 @@ hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, cons
 }
 
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
-                             hipStream_t stream, int a_panels, KSplit clear) {
+                             hipStream_t stream, int a_panels, KSplit ks) {
   return launch_gemm<MODE_STORE, false>(X, W, nullptr, nullptr, nullptr, nullptr, T, nullptr, nullptr, M, K, N, stream,
-                                        RopeParams{}, RowFold{}, nullptr, a_panels, clear);
+                                        RopeParams{}, RowFold{}, nullptr, a_panels, ks);
 }
 
 hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,

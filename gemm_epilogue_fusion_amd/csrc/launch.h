@@ -6,19 +6,21 @@
 
 namespace coda {
 
-// Split of the second GEMM's last, partial wave of output tiles.  When the tile count leaves a last wave that fills
-// at most a quarter of the CUs, the tiles of that wave (the last ones in the tile order) are each computed as two
-// pieces over the two halves of K, so the last wave runs on twice as many CUs: the grid holds `full` whole tiles,
-// then 2 (ntiles - full) pieces.  Each piece stores its fp32 accumulators in its slot of `part`, then takes a ticket
+// Split of a GEMM's last, partial wave of output tiles.  When the tile count leaves a last wave that fills at most a
+// quarter of the CUs, the tiles of that wave (the last ones in the tile order) are each computed as two pieces over
+// the two halves of K, so the last wave runs on twice as many CUs: the grid holds `full` whole tiles, then
+// 2 (ntiles - full) pieces.  Each piece stores its fp32 accumulators in its slot of `part`, then takes a ticket
 // from its tile's counter; the piece that draws the second ticket adds the other piece's slot to its own
 // accumulators (fp32 addition is commutative, so the sum does not depend on which piece comes second) and runs the
 // epilogue; the first one exits.  No piece waits for another.  The counters must be zero at launch: the block's
-// first kernel clears them (`ncnt` counters from `cnt` when it is given them).
+// first GEMM clears those of its second GEMM (`clear`, `nclear`), and launch_clear_tickets clears the first GEMM's
+// own before it runs.  Both GEMMs of the bf16 blocks (K1 or U1, and K3 or U3) can be split.
 struct KSplit {
   int full = -1;          // whole tiles; negative: no split
-  int ncnt = 0;           // first kernels: counters to clear
   float* part = nullptr;  // 2 (ntiles - full) slots of KSPLIT_SLOT_FLOATS fp32
   int* cnt = nullptr;     // ntiles - full tickets
+  int* clear = nullptr;   // the block's first GEMM: the second GEMM's tickets, zeroed by its workgroup 0
+  int nclear = 0;
 };
 constexpr int KSPLIT_SLOT_FLOATS = 512 * 128;  // one workgroup's accumulators (512 lanes x 128)
 // The number of whole tiles of a split for `ntiles` output tiles over K on `cus` CUs; ntiles when no split pays:
@@ -28,6 +30,8 @@ constexpr int KSPLIT_SLOT_FLOATS = 512 * 128;  // one workgroup's accumulators (
 // the pieces' fp32 slots cross the memory system (256 KiB written per piece, 256 KiB read per tile), and a last
 // wave of whole tiles on part of the chip runs at a higher clock than the full chip does.
 int ksplit_full(int64_t ntiles, int64_t K, int cus);
+// Zeroes n tickets (a small kernel on `stream`; graph-capturable, unlike a memset node).
+hipError_t launch_clear_tickets(int* cnt, int n, hipStream_t stream);
 
 // K1: H = bf16(X W1 + R), HG = bf16((X W1 + R) * gamma) and part[t][m] = sum over tile t's 256 columns of
 // the fp32 (X W1 + R)^2.
@@ -35,12 +39,11 @@ int ksplit_full(int64_t ntiles, int64_t K, int cus);
 // mainloop's stage width ([D / 32][M][32] bf16, [D / 64][M][64] e4m3 bytes) instead of row-major [M, D].
 hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const uint16_t* R, const float* gamma,
                                  uint16_t* H, uint16_t* HG, float* part, int M, int K1, int D, hipStream_t stream,
-                                 int panels = 0, KSplit clear = KSplit());
+                                 int panels = 0, KSplit ks = KSplit());
 // K2: r[m] = 1 / sqrt(sum_t part[t][m] / D + eps).
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream);
 // K3 (r non-null; A = h * gamma) and U3 (r null; A = the normalised rows): Y = bf16(epi(r * (A W2))).
-// ks (here and in the fold and rope launchers): the split of the last wave (KSplit); K1 and U1 take the same
-// struct as `clear` and zero its counters.
+// ks (here, in the fold and rope launchers, and for K1 and U1): the split of the GEMM's last wave (KSplit).
 // Z (SwiGLU only, may be null): also store the pre-activation z = [gate | up] = r (A W2) as bf16 [M, N2].
 hipError_t launch_gemm2_rowscale(const uint16_t* A, const uint16_t* W2, const float* r, int swiglu, uint16_t* Y,
                                  int M, int D, int N2, hipStream_t stream, uint16_t* Z = nullptr, int panels = 0,
@@ -63,7 +66,7 @@ hipError_t launch_gemm2_rowscale_rope_fold(const uint16_t* A, const uint16_t* W2
 hipError_t launch_rope_rows(uint16_t* Y, int M, int N, int seq_len, int n_rot, float base, hipStream_t stream);
 // U1: T = bf16(X W); a_panels: X given in K panels of 32 ([K/32][M][32], as launch_panelize_bf16 writes).
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
-                             hipStream_t stream, int a_panels = 0, KSplit clear = KSplit());
+                             hipStream_t stream, int a_panels = 0, KSplit ks = KSplit());
 // U2: H = bf16(T + R), N = bf16((T + R) r gamma), r[m] (optional).  D <= 8192.
 hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* N,
                               float* r, int M, int D, float eps, hipStream_t stream);

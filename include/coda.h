@@ -93,15 +93,16 @@ const char* coda_last_error(void);
  *            ((k / P) * M + m) * P + k % P with P = 32 (bf16) or 64 (e4m3), so that the second product reads
  *            whole cache lines
  *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]), row-major.
- * then, for the bf16 blocks (fp8 = 0) where the second product's tile count, ceil(M/256) * N2/256, leaves a last
- * wave that fills at most a quarter of 256 CUs (and D >= 1024), the room to split that wave along K: one int32 ticket
- * per tile of the last wave (256-byte aligned), then two fp32 slots of 256 KiB per such tile.  A block given a
- * workspace of at least the size without that room runs; it splits the last wave only where the room is there
- * (the results of the two forms differ in the last bits of the fp32 sums, nowhere else). */
+ * then, for the bf16 blocks (fp8 = 0), the room to split a product's last wave of tiles along K where that wave
+ * fills at most a quarter of 256 CUs: the second product (ceil(M/256) * N2/256 tiles over K = D), then the first
+ * (ceil(M/256) * D/256 tiles over K1), each where its K >= 1024: one int32 ticket per tile of the last wave
+ * (256-byte aligned), then two fp32 slots of 256 KiB per such tile.  A block given a workspace of at least the size
+ * without that room runs; it splits the last waves only where the room is there (the results of the two forms
+ * differ in the last bits of the fp32 sums, nowhere else). */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
-/* The part of coda_workspace_bytes (same arguments) that is the split room of the second product's last wave:
- * 0 where there is none; coda_workspace_bytes minus this is the smallest workspace a block accepts. */
+/* The part of coda_workspace_bytes (same arguments) that is the split room of the products' last waves: 0 where
+ * there is none; coda_workspace_bytes minus this is the smallest workspace a block accepts. */
 size_t coda_workspace_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
 /* The fused block, bf16 operands: the GEMM -> residual -> RMSNorm -> GEMM block of the write-up's section
@@ -114,10 +115,11 @@ size_t coda_workspace_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, 
  *   out_y [M,N2 or N2/2] bf16 = bf16(epi(r * (hg W2))), hg = bf16(h * gamma)          (output)
  * Two kernels on `stream` where D <= 4096: GEMM1 + residual + gamma + partial sums of squares, then GEMM2 on
  * hg whose workgroups reduce their rows' partial sums to r themselves and apply r (+ SwiGLU) in the epilogue.
- * Where D > 4096 the reduction runs as a kernel of its own between the two (three kernels).  Where the second
- * product's last wave of 256 x 256 tiles would leave more than three quarters of the CUs idle, each of its tiles is computed
+ * Where D > 4096 the reduction runs as a kernel of its own between the two (three kernels).  Where a product's
+ * last wave of 256 x 256 tiles would leave more than three quarters of the CUs idle, each of its tiles is computed
  * as two halves of K whose fp32 sums are added before the epilogue (see coda_workspace_bytes for the room this
- * takes).  After the call the workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D).  Ownership, errors and the
+ * takes); where the first product is split, a small kernel that zeroes its tickets runs first.  After the call the
+ * workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D).  Ownership, errors and the
  * asynchronous contract are the shared conventions above. */
 int coda_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
                    float eps, int epi_kind, void* out_h, void* out_y,
@@ -135,7 +137,7 @@ int coda_block_fwd(const void* X, const void* W1, const void* R, const float* ga
  * call (no hipMalloc, hipFree or allocating library routine); the first call on a device looks the array's
  * address up once (hipGetSymbolAddress).  Limit: the workspace without the split room (coda_workspace_bytes)
  * must not exceed CODA_NOALLOC_SCRATCH_BYTES (M * D up to about 33 million: the 1B shapes fit, M = 16384 with
- * D = 4096 does not), else CODA_ERR_WORKSPACE before anything is enqueued; the last wave is split as in
+ * D = 4096 does not), else CODA_ERR_WORKSPACE before anything is enqueued; the last waves are split as in
  * coda_block_fwd where the scratch also holds the split room, so the outputs equal coda_block_fwd's bit for bit
  * wherever coda_workspace_bytes(M, K1, D, N2, epi_kind, 0, 0) fits the scratch.  Every call on one device shares that
  * device's array and leaves its contents there (nothing in it needs clearing between calls: every byte the
@@ -168,7 +170,7 @@ int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const f
  *   T = bf16(X W1)  ->  hf = fp32(T) + fp32(R), h = bf16(hf), r = 1 / sqrt(mean(hf^2) + eps),
  *   n = bf16(hf * r * gamma)  ->  y = bf16(epi(n W2)).
  * T and n live in the workspace (row-major).  Same arguments, outputs, errors and conventions as
- * coda_block_fwd, including the split of the second product's last wave; after the call the workspace holds r
+ * coda_block_fwd, including the splits of the products' last waves; after the call the workspace holds r
  * at coda_workspace_r_offset(M, D). */
 int coda_block_unfused(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
                        float eps, int epi_kind, void* out_h, void* out_y,

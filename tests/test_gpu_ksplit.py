@@ -1,20 +1,21 @@
-"""GPU tests of the split of the second product's last wave of tiles, through the C ABI.
+"""GPU tests of the split of the GEMMs' last waves of tiles, through the C ABI.
 
-Where the second product's 256 x 256 output tiles leave a last wave that fills at most a quarter of the CUs, each tile
-of that wave is computed as two halves of K whose fp32 sums are added before the epilogue (coda_workspace_bytes
-in include/coda.h describes the room this takes in the workspace).  Checked here:
-- the split is taken where it is planned: after a call every tile of the last wave holds ticket 2 (both halves
-  ran and each took its ticket);
-- small shapes whose every tile is split (a ragged row tile, SwiGLU and identity epilogues, the path with the
-  reduce as a kernel of its own) and a shape with a whole wave plus a split tail, fused and unfused, against the
-  oracle (every element on the small shapes; rows covering every row tile on the tail shape), and against the
-  same block run on whole tiles (a workspace without the split room): h and r equal bit for bit, y within the
-  fp32 summation-order difference;
+Where a GEMM's 256 x 256 output tiles leave a last wave that fills at most a quarter of the CUs, each tile of that wave
+is computed as two halves of K whose fp32 sums are added before the epilogue, in either GEMM of the bf16 blocks
+(coda_workspace_bytes in include/coda.h describes the room this takes in the workspace).  Checked here:
+- the split is taken where it is planned: after a call every split tile of either GEMM holds ticket 2 (both halves
+  ran and each took its ticket), and the workspace's split room matches the rule written out here;
+- small shapes with the second GEMM's tiles split (a ragged row tile, SwiGLU and identity epilogues, the path with
+  the reduce as a kernel of its own), the first GEMM's, or both, and a shape with a whole wave plus a split tail,
+  fused and unfused, against the oracle (every element on the small shapes; rows covering every row tile on the
+  tail shape), and against the same block run on whole tiles (a workspace without the split room): y within the
+  fp32 summation-order difference, h and r equal bit for bit where the first GEMM is not split;
 - outputs bit-identical run to run, whichever half finishes second;
-- a full-size shape with a last wave of 32 tiles (a QKV projection with 2 key-value heads of 64 after the 1B
-  hidden size: 8192 rows, D = 2048, 2048 + 2 x 128 output columns, 288 tiles): tickets, run-to-run identity, a row
-  in every row tile against the oracle and every row against the whole-tile run; the 1B MLP-out -> QKV shape itself
-  (384 tiles, a last wave of 128) is not split, the rule written out here and in the CPU tests;
+- full size: a last wave of 32 tiles in the second GEMM (a QKV projection with 2 key-value heads of 64 after the 1B
+  hidden size: 8192 rows, D = 2048, 2048 + 2 x 128 output columns, 288 tiles), and the 1B MLP-out -> QKV block on
+  1024 rows (both GEMMs' tiles split): tickets, run-to-run identity, a row in every row tile against the oracle and
+  every row against the whole-tile run; the 1B MLP-out -> QKV shape itself (384 tiles, a last wave of 128) is not
+  split;
 - the block with the rotary embedding and the forward that keeps z take the same split.
 """
 import sys
@@ -54,24 +55,41 @@ def _need_gpu():
         pytest.skip("the split room is planned for 256 CUs")
 
 
-def _tail(wl: Workload, unfused: bool = False) -> int:
-    """Tiles of the last wave the workspace has room to split (from the library's own size query)."""
-    split = cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
-    return split // (2 * SLOT_BYTES)
-
-
-def _expected_tail(wl: Workload) -> int:
-    """The plan written out: the tiles of a last wave that fills at most a quarter of the CUs, for K = D >= 1024."""
-    tiles = (wl.M + 255) // 256 * (wl.N2 // 256)
+def _rule(tiles: int, K: int) -> int:
+    """The split rule written out: the tiles of a last wave that fills at most a quarter of the CUs, for K >= 1024 (a
+    multiple of 256)."""
     rem = tiles % PLAN_CUS
-    return rem if (wl.D >= 1024 and wl.D % 256 == 0 and 0 < rem and 4 * rem <= PLAN_CUS) else 0
+    return rem if (K >= 1024 and K % 256 == 0 and 0 < rem and 4 * rem <= PLAN_CUS) else 0
 
 
-def _tickets(ws: torch.Tensor, wl: Workload, unfused: bool = False) -> torch.Tensor:
+def _tails(wl: Workload):
+    """(split tiles of the first GEMM, over K1; split tiles of the second, over D)."""
+    rt = (wl.M + 255) // 256
+    return _rule(rt * (wl.D // 256), wl.K1), _rule(rt * (wl.N2 // 256), wl.D)
+
+
+def _al(x: int) -> int:
+    return (x + 255) // 256 * 256
+
+
+def _room(t: int) -> int:
+    return _al(4 * t) + 2 * t * SLOT_BYTES if t else 0
+
+
+def _tickets(ws: torch.Tensor, wl: Workload, unfused: bool = False):
+    """The tickets after a call: (the first GEMM's, the second GEMM's).  The split room follows the workspace's base
+    part: the second GEMM's tickets and slots, then the first GEMM's."""
     total = cb.coda_workspace_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
     base = total - cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
-    n = _tail(wl, unfused)
-    return ws[base: base + 4 * n].view(torch.int32).cpu()
+    t1, t2 = _tails(wl)
+    g2 = ws[base: base + 4 * t2].view(torch.int32).cpu()
+    o1 = base + _room(t2)
+    g1 = ws[o1: o1 + 4 * t1].view(torch.int32).cpu()
+    return g1, g2
+
+
+def _both_tickets_taken(ws, wl, unfused=False) -> bool:
+    return all(bool((g == 2).all()) for g in _tickets(ws, wl, unfused))
 
 
 def _run(d: DeviceInputs, unfused=False, split=True):
@@ -83,21 +101,35 @@ def _run(d: DeviceInputs, unfused=False, split=True):
 # a QKV projection with 2 key-value heads of 64 at the 1B hidden size: 32 x 9 = 288 tiles, a last wave of 32
 QKV_2KV = Workload("1b_qkv_2kv", M=8192, K1=2048, D=2048, N2=2304, epi=EPI_IDENTITY, eps=1e-5, seed=65)
 
+# the 1B MLP-out -> QKV block on 1024 rows (an eighth of the rows, as one GPU of eight holds them): the first GEMM's
+# 4 x 8 = 32 tiles and the second's 4 x 12 = 48 tiles are all split
+QKV_ROWS1024 = Workload("1b_mlp_out_qkv_1024_rows", M=1024, K1=8192, D=2048, N2=3072, epi=EPI_IDENTITY, eps=1e-5,
+                        seed=66)
+
 SMALL = [
     Workload("split_swiglu_ragged", M=300, K1=256, D=1024, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=61),
     Workload("split_identity_one_row_tile", M=64, K1=128, D=2048, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=62),
     # D / 256 = 17: the reduce is a kernel of its own, the second product reads r; halves of K = 2176
     Workload("split_no_fold", M=130, K1=128, D=4352, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=63),
+    # the first GEMM split (4 tiles over K1 = 2048), the second not (D = 512)
+    Workload("split_first_gemm", M=300, K1=2048, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=67),
+    # both GEMMs split: 8 tiles over K1 = 1024, 4 tiles over D = 1024
+    Workload("split_both_gemms", M=260, K1=1024, D=1024, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=68),
 ]
 
 
 def test_plan_matches_the_written_rule():
-    for wl in SMALL + [WORKLOADS["1b_mlp_out_qkv"], WORKLOADS["1b_attn_out_mlp_in"], WORKLOADS["tiny"]]:
+    for wl in SMALL + [QKV_2KV, QKV_ROWS1024, WORKLOADS["1b_mlp_out_qkv"], WORKLOADS["1b_attn_out_mlp_in"],
+                       WORKLOADS["tiny"]]:
+        t1, t2 = _tails(wl)
         for unfused in (False, True):
-            assert _tail(wl, unfused) == _expected_tail(wl), (wl.name, unfused)
-    assert _expected_tail(WORKLOADS["1b_mlp_out_qkv"]) == 0   # a last wave of 128 tiles: over a quarter
-    assert _expected_tail(WORKLOADS["1b_attn_out_mlp_in"]) == 0
-    assert _expected_tail(QKV_2KV) == 32
+            assert cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused)) == \
+                _room(t1) + _room(t2), (wl.name, unfused)
+    assert _tails(WORKLOADS["1b_mlp_out_qkv"]) == (0, 0)   # 256 tiles; a last wave of 128 tiles: over a quarter
+    assert _tails(WORKLOADS["1b_attn_out_mlp_in"]) == (0, 0)
+    assert _tails(QKV_2KV) == (0, 32)
+    assert _tails(QKV_ROWS1024) == (32, 48)
+    assert [_tails(w) for w in SMALL] == [(0, 8), (0, 2), (0, 2), (4, 0), (8, 4)]
 
 
 @pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
@@ -106,10 +138,10 @@ def test_split_small_against_oracle(wl, unfused):
     _say(f"[gpu] split {'unfused' if unfused else 'fused'} {wl}")
     inp = make_inputs(wl)
     d = DeviceInputs(inp)
-    n = _tail(wl, unfused)
-    assert n == (wl.M + 255) // 256 * (wl.N2 // 256) > 0  # every tile split
+    t1, t2 = _tails(wl)
+    assert t1 + t2 > 0
     h, y, r, ws = _run(d, unfused)
-    assert bool((_tickets(ws, wl, unfused) == 2).all()), "a split tile did not take both tickets"
+    assert _both_tickets_taken(ws, wl, unfused), "a split tile did not take both tickets"
     form = "unfused" if unfused else "fused"
     oh, orr, oy = oracle_rows(inp, form=form)
     check_h(f64(h), oh)
@@ -119,11 +151,15 @@ def test_split_small_against_oracle(wl, unfused):
     else:
         np.testing.assert_allclose(f64(r), orr, rtol=2e-5)
         check_roundpts(f64(y), oracle_rows(inp, form="roundpts")[2])
-    # the same block on whole tiles: the first product and r are untouched by the split, y differs only by the
-    # order of the fp32 sums
+    # the same block on whole tiles: the outputs differ only by the order of the fp32 sums (h and r not at all where
+    # the first GEMM is not split)
     h0, y0, r0, _ = _run(d, unfused, split=False)
-    assert torch.equal(h.view(torch.int16), h0.view(torch.int16))
-    assert torch.equal(r.view(torch.int32), r0.view(torch.int32))
+    if t1 == 0:
+        assert torch.equal(h.view(torch.int16), h0.view(torch.int16))
+        assert torch.equal(r.view(torch.int32), r0.view(torch.int32))
+    else:
+        assert normwise(f64(h), f64(h0)) <= CLOSE_NORMWISE
+        np.testing.assert_allclose(f64(r), f64(r0), rtol=1e-5)
     g, w = f64(y), f64(y0)
     assert normwise(g, w) <= CLOSE_NORMWISE and mae_rel(g, w) <= CLOSE_MAE_REL
 
@@ -144,11 +180,11 @@ def test_split_tail_after_a_whole_wave():
     against the oracle, every row against the whole-tile run."""
     wl = Workload("split_tail", M=2048, K1=256, D=1024, N2=8448, epi=EPI_IDENTITY, eps=1e-5, seed=64)
     _say(f"[gpu] split tail {wl}")
-    assert _tail(wl) == 8
+    assert _tails(wl) == (0, 8)
     inp = make_inputs(wl)
     d = DeviceInputs(inp)
     h, y, r, ws = _run(d)
-    assert bool((_tickets(ws, wl) == 2).all())
+    assert _both_tickets_taken(ws, wl)
     rows = sample_rows_covering(wl.M, n=64, seed=5)
     oh, orr, oy = oracle_rows(inp, rows)
     hg, yg = f64(h), f64(y)
@@ -162,14 +198,13 @@ def test_split_tail_after_a_whole_wave():
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
-def test_split_full_size_tail(unfused):
-    wl = QKV_2KV
+@pytest.mark.parametrize("wl", [QKV_2KV, QKV_ROWS1024], ids=[QKV_2KV.name, QKV_ROWS1024.name])
+def test_split_full_size(wl, unfused):
     _say(f"[gpu] split full size {'unfused' if unfused else 'fused'} {wl}")
-    assert _tail(wl, unfused) == 32
     inp = make_inputs(wl)
     d = DeviceInputs(inp)
     h1, y1, r1, ws = _run(d, unfused)
-    assert bool((_tickets(ws, wl, unfused) == 2).all())
+    assert _both_tickets_taken(ws, wl, unfused)
     del ws
     _, y2, _, _ = _run(d, unfused)
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
@@ -198,7 +233,7 @@ def test_split_rope_block():
     ws.fill_(0xFF)
     cb.coda_block_fwd_rope(d.X, d.W1, d.R, d.gamma, d.W2, wl.eps, seq_len, n_rot, base, h, y, ws)
     torch.cuda.synchronize()
-    assert bool((_tickets(ws, wl) == 2).all())
+    assert _both_tickets_taken(ws, wl)
     oh, _, oy = oracle_rows(inp)
     check_h(f64(h), oh)
     check_y(f64(y), oracle.rope_rows(oy, 64, n_rot, seq_len, base))
