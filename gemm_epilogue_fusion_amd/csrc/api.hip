@@ -176,11 +176,14 @@ constexpr int kPlanCus = 256;
 
 int64_t gemm_tiles(int64_t M, int64_t N) { return (M + 255) / 256 * (N / 256); }
 
-// One GEMM's split room for `ntiles` tiles over K on `cus` CUs (0: no split).
+// One GEMM's split room for `ntiles` tiles over K on `cus` CUs (0: no split): per split tile S - 1 tickets and
+// 2 S - 2 slots (the tree of coda::KSplit).
 size_t split_bytes_one(int64_t ntiles, int64_t K, int cus) {
-  const int64_t tail = ntiles - coda::ksplit_full(ntiles, K, cus);
+  int lg = 0;
+  const int64_t tail = ntiles - coda::ksplit_plan(ntiles, K, cus, &lg);
   if (tail <= 0) return 0;
-  return align256((size_t)tail * 4) + (size_t)(2 * tail) * coda::KSPLIT_SLOT_FLOATS * 4;
+  const int64_t S = (int64_t)1 << lg;
+  return align256((size_t)(tail * (S - 1)) * 4) + (size_t)(tail * (2 * S - 2)) * coda::KSPLIT_SLOT_FLOATS * 4;
 }
 
 size_t ws_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int fp8, int cus) {
@@ -212,15 +215,19 @@ int device_cus() {
 }
 
 // One GEMM's split laid out from `at` (which then moves past it); no split where the plan has none.
-coda::KSplit split_one(char*& at, int64_t ntiles, int64_t K, int cus) {
+coda::KSplit split_one(char*& at, int64_t ntiles, int64_t K, int cus, int* tickets) {
   coda::KSplit ks;
-  const int64_t full = coda::ksplit_full(ntiles, K, cus);
+  int lg = 0;
+  const int64_t full = coda::ksplit_plan(ntiles, K, cus, &lg);
+  *tickets = 0;
   if (full >= ntiles) return ks;
-  const int64_t tail = ntiles - full;
+  const int64_t tail = ntiles - full, S = (int64_t)1 << lg;
   ks.full = (int)full;
+  ks.lg = lg;
   ks.cnt = (int*)at;
-  ks.part = (float*)(at + align256((size_t)tail * 4));
-  at += align256((size_t)tail * 4) + (size_t)(2 * tail) * coda::KSPLIT_SLOT_FLOATS * 4;
+  ks.part = (float*)(at + align256((size_t)(tail * (S - 1)) * 4));
+  at += split_bytes_one(ntiles, K, cus);
+  *tickets = (int)(tail * (S - 1));
   return ks;
 }
 
@@ -238,13 +245,13 @@ SplitPlan split_plan(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int
   const size_t need = ws_split_bytes(M, K1, D, N2, 0, cus);
   if (!need || need > room) return p;
   char* at = (char*)ws + ws_bytes(M, D, 0, unfused);
-  p.g2 = split_one(at, gemm_tiles(M, N2), D, cus);
-  p.g1 = split_one(at, gemm_tiles(M, D), K1, cus);
+  int tickets2 = 0;
+  p.g2 = split_one(at, gemm_tiles(M, N2), D, cus, &tickets2);
+  p.g1 = split_one(at, gemm_tiles(M, D), K1, cus, &p.tickets1);
   if (p.g2.full >= 0) {
     p.g1.clear = p.g2.cnt;
-    p.g1.nclear = (int)(gemm_tiles(M, N2) - p.g2.full);
+    p.g1.nclear = tickets2;
   }
-  if (p.g1.full >= 0) p.tickets1 = (int)(gemm_tiles(M, D) - p.g1.full);
   return p;
 }
 

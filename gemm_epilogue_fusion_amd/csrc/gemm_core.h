@@ -781,12 +781,12 @@ __device__ __forceinline__ void tile_coords(int tiles_m, int tiles_n, int group_
   tile_of_order(b, tiles_m, tiles_n, group_m, tm, tn);
 }
 
-// The same with the tiles from `full` on (in tile order) split in two pieces along K: workgroups 0 .. full-1 take
-// whole tiles as tile_coords deals them (over `full` tiles), the next 2 (ntiles - full) take pieces, XCD by XCD in
-// contiguous ranges of the piece order with both pieces of a tile on one XCD where the count allows.  Returns the
-// piece (0: the first half of K, 1: the second) or -1 for a whole tile; b_out is the tile's place in the tile order.
-__device__ __forceinline__ int tile_coords_split(int tiles_m, int tiles_n, int group_m, int full, int& tm, int& tn,
-                                                 int& b_out) {
+// The same with the tiles from `full` on (in tile order) split in 2^lg pieces along K: workgroups 0 .. full-1 take
+// whole tiles as tile_coords deals them (over `full` tiles), the next (ntiles - full) 2^lg take pieces, XCD by XCD in
+// contiguous ranges of the piece order, with all pieces of a tile on one XCD where the count allows.  Returns the
+// piece (0 .. 2^lg - 1: its place along K) or -1 for a whole tile; b_out is the tile's place in the tile order.
+__device__ __forceinline__ int tile_coords_split(int tiles_m, int tiles_n, int group_m, int full, int lg, int& tm,
+                                                 int& tn, int& b_out) {
   const int ntiles = tiles_m * tiles_n;
   int b = blockIdx.x;
   int piece = -1;
@@ -794,10 +794,10 @@ __device__ __forceinline__ int tile_coords_split(int tiles_m, int tiles_n, int g
     if ((full & 7) == 0) b = (b & 7) * (full >> 3) + (b >> 3);
   } else {
     int p = b - full;
-    const int np = 2 * (ntiles - full);
-    if ((np & 15) == 0) p = (p & 7) * (np >> 3) + (p >> 3);  // np / 8 even: a pair never straddles two XCDs
-    piece = p & 1;
-    b = full + (p >> 1);
+    const int np = (ntiles - full) << lg;
+    if ((np & ((8 << lg) - 1)) == 0) p = (p & 7) * (np >> 3) + (p >> 3);  // np / 8 a multiple of 2^lg
+    piece = p & ((1 << lg) - 1);
+    b = full + (p >> lg);
   }
   b_out = b;
   tile_of_order(b, tiles_m, tiles_n, group_m, tm, tn);

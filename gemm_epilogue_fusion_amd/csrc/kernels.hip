@@ -145,13 +145,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     for (int i = threadIdx.x; i < ks.nclear; i += NTHREADS) ks.clear[i] = 0;
   int tm, tn, piece = -1, tile_ord = 0;
   if (CAN_SPLIT && ks.full >= 0)
-    piece = tile_coords_split(tiles_m, tiles_n, group_m, ks.full, tm, tn, tile_ord);
+    piece = tile_coords_split(tiles_m, tiles_n, group_m, ks.full, ks.lg, tm, tn, tile_ord);
   else
     tile_coords(tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM;
-  // a piece multiplies over its half of K
-  const int kpart = piece >= 0 ? K / 2 : K;
-  const int kbeg = piece > 0 ? kpart : 0;
+  // a piece multiplies over its share of K
+  const int kpart = piece >= 0 ? K >> ks.lg : K;
+  const int kbeg = piece > 0 ? piece * kpart : 0;
 
   // folded reduce: before the mainloop the partial sums of the tile's rows go global -> LDS (4 bytes per lane,
   // 64 rows per load, rows past M read row M-1), older than every stage load, so the mainloop's first wait
@@ -218,9 +218,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(acc[mb][nb]));
 
   if (CAN_SPLIT && piece >= 0) {
-    // A piece of a split tile (KSplit): its accumulators go to its slot, lane-major (wave w's register group j at
-    // w * 8192 + j * 256 floats, lane l at 4 l: each store instruction writes 1 KiB), then it takes a ticket.  The
-    // workgroup that draws ticket 1 adds the other piece's slot, written in the same layout, to its accumulators.
+    // A piece of a split tile (KSplit): the pieces meet in a binary tree.  At level l the piece stores its
+    // accumulators in its slot, lane-major (wave w's register group j at w * 8192 + j * 256 floats, lane l at 4 l:
+    // each store instruction writes 1 KiB), then takes a ticket from its node's counter; the workgroup that draws
+    // ticket 1 adds the sibling's slot, written in the same layout, to its accumulators and goes up a level.
     // Ordering: every wave waits for its own slot stores to complete (vmcnt(0); a workgroup barrier alone does not
     // wait for other waves' global stores), then after the barrier one wave makes them visible on every XCD
     // (agent-scope release: the L2 writes its dirty lines back, whichever wave wrote them) and takes the ticket.  On
@@ -235,36 +236,47 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     // (measured: 40% on the product's time, whole tiles included).
     static_assert(!CAN_SPLIT || !ROWSCALE_MODE || FOLD_LDS > 0, "the split needs the folded-reduce area");
     int& ticket = *(int*)(MODE == MODE_RES_PRMS ? smem + LDS_BYTES : ROWSCALE_MODE ? smem + LDS_BYTES + 1024 : smem);
-    const int64_t pair = tile_ord - ks.full;
+    const int S = 1 << ks.lg;
+    const int64_t st = tile_ord - ks.full;  // the split tile's index
+    float* slots = ks.part + st * (2 * S - 2) * KSPLIT_SLOT_FLOATS;
+    int* tickets = ks.cnt + st * (S - 1);
     const int lane_off = (int)(threadIdx.x >> 6) * 8192 + (int)(threadIdx.x & 63) * 4;
-    float* mine = ks.part + (pair * 2 + piece) * KSPLIT_SLOT_FLOATS + lane_off;
-    const float* other = ks.part + (pair * 2 + (piece ^ 1)) * KSPLIT_SLOT_FLOATS + lane_off;
+    int idx = piece;  // this workgroup's node at the current level
+#pragma unroll 1
+    for (int l = 0; l < ks.lg; ++l) {
+      const int slot0 = 2 * S - 2 * (S >> l);  // level l's first slot
+      float* mine = slots + (int64_t)(slot0 + idx) * KSPLIT_SLOT_FLOATS + lane_off;
+      const float* other = slots + (int64_t)(slot0 + (idx ^ 1)) * KSPLIT_SLOT_FLOATS + lane_off;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x16& a = acc[mb][nb];
-          *(f32x4*)(mine + ((mb * NB + nb) * 4 + q) * 256) =
-              (f32x4){a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
-        }
-    wait_barrier<0>();  // every wave's slot stores have completed (a workgroup barrier alone does not wait for them)
-    if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(ks.cnt + pair, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (ticket == 0) return;  // the other piece finishes the tile
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // each wave, before its own slot loads
+          for (int q = 0; q < 4; ++q) {
+            const f32x16& a = acc[mb][nb];
+            *(f32x4*)(mine + ((mb * NB + nb) * 4 + q) * 256) =
+                (f32x4){a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+          }
+      wait_barrier<0>();  // every wave's slot stores have completed (a workgroup barrier alone does not wait for them)
+      if (threadIdx.x < 64) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (threadIdx.x == 0)
+        ticket = __hip_atomic_fetch_add(tickets + (S - (S >> l)) + (idx >> 1), 1, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (ticket == 0) return;  // the sibling goes on
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // each wave, before its own slot loads
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 o = *(const f32x4*)(other + ((mb * NB + nb) * 4 + q) * 256);
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 o = *(const f32x4*)(other + ((mb * NB + nb) * 4 + q) * 256);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[mb][nb][4 * q + e] += o[e];
-        }
+            for (int e = 0; e < 4; ++e) acc[mb][nb][4 * q + e] += o[e];
+          }
+      idx >>= 1;
+    }
   }
 
   // ---- epilogue: the accumulator tile is still in registers ----
@@ -837,8 +849,9 @@ static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, 
   constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
   constexpr bool CAN_SPLIT = (ROWSCALE_MODE || MODE == MODE_RES_PRMS || MODE == MODE_STORE) && !FP8;
   int nwg = ntiles;
-  if (CAN_SPLIT && ks.full >= 0 && ks.full < ntiles && ks.part && ks.cnt && K % 256 == 0 && K >= 1024)
-    nwg = ks.full + 2 * (ntiles - ks.full);
+  if (CAN_SPLIT && ks.full >= 0 && ks.full < ntiles && ks.part && ks.cnt && ks.lg >= 1 && ks.lg <= KSPLIT_MAX_LG &&
+      K % (128 << ks.lg) == 0 && (K >> ks.lg) >= KSPLIT_MIN_PIECE_K)
+    nwg = ks.full + ((ntiles - ks.full) << ks.lg);
   else
     ks.full = -1;  // nothing to split, or a split this kernel or K cannot take: whole tiles
   dim3 grid(nwg), block(NTHREADS);
@@ -865,10 +878,17 @@ hipError_t launch_clear_tickets(int* cnt, int n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int ksplit_full(int64_t ntiles, int64_t K, int cus) {
-  if (cus <= 0 || ntiles <= 0 || K < 1024 || K % 256) return (int)ntiles;
+int ksplit_plan(int64_t ntiles, int64_t K, int cus, int* lg) {
+  *lg = 0;
+  if (cus <= 0 || ntiles <= 0) return (int)ntiles;
   const int64_t rem = ntiles % cus;
   if (rem == 0 || 4 * rem > cus) return (int)ntiles;
+  if (K % 256 || K / 2 < KSPLIT_MIN_PIECE_K) return (int)ntiles;  // two pieces of at least KSPLIT_MIN_PIECE_K
+  int g = 1;  // more pieces while they stay within half of the CUs and each keeps KSPLIT_TREE_MIN_PIECE_K of K
+  while (g < KSPLIT_MAX_LG && 2 * (rem << (g + 1)) <= cus && K % (128 << (g + 1)) == 0 &&
+         (K >> (g + 1)) >= KSPLIT_TREE_MIN_PIECE_K)
+    ++g;
+  *lg = g;
   return (int)(ntiles - rem);
 }
 

@@ -7,29 +7,39 @@
 namespace coda {
 
 // Split of a GEMM's last, partial wave of output tiles.  When the tile count leaves a last wave that fills at most a
-// quarter of the CUs, the tiles of that wave (the last ones in the tile order) are each computed as two pieces over
-// the two halves of K, so the last wave runs on twice as many CUs: the grid holds `full` whole tiles, then
-// 2 (ntiles - full) pieces.  Each piece stores its fp32 accumulators in its slot of `part`, then takes a ticket
-// from its tile's counter; the piece that draws the second ticket adds the other piece's slot to its own
-// accumulators (fp32 addition is commutative, so the sum does not depend on which piece comes second) and runs the
-// epilogue; the first one exits.  No piece waits for another.  The counters must be zero at launch: the block's
-// first GEMM clears those of its second GEMM (`clear`, `nclear`), and launch_clear_tickets clears the first GEMM's
-// own before it runs.  Both GEMMs of the bf16 blocks (K1 or U1, and K3 or U3) can be split.
+// quarter of the CUs, the tiles of that wave (the last ones in the tile order) are each computed as S = 2^lg pieces
+// over S equal ranges of K, so the last wave runs on S times as many CUs: the grid holds `full` whole tiles, then
+// (ntiles - full) S pieces.  The pieces of a tile meet in a binary tree of S - 1 nodes: at each level a piece stores
+// its fp32 accumulators in its slot of `part`, then takes a ticket from its node's counter; the piece that draws the
+// node's second ticket adds its sibling's slot to its own accumulators (fp32 addition is commutative, so each node's
+// sum does not depend on which of its two pieces comes second, and the tree fixes the order of the rest) and goes
+// on to the next level; the first one exits.  The root's second arrival runs the epilogue.  No piece waits for
+// another.  The counters must be zero at launch: the block's first GEMM clears those of its second GEMM (`clear`,
+// `nclear`), and launch_clear_tickets clears the first GEMM's own before it runs.  Both GEMMs of the bf16 blocks (K1
+// or U1, and K3 or U3) can be split.
 struct KSplit {
   int full = -1;          // whole tiles; negative: no split
-  float* part = nullptr;  // 2 (ntiles - full) slots of KSPLIT_SLOT_FLOATS fp32
-  int* cnt = nullptr;     // ntiles - full tickets
+  int lg = 1;             // S = 2^lg pieces per split tile (1 .. 3)
+  float* part = nullptr;  // (ntiles - full) (2 S - 2) slots of KSPLIT_SLOT_FLOATS fp32: level l's 2^(lg-l) slots
+                          // per tile follow the lower levels'
+  int* cnt = nullptr;     // (ntiles - full) (S - 1) tickets: level l's 2^(lg-l-1) per tile after the lower levels'
   int* clear = nullptr;   // the block's first GEMM: the second GEMM's tickets, zeroed by its workgroup 0
   int nclear = 0;
 };
 constexpr int KSPLIT_SLOT_FLOATS = 512 * 128;  // one workgroup's accumulators (512 lanes x 128)
-// The number of whole tiles of a split for `ntiles` output tiles over K on `cus` CUs; ntiles when no split pays:
-// the last wave fills more than a quarter of the CUs, or the halves of K would be shorter than 512 (or K is not a
-// multiple of 256, the mainloop's K granule times two).  Measured on MI355X (K = 2048, identity epilogue, the
-// block's time): a last wave of 16 or 32 tiles gains 7-10 us, one of 64 about 2 us, one of 96 or 128 loses 2-7 us:
-// the pieces' fp32 slots cross the memory system (256 KiB written per piece, 256 KiB read per tile), and a last
-// wave of whole tiles on part of the chip runs at a higher clock than the full chip does.
-int ksplit_full(int64_t ntiles, int64_t K, int cus);
+constexpr int KSPLIT_MIN_PIECE_K = 512;        // K of one piece at least
+constexpr int KSPLIT_TREE_MIN_PIECE_K = 1024;  // K of one piece at least where a tile has more than two
+constexpr int KSPLIT_MAX_LG = 3;               // at most 8 pieces per tile
+// The split of `ntiles` output tiles over K on `cus` CUs: returns the number of whole tiles (ntiles when no split
+// pays) and sets *lg.  No split where the last wave fills more than a quarter of the CUs or K does not give two pieces
+// of KSPLIT_MIN_PIECE_K (K a multiple of 256); else two pieces, or more (up to 8) while all the pieces stay within half
+// of the CUs and each keeps KSPLIT_TREE_MIN_PIECE_K of K (a multiple of 128).  Measured on MI355X (the block's time):
+// with two pieces, a last wave of 16 or 32 tiles at K = 2048 gains 7-10 us, one of 64 about 2 us, one of 96 or 128
+// loses 2-7 us (the pieces' fp32 slots cross the memory system, 256 KiB written per piece and level, and a last wave
+// of whole tiles on part of the chip runs at a higher clock than the full chip does); more pieces pay where each
+// keeps 1024 of K or more (one tile over K1 = 8192 in eight: 150 -> 57 us; 32 tiles over K1 = 8192 in four rather
+// than two: 123 -> 105 us) and lose below that (32 tiles over K = 2048 in four: 113 -> 120 us).
+int ksplit_plan(int64_t ntiles, int64_t K, int cus, int* lg);
 // Zeroes n tickets (a small kernel on `stream`; graph-capturable, unlike a memset node).
 hipError_t launch_clear_tickets(int* cnt, int n, hipStream_t stream);
 

@@ -191,9 +191,9 @@ def test_fp8_validation(lib, fn):
 
 def test_workspace_split_bytes(lib):
     """The room to split each GEMM's last wave, planned for 256 CUs: none where the tiles fill whole waves, the last
-    wave fills more than a quarter of the CUs or K (D for the second GEMM, K1 for the first) is below 1024; else one
-    int32 ticket per tile of the last wave (256-byte aligned) and two 256 KiB fp32 slots per such tile, the second
-    GEMM's room first.  coda_workspace_bytes includes it."""
+    wave fills more than a quarter of the CUs or K (D for the second GEMM, K1 for the first) is below 1024; else, for
+    S pieces per tile, S - 1 int32 tickets per tile of the last wave (256-byte aligned) and 2 S - 2 fp32 slots of
+    256 KiB per such tile, the second GEMM's room first.  coda_workspace_bytes includes it."""
     al = lambda x: (x + 255) // 256 * 256
     slot = 512 * 128 * 4
     base = lambda M, D, unfused=0: al(D // 256 * M * 4) + al(M * 4) + (2 if unfused else 1) * al(M * D * 2)
@@ -215,8 +215,13 @@ def test_workspace_split_bytes(lib):
     assert f(130, 128, 4352, 256, 0, 0, 0) == al(4) + 2 * slot  # one tile, K = 4352 (halves of 2176)
     # the first GEMM too (its tiles ceil(M/256) x D/256 over K1): 300 rows, K1 = 2048, D = 512 -> 4 tiles split
     assert f(300, 2048, 512, 512, 0, 0, 0) == al(4 * 4) + 8 * slot
-    # 1024 rows of the 1B MLP-out -> QKV block: the second GEMM's 48 tiles, then the first GEMM's 32 (K1 = 8192)
-    assert f(1024, 8192, 2048, 3072, 0, 0, 0) == al(48 * 4) + 96 * slot + al(32 * 4) + 64 * slot
+    # more than two pieces (a tree of S - 1 tickets and 2 S - 2 slots per tile) where all of them stay within half of
+    # the CUs and each keeps 1024 of K: 1024 rows of the 1B MLP-out -> QKV block: the second GEMM's 48 tiles in two
+    # (K = 2048), then the first GEMM's 32 tiles in four (K1 = 8192; eight would be 256 pieces)
+    assert f(1024, 8192, 2048, 3072, 0, 0, 0) == al(48 * 4) + 96 * slot + al(32 * 3 * 4) + 32 * 6 * slot
+    # one tile over K = 4096: four pieces of 1024; over K1 = 8192: eight of 1024
+    assert f(130, 256, 4096, 512, 0, 0, 0) == al(2 * 3 * 4) + 2 * 6 * slot
+    assert f(64, 8192, 256, 256, 0, 0, 0) == al(7 * 4) + 14 * slot
     assert f(0, 256, 2048, 3072, 0, 0, 0) == 0                  # invalid dimensions
     assert f(8192, 256, 2048, 3000, 0, 0, 0) == 0
 

@@ -55,36 +55,45 @@ def _need_gpu():
         pytest.skip("the split room is planned for 256 CUs")
 
 
-def _rule(tiles: int, K: int) -> int:
-    """The split rule written out: the tiles of a last wave that fills at most a quarter of the CUs, for K >= 1024 (a
-    multiple of 256)."""
+def _plan(tiles: int, K: int):
+    """The split rule written out: (split tiles, log2 of the pieces per tile).  A last wave that fills at most a
+    quarter of the CUs splits in two where K gives two pieces of at least 512 (K a multiple of 256); in more, up to 8,
+    while all pieces stay within half of the CUs and each keeps at least 1024 of K (a multiple of 128)."""
     rem = tiles % PLAN_CUS
-    return rem if (K >= 1024 and K % 256 == 0 and 0 < rem and 4 * rem <= PLAN_CUS) else 0
+    if rem == 0 or 4 * rem > PLAN_CUS or K % 256 or K // 2 < 512:
+        return 0, 0
+    g = 1
+    while g < 3 and 2 * (rem << (g + 1)) <= PLAN_CUS and K % (128 << (g + 1)) == 0 and (K >> (g + 1)) >= 1024:
+        g += 1
+    return rem, g
 
 
-def _tails(wl: Workload):
-    """(split tiles of the first GEMM, over K1; split tiles of the second, over D)."""
+def _plans(wl: Workload):
+    """(the first GEMM's plan, over K1; the second's, over D)."""
     rt = (wl.M + 255) // 256
-    return _rule(rt * (wl.D // 256), wl.K1), _rule(rt * (wl.N2 // 256), wl.D)
+    return _plan(rt * (wl.D // 256), wl.K1), _plan(rt * (wl.N2 // 256), wl.D)
 
 
 def _al(x: int) -> int:
     return (x + 255) // 256 * 256
 
 
-def _room(t: int) -> int:
-    return _al(4 * t) + 2 * t * SLOT_BYTES if t else 0
+def _room(plan) -> int:
+    t, g = plan
+    S = 1 << g
+    return _al(4 * t * (S - 1)) + t * (2 * S - 2) * SLOT_BYTES if t else 0
 
 
 def _tickets(ws: torch.Tensor, wl: Workload, unfused: bool = False):
-    """The tickets after a call: (the first GEMM's, the second GEMM's).  The split room follows the workspace's base
-    part: the second GEMM's tickets and slots, then the first GEMM's."""
+    """The tickets after a call: (the first GEMM's, the second GEMM's), S - 1 per split tile.  The split room follows
+    the workspace's base part: the second GEMM's tickets and slots, then the first GEMM's."""
     total = cb.coda_workspace_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
     base = total - cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused))
-    t1, t2 = _tails(wl)
-    g2 = ws[base: base + 4 * t2].view(torch.int32).cpu()
-    o1 = base + _room(t2)
-    g1 = ws[o1: o1 + 4 * t1].view(torch.int32).cpu()
+    p1, p2 = _plans(wl)
+    n = lambda p: p[0] * ((1 << p[1]) - 1)
+    g2 = ws[base: base + 4 * n(p2)].view(torch.int32).cpu()
+    o1 = base + _room(p2)
+    g1 = ws[o1: o1 + 4 * n(p1)].view(torch.int32).cpu()
     return g1, g2
 
 
@@ -115,21 +124,27 @@ SMALL = [
     Workload("split_first_gemm", M=300, K1=2048, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=67),
     # both GEMMs split: 8 tiles over K1 = 1024, 4 tiles over D = 1024
     Workload("split_both_gemms", M=260, K1=1024, D=1024, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=68),
+    # the second GEMM's 2 tiles in 4 pieces each (K = D = 4096, the tree's two levels)
+    Workload("split_four_pieces", M=130, K1=256, D=4096, N2=512, epi=EPI_IDENTITY, eps=1e-5, seed=69),
+    # the first GEMM's one tile in 8 pieces (K1 = 8192, three levels), on 64 rows (the small-row form)
+    Workload("split_eight_pieces", M=64, K1=8192, D=256, N2=256, epi=EPI_IDENTITY, eps=1e-5, seed=70),
 ]
 
 
 def test_plan_matches_the_written_rule():
     for wl in SMALL + [QKV_2KV, QKV_ROWS1024, WORKLOADS["1b_mlp_out_qkv"], WORKLOADS["1b_attn_out_mlp_in"],
                        WORKLOADS["tiny"]]:
-        t1, t2 = _tails(wl)
+        p1, p2 = _plans(wl)
         for unfused in (False, True):
             assert cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused)) == \
-                _room(t1) + _room(t2), (wl.name, unfused)
-    assert _tails(WORKLOADS["1b_mlp_out_qkv"]) == (0, 0)   # 256 tiles; a last wave of 128 tiles: over a quarter
-    assert _tails(WORKLOADS["1b_attn_out_mlp_in"]) == (0, 0)
-    assert _tails(QKV_2KV) == (0, 32)
-    assert _tails(QKV_ROWS1024) == (32, 48)
-    assert [_tails(w) for w in SMALL] == [(0, 8), (0, 2), (0, 2), (4, 0), (8, 4)]
+                _room(p1) + _room(p2), (wl.name, unfused)
+    none = ((0, 0), (0, 0))
+    assert _plans(WORKLOADS["1b_mlp_out_qkv"]) == none   # 256 tiles; a last wave of 128 tiles: over a quarter
+    assert _plans(WORKLOADS["1b_attn_out_mlp_in"]) == none
+    assert _plans(QKV_2KV) == ((0, 0), (32, 1))
+    assert _plans(QKV_ROWS1024) == ((32, 2), (48, 1))      # the first GEMM in 4 pieces of 2048
+    assert [_plans(w) for w in SMALL] == [((0, 0), (8, 1)), ((0, 0), (2, 1)), ((0, 0), (2, 1)), ((4, 1), (0, 0)),
+                                          ((8, 1), (4, 1)), ((0, 0), (2, 2)), ((1, 3), (0, 0))]
 
 
 @pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
@@ -138,7 +153,7 @@ def test_split_small_against_oracle(wl, unfused):
     _say(f"[gpu] split {'unfused' if unfused else 'fused'} {wl}")
     inp = make_inputs(wl)
     d = DeviceInputs(inp)
-    t1, t2 = _tails(wl)
+    (t1, _), (t2, _) = _plans(wl)
     assert t1 + t2 > 0
     h, y, r, ws = _run(d, unfused)
     assert _both_tickets_taken(ws, wl, unfused), "a split tile did not take both tickets"
@@ -180,7 +195,7 @@ def test_split_tail_after_a_whole_wave():
     against the oracle, every row against the whole-tile run."""
     wl = Workload("split_tail", M=2048, K1=256, D=1024, N2=8448, epi=EPI_IDENTITY, eps=1e-5, seed=64)
     _say(f"[gpu] split tail {wl}")
-    assert _tails(wl) == (0, 8)
+    assert _plans(wl) == ((0, 0), (8, 1))
     inp = make_inputs(wl)
     d = DeviceInputs(inp)
     h, y, r, ws = _run(d)

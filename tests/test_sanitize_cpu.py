@@ -46,10 +46,11 @@ def _stub_source(fatbin_symbol: str) -> str:
         params = re.sub(r"\s*=\s*[^,]+", "", params)  # default arguments belong to the declaration only
         if name == "fold_supported":
             body = "return D / 256 <= 16;"
-        elif name == "ksplit_full":  # the split rule of the second product's last wave
-            body = ("if (cus <= 0 || ntiles <= 0 || K < 1024 || K % 256) return (int)ntiles; "
-                    "const int64_t rem = ntiles % cus; "
-                    "return (rem == 0 || 4 * rem > cus) ? (int)ntiles : (int)(ntiles - rem);")
+        elif name == "ksplit_plan":  # the split rule of a GEMM's last wave
+            body = ("*lg = 0; if (cus <= 0 || ntiles <= 0) return (int)ntiles; "
+                    "const int64_t rem = ntiles % cus; if (rem == 0 || 4 * rem > cus) return (int)ntiles; "
+                    "int g = 0; while (g < 3 && (rem << (g + 1)) <= cus && K % (128 << (g + 1)) == 0 && "
+                    "(K >> (g + 1)) >= 512) ++g; if (g == 0) return (int)ntiles; *lg = g; return (int)(ntiles - rem);")
         elif name == "gemm_ksplit":  # the split rule of the weight-gradient products
             body = ("const int tiles = ((M + 255) / 256) * (N / 256); int s = 1; "
                     "while (s < 8 && tiles * s < 256 && K % (128 * s * 2) == 0) s *= 2; return s;")
