@@ -16,7 +16,8 @@ is computed as two halves of K whose fp32 sums are added before the epilogue, in
   1024 rows (both GEMMs' tiles split): tickets, run-to-run identity, a row in every row tile against the oracle and
   every row against the whole-tile run; the 1B MLP-out -> QKV shape itself (384 tiles, a last wave of 128) is not
   split;
-- the block with the rotary embedding and the forward that keeps z take the same split.
+- the block with the rotary embedding and the forward that keeps z take the same split;
+- seeded random shapes that split either GEMM or both, into 2, 4 and 8 pieces, every element against the oracle.
 """
 import sys
 
@@ -275,3 +276,52 @@ def test_split_save_z():
     # SwiGLU tiles hold 128 gate and the matching 128 up columns, identity tiles 256 contiguous columns: the tile
     # grid is the same, the accumulation per column too, so z is the identity block's y bit for bit
     assert torch.equal(z.view(torch.int16), z_plain.view(torch.int16))
+
+
+def _split_shapes(n: int = 10, seed: int = 4096):
+    """n seeded shapes whose first or second GEMM (or both) splits, in 2, 4 or 8 pieces, at most about 0.5 G
+    multiply-adds each (the oracle's fp64 cost)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        M = int(rng.integers(1, 600))
+        if len(out) % 3 == 2:  # a long first product over a narrow D: eight pieces where its tiles are few
+            K1, D = 8192, 256 * int(rng.choice([1, 2]))
+        else:
+            K1 = int(rng.choice([256, 1024, 2048, 4096, 8192]))
+            D = 256 * int(rng.choice([1, 2, 4, 8, 16]))
+        N2 = 256 * int(rng.integers(1, 5))
+        epi = int(rng.integers(0, 2))
+        wl = Workload(f"split_rand{len(out)}_M{M}_K{K1}_D{D}_N{N2}_{'swiglu' if epi else 'id'}", M=M, K1=K1, D=D,
+                      N2=N2, epi=EPI_SWIGLU if epi else EPI_IDENTITY, eps=1e-5, seed=300 + len(out))
+        (t1, _), (t2, _) = _plans(wl)
+        if t1 + t2 == 0 or M * (K1 * D + D * N2) > 5e8:
+            continue
+        out.append(wl)
+    return out
+
+
+SPLIT_RANDOM = _split_shapes()
+
+
+def test_split_random_shapes_cover_every_piece_count():
+    lgs = {g for wl in SPLIT_RANDOM for (t, g) in _plans(wl) if t}
+    assert lgs == {1, 2, 3}, lgs
+
+
+@pytest.mark.parametrize("wl", SPLIT_RANDOM, ids=[w.name for w in SPLIT_RANDOM])
+def test_split_random_shape(wl):
+    """Fused and unfused, every element against the oracle, both GEMMs' tickets, and the whole-tile run."""
+    _say(f"[gpu] split random shape {wl} plans {_plans(wl)}")
+    inp = make_inputs(wl)
+    d = DeviceInputs(inp)
+    for unfused in (False, True):
+        h, y, r, ws = _run(d, unfused)
+        assert _both_tickets_taken(ws, wl, unfused)
+        oh, orr, oy = oracle_rows(inp, form="unfused" if unfused else "fused")
+        check_h(f64(h), oh)
+        check_y(f64(y), oy)
+        np.testing.assert_allclose(f64(r), orr, rtol=2e-3 if unfused else 2e-5)
+        _, y0, _, _ = _run(d, unfused, split=False)
+        g, w = f64(y), f64(y0)
+        assert normwise(g, w) <= CLOSE_NORMWISE and mae_rel(g, w) <= CLOSE_MAE_REL
