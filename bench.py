@@ -606,6 +606,37 @@ def time_tiny(dev, torch, cb) -> dict:
             "graph_blocks_per_replay": per_graph}
 
 
+def time_row_shard(dev, n_ev: int, torch, cb) -> dict:
+    """One GPU's share of the two bf16 1B blocks with their rows sharded over eight GPUs (1024 of 8192 rows; no
+    communication, the rows are independent): the fused block with the split of the GEMMs' last waves (the default
+    workspace), the same block on whole tiles (a workspace without the split room), and the unfused baseline with its
+    split; milliseconds per call from HIP events after EXTRAS_SETTLE_MS of untimed calls."""
+    from gemm_epilogue_fusion_amd.inputs import WORKLOADS, make_inputs
+
+    out = {}
+    for name in ("1b_attn_out_mlp_in", "1b_mlp_out_qkv"):
+        wl = WORKLOADS[name].with_(M=1024)
+        inp = make_inputs(wl)
+        X, W1, R, g, W2 = (t.to(dev) for t in (inp.X, inp.W1, inp.R, inp.gamma, inp.W2))
+        h = torch.empty(wl.M, wl.D, dtype=torch.bfloat16, device=dev)
+        y = torch.empty(wl.M, wl.n_out, dtype=torch.bfloat16, device=dev)
+        ws = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev)
+        ws_whole = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, device=dev, split=False)
+        wsu = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=1, device=dev)
+        split = lambda: cb.coda_block_fwd(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws)
+        whole = lambda: cb.coda_block_fwd(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws_whole)
+        unf = lambda: cb.coda_block_unfused(X, W1, R, g, W2, wl.eps, wl.epi, h, y, wsu)
+        ms = {k: time_loop(fn, n_ev, torch) for k, fn in (("split", split), ("whole_tiles", whole), ("unfused", unf))}
+        out[name + "_1024_rows"] = {
+            "M": wl.M, "K1": wl.K1, "D": wl.D, "N2": wl.N2, "split_room_bytes": ws.numel() - ws_whole.numel(),
+            "fused_ms": round(ms["split"], 4), "fused_whole_tiles_ms": round(ms["whole_tiles"], 4),
+            "unfused_ms": round(ms["unfused"], 4),
+            "tflops": round(wl.flops / (ms["split"] * 1e-3) / 1e12, 2),
+            "speedup_split_vs_whole_tiles": round(ms["whole_tiles"] / ms["split"], 4)}
+        del ws, ws_whole, wsu
+    return out
+
+
 def time_rope(dev, n_ev: int, warmup: int, torch, cb) -> dict:
     """The QKV block with RoPE on the q and k heads (32 + 8 heads of 64 of the 48), seq_len 2048, base 5e5:
     fused into GEMM2's epilogue, against the plain block alone and the plain block + a separate pass."""
@@ -745,6 +776,8 @@ def main() -> int:
     ap.add_argument("--no-ce", action="store_true", help="skip the cross-entropy timing")
     ap.add_argument("--no-swiglu", action="store_true", help="skip the SwiGLU forward-with-z / backward timing")
     ap.add_argument("--no-tiny", action="store_true", help="skip the launch-bound tiny block (eager and graph)")
+    ap.add_argument("--no-shard", action="store_true",
+                    help="skip the 1024-row blocks (one GPU's share of the rows sharded over eight)")
     ap.add_argument("--settle-ms", type=float, default=500.0,
                     help="untimed calls for at least this many ms before the warm-up calls of each timed window: the "
                          "device's clock settles under sustained load only after some milliseconds (0: none)")
@@ -965,6 +998,8 @@ def main() -> int:
         extra("swiglu", lambda: time_swiglu(wl, X, W1, R, g, W2, dev, n_ev, args.warmup, torch, cb))
     if not args.no_tiny:
         extra("tiny", lambda: time_tiny(dev, torch, cb))
+    if not args.no_shard:
+        extra("row_shard", lambda: time_row_shard(dev, n_ev, torch, cb))
     extra("env", lambda: environment(torch))
     if not args.no_clock:
         extra("clock", lambda: clock_under_load(step, torch))
