@@ -882,7 +882,9 @@ int ksplit_plan(int64_t ntiles, int64_t K, int cus, int* lg) {
   *lg = 0;
   if (cus <= 0 || ntiles <= 0) return (int)ntiles;
   const int64_t rem = ntiles % cus;
-  if (rem == 0 || 4 * rem > cus) return (int)ntiles;
+  if (rem == 0) return (int)ntiles;
+  // a last wave of at most a quarter of the CUs, or of at most three eighths where K >= KSPLIT_LONG_K
+  if (4 * rem > cus && !(8 * rem <= 3 * cus && K >= KSPLIT_LONG_K)) return (int)ntiles;
   if (K % 256 || K / 2 < KSPLIT_MIN_PIECE_K) return (int)ntiles;  // two pieces of at least KSPLIT_MIN_PIECE_K
   int g = 1;  // more pieces while they stay within half of the CUs and each keeps KSPLIT_TREE_MIN_PIECE_K of K
   while (g < KSPLIT_MAX_LG && 2 * (rem << (g + 1)) <= cus && K % (128 << (g + 1)) == 0 &&

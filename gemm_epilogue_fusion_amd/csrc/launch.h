@@ -30,13 +30,16 @@ constexpr int KSPLIT_SLOT_FLOATS = 512 * 128;  // one workgroup's accumulators (
 constexpr int KSPLIT_MIN_PIECE_K = 512;        // K of one piece at least
 constexpr int KSPLIT_TREE_MIN_PIECE_K = 1024;  // K of one piece at least where a tile has more than two
 constexpr int KSPLIT_MAX_LG = 3;               // at most 8 pieces per tile
+constexpr int KSPLIT_LONG_K = 4096;            // K from which a last wave of up to three eighths of the CUs splits
 // The split of `ntiles` output tiles over K on `cus` CUs: returns the number of whole tiles (ntiles when no split
-// pays) and sets *lg.  No split where the last wave fills more than a quarter of the CUs or K does not give two pieces
-// of KSPLIT_MIN_PIECE_K (K a multiple of 256); else two pieces, or more (up to 8) while all the pieces stay within half
-// of the CUs and each keeps KSPLIT_TREE_MIN_PIECE_K of K (a multiple of 128).  Measured on MI355X (the block's time):
-// with two pieces, a last wave of 16 or 32 tiles at K = 2048 gains 7-10 us, one of 64 about 2 us, one of 96 or 128
-// loses 2-7 us (the pieces' fp32 slots cross the memory system, 256 KiB written per piece and level, and a last wave
-// of whole tiles on part of the chip runs at a higher clock than the full chip does); more pieces pay where each
+// pays) and sets *lg.  A last wave splits where it fills at most a quarter of the CUs, or at most three eighths where
+// K >= KSPLIT_LONG_K, and K gives two pieces of KSPLIT_MIN_PIECE_K (K a multiple of 256): in two pieces, or more (up
+// to 8) while all the pieces stay within half of the CUs and each keeps KSPLIT_TREE_MIN_PIECE_K of K (a multiple of
+// 128).  Measured on MI355X (the block's time): with two pieces, a last wave of 16 or 32 tiles at K = 2048 gains
+// 7-10 us, one of 64 about 2 us, one of 96 or 128 loses 2-7 us (the pieces' fp32 slots cross the memory system,
+// 256 KiB written per piece and level, and a last wave of whole tiles on part of the chip runs at a higher clock
+// than the full chip does); over longer K the savings grow and the exchange does not: last waves of 80 and 96 tiles
+// gain 8-15 us at K = 4096 and 32-53 us at K = 8192, one of 128 still loses up to 7 us.  More pieces pay where each
 // keeps 1024 of K or more (one tile over K1 = 8192 in eight: 150 -> 57 us; 32 tiles over K1 = 8192 in four rather
 // than two: 123 -> 105 us) and lose below that (32 tiles over K = 2048 in four: 113 -> 120 us).
 int ksplit_plan(int64_t ntiles, int64_t K, int cus, int* lg);

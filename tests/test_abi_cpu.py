@@ -222,6 +222,12 @@ def test_workspace_split_bytes(lib):
     # one tile over K = 4096: four pieces of 1024; over K1 = 8192: eight of 1024
     assert f(130, 256, 4096, 512, 0, 0, 0) == al(2 * 3 * 4) + 2 * 6 * slot
     assert f(64, 8192, 256, 256, 0, 0, 0) == al(7 * 4) + 14 * slot
+    # over K >= 4096 a last wave of up to three eighths of the CUs splits too: 3072 rows, D = 2048 -> 96 tiles of the
+    # first GEMM over K1 = 4096 or 8192 (in two: four would pass half of the CUs), none over K1 = 2048
+    assert f(3072, 4096, 2048, 2048, 0, 0, 0) == al(96 * 4) + 192 * slot
+    assert f(3072, 8192, 2048, 2048, 0, 0, 0) == al(96 * 4) + 192 * slot
+    assert f(3072, 2048, 2048, 2048, 0, 0, 0) == 0
+    assert f(256 * 104, 256, 4096, 256, 0, 0, 0) == 0           # 104 tiles: over three eighths
     assert f(0, 256, 2048, 3072, 0, 0, 0) == 0                  # invalid dimensions
     assert f(8192, 256, 2048, 3000, 0, 0, 0) == 0
 

@@ -12,8 +12,8 @@ is computed as two halves of K whose fp32 sums are added before the epilogue, in
   fp32 summation-order difference, h and r equal bit for bit where the first GEMM is not split;
 - outputs bit-identical run to run, whichever half finishes second;
 - full size: a last wave of 32 tiles in the second GEMM (a QKV projection with 2 key-value heads of 64 after the 1B
-  hidden size: 8192 rows, D = 2048, 2048 + 2 x 128 output columns, 288 tiles), and the 1B MLP-out -> QKV block on
-  1024 rows (both GEMMs' tiles split): tickets, run-to-run identity, a row in every row tile against the oracle and
+  hidden size: 8192 rows, D = 2048, 2048 + 2 x 128 output columns, 288 tiles), the 1B MLP-out -> QKV block on
+  1024 rows (both GEMMs' tiles split) and 3072 rows over K1 = 4096 (a last wave of 96 tiles): tickets, run-to-run identity, a row in every row tile against the oracle and
   every row against the whole-tile run; the 1B MLP-out -> QKV shape itself (384 tiles, a last wave of 128) is not
   split;
 - the block with the rotary embedding and the forward that keeps z take the same split;
@@ -58,10 +58,11 @@ def _need_gpu():
 
 def _plan(tiles: int, K: int):
     """The split rule written out: (split tiles, log2 of the pieces per tile).  A last wave that fills at most a
-    quarter of the CUs splits in two where K gives two pieces of at least 512 (K a multiple of 256); in more, up to 8,
-    while all pieces stay within half of the CUs and each keeps at least 1024 of K (a multiple of 128)."""
+    quarter of the CUs (three eighths where K >= 4096) splits in two where K gives two pieces of at least 512 (K a
+    multiple of 256); in more, up to 8, while all pieces stay within half of the CUs and each keeps at least 1024 of
+    K (a multiple of 128)."""
     rem = tiles % PLAN_CUS
-    if rem == 0 or 4 * rem > PLAN_CUS or K % 256 or K // 2 < 512:
+    if rem == 0 or (4 * rem > PLAN_CUS and not (8 * rem <= 3 * PLAN_CUS and K >= 4096)) or K % 256 or K // 2 < 512:
         return 0, 0
     g = 1
     while g < 3 and 2 * (rem << (g + 1)) <= PLAN_CUS and K % (128 << (g + 1)) == 0 and (K >> (g + 1)) >= 1024:
@@ -133,8 +134,7 @@ SMALL = [
 
 
 def test_plan_matches_the_written_rule():
-    for wl in SMALL + [QKV_2KV, QKV_ROWS1024, WORKLOADS["1b_mlp_out_qkv"], WORKLOADS["1b_attn_out_mlp_in"],
-                       WORKLOADS["tiny"]]:
+    for wl in SMALL + FULL + [WORKLOADS["1b_mlp_out_qkv"], WORKLOADS["1b_attn_out_mlp_in"], WORKLOADS["tiny"]]:
         p1, p2 = _plans(wl)
         for unfused in (False, True):
             assert cb.coda_workspace_split_bytes(wl.M, wl.K1, wl.D, wl.N2, wl.epi, 0, int(unfused)) == \
@@ -144,6 +144,7 @@ def test_plan_matches_the_written_rule():
     assert _plans(WORKLOADS["1b_attn_out_mlp_in"]) == none
     assert _plans(QKV_2KV) == ((0, 0), (32, 1))
     assert _plans(QKV_ROWS1024) == ((32, 2), (48, 1))      # the first GEMM in 4 pieces of 2048
+    assert _plans(ROWS3072) == ((96, 1), (12, 1))
     assert [_plans(w) for w in SMALL] == [((0, 0), (8, 1)), ((0, 0), (2, 1)), ((0, 0), (2, 1)), ((4, 1), (0, 0)),
                                           ((8, 1), (4, 1)), ((0, 0), (2, 2)), ((1, 3), (0, 0))]
 
@@ -212,9 +213,15 @@ def test_split_tail_after_a_whole_wave():
     assert normwise(yg, w) <= CLOSE_NORMWISE and mae_rel(yg, w) <= CLOSE_MAE_REL
 
 
+# 3072 rows over K1 = 4096: the first GEMM's 96 tiles, three eighths of the CUs, split in two (K >= 4096); the
+# second GEMM's 12 tiles in two
+ROWS3072 = Workload("rows3072_k1_4096", M=3072, K1=4096, D=2048, N2=256, epi=EPI_IDENTITY, eps=1e-5, seed=71)
+FULL = [QKV_2KV, QKV_ROWS1024, ROWS3072]
+
+
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("unfused", [False, True], ids=["fused", "unfused"])
-@pytest.mark.parametrize("wl", [QKV_2KV, QKV_ROWS1024], ids=[QKV_2KV.name, QKV_ROWS1024.name])
+@pytest.mark.parametrize("wl", FULL, ids=[w.name for w in FULL])
 def test_split_full_size(wl, unfused):
     _say(f"[gpu] split full size {'unfused' if unfused else 'fused'} {wl}")
     inp = make_inputs(wl)
