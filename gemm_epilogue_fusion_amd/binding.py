@@ -150,8 +150,8 @@ def coda_workspace_split_bytes(M: int, K1: int, D: int, N2: int, epi_kind: int, 
 
 def alloc_workspace(M: int, K1: int, D: int, N2: int, epi_kind: int, unfused: int = 0, device="cuda", fp8: int = 0,
                     split: bool = True):
-    """The workspace of a block entry point; split=False leaves out the room for splitting the second product's
-    last wave (the block then runs that wave as whole tiles)."""
+    """The workspace of a block entry point; split=False leaves out the room for splitting the products' last
+    waves (the block then runs them as whole tiles)."""
     n = coda_workspace_bytes(M, K1, D, N2, epi_kind, fp8, unfused)
     if n == 0:
         raise ValueError("no workspace size for these dimensions")

@@ -168,7 +168,7 @@ size_t carve(void* ws, int64_t M, int64_t D, int fp8, int unfused, Workspace* w)
 
 size_t ws_bytes(int64_t M, int64_t D, int fp8, int unfused) { return carve(nullptr, M, D, fp8, unfused, nullptr); }
 
-// After those bytes the bf16 blocks keep the splits of their GEMMs' last waves of tiles (coda::KSplit): for the
+// After those bytes the blocks keep the splits of their GEMMs' last waves of tiles (coda::KSplit): for the
 // second GEMM, then for the first, the tickets (align256(tail * 4) bytes) and two accumulator slots per split tile.
 // The size is planned for 256 CUs (MI355X); coda_workspace_bytes includes it, and a block splits only where the
 // workspace it is given has that room (with less, from the base size on, its GEMMs run whole tiles).
@@ -178,17 +178,17 @@ int64_t gemm_tiles(int64_t M, int64_t N) { return (M + 255) / 256 * (N / 256); }
 
 // One GEMM's split room for `ntiles` tiles over K on `cus` CUs (0: no split): per split tile S - 1 tickets and
 // 2 S - 2 slots (the tree of coda::KSplit).
-size_t split_bytes_one(int64_t ntiles, int64_t K, int cus) {
+size_t split_bytes_one(int64_t ntiles, int64_t K, int cus, int fp8) {
   int lg = 0;
-  const int64_t tail = ntiles - coda::ksplit_plan(ntiles, K, cus, &lg);
+  const int64_t tail = ntiles - coda::ksplit_plan(ntiles, K, cus, fp8, &lg);
   if (tail <= 0) return 0;
   const int64_t S = (int64_t)1 << lg;
   return align256((size_t)(tail * (S - 1)) * 4) + (size_t)(tail * (2 * S - 2)) * coda::KSPLIT_SLOT_FLOATS * 4;
 }
 
 size_t ws_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int fp8, int cus) {
-  if (fp8 || M < 1 || D < 256 || N2 < 256) return 0;
-  return split_bytes_one(gemm_tiles(M, N2), D, cus) + split_bytes_one(gemm_tiles(M, D), K1, cus);
+  if (M < 1 || D < 256 || N2 < 256) return 0;
+  return split_bytes_one(gemm_tiles(M, N2), D, cus, fp8) + split_bytes_one(gemm_tiles(M, D), K1, cus, fp8);
 }
 
 // The split room a block validated with `workspace_bytes` may use: the planned region when it fits, else none.
@@ -215,10 +215,10 @@ int device_cus() {
 }
 
 // One GEMM's split laid out from `at` (which then moves past it); no split where the plan has none.
-coda::KSplit split_one(char*& at, int64_t ntiles, int64_t K, int cus, int* tickets) {
+coda::KSplit split_one(char*& at, int64_t ntiles, int64_t K, int cus, int fp8, int* tickets) {
   coda::KSplit ks;
   int lg = 0;
-  const int64_t full = coda::ksplit_plan(ntiles, K, cus, &lg);
+  const int64_t full = coda::ksplit_plan(ntiles, K, cus, fp8, &lg);
   *tickets = 0;
   if (full >= ntiles) return ks;
   const int64_t tail = ntiles - full, S = (int64_t)1 << lg;
@@ -226,7 +226,7 @@ coda::KSplit split_one(char*& at, int64_t ntiles, int64_t K, int cus, int* ticke
   ks.lg = lg;
   ks.cnt = (int*)at;
   ks.part = (float*)(at + align256((size_t)(tail * (S - 1)) * 4));
-  at += split_bytes_one(ntiles, K, cus);
+  at += split_bytes_one(ntiles, K, cus, fp8);
   *tickets = (int)(tail * (S - 1));
   return ks;
 }
@@ -238,16 +238,16 @@ struct SplitPlan {
   int tickets1 = 0;  // the first GEMM's tickets, cleared before it runs
 };
 
-SplitPlan split_plan(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int unfused, size_t room) {
+SplitPlan split_plan(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int fp8, int unfused, size_t room) {
   SplitPlan p;
   if (!room) return p;
   const int cus = device_cus();
-  const size_t need = ws_split_bytes(M, K1, D, N2, 0, cus);
+  const size_t need = ws_split_bytes(M, K1, D, N2, fp8, cus);
   if (!need || need > room) return p;
-  char* at = (char*)ws + ws_bytes(M, D, 0, unfused);
+  char* at = (char*)ws + ws_bytes(M, D, fp8, unfused);
   int tickets2 = 0;
-  p.g2 = split_one(at, gemm_tiles(M, N2), D, cus, &tickets2);
-  p.g1 = split_one(at, gemm_tiles(M, D), K1, cus, &p.tickets1);
+  p.g2 = split_one(at, gemm_tiles(M, N2), D, cus, fp8, &tickets2);
+  p.g1 = split_one(at, gemm_tiles(M, D), K1, cus, fp8, &p.tickets1);
   if (p.g2.full >= 0) {
     p.g1.clear = p.g2.cnt;
     p.g1.nclear = tickets2;
@@ -375,7 +375,7 @@ int launch_block_fwd(const void* X, const void* W1, const void* R, const float* 
   int s;
   Workspace w;
   carve(workspace, M, D, 0, 0, &w);
-  const SplitPlan sp = split_plan(workspace, M, K1, D, N2, 0, ws_split_room(M, K1, D, N2, 0, 0, workspace_bytes));
+  const SplitPlan sp = split_plan(workspace, M, K1, D, N2, 0, 0, ws_split_room(M, K1, D, N2, 0, 0, workspace_bytes));
   if (sp.tickets1 && (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
     return s;
   if ((s = hip_check(coda::launch_gemm1_res_prms((const uint16_t*)X, (const uint16_t*)W1, (const uint16_t*)R, gamma,
@@ -455,7 +455,7 @@ const char* coda_last_error(void) { return g_last_error.c_str(); }
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused) {
   (void)epi_kind;
   if (M < 1 || D < 256 || M > kMaxDim || D > kMaxDim || fp8 < 0 || fp8 > 2 || (fp8 == 2 && unfused)) return 0;
-  // the split room of the bf16 blocks (N2 outside the shape rules: none)
+  // the split room (N2 outside the shape rules: none)
   const size_t split = (N2 >= 256 && N2 <= kMaxDim && N2 % 256 == 0 && K1 >= 1 && K1 <= kMaxDim)
                            ? ws_split_bytes(M, K1, D, N2, fp8, kPlanCus)
                            : 0;
@@ -518,7 +518,8 @@ int coda_block_fwd_rope(const void* X, const void* W1, const void* R, const floa
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 0, 0, &w);
-    const SplitPlan sp = split_plan(workspace, M, K1, D, N2, 0, ws_split_room(M, K1, D, N2, 0, 0, workspace_bytes));
+    const SplitPlan sp =
+        split_plan(workspace, M, K1, D, N2, 0, 0, ws_split_room(M, K1, D, N2, 0, 0, workspace_bytes));
     if (sp.tickets1 &&
         (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
       return s;
@@ -573,7 +574,8 @@ int coda_block_unfused(const void* X, const void* W1, const void* R, const float
     Workspace w;
     carve(workspace, M, D, 0, 1, &w);
     // the same splits of the GEMMs' last waves as the fused block (the same kernel family on the same tiles)
-    const SplitPlan sp = split_plan(workspace, M, K1, D, N2, 1, ws_split_room(M, K1, D, N2, 0, 1, workspace_bytes));
+    const SplitPlan sp =
+        split_plan(workspace, M, K1, D, N2, 0, 1, ws_split_room(M, K1, D, N2, 0, 1, workspace_bytes));
     if (sp.tickets1 &&
         (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
       return s;
@@ -605,9 +607,14 @@ int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const f
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 1, 0, &w);
+    const SplitPlan sp =
+        split_plan(workspace, M, K1, D, N2, 1, 0, ws_split_room(M, K1, D, N2, 1, 0, workspace_bytes));
+    if (sp.tickets1 &&
+        (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
+      return s;
     if ((s = hip_check(coda::launch_gemm1_res_prms_fp8((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1,
                                                        (const uint16_t*)R, (uint16_t*)out_h, w.part, (int)M,
-                                                       (int)K1, (int)D, st),
+                                                       (int)K1, (int)D, st, sp.g1),
                        "fp8 gemm1_res_prms launch")))
       return s;
     if ((s = hip_check(coda::launch_prms_reduce_quant(w.part, (int)(D / 256), (int)M, (int)D, eps,
@@ -616,7 +623,7 @@ int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const f
                        "prms_reduce_quant launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale_fp8(w.q, (const uint8_t*)W2q, w.rs2, sw2, epi_kind == CODA_EPI_SWIGLU,
-                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, kPanels),
+                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, kPanels, sp.g2),
                      "fp8 gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -634,9 +641,14 @@ int coda_block_fwd_fp8_mx(const void* Xq, const float* sx, const void* W1q, cons
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 2, 0, &w);
+    const SplitPlan sp =
+        split_plan(workspace, M, K1, D, N2, 2, 0, ws_split_room(M, K1, D, N2, 2, 0, workspace_bytes));
+    if (sp.tickets1 &&
+        (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
+      return s;
     if ((s = hip_check(coda::launch_gemm1_res_prms_fp8_mx((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1,
                                                           (const uint16_t*)R, gamma, (uint16_t*)out_h, w.q, w.mxs,
-                                                          w.part, (int)M, (int)K1, (int)D, st, kPanels),
+                                                          w.part, (int)M, (int)K1, (int)D, st, kPanels, sp.g1),
                        "fp8 block-scaled gemm1_res_prms launch")))
       return s;
     const bool fold = coda::fold_supported((int)D);
@@ -646,7 +658,7 @@ int coda_block_fwd_fp8_mx(const void* Xq, const float* sx, const void* W1q, cons
     return hip_check(coda::launch_gemm2_rowscale_fp8_mx(w.q, w.mxs, (const uint8_t*)W2q, sw2, w.r,
                                                         fold ? w.part : nullptr, eps, w.r,
                                                         epi_kind == CODA_EPI_SWIGLU, (uint16_t*)out_y, (int)M,
-                                                        (int)D, (int)N2, st, kPanels),
+                                                        (int)D, (int)N2, st, kPanels, sp.g2),
                      "fp8 block-scaled gemm2_rowscale launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");
@@ -664,8 +676,13 @@ int coda_block_unfused_fp8(const void* Xq, const float* sx, const void* W1q, con
     hipStream_t st = (hipStream_t)stream;
     Workspace w;
     carve(workspace, M, D, 1, 1, &w);
+    const SplitPlan sp =
+        split_plan(workspace, M, K1, D, N2, 1, 1, ws_split_room(M, K1, D, N2, 1, 1, workspace_bytes));
+    if (sp.tickets1 &&
+        (s = hip_check(coda::launch_clear_tickets(sp.g1.cnt, sp.tickets1, st), "clear_tickets launch")))
+      return s;
     if ((s = hip_check(coda::launch_gemm_store_fp8((const uint8_t*)Xq, sx, (const uint8_t*)W1q, sw1, w.t, (int)M,
-                                                   (int)K1, (int)D, st),
+                                                   (int)K1, (int)D, st, sp.g1),
                        "fp8 gemm_store launch")))
       return s;
     if ((s = hip_check(coda::launch_add_rmsnorm_quant(w.t, (const uint16_t*)R, gamma, (uint16_t*)out_h, w.q, w.r, w.qs,
@@ -673,7 +690,7 @@ int coda_block_unfused_fp8(const void* Xq, const float* sx, const void* W1q, con
                        "add_rmsnorm_quant launch")))
       return s;
     return hip_check(coda::launch_gemm2_rowscale_fp8(w.q, (const uint8_t*)W2q, w.qs, sw2, epi_kind == CODA_EPI_SWIGLU,
-                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st),
+                                                     (uint16_t*)out_y, (int)M, (int)D, (int)N2, st, 0, sp.g2),
                      "unfused fp8 gemm2 launch");
   } catch (...) {
     return fail(CODA_ERR_INTERNAL, "unexpected exception");

@@ -137,10 +137,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
                                                     (MX_A ? NSTAGE * MX_STAGE_BYTES : 0)];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
-  // the split of the last wave (KSplit) exists for the bf16 kernels; the first GEMMs also clear the second GEMM's
-  // tickets
+  // the split of the last wave (KSplit); the first GEMMs also clear the second GEMM's tickets
   constexpr bool FIRST_GEMM = MODE == MODE_RES_PRMS || MODE == MODE_STORE;
-  constexpr bool CAN_SPLIT = (ROWSCALE_MODE || FIRST_GEMM) && !FP8;
+  constexpr bool CAN_SPLIT = ROWSCALE_MODE || FIRST_GEMM;
   if (FIRST_GEMM && ks.clear && blockIdx.x == 0)
     for (int i = threadIdx.x; i < ks.nclear; i += NTHREADS) ks.clear[i] = 0;
   int tm, tn, piece = -1, tile_ord = 0;
@@ -183,18 +182,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
                                                                         : ALayout{K, KS};
   f32x16 acc[4][NB];
   if (FP8) {
-    const uint8_t* A8 = (const uint8_t*)A;
-    const uint8_t* B8 = (const uint8_t*)B;
+    // a piece's share of K starts kbeg / KS stages in: A and B by that offset, and the block scales (MX) by
+    // that many K steps of their layout (mx_scale_index: tiles_m * 512 bytes per step)
+    const uint8_t* A8 = (const uint8_t*)A + (int64_t)(kbeg / KS) * al.step;
+    const uint8_t* B8 = (const uint8_t*)B + (int64_t)kbeg * Nb;
+    const uint8_t* asc = MX_A ? mxs + (int64_t)(kbeg / KS) * tiles_m * 512 : mxs;
     char* mx_smem = smem + LDS_BYTES + FOLD_LDS;
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, GateUpCols<16>{(int64_t)tn * 128, Nb / 2}, K, smem, acc,
-                              fold_hook, mxs, mx_smem);
+      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, GateUpCols<16>{(int64_t)tn * 128, Nb / 2}, kpart, smem, acc,
+                              fold_hook, asc, mx_smem);
     else if (MODE == MODE_RES_PRMS)  // the residual tile's first 192 rows arrive as the ring drains
-      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
-                              mxs, mx_smem, TileRowsDrain{R, Nb, m0, tn * BN, M, smem});
+      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, kpart, smem, acc,
+                              fold_hook, asc, mx_smem, TileRowsDrain{R, Nb, m0, tn * BN, M, smem});
     else
-      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, K, smem, acc, fold_hook,
-                              mxs, mx_smem);
+      gemm_mainloop_fp8<MX_A>(A8, al, M, m0, B8, Nb, ContiguousCols<16>{(int64_t)tn * BN}, kpart, smem, acc,
+                              fold_hook, asc, mx_smem);
   } else {
     const uint16_t* A16 = (const uint16_t*)A + (int64_t)(kbeg / KS) * al.step;
     const uint16_t* B16 = (const uint16_t*)B + (int64_t)kbeg * Nb;
@@ -229,13 +231,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     // release runs in one wave only: it acts on the whole L2, and in all eight waves (as seq_cst fences) it made the
     // 1B MLP-out -> QKV GEMM2 2.4x slower; the acquire in every wave cost 0.2-3 us per block against one wave's.
     // The ticket is broadcast through a word of the kernel's LDS array that nothing reads or writes at this point:
-    // the first word of the folded-reduce area (its partial sums were consumed by the hook long before), of the row
-    // sums' exchange area (used later in the epilogue), or of ring stage 0 (free after the mainloop where no drain
-    // refills it).  A __shared__ variable of its own would make the compiler wait for every in-flight direct load
-    // (vmcnt(0)) before each LDS read of the mainloop, unable to tell that the two objects do not overlap
+    // the first word of the row sums' exchange area (used later in the epilogue), of the folded-reduce area (its
+    // partial sums were consumed by the hook long before), or of ring stage 0 (free after the mainloop where no
+    // drain refills it).  A __shared__ variable of its own would make the compiler wait for every in-flight direct
+    // load (vmcnt(0)) before each LDS read of the mainloop, unable to tell that the two objects do not overlap
     // (measured: 40% on the product's time, whole tiles included).
-    static_assert(!CAN_SPLIT || !ROWSCALE_MODE || FOLD_LDS > 0, "the split needs the folded-reduce area");
-    int& ticket = *(int*)(MODE == MODE_RES_PRMS ? smem + LDS_BYTES : ROWSCALE_MODE ? smem + LDS_BYTES + 1024 : smem);
+    int& ticket = *(int*)(MODE == MODE_RES_PRMS ? smem + LDS_BYTES : FOLD_LDS > 0 ? smem + LDS_BYTES + 1024 : smem);
     const int S = 1 << ks.lg;
     const int64_t st = tile_ord - ks.full;  // the split tile's index
     float* slots = ks.part + st * (2 * S - 2) * KSPLIT_SLOT_FLOATS;
@@ -513,7 +514,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     store_tile_rows<32>(smem, out, Nb, m0, tn * BN, M);
   } else {  // MODE_ROWSCALE_SWIGLU: accumulator block 0 holds gate columns, block 1 the matching up columns
     const int ny = Nb / 2;
-    const int c_base = tn * 128 + wn * 32 + 4 * half;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int r = wm * 128 + mb * 32 + (lane & 31);
@@ -846,11 +846,11 @@ static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, 
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
   const int ntiles = tiles_m * tiles_n;
-  constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
-  constexpr bool CAN_SPLIT = (ROWSCALE_MODE || MODE == MODE_RES_PRMS || MODE == MODE_STORE) && !FP8;
+  constexpr KSplitRule rule = FP8 ? KSPLIT_E4M3 : KSPLIT_BF16;
+  static_assert(rule.gran == (FP8 ? K8_MULTIPLE : K_MULTIPLE), "the split's K granule is one ring fill");
   int nwg = ntiles;
-  if (CAN_SPLIT && ks.full >= 0 && ks.full < ntiles && ks.part && ks.cnt && ks.lg >= 1 && ks.lg <= KSPLIT_MAX_LG &&
-      K % (128 << ks.lg) == 0 && (K >> ks.lg) >= KSPLIT_MIN_PIECE_K)
+  if (ks.full >= 0 && ks.full < ntiles && ks.part && ks.cnt && ks.lg >= 1 && ks.lg <= KSPLIT_MAX_LG &&
+      K % (rule.gran << ks.lg) == 0 && (K >> ks.lg) >= rule.min_piece)
     nwg = ks.full + ((ntiles - ks.full) << ks.lg);
   else
     ks.full = -1;  // nothing to split, or a split this kernel or K cannot take: whole tiles
@@ -878,17 +878,18 @@ hipError_t launch_clear_tickets(int* cnt, int n, hipStream_t stream) {
   return hipGetLastError();
 }
 
-int ksplit_plan(int64_t ntiles, int64_t K, int cus, int* lg) {
+int ksplit_plan(int64_t ntiles, int64_t K, int cus, int fp8, int* lg) {
+  const KSplitRule& u = fp8 ? KSPLIT_E4M3 : KSPLIT_BF16;
   *lg = 0;
   if (cus <= 0 || ntiles <= 0) return (int)ntiles;
   const int64_t rem = ntiles % cus;
   if (rem == 0) return (int)ntiles;
-  // a last wave of at most a quarter of the CUs, or of at most three eighths where K >= KSPLIT_LONG_K
-  if (4 * rem > cus && !(8 * rem <= 3 * cus && K >= KSPLIT_LONG_K)) return (int)ntiles;
-  if (K % 256 || K / 2 < KSPLIT_MIN_PIECE_K) return (int)ntiles;  // two pieces of at least KSPLIT_MIN_PIECE_K
-  int g = 1;  // more pieces while they stay within half of the CUs and each keeps KSPLIT_TREE_MIN_PIECE_K of K
-  while (g < KSPLIT_MAX_LG && 2 * (rem << (g + 1)) <= cus && K % (128 << (g + 1)) == 0 &&
-         (K >> (g + 1)) >= KSPLIT_TREE_MIN_PIECE_K)
+  // a last wave of at most cus / tail_den tiles, or of at most three eighths of the CUs where K >= long_k
+  if (u.tail_den * rem > cus && !(8 * rem <= 3 * cus && K >= u.long_k)) return (int)ntiles;
+  if (K % (2 * u.gran) || K / 2 < u.min_piece) return (int)ntiles;  // two pieces of at least min_piece
+  int g = 1;  // more pieces while they stay within half of the CUs and each keeps tree_piece of K
+  while (g < KSPLIT_MAX_LG && 2 * (rem << (g + 1)) <= cus && K % ((int64_t)u.gran << (g + 1)) == 0 &&
+         (K >> (g + 1)) >= u.tree_piece)
     ++g;
   *lg = g;
   return (int)(ntiles - rem);
@@ -903,27 +904,31 @@ hipError_t launch_gemm1_res_prms(const uint16_t* X, const uint16_t* W1, const ui
 
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
                                      const uint16_t* R, uint16_t* H, float* part, int M, int K1, int D,
-                                     hipStream_t stream) {
-  return launch_gemm<MODE_RES_PRMS, true>(Xq, W1q, nullptr, R, sx, sw1, H, nullptr, part, M, K1, D, stream);
+                                     hipStream_t stream, KSplit ks) {
+  return launch_gemm<MODE_RES_PRMS, true>(Xq, W1q, nullptr, R, sx, sw1, H, nullptr, part, M, K1, D, stream,
+                                          RopeParams{}, RowFold{}, nullptr, 0, ks);
 }
 
 hipError_t launch_gemm1_res_prms_fp8_mx(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
                                         const uint16_t* R, const float* gamma, uint16_t* H, uint8_t* HQ, uint8_t* HS,
-                                        float* part, int M, int K1, int D, hipStream_t stream, int panels) {
+                                        float* part, int M, int K1, int D, hipStream_t stream, int panels,
+                                        KSplit ks) {
   return launch_gemm<MODE_RES_PRMS, true, true>(Xq, W1q, gamma, R, sx, sw1, H, (uint16_t*)HQ, part, M, K1, D, stream,
-                                                RopeParams{}, RowFold{}, HS, panels);
+                                                RopeParams{}, RowFold{}, HS, panels, ks);
 }
 
 hipError_t launch_gemm2_rowscale_fp8_mx(const uint8_t* HQ, const uint8_t* HS, const uint8_t* W2q, const float* sw2,
                                         const float* r_in, const float* part, float eps, float* r_out, int swiglu,
-                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels) {
+                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels,
+                                        KSplit ks) {
   const RowFold f = part ? RowFold{D / BN, (float)D, eps, r_out} : RowFold{};
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, true, true>(HQ, W2q, nullptr, nullptr, part ? nullptr : r_in, sw2, Y,
                                                          nullptr, (float*)part, M, D, N2, stream, RopeParams{}, f,
-                                                         (uint8_t*)HS, panels);
+                                                         (uint8_t*)HS, panels, ks);
   return launch_gemm<MODE_ROWSCALE, true, true>(HQ, W2q, nullptr, nullptr, part ? nullptr : r_in, sw2, Y, nullptr,
-                                                (float*)part, M, D, N2, stream, RopeParams{}, f, (uint8_t*)HS, panels);
+                                                (float*)part, M, D, N2, stream, RopeParams{}, f, (uint8_t*)HS, panels,
+                                                ks);
 }
 
 hipError_t launch_prms_reduce(const float* part, int T, int M, int D, float eps, float* r, hipStream_t stream) {
@@ -1025,12 +1030,13 @@ hipError_t launch_rope_rows(uint16_t* Y, int M, int N, int seq_len, int n_rot, f
 }
 
 hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,
-                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels) {
+                                     int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels,
+                                     KSplit ks) {
   if (swiglu)
     return launch_gemm<MODE_ROWSCALE_SWIGLU, true>(Aq, W2q, nullptr, nullptr, rowsc, sw2, Y, nullptr, nullptr, M, D,
-                                                   N2, stream, RopeParams{}, RowFold{}, nullptr, panels);
+                                                   N2, stream, RopeParams{}, RowFold{}, nullptr, panels, ks);
   return launch_gemm<MODE_ROWSCALE, true>(Aq, W2q, nullptr, nullptr, rowsc, sw2, Y, nullptr, nullptr, M, D, N2, stream,
-                                          RopeParams{}, RowFold{}, nullptr, panels);
+                                          RopeParams{}, RowFold{}, nullptr, panels, ks);
 }
 
 hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, int M, int K, int N,
@@ -1040,8 +1046,9 @@ hipError_t launch_gemm_store(const uint16_t* X, const uint16_t* W, uint16_t* T, 
 }
 
 hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,
-                                 int M, int K, int N, hipStream_t stream) {
-  return launch_gemm<MODE_STORE, true>(Xq, Wq, nullptr, nullptr, sx, sw, T, nullptr, nullptr, M, K, N, stream);
+                                 int M, int K, int N, hipStream_t stream, KSplit ks) {
+  return launch_gemm<MODE_STORE, true>(Xq, Wq, nullptr, nullptr, sx, sw, T, nullptr, nullptr, M, K, N, stream,
+                                       RopeParams{}, RowFold{}, nullptr, 0, ks);
 }
 
 hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H, uint16_t* N,

@@ -6,17 +6,17 @@
 
 namespace coda {
 
-// Split of a GEMM's last, partial wave of output tiles.  When the tile count leaves a last wave that fills at most a
-// quarter of the CUs, the tiles of that wave (the last ones in the tile order) are each computed as S = 2^lg pieces
-// over S equal ranges of K, so the last wave runs on S times as many CUs: the grid holds `full` whole tiles, then
-// (ntiles - full) S pieces.  The pieces of a tile meet in a binary tree of S - 1 nodes: at each level a piece stores
+// Split of a GEMM's last, partial wave of output tiles.  When the tile count leaves a last wave that fills a small
+// part of the CUs (ksplit_plan), the tiles of that wave (the last ones in the tile order) are each computed as
+// S = 2^lg pieces over S equal ranges of K, so the last wave runs on S times as many CUs: the grid holds `full` whole
+// tiles, then (ntiles - full) S pieces.  The pieces of a tile meet in a binary tree of S - 1 nodes: at each level a piece stores
 // its fp32 accumulators in its slot of `part`, then takes a ticket from its node's counter; the piece that draws the
 // node's second ticket adds its sibling's slot to its own accumulators (fp32 addition is commutative, so each node's
 // sum does not depend on which of its two pieces comes second, and the tree fixes the order of the rest) and goes
 // on to the next level; the first one exits.  The root's second arrival runs the epilogue.  No piece waits for
 // another.  The counters must be zero at launch: the block's first GEMM clears those of its second GEMM (`clear`,
-// `nclear`), and launch_clear_tickets clears the first GEMM's own before it runs.  Both GEMMs of the bf16 blocks (K1
-// or U1, and K3 or U3) can be split.
+// `nclear`), and launch_clear_tickets clears the first GEMM's own before it runs.  Both GEMMs of every block (K1 or
+// U1, and K3 or U3; bf16 and e4m3) can be split.
 struct KSplit {
   int full = -1;          // whole tiles; negative: no split
   int lg = 1;             // S = 2^lg pieces per split tile (1 .. 3)
@@ -27,22 +27,29 @@ struct KSplit {
   int nclear = 0;
 };
 constexpr int KSPLIT_SLOT_FLOATS = 512 * 128;  // one workgroup's accumulators (512 lanes x 128)
-constexpr int KSPLIT_MIN_PIECE_K = 512;        // K of one piece at least
-constexpr int KSPLIT_TREE_MIN_PIECE_K = 1024;  // K of one piece at least where a tile has more than two
-constexpr int KSPLIT_MAX_LG = 3;               // at most 8 pieces per tile
-constexpr int KSPLIT_LONG_K = 4096;            // K from which a last wave of up to three eighths of the CUs splits
-// The split of `ntiles` output tiles over K on `cus` CUs: returns the number of whole tiles (ntiles when no split
-// pays) and sets *lg.  A last wave splits where it fills at most a quarter of the CUs, or at most three eighths where
-// K >= KSPLIT_LONG_K, and K gives two pieces of KSPLIT_MIN_PIECE_K (K a multiple of 256): in two pieces, or more (up
-// to 8) while all the pieces stay within half of the CUs and each keeps KSPLIT_TREE_MIN_PIECE_K of K (a multiple of
-// 128).  Measured on MI355X (the block's time): with two pieces, a last wave of 16 or 32 tiles at K = 2048 gains
-// 7-10 us, one of 64 about 2 us, one of 96 or 128 loses 2-7 us (the pieces' fp32 slots cross the memory system,
-// 256 KiB written per piece and level, and a last wave of whole tiles on part of the chip runs at a higher clock
-// than the full chip does); over longer K the savings grow and the exchange does not: last waves of 80 and 96 tiles
-// gain 8-15 us at K = 4096 and 32-53 us at K = 8192, one of 128 still loses up to 7 us.  More pieces pay where each
-// keeps 1024 of K or more (one tile over K1 = 8192 in eight: 150 -> 57 us; 32 tiles over K1 = 8192 in four rather
-// than two: 123 -> 105 us) and lose below that (32 tiles over K = 2048 in four: 113 -> 120 us).
-int ksplit_plan(int64_t ntiles, int64_t K, int cus, int* lg);
+constexpr int KSPLIT_MAX_LG = 3;  // at most 8 pieces per tile
+// The split rule of one operand type (all K in elements): a last wave of at most cus / tail_den tiles splits, or of at
+// most three eighths of the CUs where K >= long_k, if K gives two pieces of at least min_piece (K a multiple of
+// 2 gran, gran = one fill of the 4-stage ring); into 4 or 8 pieces while all the pieces stay within half of the CUs
+// and each keeps tree_piece of K (K a multiple of gran times the pieces).
+struct KSplitRule {
+  int gran, min_piece, tree_piece, long_k, tail_den;
+};
+// bf16, measured on MI355X (the block's time): with two pieces, a last wave of 16 or 32 tiles at K = 2048 gains
+// 7-10 us, one of 64 about 2 us, one of 96 or 128 loses 2-7 us (the pieces' fp32 slots cross the memory system, 256 KiB
+// written per piece and level, and a last wave of whole tiles on part of the chip runs at a higher clock than the
+// full chip does); over longer K the savings grow and the exchange does not: last waves of 80 and 96 tiles gain 8-15
+// us at K = 4096 and 32-53 us at K = 8192, one of 128 still loses up to 7 us.  More pieces pay where each keeps 1024
+// of K or more (one tile over K1 = 8192 in eight: 150 -> 57 us; 32 tiles over K1 = 8192 in four rather than two:
+// 123 -> 105 us) and lose below that (32 tiles over K = 2048 in four: 113 -> 120 us).
+constexpr KSplitRule KSPLIT_BF16{128, 512, 1024, 4096, 4};
+// e4m3 (an e4m3 K value costs the MFMAs half a bf16 one, the exchange the same): in two pieces, last waves of 16 or
+// 32 tiles lose up to 3 us at K = 2048 and gain 4-9 us at K = 4096, one of 64 loses 3-8 us at K = 2048 and 2-6 us at
+// K = 4096; 32 tiles over K1 = 8192 in four gain 20 us (107 -> 87 us), 96 tiles over K1 = 8192 in two 4-5 us.
+constexpr KSplitRule KSPLIT_E4M3{256, 2048, 2048, 8192, 8};
+// The split of `ntiles` output tiles over K on `cus` CUs, by the rule of the operands' type (fp8 != 0: e4m3):
+// returns the number of whole tiles (ntiles when no split pays) and sets *lg to log2 of the pieces per split tile.
+int ksplit_plan(int64_t ntiles, int64_t K, int cus, int fp8, int* lg);
 // Zeroes n tickets (a small kernel on `stream`; graph-capturable, unlike a memset node).
 hipError_t launch_clear_tickets(int* cnt, int n, hipStream_t stream);
 
@@ -88,18 +95,20 @@ hipError_t launch_add_rmsnorm(const uint16_t* T, const uint16_t* R, const float*
 // K1: as launch_gemm1_res_prms with X W1 = (Xq W1q) * sx[m] * sw1[n].
 hipError_t launch_gemm1_res_prms_fp8(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
                                      const uint16_t* R, uint16_t* H, float* part, int M, int K1, int D,
-                                     hipStream_t stream);
+                                     hipStream_t stream, KSplit ks = KSplit());
 // MX variant of K1: also HQ = e4m3 codes of a = bf16(H) * gamma in blocks of 32 columns with power-of-two scales
 // (HS: one byte e + 127 per block, laid out as mx_scale_index in gemm_core.h; ceil(M / 256) * 256 rows * D / 32
 // bytes).  D % 256 == 0.
 hipError_t launch_gemm1_res_prms_fp8_mx(const uint8_t* Xq, const float* sx, const uint8_t* W1q, const float* sw1,
                                         const uint16_t* R, const float* gamma, uint16_t* H, uint8_t* HQ, uint8_t* HS,
-                                        float* part, int M, int K1, int D, hipStream_t stream, int panels = 0);
+                                        float* part, int M, int K1, int D, hipStream_t stream, int panels = 0,
+                                        KSplit ks = KSplit());
 // MX variant of K3: Y = bf16(epi(r * (HQ W2q) * sw2[n])) with HQ's block scales inside the MFMA.  With part
 // non-null the reduce is folded in (D / 256 <= 16; r written to r_out), else the row scale is r_in.
 hipError_t launch_gemm2_rowscale_fp8_mx(const uint8_t* HQ, const uint8_t* HS, const uint8_t* W2q, const float* sw2,
                                         const float* r_in, const float* part, float eps, float* r_out, int swiglu,
-                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels = 0);
+                                        uint16_t* Y, int M, int D, int N2, hipStream_t stream, int panels = 0,
+                                        KSplit ks = KSplit());
 // K2: r from the partial sums; with a = H * gamma (fp32), HQ = e4m3(a * (1 / sa)) per row, sa = amax|a row| / 448;
 // rs2 = sa * r.
 hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, float eps, const uint16_t* H,
@@ -108,10 +117,10 @@ hipError_t launch_prms_reduce_quant(const float* part, int T, int M, int D, floa
 // K3 / U3: Y = bf16(epi((Aq W2q) * rowsc[m] * sw2[n])).
 hipError_t launch_gemm2_rowscale_fp8(const uint8_t* Aq, const uint8_t* W2q, const float* rowsc, const float* sw2,
                                      int swiglu, uint16_t* Y, int M, int D, int N2, hipStream_t stream,
-                                     int panels = 0);
+                                     int panels = 0, KSplit ks = KSplit());
 // U1: T = bf16((Xq Wq) * sx[m] * sw[n]).
 hipError_t launch_gemm_store_fp8(const uint8_t* Xq, const float* sx, const uint8_t* Wq, const float* sw, uint16_t* T,
-                                 int M, int K, int N, hipStream_t stream);
+                                 int M, int K, int N, hipStream_t stream, KSplit ks = KSplit());
 // U2: H = bf16(T + R); NQ = e4m3(n / sn) per row with n = (T + R) r gamma and sn = amax|n row| / 448.
 hipError_t launch_add_rmsnorm_quant(const uint16_t* T, const uint16_t* R, const float* gamma, uint16_t* H,
                                     uint8_t* NQ, float* r, float* sn, int M, int D, float eps, hipStream_t stream);

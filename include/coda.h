@@ -93,12 +93,15 @@ const char* coda_last_error(void);
  *            ((k / P) * M + m) * P + k % P with P = 32 (bf16) or 64 (e4m3), so that the second product reads
  *            whole cache lines
  *   unfused: T [M,D] bf16 and n [M,D] bf16 (fp8: n as e4m3 [M,D] and its row scales [M]), row-major.
- * then, for the bf16 blocks (fp8 = 0), the room to split a product's last wave of tiles along K where that wave
- * fills at most a quarter of 256 CUs: the second product (ceil(M/256) * N2/256 tiles over K = D), then the first
- * (ceil(M/256) * D/256 tiles over K1), each where its K >= 1024: one int32 ticket per tile of the last wave
- * (256-byte aligned), then two fp32 slots of 256 KiB per such tile.  A block given a workspace of at least the size
- * without that room runs; it splits the last waves only where the room is there (the results of the two forms
- * differ in the last bits of the fp32 sums, nowhere else). */
+ * then the room to split a product's last wave of tiles along K, planned for 256 CUs: the second product
+ * (ceil(M/256) * N2/256 tiles over K = D), then the first (ceil(M/256) * D/256 tiles over K1).  bf16 blocks: a
+ * last wave splits where it fills at most a quarter of the CUs (three eighths where K >= 4096) and K >= 1024, into
+ * S = 2 pieces per tile, or 4 or 8 while all the pieces fill at most half of the CUs and each keeps 1024 of K.
+ * e4m3 blocks: at most an eighth of the CUs (three eighths where K >= 8192), K >= 4096, more pieces while each
+ * keeps 2048 of K.  Per tile of the last wave: S - 1 int32 tickets (all of them 256-byte aligned), then 2 S - 2
+ * fp32 slots of 256 KiB.  A block given a workspace of at least the size without that room
+ * runs; it splits the last waves only where the room is there (the results of the two forms differ in the last
+ * bits of the fp32 sums, nowhere else). */
 size_t coda_workspace_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, int epi_kind, int fp8, int unfused);
 
 /* The part of coda_workspace_bytes (same arguments) that is the split room of the products' last waves: 0 where
@@ -116,11 +119,11 @@ size_t coda_workspace_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, 
  * Two kernels on `stream` where D <= 4096: GEMM1 + residual + gamma + partial sums of squares, then GEMM2 on
  * hg whose workgroups reduce their rows' partial sums to r themselves and apply r (+ SwiGLU) in the epilogue.
  * Where D > 4096 the reduction runs as a kernel of its own between the two (three kernels).  Where a product's
- * last wave of 256 x 256 tiles would leave more than three quarters of the CUs idle, each of its tiles is computed
- * as two halves of K whose fp32 sums are added before the epilogue (see coda_workspace_bytes for the room this
- * takes); where the first product is split, a small kernel that zeroes its tickets runs first.  After the call the
- * workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D).  Ownership, errors and the
- * asynchronous contract are the shared conventions above. */
+ * last wave of 256 x 256 tiles would leave most of the CUs idle, each of its tiles is computed as 2, 4 or 8 equal
+ * ranges of K whose fp32 sums meet in a fixed binary tree before the epilogue (coda_workspace_bytes gives the rule
+ * and the room this takes); where the first product is split, a small kernel that zeroes its tickets runs first.
+ * After the call the workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D).  Ownership, errors
+ * and the asynchronous contract are the shared conventions above. */
 int coda_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,
                    float eps, int epi_kind, void* out_h, void* out_y,
                    int64_t M, int64_t K1, int64_t D, int64_t N2,
@@ -158,7 +161,8 @@ int coda_block_fwd_noalloc(const void* X, const void* W1, const void* R, const f
  * The second product's A operand is a = h * gamma (fp32, h the stored bf16 out_h) quantised per row to
  * e4m3(a * (1 / s_a)) with s_a = amax_j |a_ij| / 448 (1 for an all-zero row; 1 / s_a rounded to fp32 once)
  * by the reduction kernel, which has the whole row; y = bf16(epi(acc * s_a_i * r_i * sw2_n)).  Shape rules as coda_block_fwd, and K1 a multiple
- * of 256.  Workspace: coda_workspace_bytes(..., fp8 = 1, unfused = 0). */
+ * of 256.  Workspace: coda_workspace_bytes(..., fp8 = 1, unfused = 0); the products' last waves are split as in
+ * coda_block_fwd, by the e4m3 rule given there. */
 int coda_block_fwd_fp8(const void* Xq, const float* sx, const void* W1q, const float* sw1, const void* R,
                        const float* gamma, const void* W2q, const float* sw2, float eps, int epi_kind, void* out_h,
                        void* out_y, int64_t M, int64_t K1, int64_t D, int64_t N2, void* workspace,

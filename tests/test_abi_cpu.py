@@ -193,7 +193,8 @@ def test_workspace_split_bytes(lib):
     """The room to split each GEMM's last wave, planned for 256 CUs: none where the tiles fill whole waves, the last
     wave fills more than a quarter of the CUs or K (D for the second GEMM, K1 for the first) is below 1024; else, for
     S pieces per tile, S - 1 int32 tickets per tile of the last wave (256-byte aligned) and 2 S - 2 fp32 slots of
-    256 KiB per such tile, the second GEMM's room first.  coda_workspace_bytes includes it."""
+    256 KiB per such tile, the second GEMM's room first.  The e4m3 blocks have a rule of their own (an eighth of the
+    CUs, three eighths from K = 8192; pieces of at least 2048).  coda_workspace_bytes includes it."""
     al = lambda x: (x + 255) // 256 * 256
     slot = 512 * 128 * 4
     base = lambda M, D, unfused=0: al(D // 256 * M * 4) + al(M * 4) + (2 if unfused else 1) * al(M * D * 2)
@@ -206,8 +207,22 @@ def test_workspace_split_bytes(lib):
     assert lib.coda_workspace_bytes(8192, 2048, 2048, 2304, 0, 0, 0) == base(8192, 2048) + tail32
     assert f(8192, 2048, 2048, 2304, 0, 0, 1) == tail32       # the unfused bf16 block: the same room
     assert lib.coda_workspace_bytes(8192, 2048, 2048, 2304, 0, 0, 1) == base(8192, 2048, 1) + tail32
-    assert f(8192, 2048, 2048, 2304, 0, 1, 0) == 0            # e4m3 blocks: none
+    # e4m3 blocks (their own rule): a last wave of at most an eighth of the CUs (three eighths from K = 8192), pieces
+    # of at least 2048 of K
+    assert f(8192, 2048, 2048, 2304, 0, 1, 0) == 0            # 32 tiles over K = 2048: none
     assert f(8192, 2048, 2048, 2304, 0, 2, 0) == 0
+    assert f(8192, 2048, 4096, 4352, 0, 1, 0) == tail32       # 32 x 17 = 544 tiles, K = 4096: a last wave of 32
+    assert f(8192, 2048, 4096, 4352, 0, 2, 0) == tail32
+    assert f(8192, 2048, 4096, 4352, 0, 1, 1) == tail32
+    base8 = al(16 * 8192 * 4) + al(8192 * 4) + al(8192 * 4096) + 2 * al(8192 * 4)  # the fused e4m3 block's base
+    assert lib.coda_workspace_bytes(8192, 2048, 4096, 4352, 0, 1, 0) == base8 + tail32
+    assert f(8192, 2048, 4096, 4608, 0, 1, 0) == 0            # 32 x 18 = 576 tiles: a last wave of 64
+    assert f(8192, 2048, 4096, 4608, 0, 0, 0) == al(64 * 4) + 128 * slot  # (bf16: a quarter, split)
+    assert f(300, 256, 4096, 1024, 1, 1, 0) == al(8 * 4) + 16 * slot
+    assert f(64, 8192, 256, 256, 0, 1, 0) == al(3 * 4) + 6 * slot   # one tile over K1 = 8192 in four of 2048
+    assert f(64, 16384, 256, 256, 0, 1, 0) == al(7 * 4) + 14 * slot  # over K1 = 16384 in eight
+    assert f(3072, 4096, 2048, 2048, 0, 1, 0) == 0            # 96 tiles: three eighths only from K = 8192
+    assert f(3072, 8192, 2048, 2048, 0, 1, 0) == al(96 * 4) + 192 * slot
     assert f(256 * 65, 256, 1024, 256, 0, 0, 0) == 0            # 65 tiles: the last wave is over a quarter
     assert f(256 * 64, 256, 1024, 256, 0, 0, 0) == al(64 * 4) + 128 * slot  # 64 tiles: exactly a quarter
     assert f(300, 256, 768, 1024, 1, 0, 0) == 0                 # K = 768

@@ -46,13 +46,14 @@ def _stub_source(fatbin_symbol: str) -> str:
         params = re.sub(r"\s*=\s*[^,]+", "", params)  # default arguments belong to the declaration only
         if name == "fold_supported":
             body = "return D / 256 <= 16;"
-        elif name == "ksplit_plan":  # the split rule of a GEMM's last wave
-            body = ("*lg = 0; if (cus <= 0 || ntiles <= 0) return (int)ntiles; "
+        elif name == "ksplit_plan":  # the split rule of a GEMM's last wave (the rules themselves are in launch.h)
+            body = ("const KSplitRule& u = fp8 ? KSPLIT_E4M3 : KSPLIT_BF16; "
+                    "*lg = 0; if (cus <= 0 || ntiles <= 0) return (int)ntiles; "
                     "const int64_t rem = ntiles % cus; if (rem == 0) return (int)ntiles; "
-                    "if (4 * rem > cus && !(8 * rem <= 3 * cus && K >= 4096)) return (int)ntiles; "
-                    "if (K % 256 || K / 2 < 512) return (int)ntiles; "
-                    "int g = 1; while (g < 3 && 2 * (rem << (g + 1)) <= cus && K % (128 << (g + 1)) == 0 && "
-                    "(K >> (g + 1)) >= 1024) ++g; *lg = g; return (int)(ntiles - rem);")
+                    "if (u.tail_den * rem > cus && !(8 * rem <= 3 * cus && K >= u.long_k)) return (int)ntiles; "
+                    "if (K % (2 * u.gran) || K / 2 < u.min_piece) return (int)ntiles; "
+                    "int g = 1; while (g < 3 && 2 * (rem << (g + 1)) <= cus && K % ((int64_t)u.gran << (g + 1)) == 0 "
+                    "&& (K >> (g + 1)) >= u.tree_piece) ++g; *lg = g; return (int)(ntiles - rem);")
         elif name == "gemm_ksplit":  # the split rule of the weight-gradient products
             body = ("const int tiles = ((M + 255) / 256) * (N / 256); int s = 1; "
                     "while (s < 8 && tiles * s < 256 && K % (128 * s * 2) == 0) s *= 2; return s;")
