@@ -231,7 +231,8 @@ coda::KSplit split_one(char*& at, int64_t ntiles, int64_t K, int cus, int fp8, i
   return ks;
 }
 
-// The splits a block's GEMMs run with on this device, inside the validated room (none if they do not fit): g1 for
+// The splits a block's GEMMs run with on this device, inside the validated room (none if they do not fit), and the
+// half-tile form of the second GEMM's last wave where it is not split (bf16; needs no room): g1 for
 // the first GEMM (K1 or U1, over K1), g2 for the second (K3 or U3, over D).  g1 carries g2's tickets to clear.
 struct SplitPlan {
   coda::KSplit g1, g2;
@@ -240,18 +241,20 @@ struct SplitPlan {
 
 SplitPlan split_plan(void* ws, int64_t M, int64_t K1, int64_t D, int64_t N2, int fp8, int unfused, size_t room) {
   SplitPlan p;
-  if (!room) return p;
   const int cus = device_cus();
-  const size_t need = ws_split_bytes(M, K1, D, N2, fp8, cus);
-  if (!need || need > room) return p;
-  char* at = (char*)ws + ws_bytes(M, D, fp8, unfused);
-  int tickets2 = 0;
-  p.g2 = split_one(at, gemm_tiles(M, N2), D, cus, fp8, &tickets2);
-  p.g1 = split_one(at, gemm_tiles(M, D), K1, cus, fp8, &p.tickets1);
-  if (p.g2.full >= 0) {
-    p.g1.clear = p.g2.cnt;
-    p.g1.nclear = tickets2;
+  const size_t need = room ? ws_split_bytes(M, K1, D, N2, fp8, cus) : 0;
+  if (need && need <= room) {
+    char* at = (char*)ws + ws_bytes(M, D, fp8, unfused);
+    int tickets2 = 0;
+    p.g2 = split_one(at, gemm_tiles(M, N2), D, cus, fp8, &tickets2);
+    p.g1 = split_one(at, gemm_tiles(M, D), K1, cus, fp8, &p.tickets1);
+    if (p.g2.full >= 0) {
+      p.g1.clear = p.g2.cnt;
+      p.g1.nclear = tickets2;
+    }
   }
+  // bf16: where the second GEMM's last wave is not split along K, its tiles may run as 128-row halves (no room needed)
+  if (p.g2.full < 0 && !fp8) p.g2 = coda::halves_plan(gemm_tiles(M, N2), M, cus);
   return p;
 }
 

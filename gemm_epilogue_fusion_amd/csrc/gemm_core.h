@@ -107,6 +107,8 @@ struct LaneOffs {
   int b[NB];
 };
 
+// HALF: the half-tile form (gemm_mainloop), where wave row block wm covers rows 64 wm .. +64.
+template <bool HALF = false>
 __device__ __forceinline__ void lane_offsets(int wm, int wn, int lane, LaneOffs& o) {
   const int q = lane >> 4, j = lane & 15;
 #pragma unroll
@@ -118,12 +120,12 @@ __device__ __forceinline__ void lane_offsets(int wm, int wn, int lane, LaneOffs&
     const int piece = (n0 >> 2) + (j & 3);  // 8-byte piece within the 512-byte row
     o.b[nb] = A_BYTES + b_off(krow, piece >> 1) + ((piece & 1) << 3);
   }
-  const int m = wm * 128 + (lane & 31);
+  const int m = wm * (HALF ? 64 : 128) + (lane & 31);
 #pragma unroll
   for (int s = 0; s < 2; ++s) o.a[s] = a_off(m, 2 * s + (lane >> 5));
 }
 
-// RB: the wave's 32-row blocks that are computed (4; 2 in the small-row form, see wave_pos)
+// RB: the wave's 32-row blocks that are computed (4; 2 in the small-row and half-tile forms)
 template <int RB = 4>
 __device__ __forceinline__ void read_frags(const char* st, const LaneOffs& o, int s, Frags& f) {
 #pragma unroll
@@ -202,14 +204,21 @@ struct NoDrain {
 // SMALL: the small-row form (at most SMALL_MAX_ROWS rows; wave_pos): every wave fetches and waits as usual, the
 // waves of rows 128 .. 255 skip the fragment reads and MFMAs, the others compute their first two row blocks only
 // (the other accumulators stay zero).
-template <class BCol, class Hook = NoHook, class Drain = NoDrain, bool SMALL = false>
+// HALF: the half-tile form, a 128 x 256 tile (rows m0 .. m0+127) on the same eight waves: each wave computes two
+// row blocks, rows 64 wm .. +64 (lane_offsets), the A stage holds 128 rows (one direct load per wave and stage) and
+// acc[2], acc[3] stay zero.  Each output is the same chain of MFMAs over K as in the full tile, so the results are
+// the same bit for bit.
+template <class BCol, class Hook = NoHook, class Drain = NoDrain, bool SMALL = false, bool HALF = false>
 __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, ALayout al, int M, int m0,
                                               const uint16_t* __restrict__ B, int64_t ldb, BCol bcol, int K,
                                               char* smem, f32x16 (&acc)[4][NB], Hook hook = Hook{},
-                                              Drain drain = Drain{}, std::integral_constant<bool, SMALL> = {}) {
+                                              Drain drain = Drain{}, std::integral_constant<bool, SMALL> = {},
+                                              std::integral_constant<bool, HALF> = {}) {
+  static_assert(!(SMALL && HALF), "one row form at a time");
   constexpr int LPW = 16 / NWAVES;              // 1 KiB direct loads per wave per operand per stage
-  constexpr int PER = 2 * LPW;  // VMEM instructions per wave per stage
-  constexpr int RB = SMALL ? 2 : 4;
+  constexpr int LPA = HALF ? LPW / 2 : LPW;     // the A operand's (128 rows in the half-tile form)
+  constexpr int PER = LPA + LPW;  // VMEM instructions per wave per stage
+  constexpr int RB = (SMALL || HALF) ? 2 : 4;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -223,13 +232,13 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
 
   // Direct-load unit q (1 KiB) of a stage: A rows 16q .. 16q+15 (lane -> row 16q + lane/4, slot lane%4),
   // B rows 2q, 2q+1 (lane -> row 2q + lane/32, slot lane%32).  Each lane fetches the logical chunk that
-  // the swizzle places in its slot.
+  // the swizzle places in its slot.  Wave w issues A units LPA w .. and B units LPW w .. .
   const uint16_t* aptr[LPW];
   const uint16_t* bptr[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
     const int q = LPW * wave + i;
-    const int r = 16 * q + (lane >> 2);
+    const int r = 16 * (LPA * wave + i) + (lane >> 2);  // only i < LPA is issued
     const int c = (lane & 3) ^ ((r >> 2) & 3);
     int row = m0 + r;
     row = row < M ? row : M - 1;
@@ -239,14 +248,14 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
     bptr[i] = B + (int64_t)kr * ldb + bcol(cb);
   }
   LaneOffs lo;
-  lane_offsets(wm, wn, lane, lo);
+  lane_offsets<HALF>(wm, wn, lane, lo);
   const int nk = K / BK;
 
   auto issue = [&](int kt, int stage) {
     char* st = smem + stage * STAGE_BYTES;
     const int k0 = kt * BK;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) g2lds16(aptr[i] + (int64_t)kt * al.step, st + (LPW * wave + i) * 1024);
+    for (int i = 0; i < LPA; ++i) g2lds16(aptr[i] + (int64_t)kt * al.step, st + (LPA * wave + i) * 1024);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) g2lds16(bptr[i] + (int64_t)k0 * ldb, st + A_BYTES + (LPW * wave + i) * 1024);
   };
@@ -266,7 +275,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
     if (computes) {
       read_frags<RB>(cur, lo, 1, f1);
       mma<RB>(f0, acc);
-      if (!SMALL) interleave_mma_reads();
+      if (RB == 4) interleave_mma_reads();
     }
     if (WAIT >= 0) {
       wait_barrier<(WAIT < 0 ? 0 : WAIT)>();
@@ -275,7 +284,7 @@ __device__ __forceinline__ void gemm_mainloop(const uint16_t* __restrict__ A, AL
     }
     if (computes) {
       mma<RB>(f1, acc);
-      if (!SMALL) interleave_mma_reads();
+      if (RB == 4) interleave_mma_reads();
     }
   };
   using S0 = std::integral_constant<int, 0>;

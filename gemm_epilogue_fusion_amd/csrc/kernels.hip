@@ -116,14 +116,18 @@ struct GateUpCols {
 // width ([Nb / 32][M][32] bf16, [Nb / 64][M][64] bytes), and the row-scale modes and MODE_STORE read A from such
 // panels (ALayout in gemm_core.h); A of MODE_RES_PRMS is always row-major.
 // SMALL (bf16, M <= SMALL_MAX_ROWS): the mainloop's small-row form (wave_pos in gemm_core.h).
-template <int MODE, bool FP8, bool MX = false, bool SMALL = false>
-__global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
+// HALF (bf16, row-scale modes): the half-tile form of the mainloop.  The workgroups take the tiles from ks.full on (in
+// tile order) as two 128-row halves each, both halves of a tile on one XCD (KSplit::halves).
+// The kernels are gemm_epilogue_kernel (whole tiles, the K split) and gemm_epilogue_half_kernel (HALF) below.
+template <int MODE, bool FP8, bool MX, bool SMALL, bool HALF>
+__device__ __forceinline__ void gemm_epilogue_body(
     const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
     const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
     float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs,
     int panels, KSplit ks) {
   constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
   static_assert(!SMALL || !FP8, "the small-row form is bf16 only");
+  static_assert(!HALF || (!FP8 && !SMALL && ROWSCALE_MODE), "the half-tile form is for the bf16 row-scale modes");
   // MX (e4m3 only): K1 (MODE_RES_PRMS) also quantises h * gamma in blocks of 32 columns with power-of-two
   // scales (codes to out2, scales to mxs); K3 (row-scale modes) reads its A operand's block scales from mxs
   constexpr bool MX_A = FP8 && MX && ROWSCALE_MODE;
@@ -142,12 +146,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   constexpr bool CAN_SPLIT = ROWSCALE_MODE || FIRST_GEMM;
   if (FIRST_GEMM && ks.clear && blockIdx.x == 0)
     for (int i = threadIdx.x; i < ks.nclear; i += NTHREADS) ks.clear[i] = 0;
-  int tm, tn, piece = -1, tile_ord = 0;
-  if (CAN_SPLIT && ks.full >= 0)
+  int tm, tn, piece = -1, tile_ord = 0, hrow = 0;
+  if (HALF) {
+    // workgroup p takes half p % 2 of tile ks.full + p / 2, with p remapped (as tile_coords_split remaps its pieces)
+    // so that each XCD receives a contiguous range: the two halves of a tile run on one XCD
+    int p = blockIdx.x;
+    const int np = gridDim.x;
+    if ((np & 15) == 0) p = (p & 7) * (np >> 3) + (p >> 3);
+    hrow = 128 * (p & 1);
+    tile_of_order(ks.full + (p >> 1), tiles_m, tiles_n, group_m, tm, tn);
+  } else if (CAN_SPLIT && ks.full >= 0) {
     piece = tile_coords_split(tiles_m, tiles_n, group_m, ks.full, ks.lg, tm, tn, tile_ord);
-  else
+  } else {
     tile_coords(tiles_m, tiles_n, group_m, tm, tn);
-  const int m0 = tm * BM;
+  }
+  const int m0 = tm * BM + hrow;
+  // the rows this workgroup may store: a half-tile's 128, or the tile's up to M
+  const int Mh = HALF ? (M < m0 + 128 ? M : m0 + 128) : M;
   // a piece multiplies over its share of K
   const int kpart = piece >= 0 ? K >> ks.lg : K;
   const int kbeg = piece > 0 ? piece * kpart : 0;
@@ -201,15 +216,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     const uint16_t* A16 = (const uint16_t*)A + (int64_t)(kbeg / KS) * al.step;
     const uint16_t* B16 = (const uint16_t*)B + (int64_t)kbeg * Nb;
     constexpr std::integral_constant<bool, SMALL> small{};
+    constexpr std::integral_constant<bool, HALF> half_tile{};
+    // (a half tile's A rows past its 128 read its last row, never used)
     if (MODE == MODE_ROWSCALE_SWIGLU)
-      gemm_mainloop(A16, al, M, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, kpart, smem, acc, fold_hook,
-                    NoDrain{}, small);
+      gemm_mainloop(A16, al, Mh, m0, B16, Nb, GateUpCols<8>{(int64_t)tn * 128, Nb / 2}, kpart, smem, acc, fold_hook,
+                    NoDrain{}, small, half_tile);
     else if (MODE == MODE_RES_PRMS)  // the residual tile's first 192 rows arrive as the ring drains
       gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook,
                     TileRowsDrain{R, Nb, m0, tn * BN, M, smem}, small);
     else
-      gemm_mainloop(A16, al, M, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook,
-                    NoDrain{}, small);
+      gemm_mainloop(A16, al, Mh, m0, B16, Nb, ContiguousCols<8>{(int64_t)tn * BN}, kpart, smem, acc, fold_hook,
+                    NoDrain{}, small, half_tile);
   }
 
   // Materialise the accumulators here: otherwise the compiler may sink the last MFMAs into the epilogue's
@@ -291,18 +308,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   int wm, wn;
   wave_pos<SMALL>(wave, wm, wn);
   const int half = lane >> 5;
+  // the tile row of accumulator block mb's lane 0: in the half-tile form blocks 0 and 1 hold rows 64 wm .. +64 and
+  // blocks 2 and 3 (zero) map to rows 128 .. 255, which are never stored
+  auto rowof = [&](int mb) { return HALF ? (mb >> 1) * 128 + wm * 64 + (mb & 1) * 32 : wm * 128 + mb * 32; };
 
   // per-row scales of this lane's four rows (rows past M read row M-1; they are never stored)
   float rsv[4];
   if (CAN_FOLD && folding) {
     if (t < BM) {
       fold_r[t] = rfold;
-      if (tn == 0 && m0 + t < M) fold.r[m0 + t] = rfold;
+      if (tn == 0 && m0 + t < Mh) fold.r[m0 + t] = rfold;
     }
   } else {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + wm * 128 + mb * 32 + (lane & 31);
+      const int m = m0 + rowof(mb) + (lane & 31);
       // row scales: the e4m3 dequantisation scales, or r in the row-scale modes (bf16 GEMM1 and plain stores
       // have none, so their kernels compile without the load)
       rsv[mb] = ((FP8 || ROWSCALE_MODE) && rowsc) ? rowsc[m < M ? m : M - 1] : 1.0f;
@@ -322,7 +342,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
   __syncthreads();  // every wave is done with the mainloop's LDS stages (and the folded row scales are in)
   if (CAN_FOLD && folding) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) rsv[mb] = fold_r[wm * 128 + mb * 32 + (lane & 31)];
+    for (int mb = 0; mb < 4; ++mb) rsv[mb] = fold_r[rowof(mb) + (lane & 31)];
   }
 
   if (MODE == MODE_RES_PRMS || MODE == MODE_STORE || MODE == MODE_ROWSCALE) {
@@ -348,7 +368,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
     u32x2 hgv[4][NB][4];  // bf16(h * gamma), staged after h has been written out
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int r = wm * 128 + mb * 32 + (lane & 31);
+      const int r = rowof(mb) + (lane & 31);
       float s = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
@@ -380,13 +400,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       ss[mb] = s;
     }
     __syncthreads();
-    store_tile_rows<32>(smem, out, Nb, m0, tn * BN, M);
+    store_tile_rows<32>(smem, out, Nb, m0, tn * BN, Mh);
     if (MODE == MODE_RES_PRMS) {
       if (WRITE_HG) {
         __syncthreads();
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          const int r = wm * 128 + mb * 32 + (lane & 31);
+          const int r = rowof(mb) + (lane & 31);
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -401,7 +421,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       float* red = (float*)(smem + LDS_BYTES);  // [4 wn][256 rows], outside the staging area
       if (lane < 32) {
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) red[wn * 256 + wm * 128 + mb * 32 + lane] = ss[mb];
+        for (int mb = 0; mb < 4; ++mb) red[wn * 256 + rowof(mb) + lane] = ss[mb];
       }
       __syncthreads();
       if (WRITE_HG) {
@@ -413,7 +433,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       if (wn == 0 && lane < 32) {
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-          const int row = wm * 128 + mb * 32 + lane;
+          const int row = rowof(mb) + lane;
           const int m = m0 + row;
           if (m < M) part[(int64_t)tn * M + m] = ((red[row] + red[256 + row]) + red[512 + row]) + red[768 + row];
         }
@@ -484,7 +504,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       for (int e = 0; e < 4; ++e) rev[gq][e] = half ? rope.rev[8 * gq + 4 + e] : rope.rev[8 * gq + e];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int r = wm * 128 + mb * 32 + (lane & 31);
+      const int r = rowof(mb) + (lane & 31);
       const int m = m0 + r;
       const float pos = (float)((m < M ? m : M - 1) % rope.seq_len);
       const float sc = rsv[mb];
@@ -511,12 +531,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       }
     }
     __syncthreads();
-    store_tile_rows<32>(smem, out, Nb, m0, tn * BN, M);
+    store_tile_rows<32>(smem, out, Nb, m0, tn * BN, Mh);
   } else {  // MODE_ROWSCALE_SWIGLU: accumulator block 0 holds gate columns, block 1 the matching up columns
     const int ny = Nb / 2;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const int r = wm * 128 + mb * 32 + (lane & 31);
+      const int r = rowof(mb) + (lane & 31);
       const float sc = rsv[mb];
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
@@ -532,14 +552,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
       }
     }
     __syncthreads();
-    store_tile_rows<16>(smem, out, ny, m0, tn * 128, M);
+    store_tile_rows<16>(smem, out, ny, m0, tn * 128, Mh);
     if (out2) {
       // the pre-activation z = [gate | up] (bf16 [M, Nb]) for the backward: the tile's gate columns, then its up
       // columns, staged side by side once the y tile has left the staging area
       __syncthreads();
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const int r = wm * 128 + mb * 32 + (lane & 31);
+        const int r = rowof(mb) + (lane & 31);
         const float sc = rsv[mb];
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
@@ -557,10 +577,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
         }
       }
       __syncthreads();
-      store_tile_rows<16>(smem, out2, Nb, m0, tn * 128, M);
-      store_tile_rows<16>(smem + 65536, out2, Nb, m0, ny + tn * 128, M);
+      store_tile_rows<16>(smem, out2, Nb, m0, tn * 128, Mh);
+      store_tile_rows<16>(smem + 65536, out2, Nb, m0, ny + tn * 128, Mh);
     }
   }
+}
+
+template <int MODE, bool FP8, bool MX = false, bool SMALL = false>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_kernel(
+    const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
+    const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
+    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs,
+    int panels, KSplit ks) {
+  gemm_epilogue_body<MODE, FP8, MX, SMALL, false>(A, B, gamma, R, rowsc, colsc, out, out2, part, M, K, Nb, group_m, rope, fold, mxs, panels, ks);
+}
+
+// The half-tile form of the bf16 row-scale modes: grid 2 (ntiles - ks.full), the tiles from ks.full on.
+template <int MODE>
+__global__ __launch_bounds__(NTHREADS, 1) void gemm_epilogue_half_kernel(
+    const void* __restrict__ A, const void* __restrict__ B, const float* __restrict__ gamma, const uint16_t* R,
+    const float* __restrict__ rowsc, const float* __restrict__ colsc, uint16_t* out, uint16_t* __restrict__ out2,
+    float* __restrict__ part, int M, int K, int Nb, int group_m, RopeParams rope, RowFold fold, uint8_t* mxs,
+    int panels, KSplit ks) {
+  gemm_epilogue_body<MODE, false, false, false, true>(A, B, gamma, R, rowsc, colsc, out, out2, part, M, K, Nb, group_m, rope, fold, mxs, panels, ks);
 }
 
 // K2: r[i] = 1 / sqrt((sum_t part[t][i]) / D + eps), t summed in order 0..T-1.
@@ -848,13 +887,34 @@ static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, 
   const int ntiles = tiles_m * tiles_n;
   constexpr KSplitRule rule = FP8 ? KSPLIT_E4M3 : KSPLIT_BF16;
   static_assert(rule.gran == (FP8 ? K8_MULTIPLE : K_MULTIPLE), "the split's K granule is one ring fill");
+  dim3 block(NTHREADS);
+  constexpr bool ROWSCALE_MODE = MODE == MODE_ROWSCALE || MODE == MODE_ROWSCALE_SWIGLU || MODE == MODE_ROWSCALE_ROPE;
+  if constexpr (!FP8 && ROWSCALE_MODE) {
+    if (ks.halves && ks.full >= 0 && ks.full < ntiles && M > SMALL_MAX_ROWS) {
+      // the whole tiles (a grid of `full`: tile_coords_split deals them all as whole tiles), then the last wave's tiles
+      // as 128-row halves in a launch of their own
+      KSplit whole;
+      whole.full = ks.full;
+      if (ks.full > 0) {
+        hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, false, MX>), dim3(ks.full), block, 0, stream, A, B, gamma, R,
+                           rowsc, colsc, out, out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels, whole);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+      }
+      hipLaunchKernelGGL((gemm_epilogue_half_kernel<MODE>), dim3(2 * (ntiles - ks.full)), block, 0, stream, A, B, gamma,
+                         R, rowsc, colsc, out, out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels,
+                         whole);
+      return hipGetLastError();
+    }
+  }
+  if (ks.halves) ks.full = -1;  // other kernels (or shapes) run whole tiles
   int nwg = ntiles;
   if (ks.full >= 0 && ks.full < ntiles && ks.part && ks.cnt && ks.lg >= 1 && ks.lg <= KSPLIT_MAX_LG &&
       K % (rule.gran << ks.lg) == 0 && (K >> ks.lg) >= rule.min_piece)
     nwg = ks.full + ((ntiles - ks.full) << ks.lg);
   else
     ks.full = -1;  // nothing to split, or a split this kernel or K cannot take: whole tiles
-  dim3 grid(nwg), block(NTHREADS);
+  dim3 grid(nwg);
   if constexpr (!FP8) {
     if (M <= SMALL_MAX_ROWS) {  // the small-row form: a quarter of the MFMAs per SIMD
       hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8, MX, true>), grid, block, 0, stream, A, B, gamma, R, rowsc,
@@ -865,6 +925,16 @@ static hipError_t launch_gemm(const void* A, const void* B, const float* gamma, 
   hipLaunchKernelGGL((gemm_epilogue_kernel<MODE, FP8, MX>), grid, block, 0, stream, A, B, gamma, R, rowsc, colsc, out,
                      out2, part, M, K, Nb, group_m_for(tiles_m), rope, fold, mxs, panels, ks);
   return hipGetLastError();
+}
+
+KSplit halves_plan(int64_t ntiles, int64_t M, int cus) {
+  KSplit ks;
+  if (cus <= 0 || ntiles <= 0 || M <= SMALL_MAX_ROWS) return ks;
+  const int64_t rem = ntiles % cus, tail_rows = M % BM;
+  if (rem == 0 || 2 * rem > cus || (tail_rows != 0 && tail_rows <= 128)) return ks;
+  ks.full = (int)(ntiles - rem);
+  ks.halves = 1;
+  return ks;
 }
 
 __global__ __launch_bounds__(256) void clear_tickets_kernel(int* __restrict__ cnt, int n) {

@@ -17,9 +17,15 @@ namespace coda {
 // another.  The counters must be zero at launch: the block's first GEMM clears those of its second GEMM (`clear`,
 // `nclear`), and launch_clear_tickets clears the first GEMM's own before it runs.  Both GEMMs of every block (K1 or
 // U1, and K3 or U3; bf16 and e4m3) can be split.
+//
+// The other form of a partial last wave (`halves`, the bf16 row-scale GEMMs: K3 and U3): each of its tiles is computed
+// as two 128-row halves over the whole of K, in a launch of its own right after the `full` whole tiles, so the last
+// wave runs on twice as many CUs with no exchange (gemm_mainloop's half-tile form; the results are the whole tiles'
+// bit for bit).  halves_plan chooses it where the split along K does not apply.
 struct KSplit {
   int full = -1;          // whole tiles; negative: no split
   int lg = 1;             // S = 2^lg pieces per split tile (1 .. 3)
+  int halves = 0;         // 1: the tiles from `full` on run as two 128-row halves (lg, part, cnt unused)
   float* part = nullptr;  // (ntiles - full) (2 S - 2) slots of KSPLIT_SLOT_FLOATS fp32: level l's 2^(lg-l) slots
                           // per tile follow the lower levels'
   int* cnt = nullptr;     // (ntiles - full) (S - 1) tickets: level l's 2^(lg-l-1) per tile after the lower levels'
@@ -50,6 +56,12 @@ constexpr KSplitRule KSPLIT_E4M3{256, 2048, 2048, 8192, 8};
 // The split of `ntiles` output tiles over K on `cus` CUs, by the rule of the operands' type (fp8 != 0: e4m3):
 // returns the number of whole tiles (ntiles when no split pays) and sets *lg to log2 of the pieces per split tile.
 int ksplit_plan(int64_t ntiles, int64_t K, int cus, int fp8, int* lg);
+// The half-tile form of a last wave of `ntiles` tiles of a bf16 row-scale GEMM with M rows on `cus` CUs: a KSplit with
+// halves set and `full` the whole tiles where the last wave's halves fit on the CUs (at most half of them filled by
+// whole tiles) and the last row tile has more than 128 rows or none missing; else no split.  Measured on MI355X: the
+// 1B MLP-out -> QKV second GEMM (a last wave of 128 tiles over K = 2048) 98 -> 93 us, 8192 x 2816 over K = 256
+// (96 tiles) 95 -> 89 us, a SwiGLU one with 128 tiles 98 -> 93 us.
+KSplit halves_plan(int64_t ntiles, int64_t M, int cus);
 // Zeroes n tickets (a small kernel on `stream`; graph-capturable, unlike a memset node).
 hipError_t launch_clear_tickets(int* cnt, int n, hipStream_t stream);
 

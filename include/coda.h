@@ -122,6 +122,9 @@ size_t coda_workspace_split_bytes(int64_t M, int64_t K1, int64_t D, int64_t N2, 
  * last wave of 256 x 256 tiles would leave most of the CUs idle, each of its tiles is computed as 2, 4 or 8 equal
  * ranges of K whose fp32 sums meet in a fixed binary tree before the epilogue (coda_workspace_bytes gives the rule
  * and the room this takes); where the first product is split, a small kernel that zeroes its tickets runs first.
+ * Where the second product's last wave fills at most half of the CUs and is not split along K, and M > 64 rows
+ * with a last row tile that is whole or longer than 128 rows, that wave's tiles run as two 128-row halves each, in
+ * a launch of their own after the whole tiles (no workspace; the results are the whole tiles' bit for bit).
  * After the call the workspace holds r [M] (fp32) at byte offset coda_workspace_r_offset(M, D).  Ownership, errors
  * and the asynchronous contract are the shared conventions above. */
 int coda_block_fwd(const void* X, const void* W1, const void* R, const float* gamma, const void* W2,

@@ -137,7 +137,8 @@ def test_block_equals_its_three_steps(wl):
     """coda_block_fwd (the partial-RMS reduce folded into the second GEMM where D / 256 <= 16, the separate
     reduce kernel otherwise) gives the same h, r and y, bit for bit, as the three step entry points run one
     after another: the fold forms r with the reduce kernel's own expression and summation order.  The block runs
-    whole tiles here (a workspace without the split room), as the step entry points do."""
+    without the split room here; where its second product's last wave then runs as 128-row halves (no_fold_t17),
+    each output is still the whole tile's chain of MFMAs, so the bits are the steps' too."""
     _say(f"[gpu] block vs its steps {wl.name}")
     d = DeviceInputs(make_inputs(wl))
     h, y, r = run_block(d, split=False)

@@ -42,7 +42,7 @@ def _stub_source(fatbin_symbol: str) -> str:
     src = open(os.path.join(ROOT, "gemm_epilogue_fusion_amd", "csrc", "launch.h")).read()
     src = re.sub(r"//[^\n]*", "", src)
     out = ['#include "launch.h"', "int g_launches = 0;", "namespace coda {"]
-    for ret, name, params in re.findall(r"\b(hipError_t|int)\s+(\w+)\s*\(([^;{]*)\)\s*;", src):
+    for ret, name, params in re.findall(r"\b(hipError_t|int|KSplit)\s+(\w+)\s*\(([^;{]*)\)\s*;", src):
         params = re.sub(r"\s*=\s*[^,]+", "", params)  # default arguments belong to the declaration only
         if name == "fold_supported":
             body = "return D / 256 <= 16;"
@@ -54,6 +54,11 @@ def _stub_source(fatbin_symbol: str) -> str:
                     "if (K % (2 * u.gran) || K / 2 < u.min_piece) return (int)ntiles; "
                     "int g = 1; while (g < 3 && 2 * (rem << (g + 1)) <= cus && K % ((int64_t)u.gran << (g + 1)) == 0 "
                     "&& (K >> (g + 1)) >= u.tree_piece) ++g; *lg = g; return (int)(ntiles - rem);")
+        elif name == "halves_plan":  # the half-tile rule of a row-scale GEMM's last wave
+            body = ("KSplit ks; if (cus <= 0 || ntiles <= 0 || M <= 64) return ks; "
+                    "const int64_t rem = ntiles % cus, t = M % 256; "
+                    "if (rem == 0 || 2 * rem > cus || (t != 0 && t <= 128)) return ks; "
+                    "ks.full = (int)(ntiles - rem); ks.halves = 1; return ks;")
         elif name == "gemm_ksplit":  # the split rule of the weight-gradient products
             body = ("const int tiles = ((M + 255) / 256) * (N / 256); int s = 1; "
                     "while (s < 8 && tiles * s < 256 && K % (128 * s * 2) == 0) s *= 2; return s;")
