@@ -134,10 +134,11 @@ __device__ __forceinline__ void gemm_epilogue_body(
   // row-scale modes of the second GEMM can fold the partial-RMS reduce in (see RowFold), except the e4m3 path
   // with per-row A scales, whose reduce kernel also quantises
   constexpr bool CAN_FOLD = (!FP8 || MX) && ROWSCALE_MODE;
-  // the mainloop ring (reused as the output staging area), plus the row-sum exchange of MODE_RES_PRMS or the
-  // folded row scales, plus the MX scale stages
+  // the mainloop ring (reused as the output staging area), plus the row-sum exchange of MODE_RES_PRMS (and the bf16
+  // K1's gamma) or the folded row scales, plus the MX scale stages
   constexpr int FOLD_LDS = CAN_FOLD ? 1024 + FOLD_MAX_T * BM * 4 : 0;  // row scales, then the partial sums
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 : FOLD_LDS) +
+  constexpr int GAMMA_LDS = MODE == MODE_RES_PRMS && !FP8 ? BN * 4 : 0;
+  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES + (MODE == MODE_RES_PRMS ? 4096 + GAMMA_LDS : FOLD_LDS) +
                                                     (MX_A ? NSTAGE * MX_STAGE_BYTES : 0)];
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = Nb / BN;
@@ -170,6 +171,12 @@ __device__ __forceinline__ void gemm_epilogue_body(
   // folded reduce: before the mainloop the partial sums of the tile's rows go global -> LDS (4 bytes per lane,
   // 64 rows per load, rows past M read row M-1), older than every stage load, so the mainloop's first wait
   // covers them; once the first stage has landed thread t < 256 sums row t's T values in order and forms r
+  // bf16 K1: gamma of the tile's 256 columns goes global -> LDS in one direct load of wave 0 before the mainloop,
+  // older than every stage load, so the mainloop's first wait covers it; the epilogue reads it from there (at 64
+  // rows, waiting for it after the mainloop cost 1.1 us of the block's 18 us)
+  const float* gamma_lds = (const float*)(smem + LDS_BYTES + 4096);
+  if (GAMMA_LDS > 0 && threadIdx.x < 64)
+    __builtin_amdgcn_global_load_lds(gamma + tn * BN + 4 * threadIdx.x, (lds_void*)gamma_lds, 16, 0, 0);
   const bool folding = CAN_FOLD && fold.T > 0;
   float* fold_r = (float*)(smem + LDS_BYTES);                 // [256] the row scales
   float* fold_part = (float*)(smem + LDS_BYTES + 1024);       // [T][256] the partial sums
@@ -348,15 +355,14 @@ __device__ __forceinline__ void gemm_epilogue_body(
   if (MODE == MODE_RES_PRMS || MODE == MODE_STORE || MODE == MODE_ROWSCALE) {
     // h * gamma is written by the bf16 K1 only (the e4m3 path forms it in K2 from the stored h)
     constexpr bool WRITE_HG = MODE == MODE_RES_PRMS && !FP8;
-    const int n_base = tn * BN + wn * 64 + 4 * half;
-    // gamma of this lane's 4-column groups (the same for every row), loaded before the wait for the residual tile
-    // so that the two latencies overlap
+    // gamma of this lane's 4-column groups (the same for every row), from the copy in LDS
     f32x4 gv[NB][4];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq)
-        gv[nb][gq] = WRITE_HG ? *(const f32x4*)(gamma + n_base + nb * 32 + 8 * gq) : (f32x4){1.f, 1.f, 1.f, 1.f};
+        gv[nb][gq] = WRITE_HG ? *(const f32x4*)(gamma_lds + wn * 64 + 4 * half + nb * 32 + 8 * gq)
+                              : (f32x4){1.f, 1.f, 1.f, 1.f};
     if (MODE == MODE_RES_PRMS) {
       // the residual tile R[m0.., tn*256..] into the staging area with direct loads (whole rows); the mainloop has
       // fetched rows 0 .. 191 as its ring drained.  A tile whose rows end before row 192 has nothing left to fetch
