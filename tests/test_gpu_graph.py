@@ -2,7 +2,7 @@
 block, replayed several times with other eager GPU work and synchronisations in between, gives the eager
 result bit for bit on every replay, and follows new data copied into its static inputs.  The library enqueues
 only kernels (no memset, no allocation, no host synchronisation), which is what makes a call capturable.  Two
-blocks in flight on two streams with their own workspaces give what each gives alone.
+blocks in flight on streams of their own with their own workspaces give what each gives alone.
 """
 import sys
 
@@ -51,7 +51,9 @@ def _capture(fn):
 CASES = [WORKLOADS["tiny"],
          Workload("graph_ragged_swiglu", M=300, K1=512, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=21),
          # every tile of the second product split along K: the tickets are cleared by the first kernel of each replay
-         Workload("graph_split_swiglu", M=300, K1=256, D=1024, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=23)]
+         Workload("graph_split_swiglu", M=300, K1=256, D=1024, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=23),
+         # every tile of the second product as two 128-row halves: two launches of the second GEMM's kernels
+         Workload("graph_halves", M=512, K1=256, D=256, N2=2048, epi=EPI_IDENTITY, eps=1e-5, seed=24)]
 
 
 @pytest.mark.parametrize("wl", CASES, ids=[w.name for w in CASES])
@@ -127,13 +129,15 @@ def test_backward_graph_replays_match_eager():
 
 
 def test_concurrent_streams_distinct_workspaces():
-    """Two blocks in flight at once on two streams, each with its own workspace (the documented condition for
+    """Blocks in flight at once on several streams, each with its own workspace (the documented condition for
     concurrent calls), give the results each gives alone, bit for bit."""
     wls = [Workload("stream_a", M=513, K1=256, D=512, N2=1024, epi=EPI_SWIGLU, eps=1e-5, seed=31),
            Workload("stream_b", M=300, K1=384, D=768, N2=512, epi=0, eps=1e-5, seed=32),
            # the second product split along K: each call's tickets and slots live in its own workspace
-           Workload("stream_c_split", M=200, K1=256, D=2048, N2=512, epi=0, eps=1e-5, seed=33)]
-    _say("[gpu] two streams " + ", ".join(w.name for w in wls))
+           Workload("stream_c_split", M=200, K1=256, D=2048, N2=512, epi=0, eps=1e-5, seed=33),
+           # the second product's 4 tiles as 128-row halves
+           Workload("stream_d_halves", M=450, K1=256, D=512, N2=512, epi=0, eps=1e-5, seed=34)]
+    _say("[gpu] concurrent streams " + ", ".join(w.name for w in wls))
     runs = []
     for wl in wls:
         d = DeviceInputs(make_inputs(wl))
@@ -148,7 +152,7 @@ def test_concurrent_streams_distinct_workspaces():
     streams = [torch.cuda.Stream() for _ in runs]
     for s in streams:
         s.wait_stream(torch.cuda.current_stream())
-    for _ in range(3):  # interleaved launches on the two streams
+    for _ in range(3):  # interleaved launches on the streams
         for s, (wl, d, ws, outs) in zip(streams, runs):
             with torch.cuda.stream(s):
                 cb.coda_block_fwd(d.X, d.W1, d.R, d.gamma, d.W2, wl.eps, wl.epi, outs[1][0], outs[1][1], ws)
