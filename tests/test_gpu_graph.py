@@ -10,7 +10,7 @@ import torch
 import pytest
 
 from gemm_epilogue_fusion_amd import binding as cb
-from gemm_epilogue_fusion_amd.inputs import EPI_SWIGLU, WORKLOADS, Workload, make_grads, make_inputs
+from gemm_epilogue_fusion_amd.inputs import EPI_IDENTITY, EPI_SWIGLU, WORKLOADS, Workload, make_grads, make_inputs
 
 from parity import DeviceInputs
 
