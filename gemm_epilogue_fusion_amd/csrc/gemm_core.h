@@ -687,14 +687,16 @@ __device__ __forceinline__ void store_nt(void* p, T v) { __builtin_nontemporal_s
 template <int CH>
 __device__ __forceinline__ int tile_off(int r, int c) { return r * (16 * CH) + ((c ^ (r & (CH - 1))) << 4); }
 
-// Whole rows of the staged tile to dst[(m0 + r) * ld + n0 ...], 16 bytes per lane; rows >= M are skipped.
-template <int CH>
+// Whole rows of the staged tile to dst[(m0 + r) * ld + n0 ...], 16 bytes per lane; rows >= M are skipped.  ROWS:
+// the staged rows read (the first ROWS of the tile).
+template <int CH, int ROWS = BM>
 __device__ __forceinline__ void store_tile_rows(const char* smem, uint16_t* dst, int ld, int m0, int n0, int M) {
   constexpr int ROWS_PER_PASS = NTHREADS / CH;
+  static_assert(ROWS % ROWS_PER_PASS == 0, "whole passes");
   const int t = threadIdx.x;
   const int c = t % CH;
 #pragma unroll
-  for (int p = 0; p < BM / ROWS_PER_PASS; ++p) {
+  for (int p = 0; p < ROWS / ROWS_PER_PASS; ++p) {
     const int r = p * ROWS_PER_PASS + t / CH;
     const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, c));
     const int m = m0 + r;
@@ -704,16 +706,18 @@ __device__ __forceinline__ void store_tile_rows(const char* smem, uint16_t* dst,
 
 // The staged tile to K panels of 32 columns: column n0 + 32 p + j of row m0 + r goes to
 // dst[(n0 / 32 + p) * panel + (m0 + r) * 32 + j] (panel = rows * 32 elements, the panel stride); rows >= M are
-// skipped.  Each wave writes 1 KiB of one panel per pass (16 rows x 64 bytes, contiguous).
-template <int CH>
+// skipped.  Each wave writes 1 KiB of one panel per pass (16 rows x 64 bytes, contiguous).  ROWS as in
+// store_tile_rows.
+template <int CH, int ROWS = BM>
 __device__ __forceinline__ void store_tile_panels(const char* smem, uint16_t* dst, int64_t panel, int m0, int n0,
                                                   int M) {
+  static_assert(ROWS * CH % NTHREADS == 0, "whole passes");
   const int t = threadIdx.x;
 #pragma unroll
-  for (int p = 0; p < BM * CH / NTHREADS; ++p) {
+  for (int p = 0; p < ROWS * CH / NTHREADS; ++p) {
     const int g = p * NTHREADS + t;       // 16-byte chunk of the tile in panel order
-    const int pn = g / (BM * 4);          // panel (4 chunks of 16 bytes per row)
-    const int w = g % (BM * 4);
+    const int pn = g / (ROWS * 4);        // panel (4 chunks of 16 bytes per row)
+    const int w = g % (ROWS * 4);
     const int r = w >> 2, c4 = w & 3;
     const u32x4 v = *(const u32x4*)(smem + tile_off<CH>(r, 4 * pn + c4));
     const int m = m0 + r;

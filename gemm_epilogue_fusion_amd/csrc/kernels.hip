@@ -372,43 +372,57 @@ __device__ __forceinline__ void gemm_epilogue_body(
     }
     float ss[4];
     u32x2 hgv[4][NB][4];  // bf16(h * gamma), staged after h has been written out
+    // The small-row form stores rows 0 .. 63 only, so it leaves the other rows' slots alone and stages h * gamma in
+    // rows 64 .. 127 of the staging area beside h: both tiles go out after one barrier instead of three.
+    constexpr bool ONE_PASS = SMALL && WRITE_HG;
+    constexpr int STAGED = SMALL ? SMALL_MAX_ROWS : BM;  // the staged rows that may be stored
+    char* const hg_stage = smem + SMALL_MAX_ROWS * 512;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
       const int r = rowof(mb) + (lane & 31);
       float s = 0.0f;
+      const bool live = !SMALL || (wm == 0 && mb < 2);
+      if (live) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          char* slot = smem + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half;
-          const f32x4 c = csv[nb * 4 + gq];
-          const float sc = rsv[mb];
-          float v0 = acc[mb][nb][4 * gq + 0] * sc * c[0], v1 = acc[mb][nb][4 * gq + 1] * sc * c[1];
-          float v2 = acc[mb][nb][4 * gq + 2] * sc * c[2], v3 = acc[mb][nb][4 * gq + 3] * sc * c[3];
-          if (MODE == MODE_RES_PRMS) {
-            // the slot holds this lane's residual values; h replaces them in place
-            const u32x2 r2 = *(const u32x2*)slot;
-            v0 += bf16_lo(r2[0]);
-            v1 += bf16_hi(r2[0]);
-            v2 += bf16_lo(r2[1]);
-            v3 += bf16_hi(r2[1]);
-            s += v0 * v0;
-            s += v1 * v1;
-            s += v2 * v2;
-            s += v3 * v3;
-            if (WRITE_HG) {
-              const f32x4 g = gv[nb][gq];
-              hgv[mb][nb][gq] = (u32x2){pack_bf16(v0 * g[0], v1 * g[1]), pack_bf16(v2 * g[2], v3 * g[3])};
+          for (int gq = 0; gq < 4; ++gq) {
+            char* slot = smem + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half;
+            const f32x4 c = csv[nb * 4 + gq];
+            const float sc = rsv[mb];
+            float v0 = acc[mb][nb][4 * gq + 0] * sc * c[0], v1 = acc[mb][nb][4 * gq + 1] * sc * c[1];
+            float v2 = acc[mb][nb][4 * gq + 2] * sc * c[2], v3 = acc[mb][nb][4 * gq + 3] * sc * c[3];
+            if (MODE == MODE_RES_PRMS) {
+              // the slot holds this lane's residual values; h replaces them in place
+              const u32x2 r2 = *(const u32x2*)slot;
+              v0 += bf16_lo(r2[0]);
+              v1 += bf16_hi(r2[0]);
+              v2 += bf16_lo(r2[1]);
+              v3 += bf16_hi(r2[1]);
+              s += v0 * v0;
+              s += v1 * v1;
+              s += v2 * v2;
+              s += v3 * v3;
+              if (WRITE_HG) {
+                const f32x4 g = gv[nb][gq];
+                const u32x2 hgw = {pack_bf16(v0 * g[0], v1 * g[1]), pack_bf16(v2 * g[2], v3 * g[3])};
+                if (ONE_PASS)
+                  *(u32x2*)(hg_stage + tile_off<32>(r, wn * 8 + nb * 4 + gq) + 8 * half) = hgw;
+                else
+                  hgv[mb][nb][gq] = hgw;
+              }
             }
+            *(u32x2*)slot = (u32x2){pack_bf16(v0, v1), pack_bf16(v2, v3)};
           }
-          *(u32x2*)slot = (u32x2){pack_bf16(v0, v1), pack_bf16(v2, v3)};
-        }
+      }
       ss[mb] = s;
     }
-    __syncthreads();
-    store_tile_rows<32>(smem, out, Nb, m0, tn * BN, Mh);
+    if (!ONE_PASS) {
+      __syncthreads();
+      store_tile_rows<32, STAGED>(smem, out, Nb, m0, tn * BN, Mh);
+    }
     if (MODE == MODE_RES_PRMS) {
-      if (WRITE_HG) {
+      if (WRITE_HG && !ONE_PASS) {
         __syncthreads();
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
@@ -430,11 +444,13 @@ __device__ __forceinline__ void gemm_epilogue_body(
         for (int mb = 0; mb < 4; ++mb) red[wn * 256 + rowof(mb) + lane] = ss[mb];
       }
       __syncthreads();
+      if (ONE_PASS) store_tile_rows<32, STAGED>(smem, out, Nb, m0, tn * BN, Mh);
       if (WRITE_HG) {
+        const char* hs = ONE_PASS ? hg_stage : smem;
         if (panels)
-          store_tile_panels<32>(smem, out2, (int64_t)M * 32, m0, tn * BN, M);
+          store_tile_panels<32, STAGED>(hs, out2, (int64_t)M * 32, m0, tn * BN, M);
         else
-          store_tile_rows<32>(smem, out2, Nb, m0, tn * BN, M);
+          store_tile_rows<32, STAGED>(hs, out2, Nb, m0, tn * BN, M);
       }
       if (wn == 0 && lane < 32) {
 #pragma unroll
