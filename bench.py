@@ -573,7 +573,8 @@ def time_bwd(wl, X, W1, g, W2, h, ws, n_ev: int, warmup: int, torch, cb) -> dict
 
 def time_tiny(dev, torch, cb) -> dict:
     """The tiny block (M=64, K1=D=256, N2=512), launch-bound: microseconds per block called eagerly (two kernel
-    launches through the C ABI each) and replayed from a HIP graph holding 50 blocks."""
+    launches through the C ABI each) and replayed from a HIP graph holding 50 blocks, and the unfused baseline (three
+    kernels) called eagerly the same way."""
     from gemm_epilogue_fusion_amd.inputs import WORKLOADS, make_inputs
 
     wl = WORKLOADS["tiny"]
@@ -587,6 +588,8 @@ def time_tiny(dev, torch, cb) -> dict:
         call()
     torch.cuda.synchronize()
     eager_ms = time_loop(call, 500, torch)
+    ws_u = cb.alloc_workspace(wl.M, wl.K1, wl.D, wl.N2, wl.epi, unfused=1, device=dev)
+    unfused_ms = time_loop(lambda: cb.coda_block_unfused(X, W1, R, g, W2, wl.eps, wl.epi, h, y, ws_u), 500, torch)
     per_graph = 50
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -603,7 +606,8 @@ def time_tiny(dev, torch, cb) -> dict:
     graph_ms = time_loop(graph.replay, 20, torch) / per_graph
     return {"workload": wl.name, "M": wl.M, "K1": wl.K1, "D": wl.D, "N2": wl.N2, "kernels_per_block": 2,
             "eager_us_per_block": round(eager_ms * 1e3, 2), "graph_us_per_block": round(graph_ms * 1e3, 2),
-            "graph_blocks_per_replay": per_graph}
+            "graph_blocks_per_replay": per_graph, "unfused_eager_us_per_block": round(unfused_ms * 1e3, 2),
+            "speedup_fused_vs_unfused_eager": round(unfused_ms / eager_ms, 4)}
 
 
 def time_row_shard(dev, n_ev: int, torch, cb) -> dict:
